@@ -1,0 +1,276 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each test is chosen so that a plausible slip in the oracle (a dropped term in
+GeLU or its derivative, a wrong sign, a transposed operand, a split along the
+wrong axis, a shard sum in the wrong place) fails at least one of them.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import oracle as O
+from tensor_transformer_mlp_03_amd import inputs as I
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "gelu_values.txt")
+
+
+def _rand(shape, seed, std=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * std
+
+
+def _golden():
+    rows = [l.split() for l in open(GOLDEN) if l.strip() and not l.startswith("#")]
+    return np.array([[float(v) for v in r] for r in rows])
+
+
+# --- GeLU: textbook values -------------------------------------------------
+def test_golden_table_is_the_normal_distribution():
+    # Guards the fixture against typos: scipy's ndtr is a routine separate from the
+    # erf the oracle calls.
+    from scipy.stats import norm
+    g = _golden()
+    np.testing.assert_allclose(norm.cdf(g[:, 0]), g[:, 1], rtol=1e-14, atol=1e-17)
+    np.testing.assert_allclose(norm.pdf(g[:, 0]), g[:, 2], rtol=1e-14, atol=1e-17)
+
+
+def test_gelu_textbook_values():
+    g = _golden()
+    x, Phi = g[:, 0], g[:, 1]
+    np.testing.assert_allclose(O.gelu(x), x * Phi, rtol=1e-14, atol=1e-16)
+    assert O.gelu(np.array([0.0]))[0] == 0.0
+    # exact-erf, not the tanh approximation (which gives 0.841191990608 at x = 1)
+    assert abs(O.gelu(np.array([1.0]))[0] - 0.8413447460685429) < 1e-15
+
+
+def test_gelu_grad_textbook_values():
+    g = _golden()
+    x, Phi, phi = g[:, 0], g[:, 1], g[:, 2]
+    np.testing.assert_allclose(O.gelu_grad(x), Phi + x * phi, rtol=1e-14, atol=1e-16)
+    assert O.gelu_grad(np.array([0.0]))[0] == 0.5
+
+
+def test_gelu_asymptotes():
+    big = np.array([10.0, 20.0, 40.0])
+    np.testing.assert_allclose(O.gelu(big), big, rtol=1e-15)
+    np.testing.assert_allclose(O.gelu(-big), 0.0, atol=1e-20)
+    np.testing.assert_allclose(O.gelu_grad(big), 1.0, rtol=1e-15)
+    np.testing.assert_allclose(O.gelu_grad(-big), 0.0, atol=1e-20)
+
+
+def test_gelu_grad_is_derivative_of_gelu():
+    x = np.linspace(-6, 6, 241)
+    h = 1e-5
+    fd = (O.gelu(x + h) - O.gelu(x - h)) / (2 * h)
+    np.testing.assert_allclose(O.gelu_grad(x), fd, rtol=1e-8, atol=1e-10)
+
+
+# --- bf16 decoding ("大模型训练" notes §6.1) ------------------------------------
+def test_decode_bf16_exact_values():
+    bits = np.array([0x0000, 0x8000, 0x3F80, 0xBF80, 0xC000, 0x4140, 0x7F7F, 0x0080, 0x3C00], dtype=np.uint16)
+    want = [0.0, -0.0, 1.0, -1.0, -2.0, 12.0, 3.3895313892515355e38, 1.1754943508222875e-38, 0.0078125]
+    got = O.decode_bf16(bits)
+    assert list(got) == want
+    assert math.copysign(1.0, got[1]) == -1.0
+
+
+def test_decode_bf16_matches_torch():
+    torch = pytest.importorskip("torch")
+    bits = np.random.default_rng(3).integers(0, 1 << 16, size=200000, dtype=np.uint32).astype(np.uint16)
+    finite = (bits & 0x7F80) != 0x7F80
+    bits = bits[finite]
+    t = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(O.decode_bf16(bits), t)
+
+
+# --- brute force on tiny shapes --------------------------------------------
+def _brute(X, A, B, dZ):
+    M, H, F = len(X), len(X[0]), len(A[0])
+    P = [[sum(X[m][h] * A[h][f] for h in range(H)) for f in range(F)] for m in range(M)]
+    G = [[0.5 * p * (1 + math.erf(p / math.sqrt(2))) for p in row] for row in P]
+    Z = [[sum(G[m][f] * B[f][h] for f in range(F)) for h in range(H)] for m in range(M)]
+    dG = [[sum(dZ[m][h] * B[f][h] for h in range(H)) for f in range(F)] for m in range(M)]
+    dP = [[dG[m][f] * (0.5 * (1 + math.erf(P[m][f] / math.sqrt(2)))
+                       + P[m][f] * math.exp(-P[m][f] ** 2 / 2) / math.sqrt(2 * math.pi))
+           for f in range(F)] for m in range(M)]
+    dB = [[sum(G[m][f] * dZ[m][h] for m in range(M)) for h in range(H)] for f in range(F)]
+    dA = [[sum(X[m][h] * dP[m][f] for m in range(M)) for f in range(F)] for h in range(H)]
+    dX = [[sum(dP[m][f] * A[h][f] for f in range(F)) for h in range(H)] for m in range(M)]
+    return {k: np.array(v) for k, v in dict(Z=Z, dB=dB, dA=dA, dX=dX, P=P, G=G, dP=dP).items()}
+
+
+@pytest.mark.parametrize("shape", [(3, 4, 5), (5, 2, 7), (1, 6, 3)])
+def test_brute_force_tiny(shape):
+    M, H, F = shape
+    X, A, B, dZ = _rand((M, H), 1), _rand((H, F), 2), _rand((F, H), 3), _rand((M, H), 4)
+    want = _brute(X.tolist(), A.tolist(), B.tolist(), dZ.tolist())
+    fwd = O.mlp_forward(X, A, B)
+    bwd = O.mlp_backward(dZ, X, A, B)
+    for k in ("P", "G", "Z"):
+        np.testing.assert_allclose(fwd[k], want[k], rtol=1e-13, atol=1e-14)
+    for k in ("dP", "dB", "dA", "dX"):
+        np.testing.assert_allclose(bwd[k], want[k], rtol=1e-13, atol=1e-14)
+
+
+# --- finite differences: the backward is the derivative of the forward ------
+def test_finite_differences():
+    M, H, F = 4, 5, 6
+    X, A, B, dZ = _rand((M, H), 11), _rand((H, F), 12), _rand((F, H), 13), _rand((M, H), 14)
+    bwd = O.mlp_backward(dZ, X, A, B)
+
+    def loss(X_, A_, B_):
+        return float(np.sum(dZ * O.mlp_forward(X_, A_, B_)["Z"]))
+
+    h = 1e-6
+    for name, T, grad in (("X", X, bwd["dX"]), ("A", A, bwd["dA"]), ("B", B, bwd["dB"])):
+        fd = np.zeros_like(T)
+        for idx in np.ndindex(T.shape):
+            Tp, Tm = T.copy(), T.copy()
+            Tp[idx] += h
+            Tm[idx] -= h
+            args_p = {"X": X, "A": A, "B": B, name: Tp}
+            args_m = {"X": X, "A": A, "B": B, name: Tm}
+            fd[idx] = (loss(args_p["X"], args_p["A"], args_p["B"]) - loss(args_m["X"], args_m["A"], args_m["B"])) / (2 * h)
+        np.testing.assert_allclose(grad, fd, rtol=1e-6, atol=1e-7, err_msg=name)
+
+
+# --- an independent library implementation -----------------------------------
+@pytest.mark.parametrize("shape", [(64, 256, 512), (37, 40, 72)])
+def test_matches_torch_float64_autograd(shape):
+    torch = pytest.importorskip("torch")
+    M, H, F = shape
+    X, A, B, dZ = _rand((M, H), 21), _rand((H, F), 22, 0.05), _rand((F, H), 23, 0.05), _rand((M, H), 24)
+    tX, tA, tB = (torch.tensor(v, dtype=torch.float64, requires_grad=True) for v in (X, A, B))
+    tZ = torch.nn.functional.gelu(tX @ tA, approximate="none") @ tB
+    tZ.backward(torch.tensor(dZ, dtype=torch.float64))
+    fwd = O.mlp_forward(X, A, B)
+    bwd = O.mlp_backward(dZ, X, A, B)
+    np.testing.assert_allclose(fwd["Z"], tZ.detach().numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(bwd["dX"], tX.grad.numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(bwd["dA"], tA.grad.numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(bwd["dB"], tB.grad.numpy(), rtol=1e-12, atol=1e-12)
+
+
+# --- the tensor-parallel split ("大模型训练" notes §3.1) ------------------------
+def _rel(a, b):
+    return float(np.max(np.abs(a - b)) / np.max(np.abs(b)))
+
+
+@pytest.mark.parametrize("t", [1, 2, 4, 8])
+def test_shard_sum_identity(t):
+    w = I.custom_workload(900, M=96, H=128, F_i=64, t=8)
+    inp = I.make_inputs(w)
+    X = O.decode_bf16(inp.X)
+    A = np.concatenate([O.decode_bf16(a) for a in inp.A], axis=1)
+    B = np.concatenate([O.decode_bf16(b) for b in inp.B], axis=0)
+    full = O.mlp_forward(X, A, B)["Z"]
+    Z, parts = O.tp_forward(X, O.split_columns(A, t), O.split_rows(B, t))
+    assert len(parts) == t
+    assert _rel(Z, full) < 1e-12
+    if t > 1:  # a single shard is not the whole answer
+        assert _rel(parts[0], full) > 1e-2
+
+
+@pytest.mark.parametrize("t", [2, 4, 8])
+def test_sharded_gradients_equal_unsharded(t):
+    M, H, F = 48, 64, 256
+    X, A, B, dZ = _rand((M, H), 31), _rand((H, F), 32, 0.05), _rand((F, H), 33, 0.05), _rand((M, H), 34)
+    ref = O.mlp_backward(dZ, X, A, B)
+    dX, dX_parts, dA_parts, dB_parts = O.tp_backward(dZ, X, O.split_columns(A, t), O.split_rows(B, t))
+    assert _rel(dX, ref["dX"]) < 1e-12
+    assert _rel(np.concatenate(dA_parts, axis=1), ref["dA"]) < 1e-12
+    assert _rel(np.concatenate(dB_parts, axis=0), ref["dB"]) < 1e-12
+    assert _rel(dX_parts[0], ref["dX"]) > 1e-2
+
+
+def test_split_direction_matters():
+    """Cutting A by rows (and X by columns) and applying GeLU per rank is wrong,
+    because GeLU is non-linear (QLM page §2.1.2.2 part 3); without the GeLU the
+    same row split is exact."""
+    M, H, F, t = 32, 64, 96, 2
+    X, A = _rand((M, H), 41), _rand((H, F), 42, 0.2)
+    h = H // t
+    row_split = sum(O.gelu(X[:, i * h:(i + 1) * h] @ A[i * h:(i + 1) * h, :]) for i in range(t))
+    col_split = np.concatenate([O.gelu(X @ a) for a in O.split_columns(A, t)], axis=1)
+    exact = O.gelu(X @ A)
+    assert _rel(col_split, exact) < 1e-14
+    assert _rel(row_split, exact) > 0.05
+    linear = sum(X[:, i * h:(i + 1) * h] @ A[i * h:(i + 1) * h, :] for i in range(t))
+    assert _rel(linear, X @ A) < 1e-13
+
+
+def test_split_helpers_partition():
+    A = np.arange(4 * 12, dtype=np.float64).reshape(4, 12)
+    cols = O.split_columns(A, 3)
+    assert [c.shape for c in cols] == [(4, 4)] * 3
+    np.testing.assert_array_equal(np.concatenate(cols, axis=1), A)
+    rows = O.split_rows(A.T, 3)
+    np.testing.assert_array_equal(np.concatenate(rows, axis=0), A.T)
+    with pytest.raises(ValueError):
+        O.split_columns(A, 5)
+
+
+# --- linearity and special cases -------------------------------------------
+def test_linearity():
+    M, H, F = 16, 24, 40
+    X, A, B, B2 = _rand((M, H), 51), _rand((H, F), 52, 0.1), _rand((F, H), 53), _rand((F, H), 54)
+    dZ, dZ2 = _rand((M, H), 55), _rand((M, H), 56)
+    a, b = 0.75, -1.5
+    Zc = O.mlp_forward(X, A, a * B + b * B2)["Z"]
+    np.testing.assert_allclose(Zc, a * O.mlp_forward(X, A, B)["Z"] + b * O.mlp_forward(X, A, B2)["Z"], rtol=1e-12, atol=1e-12)
+    g1, g2, gc = O.mlp_backward(dZ, X, A, B), O.mlp_backward(dZ2, X, A, B), O.mlp_backward(a * dZ + b * dZ2, X, A, B)
+    for k in ("dX", "dA", "dB"):
+        np.testing.assert_allclose(gc[k], a * g1[k] + b * g2[k], rtol=1e-12, atol=1e-12)
+
+
+def test_zero_weights_closed_form():
+    # A = 0: P = 0, GeLU(0) = 0 and GeLU'(0) = 1/2, so Z = 0, dB = 0, dX = 0 and
+    # dA = 1/2 X^T dZ B^T.
+    M, H, F = 12, 10, 14
+    X, B, dZ = _rand((M, H), 61), _rand((F, H), 62), _rand((M, H), 63)
+    A = np.zeros((H, F))
+    f, g = O.mlp_forward(X, A, B), O.mlp_backward(dZ, X, A, B)
+    assert np.all(f["Z"] == 0) and np.all(g["dB"] == 0) and np.all(g["dX"] == 0)
+    np.testing.assert_allclose(g["dA"], 0.5 * X.T @ (dZ @ B.T), rtol=1e-14, atol=1e-14)
+
+
+def test_zero_input_closed_form():
+    # X = 0: Z = 0, dA = 0, dB = 0, dX = 1/2 dZ B^T A^T.
+    M, H, F = 9, 8, 16
+    A, B, dZ = _rand((H, F), 71), _rand((F, H), 72), _rand((M, H), 73)
+    X = np.zeros((M, H))
+    f, g = O.mlp_forward(X, A, B), O.mlp_backward(dZ, X, A, B)
+    assert np.all(f["Z"] == 0) and np.all(g["dA"] == 0) and np.all(g["dB"] == 0)
+    np.testing.assert_allclose(g["dX"], 0.5 * (dZ @ B.T) @ A.T, rtol=1e-14, atol=1e-14)
+
+
+def test_tokens_independent():
+    # a permutation of the rows of X (and dZ) permutes Z and dX, and leaves the
+    # weight gradients unchanged (sequence-parallel series §2.4)
+    M, H, F = 20, 16, 32
+    X, A, B, dZ = _rand((M, H), 81), _rand((H, F), 82, 0.2), _rand((F, H), 83), _rand((M, H), 84)
+    perm = np.random.default_rng(85).permutation(M)
+    f, fp = O.mlp_forward(X, A, B), O.mlp_forward(X[perm], A, B)
+    np.testing.assert_allclose(fp["Z"], f["Z"][perm], rtol=1e-14, atol=1e-14)
+    g, gp = O.mlp_backward(dZ, X, A, B), O.mlp_backward(dZ[perm], X[perm], A, B)
+    np.testing.assert_allclose(gp["dX"], g["dX"][perm], rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(gp["dA"], g["dA"], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(gp["dB"], g["dB"], rtol=1e-12, atol=1e-13)
+
+
+def test_sampled_outputs_match_full():
+    M, H, F = 40, 24, 56
+    X, A, B, dZ = _rand((M, H), 91), _rand((H, F), 92, 0.2), _rand((F, H), 93), _rand((M, H), 94)
+    f, g = O.mlp_forward(X, A, B), O.mlp_backward(dZ, X, A, B)
+    rows, cols = np.array([0, 7, 39]), np.array([1, 30, 55])
+    np.testing.assert_allclose(O.forward_rows(X, A, B, rows), f["Z"][rows], rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(O.backward_dX_rows(dZ, X, A, B, rows), g["dX"][rows], rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(O.backward_dA_cols(dZ, X, A, B, cols), g["dA"][:, cols], rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(O.backward_dB_rows(dZ, X, A, B, cols), g["dB"][cols, :], rtol=1e-13, atol=1e-14)
+
+
+def test_tolerance_rule():
+    ref = np.array([[-4.0, 2.0], [1.0, 0.5]])
+    assert O.tolerance(ref) == pytest.approx(1e-2 * 4.0 + 1e-3)
+    assert O.max_abs_err(ref + 0.01, ref) == pytest.approx(0.01)
