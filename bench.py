@@ -1,0 +1,171 @@
+#!/usr/bin/env python3
+"""Benchmark of one tensor-parallel rank's share of the transformer MLP on MI355X.
+
+A step is one pass of the whole path over one batch of synthetic input: the
+forward of every shard (GEMM1 + GeLU, GEMM2), the rank-order sum of the partial
+outputs, the backward of every shard (dGeLU GEMM, dB, dA, dX GEMMs, split-K
+reductions) and the sum of the partial input gradients.  Inputs are resident in
+HBM before the timed region starts.
+
+Prints ONE JSON line.  ``value`` is model TFLOP/s of the whole job
+(12*M*H*F_i per shard and step; recompute FLOPs are not counted), ``roofline``
+describes the kernel that takes the most time (algorithmic FLOPs per launch over
+its average launch time from HIP events recorded on its stream inside the timed
+region), ``cpu_baseline`` is the CPU oracle timed on a bounded row sample of the
+same workload.
+
+    python bench.py [--config 3] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+METRIC = "TP-MLP fwd+bwd TFLOP/s per rank shard (bf16) and % of MFMA dense peak"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def gemm_flops(w):
+    """Algorithmic FLOPs of one launch of each GEMM kind for one shard."""
+    M, H, F = w.M, w.H, w.F_i
+    f = 2.0 * M * H * F
+    return {"fwd_gemm1_gelu": f, "fwd_gemm2": f, "bwd_recompute": f, "bwd_dgelu": f, "bwd_dB": f, "bwd_dA": f,
+            "bwd_dX": f}
+
+
+def cpu_baseline(w, target_s=12.0):
+    """The oracle's forward+backward of the first timed shard on a sample of token
+    rows (tokens are independent, so the work per row is the full per-row work)."""
+    import numpy as np
+    from oracle import oracle as O
+    from tensor_transformer_mlp_03_amd import inputs as I
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    i = w.shards_timed[0]
+    A = O.decode_bf16(I.make_A_shard(w, i))
+    B = O.decode_bf16(I.make_B_shard(w, i))
+    X_all, dZ_all = I.make_X(w), I.make_dZ(w)
+
+    def run(rows):
+        X, dZ = O.decode_bf16(X_all[:rows]), O.decode_bf16(dZ_all[:rows])
+        t0 = time.perf_counter()
+        O.mlp_forward(X, A, B)
+        O.mlp_backward(dZ, X, A, B)
+        return time.perf_counter() - t0
+
+    rows = min(w.M, 256)
+    dt = run(rows)
+    if dt < target_s / 4 and rows < w.M:
+        rows = int(min(w.M, max(rows, rows * target_s / max(dt, 1e-3))) // 8 * 8)
+        dt = run(rows)
+    flops = 12.0 * rows * w.H * w.F_i
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"float64 oracle forward+backward of shard {i} on the first {rows} of {w.M} token rows "
+                      f"(H={w.H}, F_i={w.F_i}); {dt:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=3, help="workload index 0-4 (default 3)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the tensor-parallel "
+              "ranks' shards run one after another on a single GPU).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from tensor_transformer_mlp_03_amd import _lib as L
+    from tensor_transformer_mlp_03_amd import inputs as I
+    from tensor_transformer_mlp_03_amd.device import DeviceMLP
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    L.lib()
+    w = I.CONFIGS[args.config]
+    shards = list(w.shards_timed)
+    driver = len(shards) == w.t
+    log(f"[bench] workload {w.name}: M={w.M} H={w.H} F_i={w.F_i} t={w.t} shards={shards} "
+        f"{'recompute' if w.recompute else 'store P'}; generating inputs")
+    inp = I.make_inputs(w, shards=shards)
+    d = DeviceMLP(inp, store_p=not w.recompute, driver=driver)
+    del inp
+    torch.cuda.synchronize()
+    log("[bench] inputs resident; warmup")
+    for _ in range(args.warmup):
+        d.step()
+    torch.cuda.synchronize()
+
+    n_launch = 16 * (len(shards) + 1) * max(args.steps, 1)
+    L.tpmlp_timing_begin(n_launch)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        d.step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    stats, dropped = L.tpmlp_timing_end()
+    log(f"[bench] timed {args.steps} steps in {t1 - t0:.4f} s")
+
+    ms_per_step = (t1 - t0) * 1e3 / max(args.steps, 1)
+    flops_step = w.model_flops_per_shard() * len(shards)
+    value = flops_step / (ms_per_step * 1e-3) / 1e12
+
+    per_launch = gemm_flops(w)
+    kernels = {}
+    for name, (count, total_ms) in stats.items():
+        if count:
+            kernels[name] = {"launches": count, "avg_us": round(total_ms * 1e3 / count, 2),
+                             "share": round(total_ms / sum(v[1] for v in stats.values()), 4)}
+            if name in per_launch:
+                kernels[name]["tflops"] = round(per_launch[name] / (total_ms * 1e-3 / count) / 1e12, 1)
+    for name, k in sorted(kernels.items(), key=lambda kv: -kv[1]["share"]):
+        log(f"  {name:16s} {k}")
+    dom = max((n for n in kernels if n in per_launch), key=lambda n: stats[n][1])
+    avg_s = stats[dom][1] * 1e-3 / stats[dom][0]
+    achieved = per_launch[dom] / avg_s / 1e12
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "avg_launch_us": round(avg_s * 1e6, 2)}
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "M": w.M, "H": w.H, "F": w.F, "t": w.t, "F_i": w.F_i,
+                   "shards_per_step": len(shards), "pre_activation": "recompute" if w.recompute else "stored",
+                   "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4), "timing_dropped": dropped},
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a row sample")
+        result["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

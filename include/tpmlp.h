@@ -1,0 +1,190 @@
+/*
+ * libtpmlp — one tensor-parallel rank's share of the transformer MLP on MI355X (gfx950).
+ *
+ * The MLP is Y = GeLU(X A) B.  Its first weight A[H, F] is cut into column blocks
+ * A_i[H, F_i] and its second weight B[F, H] into row blocks B_i[F_i, H], so rank i
+ * computes Z_i = GeLU(X A_i) B_i with no exchange between the two products, and
+ * the layer output is the sum of the ranks' Z_i ("大模型训练" notes, §3.1 张量并行,
+ * MLP-layer formula and its two-GPU split).  The first product widens H to 4H and
+ * the second narrows it back, with GeLU between them (QLM page, "大模型训练技术：
+ * 使用QLM提升Qwen2-7B 128k训练效率3.4倍", §2.1.2.2 part 3); GeLU is taken in its
+ * exact form p * Phi(p) = 0.5 p (1 + erf(p / sqrt 2)).
+ *
+ * Conventions for every call below
+ * --------------------------------
+ *  - Tensors are DEVICE pointers, row-major and contiguous.  bf16 tensors are raw
+ *    16-bit patterns (1 sign, 8 exponent, 7 mantissa bits; "大模型训练" notes §6.1).
+ *    Gradients and the partial outputs that ranks sum are float32.
+ *  - The caller owns every buffer.  The library allocates nothing on these paths;
+ *    its scratch space is the caller's workspace `ws` of at least the size the
+ *    matching *_workspace_bytes query returns (any contents; it is overwritten).
+ *  - Outputs are fully overwritten.  No output may overlap an input or another
+ *    output (TPMLP_ERR_ALIAS).
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  A call
+ *    validates its arguments, enqueues its kernels on `stream` and returns; it
+ *    does not synchronise.  Argument errors are reported before any HIP call is
+ *    made and nothing is enqueued then.
+ *  - M (token rows), H (hidden size) and F_i (the rank's slice of the intermediate
+ *    size) must be positive multiples of 8 and at most 2^24; pointers must be
+ *    16-byte aligned.  Sizes need not be multiples of any tile size.
+ *  - Only gfx950 devices are supported (TPMLP_ERR_UNSUPPORTED otherwise).
+ *  - All entry points are thread-safe; calls that share a workspace must not
+ *    overlap in time.
+ */
+#ifndef TPMLP_H_
+#define TPMLP_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TPMLP_ABI_VERSION 1
+#define TPMLP_MAX_SHARDS 64
+
+typedef uint16_t tpmlp_bf16; /* raw bf16 bits */
+
+typedef enum {
+  TPMLP_OK = 0,
+  TPMLP_ERR_NULL = 1,        /* a required pointer is NULL */
+  TPMLP_ERR_SHAPE = 2,       /* M, H or F_i not a positive multiple of 8, or above 2^24 */
+  TPMLP_ERR_ALIGN = 3,       /* a pointer is not 16-byte aligned */
+  TPMLP_ERR_WORKSPACE = 4,   /* ws_bytes is below the workspace query's result */
+  TPMLP_ERR_SHARDS = 5,      /* t outside 1..TPMLP_MAX_SHARDS */
+  TPMLP_ERR_HIP = 6,         /* a HIP runtime call or a kernel launch failed */
+  TPMLP_ERR_UNSUPPORTED = 7, /* the current device is not gfx950 */
+  TPMLP_ERR_ALIAS = 8        /* an output overlaps an input or another output */
+} tpmlp_status;
+
+/* TPMLP_ABI_VERSION of the built library. */
+int tpmlp_abi_version(void);
+
+/* Static English name of a status code; never NULL. */
+const char* tpmlp_status_str(int status);
+
+/* Detail of the last error on the calling thread (which argument, which HIP
+ * error); "" if the last call succeeded.  Valid until the thread's next call. */
+const char* tpmlp_last_error(void);
+
+/* ------------------------------------------------------------------------ */
+/* One rank's shard                                                          */
+/* ------------------------------------------------------------------------ */
+
+/* Workspace bytes that tpmlp_fwd needs for (M, H, F_i); 0 if the shape is invalid. */
+size_t tpmlp_fwd_workspace_bytes(int64_t M, int64_t H, int64_t F_i);
+
+/* Rank i's forward (the column-parallel GEMM, GeLU, the row-parallel GEMM):
+ *   P_i = X A_i            X[M,H] bf16, A_i[H,F_i] bf16, float32 accumulation
+ *   G_i = GeLU(P_i)        kept in the workspace as bf16 (round to nearest even)
+ *   Z_i = G_i B_i          B_i[F_i,H] bf16 -> Z_i[M,H] float32 (the rank's partial)
+ * P_save (nullable): if given, receives P_i[M,F_i] in bf16 (round to nearest even),
+ * for a backward that keeps the pre-activation instead of recomputing it.
+ * Sources: "大模型训练" notes §3.1; QLM page §2.1.2.2 part 3. */
+tpmlp_status tpmlp_fwd(const tpmlp_bf16* X, const tpmlp_bf16* A_i, const tpmlp_bf16* B_i,
+                       float* Z_i, tpmlp_bf16* P_save,
+                       int64_t M, int64_t H, int64_t F_i,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes that tpmlp_bwd needs; `recompute` is 1 when P_saved will be
+ * NULL.  0 if the shape is invalid. */
+size_t tpmlp_bwd_workspace_bytes(int64_t M, int64_t H, int64_t F_i, int recompute);
+
+/* Rank i's backward, given the output gradient dZ[M,H] (bf16), which every rank
+ * holds whole because the row-parallel layer's forward sum has an identity
+ * backward (QLM page §2.1.2.2 parts 1-2, operators read as the f/g pair):
+ *   P_i   = P_saved, or X A_i recomputed when P_saved is NULL (products need their
+ *           inputs for their gradients: asorrir.com survey, part 二, Checkpoint 技术;
+ *           recompute: "大模型训练" notes §7)
+ *   dG_i  = dZ B_i^T
+ *   dP_i  = dG_i * GeLU'(P_i), GeLU'(p) = Phi(p) + p phi(p)   (bf16 in the workspace)
+ *   dB_i  = GeLU(P_i)^T dZ     -> dB_i[F_i,H] float32
+ *   dA_i  = X^T dP_i           -> dA_i[H,F_i] float32
+ *   dX_i  = dP_i A_i^T         -> dX_i[M,H] float32, this rank's partial of dX
+ * P_saved is bf16 [M,F_i] as written by tpmlp_fwd's P_save. */
+tpmlp_status tpmlp_bwd(const tpmlp_bf16* dZ, const tpmlp_bf16* X, const tpmlp_bf16* A_i,
+                       const tpmlp_bf16* B_i, const tpmlp_bf16* P_saved,
+                       float* dX_i, float* dA_i, float* dB_i,
+                       int64_t M, int64_t H, int64_t F_i,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* The t-shard driver: all t ranks' shards run one after another on one GPU and */
+/* their partials are summed locally in rank order 0..t-1, in float32.  The sum */
+/* stands in for the all-reduce of Z (forward) and of dX (backward).           */
+/* ------------------------------------------------------------------------ */
+
+/* Workspace bytes for tpmlp_tp_fwd and tpmlp_tp_bwd (either backward mode) with
+ * t shards: the largest per-shard workspace plus room for t float32 partials
+ * [M,H].  0 if the arguments are invalid. */
+size_t tpmlp_tp_workspace_bytes(int t, int64_t M, int64_t H, int64_t F_i);
+
+/* Z = sum_i GeLU(X A_sh[i]) B_sh[i].
+ * A_sh, B_sh: host arrays of t device pointers (shard i's A_i[H,F_i], B_i[F_i,H]).
+ * P_sh (nullable host array; entries nullable): per-shard P_save.
+ * Z_sh (nullable host array; entries nullable): where shard i's partial Z_i[M,H]
+ * goes; a NULL array or entry puts it in the workspace.
+ * Z[M,H] float32: the summed output. */
+tpmlp_status tpmlp_tp_fwd(const tpmlp_bf16* X, const tpmlp_bf16* const* A_sh,
+                          const tpmlp_bf16* const* B_sh, tpmlp_bf16* const* P_sh,
+                          float* const* Z_sh, float* Z,
+                          int t, int64_t M, int64_t H, int64_t F_i,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/* Backward of all t shards, dX = sum_i dX_i.
+ * P_sh: NULL host array => every shard recomputes P_i; otherwise t device
+ * pointers written by tpmlp_tp_fwd (no NULL entries).
+ * dA_sh, dB_sh: host arrays of t device pointers (float32 weight gradients).
+ * dX_sh (nullable host array; entries nullable): per-shard partial dX_i. */
+tpmlp_status tpmlp_tp_bwd(const tpmlp_bf16* dZ, const tpmlp_bf16* X,
+                          const tpmlp_bf16* const* A_sh, const tpmlp_bf16* const* B_sh,
+                          const tpmlp_bf16* const* P_sh,
+                          float* const* dA_sh, float* const* dB_sh, float* const* dX_sh,
+                          float* dX, int t, int64_t M, int64_t H, int64_t F_i,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/* out[j] = parts[0][j] + parts[1][j] + ... + parts[t-1][j] (float32, left to right)
+ * for j < n: the local stand-in for a sum all-reduce across t ranks
+ * ("大模型训练" notes §3.1, the AllReduce of the ranks' Y_i).  `parts` is a host
+ * array of t device pointers; n must be a positive multiple of 4.  `out` may not
+ * overlap any part. */
+tpmlp_status tpmlp_shard_sum(const float* const* parts, int t, float* out, int64_t n, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Kernel timing (measurement aid; not needed to compute anything)           */
+/* ------------------------------------------------------------------------ */
+
+/* Kernel kinds that timing distinguishes. */
+typedef enum {
+  TPMLP_K_FWD_GEMM1_GELU = 0, /* P_i = X A_i, G_i = GeLU(P_i) */
+  TPMLP_K_FWD_GEMM2 = 1,      /* Z_i = G_i B_i */
+  TPMLP_K_BWD_RECOMPUTE = 2,  /* P_i = X A_i recomputed */
+  TPMLP_K_BWD_DGELU = 3,      /* dG_i = dZ B_i^T, dP_i, G_i */
+  TPMLP_K_BWD_DB = 4,         /* dB_i = G_i^T dZ */
+  TPMLP_K_BWD_DA = 5,         /* dA_i = X^T dP_i */
+  TPMLP_K_BWD_DX = 6,         /* dX_i = dP_i A_i^T */
+  TPMLP_K_SPLITK_REDUCE = 7,  /* sum of split-K float32 partials */
+  TPMLP_K_SHARD_SUM = 8,      /* tpmlp_shard_sum and the drivers' partial sums */
+  TPMLP_K_COUNT = 9
+} tpmlp_kernel_kind;
+
+/* Static name of a kernel kind ("?" if out of range). */
+const char* tpmlp_kernel_name(int kind);
+
+/* Start recording a HIP event pair around every kernel the library enqueues on
+ * the calling thread, on the stream it is enqueued on, for up to `capacity`
+ * launches (events are created here, outside any timed region).  Restarting
+ * discards earlier records. */
+tpmlp_status tpmlp_timing_begin(int capacity);
+
+/* Stop recording, wait for the recorded events and add up, per kernel kind, the
+ * launches (`counts[kind]`) and their total milliseconds (`total_ms[kind]`).
+ * Both arrays have TPMLP_K_COUNT entries.  Records beyond `capacity` are dropped
+ * and counted in *dropped (nullable). */
+tpmlp_status tpmlp_timing_end(int* counts, double* total_ms, int* dropped);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TPMLP_H_ */

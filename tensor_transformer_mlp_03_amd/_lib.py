@@ -1,0 +1,228 @@
+"""ctypes binding of libtpmlp (include/tpmlp.h).
+
+Argument marshalling only: every step of the MLP runs in the library's HIP
+kernels.  Functions keep the C names; tensors are torch tensors on the GPU
+(bf16 data as ``torch.bfloat16`` or ``torch.uint16``/``torch.int16`` bits,
+float32 outputs as ``torch.float32``); sizes come from the tensors' shapes.
+A status other than TPMLP_OK raises :class:`TpmlpError`.
+
+If the shared library has not been built, loading fails loudly; there is no
+fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional, Sequence
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libtpmlp.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "tpmlp.h")
+
+STATUS = {
+    0: "TPMLP_OK", 1: "TPMLP_ERR_NULL", 2: "TPMLP_ERR_SHAPE", 3: "TPMLP_ERR_ALIGN",
+    4: "TPMLP_ERR_WORKSPACE", 5: "TPMLP_ERR_SHARDS", 6: "TPMLP_ERR_HIP",
+    7: "TPMLP_ERR_UNSUPPORTED", 8: "TPMLP_ERR_ALIAS",
+}
+KERNEL_COUNT = 9
+MAX_SHARDS = 64
+
+
+class TpmlpError(RuntimeError):
+    def __init__(self, status: int, func: str, detail: str):
+        self.status = status
+        super().__init__(f"{func}: {STATUS.get(status, status)} ({detail})")
+
+
+_lib = None
+
+_vp, _sz, _i64, _int = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int64, ctypes.c_int
+_PP = ctypes.POINTER(ctypes.c_void_p)
+
+_SIGS = {
+    "tpmlp_abi_version": ([], _int),
+    "tpmlp_status_str": ([_int], ctypes.c_char_p),
+    "tpmlp_last_error": ([], ctypes.c_char_p),
+    "tpmlp_kernel_name": ([_int], ctypes.c_char_p),
+    "tpmlp_fwd_workspace_bytes": ([_i64, _i64, _i64], _sz),
+    "tpmlp_bwd_workspace_bytes": ([_i64, _i64, _i64, _int], _sz),
+    "tpmlp_tp_workspace_bytes": ([_int, _i64, _i64, _i64], _sz),
+    "tpmlp_fwd": ([_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _sz, _vp], _int),
+    "tpmlp_bwd": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _sz, _vp], _int),
+    "tpmlp_tp_fwd": ([_vp, _PP, _PP, _PP, _PP, _vp, _int, _i64, _i64, _i64, _vp, _sz, _vp], _int),
+    "tpmlp_tp_bwd": ([_vp, _vp, _PP, _PP, _PP, _PP, _PP, _PP, _vp, _int, _i64, _i64, _i64, _vp, _sz, _vp], _int),
+    "tpmlp_shard_sum": ([_PP, _int, _vp, _i64, _vp], _int),
+    "tpmlp_timing_begin": ([_int], _int),
+    "tpmlp_timing_end": ([ctypes.POINTER(_int), ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_int)], _int),
+}
+
+
+def header_functions() -> list:
+    """Names of the functions include/tpmlp.h declares."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tpmlp_\w+)\s*\(", text)))
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (loads it on first use).  Raises if it is not built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is not built; run `python -m tensor_transformer_mlp_03_amd.build` "
+                "(hipcc for gfx950). There is no fallback path.")
+        try:  # share torch's HIP runtime (same soname) when torch is present
+            import torch  # noqa: F401
+        except ImportError:
+            pass
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+    return _lib
+
+
+def _check(status: int, func: str):
+    if status != 0:
+        raise TpmlpError(status, func, lib().tpmlp_last_error().decode())
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _ptr_array(items: Optional[Sequence], n: int):
+    if items is None:
+        return None
+    arr = (ctypes.c_void_p * n)()
+    for i in range(n):
+        arr[i] = _ptr(items[i]) if items[i] is not None else None
+    return ctypes.cast(arr, _PP)
+
+
+def _bf16(t, name):
+    import torch
+    if t.dtype not in (torch.bfloat16, torch.uint16, torch.int16):
+        raise TypeError(f"{name} must hold bf16 bits (bfloat16/uint16/int16), got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _f32(t, name):
+    import torch
+    if t.dtype != torch.float32 or not t.is_contiguous():
+        raise TypeError(f"{name} must be a contiguous float32 tensor")
+    return t
+
+
+# --- queries ------------------------------------------------------------------
+def tpmlp_abi_version() -> int:
+    return lib().tpmlp_abi_version()
+
+
+def tpmlp_status_str(status: int) -> str:
+    return lib().tpmlp_status_str(status).decode()
+
+
+def tpmlp_kernel_name(kind: int) -> str:
+    return lib().tpmlp_kernel_name(kind).decode()
+
+
+def tpmlp_fwd_workspace_bytes(M: int, H: int, F_i: int) -> int:
+    return lib().tpmlp_fwd_workspace_bytes(M, H, F_i)
+
+
+def tpmlp_bwd_workspace_bytes(M: int, H: int, F_i: int, recompute: bool) -> int:
+    return lib().tpmlp_bwd_workspace_bytes(M, H, F_i, int(bool(recompute)))
+
+
+def tpmlp_tp_workspace_bytes(t: int, M: int, H: int, F_i: int) -> int:
+    return lib().tpmlp_tp_workspace_bytes(t, M, H, F_i)
+
+
+# --- compute ------------------------------------------------------------------
+def tpmlp_fwd(X, A_i, B_i, Z_i, P_save, ws, stream=None):
+    """Rank i's forward; shapes X[M,H], A_i[H,F_i], B_i[F_i,H], Z_i[M,H] float32."""
+    M, H = X.shape
+    F = A_i.shape[1]
+    _bf16(X, "X"), _bf16(A_i, "A_i"), _bf16(B_i, "B_i"), _f32(Z_i, "Z_i")
+    if P_save is not None:
+        _bf16(P_save, "P_save")
+    st = lib().tpmlp_fwd(_ptr(X), _ptr(A_i), _ptr(B_i), _ptr(Z_i), _ptr(P_save), M, H, F,
+                         _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "tpmlp_fwd")
+
+
+def tpmlp_bwd(dZ, X, A_i, B_i, P_saved, dX_i, dA_i, dB_i, ws, stream=None):
+    """Rank i's backward; P_saved None recomputes the pre-activation."""
+    M, H = X.shape
+    F = A_i.shape[1]
+    for t, n in ((dZ, "dZ"), (X, "X"), (A_i, "A_i"), (B_i, "B_i")):
+        _bf16(t, n)
+    for t, n in ((dX_i, "dX_i"), (dA_i, "dA_i"), (dB_i, "dB_i")):
+        _f32(t, n)
+    if P_saved is not None:
+        _bf16(P_saved, "P_saved")
+    st = lib().tpmlp_bwd(_ptr(dZ), _ptr(X), _ptr(A_i), _ptr(B_i), _ptr(P_saved), _ptr(dX_i), _ptr(dA_i),
+                         _ptr(dB_i), M, H, F, _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "tpmlp_bwd")
+
+
+def tpmlp_tp_fwd(X, A_sh, B_sh, P_sh, Z_sh, Z, ws, stream=None):
+    """All t shards' forward, partials summed into Z[M,H] float32."""
+    t = len(A_sh)
+    M, H = X.shape
+    F = A_sh[0].shape[1]
+    st = lib().tpmlp_tp_fwd(_ptr(X), _ptr_array(A_sh, t), _ptr_array(B_sh, t), _ptr_array(P_sh, t),
+                            _ptr_array(Z_sh, t), _ptr(Z), t, M, H, F, _ptr(ws),
+                            ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "tpmlp_tp_fwd")
+
+
+def tpmlp_tp_bwd(dZ, X, A_sh, B_sh, P_sh, dA_sh, dB_sh, dX_sh, dX, ws, stream=None):
+    """All t shards' backward, dX = sum of the shards' partials."""
+    t = len(A_sh)
+    M, H = X.shape
+    F = A_sh[0].shape[1]
+    st = lib().tpmlp_tp_bwd(_ptr(dZ), _ptr(X), _ptr_array(A_sh, t), _ptr_array(B_sh, t), _ptr_array(P_sh, t),
+                            _ptr_array(dA_sh, t), _ptr_array(dB_sh, t), _ptr_array(dX_sh, t), _ptr(dX), t, M,
+                            H, F, _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "tpmlp_tp_bwd")
+
+
+def tpmlp_shard_sum(parts, out, stream=None):
+    """out = parts[0] + ... + parts[t-1] (float32, in order)."""
+    t = len(parts)
+    st = lib().tpmlp_shard_sum(_ptr_array(parts, t), t, _ptr(out), out.numel(), _stream(stream))
+    _check(st, "tpmlp_shard_sum")
+
+
+def tpmlp_timing_begin(capacity: int):
+    _check(lib().tpmlp_timing_begin(capacity), "tpmlp_timing_begin")
+
+
+def tpmlp_timing_end():
+    """Returns ({kernel name: (launches, total ms)}, dropped)."""
+    counts = (ctypes.c_int * KERNEL_COUNT)()
+    total = (ctypes.c_double * KERNEL_COUNT)()
+    dropped = ctypes.c_int(0)
+    _check(lib().tpmlp_timing_end(counts, total, ctypes.byref(dropped)), "tpmlp_timing_end")
+    return {tpmlp_kernel_name(k): (counts[k], total[k]) for k in range(KERNEL_COUNT)}, dropped.value

@@ -1,0 +1,57 @@
+// Internal declarations shared by the library's host and kernel sources.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tpmlp {
+
+// How an operand sits in memory, seen from the GEMM C[m,n] = sum_k A[m,k] B[k,n].
+//   KC: K is the contiguous dimension (A stored [M][ld], B stored [N][ld]).
+//   MC: the other dimension is contiguous (A stored [K][ld] with M contiguous,
+//       B stored [K][ld] with N contiguous).
+enum Layout : int { KC = 0, MC = 1 };
+
+// What the epilogue does with the float32 accumulator of C[m,n].
+enum Epi : int {
+  EPI_F32 = 0,      // out_f32[m,n] = acc (split-K: slice z writes its own partial)
+  EPI_GELU = 1,     // out_bf16[m,n] = GeLU(acc); out2_bf16[m,n] = acc if out2 != null
+  EPI_BF16 = 2,     // out_bf16[m,n] = acc
+  EPI_DGELU = 3,    // p = aux_bf16[m,n]; out_bf16 = acc * GeLU'(p); out2_bf16 = GeLU(p)
+};
+
+struct GemmArgs {
+  const uint16_t* a;  // A operand base (bf16 bits)
+  const uint16_t* b;  // B operand base
+  int64_t lda, ldb;   // leading dimensions in elements
+  int M, N, K;        // problem size
+  int k_split;        // K elements per split-K slice (multiple of the K tile); K if none
+  void* out;          // float* (EPI_F32) or uint16_t* (bf16 epilogues)
+  uint16_t* out2;     // second bf16 output or null
+  const uint16_t* aux;  // EPI_DGELU's pre-activation input
+  int64_t ldo;        // leading dimension of out, out2 and aux
+  int64_t split_stride;  // elements between split-K partial outputs
+  int tiles_m, tiles_n;  // output tiles along M and N
+};
+
+// Tile shapes the library instantiates.
+enum TileCfg : int {
+  TILE_256x256 = 0,  // 8 waves, 2 x 4, wave tile 128 x 64
+  TILE_128x128 = 1,  // 4 waves, 2 x 2, wave tile 64 x 64
+  TILE_COUNT = 2,
+};
+
+// Launches C = A B with the given layouts and epilogue on `stream`.
+// Returns the launch error (hipSuccess on success).  Shapes must already be valid.
+hipError_t launch_gemm(TileCfg tile, Layout la, Layout lb, Epi epi, const GemmArgs& args,
+                       int splits, hipStream_t stream);
+
+// out[j] = sum over i < n_parts of parts[i][j], left to right, j < n (n % 4 == 0).
+hipError_t launch_sum(const float* const* parts, int n_parts, float* out, int64_t n,
+                      hipStream_t stream);
+
+int tile_bm(TileCfg t);
+int tile_bn(TileCfg t);
+constexpr int TILE_BK = 64;
+
+}  // namespace tpmlp

@@ -1,0 +1,582 @@
+// libtpmlp host side: the C ABI of include/tpmlp.h.
+//
+// Argument checking (pointers, shapes, alignment, workspace size, overlaps)
+// happens before any HIP call, so that every error path can be exercised on a
+// machine without a GPU.  Then the device is checked to be gfx950 and the
+// kernels are enqueued on the caller's stream.
+//
+// Rank i's forward is two launches (the column-parallel GEMM with the GeLU
+// epilogue, the row-parallel GEMM writing the float32 partial); its backward is
+// four or five (optional recompute of the pre-activation, the dGeLU GEMM, the
+// two weight-gradient GEMMs, the input-gradient GEMM), plus split-K reductions
+// where an output has too few tiles to fill the chip.  The t-shard drivers run
+// the shards one after another and add the partials in rank order, standing in
+// for the all-reduces of the row-parallel output (forward) and of the
+// column-parallel input gradient (backward) ("大模型训练" notes §3.1; QLM page
+// §2.1.2.2 parts 1-3).
+
+#include "../../include/tpmlp.h"
+#include "common.h"
+
+#include <algorithm>
+#include <mutex>
+#include <string>
+#include <vector>
+
+namespace tpmlp {
+namespace {
+
+constexpr int64_t MAX_DIM = int64_t(1) << 24;
+constexpr int NUM_CU = 256;  // MI355X compute units, used to size split-K
+constexpr size_t WS_ALIGN = 256;
+
+thread_local std::string g_last_error;
+
+tpmlp_status fail(tpmlp_status s, const std::string& what) {
+  g_last_error = what;
+  return s;
+}
+
+size_t align_up(size_t x) { return (x + WS_ALIGN - 1) / WS_ALIGN * WS_ALIGN; }
+
+bool shape_ok(int64_t v) { return v > 0 && v <= MAX_DIM && (v % 8) == 0; }
+
+// ---------------------------------------------------------------------------
+// Launch plan: tile shape and split-K count of each GEMM, workspace layout.
+// Depends on shapes only, so workspace queries need no device.
+// ---------------------------------------------------------------------------
+struct GemmPlan {
+  TileCfg tile;
+  int splits;
+  int k_split;
+};
+
+int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+TileCfg choose_tile(int64_t M, int64_t N) {
+  const int64_t big = (int64_t)ceil_div(M, 256) * ceil_div(N, 256);
+  return big >= NUM_CU ? TILE_256x256 : TILE_128x128;
+}
+
+// Split K when the output has fewer tiles than the chip has workgroup slots, as
+// long as every slice keeps at least 1024 of K.  Picks the split count whose last
+// wave of workgroups is fullest.
+GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool allow_split) {
+  GemmPlan p;
+  p.tile = choose_tile(M, N);
+  const int slots = NUM_CU * (p.tile == TILE_256x256 ? 1 : 2);
+  const int64_t tiles = (int64_t)ceil_div(M, tile_bm(p.tile)) * ceil_div(N, tile_bn(p.tile));
+  int best = 1;
+  if (allow_split && tiles < slots) {
+    double best_eff = 0.0;
+    for (int s = 1; s <= 16; ++s) {
+      if (s > 1 && K / s < 1024) break;
+      const double waves = double(tiles * s) / slots;
+      const double eff = waves / double(ceil_div(tiles * s, slots)) * (waves < 1.0 ? waves : 1.0);
+      if (eff > best_eff + 1e-9) {
+        best_eff = eff;
+        best = s;
+      }
+    }
+  }
+  const int64_t per = ((K + best - 1) / best + TILE_BK - 1) / TILE_BK * TILE_BK;
+  p.k_split = (int)per;
+  p.splits = ceil_div(K, per);
+  return p;
+}
+
+struct FwdPlan {
+  GemmPlan g1, g2;
+  size_t off_G, off_part, total;
+};
+
+FwdPlan plan_fwd(int64_t M, int64_t H, int64_t F) {
+  FwdPlan p;
+  p.g1 = plan_gemm(M, F, H, false);
+  p.g2 = plan_gemm(M, H, F, true);
+  p.off_G = 0;
+  p.off_part = align_up(size_t(M) * F * 2);
+  const size_t part = p.g2.splits > 1 ? size_t(p.g2.splits) * M * H * 4 : 0;
+  p.total = p.off_part + align_up(part);
+  return p;
+}
+
+struct BwdPlan {
+  GemmPlan g0, g1, gdb, gda, gdx;
+  size_t off_P, off_G, off_dP, off_part, total;
+};
+
+BwdPlan plan_bwd(int64_t M, int64_t H, int64_t F, bool recompute) {
+  BwdPlan p;
+  p.g0 = plan_gemm(M, F, H, false);
+  p.g1 = plan_gemm(M, F, H, false);
+  p.gdb = plan_gemm(F, H, M, true);
+  p.gda = plan_gemm(H, F, M, true);
+  p.gdx = plan_gemm(M, H, F, true);
+  const size_t mf = align_up(size_t(M) * F * 2);
+  p.off_P = 0;
+  p.off_G = recompute ? mf : 0;
+  p.off_dP = p.off_G + mf;
+  p.off_part = p.off_dP + mf;
+  size_t part = 0;
+  if (p.gdb.splits > 1) part = std::max(part, size_t(p.gdb.splits) * F * H * 4);
+  if (p.gda.splits > 1) part = std::max(part, size_t(p.gda.splits) * H * F * 4);
+  if (p.gdx.splits > 1) part = std::max(part, size_t(p.gdx.splits) * M * H * 4);
+  p.total = p.off_part + align_up(part);
+  return p;
+}
+
+// Workspace of one shard inside the t-shard drivers: fits the forward and both
+// backward modes; the drivers' partial buffers follow it.
+size_t shard_ws_bytes(int64_t M, int64_t H, int64_t F) {
+  return align_up(std::max(plan_fwd(M, H, F).total, plan_bwd(M, H, F, true).total));
+}
+
+// ---------------------------------------------------------------------------
+// Device check (gfx950 only), cached per device.
+// ---------------------------------------------------------------------------
+std::mutex g_dev_mu;
+std::vector<int> g_dev_ok;  // -1 unknown, 0 no, 1 yes
+
+tpmlp_status check_device() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(TPMLP_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  if ((int)g_dev_ok.size() <= dev) g_dev_ok.resize(dev + 1, -1);
+  if (g_dev_ok[dev] < 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess)
+      return fail(TPMLP_ERR_HIP, std::string("hipGetDeviceProperties: ") + hipGetErrorString(e));
+    g_dev_ok[dev] = std::string(prop.gcnArchName).rfind("gfx950", 0) == 0 ? 1 : 0;
+    if (!g_dev_ok[dev]) {
+      g_last_error = std::string("device is ") + prop.gcnArchName + ", not gfx950";
+    }
+  }
+  if (!g_dev_ok[dev]) return fail(TPMLP_ERR_UNSUPPORTED, "current device is not gfx950");
+  return TPMLP_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Kernel timing: an event pair around each launch while enabled.
+// ---------------------------------------------------------------------------
+struct Timing {
+  bool on = false;
+  int cap = 0, n = 0, dropped = 0;
+  std::vector<hipEvent_t> ev;
+  std::vector<int> kind;
+  ~Timing() {
+    for (hipEvent_t e : ev) (void)hipEventDestroy(e);
+  }
+};
+thread_local Timing g_timing;
+
+template <class F>
+hipError_t timed(int kind, hipStream_t s, F&& launch) {
+  Timing& t = g_timing;
+  if (!t.on) return launch();
+  if (t.n >= t.cap) {
+    ++t.dropped;
+    return launch();
+  }
+  hipError_t e = hipEventRecord(t.ev[2 * t.n], s);
+  if (e != hipSuccess) return e;
+  e = launch();
+  if (e != hipSuccess) return e;
+  e = hipEventRecord(t.ev[2 * t.n + 1], s);
+  if (e != hipSuccess) return e;
+  t.kind[t.n++] = kind;
+  return hipSuccess;
+}
+
+// ---------------------------------------------------------------------------
+// Argument checks
+// ---------------------------------------------------------------------------
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+struct Range {
+  const void* p;
+  size_t bytes;
+  const char* name;
+};
+
+bool overlap(const Range& a, const Range& b) {
+  if (!a.p || !b.p || !a.bytes || !b.bytes) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+  return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+// Each output must be disjoint from every other range.
+tpmlp_status check_alias(const std::vector<Range>& outs, const std::vector<Range>& ins) {
+  for (size_t i = 0; i < outs.size(); ++i) {
+    for (size_t j = i + 1; j < outs.size(); ++j)
+      if (overlap(outs[i], outs[j]))
+        return fail(TPMLP_ERR_ALIAS, std::string(outs[i].name) + " overlaps " + outs[j].name);
+    for (const Range& r : ins)
+      if (overlap(outs[i], r)) return fail(TPMLP_ERR_ALIAS, std::string(outs[i].name) + " overlaps " + r.name);
+  }
+  return TPMLP_OK;
+}
+
+tpmlp_status check_shape(int64_t M, int64_t H, int64_t F) {
+  if (!shape_ok(M) || !shape_ok(H) || !shape_ok(F))
+    return fail(TPMLP_ERR_SHAPE, "M, H and F_i must be positive multiples of 8, at most 2^24");
+  return TPMLP_OK;
+}
+
+tpmlp_status check_ptrs(std::initializer_list<std::pair<const void*, const char*>> ptrs) {
+  for (auto& p : ptrs)
+    if (!p.first) return fail(TPMLP_ERR_NULL, std::string(p.second) + " is NULL");
+  for (auto& p : ptrs)
+    if (!aligned16(p.first)) return fail(TPMLP_ERR_ALIGN, std::string(p.second) + " is not 16-byte aligned");
+  return TPMLP_OK;
+}
+
+tpmlp_status hip_fail(hipError_t e, const char* what) {
+  return fail(TPMLP_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+// ---------------------------------------------------------------------------
+// GEMM launch helpers
+// ---------------------------------------------------------------------------
+GemmArgs gemm_args(const void* a, int64_t lda, const void* b, int64_t ldb, int64_t M, int64_t N,
+                   int64_t K, const GemmPlan& p, void* out, int64_t ldo) {
+  GemmArgs g{};
+  g.a = static_cast<const uint16_t*>(a);
+  g.b = static_cast<const uint16_t*>(b);
+  g.lda = lda;
+  g.ldb = ldb;
+  g.M = (int)M;
+  g.N = (int)N;
+  g.K = (int)K;
+  g.k_split = p.k_split;
+  g.out = out;
+  g.ldo = ldo;
+  g.split_stride = M * N;
+  g.tiles_m = ceil_div(M, tile_bm(p.tile));
+  g.tiles_n = ceil_div(N, tile_bn(p.tile));
+  return g;
+}
+
+// float32 output GEMM; with split-K the slices go to `part` and are summed into out.
+hipError_t gemm_f32(int kind, Layout la, Layout lb, const void* a, int64_t lda, const void* b, int64_t ldb,
+                    int64_t M, int64_t N, int64_t K, const GemmPlan& p, float* out, float* part,
+                    hipStream_t s) {
+  if (p.splits == 1) {
+    GemmArgs g = gemm_args(a, lda, b, ldb, M, N, K, p, out, N);
+    return timed(kind, s, [&] { return launch_gemm(p.tile, la, lb, EPI_F32, g, 1, s); });
+  }
+  GemmArgs g = gemm_args(a, lda, b, ldb, M, N, K, p, part, N);
+  hipError_t e = timed(kind, s, [&] { return launch_gemm(p.tile, la, lb, EPI_F32, g, p.splits, s); });
+  if (e != hipSuccess) return e;
+  const float* parts[TPMLP_MAX_SHARDS];
+  for (int i = 0; i < p.splits; ++i) parts[i] = part + size_t(i) * M * N;
+  return timed(TPMLP_K_SPLITK_REDUCE, s, [&] { return launch_sum(parts, p.splits, out, M * N, s); });
+}
+
+char* ws_at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
+
+// Enqueue rank i's forward (arguments already checked).
+hipError_t enqueue_fwd(const tpmlp_bf16* X, const tpmlp_bf16* A, const tpmlp_bf16* B, float* Z,
+                       tpmlp_bf16* P_save, int64_t M, int64_t H, int64_t F, void* ws, hipStream_t s) {
+  const FwdPlan p = plan_fwd(M, H, F);
+  uint16_t* G = reinterpret_cast<uint16_t*>(ws_at(ws, p.off_G));
+  // P_i = X A_i; G_i = GeLU(P_i)        X: [M][H] (K-contig), A_i: [H][F] (N-contig)
+  GemmArgs g1 = gemm_args(X, H, A, F, M, F, H, p.g1, G, F);
+  g1.out2 = P_save;
+  hipError_t e = timed(TPMLP_K_FWD_GEMM1_GELU, s, [&] { return launch_gemm(p.g1.tile, KC, MC, EPI_GELU, g1, 1, s); });
+  if (e != hipSuccess) return e;
+  // Z_i = G_i B_i                      G_i: [M][F] (K-contig), B_i: [F][H] (N-contig)
+  return gemm_f32(TPMLP_K_FWD_GEMM2, KC, MC, G, F, B, H, M, H, F, p.g2, Z,
+                  reinterpret_cast<float*>(ws_at(ws, p.off_part)), s);
+}
+
+// Enqueue rank i's backward (arguments already checked).
+hipError_t enqueue_bwd(const tpmlp_bf16* dZ, const tpmlp_bf16* X, const tpmlp_bf16* A, const tpmlp_bf16* B,
+                       const tpmlp_bf16* P_saved, float* dX, float* dA, float* dB, int64_t M, int64_t H,
+                       int64_t F, void* ws, hipStream_t s) {
+  const bool recompute = P_saved == nullptr;
+  const BwdPlan p = plan_bwd(M, H, F, recompute);
+  uint16_t* G = reinterpret_cast<uint16_t*>(ws_at(ws, p.off_G));
+  uint16_t* dP = reinterpret_cast<uint16_t*>(ws_at(ws, p.off_dP));
+  float* part = reinterpret_cast<float*>(ws_at(ws, p.off_part));
+  const uint16_t* P = P_saved;
+  hipError_t e;
+  if (recompute) {
+    // P_i = X A_i again, kept as bf16 like a saved pre-activation
+    uint16_t* Pw = reinterpret_cast<uint16_t*>(ws_at(ws, p.off_P));
+    GemmArgs g0 = gemm_args(X, H, A, F, M, F, H, p.g0, Pw, F);
+    e = timed(TPMLP_K_BWD_RECOMPUTE, s, [&] { return launch_gemm(p.g0.tile, KC, MC, EPI_BF16, g0, 1, s); });
+    if (e != hipSuccess) return e;
+    P = Pw;
+  }
+  // dG_i = dZ B_i^T; dP_i = dG_i GeLU'(P_i); G_i = GeLU(P_i)
+  //   dZ: [M][H] (K-contig), B_i: [F][H] = [N][K] (K-contig)
+  GemmArgs g1 = gemm_args(dZ, H, B, H, M, F, H, p.g1, dP, F);
+  g1.out2 = G;
+  g1.aux = P;
+  e = timed(TPMLP_K_BWD_DGELU, s, [&] { return launch_gemm(p.g1.tile, KC, KC, EPI_DGELU, g1, 1, s); });
+  if (e != hipSuccess) return e;
+  // dB_i = G_i^T dZ    G_i: [M][F] = [K][M'] (M'-contig), dZ: [M][H] = [K][N'] (N'-contig)
+  e = gemm_f32(TPMLP_K_BWD_DB, MC, MC, G, F, dZ, H, F, H, M, p.gdb, dB, part, s);
+  if (e != hipSuccess) return e;
+  // dA_i = X^T dP_i    X: [M][H] = [K][M'], dP_i: [M][F] = [K][N']
+  e = gemm_f32(TPMLP_K_BWD_DA, MC, MC, X, H, dP, F, H, F, M, p.gda, dA, part, s);
+  if (e != hipSuccess) return e;
+  // dX_i = dP_i A_i^T  dP_i: [M][F] (K-contig), A_i: [H][F] = [N][K] (K-contig)
+  return gemm_f32(TPMLP_K_BWD_DX, KC, KC, dP, F, A, F, M, H, F, p.gdx, dX, part, s);
+}
+
+}  // namespace
+}  // namespace tpmlp
+
+using namespace tpmlp;
+
+extern "C" {
+
+int tpmlp_abi_version(void) { return TPMLP_ABI_VERSION; }
+
+const char* tpmlp_status_str(int status) {
+  switch (status) {
+    case TPMLP_OK: return "ok";
+    case TPMLP_ERR_NULL: return "null pointer";
+    case TPMLP_ERR_SHAPE: return "invalid shape";
+    case TPMLP_ERR_ALIGN: return "misaligned pointer";
+    case TPMLP_ERR_WORKSPACE: return "workspace too small";
+    case TPMLP_ERR_SHARDS: return "invalid shard count";
+    case TPMLP_ERR_HIP: return "HIP error";
+    case TPMLP_ERR_UNSUPPORTED: return "unsupported device";
+    case TPMLP_ERR_ALIAS: return "output overlaps another buffer";
+    default: return "unknown status";
+  }
+}
+
+const char* tpmlp_last_error(void) { return g_last_error.c_str(); }
+
+const char* tpmlp_kernel_name(int kind) {
+  static const char* names[TPMLP_K_COUNT] = {"fwd_gemm1_gelu", "fwd_gemm2", "bwd_recompute", "bwd_dgelu",
+                                             "bwd_dB", "bwd_dA", "bwd_dX", "splitk_reduce", "shard_sum"};
+  return (kind >= 0 && kind < TPMLP_K_COUNT) ? names[kind] : "?";
+}
+
+size_t tpmlp_fwd_workspace_bytes(int64_t M, int64_t H, int64_t F_i) {
+  if (!shape_ok(M) || !shape_ok(H) || !shape_ok(F_i)) return 0;
+  return plan_fwd(M, H, F_i).total;
+}
+
+size_t tpmlp_bwd_workspace_bytes(int64_t M, int64_t H, int64_t F_i, int recompute) {
+  if (!shape_ok(M) || !shape_ok(H) || !shape_ok(F_i)) return 0;
+  return plan_bwd(M, H, F_i, recompute != 0).total;
+}
+
+tpmlp_status tpmlp_fwd(const tpmlp_bf16* X, const tpmlp_bf16* A_i, const tpmlp_bf16* B_i, float* Z_i,
+                       tpmlp_bf16* P_save, int64_t M, int64_t H, int64_t F_i, void* ws, size_t ws_bytes,
+                       void* stream) {
+  g_last_error.clear();
+  tpmlp_status st = check_ptrs({{X, "X"}, {A_i, "A_i"}, {B_i, "B_i"}, {Z_i, "Z_i"}, {ws, "ws"}});
+  if (st) return st;
+  if (P_save && !aligned16(P_save)) return fail(TPMLP_ERR_ALIGN, "P_save is not 16-byte aligned");
+  if ((st = check_shape(M, H, F_i))) return st;
+  const size_t need = tpmlp_fwd_workspace_bytes(M, H, F_i);
+  if (ws_bytes < need) return fail(TPMLP_ERR_WORKSPACE, "ws_bytes below tpmlp_fwd_workspace_bytes");
+  const size_t mh = size_t(M) * H, hf = size_t(H) * F_i, mf = size_t(M) * F_i;
+  std::vector<Range> ins = {{X, mh * 2, "X"}, {A_i, hf * 2, "A_i"}, {B_i, hf * 2, "B_i"}};
+  std::vector<Range> outs = {{Z_i, mh * 4, "Z_i"}, {P_save, P_save ? mf * 2 : 0, "P_save"}, {ws, need, "ws"}};
+  if ((st = check_alias(outs, ins))) return st;
+  if ((st = check_device())) return st;
+  hipError_t e = enqueue_fwd(X, A_i, B_i, Z_i, P_save, M, H, F_i, ws, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TPMLP_OK : hip_fail(e, "tpmlp_fwd launch");
+}
+
+tpmlp_status tpmlp_bwd(const tpmlp_bf16* dZ, const tpmlp_bf16* X, const tpmlp_bf16* A_i, const tpmlp_bf16* B_i,
+                       const tpmlp_bf16* P_saved, float* dX_i, float* dA_i, float* dB_i, int64_t M, int64_t H,
+                       int64_t F_i, void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  tpmlp_status st = check_ptrs({{dZ, "dZ"}, {X, "X"}, {A_i, "A_i"}, {B_i, "B_i"}, {dX_i, "dX_i"},
+                                {dA_i, "dA_i"}, {dB_i, "dB_i"}, {ws, "ws"}});
+  if (st) return st;
+  if (P_saved && !aligned16(P_saved)) return fail(TPMLP_ERR_ALIGN, "P_saved is not 16-byte aligned");
+  if ((st = check_shape(M, H, F_i))) return st;
+  const size_t need = tpmlp_bwd_workspace_bytes(M, H, F_i, P_saved == nullptr);
+  if (ws_bytes < need) return fail(TPMLP_ERR_WORKSPACE, "ws_bytes below tpmlp_bwd_workspace_bytes");
+  const size_t mh = size_t(M) * H, hf = size_t(H) * F_i, mf = size_t(M) * F_i;
+  std::vector<Range> ins = {{dZ, mh * 2, "dZ"}, {X, mh * 2, "X"}, {A_i, hf * 2, "A_i"}, {B_i, hf * 2, "B_i"},
+                            {P_saved, P_saved ? mf * 2 : 0, "P_saved"}};
+  std::vector<Range> outs = {{dX_i, mh * 4, "dX_i"}, {dA_i, hf * 4, "dA_i"}, {dB_i, hf * 4, "dB_i"}, {ws, need, "ws"}};
+  if ((st = check_alias(outs, ins))) return st;
+  if ((st = check_device())) return st;
+  hipError_t e = enqueue_bwd(dZ, X, A_i, B_i, P_saved, dX_i, dA_i, dB_i, M, H, F_i, ws,
+                             static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TPMLP_OK : hip_fail(e, "tpmlp_bwd launch");
+}
+
+size_t tpmlp_tp_workspace_bytes(int t, int64_t M, int64_t H, int64_t F_i) {
+  if (t < 1 || t > TPMLP_MAX_SHARDS || !shape_ok(M) || !shape_ok(H) || !shape_ok(F_i)) return 0;
+  return shard_ws_bytes(M, H, F_i) + align_up(size_t(t) * M * H * 4);
+}
+
+tpmlp_status tpmlp_shard_sum(const float* const* parts, int t, float* out, int64_t n, void* stream) {
+  g_last_error.clear();
+  if (!parts || !out) return fail(TPMLP_ERR_NULL, "parts or out is NULL");
+  if (t < 1 || t > TPMLP_MAX_SHARDS) return fail(TPMLP_ERR_SHARDS, "t outside 1..TPMLP_MAX_SHARDS");
+  if (n <= 0 || (n % 4)) return fail(TPMLP_ERR_SHAPE, "n must be a positive multiple of 4");
+  if (!aligned16(out)) return fail(TPMLP_ERR_ALIGN, "out is not 16-byte aligned");
+  std::vector<Range> ins;
+  for (int i = 0; i < t; ++i) {
+    if (!parts[i]) return fail(TPMLP_ERR_NULL, "parts[" + std::to_string(i) + "] is NULL");
+    if (!aligned16(parts[i])) return fail(TPMLP_ERR_ALIGN, "parts[" + std::to_string(i) + "] is not 16-byte aligned");
+    ins.push_back({parts[i], size_t(n) * 4, "a part"});
+  }
+  tpmlp_status st = check_alias({{out, size_t(n) * 4, "out"}}, ins);
+  if (st) return st;
+  if ((st = check_device())) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = timed(TPMLP_K_SHARD_SUM, s, [&] { return launch_sum(parts, t, out, n, s); });
+  return e == hipSuccess ? TPMLP_OK : hip_fail(e, "tpmlp_shard_sum launch");
+}
+
+tpmlp_status tpmlp_tp_fwd(const tpmlp_bf16* X, const tpmlp_bf16* const* A_sh, const tpmlp_bf16* const* B_sh,
+                          tpmlp_bf16* const* P_sh, float* const* Z_sh, float* Z, int t, int64_t M, int64_t H,
+                          int64_t F_i, void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  if (!A_sh || !B_sh) return fail(TPMLP_ERR_NULL, "A_sh or B_sh is NULL");
+  if (t < 1 || t > TPMLP_MAX_SHARDS) return fail(TPMLP_ERR_SHARDS, "t outside 1..TPMLP_MAX_SHARDS");
+  tpmlp_status st = check_ptrs({{X, "X"}, {Z, "Z"}, {ws, "ws"}});
+  if (st) return st;
+  if ((st = check_shape(M, H, F_i))) return st;
+  const size_t need = tpmlp_tp_workspace_bytes(t, M, H, F_i);
+  if (ws_bytes < need) return fail(TPMLP_ERR_WORKSPACE, "ws_bytes below tpmlp_tp_workspace_bytes");
+  const size_t mh = size_t(M) * H, hf = size_t(H) * F_i, mf = size_t(M) * F_i;
+  std::vector<Range> ins = {{X, mh * 2, "X"}};
+  std::vector<Range> outs = {{Z, mh * 4, "Z"}, {ws, need, "ws"}};
+  for (int i = 0; i < t; ++i) {
+    if (!A_sh[i] || !B_sh[i]) return fail(TPMLP_ERR_NULL, "A_sh[" + std::to_string(i) + "] or B_sh[i] is NULL");
+    if (!aligned16(A_sh[i]) || !aligned16(B_sh[i])) return fail(TPMLP_ERR_ALIGN, "a weight shard is not 16-byte aligned");
+    ins.push_back({A_sh[i], hf * 2, "A_sh[i]"});
+    ins.push_back({B_sh[i], hf * 2, "B_sh[i]"});
+    if (P_sh && P_sh[i]) {
+      if (!aligned16(P_sh[i])) return fail(TPMLP_ERR_ALIGN, "P_sh[i] is not 16-byte aligned");
+      outs.push_back({P_sh[i], mf * 2, "P_sh[i]"});
+    }
+    if (Z_sh && Z_sh[i]) {
+      if (!aligned16(Z_sh[i])) return fail(TPMLP_ERR_ALIGN, "Z_sh[i] is not 16-byte aligned");
+      outs.push_back({Z_sh[i], mh * 4, "Z_sh[i]"});
+    }
+  }
+  if ((st = check_alias(outs, ins))) return st;
+  if ((st = check_device())) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* partials = reinterpret_cast<float*>(ws_at(ws, shard_ws_bytes(M, H, F_i)));
+  const bool direct = (t == 1) && !(Z_sh && Z_sh[0]);
+  const float* parts[TPMLP_MAX_SHARDS];
+  for (int i = 0; i < t; ++i) {
+    float* Zi = direct ? Z : (Z_sh && Z_sh[i]) ? Z_sh[i] : partials + size_t(i) * mh;
+    parts[i] = Zi;
+    hipError_t e = enqueue_fwd(X, A_sh[i], B_sh[i], Zi, P_sh ? P_sh[i] : nullptr, M, H, F_i, ws, s);
+    if (e != hipSuccess) return hip_fail(e, "tpmlp_tp_fwd launch");
+  }
+  if (!direct) {
+    hipError_t e = timed(TPMLP_K_SHARD_SUM, s, [&] { return launch_sum(parts, t, Z, int64_t(mh), s); });
+    if (e != hipSuccess) return hip_fail(e, "tpmlp_tp_fwd sum");
+  }
+  return TPMLP_OK;
+}
+
+tpmlp_status tpmlp_tp_bwd(const tpmlp_bf16* dZ, const tpmlp_bf16* X, const tpmlp_bf16* const* A_sh,
+                          const tpmlp_bf16* const* B_sh, const tpmlp_bf16* const* P_sh, float* const* dA_sh,
+                          float* const* dB_sh, float* const* dX_sh, float* dX, int t, int64_t M, int64_t H,
+                          int64_t F_i, void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  if (!A_sh || !B_sh || !dA_sh || !dB_sh) return fail(TPMLP_ERR_NULL, "a shard array is NULL");
+  if (t < 1 || t > TPMLP_MAX_SHARDS) return fail(TPMLP_ERR_SHARDS, "t outside 1..TPMLP_MAX_SHARDS");
+  tpmlp_status st = check_ptrs({{dZ, "dZ"}, {X, "X"}, {dX, "dX"}, {ws, "ws"}});
+  if (st) return st;
+  if ((st = check_shape(M, H, F_i))) return st;
+  const size_t need = tpmlp_tp_workspace_bytes(t, M, H, F_i);
+  if (ws_bytes < need) return fail(TPMLP_ERR_WORKSPACE, "ws_bytes below tpmlp_tp_workspace_bytes");
+  const size_t mh = size_t(M) * H, hf = size_t(H) * F_i, mf = size_t(M) * F_i;
+  std::vector<Range> ins = {{dZ, mh * 2, "dZ"}, {X, mh * 2, "X"}};
+  std::vector<Range> outs = {{dX, mh * 4, "dX"}, {ws, need, "ws"}};
+  for (int i = 0; i < t; ++i) {
+    const std::string idx = "[" + std::to_string(i) + "]";
+    if (!A_sh[i] || !B_sh[i] || !dA_sh[i] || !dB_sh[i]) return fail(TPMLP_ERR_NULL, "a shard pointer" + idx + " is NULL");
+    if (P_sh && !P_sh[i]) return fail(TPMLP_ERR_NULL, "P_sh" + idx + " is NULL");
+    for (const void* p : {(const void*)A_sh[i], (const void*)B_sh[i], (const void*)dA_sh[i], (const void*)dB_sh[i]})
+      if (!aligned16(p)) return fail(TPMLP_ERR_ALIGN, "a shard pointer" + idx + " is not 16-byte aligned");
+    if (P_sh && !aligned16(P_sh[i])) return fail(TPMLP_ERR_ALIGN, "P_sh" + idx + " is not 16-byte aligned");
+    ins.push_back({A_sh[i], hf * 2, "A_sh[i]"});
+    ins.push_back({B_sh[i], hf * 2, "B_sh[i]"});
+    if (P_sh) ins.push_back({P_sh[i], mf * 2, "P_sh[i]"});
+    outs.push_back({dA_sh[i], hf * 4, "dA_sh[i]"});
+    outs.push_back({dB_sh[i], hf * 4, "dB_sh[i]"});
+    if (dX_sh && dX_sh[i]) {
+      if (!aligned16(dX_sh[i])) return fail(TPMLP_ERR_ALIGN, "dX_sh" + idx + " is not 16-byte aligned");
+      outs.push_back({dX_sh[i], mh * 4, "dX_sh[i]"});
+    }
+  }
+  if ((st = check_alias(outs, ins))) return st;
+  if ((st = check_device())) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* partials = reinterpret_cast<float*>(ws_at(ws, shard_ws_bytes(M, H, F_i)));
+  const bool direct = (t == 1) && !(dX_sh && dX_sh[0]);
+  const float* parts[TPMLP_MAX_SHARDS];
+  for (int i = 0; i < t; ++i) {
+    float* dXi = direct ? dX : (dX_sh && dX_sh[i]) ? dX_sh[i] : partials + size_t(i) * mh;
+    parts[i] = dXi;
+    hipError_t e = enqueue_bwd(dZ, X, A_sh[i], B_sh[i], P_sh ? P_sh[i] : nullptr, dXi, dA_sh[i], dB_sh[i], M, H,
+                               F_i, ws, s);
+    if (e != hipSuccess) return hip_fail(e, "tpmlp_tp_bwd launch");
+  }
+  if (!direct) {
+    hipError_t e = timed(TPMLP_K_SHARD_SUM, s, [&] { return launch_sum(parts, t, dX, int64_t(mh), s); });
+    if (e != hipSuccess) return hip_fail(e, "tpmlp_tp_bwd sum");
+  }
+  return TPMLP_OK;
+}
+
+tpmlp_status tpmlp_timing_begin(int capacity) {
+  g_last_error.clear();
+  if (capacity < 1) return fail(TPMLP_ERR_SHAPE, "capacity must be positive");
+  Timing& t = g_timing;
+  for (hipEvent_t e : t.ev) (void)hipEventDestroy(e);
+  t.ev.assign(2 * size_t(capacity), nullptr);
+  t.kind.assign(capacity, 0);
+  for (auto& e : t.ev) {
+    hipError_t r = hipEventCreate(&e);
+    if (r != hipSuccess) {
+      t.on = false;
+      return hip_fail(r, "hipEventCreate");
+    }
+  }
+  t.cap = capacity;
+  t.n = 0;
+  t.dropped = 0;
+  t.on = true;
+  return TPMLP_OK;
+}
+
+tpmlp_status tpmlp_timing_end(int* counts, double* total_ms, int* dropped) {
+  g_last_error.clear();
+  if (!counts || !total_ms) return fail(TPMLP_ERR_NULL, "counts or total_ms is NULL");
+  Timing& t = g_timing;
+  for (int k = 0; k < TPMLP_K_COUNT; ++k) {
+    counts[k] = 0;
+    total_ms[k] = 0.0;
+  }
+  if (dropped) *dropped = t.dropped;
+  t.on = false;
+  for (int i = 0; i < t.n; ++i) {
+    hipError_t e = hipEventSynchronize(t.ev[2 * i + 1]);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+    float ms = 0.0f;
+    e = hipEventElapsedTime(&ms, t.ev[2 * i], t.ev[2 * i + 1]);
+    if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+    counts[t.kind[i]] += 1;
+    total_ms[t.kind[i]] += ms;
+  }
+  t.n = 0;
+  return TPMLP_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,90 @@
+"""Device-side setup of one workload for the library: uploads the seeded bf16
+inputs, allocates outputs and the workspace with torch (memory only), and calls
+the C ABI.  No arithmetic of the method happens here.
+"""
+from __future__ import annotations
+
+from typing import List, Optional
+
+import numpy as np
+
+from . import _lib as L
+from .inputs import Inputs
+
+
+def to_device(bits: Optional[np.ndarray], device="cuda"):
+    """uint16 bf16 bits -> an int16 device tensor holding the same bits."""
+    import torch
+    if bits is None:
+        return None
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(device)
+
+
+def bits_of(t) -> np.ndarray:
+    """Device int16/bf16 tensor -> uint16 numpy bits."""
+    import torch
+    return t.detach().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+class DeviceMLP:
+    """All buffers of one workload on the GPU.
+
+    ``shards``: which weight shards to place (default: those generated in
+    ``inputs``).  ``store_p``: keep the pre-activation from the forward (True) or
+    recompute it in the backward (False).  ``driver``: run the shards through the
+    t-shard driver (partials summed into Z and dX); otherwise each shard is one
+    rank's ``tpmlp_fwd`` / ``tpmlp_bwd`` call with its own outputs.
+    """
+
+    def __init__(self, inputs: Inputs, store_p: bool = True, driver: bool = True, shards=None,
+                 keep_partials: bool = False, device="cuda"):
+        import torch
+        w = inputs.workload
+        self.w, self.device, self.store_p, self.driver = w, device, store_p, driver
+        self.M, self.H, self.F = w.M, w.H, w.F_i
+        self.shards = [i for i in range(w.t) if inputs.A[i] is not None] if shards is None else list(shards)
+        if driver and len(self.shards) != w.t:
+            raise ValueError("the t-shard driver needs every shard")
+        f32 = dict(dtype=torch.float32, device=device)
+        bf = dict(dtype=torch.int16, device=device)
+        self.X = to_device(inputs.X, device)
+        self.dZ = to_device(inputs.dZ, device) if w.backward else None
+        self.A: List = [to_device(inputs.A[i], device) for i in self.shards]
+        self.B: List = [to_device(inputs.B[i], device) for i in self.shards]
+        n = len(self.shards)
+        M, H, F = self.M, self.H, self.F
+        self.P = [torch.empty((M, F), **bf) for _ in range(n)] if store_p else None
+        self.Z_sh = [torch.empty((M, H), **f32) for _ in range(n)] if (keep_partials or not driver) else None
+        self.Z = torch.empty((M, H), **f32) if driver else None
+        if w.backward:
+            self.dA = [torch.empty((H, F), **f32) for _ in range(n)]
+            self.dB = [torch.empty((F, H), **f32) for _ in range(n)]
+            self.dX_sh = [torch.empty((M, H), **f32) for _ in range(n)] if (keep_partials or not driver) else None
+            self.dX = torch.empty((M, H), **f32) if driver else None
+        if driver:
+            ws = L.tpmlp_tp_workspace_bytes(n, M, H, F)
+        else:
+            ws = max(L.tpmlp_fwd_workspace_bytes(M, H, F), L.tpmlp_bwd_workspace_bytes(M, H, F, not store_p))
+        self.ws = torch.empty(ws, dtype=torch.uint8, device=device)
+
+    def forward(self, stream=None):
+        if self.driver:
+            L.tpmlp_tp_fwd(self.X, self.A, self.B, self.P, self.Z_sh, self.Z, self.ws, stream)
+        else:
+            for j in range(len(self.shards)):
+                L.tpmlp_fwd(self.X, self.A[j], self.B[j], self.Z_sh[j], self.P[j] if self.P else None, self.ws,
+                            stream)
+
+    def backward(self, stream=None):
+        if self.driver:
+            L.tpmlp_tp_bwd(self.dZ, self.X, self.A, self.B, self.P, self.dA, self.dB, self.dX_sh, self.dX, self.ws,
+                           stream)
+        else:
+            for j in range(len(self.shards)):
+                L.tpmlp_bwd(self.dZ, self.X, self.A[j], self.B[j], self.P[j] if self.P else None, self.dX_sh[j],
+                            self.dA[j], self.dB[j], self.ws, stream)
+
+    def step(self, stream=None):
+        self.forward(stream)
+        if self.w.backward:
+            self.backward(stream)

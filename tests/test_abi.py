@@ -1,0 +1,171 @@
+"""The C-ABI library loads, exports what include/tpmlp.h declares, and rejects bad
+arguments before touching the GPU.
+
+Every call here with made-up device addresses is invalid in at least one way
+that the library checks before any HIP call, so none of them can reach a kernel.
+"""
+import ctypes
+import subprocess
+
+import pytest
+
+from tensor_transformer_mlp_03_amd import _lib as L
+
+def _gpu_visible():
+    try:
+        import torch
+        return torch.cuda.device_count() > 0
+    except Exception:
+        return False
+
+
+# Host-side validation tests.  They run where no GPU is visible, so that even a
+# validation bug could not send a made-up address to a kernel.
+pytestmark = [
+    pytest.mark.skipif(not __import__("os").path.exists(L.LIB_PATH), reason="libtpmlp.so not built"),
+    pytest.mark.skipif(_gpu_visible(), reason="made-up device addresses are only passed where no GPU is visible"),
+]
+
+OK, NULL, SHAPE, ALIGN, WS, SHARDS, HIP, UNSUP, ALIAS = range(9)
+
+
+def test_exports_every_declared_function():
+    declared = L.header_functions()
+    assert "tpmlp_fwd" in declared and "tpmlp_tp_bwd" in declared
+    out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if l.strip()}
+    missing = [f for f in declared if f not in exported]
+    assert not missing, missing
+    lib = L.lib()
+    for f in declared:
+        assert hasattr(lib, f)
+    assert set(declared) == set(L._SIGS)
+
+
+def test_version_and_strings():
+    assert L.tpmlp_abi_version() == 1
+    assert L.tpmlp_status_str(0) == "ok"
+    assert L.tpmlp_status_str(ALIAS) == "output overlaps another buffer"
+    assert L.tpmlp_status_str(99) == "unknown status"
+    assert L.tpmlp_kernel_name(0) == "fwd_gemm1_gelu"
+    assert L.tpmlp_kernel_name(99) == "?"
+
+
+def _align(x, a=256):
+    return (x + a - 1) // a * a
+
+
+def test_workspace_queries():
+    M, H, F = 4096, 1024, 4096
+    fwd = L.tpmlp_fwd_workspace_bytes(M, H, F)
+    assert fwd >= M * F * 2
+    assert L.tpmlp_bwd_workspace_bytes(M, H, F, True) >= L.tpmlp_bwd_workspace_bytes(M, H, F, False) + M * F * 2
+    assert L.tpmlp_bwd_workspace_bytes(M, H, F, False) >= 2 * M * F * 2
+    tp = L.tpmlp_tp_workspace_bytes(4, M, H, F)
+    assert tp >= 4 * M * H * 4 + L.tpmlp_bwd_workspace_bytes(M, H, F, True)
+    for bad in ((0, H, F), (M, 12, F), (M, H, -8), (1 << 25, H, F)):
+        assert L.tpmlp_fwd_workspace_bytes(*bad) == 0
+        assert L.tpmlp_bwd_workspace_bytes(*bad, 1) == 0
+    assert L.tpmlp_tp_workspace_bytes(0, M, H, F) == 0
+    assert L.tpmlp_tp_workspace_bytes(65, M, H, F) == 0
+
+
+FAKE = 1 << 40  # an address never dereferenced: every call below fails validation first
+
+
+def _p(i):
+    return FAKE + i * (1 << 34)
+
+
+def _fwd(**kw):
+    a = dict(X=_p(0), A=_p(1), B=_p(2), Z=_p(3), P=None, M=64, H=256, F=512, ws=_p(4), wsb=1 << 30)
+    a.update(kw)
+    st = L.lib().tpmlp_fwd(a["X"], a["A"], a["B"], a["Z"], a["P"], a["M"], a["H"], a["F"], a["ws"], a["wsb"], None)
+    return st, L.lib().tpmlp_last_error().decode()
+
+
+def test_fwd_argument_errors():
+    assert _fwd(X=None)[0] == NULL
+    assert _fwd(ws=None)[0] == NULL
+    assert _fwd(A=_p(1) + 2)[0] == ALIGN
+    assert _fwd(P=_p(5) + 8)[0] == ALIGN
+    for M, H, F in ((0, 256, 512), (60, 256, 512), (64, 250, 512), (64, 256, 0), (1 << 25, 256, 512)):
+        st, msg = _fwd(M=M, H=H, F=F)
+        assert st == SHAPE and "multiples of 8" in msg
+    need = L.tpmlp_fwd_workspace_bytes(64, 256, 512)
+    assert _fwd(wsb=need - 1)[0] == WS
+    # outputs overlapping inputs or each other
+    assert _fwd(Z=_p(0) + 64)[0] == ALIAS            # Z inside X
+    assert _fwd(ws=_p(3) + 1024)[0] == ALIAS         # workspace inside Z
+    assert _fwd(P=_p(2))[0] == ALIAS                 # P_save on B_i
+    st, msg = _fwd(Z=_p(1))
+    assert st == ALIAS and "Z_i" in msg
+
+
+def _bwd(**kw):
+    a = dict(dZ=_p(0), X=_p(1), A=_p(2), B=_p(3), P=None, dX=_p(4), dA=_p(5), dB=_p(6), M=64, H=256, F=512,
+             ws=_p(7), wsb=1 << 30)
+    a.update(kw)
+    return L.lib().tpmlp_bwd(a["dZ"], a["X"], a["A"], a["B"], a["P"], a["dX"], a["dA"], a["dB"], a["M"], a["H"],
+                             a["F"], a["ws"], a["wsb"], None)
+
+
+def test_bwd_argument_errors():
+    assert _bwd(dZ=None) == NULL
+    assert _bwd(dB=None) == NULL
+    assert _bwd(dA=_p(5) + 4) == ALIGN
+    assert _bwd(M=7) == SHAPE
+    # recompute needs more workspace than the stored pre-activation
+    need_rc = L.tpmlp_bwd_workspace_bytes(64, 256, 512, True)
+    need_st = L.tpmlp_bwd_workspace_bytes(64, 256, 512, False)
+    assert _bwd(wsb=need_rc - 1) == WS
+    assert _bwd(P=_p(8), wsb=need_st - 1) == WS
+    assert _bwd(dA=_p(6)) == ALIAS                   # dA on dB
+    assert _bwd(dX=_p(8), P=_p(8)) == ALIAS          # dX on P_saved
+    assert _bwd(ws=_p(1)) == ALIAS                   # workspace on X
+
+
+def _arr(ptrs):
+    arr = (ctypes.c_void_p * len(ptrs))(*ptrs)
+    return ctypes.cast(arr, L._PP)
+
+
+def test_tp_argument_errors():
+    lib = L.lib()
+    t, M, H, F = 4, 64, 256, 128
+    A = _arr([_p(10 + i) for i in range(t)])
+    B = _arr([_p(20 + i) for i in range(t)])
+    assert lib.tpmlp_tp_fwd(_p(0), None, B, None, None, _p(1), t, M, H, F, _p(2), 1 << 40, None) == NULL
+    assert lib.tpmlp_tp_fwd(_p(0), A, B, None, None, _p(1), 0, M, H, F, _p(2), 1 << 40, None) == SHARDS
+    assert lib.tpmlp_tp_fwd(_p(0), A, B, None, None, _p(1), 65, M, H, F, _p(2), 1 << 40, None) == SHARDS
+    need = L.tpmlp_tp_workspace_bytes(t, M, H, F)
+    assert lib.tpmlp_tp_fwd(_p(0), A, B, None, None, _p(1), t, M, H, F, _p(2), need - 1, None) == WS
+    Abad = _arr([_p(10), None, _p(12), _p(13)])
+    assert lib.tpmlp_tp_fwd(_p(0), Abad, B, None, None, _p(1), t, M, H, F, _p(2), need, None) == NULL
+    Bsame = _arr([_p(10)] + [_p(21 + i) for i in range(t - 1)])  # B_0 is A_0: fine, both inputs
+    Zsh = _arr([_p(30), _p(30), None, None])                         # two partials on one buffer
+    assert lib.tpmlp_tp_fwd(_p(0), A, Bsame, None, Zsh, _p(1), t, M, H, F, _p(2), need - 1, None) == WS
+    assert lib.tpmlp_tp_fwd(_p(0), A, B, None, Zsh, _p(1), t, M, H, F, _p(2), need, None) == ALIAS
+    dA = _arr([_p(40 + i) for i in range(t)])
+    dB = _arr([_p(50 + i) for i in range(t)])
+    assert lib.tpmlp_tp_bwd(_p(0), _p(3), A, B, None, dA, None, None, _p(1), t, M, H, F, _p(2), need, None) == NULL
+    Pbad = _arr([_p(60), None, _p(62), _p(63)])
+    assert lib.tpmlp_tp_bwd(_p(0), _p(3), A, B, Pbad, dA, dB, None, _p(1), t, M, H, F, _p(2), need, None) == NULL
+    dBov = _arr([_p(40)] + [_p(51 + i) for i in range(t - 1)])       # dB_0 on dA_0
+    assert lib.tpmlp_tp_bwd(_p(0), _p(3), A, B, None, dA, dBov, None, _p(1), t, M, H, F, _p(2), need, None) == ALIAS
+
+
+def test_shard_sum_argument_errors():
+    lib = L.lib()
+    parts = _arr([_p(0), _p(1)])
+    assert lib.tpmlp_shard_sum(None, 2, _p(2), 1024, None) == NULL
+    assert lib.tpmlp_shard_sum(parts, 0, _p(2), 1024, None) == SHARDS
+    assert lib.tpmlp_shard_sum(parts, 2, _p(2), 1022, None) == SHAPE
+    assert lib.tpmlp_shard_sum(parts, 2, _p(2) + 4, 1024, None) == ALIGN
+    assert lib.tpmlp_shard_sum(parts, 2, _p(1) + 16, 1024, None) == ALIAS
+
+
+def test_timing_argument_errors():
+    lib = L.lib()
+    assert lib.tpmlp_timing_begin(0) == SHAPE
+    assert lib.tpmlp_timing_end(None, None, None) == NULL

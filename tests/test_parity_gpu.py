@@ -1,0 +1,297 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Acceptance per output tensor: max|gpu - oracle| <= 1e-2 * max|oracle| + 1e-3.
+Small shapes are compared in full, with ragged tails on every dimension; the
+benchmark configurations are run in the launch configuration the benchmark
+times and compared in full where the oracle is quick, on sampled rows/columns
+(each computed from the definition) where it is not.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+from oracle import oracle as O
+from tensor_transformer_mlp_03_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from tensor_transformer_mlp_03_amd import _lib as L
+    L.lib()  # fails loudly if the library is not built
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dec(bits):
+    return O.decode_bf16(bits)
+
+
+def check(name, got, ref, ratios):
+    err = O.max_abs_err(got, ref)
+    tol = O.tolerance(ref)
+    ratios[name] = err / tol
+    assert np.all(np.isfinite(got)), f"{name}: non-finite values"
+    assert err <= tol, f"{name}: max err {err:.3e} > tol {tol:.3e}"
+
+
+def run_device(inp, store_p=True, keep_partials=True):
+    from tensor_transformer_mlp_03_amd.device import DeviceMLP
+    d = DeviceMLP(inp, store_p=store_p, driver=True, keep_partials=keep_partials)
+    d.step()
+    torch.cuda.synchronize()
+    return d
+
+
+SMALL = [
+    # (M, H, F_i, t, store_p): ragged in every dimension vs the 128/256 tiles and the 64-wide K step
+    (64, 256, 512, 2, True),
+    (200, 264, 392, 2, True),
+    (328, 136, 776, 3, False),
+    (8, 8, 8, 1, True),
+    (520, 520, 264, 2, False),
+    (1032, 1040, 1048, 1, True),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "x".join(map(str, c[:4])) + ("_store" if c[4] else "_recompute"))
+def test_small_full(case):
+    M, H, F, t, store = case
+    say(f"[parity small] M={M} H={H} F_i={F} t={t} store_p={store}")
+    w = I.custom_workload(200 + M % 97, M=M, H=H, F_i=F, t=t, w_std=0.05)
+    inp = I.make_inputs(w)
+    d = run_device(inp, store_p=store)
+    X, dZ = dec(inp.X), dec(inp.dZ)
+    A = [dec(a) for a in inp.A]
+    B = [dec(b) for b in inp.B]
+    Z, Zp = O.tp_forward(X, A, B)
+    dX, dXp, dAp, dBp = O.tp_backward(dZ, X, A, B)
+    r = {}
+    check("Z", d.Z.cpu().numpy(), Z, r)
+    check("dX", d.dX.cpu().numpy(), dX, r)
+    for i in range(t):
+        check(f"Z_{i}", d.Z_sh[i].cpu().numpy(), Zp[i], r)
+        check(f"dX_{i}", d.dX_sh[i].cpu().numpy(), dXp[i], r)
+        check(f"dA_{i}", d.dA[i].cpu().numpy(), dAp[i], r)
+        check(f"dB_{i}", d.dB[i].cpu().numpy(), dBp[i], r)
+    say("  err/tol:", {k: round(v, 3) for k, v in r.items()})
+
+
+def test_config0_forward():
+    w = I.CONFIGS[0]
+    say(f"[parity config0] {w}")
+    inp = I.make_inputs(w)
+    d = run_device(inp)
+    X = dec(inp.X)
+    A = [dec(a) for a in inp.A]
+    B = [dec(b) for b in inp.B]
+    Z, Zp = O.tp_forward(X, A, B)
+    r = {}
+    check("Z", d.Z.cpu().numpy(), Z, r)
+    for i in range(w.t):
+        check(f"Z_{i}", d.Z_sh[i].cpu().numpy(), Zp[i], r)
+    # shard-sum identity against the unsharded MLP
+    Zfull = O.mlp_forward(X, np.concatenate(A, 1), np.concatenate(B, 0))["Z"]
+    check("Z_vs_unsharded", d.Z.cpu().numpy(), Zfull, r)
+    say("  err/tol:", {k: round(v, 3) for k, v in r.items()})
+
+
+@pytest.mark.parametrize("cfg", [1, 2])
+def test_config_full(cfg):
+    w = I.CONFIGS[cfg]
+    say(f"[parity config{cfg}] {w}")
+    inp = I.make_inputs(w)
+    d = run_device(inp, store_p=not w.recompute, keep_partials=False)
+    X, dZ = dec(inp.X), dec(inp.dZ)
+    A = [dec(a) for a in inp.A]
+    B = [dec(b) for b in inp.B]
+    r = {}
+    Zsum, dXsum = None, None
+    for i in range(w.t):
+        f = O.mlp_forward(X, A[i], B[i])
+        g = O.mlp_backward(dZ, X, A[i], B[i])
+        Zsum = f["Z"] if Zsum is None else Zsum + f["Z"]
+        dXsum = g["dX"] if dXsum is None else dXsum + g["dX"]
+        check(f"dA_{i}", d.dA[i].cpu().numpy(), g["dA"], r)
+        check(f"dB_{i}", d.dB[i].cpu().numpy(), g["dB"], r)
+    check("Z", d.Z.cpu().numpy(), Zsum, r)
+    check("dX", d.dX.cpu().numpy(), dXsum, r)
+    say("  err/tol:", {k: round(v, 3) for k, v in r.items()})
+
+
+def _sample(n, k, rng, must=()):
+    idx = set(int(v) for v in must)
+    while len(idx) < min(k + len(must), n):
+        idx.add(int(rng.integers(0, n)))
+    return np.array(sorted(idx))
+
+
+@pytest.mark.parametrize("cfg", [3, 4])
+def test_config_sampled(cfg):
+    """Full-size runs; rows of Z/dX and columns of dA_i / rows of dB_i compared."""
+    w = I.CONFIGS[cfg]
+    say(f"[parity config{cfg} sampled] {w}")
+    shards = list(w.shards_timed)
+    inp = I.make_inputs(w, shards=shards)
+    from tensor_transformer_mlp_03_amd.device import DeviceMLP
+    driver = len(shards) == w.t
+    d = DeviceMLP(inp, store_p=not w.recompute, driver=driver, keep_partials=True)
+    d.step()
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(1234 + cfg)
+    rows = _sample(w.M, 24, rng, must=inp.outliers[:8])
+    X, dZ = dec(inp.X), dec(inp.dZ)
+    r = {}
+    Zs, dXs = None, None
+    for j, i in enumerate(shards):
+        A, B = dec(inp.A[i]), dec(inp.B[i])
+        z = O.forward_rows(X, A, B, rows)
+        dx = O.backward_dX_rows(dZ, X, A, B, rows)
+        Zs = z if Zs is None else Zs + z
+        dXs = dx if dXs is None else dXs + dx
+        check(f"Z_{i}[rows]", d.Z_sh[j][rows].cpu().numpy(), z, r)
+        check(f"dX_{i}[rows]", d.dX_sh[j][rows].cpu().numpy(), dx, r)
+        cols = _sample(w.F_i, 6, rng, must=[0, w.F_i - 1])
+        check(f"dA_{i}[:,cols]", d.dA[j][:, cols].cpu().numpy(), O.backward_dA_cols(dZ, X, A, B, cols), r)
+        check(f"dB_{i}[cols,:]", d.dB[j][cols, :].cpu().numpy(), O.backward_dB_rows(dZ, X, A, B, cols), r)
+        del A, B
+    if driver:
+        check("Z[rows]", d.Z[rows].cpu().numpy(), Zs, r)
+        check("dX[rows]", d.dX[rows].cpu().numpy(), dXs, r)
+    say("  err/tol:", {k: round(v, 3) for k, v in r.items()})
+
+
+@pytest.mark.parametrize("t", [2, 4, 8])
+def test_gpu_shard_sum_identity(t):
+    """The t-shard driver's sum equals one unsharded run (t = 1) of the same A, B."""
+    M, H, F = 512, 512, 2048
+    say(f"[identity gpu] t={t} M={M} H={H} F={F}")
+    w8 = I.custom_workload(300, M=M, H=H, F_i=F // 8, t=8)
+    inp = I.make_inputs(w8)
+    A = np.concatenate(inp.A, axis=1)
+    B = np.concatenate(inp.B, axis=0)
+    wt = I.custom_workload(301, M=M, H=H, F_i=F // t, t=t)
+    sh = I.Inputs(wt, inp.X, [np.ascontiguousarray(a) for a in np.split(A, t, axis=1)],
+                  [np.ascontiguousarray(b) for b in np.split(B, t, axis=0)], inp.dZ)
+    w1 = I.custom_workload(302, M=M, H=H, F_i=F, t=1)
+    one = I.Inputs(w1, inp.X, [A], [B], inp.dZ)
+    ds, d1 = run_device(sh), run_device(one)
+    ref = O.mlp_forward(dec(inp.X), dec(A), dec(B))["Z"]
+    r = {}
+    check("Z_t_vs_t1", ds.Z.cpu().numpy(), d1.Z.cpu().numpy().astype(np.float64), r)
+    check("Z_t_vs_oracle", ds.Z.cpu().numpy(), ref, r)
+    check("dX_t_vs_t1", ds.dX.cpu().numpy(), d1.dX.cpu().numpy().astype(np.float64), r)
+    # the weight gradients of the shards are the column/row blocks of the unsharded ones
+    check("dA_blocks", np.concatenate([a.cpu().numpy() for a in ds.dA], 1), d1.dA[0].cpu().numpy().astype(np.float64), r)
+    check("dB_blocks", np.concatenate([b.cpu().numpy() for b in ds.dB], 0), d1.dB[0].cpu().numpy().astype(np.float64), r)
+    say("  err/tol:", {k: round(v, 3) for k, v in r.items()})
+
+
+def test_store_equals_recompute_bitwise():
+    """Keeping the bf16 pre-activation or recomputing it gives identical bits: both
+    come from the same GEMM with the same tile and accumulation order."""
+    w = I.custom_workload(310, M=1000, H=520, F_i=776, t=2)
+    say(f"[store vs recompute] {w}")
+    inp = I.make_inputs(w)
+    a, b = run_device(inp, store_p=True), run_device(inp, store_p=False)
+    for x, y in [(a.dX, b.dX)] + list(zip(a.dA, b.dA)) + list(zip(a.dB, b.dB)):
+        assert torch.equal(x, y)
+
+
+def test_deterministic():
+    w = I.custom_workload(311, M=768, H=1024, F_i=1536, t=2)
+    say(f"[determinism] {w}")
+    inp = I.make_inputs(w)
+    a, b = run_device(inp), run_device(inp)
+    assert torch.equal(a.Z, b.Z) and torch.equal(a.dX, b.dX)
+    for x, y in list(zip(a.dA, b.dA)) + list(zip(a.dB, b.dB)):
+        assert torch.equal(x, y)
+
+
+def test_zero_input_gives_exact_zeros():
+    """X = 0: P = 0 and GeLU(0) = 0, so Z, dA and dB are exactly zero."""
+    w = I.custom_workload(312, M=264, H=256, F_i=384, t=2)
+    inp = I.make_inputs(w)
+    inp.X[:] = 0
+    d = run_device(inp)
+    assert torch.count_nonzero(d.Z) == 0
+    for x in d.dA + d.dB:
+        assert torch.count_nonzero(x) == 0
+    # dX = 1/2 dZ B^T A^T per shard, summed
+    X, dZ = dec(inp.X), dec(inp.dZ)
+    ref = sum(0.5 * (dZ @ dec(b).T) @ dec(a).T for a, b in zip(inp.A, inp.B))
+    r = {}
+    check("dX", d.dX.cpu().numpy(), ref, r)
+
+
+def test_no_writes_outside_outputs():
+    """Outputs are views into larger buffers filled with a canary; after a forward and
+    backward at a ragged shape the canary bands are untouched."""
+    from tensor_transformer_mlp_03_amd import _lib as L
+    M, H, F = 136, 264, 200
+    say(f"[canary] M={M} H={H} F_i={F}")
+    w = I.custom_workload(313, M=M, H=H, F_i=F, t=1)
+    inp = I.make_inputs(w)
+    from tensor_transformer_mlp_03_amd.device import to_device
+    X, dZ, A, B = (to_device(v) for v in (inp.X, inp.dZ, inp.A[0], inp.B[0]))
+    pad = 4096
+    canary = float("nan")
+
+    def padded(n, dtype):
+        buf = torch.full((n + 2 * pad,), canary, dtype=torch.float32, device="cuda") if dtype == torch.float32 \
+            else torch.full((n + 2 * pad,), -12345, dtype=torch.int16, device="cuda")
+        return buf, buf[pad:pad + n]
+
+    (Zb, Z), (Pb, P) = padded(M * H, torch.float32), padded(M * F, torch.int16)
+    (dXb, dX), (dAb, dA), (dBb, dB) = padded(M * H, torch.float32), padded(H * F, torch.float32), padded(F * H, torch.float32)
+    wsn = max(L.tpmlp_fwd_workspace_bytes(M, H, F), L.tpmlp_bwd_workspace_bytes(M, H, F, False))
+    wsb = torch.full((wsn + 2 * 4096,), 77, dtype=torch.uint8, device="cuda")
+    ws = wsb[4096:4096 + wsn]
+    L.tpmlp_fwd(X, A, B, Z.view(M, H), P.view(M, F), ws)
+    L.tpmlp_bwd(dZ, X, A, B, P.view(M, F), dX.view(M, H), dA.view(H, F), dB.view(F, H), ws)
+    torch.cuda.synchronize()
+    for buf, n in ((Zb, M * H), (dXb, M * H), (dAb, H * F), (dBb, F * H)):
+        assert torch.isnan(buf[:pad]).all() and torch.isnan(buf[pad + n:]).all()
+        assert torch.isfinite(buf[pad:pad + n]).all()
+    assert (Pb[:pad] == -12345).all() and (Pb[pad + M * F:] == -12345).all()
+    assert (wsb[:4096] == 77).all() and (wsb[4096 + wsn:] == 77).all()
+
+
+def test_shard_sum_kernel_exact():
+    from tensor_transformer_mlp_03_amd import _lib as L
+    rng = np.random.default_rng(5)
+    n, t = 3 * 1024 * 1024 + 12, 5
+    parts = [rng.standard_normal(n).astype(np.float32) for _ in range(t)]
+    want = parts[0].copy()
+    for p in parts[1:]:
+        want = want + p  # float32, left to right
+    dev = [torch.from_numpy(p).cuda() for p in parts]
+    out = torch.empty(n, dtype=torch.float32, device="cuda")
+    L.tpmlp_shard_sum(dev, out)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out.cpu().numpy(), want)
+
+
+def test_timing_counts_launches():
+    from tensor_transformer_mlp_03_amd import _lib as L
+    w = I.custom_workload(314, M=256, H=256, F_i=256, t=2)
+    inp = I.make_inputs(w)
+    from tensor_transformer_mlp_03_amd.device import DeviceMLP
+    d = DeviceMLP(inp, store_p=True, driver=True)
+    L.tpmlp_timing_begin(64)
+    d.step()
+    stats, dropped = L.tpmlp_timing_end()
+    assert dropped == 0
+    assert stats["fwd_gemm1_gelu"][0] == 2 and stats["fwd_gemm2"][0] == 2
+    assert stats["bwd_dgelu"][0] == 2 and stats["bwd_dX"][0] == 2 and stats["shard_sum"][0] == 2
+    assert stats["bwd_recompute"][0] == 0
+    assert all(ms >= 0 for _, ms in stats.values())
