@@ -81,6 +81,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=3, help="workload index 0-4 (default 3)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a plain copy of this many MiB through tpmlp_shard_sum with one part "
+                         "(reference dispatch for scaling HBM byte counters), then exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the tensor-parallel "
@@ -96,6 +99,15 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     L.lib()
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            L.tpmlp_shard_sum([src], dst)
+        torch.cuda.synchronize()
+        log(f"[bench] copy probe: 3 dispatches, each reads and writes {args.copy_probe_mib} MiB")
+        return
     w = I.CONFIGS[args.config]
     shards = list(w.shards_timed)
     driver = len(shards) == w.t

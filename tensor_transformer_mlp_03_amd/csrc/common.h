@@ -50,6 +50,11 @@ hipError_t launch_gemm(TileCfg tile, Layout la, Layout lb, Epi epi, const GemmAr
 hipError_t launch_sum(const float* const* parts, int n_parts, float* out, int64_t n,
                       hipStream_t stream);
 
+// Sum of `splits` float32 slices (slice i at part + i*n) finished with the
+// epilogue `epi` into out/out2 (aux: the dGeLU pre-activation), n % 4 == 0.
+hipError_t launch_splitk_epilogue(Epi epi, const float* part, int splits, int64_t n, void* out,
+                                  uint16_t* out2, const uint16_t* aux, hipStream_t stream);
+
 int tile_bm(TileCfg t);
 int tile_bn(TileCfg t);
 constexpr int TILE_BK = 64;

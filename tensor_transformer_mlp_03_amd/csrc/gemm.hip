@@ -23,20 +23,24 @@
 //  * A block computes a BM x BN output tile with 64-wide waves laid out
 //    WAVES_M x WAVES_N; each wave owns a (BM/WAVES_M) x (BN/WAVES_N) sub-tile of
 //    32 x 32 MFMA fragments held in accumulator registers.
-//  * Operand tiles go from memory straight into LDS with buffer_load ... lds
-//    (16 bytes per lane, no staging registers, no LDS write instructions) into a
-//    ring of STAGES buffers, STAGES-1 K steps ahead of the MFMAs.  A buffer
-//    descriptor returns zeros for out-of-range chunks, which handles ragged
-//    sizes without branches.  One s_waitcnt + s_barrier per K step.
-//  * LDS keeps each operand in its memory layout.  A K-contiguous tile is read
-//    with ds_read_b128 (8 consecutive k of one row per lane, the MFMA operand
-//    layout); an M/N-contiguous tile is read with two ds_read_b64_tr_b16, whose
-//    16-lane transpose delivers 4 consecutive k of one column per lane.  No
-//    operand is transposed in registers or in memory.
-//  * 16-byte chunks are XOR-swizzled inside each LDS row so that the rows one
-//    read instruction touches fall on distinct banks; the loads apply the
-//    inverse permutation on the memory side, so each DMA still writes 1 KiB of
-//    contiguous LDS.
+//  * Every operand tile sits in LDS K-contiguous ([rows][BK]), so every MFMA
+//    operand fragment is one ds_read_b128 per lane (8 consecutive k of one
+//    row).  64-bit LDS reads, the transposing ds_read_b64_tr_b16 included,
+//    move about a third of the bytes per clock that 128-bit reads do on
+//    gfx950, so no operand is read through them.
+//  * A K-contiguous operand goes from memory straight into LDS with
+//    buffer_load ... lds (16 bytes per lane, no staging registers, no LDS write
+//    instructions).  An M/N-contiguous operand is loaded into registers in 8x8
+//    blocks (8 k-rows of 8 contiguous elements), transposed in registers with
+//    v_perm_b32 and written K-contiguous with ds_write_b128.  Buffer
+//    descriptors return zeros for out-of-range chunks, which handles ragged
+//    sizes without branches.
+//  * Two LDS stages: the loads of K step kt+1 are issued right after the
+//    barrier that opens step kt, and land while step kt's MFMAs run.
+//  * 16-byte chunks are XOR-swizzled inside each 128-byte LDS row so that the
+//    rows one read instruction touches fall on distinct banks; the DMA loads
+//    apply the inverse permutation on the memory side, so each DMA still
+//    writes 1 KiB of contiguous LDS.
 //  * The MFMA takes the B fragment as its first operand, so each lane ends with
 //    4 consecutive output columns of one row: epilogues store 8- or 16-byte
 //    vectors.
@@ -44,163 +48,116 @@
 //    operand panels) run on the same XCD and its L2, then grouped 8 tiles tall.
 
 #include "common.h"
+#include "epilogue.h"
 
 namespace tpmlp {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
-typedef short i16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint16_t u16x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
-
-#ifndef TPMLP_GEMM_BK
-#define TPMLP_GEMM_BK 64
-#endif
-#ifndef TPMLP_GEMM_STAGES
-#define TPMLP_GEMM_STAGES 2
-#endif
-#ifndef TPMLP_GEMM_WAVES_M
-#define TPMLP_GEMM_WAVES_M 2
-#endif
-#ifndef TPMLP_GEMM_WAVES_N
-#define TPMLP_GEMM_WAVES_N 4
-#endif
 
 constexpr int GROUP_M = 8;
 constexpr int NUM_XCD = 8;
 constexpr uint32_t OOB = 0x7FFFFFF0u;  // voffset past num_records: the load returns 0
 
-// ds read offsets below are byte offsets inside one LDS stage.
+// Swizzle of the 16-byte chunk index inside a 128-byte row of a K-contiguous
+// tile ([rows][64]): rows r .. r+15 read at one chunk land on 16 distinct
+// (row parity, chunk) bank groups, and rows r .. r+7 on 8 distinct chunks.
+__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
 
-// Swizzle of the 16-byte chunk index inside a row of a K-contiguous tile
-// ([rows][BK]).  With 8 chunks per row: rows r .. r+15 read at one chunk land on
-// 16 distinct (row parity, chunk) bank groups.  With 4 chunks per row (64-byte
-// rows, four to a 256-byte bank window): rows r, r+4, r+8, r+12 get distinct chunks.
-template <int CHUNKS>
-__device__ __forceinline__ int swz_kc(int r) {
-  if (CHUNKS == 8) return (r ^ (r >> 3)) & 7;
-  return (r >> 2) & 3;
-}
-
-// Swizzle of the chunk index inside a row of an M/N-contiguous tile ([BK][cols],
-// one row per k).  A transpose read touches rows k..k+3 at 2-4 adjacent chunks;
-// XOR-ing chunk bits 1..3 with (k0, k1, k0) sends them to distinct banks.
-template <int CHUNKS>
-__device__ __forceinline__ int swz_mc(int k) {
-  int s = ((k & 1) << 1) | ((k & 2) << 1) | ((k & 1) << 3);
-  return s & (CHUNKS - 1);
-}
-
-__device__ __forceinline__ uint16_t f32_to_bf16(float x) {
-  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
-}
-__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
-  return __builtin_bit_cast(float, static_cast<uint32_t>(b) << 16);
-}
-
-// GeLU(p) = p Phi(p), Phi(p) = (1 + erf(p / sqrt 2)) / 2.
-__device__ __forceinline__ float phi_cdf(float p) { return 0.5f + 0.5f * erff(p * 0.70710678118654752f); }
+// Byte offset of 16-byte chunk c (k = 8c .. 8c+7) of row r in a [rows][64] tile.
+__device__ __forceinline__ int tile_off(int r, int c) { return r * 128 + ((c ^ swz(r)) << 4); }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)OOB, 0x00020000);
 }
 
-// s_waitcnt vmcnt(N) with expcnt and lgkmcnt at their maxima (waits on vmcnt only).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
-}
-
-// Wait until at most min(ahead, S) K steps' loads (LOADS each) are outstanding.
-template <int S, int LOADS>
-__device__ __forceinline__ void wait_steps(int ahead) {
-  if constexpr (S == 0) {
-    wait_vmcnt<0>();
-  } else {
-    if (ahead >= S) wait_vmcnt<S * LOADS>();
-    else wait_steps<S - 1, LOADS>(ahead);
-  }
-}
-
-// One operand's tile of one K step, loaded straight into LDS.
-//   KC: tile [R][BK],  element (r, k) at r*BK*2 + ((k/8) ^ swz_kc(r))*16 + (k%8)*2
-//   MC: tile [BK][R],  element (k, r) at k*R*2 + ((r/8) ^ swz_mc(k))*16 + (r%8)*2
-// DMA instruction i of wave w writes LDS chunks (i*NWAVES + w)*64 + lane; each
-// lane loads the memory chunk that the swizzle places there.
-template <int R, int BK, int NWAVES, int LAYOUT>
-struct Loader {
-  static constexpr int CHUNKS = R * BK / 8;
-  static constexpr int PER_WAVE = CHUNKS / 64 / NWAVES;  // DMA instructions per wave and K step
+// A K-contiguous operand's [R][64] tile of one K step, loaded straight into LDS.
+// DMA instruction i of wave w writes LDS chunks (i*NWAVES + w)*64 + lane of the
+// tile; each lane loads the memory chunk that the swizzle places there.
+template <int R, int NWAVES>
+struct DmaLoader {
+  static constexpr int CHUNKS = R * 8;
+  static constexpr int PER_WAVE = CHUNKS / 64 / NWAVES;
   static_assert(CHUNKS % (64 * NWAVES) == 0, "tile must divide evenly over the waves");
-  uint32_t off[PER_WAVE];   // byte offset of the lane's chunk from the K step's base
-  int o_lim[PER_WAVE];      // the chunk's outer index (row for KC, column for MC)
-  int k_rel[PER_WAVE];      // the chunk's k offset inside the K step
+  uint32_t off[PER_WAVE];  // byte offset of the lane's chunk from the K step's base
+  int row[PER_WAVE];       // the chunk's row inside the tile
+  int kc[PER_WAVE];        // the chunk's first k inside the K step
 
   __device__ __forceinline__ void init(int64_t ld, int wave, int lane) {
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i) {
       const int q = (i * NWAVES + wave) * 64 + lane;
-      if (LAYOUT == KC) {
-        constexpr int CPR = BK / 8;
-        const int r = q / CPR, c = (q % CPR) ^ swz_kc<CPR>(r);
-        o_lim[i] = r;
-        k_rel[i] = 8 * c;
-        off[i] = (uint32_t)(((int64_t)r * ld + 8 * c) * 2);
-      } else {
-        constexpr int CPR = R / 8;
-        const int k = q / CPR, c = (q % CPR) ^ swz_mc<CPR>(k);
-        o_lim[i] = 8 * c;
-        k_rel[i] = k;
-        off[i] = (uint32_t)(((int64_t)k * ld + 8 * c) * 2);
-      }
+      const int r = q >> 3, c = (q & 7) ^ swz(r);
+      row[i] = r;
+      kc[i] = 8 * c;
+      off[i] = (uint32_t)(((int64_t)r * ld + 8 * c) * 2);
     }
   }
 
-  // base: the operand's element (outer0, k0) for KC, (k0, outer0) for MC.
-  __device__ __forceinline__ void issue(const uint16_t* base, char* lds_stage, int outer_left, int k_left,
+  // base: element (row0, k0) of the operand.
+  __device__ __forceinline__ void issue(const uint16_t* base, char* tile, int rows_left, int k_left,
                                         int wave) const {
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(base);
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i) {
-      const bool ok = (o_lim[i] < outer_left) && (k_rel[i] < k_left);
-      char* dst = lds_stage + (i * NWAVES + wave) * 1024;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)dst, 16, ok ? off[i] : OOB, 0, 0, 0);
+      const bool ok = (row[i] < rows_left) && (kc[i] < k_left);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(tile + (i * NWAVES + wave) * 1024), 16,
+                                               ok ? off[i] : OOB, 0, 0, 0);
     }
   }
 };
 
-// MFMA operand fragment of a 32-row (or 32-column) slice at sub-step kk (16 wide):
-// lane l gets 8 consecutive k (8*(l/32) .. +7 within the sub-step) of row/column l%32.
-template <int R, int BK, int LAYOUT>
-__device__ __forceinline__ bf16x8_t read_frag(const char* lds, int o0, int kk, int lane) {
-  if (LAYOUT == KC) {
-    constexpr int CPR = BK / 8;
-    const int r = o0 + (lane & 31);
-    const int c = 2 * kk + (lane >> 5);
-    return *reinterpret_cast<const bf16x8_t*>(lds + r * BK * 2 + ((c ^ swz_kc<CPR>(r)) << 4));
-  } else {
-    // ds_read_b64_tr_b16: in each 16-lane group, result lane i element e comes
-    // from source lane 4e + i/4, slot i%4.  Source lane j therefore reads the 4
-    // elements (k0 + j/4, o .. o+3) with o = o0 + 4*(j%4): result lane i then
-    // holds column o0 + i at k0 .. k0+3.
-    constexpr int CPR = R / 8;
-    const int g = lane >> 4, j = lane & 15;
-    const int o = o0 + 16 * (g & 1) + 4 * (j & 3);
-    const int kbase = 16 * kk + 8 * (g >> 1) + (j >> 2);
-    const int c = o >> 3, half = (o & 7) * 2;
-    const int k_lo = kbase, k_hi = kbase + 4;
-    const char* p_lo = lds + k_lo * R * 2 + ((c ^ swz_mc<CPR>(k_lo)) << 4) + half;
-    const char* p_hi = lds + k_hi * R * 2 + ((c ^ swz_mc<CPR>(k_hi)) << 4) + half;
-    i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p_lo));
-    i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p_hi));
-    i16x8_t both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    return __builtin_bit_cast(bf16x8_t, both);
+// An M/N-contiguous operand's tile of one K step (64 k-rows of R contiguous
+// elements in memory), loaded by R threads as 8x8 blocks into registers and
+// written transposed into the [R][64] LDS tile.
+template <int R>
+struct RegLoader {
+  u32x4_t v[8];  // v[i]: elements (k = 8*kb + i, r = 8*mb .. 8*mb+7)
+  int mb, kb;
+  uint32_t off0, step;
+
+  __device__ __forceinline__ void init(int64_t ld, int t) {
+    mb = t % (R / 8);
+    kb = t / (R / 8);
+    off0 = (uint32_t)(((int64_t)(8 * kb) * ld + 8 * mb) * 2);
+    step = (uint32_t)(ld * 2);
   }
+
+  // base: element (k0, r0) of the operand.
+  __device__ __forceinline__ void load(const uint16_t* base, int r_left, int k_left) {
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base);
+    const bool r_ok = 8 * mb < r_left;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const bool ok = r_ok && (8 * kb + i < k_left);
+      v[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, ok ? off0 + i * step : OOB, 0, 0));
+    }
+  }
+
+  // Row r of the block gets the 8 k-values of element r: dword e packs
+  // (k = 2e, k = 2e+1), i.e. the halves of v[2e] and v[2e+1] that hold r.
+  __device__ __forceinline__ void store(char* tile) const {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const uint32_t sel = (r & 1) ? 0x07060302u : 0x05040100u;
+      u32x4_t o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = __builtin_amdgcn_perm(v[2 * e + 1][r >> 1], v[2 * e][r >> 1], sel);
+      *reinterpret_cast<u32x4_t*>(tile + tile_off(8 * mb + r, kb)) = o;
+    }
+  }
+};
+
+// MFMA operand fragment of a 32-row slice at sub-step kk (16 wide) of a
+// [rows][64] tile: lane l gets the 8 k-values 16*kk + 8*(l/32) .. +7 of row l%32.
+__device__ __forceinline__ bf16x8_t read_frag(const char* tile, int r0, int kk, int lane) {
+  const int r = r0 + (lane & 31);
+  return *reinterpret_cast<const bf16x8_t*>(tile + tile_off(r, 2 * kk + (lane >> 5)));
 }
 
 // Logical tile of workgroup `bid`: XCD-aware renumbering, then grouped order.
@@ -227,19 +184,25 @@ __device__ __forceinline__ void tile_of(int bid, int nblocks, int tiles_m, int t
 // does not get its host launch stubs emitted for every instantiation).
 namespace kern {
 
-template <int BM, int BN, int BK, int STAGES, int WAVES_M, int WAVES_N, int LA, int LB, int EPI>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int LA, int LB, int EPI>
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N)
 gemm_kernel(GemmArgs args) {
   // The body is compiled for the device only: the host pass needs just the
   // launch stub, and device builtins (buffer descriptors, LDS DMA) have no host
   // form.
 #if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int BK = TILE_BK;
   constexpr int NWAVES = WAVES_M * WAVES_N;
+  constexpr int THREADS = 64 * NWAVES;
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   constexpr int FM = WM / 32, FN = WN / 32;
   constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
   constexpr int STAGE = A_BYTES + B_BYTES;
-  __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE];
+  // Threads that load an M/N-contiguous operand: A's blocks first, then B's.
+  constexpr int A_REG_T = (LA == MC) ? BM : 0;
+  constexpr int B_REG_T = (LB == MC) ? BN : 0;
+  static_assert(A_REG_T + B_REG_T <= THREADS, "one 8x8 block per loading thread");
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -253,26 +216,39 @@ gemm_kernel(GemmArgs args) {
   const int k_end = min(args.K, k_begin + args.k_split);
   const int nk = (k_end - k_begin + BK - 1) / BK;
 
-  using LoaderA = Loader<BM, BK, NWAVES, LA>;
-  using LoaderB = Loader<BN, BK, NWAVES, LB>;
-  LoaderA la;
-  LoaderB lb;
-  la.init(args.lda, wave, lane);
-  lb.init(args.ldb, wave, lane);
-  constexpr int LOADS = LoaderA::PER_WAVE + LoaderB::PER_WAVE;
+  DmaLoader<BM, NWAVES> da;
+  DmaLoader<BN, NWAVES> db;
+  if (LA == KC) da.init(args.lda, wave, lane);
+  if (LB == KC) db.init(args.ldb, wave, lane);
 
-  // Element (outer0, k) of an operand for the K step starting at k.
-  auto a_base = [&](int k) {
-    return LA == KC ? args.a + (int64_t)m0 * args.lda + k : args.a + (int64_t)k * args.lda + m0;
-  };
-  auto b_base = [&](int k) {
-    return LB == KC ? args.b + (int64_t)n0 * args.ldb + k : args.b + (int64_t)k * args.ldb + n0;
-  };
+  // One register loader per thread: threads [0, A_REG_T) take 8x8 blocks of
+  // A (when A is M/N-contiguous), threads [A_REG_T, A_REG_T + B_REG_T) blocks
+  // of B.  Both operands' tiles have R rows in LDS.
+  static_assert(LA == KC || LB == KC || BM == BN, "one register loader shape");
+  constexpr int R_REG = (LA == MC) ? BM : BN;
+  RegLoader<R_REG> rl;
+  const bool reg_a = (LA == MC) && tid < A_REG_T;
+  const bool reg_b = (LB == MC) && tid >= A_REG_T && tid < A_REG_T + B_REG_T;
+  const bool reg_any = reg_a || reg_b;
+  const uint16_t* reg_src = reg_a ? args.a : args.b;
+  const int64_t reg_ld = reg_a ? args.lda : args.ldb;
+  const int reg_o0 = reg_a ? m0 : n0;
+  const int reg_left = reg_a ? args.M - m0 : args.N - n0;
+  const int reg_tile = reg_a ? 0 : A_BYTES;
+  if (LA == MC || LB == MC) rl.init(reg_ld, reg_a ? tid : tid - A_REG_T);
+
+  // Issue the memory loads of K step `step`: DMA into its stage for
+  // K-contiguous operands, into registers for M/N-contiguous ones.
   auto issue = [&](int step) {
     const int k = k_begin + step * BK;
-    char* st = smem + (step % STAGES) * STAGE;
-    la.issue(a_base(k), st, args.M - m0, k_end - k, wave);
-    lb.issue(b_base(k), st + A_BYTES, args.N - n0, k_end - k, wave);
+    char* st = smem + (step & 1) * STAGE;
+    if (LA == KC) da.issue(args.a + (int64_t)m0 * args.lda + k, st, args.M - m0, k_end - k, wave);
+    if (LB == KC) db.issue(args.b + (int64_t)n0 * args.ldb + k, st + A_BYTES, args.N - n0, k_end - k, wave);
+    if ((LA == MC || LB == MC) && reg_any) rl.load(reg_src + (int64_t)k * reg_ld + reg_o0, reg_left, k_end - k);
+  };
+  // Write the register-held blocks of K step `step` into its stage.
+  auto commit = [&](int step) {
+    if ((LA == MC || LB == MC) && reg_any) rl.store(smem + (step & 1) * STAGE + reg_tile);
   };
 
   f32x16_t acc[FM][FN];
@@ -283,33 +259,65 @@ gemm_kernel(GemmArgs args) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
+  // Fragments of one 16-wide sub-step, double-buffered in registers: the reads
+  // of sub-step kk+1 are in flight while the MFMAs of sub-step kk issue.
+  bf16x8_t fa[2][FM], fb[2][FN];
+  auto read_sub = [&](int buf, const char* st, int kk) {
 #pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s)
-    if (s < nk) issue(s);
+    for (int i = 0; i < FM; ++i) fa[buf][i] = read_frag(st, wm * WM + 32 * i, kk, lane);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) fb[buf][j] = read_frag(st + A_BYTES, wn * WN + 32 * j, kk, lane);
+  };
+  auto mfma_sub = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf][j], fa[buf][i], acc[i][j], 0, 0, 0);
+  };
+  constexpr int SUB = BK / 16;
+  static_assert(SUB % 2 == 0, "sub-steps alternate between the two fragment buffers");
 
-  for (int kt = 0; kt < nk; ++kt) {
-    // This wave's loads for step kt are done once at most the loads of the
-    // steps issued after it are outstanding.
-    wait_steps<STAGES - 2, LOADS>(nk - 1 - kt);
-    // Everyone's loads for step kt have landed, and everyone has finished
-    // reading the stage that the next issue overwrites (step kt-1's).
+  if (nk > 0) {
+    issue(0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    commit(0);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
-    if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1);
-    const char* cur = smem + (kt % STAGES) * STAGE;
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      bf16x8_t af[FM], bfr[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i) af[i] = read_frag<BM, BK, LA>(cur, wm * WM + 32 * i, kk, lane);
-#pragma unroll
-      for (int j = 0; j < FN; ++j) bfr[j] = read_frag<BN, BK, LB>(cur + A_BYTES, wn * WN + 32 * j, kk, lane);
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
-    }
+    if (nk > 1) issue(1);
+    read_sub(0, smem, 0);
   }
+
+  // One K step.  With a next step: after the reads of the last sub-step, wait
+  // for this wave's loads of step kt+1, write its register-held blocks, and
+  // wait until its LDS reads and writes are complete; after the barrier the
+  // same holds for every wave, so step kt+1's stage can be read and the
+  // current stage refilled, while the last sub-step's MFMAs run from
+  // registers.  The last step is peeled so that the loop body has one path (no
+  // conservative waits at a merge).
+  auto k_step = [&](int kt, bool has_next) {
+    const char* cur = smem + (kt & 1) * STAGE;
+#pragma unroll
+    for (int kk = 0; kk < SUB - 1; ++kk) {
+      read_sub((kk + 1) & 1, cur, kk + 1);
+      mfma_sub(kk & 1);
+    }
+    if (has_next) {
+      // sched_barrier(0): the compiler may not move instructions across, so the
+      // last sub-step's MFMAs stay behind the barrier and the next reads.
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+      commit(kt + 1);
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+      __builtin_amdgcn_s_barrier();
+      if (kt + 2 < nk) issue(kt + 2);
+      read_sub(0, smem + ((kt + 1) & 1) * STAGE, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    mfma_sub((SUB - 1) & 1);
+  };
+  for (int kt = 0; kt < nk - 1; ++kt) k_step(kt, true);
+  if (nk > 0) k_step(nk - 1, false);
 
   // Epilogue.  With the B fragment as the MFMA's first operand, accumulator
   // register r of fragment (i, j) holds C[32i + lane%32][32j + 8(r/4) + 4(lane/32) + r%4]
@@ -333,7 +341,7 @@ gemm_kernel(GemmArgs args) {
           u16x4_t gv, pv;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            gv[e] = f32_to_bf16(x[e] * phi_cdf(x[e]));
+            gv[e] = epi_gelu(x[e]);
             pv[e] = f32_to_bf16(x[e]);
           }
           *reinterpret_cast<u16x4_t*>(reinterpret_cast<uint16_t*>(args.out) + o) = gv;
@@ -348,11 +356,9 @@ gemm_kernel(GemmArgs args) {
           u16x4_t dv, gv;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float p = bf16_to_f32(pb[e]);
-            const float cdf = phi_cdf(p);
-            const float pdf = 0.39894228040143268f * __expf(-0.5f * p * p);
-            dv[e] = f32_to_bf16(x[e] * (cdf + p * pdf));
-            gv[e] = f32_to_bf16(p * cdf);
+            const DGelu r = epi_dgelu(x[e], pb[e]);
+            dv[e] = r.dp;
+            gv[e] = r.g;
           }
           *reinterpret_cast<u16x4_t*>(reinterpret_cast<uint16_t*>(args.out) + o) = dv;
           *reinterpret_cast<u16x4_t*>(args.out2 + o) = gv;
@@ -369,30 +375,30 @@ gemm_kernel(GemmArgs args) {
 
 namespace {
 
-template <int BM, int BN, int BK, int ST, int WM_, int WN_, int LA, int LB, int EPI>
+template <int BM, int BN, int WM_, int WN_, int LA, int LB, int EPI>
 hipError_t launch_one(const GemmArgs& a, int splits, hipStream_t s) {
   const int blocks = a.tiles_m * a.tiles_n * splits;
-  hipLaunchKernelGGL((kern::gemm_kernel<BM, BN, BK, ST, WM_, WN_, LA, LB, EPI>), dim3(blocks), dim3(64 * WM_ * WN_), 0, s, a);
+  hipLaunchKernelGGL((kern::gemm_kernel<BM, BN, WM_, WN_, LA, LB, EPI>), dim3(blocks), dim3(64 * WM_ * WN_), 0, s, a);
   return hipGetLastError();
 }
 
-template <int BM, int BN, int BK, int ST, int WM_, int WN_>
+template <int BM, int BN, int WM_, int WN_>
 hipError_t dispatch_layout(Layout la, Layout lb, Epi epi, const GemmArgs& a, int splits, hipStream_t s) {
   if (la == KC && lb == MC) {
     switch (epi) {
-      case EPI_GELU: return launch_one<BM, BN, BK, ST, WM_, WN_, KC, MC, EPI_GELU>(a, splits, s);
-      case EPI_F32: return launch_one<BM, BN, BK, ST, WM_, WN_, KC, MC, EPI_F32>(a, splits, s);
-      case EPI_BF16: return launch_one<BM, BN, BK, ST, WM_, WN_, KC, MC, EPI_BF16>(a, splits, s);
+      case EPI_GELU: return launch_one<BM, BN, WM_, WN_, KC, MC, EPI_GELU>(a, splits, s);
+      case EPI_F32: return launch_one<BM, BN, WM_, WN_, KC, MC, EPI_F32>(a, splits, s);
+      case EPI_BF16: return launch_one<BM, BN, WM_, WN_, KC, MC, EPI_BF16>(a, splits, s);
       default: break;
     }
   } else if (la == KC && lb == KC) {
     switch (epi) {
-      case EPI_DGELU: return launch_one<BM, BN, BK, ST, WM_, WN_, KC, KC, EPI_DGELU>(a, splits, s);
-      case EPI_F32: return launch_one<BM, BN, BK, ST, WM_, WN_, KC, KC, EPI_F32>(a, splits, s);
+      case EPI_DGELU: return launch_one<BM, BN, WM_, WN_, KC, KC, EPI_DGELU>(a, splits, s);
+      case EPI_F32: return launch_one<BM, BN, WM_, WN_, KC, KC, EPI_F32>(a, splits, s);
       default: break;
     }
   } else if (la == MC && lb == MC) {
-    if (epi == EPI_F32) return launch_one<BM, BN, BK, ST, WM_, WN_, MC, MC, EPI_F32>(a, splits, s);
+    if (epi == EPI_F32) return launch_one<BM, BN, WM_, WN_, MC, MC, EPI_F32>(a, splits, s);
   }
   return hipErrorInvalidValue;
 }
@@ -405,8 +411,8 @@ int tile_bn(TileCfg t) { return t == TILE_256x256 ? 256 : 128; }
 hipError_t launch_gemm(TileCfg tile, Layout la, Layout lb, Epi epi, const GemmArgs& args, int splits,
                        hipStream_t stream) {
   switch (tile) {
-    case TILE_256x256: return dispatch_layout<256, 256, TPMLP_GEMM_BK, TPMLP_GEMM_STAGES, TPMLP_GEMM_WAVES_M, TPMLP_GEMM_WAVES_N>(la, lb, epi, args, splits, stream);
-    case TILE_128x128: return dispatch_layout<128, 128, 64, 2, 2, 2>(la, lb, epi, args, splits, stream);
+    case TILE_256x256: return dispatch_layout<256, 256, 2, 4>(la, lb, epi, args, splits, stream);
+    case TILE_128x128: return dispatch_layout<128, 128, 2, 2>(la, lb, epi, args, splits, stream);
     default: return hipErrorInvalidValue;
   }
 }

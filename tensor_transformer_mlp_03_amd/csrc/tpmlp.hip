@@ -53,36 +53,43 @@ struct GemmPlan {
 
 int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
-TileCfg choose_tile(int64_t M, int64_t N) {
-  const int64_t big = (int64_t)ceil_div(M, 256) * ceil_div(N, 256);
-  return big >= NUM_CU ? TILE_256x256 : TILE_128x128;
-}
+// Time model used to pick a tile and a split-K count: workgroups run in waves
+// over the chip's slots (one 256x256 block or two 128x128 blocks per CU); a
+// block's time is proportional to its MACs at the measured per-CU rate of its
+// tile; split-K adds a float32 round trip of the slices through memory and
+// one reduction launch.  Splits keep at least 512 of K each.
+constexpr double CU_RATE_256 = 4.3e12;   // flop/s per CU, 256x256 tile
+constexpr double CU_RATE_128 = 1.3e12;   // flop/s per 128x128 block, two per CU
+constexpr double SPLIT_BW = 4.0e12;      // bytes/s for the slices' write and re-read
+constexpr double LAUNCH_S = 5e-6;
 
-// Split K when the output has fewer tiles than the chip has workgroup slots, as
-// long as every slice keeps at least 1024 of K.  Picks the split count whose last
-// wave of workgroups is fullest.
-GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool allow_split) {
-  GemmPlan p;
-  p.tile = choose_tile(M, N);
-  const int slots = NUM_CU * (p.tile == TILE_256x256 ? 1 : 2);
-  const int64_t tiles = (int64_t)ceil_div(M, tile_bm(p.tile)) * ceil_div(N, tile_bn(p.tile));
-  int best = 1;
-  if (allow_split && tiles < slots) {
-    double best_eff = 0.0;
+GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
+  GemmPlan best{TILE_256x256, 1, (int)((K + TILE_BK - 1) / TILE_BK * TILE_BK)};
+  double best_t = 1e30;
+  for (TileCfg tile : {TILE_256x256, TILE_128x128}) {
+    const int64_t bm = tile_bm(tile), bn = tile_bn(tile);
+    const int64_t tiles = (int64_t)ceil_div(M, bm) * ceil_div(N, bn);
+    const int64_t slots = tile == TILE_256x256 ? NUM_CU : 2 * NUM_CU;
+    const double rate = tile == TILE_256x256 ? CU_RATE_256 : CU_RATE_128;
     for (int s = 1; s <= 16; ++s) {
-      if (s > 1 && K / s < 1024) break;
-      const double waves = double(tiles * s) / slots;
-      const double eff = waves / double(ceil_div(tiles * s, slots)) * (waves < 1.0 ? waves : 1.0);
-      if (eff > best_eff + 1e-9) {
-        best_eff = eff;
-        best = s;
+      const int64_t kslice = ((K + s - 1) / s + TILE_BK - 1) / TILE_BK * TILE_BK;
+      const int splits = ceil_div(K, kslice);
+      if (splits != s) continue;
+      if (s > 1 && kslice < 512) break;
+      const int64_t waves = (tiles * s + slots - 1) / slots;
+      double t = double(waves) * double(bm * bn * 2 * kslice) / rate;
+      if (s > 1) t += double(s) * M * N * 4 * 2 / SPLIT_BW + LAUNCH_S;
+      if (t < best_t * (1 - 1e-9)) {
+        best_t = t;
+        best = GemmPlan{tile, s, (int)kslice};
       }
     }
   }
-  const int64_t per = ((K + best - 1) / best + TILE_BK - 1) / TILE_BK * TILE_BK;
-  p.k_split = (int)per;
-  p.splits = ceil_div(K, per);
-  return p;
+  return best;
+}
+
+size_t part_bytes(const GemmPlan& p, int64_t M, int64_t N) {
+  return p.splits > 1 ? size_t(p.splits) * M * N * 4 : 0;
 }
 
 struct FwdPlan {
@@ -92,12 +99,11 @@ struct FwdPlan {
 
 FwdPlan plan_fwd(int64_t M, int64_t H, int64_t F) {
   FwdPlan p;
-  p.g1 = plan_gemm(M, F, H, false);
-  p.g2 = plan_gemm(M, H, F, true);
+  p.g1 = plan_gemm(M, F, H);
+  p.g2 = plan_gemm(M, H, F);
   p.off_G = 0;
   p.off_part = align_up(size_t(M) * F * 2);
-  const size_t part = p.g2.splits > 1 ? size_t(p.g2.splits) * M * H * 4 : 0;
-  p.total = p.off_part + align_up(part);
+  p.total = p.off_part + align_up(std::max(part_bytes(p.g1, M, F), part_bytes(p.g2, M, H)));
   return p;
 }
 
@@ -108,20 +114,19 @@ struct BwdPlan {
 
 BwdPlan plan_bwd(int64_t M, int64_t H, int64_t F, bool recompute) {
   BwdPlan p;
-  p.g0 = plan_gemm(M, F, H, false);
-  p.g1 = plan_gemm(M, F, H, false);
-  p.gdb = plan_gemm(F, H, M, true);
-  p.gda = plan_gemm(H, F, M, true);
-  p.gdx = plan_gemm(M, H, F, true);
+  p.g0 = plan_gemm(M, F, H);
+  p.g1 = plan_gemm(M, F, H);
+  p.gdb = plan_gemm(F, H, M);
+  p.gda = plan_gemm(H, F, M);
+  p.gdx = plan_gemm(M, H, F);
   const size_t mf = align_up(size_t(M) * F * 2);
   p.off_P = 0;
   p.off_G = recompute ? mf : 0;
   p.off_dP = p.off_G + mf;
   p.off_part = p.off_dP + mf;
-  size_t part = 0;
-  if (p.gdb.splits > 1) part = std::max(part, size_t(p.gdb.splits) * F * H * 4);
-  if (p.gda.splits > 1) part = std::max(part, size_t(p.gda.splits) * H * F * 4);
-  if (p.gdx.splits > 1) part = std::max(part, size_t(p.gdx.splits) * M * H * 4);
+  size_t part = recompute ? part_bytes(p.g0, M, F) : 0;
+  part = std::max({part, part_bytes(p.g1, M, F), part_bytes(p.gdb, F, H), part_bytes(p.gda, H, F),
+                   part_bytes(p.gdx, M, H)});
   p.total = p.off_part + align_up(part);
   return p;
 }
@@ -259,20 +264,22 @@ GemmArgs gemm_args(const void* a, int64_t lda, const void* b, int64_t ldb, int64
   return g;
 }
 
-// float32 output GEMM; with split-K the slices go to `part` and are summed into out.
-hipError_t gemm_f32(int kind, Layout la, Layout lb, const void* a, int64_t lda, const void* b, int64_t ldb,
-                    int64_t M, int64_t N, int64_t K, const GemmPlan& p, float* out, float* part,
-                    hipStream_t s) {
+// One product with its epilogue.  Split along K, the slices go to `part` as
+// float32 and the reduction applies the epilogue.
+hipError_t run_gemm(int kind, Layout la, Layout lb, Epi epi, const void* a, int64_t lda, const void* b,
+                    int64_t ldb, int64_t M, int64_t N, int64_t K, const GemmPlan& p, void* out, uint16_t* out2,
+                    const uint16_t* aux, float* part, hipStream_t s) {
   if (p.splits == 1) {
     GemmArgs g = gemm_args(a, lda, b, ldb, M, N, K, p, out, N);
-    return timed(kind, s, [&] { return launch_gemm(p.tile, la, lb, EPI_F32, g, 1, s); });
+    g.out2 = out2;
+    g.aux = aux;
+    return timed(kind, s, [&] { return launch_gemm(p.tile, la, lb, epi, g, 1, s); });
   }
   GemmArgs g = gemm_args(a, lda, b, ldb, M, N, K, p, part, N);
   hipError_t e = timed(kind, s, [&] { return launch_gemm(p.tile, la, lb, EPI_F32, g, p.splits, s); });
   if (e != hipSuccess) return e;
-  const float* parts[TPMLP_MAX_SHARDS];
-  for (int i = 0; i < p.splits; ++i) parts[i] = part + size_t(i) * M * N;
-  return timed(TPMLP_K_SPLITK_REDUCE, s, [&] { return launch_sum(parts, p.splits, out, M * N, s); });
+  return timed(TPMLP_K_SPLITK_REDUCE, s,
+               [&] { return launch_splitk_epilogue(epi, part, p.splits, M * N, out, out2, aux, s); });
 }
 
 char* ws_at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
@@ -282,14 +289,13 @@ hipError_t enqueue_fwd(const tpmlp_bf16* X, const tpmlp_bf16* A, const tpmlp_bf1
                        tpmlp_bf16* P_save, int64_t M, int64_t H, int64_t F, void* ws, hipStream_t s) {
   const FwdPlan p = plan_fwd(M, H, F);
   uint16_t* G = reinterpret_cast<uint16_t*>(ws_at(ws, p.off_G));
+  float* part = reinterpret_cast<float*>(ws_at(ws, p.off_part));
   // P_i = X A_i; G_i = GeLU(P_i)        X: [M][H] (K-contig), A_i: [H][F] (N-contig)
-  GemmArgs g1 = gemm_args(X, H, A, F, M, F, H, p.g1, G, F);
-  g1.out2 = P_save;
-  hipError_t e = timed(TPMLP_K_FWD_GEMM1_GELU, s, [&] { return launch_gemm(p.g1.tile, KC, MC, EPI_GELU, g1, 1, s); });
+  hipError_t e = run_gemm(TPMLP_K_FWD_GEMM1_GELU, KC, MC, EPI_GELU, X, H, A, F, M, F, H, p.g1, G, P_save,
+                          nullptr, part, s);
   if (e != hipSuccess) return e;
   // Z_i = G_i B_i                      G_i: [M][F] (K-contig), B_i: [F][H] (N-contig)
-  return gemm_f32(TPMLP_K_FWD_GEMM2, KC, MC, G, F, B, H, M, H, F, p.g2, Z,
-                  reinterpret_cast<float*>(ws_at(ws, p.off_part)), s);
+  return run_gemm(TPMLP_K_FWD_GEMM2, KC, MC, EPI_F32, G, F, B, H, M, H, F, p.g2, Z, nullptr, nullptr, part, s);
 }
 
 // Enqueue rank i's backward (arguments already checked).
@@ -306,26 +312,22 @@ hipError_t enqueue_bwd(const tpmlp_bf16* dZ, const tpmlp_bf16* X, const tpmlp_bf
   if (recompute) {
     // P_i = X A_i again, kept as bf16 like a saved pre-activation
     uint16_t* Pw = reinterpret_cast<uint16_t*>(ws_at(ws, p.off_P));
-    GemmArgs g0 = gemm_args(X, H, A, F, M, F, H, p.g0, Pw, F);
-    e = timed(TPMLP_K_BWD_RECOMPUTE, s, [&] { return launch_gemm(p.g0.tile, KC, MC, EPI_BF16, g0, 1, s); });
+    e = run_gemm(TPMLP_K_BWD_RECOMPUTE, KC, MC, EPI_BF16, X, H, A, F, M, F, H, p.g0, Pw, nullptr, nullptr, part, s);
     if (e != hipSuccess) return e;
     P = Pw;
   }
   // dG_i = dZ B_i^T; dP_i = dG_i GeLU'(P_i); G_i = GeLU(P_i)
   //   dZ: [M][H] (K-contig), B_i: [F][H] = [N][K] (K-contig)
-  GemmArgs g1 = gemm_args(dZ, H, B, H, M, F, H, p.g1, dP, F);
-  g1.out2 = G;
-  g1.aux = P;
-  e = timed(TPMLP_K_BWD_DGELU, s, [&] { return launch_gemm(p.g1.tile, KC, KC, EPI_DGELU, g1, 1, s); });
+  e = run_gemm(TPMLP_K_BWD_DGELU, KC, KC, EPI_DGELU, dZ, H, B, H, M, F, H, p.g1, dP, G, P, part, s);
   if (e != hipSuccess) return e;
   // dB_i = G_i^T dZ    G_i: [M][F] = [K][M'] (M'-contig), dZ: [M][H] = [K][N'] (N'-contig)
-  e = gemm_f32(TPMLP_K_BWD_DB, MC, MC, G, F, dZ, H, F, H, M, p.gdb, dB, part, s);
+  e = run_gemm(TPMLP_K_BWD_DB, MC, MC, EPI_F32, G, F, dZ, H, F, H, M, p.gdb, dB, nullptr, nullptr, part, s);
   if (e != hipSuccess) return e;
   // dA_i = X^T dP_i    X: [M][H] = [K][M'], dP_i: [M][F] = [K][N']
-  e = gemm_f32(TPMLP_K_BWD_DA, MC, MC, X, H, dP, F, H, F, M, p.gda, dA, part, s);
+  e = run_gemm(TPMLP_K_BWD_DA, MC, MC, EPI_F32, X, H, dP, F, H, F, M, p.gda, dA, nullptr, nullptr, part, s);
   if (e != hipSuccess) return e;
   // dX_i = dP_i A_i^T  dP_i: [M][F] (K-contig), A_i: [H][F] = [N][K] (K-contig)
-  return gemm_f32(TPMLP_K_BWD_DX, KC, KC, dP, F, A, F, M, H, F, p.gdx, dX, part, s);
+  return run_gemm(TPMLP_K_BWD_DX, KC, KC, EPI_F32, dP, F, A, F, M, H, F, p.gdx, dX, nullptr, nullptr, part, s);
 }
 
 }  // namespace
