@@ -19,6 +19,9 @@ same workload.
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -26,6 +29,38 @@ import time
 
 METRIC = "TP-MLP fwd+bwd TFLOP/s per rank shard (bf16) and % of MFMA dense peak"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+ROOT = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(ROOT, "tensor_transformer_mlp_03_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def source_hash() -> str:
+    """sha256 over the library's sources: counters taken from another build are stale."""
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(CSRC, "*"))):
+        h.update(os.path.basename(f).encode())
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
+def traffic_path(workload_name: str) -> str:
+    return os.path.join(PROFILES, f"{workload_name}_traffic.md")
+
+
+def read_traffic(workload_name: str):
+    """{kernel kind: HBM bytes per launch} from the committed counter summary, or None
+    if there is none or it was taken from other sources than the current ones."""
+    path = traffic_path(workload_name)
+    if not os.path.exists(path):
+        return None
+    sha, table = None, {}
+    for line in open(path):
+        parts = line.split()
+        if len(parts) == 2 and parts[0] == "source_sha256:":
+            sha = parts[1]
+        if len(parts) == 4 and parts[0] == "traffic_bytes":
+            table[parts[1]] = (float(parts[2]), float(parts[3]))
+    return table if sha == source_hash() else None
 
 
 def log(*a):
@@ -38,6 +73,21 @@ def gemm_flops(w):
     f = 2.0 * M * H * F
     return {"fwd_gemm1_gelu": f, "fwd_gemm2": f, "bwd_recompute": f, "bwd_dgelu": f, "bwd_dB": f, "bwd_dA": f,
             "bwd_dX": f}
+
+
+def gemm_alg_bytes(w, recompute):
+    """Algorithmic HBM bytes of one launch of each GEMM kind (operands read once,
+    outputs written once; bf16 = 2 bytes, float32 = 4)."""
+    M, H, F = w.M, w.H, w.F_i
+    return {
+        "fwd_gemm1_gelu": 2 * (M * H + H * F) + 2 * M * F * (1 if recompute else 2),  # X, A_i -> G (+P)
+        "fwd_gemm2": 2 * (M * F + F * H) + 4 * M * H,                                # G, B_i -> Z_i
+        "bwd_recompute": 2 * (M * H + H * F) + 2 * M * F,                             # X, A_i -> P
+        "bwd_dgelu": 2 * (M * H + F * H + M * F) + 4 * M * F,                         # dZ, B_i, P -> dP, G
+        "bwd_dB": 2 * (M * F + M * H) + 4 * F * H,                                    # G, dZ -> dB_i
+        "bwd_dA": 2 * (M * H + M * F) + 4 * H * F,                                    # X, dP -> dA_i
+        "bwd_dX": 2 * (M * F + H * F) + 4 * M * H,                                    # dP, A_i -> dX_i
+    }
 
 
 def cpu_baseline(w, target_s=12.0):
@@ -74,6 +124,80 @@ def cpu_baseline(w, target_s=12.0):
                       f"(H={w.H}, F_i={w.F_i}); {dt:.2f} s"}
 
 
+def _kernel_kinds_of(csv_path, order):
+    """Dispatches of libtpmlp kernels in a rocprofv3 counter CSV, zipped in
+    dispatch order with the launch order that bench recorded for the same run."""
+    rows = {}
+    for r in csv.DictReader(open(csv_path)):
+        if "tpmlp" not in r["Kernel_Name"]:
+            continue
+        d = int(r["Dispatch_Id"])
+        rows.setdefault(d, {"name": r["Kernel_Name"], "counters": {}})
+        rows[d]["counters"][r["Counter_Name"]] = rows[d]["counters"].get(r["Counter_Name"], 0.0) + float(
+            r["Counter_Value"])
+    disp = [rows[d] for d in sorted(rows)]
+    if len(disp) != len(order):
+        raise SystemExit(f"{csv_path}: {len(disp)} libtpmlp dispatches, {len(order)} recorded launches")
+    return list(zip(order, disp))
+
+
+def _copy_scale(csv_path, counter, mib):
+    vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(csv_path))
+            if "tpmlp" in r["Kernel_Name"] and r["Counter_Name"] == counter]
+    return (mib * 1024.0) / (sum(vals) / len(vals))  # expected KiB / counted KiB
+
+
+def summarize(d, config):
+    """Write profiles/<workload>_kernels.md and profiles/<workload>_traffic.md from the
+    rocprofv3 outputs in directory d (layout of the commands quoted in them)."""
+    from tensor_transformer_mlp_03_amd import inputs as I
+    w = I.CONFIGS[config]
+    cmd = json.load(open(os.path.join(d, "commands.json")))
+    stats = list(csv.DictReader(open(glob.glob(os.path.join(d, "trace", "*_kernel_stats.csv"))[0])))
+    order = json.load(open(os.path.join(d, "order.json")))
+    fetch = _kernel_kinds_of(glob.glob(os.path.join(d, "fetch", "*_counter_collection.csv"))[0], order)
+    write = _kernel_kinds_of(glob.glob(os.path.join(d, "write", "*_counter_collection.csv"))[0], order)
+    mib = cmd["copy_mib"]
+    f_scale = _copy_scale(glob.glob(os.path.join(d, "copy_fetch", "*_counter_collection.csv"))[0], "FETCH_SIZE", mib)
+    w_scale = _copy_scale(glob.glob(os.path.join(d, "copy_write", "*_counter_collection.csv"))[0], "WRITE_SIZE", mib)
+    agg = {}
+    for (kind, f), (kind2, wr) in zip(fetch, write):
+        assert kind == kind2
+        a = agg.setdefault(kind, {"n": 0, "fetch": 0.0, "write": 0.0, "name": f["name"]})
+        a["n"] += 1
+        a["fetch"] += f["counters"]["FETCH_SIZE"] * 1024 * f_scale
+        a["write"] += wr["counters"]["WRITE_SIZE"] * 1024 * w_scale
+    alg = gemm_alg_bytes(w, w.recompute)
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(os.path.join(PROFILES, f"{w.name}_kernels.md"), "w") as f:
+        f.write(f"# Kernel times, {w.name} (M={w.M}, H={w.H}, F_i={w.F_i}, t={w.t})\n\n")
+        f.write("Command (rocprofv3 kernel trace and stats):\n\n```\n" + cmd["trace"] + "\n```\n\n")
+        f.write("| kernel | calls | average us | total ms | % |\n|---|---|---|---|---|\n")
+        for r in stats:
+            f.write(f"| `{r['Name']}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                    f"{float(r['TotalDurationNs']) / 1e6:.2f} | {float(r['Percentage']):.1f} |\n")
+    with open(traffic_path(w.name), "w") as f:
+        f.write(f"# HBM traffic per launch, {w.name} (M={w.M}, H={w.H}, F_i={w.F_i}, t={w.t})\n\n")
+        f.write("FETCH_SIZE and WRITE_SIZE (KiB per dispatch, L2-to-fabric traffic) from two rocprofv3 --pmc "
+                "runs of one step, each scaled by what the same counter reads for a plain copy of "
+                f"{mib} MiB through tpmlp_shard_sum (one part): fetch x{f_scale:.3f}, write x{w_scale:.3f}.\n\n")
+        for k in ("fetch", "write", "copy_fetch", "copy_write"):
+            f.write(f"```\n{cmd[k]}\n```\n")
+        f.write("\n| kind | launches | fetch MB/launch | write MB/launch | algorithmic MB/launch | ratio |\n"
+                "|---|---|---|---|---|---|\n")
+        for kind, a in agg.items():
+            fb, wb = a["fetch"] / a["n"], a["write"] / a["n"]
+            al = alg.get(kind)
+            f.write(f"| {kind} | {a['n']} | {fb / 1e6:.1f} | {wb / 1e6:.1f} | "
+                    f"{al / 1e6 if al else float('nan'):.1f} | {((fb + wb) / al) if al else float('nan'):.2f} |\n")
+        f.write("\nMachine-readable (bytes per launch, fetch then write):\n\n```\n")
+        f.write(f"source_sha256: {source_hash()}\n")
+        for kind, a in agg.items():
+            f.write(f"traffic_bytes {kind} {a['fetch'] / a['n']:.0f} {a['write'] / a['n']:.0f}\n")
+        f.write("```\n")
+    print(f"wrote {PROFILES}/{w.name}_kernels.md and {traffic_path(w.name)}")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -81,10 +205,17 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=3, help="workload index 0-4 (default 3)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--trace-order", default="",
+                    help="write the kernel kinds of the timed launches, in order, to this JSON file")
+    ap.add_argument("--summarize", default="",
+                    help="directory of rocprofv3 CSV outputs to summarize into profiles/ (no GPU needed)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain copy of this many MiB through tpmlp_shard_sum with one part "
                          "(reference dispatch for scaling HBM byte counters), then exit")
     args = ap.parse_args()
+    if args.summarize:
+        summarize(args.summarize, args.config)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the tensor-parallel "
               "ranks' shards run one after another on a single GPU).", file=sys.stderr)
@@ -132,6 +263,9 @@ def main():
     t1 = time.perf_counter()
     stats, dropped = L.tpmlp_timing_end()
     log(f"[bench] timed {args.steps} steps in {t1 - t0:.4f} s")
+    if args.trace_order:
+        with open(args.trace_order, "w") as f:
+            json.dump([k for k, _ in L.tpmlp_timing_records()], f)
 
     ms_per_step = (t1 - t0) * 1e3 / max(args.steps, 1)
     flops_step = w.model_flops_per_shard() * len(shards)
@@ -150,9 +284,15 @@ def main():
     dom = max((n for n in kernels if n in per_launch), key=lambda n: stats[n][1])
     avg_s = stats[dom][1] * 1e-3 / stats[dom][0]
     achieved = per_launch[dom] / avg_s / 1e12
+    traffic = read_traffic(w.name)
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                "avg_launch_us": round(avg_s * 1e6, 2)}
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": None, "avg_launch_us": round(avg_s * 1e6, 2),
+                "alg_bytes": gemm_alg_bytes(w, w.recompute)[dom]}
+    if traffic and dom in traffic:
+        fetch, write = traffic[dom]
+        roofline["traffic"] = int(fetch + write)
+        roofline["traffic_fetch"], roofline["traffic_write"] = int(fetch), int(write)
 
     result = {
         "metric": METRIC,

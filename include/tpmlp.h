@@ -184,6 +184,12 @@ tpmlp_status tpmlp_timing_begin(int capacity);
  * and counted in *dropped (nullable). */
 tpmlp_status tpmlp_timing_end(int* counts, double* total_ms, int* dropped);
 
+/* The launches recorded by the last tpmlp_timing_begin/end pair, in launch
+ * order: kinds[i] and ms[i] for i < min(capacity, count).  Returns the number
+ * of records (or -1 if kinds or ms is NULL).  Valid until the next
+ * tpmlp_timing_begin on the calling thread. */
+int tpmlp_timing_records(int* kinds, double* ms, int capacity);
+
 #ifdef __cplusplus
 }
 #endif

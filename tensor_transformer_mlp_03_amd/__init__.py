@@ -17,6 +17,7 @@ from ._lib import (  # noqa: F401
     tpmlp_status_str,
     tpmlp_timing_begin,
     tpmlp_timing_end,
+    tpmlp_timing_records,
     tpmlp_tp_bwd,
     tpmlp_tp_fwd,
     tpmlp_tp_workspace_bytes,

@@ -55,6 +55,7 @@ _SIGS = {
     "tpmlp_shard_sum": ([_PP, _int, _vp, _i64, _vp], _int),
     "tpmlp_timing_begin": ([_int], _int),
     "tpmlp_timing_end": ([ctypes.POINTER(_int), ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_int)], _int),
+    "tpmlp_timing_records": ([ctypes.POINTER(_int), ctypes.POINTER(ctypes.c_double), _int], _int),
 }
 
 
@@ -226,3 +227,12 @@ def tpmlp_timing_end():
     dropped = ctypes.c_int(0)
     _check(lib().tpmlp_timing_end(counts, total, ctypes.byref(dropped)), "tpmlp_timing_end")
     return {tpmlp_kernel_name(k): (counts[k], total[k]) for k in range(KERNEL_COUNT)}, dropped.value
+
+
+def tpmlp_timing_records():
+    """[(kernel name, ms)] of the last timing window, in launch order."""
+    n = lib().tpmlp_timing_records((ctypes.c_int * 1)(), (ctypes.c_double * 1)(), 0)
+    kinds = (ctypes.c_int * max(n, 1))()
+    ms = (ctypes.c_double * max(n, 1))()
+    n = lib().tpmlp_timing_records(kinds, ms, n)
+    return [(tpmlp_kernel_name(kinds[i]), ms[i]) for i in range(n)]

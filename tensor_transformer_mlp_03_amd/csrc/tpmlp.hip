@@ -171,6 +171,8 @@ struct Timing {
   int cap = 0, n = 0, dropped = 0;
   std::vector<hipEvent_t> ev;
   std::vector<int> kind;
+  std::vector<int> last_kind;     // records of the last finished timing window
+  std::vector<double> last_ms;
   ~Timing() {
     for (hipEvent_t e : ev) (void)hipEventDestroy(e);
   }
@@ -568,6 +570,8 @@ tpmlp_status tpmlp_timing_end(int* counts, double* total_ms, int* dropped) {
   }
   if (dropped) *dropped = t.dropped;
   t.on = false;
+  t.last_kind.clear();
+  t.last_ms.clear();
   for (int i = 0; i < t.n; ++i) {
     hipError_t e = hipEventSynchronize(t.ev[2 * i + 1]);
     if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
@@ -576,9 +580,22 @@ tpmlp_status tpmlp_timing_end(int* counts, double* total_ms, int* dropped) {
     if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
     counts[t.kind[i]] += 1;
     total_ms[t.kind[i]] += ms;
+    t.last_kind.push_back(t.kind[i]);
+    t.last_ms.push_back(ms);
   }
   t.n = 0;
   return TPMLP_OK;
+}
+
+int tpmlp_timing_records(int* kinds, double* ms, int capacity) {
+  if (!kinds || !ms) return -1;
+  const Timing& t = g_timing;
+  const int n = (int)t.last_kind.size();
+  for (int i = 0; i < n && i < capacity; ++i) {
+    kinds[i] = t.last_kind[i];
+    ms[i] = t.last_ms[i];
+  }
+  return n;
 }
 
 }  // extern "C"
