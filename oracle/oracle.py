@@ -15,7 +15,8 @@ What it computes is the plain definition, in float64, from the bf16-rounded inpu
 * The first GEMM widens H to 4H, the second narrows 4H back to H, with GeLU in
   between (QLM page "大模型训练技术：使用QLM提升Qwen2-7B 128k训练效率3.4倍",
   §2.1.2.2 part 3).  The pages never write GeLU out; the reading taken is the exact
-  form GeLU(p) = p * Phi(p) = 0.5 p (1 + erf(p / sqrt 2)).
+  form GeLU(p) = p * Phi(p) = 0.5 p (1 + erf(p / sqrt 2)), with Phi evaluated
+  as erfc(-p / sqrt 2) / 2 (no cancellation in the negative tail).
 * Splitting A by rows instead would need a sum before the non-linear GeLU, which is
   why A is split by columns (QLM page §2.1.2.2 part 3).
 * Backward: the column-parallel input gradient is the sum of the per-rank
@@ -24,7 +25,7 @@ What it computes is the plain definition, in float64, from the bf16-rounded inpu
   the weight gradients of a product need that product's inputs (asorrir.com survey,
   part 二, Checkpoint 技术), so P_i = X A_i is either kept or recomputed.
 
-Matrix products are numpy float64 ``@`` (a BLAS dgemm); erf is ``scipy.special.erf``.
+Matrix products are numpy float64 ``@`` (a BLAS dgemm); erfc is ``scipy.special.erfc``.
 There is no blocking, fusion or reordering beyond the definition.
 
 Pins (tests/test_oracle.py): textbook GeLU values (tests/golden/gelu_values.txt),
@@ -38,7 +39,7 @@ import math
 from typing import Dict, List, Sequence, Tuple
 
 import numpy as np
-from scipy.special import erf
+from scipy.special import erfc
 
 _INV_SQRT2 = 1.0 / math.sqrt(2.0)
 _INV_SQRT_2PI = 1.0 / math.sqrt(2.0 * math.pi)
@@ -57,14 +58,20 @@ def decode_bf16(bits: np.ndarray) -> np.ndarray:
 # ---------------------------------------------------------------------------
 # The activation
 # ---------------------------------------------------------------------------
+def normal_cdf(p: np.ndarray) -> np.ndarray:
+    """Phi(p) = (1 + erf(p / sqrt 2)) / 2, evaluated as erfc(-p / sqrt 2) / 2, which
+    is the same function without the cancellation of 1 + erf for p << 0."""
+    return 0.5 * erfc(-p * _INV_SQRT2)
+
+
 def gelu(p: np.ndarray) -> np.ndarray:
-    """GeLU(p) = p * Phi(p), Phi the standard normal CDF, written with erf."""
-    return 0.5 * p * (1.0 + erf(p * _INV_SQRT2))
+    """GeLU(p) = p * Phi(p), Phi the standard normal CDF."""
+    return p * normal_cdf(p)
 
 
 def gelu_grad(p: np.ndarray) -> np.ndarray:
     """d/dp [p Phi(p)] = Phi(p) + p phi(p), phi the standard normal density."""
-    return 0.5 * (1.0 + erf(p * _INV_SQRT2)) + p * np.exp(-0.5 * p * p) * _INV_SQRT_2PI
+    return normal_cdf(p) + p * np.exp(-0.5 * p * p) * _INV_SQRT_2PI
 
 
 # ---------------------------------------------------------------------------

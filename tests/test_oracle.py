@@ -51,6 +51,12 @@ def test_gelu_grad_textbook_values():
     assert O.gelu_grad(np.array([0.0]))[0] == 0.5
 
 
+def test_gelu_negative_tail_has_no_cancellation():
+    # Phi(-10) = 7.6198530241605e-24 (standard normal tail value): GeLU(-10) must not
+    # collapse to 0 the way 0.5 p (1 + erf(p/sqrt 2)) does in float64.
+    np.testing.assert_allclose(O.gelu(np.array([-10.0])), [-10.0 * 7.6198530241605e-24], rtol=1e-10)
+
+
 def test_gelu_asymptotes():
     big = np.array([10.0, 20.0, 40.0])
     np.testing.assert_allclose(O.gelu(big), big, rtol=1e-15)
