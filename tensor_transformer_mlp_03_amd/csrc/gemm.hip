@@ -57,6 +57,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint16_t u16x4_t __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -321,47 +322,73 @@ gemm_kernel(GemmArgs args) {
 
   // Epilogue.  With the B fragment as the MFMA's first operand, accumulator
   // register r of fragment (i, j) holds C[32i + lane%32][32j + 8(r/4) + 4(lane/32) + r%4]
-  // of the wave's sub-tile: 4 consecutive columns per register group.
+  // of the wave's sub-tile.  Each wave stages 64 rows of its float32 sub-tile
+  // at a time in LDS (row stride 256 bytes, 16-byte chunks XOR-swizzled by the
+  // row), reads them back row-contiguous and finishes 8 (bf16 outputs) or 4
+  // (float32) consecutive columns per lane, so every store instruction writes
+  // whole 128-byte lines.
+  static_assert(WN == 64 && FM % 2 == 0, "staging layout: 64 columns, 64-row halves");
+  __syncthreads();  // every wave is done with the operand stages
+  char* stage = smem + wave * (64 * 256);
+  static_assert(NWAVES * 64 * 256 <= 2 * STAGE, "staging fits in the operand stages");
+  const int row_w = m0 + wm * WM;  // first output row of this wave
+  const int col_w = n0 + wn * WN;  // first output column of this wave
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    const int row = m0 + wm * WM + 32 * i + (lane & 31);
-    if (row >= args.M) continue;
+  for (int h = 0; h < FM / 2; ++h) {
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
+    for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int col = n0 + wn * WN + 32 * j + 8 * g + 4 * (lane >> 5);
-        if (col >= args.N) continue;  // N % 8 == 0: the 4 columns are in or out together
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int r = 32 * ii + (lane & 31);
+          const int c = 8 * j + 2 * g + (lane >> 5);  // 16-byte chunk (4 columns) of the row
+          const f32x4_t x = {acc[2 * h + ii][j][4 * g], acc[2 * h + ii][j][4 * g + 1], acc[2 * h + ii][j][4 * g + 2],
+                             acc[2 * h + ii][j][4 * g + 3]};
+          *reinterpret_cast<f32x4_t*>(stage + r * 256 + ((c ^ (r & 15)) << 4)) = x;
+        }
+    if (EPI == EPI_F32) {
+      float* out = reinterpret_cast<float*>(args.out) + (int64_t)split * args.split_stride;
+#pragma unroll
+      for (int it = 0; it < 16; ++it) {
+        const int q = it * 64 + lane, r = q >> 4, c = q & 15;
+        const f32x4_t x = *reinterpret_cast<const f32x4_t*>(stage + r * 256 + ((c ^ (r & 15)) << 4));
+        const int row = row_w + 64 * h + r, col = col_w + 4 * c;
+        if (row < args.M && col < args.N) *reinterpret_cast<f32x4_t*>(out + (int64_t)row * args.ldo + col) = x;
+      }
+    } else {
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        const int q = it * 64 + lane, r = q >> 3, cp = q & 7;
+        const f32x4_t x0 = *reinterpret_cast<const f32x4_t*>(stage + r * 256 + (((2 * cp) ^ (r & 15)) << 4));
+        const f32x4_t x1 = *reinterpret_cast<const f32x4_t*>(stage + r * 256 + (((2 * cp + 1) ^ (r & 15)) << 4));
+        const float x[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+        const int row = row_w + 64 * h + r, col = col_w + 8 * cp;
+        if (row >= args.M || col >= args.N) continue;  // N % 8 == 0: 8 columns in or out together
         const int64_t o = (int64_t)row * args.ldo + col;
-        const f32x4_t x = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-        if (EPI == EPI_F32) {
-          float* out = reinterpret_cast<float*>(args.out) + (int64_t)split * args.split_stride;
-          *reinterpret_cast<f32x4_t*>(out + o) = x;
-        } else if (EPI == EPI_GELU) {
-          u16x4_t gv, pv;
+        u16x8_t v1, v2;
+        if (EPI == EPI_GELU) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            gv[e] = epi_gelu(x[e]);
-            pv[e] = f32_to_bf16(x[e]);
+          for (int e = 0; e < 8; ++e) {
+            v1[e] = epi_gelu(x[e]);
+            v2[e] = f32_to_bf16(x[e]);
           }
-          *reinterpret_cast<u16x4_t*>(reinterpret_cast<uint16_t*>(args.out) + o) = gv;
-          if (args.out2) *reinterpret_cast<u16x4_t*>(args.out2 + o) = pv;
+          *reinterpret_cast<u16x8_t*>(reinterpret_cast<uint16_t*>(args.out) + o) = v1;
+          if (args.out2) *reinterpret_cast<u16x8_t*>(args.out2 + o) = v2;
         } else if (EPI == EPI_BF16) {
-          u16x4_t pv;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) pv[e] = f32_to_bf16(x[e]);
-          *reinterpret_cast<u16x4_t*>(reinterpret_cast<uint16_t*>(args.out) + o) = pv;
+          for (int e = 0; e < 8; ++e) v1[e] = f32_to_bf16(x[e]);
+          *reinterpret_cast<u16x8_t*>(reinterpret_cast<uint16_t*>(args.out) + o) = v1;
         } else {  // EPI_DGELU
-          const u16x4_t pb = *reinterpret_cast<const u16x4_t*>(args.aux + o);
-          u16x4_t dv, gv;
+          const u16x8_t pb = *reinterpret_cast<const u16x8_t*>(args.aux + o);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const DGelu r = epi_dgelu(x[e], pb[e]);
-            dv[e] = r.dp;
-            gv[e] = r.g;
+          for (int e = 0; e < 8; ++e) {
+            const DGelu d = epi_dgelu(x[e], pb[e]);
+            v1[e] = d.dp;
+            v2[e] = d.g;
           }
-          *reinterpret_cast<u16x4_t*>(reinterpret_cast<uint16_t*>(args.out) + o) = dv;
-          *reinterpret_cast<u16x4_t*>(args.out2 + o) = gv;
+          *reinterpret_cast<u16x8_t*>(reinterpret_cast<uint16_t*>(args.out) + o) = v1;
+          *reinterpret_cast<u16x8_t*>(args.out2 + o) = v2;
         }
       }
     }
