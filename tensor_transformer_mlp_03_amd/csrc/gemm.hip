@@ -8,9 +8,9 @@
 //   forward   P_i = X A_i          A: KC  B: MC  epilogue GeLU -> G_i (and P_i)
 //             Z_i = G_i B_i        A: KC  B: MC  epilogue float32
 //   backward  P_i = X A_i          A: KC  B: MC  epilogue bf16 (recompute)
-//             dG_i = dZ B_i^T      A: KC  B: KC  epilogue dGeLU -> dP_i, G_i
-//             dB_i = G_i^T dZ      A: MC  B: MC  epilogue float32 (split-K)
-//             dA_i = X^T dP_i      A: MC  B: MC  epilogue float32 (split-K)
+//             dG_i = dZ B_i^T      A: KC  B: KC  epilogue dGeLU -> dP_i, G_i^T, dP_i^T
+//             dB_i = G_i^T dZ      A: KC  B: MC  epilogue float32 (split-K)
+//             dA_i = X^T dP_i      A: MC  B: KC  epilogue float32 (split-K)
 //             dX_i = dP_i A_i^T    A: KC  B: KC  epilogue float32
 //
 // (The split of A by columns and B by rows that makes rank i's work exactly
@@ -60,6 +60,8 @@ typedef uint16_t u16x4_t __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
 constexpr int GROUP_M = 8;
 constexpr int NUM_XCD = 8;
@@ -328,9 +330,10 @@ gemm_kernel(GemmArgs args) {
   // (float32) consecutive columns per lane, so every store instruction writes
   // whole 128-byte lines.
   static_assert(WN == 64 && FM % 2 == 0, "staging layout: 64 columns, 64-row halves");
+  constexpr int ROW_B = 256;  // staged row stride in bytes (64 float32)
   __syncthreads();  // every wave is done with the operand stages
-  char* stage = smem + wave * (64 * 256);
-  static_assert(NWAVES * 64 * 256 <= 2 * STAGE, "staging fits in the operand stages");
+  char* stage = smem + wave * (64 * ROW_B);
+  static_assert(NWAVES * 64 * ROW_B <= 2 * STAGE, "staging fits in the operand stages");
   const int row_w = m0 + wm * WM;  // first output row of this wave
   const int col_w = n0 + wn * WN;  // first output column of this wave
 #pragma unroll
@@ -345,14 +348,14 @@ gemm_kernel(GemmArgs args) {
           const int c = 8 * j + 2 * g + (lane >> 5);  // 16-byte chunk (4 columns) of the row
           const f32x4_t x = {acc[2 * h + ii][j][4 * g], acc[2 * h + ii][j][4 * g + 1], acc[2 * h + ii][j][4 * g + 2],
                              acc[2 * h + ii][j][4 * g + 3]};
-          *reinterpret_cast<f32x4_t*>(stage + r * 256 + ((c ^ (r & 15)) << 4)) = x;
+          *reinterpret_cast<f32x4_t*>(stage + r * ROW_B + ((c ^ (r & 15)) << 4)) = x;
         }
     if (EPI == EPI_F32) {
       float* out = reinterpret_cast<float*>(args.out) + (int64_t)split * args.split_stride;
 #pragma unroll
       for (int it = 0; it < 16; ++it) {
         const int q = it * 64 + lane, r = q >> 4, c = q & 15;
-        const f32x4_t x = *reinterpret_cast<const f32x4_t*>(stage + r * 256 + ((c ^ (r & 15)) << 4));
+        const f32x4_t x = *reinterpret_cast<const f32x4_t*>(stage + r * ROW_B + ((c ^ (r & 15)) << 4));
         const int row = row_w + 64 * h + r, col = col_w + 4 * c;
         if (row < args.M && col < args.N) *reinterpret_cast<f32x4_t*>(out + (int64_t)row * args.ldo + col) = x;
       }
@@ -360,8 +363,8 @@ gemm_kernel(GemmArgs args) {
 #pragma unroll
       for (int it = 0; it < 8; ++it) {
         const int q = it * 64 + lane, r = q >> 3, cp = q & 7;
-        const f32x4_t x0 = *reinterpret_cast<const f32x4_t*>(stage + r * 256 + (((2 * cp) ^ (r & 15)) << 4));
-        const f32x4_t x1 = *reinterpret_cast<const f32x4_t*>(stage + r * 256 + (((2 * cp + 1) ^ (r & 15)) << 4));
+        const f32x4_t x0 = *reinterpret_cast<const f32x4_t*>(stage + r * ROW_B + (((2 * cp) ^ (r & 15)) << 4));
+        const f32x4_t x1 = *reinterpret_cast<const f32x4_t*>(stage + r * ROW_B + (((2 * cp + 1) ^ (r & 15)) << 4));
         const float x[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
         const int row = row_w + 64 * h + r, col = col_w + 8 * cp;
         if (row >= args.M || col >= args.N) continue;  // N % 8 == 0: 8 columns in or out together
@@ -388,7 +391,38 @@ gemm_kernel(GemmArgs args) {
             v2[e] = d.g;
           }
           *reinterpret_cast<u16x8_t*>(reinterpret_cast<uint16_t*>(args.out) + o) = v1;
-          *reinterpret_cast<u16x8_t*>(args.out2 + o) = v2;
+          // Keep dP and G of this row in LDS, in place of its float32 values
+          // (all 8 lanes of the row have read them): dP in bytes [0, 128), G in
+          // [128, 256), 16-byte chunks swizzled by the row.
+          *reinterpret_cast<u16x8_t*>(stage + r * ROW_B + ((cp ^ (r & 7)) << 4)) = v1;
+          *reinterpret_cast<u16x8_t*>(stage + r * ROW_B + 128 + ((cp ^ (r & 7)) << 4)) = v2;
+        }
+      }
+      if (EPI == EPI_DGELU) {
+        // Transposed stores G^T and dP^T: ds_read_b64_tr_b16 turns 4 rows x 16
+        // columns of a 16-lane group into one column per lane; two reads give 8
+        // consecutive rows, one 16-byte store into the transposed output.
+        const int g = lane >> 4, j = lane & 15;
+#pragma unroll
+        for (int it = 0; it < 8; ++it) {
+          const int o0 = 16 * (it & 3), k0 = 8 * ((it >> 2) * 4 + g);
+          const int o = o0 + 4 * (j & 3), c = o >> 3, half = (o & 4) ? 8 : 0;
+          const int ka = k0 + (j >> 2), kb = ka + 4;
+          const int f = col_w + o0 + j, m = row_w + 64 * h + k0;
+#pragma unroll
+          for (int which = 0; which < 2; ++which) {  // 0: dP^T -> out3, 1: G^T -> out2
+            const int region = which * 128;
+            const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_i16x4_t*)(stage + ka * ROW_B + region + ((c ^ (ka & 7)) << 4) + half));
+            const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_i16x4_t*)(stage + kb * ROW_B + region + ((c ^ (kb & 7)) << 4) + half));
+            if (f < args.N && m < args.M) {
+              const u16x8_t v = {(uint16_t)lo[0], (uint16_t)lo[1], (uint16_t)lo[2], (uint16_t)lo[3],
+                                 (uint16_t)hi[0], (uint16_t)hi[1], (uint16_t)hi[2], (uint16_t)hi[3]};
+              uint16_t* dst = which ? args.out2 : args.out3;
+              *reinterpret_cast<u16x8_t*>(dst + (int64_t)f * args.ldt + m) = v;
+            }
+          }
         }
       }
     }
@@ -424,6 +458,8 @@ hipError_t dispatch_layout(Layout la, Layout lb, Epi epi, const GemmArgs& a, int
       case EPI_F32: return launch_one<BM, BN, WM_, WN_, KC, KC, EPI_F32>(a, splits, s);
       default: break;
     }
+  } else if (la == MC && lb == KC) {
+    if (epi == EPI_F32) return launch_one<BM, BN, WM_, WN_, MC, KC, EPI_F32>(a, splits, s);
   } else if (la == MC && lb == MC) {
     if (epi == EPI_F32) return launch_one<BM, BN, WM_, WN_, MC, MC, EPI_F32>(a, splits, s);
   }

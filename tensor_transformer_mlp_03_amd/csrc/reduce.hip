@@ -4,8 +4,10 @@
 //    tensor-parallel all-reduce (the ranks' partial outputs are added,
 //    "大模型训练" notes §3.1).
 //  * splitk_kernel: the sum of the split-K slices of one product, finished with
-//    that product's epilogue (float32 store, GeLU, bf16 store or dGeLU), so that
-//    a product split along K ends exactly like an unsplit one.
+//    that product's epilogue (float32 store, GeLU or bf16 store), so that a
+//    product split along K ends exactly like an unsplit one.
+//  * splitk_dgelu_kernel: the same for the dGeLU epilogue, which also writes G
+//    and dP transposed; it works on 64 x 64 tiles and transposes through LDS.
 //
 // Both are HBM-bound: each lane moves 16-byte vectors of float32 (4 elements),
 // and parts are added left to right so that the result does not depend on the
@@ -69,17 +71,75 @@ __global__ void __launch_bounds__(256) splitk_kernel(SplitArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) p[e] = f32_to_bf16(s[e]);
       reinterpret_cast<u16x4_t*>(a.out)[j] = p;
-    } else {  // EPI_DGELU
-      const u16x4_t pb = reinterpret_cast<const u16x4_t*>(a.aux)[j];
-      u16x4_t dp, g;
+    }
+  }
+}
+
+struct SplitDGeluArgs {
+  const float* part;    // splits x M x N float32
+  int splits;
+  int M, N;
+  uint16_t* dp;         // [M][N]
+  uint16_t* g_t;        // [N][M]
+  uint16_t* dp_t;       // [N][M]
+  const uint16_t* p;    // [M][N] pre-activation
+};
+
+typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
+
+// One 64 x 64 tile per block of 256 threads.  Thread t finishes row t/4,
+// columns 16*(t%4) .. +15 (two 8-column vectors), then, after a barrier, writes
+// 16 consecutive rows of one column of the transposed outputs.
+__global__ void __launch_bounds__(256) splitk_dgelu_kernel(SplitDGeluArgs a) {
+  __shared__ uint16_t s_dp[64][72], s_g[64][72];  // 8 elements of padding per row
+  const int tiles_n = (a.N + 63) / 64;
+  const int m0 = (blockIdx.x / tiles_n) * 64, n0 = (blockIdx.x % tiles_n) * 64;
+  const int t = threadIdx.x;
+  const int64_t plane = (int64_t)a.M * a.N;
+  {
+    const int r = t >> 2, row = m0 + r;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const DGelu r = epi_dgelu(s[e], pb[e]);
-        dp[e] = r.dp;
-        g[e] = r.g;
+    for (int v = 0; v < 2; ++v) {
+      const int c = 16 * (t & 3) + 8 * v, col = n0 + c;
+      if (row >= a.M || col >= a.N) continue;  // N % 8 == 0: 8 columns in or out together
+      const int64_t o = (int64_t)row * a.N + col;
+      f32x4_t s0 = *reinterpret_cast<const f32x4_t*>(a.part + o);
+      f32x4_t s1 = *reinterpret_cast<const f32x4_t*>(a.part + o + 4);
+      for (int i = 1; i < a.splits; ++i) {
+        s0 += *reinterpret_cast<const f32x4_t*>(a.part + i * plane + o);
+        s1 += *reinterpret_cast<const f32x4_t*>(a.part + i * plane + o + 4);
       }
-      reinterpret_cast<u16x4_t*>(a.out)[j] = dp;
-      reinterpret_cast<u16x4_t*>(a.out2)[j] = g;
+      const float x[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+      const u16x8_t pb = *reinterpret_cast<const u16x8_t*>(a.p + o);
+      u16x8_t dp;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const DGelu d = epi_dgelu(x[e], pb[e]);
+        dp[e] = d.dp;
+        s_dp[r][c + e] = d.dp;
+        s_g[r][c + e] = d.g;
+      }
+      *reinterpret_cast<u16x8_t*>(a.dp + o) = dp;
+    }
+  }
+  __syncthreads();
+  {
+    const int c = t >> 2, col = n0 + c;   // a column of the tile = a row of the transposed outputs
+    const int r0 = 16 * (t & 3), row = m0 + r0;
+    if (col < a.N) {
+#pragma unroll
+      for (int v = 0; v < 2; ++v) {
+        if (row + 8 * v >= a.M) continue;  // M % 8 == 0
+        u16x8_t gv, dv;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          gv[e] = s_g[r0 + 8 * v + e][c];
+          dv[e] = s_dp[r0 + 8 * v + e][c];
+        }
+        const int64_t o = (int64_t)col * a.M + row + 8 * v;
+        *reinterpret_cast<u16x8_t*>(a.g_t + o) = gv;
+        *reinterpret_cast<u16x8_t*>(a.dp_t + o) = dv;
+      }
     }
   }
 }
@@ -102,16 +162,22 @@ hipError_t launch_sum(const float* const* parts, int n_parts, float* out, int64_
   return hipGetLastError();
 }
 
-hipError_t launch_splitk_epilogue(Epi epi, const float* part, int splits, int64_t n, void* out, uint16_t* out2,
-                                  const uint16_t* aux, hipStream_t stream) {
+hipError_t launch_splitk_epilogue(Epi epi, const float* part, int splits, int64_t M, int64_t N, void* out,
+                                  uint16_t* out2, uint16_t* out3, const uint16_t* aux, hipStream_t stream) {
+  const int64_t n = M * N;
   if (!part || splits < 1 || (n & 3)) return hipErrorInvalidValue;
+  if (epi == EPI_DGELU) {
+    SplitDGeluArgs a{part, splits, (int)M, (int)N, static_cast<uint16_t*>(out), out2, out3, aux};
+    const int64_t tiles = ((M + 63) / 64) * ((N + 63) / 64);
+    hipLaunchKernelGGL(splitk_dgelu_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, a);
+    return hipGetLastError();
+  }
   SplitArgs a{part, splits, n, out, out2, aux};
   const dim3 grid(grid_for(n / 4)), block(256);
   switch (epi) {
     case EPI_F32: hipLaunchKernelGGL(splitk_kernel<EPI_F32>, grid, block, 0, stream, a); break;
     case EPI_GELU: hipLaunchKernelGGL(splitk_kernel<EPI_GELU>, grid, block, 0, stream, a); break;
     case EPI_BF16: hipLaunchKernelGGL(splitk_kernel<EPI_BF16>, grid, block, 0, stream, a); break;
-    case EPI_DGELU: hipLaunchKernelGGL(splitk_kernel<EPI_DGELU>, grid, block, 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -109,7 +109,7 @@ FwdPlan plan_fwd(int64_t M, int64_t H, int64_t F) {
 
 struct BwdPlan {
   GemmPlan g0, g1, gdb, gda, gdx;
-  size_t off_P, off_G, off_dP, off_part, total;
+  size_t off_P, off_Gt, off_dP, off_dPt, off_part, total;
 };
 
 BwdPlan plan_bwd(int64_t M, int64_t H, int64_t F, bool recompute) {
@@ -121,9 +121,10 @@ BwdPlan plan_bwd(int64_t M, int64_t H, int64_t F, bool recompute) {
   p.gdx = plan_gemm(M, H, F);
   const size_t mf = align_up(size_t(M) * F * 2);
   p.off_P = 0;
-  p.off_G = recompute ? mf : 0;
-  p.off_dP = p.off_G + mf;
-  p.off_part = p.off_dP + mf;
+  p.off_Gt = recompute ? mf : 0;
+  p.off_dP = p.off_Gt + mf;
+  p.off_dPt = p.off_dP + mf;
+  p.off_part = p.off_dPt + mf;
   size_t part = recompute ? part_bytes(p.g0, M, F) : 0;
   part = std::max({part, part_bytes(p.g1, M, F), part_bytes(p.gdb, F, H), part_bytes(p.gda, H, F),
                    part_bytes(p.gdx, M, H)});
@@ -270,18 +271,20 @@ GemmArgs gemm_args(const void* a, int64_t lda, const void* b, int64_t ldb, int64
 // float32 and the reduction applies the epilogue.
 hipError_t run_gemm(int kind, Layout la, Layout lb, Epi epi, const void* a, int64_t lda, const void* b,
                     int64_t ldb, int64_t M, int64_t N, int64_t K, const GemmPlan& p, void* out, uint16_t* out2,
-                    const uint16_t* aux, float* part, hipStream_t s) {
+                    uint16_t* out3, const uint16_t* aux, float* part, hipStream_t s) {
   if (p.splits == 1) {
     GemmArgs g = gemm_args(a, lda, b, ldb, M, N, K, p, out, N);
     g.out2 = out2;
+    g.out3 = out3;
     g.aux = aux;
+    g.ldt = M;
     return timed(kind, s, [&] { return launch_gemm(p.tile, la, lb, epi, g, 1, s); });
   }
   GemmArgs g = gemm_args(a, lda, b, ldb, M, N, K, p, part, N);
   hipError_t e = timed(kind, s, [&] { return launch_gemm(p.tile, la, lb, EPI_F32, g, p.splits, s); });
   if (e != hipSuccess) return e;
   return timed(TPMLP_K_SPLITK_REDUCE, s,
-               [&] { return launch_splitk_epilogue(epi, part, p.splits, M * N, out, out2, aux, s); });
+               [&] { return launch_splitk_epilogue(epi, part, p.splits, M, N, out, out2, out3, aux, s); });
 }
 
 char* ws_at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
@@ -294,10 +297,11 @@ hipError_t enqueue_fwd(const tpmlp_bf16* X, const tpmlp_bf16* A, const tpmlp_bf1
   float* part = reinterpret_cast<float*>(ws_at(ws, p.off_part));
   // P_i = X A_i; G_i = GeLU(P_i)        X: [M][H] (K-contig), A_i: [H][F] (N-contig)
   hipError_t e = run_gemm(TPMLP_K_FWD_GEMM1_GELU, KC, MC, EPI_GELU, X, H, A, F, M, F, H, p.g1, G, P_save,
-                          nullptr, part, s);
+                          nullptr, nullptr, part, s);
   if (e != hipSuccess) return e;
   // Z_i = G_i B_i                      G_i: [M][F] (K-contig), B_i: [F][H] (N-contig)
-  return run_gemm(TPMLP_K_FWD_GEMM2, KC, MC, EPI_F32, G, F, B, H, M, H, F, p.g2, Z, nullptr, nullptr, part, s);
+  return run_gemm(TPMLP_K_FWD_GEMM2, KC, MC, EPI_F32, G, F, B, H, M, H, F, p.g2, Z, nullptr, nullptr, nullptr,
+                  part, s);
 }
 
 // Enqueue rank i's backward (arguments already checked).
@@ -306,30 +310,33 @@ hipError_t enqueue_bwd(const tpmlp_bf16* dZ, const tpmlp_bf16* X, const tpmlp_bf
                        int64_t F, void* ws, hipStream_t s) {
   const bool recompute = P_saved == nullptr;
   const BwdPlan p = plan_bwd(M, H, F, recompute);
-  uint16_t* G = reinterpret_cast<uint16_t*>(ws_at(ws, p.off_G));
+  uint16_t* Gt = reinterpret_cast<uint16_t*>(ws_at(ws, p.off_Gt));
   uint16_t* dP = reinterpret_cast<uint16_t*>(ws_at(ws, p.off_dP));
+  uint16_t* dPt = reinterpret_cast<uint16_t*>(ws_at(ws, p.off_dPt));
   float* part = reinterpret_cast<float*>(ws_at(ws, p.off_part));
   const uint16_t* P = P_saved;
   hipError_t e;
   if (recompute) {
     // P_i = X A_i again, kept as bf16 like a saved pre-activation
     uint16_t* Pw = reinterpret_cast<uint16_t*>(ws_at(ws, p.off_P));
-    e = run_gemm(TPMLP_K_BWD_RECOMPUTE, KC, MC, EPI_BF16, X, H, A, F, M, F, H, p.g0, Pw, nullptr, nullptr, part, s);
+    e = run_gemm(TPMLP_K_BWD_RECOMPUTE, KC, MC, EPI_BF16, X, H, A, F, M, F, H, p.g0, Pw, nullptr, nullptr, nullptr,
+                 part, s);
     if (e != hipSuccess) return e;
     P = Pw;
   }
-  // dG_i = dZ B_i^T; dP_i = dG_i GeLU'(P_i); G_i = GeLU(P_i)
+  // dG_i = dZ B_i^T; dP_i = dG_i GeLU'(P_i) -> dP_i [M][F] and dP_i^T [F][M]; G_i^T = GeLU(P_i)^T [F][M]
   //   dZ: [M][H] (K-contig), B_i: [F][H] = [N][K] (K-contig)
-  e = run_gemm(TPMLP_K_BWD_DGELU, KC, KC, EPI_DGELU, dZ, H, B, H, M, F, H, p.g1, dP, G, P, part, s);
+  e = run_gemm(TPMLP_K_BWD_DGELU, KC, KC, EPI_DGELU, dZ, H, B, H, M, F, H, p.g1, dP, Gt, dPt, P, part, s);
   if (e != hipSuccess) return e;
-  // dB_i = G_i^T dZ    G_i: [M][F] = [K][M'] (M'-contig), dZ: [M][H] = [K][N'] (N'-contig)
-  e = run_gemm(TPMLP_K_BWD_DB, MC, MC, EPI_F32, G, F, dZ, H, F, H, M, p.gdb, dB, nullptr, nullptr, part, s);
+  // dB_i = G_i^T dZ    G_i^T: [F][M] = [M'][K] (K-contig), dZ: [M][H] = [K][N'] (N'-contig)
+  e = run_gemm(TPMLP_K_BWD_DB, KC, MC, EPI_F32, Gt, M, dZ, H, F, H, M, p.gdb, dB, nullptr, nullptr, nullptr, part, s);
   if (e != hipSuccess) return e;
-  // dA_i = X^T dP_i    X: [M][H] = [K][M'], dP_i: [M][F] = [K][N']
-  e = run_gemm(TPMLP_K_BWD_DA, MC, MC, EPI_F32, X, H, dP, F, H, F, M, p.gda, dA, nullptr, nullptr, part, s);
+  // dA_i = X^T dP_i    X: [M][H] = [K][M'] (M'-contig), dP_i^T: [F][M] = [N'][K] (K-contig)
+  e = run_gemm(TPMLP_K_BWD_DA, MC, KC, EPI_F32, X, H, dPt, M, H, F, M, p.gda, dA, nullptr, nullptr, nullptr, part, s);
   if (e != hipSuccess) return e;
   // dX_i = dP_i A_i^T  dP_i: [M][F] (K-contig), A_i: [H][F] = [N][K] (K-contig)
-  return run_gemm(TPMLP_K_BWD_DX, KC, KC, EPI_F32, dP, F, A, F, M, H, F, p.gdx, dX, nullptr, nullptr, part, s);
+  return run_gemm(TPMLP_K_BWD_DX, KC, KC, EPI_F32, dP, F, A, F, M, H, F, p.gdx, dX, nullptr, nullptr, nullptr, part,
+                  s);
 }
 
 }  // namespace
