@@ -58,6 +58,7 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint16_t u16x4_t __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
@@ -115,6 +116,41 @@ struct DmaLoader {
   }
 };
 
+// The same for blocks of a multiple of 8 waves, with one register of per-lane
+// state: DMA instruction i of wave w fills rows (i*NWAVES + w)*8 .. +7, and
+// since NWAVES*8 rows is a multiple of 64 the swizzle of a lane's chunk, and so
+// its column, is the same for every i; the instructions differ by a uniform
+// row offset.
+template <int R, int NWAVES>
+struct DmaLoaderW {
+  static_assert(NWAVES % 8 == 0, "row offsets of the instructions keep the swizzle");
+  static constexpr int PER_WAVE = R * 8 / 64 / NWAVES;
+  static_assert(PER_WAVE * 64 * NWAVES == R * 8, "tile must divide evenly over the waves");
+  uint32_t lane_off;  // byte offset of the lane's chunk in instruction 0
+
+  __device__ __forceinline__ static int lane_row(int wave, int lane) { return wave * 8 + (lane >> 3); }
+  __device__ __forceinline__ static int lane_kc(int wave, int lane) {
+    return 8 * ((lane & 7) ^ (((lane >> 3) ^ wave) & 7));
+  }
+  __device__ __forceinline__ void init(int64_t ld, int wave, int lane) {
+    lane_off = (uint32_t)(((int64_t)lane_row(wave, lane) * ld + lane_kc(wave, lane)) * 2);
+  }
+
+  __device__ __forceinline__ void issue(const uint16_t* base, int64_t ld, char* tile, int rows_left, int k_left,
+                                        int wave, int lane) const {
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base);
+    const bool k_ok = lane_kc(wave, lane) < k_left;
+    const int row = lane_row(wave, lane);
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const bool ok = k_ok && (row + i * NWAVES * 8 < rows_left);
+      const uint32_t off = lane_off + (uint32_t)(i * NWAVES * 8 * ld * 2);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(tile + (i * NWAVES + wave) * 1024), 16,
+                                               ok ? off : OOB, 0, 0, 0);
+    }
+  }
+};
+
 // An M/N-contiguous operand's tile of one K step (64 k-rows of R contiguous
 // elements in memory), loaded by R threads as 8x8 blocks into registers and
 // written transposed into the [R][64] LDS tile.
@@ -156,12 +192,98 @@ struct RegLoader {
   }
 };
 
+// The same for the 256-row tile of the 512-thread ping-pong kernel, spread
+// over every thread so that both wave groups do equal work: thread t loads
+// elements 4*(t%64) .. +3 of k-rows 8*(t/64) .. +7 (8-byte loads; a wave reads
+// whole 512-byte k-rows) and writes 4 K-contiguous rows of 8 k-values.  Odd
+// lanes write their 4 rows in the order 1, 0, 3, 2, so that the 16 lanes of one
+// ds_write_b128 cover both row parities and, with the swizzle, 16 distinct
+// bank groups.
+struct RegLoaderH {
+  u32x2_t v[8];  // v[i]: elements (k = 8*kb + i, r = q .. q+3)
+  int q, kb;
+  uint32_t off0, step;
+
+  __device__ __forceinline__ void init(int64_t ld, int t) {
+    const int mq = t & 63;
+    q = 4 * mq;
+    kb = t >> 6;
+    off0 = (uint32_t)(((int64_t)(8 * kb) * ld + q) * 2);
+    step = (uint32_t)(ld * 2);
+  }
+
+  // base: element (k0, r0) of the operand.  r_left is a multiple of 8, so the
+  // 4 elements of a lane are all in range or all out.
+  __device__ __forceinline__ void load(const uint16_t* base, int r_left, int k_left) {
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base);
+    const bool r_ok = q < r_left;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const bool ok = r_ok && (8 * kb + i < k_left);
+      v[i] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rs, ok ? off0 + i * step : OOB, 0, 0));
+    }
+  }
+
+  // Row e = r ^ (mq & 1) of the lane's 4 gets the 8 k-values of element q + e:
+  // dword d packs (k = 2d, k = 2d+1), the halves of v[2d] and v[2d+1] that hold
+  // element q + e (dword e/2 = r/2 of each).
+  // Element q + e sits in the low half of its dword for even e, the high half
+  // for odd e.
+  __device__ __forceinline__ void store(char* tile) const {
+    const int odd = (q >> 2) & 1;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int e = r ^ odd;
+      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+      u32x4_t o;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) o[d] = __builtin_amdgcn_perm(v[2 * d + 1][r >> 1], v[2 * d][r >> 1], sel);
+      *reinterpret_cast<u32x4_t*>(tile + tile_off(q + e, kb)) = o;
+    }
+  }
+};
+
 // MFMA operand fragment of a 32-row slice at sub-step kk (16 wide) of a
 // [rows][64] tile: lane l gets the 8 k-values 16*kk + 8*(l/32) .. +7 of row l%32.
 __device__ __forceinline__ bf16x8_t read_frag(const char* tile, int r0, int kk, int lane) {
   const int r = r0 + (lane & 31);
   return *reinterpret_cast<const bf16x8_t*>(tile + tile_off(r, 2 * kk + (lane >> 5)));
 }
+
+// One group's (4 waves') LDS-DMA loads of 128 rows x 64 k of a K-contiguous
+// operand into one half of a [256][64] LDS tile: 16 instructions of 1 KiB, 4
+// per wave.  Instruction i of wave w fills rows 8*(4i + w) .. +7 of the half;
+// lane q writes 16-byte position q & 7 of row q / 8 and loads the chunk that
+// the swizzle places there.  Within a half, a row's swizzle depends on the
+// lane and on (4i + w) & 7, so even and odd i use two lane patterns; the
+// second half's rows are 128 further on, which leaves the swizzle unchanged.
+struct HalfDma {
+  static constexpr int PER_WAVE = 4;
+  uint32_t lane_off[2];  // byte offset of the lane's chunk for even / odd i
+  int kc[2];             // its first k inside the K step
+
+  __device__ __forceinline__ void init(int64_t ld, int w, int lane) {
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+      const int c = (lane & 7) ^ (((lane >> 3) ^ (4 * par + w)) & 7);
+      kc[par] = 8 * c;
+      lane_off[par] = (uint32_t)(((int64_t)(lane >> 3) * ld + 8 * c) * 2);
+    }
+  }
+  // base: element (first row of the half, first k of the step).
+  __device__ __forceinline__ void issue(const uint16_t* base, int64_t ld, char* half, int rows_left, int k_left,
+                                        int w, int lane) const {
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base);
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int r0 = 8 * (4 * i + w);
+      const bool ok = (kc[i & 1] < k_left) && (r0 + (lane >> 3) < rows_left);
+      const uint32_t off = lane_off[i & 1] + (uint32_t)((int64_t)r0 * ld * 2);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(half + (4 * i + w) * 1024), 16, ok ? off : OOB, 0, 0,
+                                               0);
+    }
+  }
+};
 
 // Logical tile of workgroup `bid`: XCD-aware renumbering, then grouped order.
 __device__ __forceinline__ void tile_of(int bid, int nblocks, int tiles_m, int tiles_n, int& tm, int& tn,
@@ -179,6 +301,114 @@ __device__ __forceinline__ void tile_of(int bid, int nblocks, int tiles_m, int t
   const int in_group = t % per_group;
   tm = first_m + in_group % gsize;
   tn = in_group / gsize;
+}
+
+// Epilogue.  With the B fragment as the MFMA's first operand, accumulator
+// register r of fragment (i, j) holds C[32i + lane%32][32j + 8(r/4) + 4(lane/32) + r%4]
+// of the wave's sub-tile.  Each wave stages 64 rows of its float32 sub-tile
+// at a time in LDS (row stride 256 bytes, 16-byte chunks XOR-swizzled by the
+// row), reads them back row-contiguous and finishes 8 (bf16 outputs) or 4
+// (float32) consecutive columns per lane, so every store instruction writes
+// whole 128-byte lines.
+// `stage` is this wave's 16 KiB of LDS, free of operand data; row_w and col_w
+// are the first output row and column of the wave's (32 FM) x 64 tile.
+constexpr int ROW_B = 256;  // staged row stride in bytes (64 float32)
+
+template <int EPI, int FM, int FN>
+__device__ __forceinline__ void store_tile(const f32x16_t (&acc)[FM][FN], const GemmArgs& args, char* stage,
+                                           int row_w, int col_w, int split, int lane) {
+  static_assert(FN == 2 && FM % 2 == 0, "staging layout: 64 columns, 64-row halves");
+#pragma unroll
+  for (int h = 0; h < FM / 2; ++h) {
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int r = 32 * ii + (lane & 31);
+          const int c = 8 * j + 2 * g + (lane >> 5);  // 16-byte chunk (4 columns) of the row
+          const f32x4_t x = {acc[2 * h + ii][j][4 * g], acc[2 * h + ii][j][4 * g + 1], acc[2 * h + ii][j][4 * g + 2],
+                             acc[2 * h + ii][j][4 * g + 3]};
+          *reinterpret_cast<f32x4_t*>(stage + r * ROW_B + ((c ^ (r & 15)) << 4)) = x;
+        }
+    if (EPI == EPI_F32) {
+      float* out = reinterpret_cast<float*>(args.out) + (int64_t)split * args.split_stride;
+#pragma unroll
+      for (int it = 0; it < 16; ++it) {
+        const int q = it * 64 + lane, r = q >> 4, c = q & 15;
+        const f32x4_t x = *reinterpret_cast<const f32x4_t*>(stage + r * ROW_B + ((c ^ (r & 15)) << 4));
+        const int row = row_w + 64 * h + r, col = col_w + 4 * c;
+        if (row < args.M && col < args.N) *reinterpret_cast<f32x4_t*>(out + (int64_t)row * args.ldo + col) = x;
+      }
+    } else {
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        const int q = it * 64 + lane, r = q >> 3, cp = q & 7;
+        const f32x4_t x0 = *reinterpret_cast<const f32x4_t*>(stage + r * ROW_B + (((2 * cp) ^ (r & 15)) << 4));
+        const f32x4_t x1 = *reinterpret_cast<const f32x4_t*>(stage + r * ROW_B + (((2 * cp + 1) ^ (r & 15)) << 4));
+        const float x[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+        const int row = row_w + 64 * h + r, col = col_w + 8 * cp;
+        if (row >= args.M || col >= args.N) continue;  // N % 8 == 0: 8 columns in or out together
+        const int64_t o = (int64_t)row * args.ldo + col;
+        u16x8_t v1, v2;
+        if (EPI == EPI_GELU) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            v1[e] = epi_gelu(x[e]);
+            v2[e] = f32_to_bf16(x[e]);
+          }
+          *reinterpret_cast<u16x8_t*>(reinterpret_cast<uint16_t*>(args.out) + o) = v1;
+          if (args.out2) *reinterpret_cast<u16x8_t*>(args.out2 + o) = v2;
+        } else if (EPI == EPI_BF16) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v1[e] = f32_to_bf16(x[e]);
+          *reinterpret_cast<u16x8_t*>(reinterpret_cast<uint16_t*>(args.out) + o) = v1;
+        } else {  // EPI_DGELU
+          const u16x8_t pb = *reinterpret_cast<const u16x8_t*>(args.aux + o);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const DGelu d = epi_dgelu(x[e], pb[e]);
+            v1[e] = d.dp;
+            v2[e] = d.g;
+          }
+          *reinterpret_cast<u16x8_t*>(reinterpret_cast<uint16_t*>(args.out) + o) = v1;
+          // Keep dP and G of this row in LDS, in place of its float32 values
+          // (all 8 lanes of the row have read them): dP in bytes [0, 128), G in
+          // [128, 256), 16-byte chunks swizzled by the row.
+          *reinterpret_cast<u16x8_t*>(stage + r * ROW_B + ((cp ^ (r & 7)) << 4)) = v1;
+          *reinterpret_cast<u16x8_t*>(stage + r * ROW_B + 128 + ((cp ^ (r & 7)) << 4)) = v2;
+        }
+      }
+      if (EPI == EPI_DGELU) {
+        // Transposed stores G^T and dP^T: ds_read_b64_tr_b16 turns 4 rows x 16
+        // columns of a 16-lane group into one column per lane; two reads give 8
+        // consecutive rows, one 16-byte store into the transposed output.
+        const int g = lane >> 4, j = lane & 15;
+#pragma unroll
+        for (int it = 0; it < 8; ++it) {
+          const int o0 = 16 * (it & 3), k0 = 8 * ((it >> 2) * 4 + g);
+          const int o = o0 + 4 * (j & 3), c = o >> 3, half = (o & 4) ? 8 : 0;
+          const int ka = k0 + (j >> 2), kb = ka + 4;
+          const int f = col_w + o0 + j, m = row_w + 64 * h + k0;
+#pragma unroll
+          for (int which = 0; which < 2; ++which) {  // 0: dP^T -> out3, 1: G^T -> out2
+            const int region = which * 128;
+            const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_i16x4_t*)(stage + ka * ROW_B + region + ((c ^ (ka & 7)) << 4) + half));
+            const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_i16x4_t*)(stage + kb * ROW_B + region + ((c ^ (kb & 7)) << 4) + half));
+            if (f < args.N && m < args.M) {
+              const u16x8_t v = {(uint16_t)lo[0], (uint16_t)lo[1], (uint16_t)lo[2], (uint16_t)lo[3],
+                                 (uint16_t)hi[0], (uint16_t)hi[1], (uint16_t)hi[2], (uint16_t)hi[3]};
+              uint16_t* dst = which ? args.out2 : args.out3;
+              *reinterpret_cast<u16x8_t*>(dst + (int64_t)f * args.ldt + m) = v;
+            }
+          }
+        }
+      }
+    }
+  }
 }
 
 }  // namespace
@@ -322,111 +552,206 @@ gemm_kernel(GemmArgs args) {
   for (int kt = 0; kt < nk - 1; ++kt) k_step(kt, true);
   if (nk > 0) k_step(nk - 1, false);
 
-  // Epilogue.  With the B fragment as the MFMA's first operand, accumulator
-  // register r of fragment (i, j) holds C[32i + lane%32][32j + 8(r/4) + 4(lane/32) + r%4]
-  // of the wave's sub-tile.  Each wave stages 64 rows of its float32 sub-tile
-  // at a time in LDS (row stride 256 bytes, 16-byte chunks XOR-swizzled by the
-  // row), reads them back row-contiguous and finishes 8 (bf16 outputs) or 4
-  // (float32) consecutive columns per lane, so every store instruction writes
-  // whole 128-byte lines.
-  static_assert(WN == 64 && FM % 2 == 0, "staging layout: 64 columns, 64-row halves");
-  constexpr int ROW_B = 256;  // staged row stride in bytes (64 float32)
-  __syncthreads();  // every wave is done with the operand stages
-  char* stage = smem + wave * (64 * ROW_B);
+  // Epilogue: each wave stages its tile through its own 16 KiB of LDS.
   static_assert(NWAVES * 64 * ROW_B <= 2 * STAGE, "staging fits in the operand stages");
-  const int row_w = m0 + wm * WM;  // first output row of this wave
-  const int col_w = n0 + wn * WN;  // first output column of this wave
-#pragma unroll
-  for (int h = 0; h < FM / 2; ++h) {
-#pragma unroll
-    for (int ii = 0; ii < 2; ++ii)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int r = 32 * ii + (lane & 31);
-          const int c = 8 * j + 2 * g + (lane >> 5);  // 16-byte chunk (4 columns) of the row
-          const f32x4_t x = {acc[2 * h + ii][j][4 * g], acc[2 * h + ii][j][4 * g + 1], acc[2 * h + ii][j][4 * g + 2],
-                             acc[2 * h + ii][j][4 * g + 3]};
-          *reinterpret_cast<f32x4_t*>(stage + r * ROW_B + ((c ^ (r & 15)) << 4)) = x;
-        }
-    if (EPI == EPI_F32) {
-      float* out = reinterpret_cast<float*>(args.out) + (int64_t)split * args.split_stride;
-#pragma unroll
-      for (int it = 0; it < 16; ++it) {
-        const int q = it * 64 + lane, r = q >> 4, c = q & 15;
-        const f32x4_t x = *reinterpret_cast<const f32x4_t*>(stage + r * ROW_B + ((c ^ (r & 15)) << 4));
-        const int row = row_w + 64 * h + r, col = col_w + 4 * c;
-        if (row < args.M && col < args.N) *reinterpret_cast<f32x4_t*>(out + (int64_t)row * args.ldo + col) = x;
-      }
+  __syncthreads();  // every wave is done with the operand stages
+  store_tile<EPI>(acc, args, smem + wave * (64 * ROW_B), m0 + wm * WM, n0 + wn * WN, split, lane);
+#else
+  (void)args;
+#endif
+}
+
+
+// 256 x 256 tile, both operands K-contiguous, 8 waves in two groups that take
+// turns on the matrix cores.
+//
+// Waves 0-3 (group 0) own output rows 0-127 of the tile, waves 4-7 (group 1)
+// rows 128-255; each wave a 128 x 64 sub-tile.  The hardware places wave w on
+// SIMD w % 4, so every SIMD holds one wave of each group.  K advances in steps
+// of 64, each read in two halves of 32.  A wave alternates a memory phase
+// (issue one batch of its group's loads, read half a K step's operand
+// fragments from LDS into registers) with a compute phase (that half step's 16
+// MFMAs, from registers only).  Group 1 starts one phase late, so while one
+// group computes the other reads, and block-wide barriers between phases keep
+// the two in step.  Counting phases from 0: group 0 reads K step k in phases
+// 4k and 4k+2, group 1 in 4k+1 and 4k+3; the even phases are group 0's memory
+// phases, the odd ones group 1's.
+//
+// Operand tiles are [rows][64] in LDS (128-byte rows, so every DMA request
+// fetches a whole 128-byte line).  A has two buffers, B three (160 KiB in
+// all).  Group 0 reads only A's rows 0-127 and group 1 only rows 128-255, so
+// the two halves of an A buffer free up one phase apart.  Every memory phase
+// issues one batch: 16 KiB, 4 LDS-DMA instructions per wave of the reading
+// group, in the rotation
+//   phase 4k+1 (group 1): B rows   0-127 of step k+2
+//   phase 4k+2 (group 0): B rows 128-255 of step k+2
+//   phase 4k+3 (group 1): A rows   0-127 of step k+2
+//   phase 4k+4 (group 0): A rows 128-255 of step k+2
+// Each batch lands in a buffer half whose last reader finished in an earlier
+// phase, and is read first at least five phases after it is issued: a wave
+// waits, at the end of each memory phase, until only its batches of this and
+// its previous memory phase are in flight.  The load path thus stays about
+// half busy at an even rate, and the computing group never issues a load.
+//
+// Both groups execute the same number of barriers: group 1's extra barrier at
+// the start is matched by skipping the barrier after its last compute phase.
+// Group 0 stages its epilogue in LDS while group 1 still computes.
+template <int EPI>
+__global__ void __launch_bounds__(512)
+gemm_kc_kernel(GemmArgs args) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int BM = 256, BN = 256, BK = TILE_BK;
+  constexpr int WM = 128, WN = 64, FM = WM / 32, FN = WN / 32;
+  constexpr int HALF_BYTES = 128 * BK * 2;      // 128 rows of one operand
+  constexpr int BUF_BYTES = 2 * HALF_BYTES;      // one K step of one operand
+  constexpr int B_BASE = 2 * BUF_BYTES;          // A: 2 buffers, then B: 3
+  constexpr int LDS_BYTES = 5 * BUF_BYTES;
+  static_assert(LDS_BYTES == 160 * 1024, "two A and three B buffers fill the LDS");
+  static_assert(8 * 64 * ROW_B <= LDS_BYTES, "staging fits");
+  __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;
+  const int wg = wave & 3;
+  const int wm = grp, wn = wg;
+
+  int tm, tn, split;
+  tile_of(blockIdx.x, gridDim.x, args.tiles_m, args.tiles_n, tm, tn, split);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int k_begin = split * args.k_split;
+  const int k_end = min(args.K, k_begin + args.k_split);
+  const int nk = (k_end - k_begin + BK - 1) / BK;
+
+  HalfDma dma_a, dma_b;
+  dma_a.init(args.lda, wg, lane);
+  dma_b.init(args.ldb, wg, lane);
+  // Issue this group's share of one operand half of K step `step`:
+  // is_b selects B (else A), hi the rows 128-255 (else 0-127).
+  auto issue = [&](bool is_b, int hi, int step, int b_buf) {
+    const int k = k_begin + step * BK;
+    if (is_b) {
+      dma_b.issue(args.b + (int64_t)(n0 + 128 * hi) * args.ldb + k, args.ldb, smem + B_BASE + b_buf * BUF_BYTES + hi * HALF_BYTES,
+                  args.N - n0 - 128 * hi, k_end - k, wg, lane);
     } else {
+      dma_a.issue(args.a + (int64_t)(m0 + 128 * hi) * args.lda + k, args.lda, smem + (step & 1) * BUF_BYTES + hi * HALF_BYTES,
+                  args.M - m0 - 128 * hi, k_end - k, wg, lane);
+    }
+  };
+
+  f32x16_t acc[FM][FN];
 #pragma unroll
-      for (int it = 0; it < 8; ++it) {
-        const int q = it * 64 + lane, r = q >> 3, cp = q & 7;
-        const f32x4_t x0 = *reinterpret_cast<const f32x4_t*>(stage + r * ROW_B + (((2 * cp) ^ (r & 15)) << 4));
-        const f32x4_t x1 = *reinterpret_cast<const f32x4_t*>(stage + r * ROW_B + (((2 * cp + 1) ^ (r & 15)) << 4));
-        const float x[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-        const int row = row_w + 64 * h + r, col = col_w + 8 * cp;
-        if (row >= args.M || col >= args.N) continue;  // N % 8 == 0: 8 columns in or out together
-        const int64_t o = (int64_t)row * args.ldo + col;
-        u16x8_t v1, v2;
-        if (EPI == EPI_GELU) {
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            v1[e] = epi_gelu(x[e]);
-            v2[e] = f32_to_bf16(x[e]);
-          }
-          *reinterpret_cast<u16x8_t*>(reinterpret_cast<uint16_t*>(args.out) + o) = v1;
-          if (args.out2) *reinterpret_cast<u16x8_t*>(args.out2 + o) = v2;
-        } else if (EPI == EPI_BF16) {
+    for (int j = 0; j < FN; ++j)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) v1[e] = f32_to_bf16(x[e]);
-          *reinterpret_cast<u16x8_t*>(reinterpret_cast<uint16_t*>(args.out) + o) = v1;
-        } else {  // EPI_DGELU
-          const u16x8_t pb = *reinterpret_cast<const u16x8_t*>(args.aux + o);
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  constexpr int HSUB = BK / 32;  // 16-wide sub-steps per phase
+  bf16x8_t fa[HSUB][FM], fb[HSUB][FN];
+  auto read_half = [&](int step, int b_buf, int h) {
+    const char* ta = smem + (step & 1) * BUF_BYTES;
+    const char* tb = smem + B_BASE + b_buf * BUF_BYTES;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const DGelu d = epi_dgelu(x[e], pb[e]);
-            v1[e] = d.dp;
-            v2[e] = d.g;
-          }
-          *reinterpret_cast<u16x8_t*>(reinterpret_cast<uint16_t*>(args.out) + o) = v1;
-          // Keep dP and G of this row in LDS, in place of its float32 values
-          // (all 8 lanes of the row have read them): dP in bytes [0, 128), G in
-          // [128, 256), 16-byte chunks swizzled by the row.
-          *reinterpret_cast<u16x8_t*>(stage + r * ROW_B + ((cp ^ (r & 7)) << 4)) = v1;
-          *reinterpret_cast<u16x8_t*>(stage + r * ROW_B + 128 + ((cp ^ (r & 7)) << 4)) = v2;
-        }
-      }
-      if (EPI == EPI_DGELU) {
-        // Transposed stores G^T and dP^T: ds_read_b64_tr_b16 turns 4 rows x 16
-        // columns of a 16-lane group into one column per lane; two reads give 8
-        // consecutive rows, one 16-byte store into the transposed output.
-        const int g = lane >> 4, j = lane & 15;
+    for (int s2 = 0; s2 < HSUB; ++s2) {
 #pragma unroll
-        for (int it = 0; it < 8; ++it) {
-          const int o0 = 16 * (it & 3), k0 = 8 * ((it >> 2) * 4 + g);
-          const int o = o0 + 4 * (j & 3), c = o >> 3, half = (o & 4) ? 8 : 0;
-          const int ka = k0 + (j >> 2), kb = ka + 4;
-          const int f = col_w + o0 + j, m = row_w + 64 * h + k0;
+      for (int i = 0; i < FM; ++i) fa[s2][i] = read_frag(ta, wm * WM + 32 * i, HSUB * h + s2, lane);
 #pragma unroll
-          for (int which = 0; which < 2; ++which) {  // 0: dP^T -> out3, 1: G^T -> out2
-            const int region = which * 128;
-            const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_i16x4_t*)(stage + ka * ROW_B + region + ((c ^ (ka & 7)) << 4) + half));
-            const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_i16x4_t*)(stage + kb * ROW_B + region + ((c ^ (kb & 7)) << 4) + half));
-            if (f < args.N && m < args.M) {
-              const u16x8_t v = {(uint16_t)lo[0], (uint16_t)lo[1], (uint16_t)lo[2], (uint16_t)lo[3],
-                                 (uint16_t)hi[0], (uint16_t)hi[1], (uint16_t)hi[2], (uint16_t)hi[3]};
-              uint16_t* dst = which ? args.out2 : args.out3;
-              *reinterpret_cast<u16x8_t*>(dst + (int64_t)f * args.ldt + m) = v;
-            }
-          }
-        }
+      for (int j = 0; j < FN; ++j) fb[s2][j] = read_frag(tb, wn * WN + 32 * j, HSUB * h + s2, lane);
+    }
+  };
+  auto mfma_half = [&]() {
+#pragma unroll
+    for (int s2 = 0; s2 < HSUB; ++s2)
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[s2][j], fa[s2][i], acc[i][j], 0, 0, 0);
+  };
+  // Block-wide barrier that the compiler may not move instructions across.
+  auto sync = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto lds_wait = [&]() { __builtin_amdgcn_s_waitcnt(0xC07F); };  // lgkmcnt(0)
+  // End of a memory phase: at most the batches of this and the previous memory
+  // phase (HalfDma::PER_WAVE loads each) may still be in flight.
+  int prev_issued = 0;
+  auto end_memory_phase = [&](int cur_issued) {
+    static_assert(HalfDma::PER_WAVE == 4, "vmcnt immediates below assume 4 loads per batch");
+    const int newer = prev_issued + cur_issued;
+    if (newer >= 2) __builtin_amdgcn_s_waitcnt(0x0F78);       // vmcnt(8)
+    else if (newer == 1) __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
+    else __builtin_amdgcn_s_waitcnt(0x0F70);                  // vmcnt(0)
+    prev_issued = cur_issued;
+    lds_wait();
+    sync();
+  };
+
+  if (nk > 0) {
+    // Prologue: K step 0 entirely, and of step 1 all of B and A's rows 0-127.
+    if (grp == 0) {
+      issue(false, 0, 0, 0);
+      issue(false, 1, 0, 0);
+      if (nk > 1) issue(false, 0, 1, 0);
+    } else {
+      issue(true, 0, 0, 0);
+      issue(true, 1, 0, 0);
+      if (nk > 1) {
+        issue(true, 0, 1, 1);
+        issue(true, 1, 1, 1);
       }
     }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    sync();
+    int bb = 0;  // B buffer of step k: k % 3
+    if (grp == 0) {
+      for (int k = 0; k < nk; ++k) {
+        const int bb2 = bb == 0 ? 2 : bb - 1;  // (k + 2) % 3
+        // phase 4k: A rows 128-255 of step k+1
+        const bool i0 = k + 1 < nk;
+        if (i0) issue(false, 1, k + 1, 0);
+        read_half(k, bb, 0);
+        end_memory_phase(i0);
+        mfma_half();
+        sync();
+        // phase 4k+2: B rows 128-255 of step k+2
+        const bool i1 = k + 2 < nk;
+        if (i1) issue(true, 1, k + 2, bb2);
+        read_half(k, bb, 1);
+        end_memory_phase(i1);
+        mfma_half();
+        sync();
+        bb = bb == 2 ? 0 : bb + 1;
+      }
+    } else {
+      sync();
+      for (int k = 0; k < nk; ++k) {
+        const int bb2 = bb == 0 ? 2 : bb - 1;
+        // phase 4k+1: B rows 0-127 of step k+2
+        const bool i0 = k + 2 < nk;
+        if (i0) issue(true, 0, k + 2, bb2);
+        read_half(k, bb, 0);
+        end_memory_phase(i0);
+        mfma_half();
+        sync();
+        // phase 4k+3: A rows 0-127 of step k+2
+        const bool i1 = k + 2 < nk;
+        if (i1) issue(false, 0, k + 2, 0);
+        read_half(k, bb, 1);
+        end_memory_phase(i1);
+        mfma_half();
+        if (k + 1 < nk) sync();
+        bb = bb == 2 ? 0 : bb + 1;
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // nothing is in flight; keeps the staging below safe
   }
+
+  store_tile<EPI>(acc, args, smem + wave * (64 * ROW_B), m0 + wm * WM, n0 + wn * WN, split, lane);
 #else
   (void)args;
 #endif
@@ -439,7 +764,11 @@ namespace {
 template <int BM, int BN, int WM_, int WN_, int LA, int LB, int EPI>
 hipError_t launch_one(const GemmArgs& a, int splits, hipStream_t s) {
   const int blocks = a.tiles_m * a.tiles_n * splits;
-  hipLaunchKernelGGL((kern::gemm_kernel<BM, BN, WM_, WN_, LA, LB, EPI>), dim3(blocks), dim3(64 * WM_ * WN_), 0, s, a);
+  if constexpr (BM == 256 && LA == KC && LB == KC)
+    hipLaunchKernelGGL((kern::gemm_kc_kernel<EPI>), dim3(blocks), dim3(512), 0, s, a);
+  else
+    hipLaunchKernelGGL((kern::gemm_kernel<BM, BN, WM_, WN_, LA, LB, EPI>), dim3(blocks), dim3(64 * WM_ * WN_), 0, s,
+                       a);
   return hipGetLastError();
 }
 
@@ -460,8 +789,6 @@ hipError_t dispatch_layout(Layout la, Layout lb, Epi epi, const GemmArgs& a, int
     }
   } else if (la == MC && lb == KC) {
     if (epi == EPI_F32) return launch_one<BM, BN, WM_, WN_, MC, KC, EPI_F32>(a, splits, s);
-  } else if (la == MC && lb == MC) {
-    if (epi == EPI_F32) return launch_one<BM, BN, WM_, WN_, MC, MC, EPI_F32>(a, splits, s);
   }
   return hipErrorInvalidValue;
 }
