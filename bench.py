@@ -84,9 +84,10 @@ def gemm_alg_bytes(w, recompute):
         "fwd_gemm2": 2 * (M * F + F * H) + 4 * M * H,                                # G, B_i -> Z_i
         "bwd_recompute": 2 * (M * H + H * F) + 2 * M * F,                             # X, A_i -> P
         "bwd_dgelu": 2 * (M * H + F * H + M * F) + 6 * M * F,                         # dZ, B_i, P -> dP, dP^T, G^T
-        "bwd_dB": 2 * (M * F + M * H) + 4 * F * H,                                    # G, dZ -> dB_i
-        "bwd_dA": 2 * (M * H + M * F) + 4 * H * F,                                    # X, dP -> dA_i
+        "bwd_dB": 2 * (M * F + M * H) + 4 * F * H,                                    # G^T, dZ^T -> dB_i
+        "bwd_dA": 2 * (M * H + M * F) + 4 * H * F,                                    # X^T, dP^T -> dA_i
         "bwd_dX": 2 * (M * F + H * F) + 4 * M * H,                                    # dP, A_i -> dX_i
+        "transpose": 4 * M * H,                                                       # X -> X^T, dZ -> dZ^T
     }
 
 

@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define TPMLP_ABI_VERSION 1
+#define TPMLP_ABI_VERSION 2
 #define TPMLP_MAX_SHARDS 64
 
 typedef uint16_t tpmlp_bf16; /* raw bf16 bits */
@@ -88,7 +88,9 @@ tpmlp_status tpmlp_fwd(const tpmlp_bf16* X, const tpmlp_bf16* A_i, const tpmlp_b
                        void* ws, size_t ws_bytes, void* stream);
 
 /* Workspace bytes that tpmlp_bwd needs; `recompute` is 1 when P_saved will be
- * NULL.  0 if the shape is invalid. */
+ * NULL.  0 if the shape is invalid.  The workspace holds the bf16 intermediates
+ * [M,F_i] (dP_i, dP_i^T, G_i^T, and P_i when recomputed), the transposes X^T and
+ * dZ^T [H,M] in bf16, and float32 split-K slices. */
 size_t tpmlp_bwd_workspace_bytes(int64_t M, int64_t H, int64_t F_i, int recompute);
 
 /* Rank i's backward, given the output gradient dZ[M,H] (bf16), which every rank
@@ -166,7 +168,8 @@ typedef enum {
   TPMLP_K_BWD_DX = 6,         /* dX_i = dP_i A_i^T */
   TPMLP_K_SPLITK_REDUCE = 7,  /* sum of split-K float32 partials */
   TPMLP_K_SHARD_SUM = 8,      /* tpmlp_shard_sum and the drivers' partial sums */
-  TPMLP_K_COUNT = 9
+  TPMLP_K_TRANSPOSE = 9,      /* X^T and dZ^T for the weight-gradient products */
+  TPMLP_K_COUNT = 10
 } tpmlp_kernel_kind;
 
 /* Static name of a kernel kind ("?" if out of range). */

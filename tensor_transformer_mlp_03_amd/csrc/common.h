@@ -59,6 +59,9 @@ hipError_t launch_sum(const float* const* parts, int n_parts, float* out, int64_
 hipError_t launch_splitk_epilogue(Epi epi, const float* part, int splits, int64_t M, int64_t N, void* out,
                                   uint16_t* out2, uint16_t* out3, const uint16_t* aux, hipStream_t stream);
 
+// out[c][r] = in[r][c] for a bf16 matrix in[R][C] (R, C multiples of 8).
+hipError_t launch_transpose(const uint16_t* in, int64_t R, int64_t C, uint16_t* out, hipStream_t stream);
+
 int tile_bm(TileCfg t);
 int tile_bn(TileCfg t);
 constexpr int TILE_BK = 64;

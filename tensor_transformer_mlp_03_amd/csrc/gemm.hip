@@ -787,8 +787,6 @@ hipError_t dispatch_layout(Layout la, Layout lb, Epi epi, const GemmArgs& a, int
       case EPI_F32: return launch_one<BM, BN, WM_, WN_, KC, KC, EPI_F32>(a, splits, s);
       default: break;
     }
-  } else if (la == MC && lb == KC) {
-    if (epi == EPI_F32) return launch_one<BM, BN, WM_, WN_, MC, KC, EPI_F32>(a, splits, s);
   }
   return hipErrorInvalidValue;
 }

@@ -1,4 +1,5 @@
-// Ordered float32 sums of equally shaped buffers.
+// Memory-bound helpers: ordered float32 sums of equally shaped buffers and a
+// bf16 transpose.
 //
 //  * sum_kernel: out = p_0 + p_1 + ... + p_{t-1}, the local stand-in for the
 //    tensor-parallel all-reduce (the ranks' partial outputs are added,
@@ -9,9 +10,11 @@
 //  * splitk_dgelu_kernel: the same for the dGeLU epilogue, which also writes G
 //    and dP transposed; it works on 64 x 64 tiles and transposes through LDS.
 //
-// Both are HBM-bound: each lane moves 16-byte vectors of float32 (4 elements),
-// and parts are added left to right so that the result does not depend on the
-// launch shape.
+//  * transpose_kernel: out[c][r] = in[r][c] for bf16 matrices, so that the
+//    weight-gradient products read both operands K-contiguous.
+//
+// All are HBM-bound: each lane moves 16-byte vectors, and parts are added left
+// to right so that a sum does not depend on the launch shape.
 
 #include "../../include/tpmlp.h"
 #include "common.h"
@@ -149,6 +152,62 @@ int grid_for(int64_t n4) {
   return (int)(want < 4096 ? (want > 0 ? want : 1) : 4096);
 }
 
+// bf16 transpose, one 64 x 64 tile per wave.  Lane (rb, cb) = (lane / 8,
+// lane % 8) loads the 8 x 8 block at rows 8*rb .. +7, columns 8*cb .. +7 of the
+// tile (8 loads of 16 bytes: one instruction reads 8 rows x 128 bytes), turns
+// it around in registers with v_perm_b32 and writes rows 8*cb .. +7 of the
+// output tile, columns 8*rb .. +7 (one instruction writes 8 rows x 128 bytes).
+// R and C are multiples of 8, so a block is entirely inside or outside.
+// The four waves of a workgroup take four consecutive row tiles of one column
+// tile, and consecutive workgroups continue along the rows, so that the output
+// rows (R * 2 bytes apart, often a power of two) are written in long runs
+// rather than 64 rows at a time at one stride, which would load one memory
+// channel.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+struct TransposeArgs {
+  const uint16_t* in;
+  uint16_t* out;
+  int64_t R, C;  // in is [R][C], out is [C][R]
+  int row_groups;  // groups of four 64-row tiles
+};
+
+__global__ void __launch_bounds__(256) transpose_kernel(TransposeArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const int lane = threadIdx.x & 63;
+  const int rg = blockIdx.x % a.row_groups, ct = blockIdx.x / a.row_groups;
+  // The wave's 64 x 64 tile starts at (tr, tc); the buffer descriptor is built
+  // from that wave-uniform origin (a per-lane base would not fit the scalar
+  // descriptor and would serialize the loads).
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t tr = ((int64_t)rg * 4 + wave) * 64, tc = (int64_t)ct * 64;
+  if (tr >= a.R) return;
+  const int lr = 8 * (lane >> 3), lc = 8 * (lane & 7);
+  const int64_t r0 = tr + lr, c0 = tc + lc;
+  if (r0 >= a.R || c0 >= a.C) return;
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.in + tr * a.C + tc), (short)0, 0x7FFFFFF0, 0x00020000);
+  u32x4_t v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    v[i] = __builtin_bit_cast(u32x4_t,
+                              __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)(((lr + i) * a.C + lc) * 2), 0, 0));
+  // Output row c0 + j takes element j of each of the 8 input rows: dword e
+  // packs input rows 2e and 2e+1, i.e. the halves of v[2e] and v[2e+1] that
+  // hold column j (low halves for even j, high halves for odd j).
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+    u32x4_t o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = __builtin_amdgcn_perm(v[2 * e + 1][j >> 1], v[2 * e][j >> 1], sel);
+    *reinterpret_cast<u32x4_t*>(a.out + (c0 + j) * a.R + r0) = o;
+  }
+#else
+  (void)a;
+#endif
+}
+
 }  // namespace
 
 hipError_t launch_sum(const float* const* parts, int n_parts, float* out, int64_t n, hipStream_t stream) {
@@ -180,6 +239,18 @@ hipError_t launch_splitk_epilogue(Epi epi, const float* part, int splits, int64_
     case EPI_BF16: hipLaunchKernelGGL(splitk_kernel<EPI_BF16>, grid, block, 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose(const uint16_t* in, int64_t R, int64_t C, uint16_t* out, hipStream_t stream) {
+  TransposeArgs a;
+  a.in = in;
+  a.out = out;
+  a.R = R;
+  a.C = C;
+  a.row_groups = (int)((R + 255) / 256);
+  const int64_t blocks = (int64_t)a.row_groups * ((C + 63) / 64);
+  hipLaunchKernelGGL(transpose_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -9,7 +9,10 @@
 // epilogue, the row-parallel GEMM writing the float32 partial); its backward is
 // four or five (optional recompute of the pre-activation, the dGeLU GEMM, the
 // two weight-gradient GEMMs, the input-gradient GEMM), plus split-K reductions
-// where an output has too few tiles to fill the chip.  The t-shard drivers run
+// where an output has too few tiles to fill the chip.  The weight-gradient
+// GEMMs read X and dZ transposed, so that every operand of the backward is
+// K-contiguous; the transposes are made once per backward call (once for all
+// shards in the t-shard driver).  The t-shard drivers run
 // the shards one after another and add the partials in rank order, standing in
 // for the all-reduces of the row-parallel output (forward) and of the
 // column-parallel input gradient (backward) ("大模型训练" notes §3.1; QLM page
@@ -109,7 +112,7 @@ FwdPlan plan_fwd(int64_t M, int64_t H, int64_t F) {
 
 struct BwdPlan {
   GemmPlan g0, g1, gdb, gda, gdx;
-  size_t off_P, off_Gt, off_dP, off_dPt, off_part, total;
+  size_t off_Xt, off_dZt, off_P, off_Gt, off_dP, off_dPt, off_part, total;
 };
 
 BwdPlan plan_bwd(int64_t M, int64_t H, int64_t F, bool recompute) {
@@ -120,8 +123,11 @@ BwdPlan plan_bwd(int64_t M, int64_t H, int64_t F, bool recompute) {
   p.gda = plan_gemm(H, F, M);
   p.gdx = plan_gemm(M, H, F);
   const size_t mf = align_up(size_t(M) * F * 2);
-  p.off_P = 0;
-  p.off_Gt = recompute ? mf : 0;
+  const size_t mh = align_up(size_t(M) * H * 2);
+  p.off_Xt = 0;
+  p.off_dZt = mh;
+  p.off_P = 2 * mh;
+  p.off_Gt = p.off_P + (recompute ? mf : 0);
   p.off_dP = p.off_Gt + mf;
   p.off_dPt = p.off_dP + mf;
   p.off_part = p.off_dPt + mf;
@@ -305,11 +311,26 @@ hipError_t enqueue_fwd(const tpmlp_bf16* X, const tpmlp_bf16* A, const tpmlp_bf1
 }
 
 // Enqueue rank i's backward (arguments already checked).
+// X^T and dZ^T [H][M] into the backward workspace (shared by all shards).
+hipError_t enqueue_transposes(const tpmlp_bf16* dZ, const tpmlp_bf16* X, int64_t M, int64_t H, void* ws,
+                              hipStream_t s) {
+  const BwdPlan p = plan_bwd(M, H, 8, false);  // the transposes' offsets do not depend on F or recompute
+  uint16_t* Xt = reinterpret_cast<uint16_t*>(ws_at(ws, p.off_Xt));
+  uint16_t* dZt = reinterpret_cast<uint16_t*>(ws_at(ws, p.off_dZt));
+  hipError_t e = timed(TPMLP_K_TRANSPOSE, s, [&] { return launch_transpose(X, M, H, Xt, s); });
+  if (e != hipSuccess) return e;
+  return timed(TPMLP_K_TRANSPOSE, s, [&] { return launch_transpose(dZ, M, H, dZt, s); });
+}
+
+// Enqueue rank i's backward (arguments already checked; X^T and dZ^T already
+// in the workspace).
 hipError_t enqueue_bwd(const tpmlp_bf16* dZ, const tpmlp_bf16* X, const tpmlp_bf16* A, const tpmlp_bf16* B,
                        const tpmlp_bf16* P_saved, float* dX, float* dA, float* dB, int64_t M, int64_t H,
                        int64_t F, void* ws, hipStream_t s) {
   const bool recompute = P_saved == nullptr;
   const BwdPlan p = plan_bwd(M, H, F, recompute);
+  const uint16_t* Xt = reinterpret_cast<const uint16_t*>(ws_at(ws, p.off_Xt));
+  const uint16_t* dZt = reinterpret_cast<const uint16_t*>(ws_at(ws, p.off_dZt));
   uint16_t* Gt = reinterpret_cast<uint16_t*>(ws_at(ws, p.off_Gt));
   uint16_t* dP = reinterpret_cast<uint16_t*>(ws_at(ws, p.off_dP));
   uint16_t* dPt = reinterpret_cast<uint16_t*>(ws_at(ws, p.off_dPt));
@@ -328,11 +349,11 @@ hipError_t enqueue_bwd(const tpmlp_bf16* dZ, const tpmlp_bf16* X, const tpmlp_bf
   //   dZ: [M][H] (K-contig), B_i: [F][H] = [N][K] (K-contig)
   e = run_gemm(TPMLP_K_BWD_DGELU, KC, KC, EPI_DGELU, dZ, H, B, H, M, F, H, p.g1, dP, Gt, dPt, P, part, s);
   if (e != hipSuccess) return e;
-  // dB_i = G_i^T dZ    G_i^T: [F][M] = [M'][K] (K-contig), dZ: [M][H] = [K][N'] (N'-contig)
-  e = run_gemm(TPMLP_K_BWD_DB, KC, MC, EPI_F32, Gt, M, dZ, H, F, H, M, p.gdb, dB, nullptr, nullptr, nullptr, part, s);
+  // dB_i = G_i^T dZ    G_i^T: [F][M] = [M'][K], dZ^T: [H][M] = [N'][K] (both K-contig)
+  e = run_gemm(TPMLP_K_BWD_DB, KC, KC, EPI_F32, Gt, M, dZt, M, F, H, M, p.gdb, dB, nullptr, nullptr, nullptr, part, s);
   if (e != hipSuccess) return e;
-  // dA_i = X^T dP_i    X: [M][H] = [K][M'] (M'-contig), dP_i^T: [F][M] = [N'][K] (K-contig)
-  e = run_gemm(TPMLP_K_BWD_DA, MC, KC, EPI_F32, X, H, dPt, M, H, F, M, p.gda, dA, nullptr, nullptr, nullptr, part, s);
+  // dA_i = X^T dP_i    X^T: [H][M] = [M'][K], dP_i^T: [F][M] = [N'][K] (both K-contig)
+  e = run_gemm(TPMLP_K_BWD_DA, KC, KC, EPI_F32, Xt, M, dPt, M, H, F, M, p.gda, dA, nullptr, nullptr, nullptr, part, s);
   if (e != hipSuccess) return e;
   // dX_i = dP_i A_i^T  dP_i: [M][F] (K-contig), A_i: [H][F] = [N][K] (K-contig)
   return run_gemm(TPMLP_K_BWD_DX, KC, KC, EPI_F32, dP, F, A, F, M, H, F, p.gdx, dX, nullptr, nullptr, nullptr, part,
@@ -367,7 +388,7 @@ const char* tpmlp_last_error(void) { return g_last_error.c_str(); }
 
 const char* tpmlp_kernel_name(int kind) {
   static const char* names[TPMLP_K_COUNT] = {"fwd_gemm1_gelu", "fwd_gemm2", "bwd_recompute", "bwd_dgelu",
-                                             "bwd_dB", "bwd_dA", "bwd_dX", "splitk_reduce", "shard_sum"};
+                                             "bwd_dB", "bwd_dA", "bwd_dX", "splitk_reduce", "shard_sum", "transpose"};
   return (kind >= 0 && kind < TPMLP_K_COUNT) ? names[kind] : "?";
 }
 
@@ -417,8 +438,9 @@ tpmlp_status tpmlp_bwd(const tpmlp_bf16* dZ, const tpmlp_bf16* X, const tpmlp_bf
   std::vector<Range> outs = {{dX_i, mh * 4, "dX_i"}, {dA_i, hf * 4, "dA_i"}, {dB_i, hf * 4, "dB_i"}, {ws, need, "ws"}};
   if ((st = check_alias(outs, ins))) return st;
   if ((st = check_device())) return st;
-  hipError_t e = enqueue_bwd(dZ, X, A_i, B_i, P_saved, dX_i, dA_i, dB_i, M, H, F_i, ws,
-                             static_cast<hipStream_t>(stream));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = enqueue_transposes(dZ, X, M, H, ws, s);
+  if (e == hipSuccess) e = enqueue_bwd(dZ, X, A_i, B_i, P_saved, dX_i, dA_i, dB_i, M, H, F_i, ws, s);
   return e == hipSuccess ? TPMLP_OK : hip_fail(e, "tpmlp_bwd launch");
 }
 
@@ -532,6 +554,8 @@ tpmlp_status tpmlp_tp_bwd(const tpmlp_bf16* dZ, const tpmlp_bf16* X, const tpmlp
   float* partials = reinterpret_cast<float*>(ws_at(ws, shard_ws_bytes(M, H, F_i)));
   const bool direct = (t == 1) && !(dX_sh && dX_sh[0]);
   const float* parts[TPMLP_MAX_SHARDS];
+  hipError_t et = enqueue_transposes(dZ, X, M, H, ws, s);
+  if (et != hipSuccess) return hip_fail(et, "tpmlp_tp_bwd transpose");
   for (int i = 0; i < t; ++i) {
     float* dXi = direct ? dX : (dX_sh && dX_sh[i]) ? dX_sh[i] : partials + size_t(i) * mh;
     parts[i] = dXi;

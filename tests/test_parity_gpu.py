@@ -294,6 +294,7 @@ def test_timing_counts_launches():
     assert stats["fwd_gemm1_gelu"][0] == 2 and stats["fwd_gemm2"][0] == 2
     assert stats["bwd_dgelu"][0] == 2 and stats["bwd_dX"][0] == 2 and stats["shard_sum"][0] == 2
     assert stats["bwd_recompute"][0] == 0
+    assert stats["transpose"][0] == 2  # X^T and dZ^T once for both shards
     assert all(ms >= 0 for _, ms in stats.values())
 
 
