@@ -785,6 +785,8 @@ hipError_t dispatch_layout(Layout la, Layout lb, Epi epi, const GemmArgs& a, int
     switch (epi) {
       case EPI_DGELU: return launch_one<BM, BN, WM_, WN_, KC, KC, EPI_DGELU>(a, splits, s);
       case EPI_F32: return launch_one<BM, BN, WM_, WN_, KC, KC, EPI_F32>(a, splits, s);
+      case EPI_GELU: return launch_one<BM, BN, WM_, WN_, KC, KC, EPI_GELU>(a, splits, s);
+      case EPI_BF16: return launch_one<BM, BN, WM_, WN_, KC, KC, EPI_BF16>(a, splits, s);
       default: break;
     }
   }

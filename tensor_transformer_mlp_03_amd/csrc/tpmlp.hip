@@ -95,24 +95,45 @@ size_t part_bytes(const GemmPlan& p, int64_t M, int64_t N) {
   return p.splits > 1 ? size_t(p.splits) * M * N * 4 : 0;
 }
 
+// The forward products read A_i and B_i N-contiguous.  Transposing them first
+// (4*H*F bytes of memory traffic at about 5.5 TB/s) lets the products run on
+// the K-contiguous kernel, measured at about 1.2 PFLOP/s against about 1.05 for
+// the register-transposing one.  On two products of 2*M*H*F flops that saves
+// about M*H*F*4.8e-16 s against H*F*7.3e-13 s for the transposes; they are made
+// only when the saving is 1.5 times the cost, which covers the rates' spread
+// over shapes (the long-context chunk, M = 32768, qualifies; M = 2048 does not).
+constexpr double RATE_KC = 1.2e15, RATE_MC = 1.05e15, TRANSPOSE_BW = 5.5e12, TRANSPOSE_MARGIN = 1.5;
+
+bool transpose_weights(int64_t M, int64_t H, int64_t F) {
+  const double saved = 2.0 * 2.0 * double(M) * H * F * (1.0 / RATE_MC - 1.0 / RATE_KC);
+  const double cost = 4.0 * double(H) * F / TRANSPOSE_BW;
+  return saved > TRANSPOSE_MARGIN * cost;
+}
+
 struct FwdPlan {
   GemmPlan g1, g2;
-  size_t off_G, off_part, total;
+  bool wt;  // products read A_i^T and B_i^T from the workspace
+  size_t off_G, off_At, off_Bt, off_part, total;
 };
 
 FwdPlan plan_fwd(int64_t M, int64_t H, int64_t F) {
   FwdPlan p;
   p.g1 = plan_gemm(M, F, H);
   p.g2 = plan_gemm(M, H, F);
+  p.wt = transpose_weights(M, H, F);
+  const size_t hf = p.wt ? align_up(size_t(H) * F * 2) : 0;
   p.off_G = 0;
-  p.off_part = align_up(size_t(M) * F * 2);
+  p.off_At = align_up(size_t(M) * F * 2);
+  p.off_Bt = p.off_At + hf;
+  p.off_part = p.off_Bt + hf;
   p.total = p.off_part + align_up(std::max(part_bytes(p.g1, M, F), part_bytes(p.g2, M, H)));
   return p;
 }
 
 struct BwdPlan {
   GemmPlan g0, g1, gdb, gda, gdx;
-  size_t off_Xt, off_dZt, off_P, off_Gt, off_dP, off_dPt, off_part, total;
+  bool wt;  // the recompute product reads A_i^T from the workspace
+  size_t off_Xt, off_dZt, off_At, off_P, off_Gt, off_dP, off_dPt, off_part, total;
 };
 
 BwdPlan plan_bwd(int64_t M, int64_t H, int64_t F, bool recompute) {
@@ -124,9 +145,11 @@ BwdPlan plan_bwd(int64_t M, int64_t H, int64_t F, bool recompute) {
   p.gdx = plan_gemm(M, H, F);
   const size_t mf = align_up(size_t(M) * F * 2);
   const size_t mh = align_up(size_t(M) * H * 2);
+  p.wt = recompute && transpose_weights(M, H, F);
   p.off_Xt = 0;
   p.off_dZt = mh;
-  p.off_P = 2 * mh;
+  p.off_At = 2 * mh;
+  p.off_P = p.off_At + (p.wt ? align_up(size_t(H) * F * 2) : 0);
   p.off_Gt = p.off_P + (recompute ? mf : 0);
   p.off_dP = p.off_Gt + mf;
   p.off_dPt = p.off_dP + mf;
@@ -301,9 +324,25 @@ hipError_t enqueue_fwd(const tpmlp_bf16* X, const tpmlp_bf16* A, const tpmlp_bf1
   const FwdPlan p = plan_fwd(M, H, F);
   uint16_t* G = reinterpret_cast<uint16_t*>(ws_at(ws, p.off_G));
   float* part = reinterpret_cast<float*>(ws_at(ws, p.off_part));
+  hipError_t e;
+  if (p.wt) {
+    uint16_t* At = reinterpret_cast<uint16_t*>(ws_at(ws, p.off_At));
+    uint16_t* Bt = reinterpret_cast<uint16_t*>(ws_at(ws, p.off_Bt));
+    e = timed(TPMLP_K_TRANSPOSE, s, [&] { return launch_transpose(A, H, F, At, s); });
+    if (e != hipSuccess) return e;
+    e = timed(TPMLP_K_TRANSPOSE, s, [&] { return launch_transpose(B, F, H, Bt, s); });
+    if (e != hipSuccess) return e;
+    // P_i = X A_i; G_i = GeLU(P_i)      X: [M][H], A_i^T: [F][H] (both K-contig)
+    e = run_gemm(TPMLP_K_FWD_GEMM1_GELU, KC, KC, EPI_GELU, X, H, At, H, M, F, H, p.g1, G, P_save, nullptr,
+                 nullptr, part, s);
+    if (e != hipSuccess) return e;
+    // Z_i = G_i B_i                    G_i: [M][F], B_i^T: [H][F] (both K-contig)
+    return run_gemm(TPMLP_K_FWD_GEMM2, KC, KC, EPI_F32, G, F, Bt, F, M, H, F, p.g2, Z, nullptr, nullptr, nullptr,
+                    part, s);
+  }
   // P_i = X A_i; G_i = GeLU(P_i)        X: [M][H] (K-contig), A_i: [H][F] (N-contig)
-  hipError_t e = run_gemm(TPMLP_K_FWD_GEMM1_GELU, KC, MC, EPI_GELU, X, H, A, F, M, F, H, p.g1, G, P_save,
-                          nullptr, nullptr, part, s);
+  e = run_gemm(TPMLP_K_FWD_GEMM1_GELU, KC, MC, EPI_GELU, X, H, A, F, M, F, H, p.g1, G, P_save, nullptr, nullptr,
+               part, s);
   if (e != hipSuccess) return e;
   // Z_i = G_i B_i                      G_i: [M][F] (K-contig), B_i: [F][H] (N-contig)
   return run_gemm(TPMLP_K_FWD_GEMM2, KC, MC, EPI_F32, G, F, B, H, M, H, F, p.g2, Z, nullptr, nullptr, nullptr,
@@ -340,8 +379,16 @@ hipError_t enqueue_bwd(const tpmlp_bf16* dZ, const tpmlp_bf16* X, const tpmlp_bf
   if (recompute) {
     // P_i = X A_i again, kept as bf16 like a saved pre-activation
     uint16_t* Pw = reinterpret_cast<uint16_t*>(ws_at(ws, p.off_P));
-    e = run_gemm(TPMLP_K_BWD_RECOMPUTE, KC, MC, EPI_BF16, X, H, A, F, M, F, H, p.g0, Pw, nullptr, nullptr, nullptr,
-                 part, s);
+    if (p.wt) {
+      uint16_t* At = reinterpret_cast<uint16_t*>(ws_at(ws, p.off_At));
+      e = timed(TPMLP_K_TRANSPOSE, s, [&] { return launch_transpose(A, H, F, At, s); });
+      if (e != hipSuccess) return e;
+      e = run_gemm(TPMLP_K_BWD_RECOMPUTE, KC, KC, EPI_BF16, X, H, At, H, M, F, H, p.g0, Pw, nullptr, nullptr,
+                   nullptr, part, s);
+    } else {
+      e = run_gemm(TPMLP_K_BWD_RECOMPUTE, KC, MC, EPI_BF16, X, H, A, F, M, F, H, p.g0, Pw, nullptr, nullptr,
+                   nullptr, part, s);
+    }
     if (e != hipSuccess) return e;
     P = Pw;
   }

@@ -60,6 +60,10 @@ SMALL = [
     (8, 8, 8, 1, True),
     (520, 520, 264, 2, False),
     (1032, 1040, 1048, 1, True),
+    # M large enough that the forward (and the recompute) transpose the weights
+    # first and run every product K-contiguous
+    (4104, 264, 392, 2, False),
+    (4104, 136, 520, 2, True),
 ]
 
 
