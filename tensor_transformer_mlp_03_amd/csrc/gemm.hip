@@ -318,8 +318,32 @@ template <int EPI, int FM, int FN>
 __device__ __forceinline__ void store_tile(const f32x16_t (&acc)[FM][FN], const GemmArgs& args, char* stage,
                                            int row_w, int col_w, int split, int lane) {
   static_assert(FN == 2 && FM % 2 == 0, "staging layout: 64 columns, 64-row halves");
+  constexpr int NH = FM / 2;
+  // Each phase below issues all of its memory operations before it waits for
+  // any: the dGeLU pre-activations of a 64-row half are loaded together (one
+  // memory latency instead of one per vector; the next half's are in flight
+  // while this half is finished), and LDS reads are batched ahead of the
+  // stores that use them.  The pre-activations come through a buffer
+  // descriptor on the wave's (uniform) first row and column, so rows and
+  // columns outside the output read as zero without a branch.
+  u16x8_t pre[2][8];
+  __amdgpu_buffer_rsrc_t pre_rs;
+  auto load_pre = [&](int h) {
 #pragma unroll
-  for (int h = 0; h < FM / 2; ++h) {
+    for (int it = 0; it < 8; ++it) {
+      const int q = it * 64 + lane, r = q >> 3, cp = q & 7;
+      const int row = row_w + 64 * h + r, col = col_w + 8 * cp;
+      const bool ok = row < args.M && col < args.N;  // N % 8 == 0: 8 columns in or out together
+      const uint32_t off = (uint32_t)(((int64_t)(64 * h + r) * args.ldo + 8 * cp) * 2);
+      pre[h & 1][it] = __builtin_bit_cast(u16x8_t, __builtin_amdgcn_raw_buffer_load_b128(pre_rs, ok ? off : OOB, 0, 0));
+    }
+  };
+  if (EPI == EPI_DGELU) {
+    pre_rs = make_rsrc(args.aux + (int64_t)row_w * args.ldo + col_w);
+    load_pre(0);
+  }
+#pragma unroll
+  for (int h = 0; h < NH; ++h) {
 #pragma unroll
     for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
@@ -332,24 +356,36 @@ __device__ __forceinline__ void store_tile(const f32x16_t (&acc)[FM][FN], const 
                              acc[2 * h + ii][j][4 * g + 3]};
           *reinterpret_cast<f32x4_t*>(stage + r * ROW_B + ((c ^ (r & 15)) << 4)) = x;
         }
+    if (EPI == EPI_DGELU && h + 1 < NH) load_pre(h + 1);
     if (EPI == EPI_F32) {
       float* out = reinterpret_cast<float*>(args.out) + (int64_t)split * args.split_stride;
+      f32x4_t xs[16];
 #pragma unroll
       for (int it = 0; it < 16; ++it) {
         const int q = it * 64 + lane, r = q >> 4, c = q & 15;
-        const f32x4_t x = *reinterpret_cast<const f32x4_t*>(stage + r * ROW_B + ((c ^ (r & 15)) << 4));
+        xs[it] = *reinterpret_cast<const f32x4_t*>(stage + r * ROW_B + ((c ^ (r & 15)) << 4));
+      }
+#pragma unroll
+      for (int it = 0; it < 16; ++it) {
+        const int q = it * 64 + lane, r = q >> 4, c = q & 15;
         const int row = row_w + 64 * h + r, col = col_w + 4 * c;
-        if (row < args.M && col < args.N) *reinterpret_cast<f32x4_t*>(out + (int64_t)row * args.ldo + col) = x;
+        if (row < args.M && col < args.N) *reinterpret_cast<f32x4_t*>(out + (int64_t)row * args.ldo + col) = xs[it];
       }
     } else {
+      f32x4_t x0s[8], x1s[8];
 #pragma unroll
       for (int it = 0; it < 8; ++it) {
         const int q = it * 64 + lane, r = q >> 3, cp = q & 7;
-        const f32x4_t x0 = *reinterpret_cast<const f32x4_t*>(stage + r * ROW_B + (((2 * cp) ^ (r & 15)) << 4));
-        const f32x4_t x1 = *reinterpret_cast<const f32x4_t*>(stage + r * ROW_B + (((2 * cp + 1) ^ (r & 15)) << 4));
-        const float x[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+        x0s[it] = *reinterpret_cast<const f32x4_t*>(stage + r * ROW_B + (((2 * cp) ^ (r & 15)) << 4));
+        x1s[it] = *reinterpret_cast<const f32x4_t*>(stage + r * ROW_B + (((2 * cp + 1) ^ (r & 15)) << 4));
+      }
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        const int q = it * 64 + lane, r = q >> 3, cp = q & 7;
+        const float x[8] = {x0s[it][0], x0s[it][1], x0s[it][2], x0s[it][3],
+                            x1s[it][0], x1s[it][1], x1s[it][2], x1s[it][3]};
         const int row = row_w + 64 * h + r, col = col_w + 8 * cp;
-        if (row >= args.M || col >= args.N) continue;  // N % 8 == 0: 8 columns in or out together
+        const bool ok = row < args.M && col < args.N;  // N % 8 == 0: 8 columns in or out together
         const int64_t o = (int64_t)row * args.ldo + col;
         u16x8_t v1, v2;
         if (EPI == EPI_GELU) {
@@ -358,24 +394,27 @@ __device__ __forceinline__ void store_tile(const f32x16_t (&acc)[FM][FN], const 
             v1[e] = epi_gelu(x[e]);
             v2[e] = f32_to_bf16(x[e]);
           }
-          *reinterpret_cast<u16x8_t*>(reinterpret_cast<uint16_t*>(args.out) + o) = v1;
-          if (args.out2) *reinterpret_cast<u16x8_t*>(args.out2 + o) = v2;
+          if (ok) {
+            *reinterpret_cast<u16x8_t*>(reinterpret_cast<uint16_t*>(args.out) + o) = v1;
+            if (args.out2) *reinterpret_cast<u16x8_t*>(args.out2 + o) = v2;
+          }
         } else if (EPI == EPI_BF16) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) v1[e] = f32_to_bf16(x[e]);
-          *reinterpret_cast<u16x8_t*>(reinterpret_cast<uint16_t*>(args.out) + o) = v1;
+          if (ok) *reinterpret_cast<u16x8_t*>(reinterpret_cast<uint16_t*>(args.out) + o) = v1;
         } else {  // EPI_DGELU
-          const u16x8_t pb = *reinterpret_cast<const u16x8_t*>(args.aux + o);
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const DGelu d = epi_dgelu(x[e], pb[e]);
+            const DGelu d = epi_dgelu(x[e], pre[h & 1][it][e]);
             v1[e] = d.dp;
             v2[e] = d.g;
           }
-          *reinterpret_cast<u16x8_t*>(reinterpret_cast<uint16_t*>(args.out) + o) = v1;
+          if (ok) *reinterpret_cast<u16x8_t*>(reinterpret_cast<uint16_t*>(args.out) + o) = v1;
           // Keep dP and G of this row in LDS, in place of its float32 values
-          // (all 8 lanes of the row have read them): dP in bytes [0, 128), G in
-          // [128, 256), 16-byte chunks swizzled by the row.
+          // (every lane has read its float32 values above): dP in bytes
+          // [0, 128), G in [128, 256), 16-byte chunks swizzled by the row.
+          // Rows and columns outside the output hold values that no
+          // transposed store below reads.
           *reinterpret_cast<u16x8_t*>(stage + r * ROW_B + ((cp ^ (r & 7)) << 4)) = v1;
           *reinterpret_cast<u16x8_t*>(stage + r * ROW_B + 128 + ((cp ^ (r & 7)) << 4)) = v2;
         }
@@ -383,26 +422,42 @@ __device__ __forceinline__ void store_tile(const f32x16_t (&acc)[FM][FN], const 
       if (EPI == EPI_DGELU) {
         // Transposed stores G^T and dP^T: ds_read_b64_tr_b16 turns 4 rows x 16
         // columns of a 16-lane group into one column per lane; two reads give 8
-        // consecutive rows, one 16-byte store into the transposed output.
+        // consecutive rows, one 16-byte store into the transposed output.  Four
+        // of the eight steps are read at a time, then stored.
         const int g = lane >> 4, j = lane & 15;
 #pragma unroll
-        for (int it = 0; it < 8; ++it) {
-          const int o0 = 16 * (it & 3), k0 = 8 * ((it >> 2) * 4 + g);
-          const int o = o0 + 4 * (j & 3), c = o >> 3, half = (o & 4) ? 8 : 0;
-          const int ka = k0 + (j >> 2), kb = ka + 4;
-          const int f = col_w + o0 + j, m = row_w + 64 * h + k0;
+        for (int batch = 0; batch < 2; ++batch) {
+          i16x4_t lo[4][2], hi[4][2];
 #pragma unroll
-          for (int which = 0; which < 2; ++which) {  // 0: dP^T -> out3, 1: G^T -> out2
-            const int region = which * 128;
-            const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_i16x4_t*)(stage + ka * ROW_B + region + ((c ^ (ka & 7)) << 4) + half));
-            const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_i16x4_t*)(stage + kb * ROW_B + region + ((c ^ (kb & 7)) << 4) + half));
+          for (int b4 = 0; b4 < 4; ++b4) {
+            const int it = 4 * batch + b4;
+            const int o0 = 16 * (it & 3), k0 = 8 * ((it >> 2) * 4 + g);
+            const int o = o0 + 4 * (j & 3), c = o >> 3, half = (o & 4) ? 8 : 0;
+            const int ka = k0 + (j >> 2), kb = ka + 4;
+#pragma unroll
+            for (int which = 0; which < 2; ++which) {  // 0: dP^T -> out3, 1: G^T -> out2
+              const int region = which * 128;
+              lo[b4][which] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                  (lds_i16x4_t*)(stage + ka * ROW_B + region + ((c ^ (ka & 7)) << 4) + half));
+              hi[b4][which] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                  (lds_i16x4_t*)(stage + kb * ROW_B + region + ((c ^ (kb & 7)) << 4) + half));
+            }
+          }
+#pragma unroll
+          for (int b4 = 0; b4 < 4; ++b4) {
+            const int it = 4 * batch + b4;
+            const int o0 = 16 * (it & 3), k0 = 8 * ((it >> 2) * 4 + g);
+            const int f = col_w + o0 + j, m = row_w + 64 * h + k0;
             if (f < args.N && m < args.M) {
-              const u16x8_t v = {(uint16_t)lo[0], (uint16_t)lo[1], (uint16_t)lo[2], (uint16_t)lo[3],
-                                 (uint16_t)hi[0], (uint16_t)hi[1], (uint16_t)hi[2], (uint16_t)hi[3]};
-              uint16_t* dst = which ? args.out2 : args.out3;
-              *reinterpret_cast<u16x8_t*>(dst + (int64_t)f * args.ldt + m) = v;
+#pragma unroll
+              for (int which = 0; which < 2; ++which) {
+                const u16x8_t v = {(uint16_t)lo[b4][which][0], (uint16_t)lo[b4][which][1],
+                                   (uint16_t)lo[b4][which][2], (uint16_t)lo[b4][which][3],
+                                   (uint16_t)hi[b4][which][0], (uint16_t)hi[b4][which][1],
+                                   (uint16_t)hi[b4][which][2], (uint16_t)hi[b4][which][3]};
+                uint16_t* dst = which ? args.out2 : args.out3;
+                *reinterpret_cast<u16x8_t*>(dst + (int64_t)f * args.ldt + m) = v;
+              }
             }
           }
         }
