@@ -205,7 +205,63 @@ def summarize(d, config):
         for kind, a in agg.items():
             f.write(f"traffic_bytes {kind} {a['fetch'] / a['n']:.0f} {a['write'] / a['n']:.0f}\n")
         f.write("```\n")
-    print(f"wrote {PROFILES}/{w.name}_kernels.md and {traffic_path(w.name)}")
+    counters_md = _summarize_counters(d, w, cmd, order, agg)
+    print(f"wrote {PROFILES}/{w.name}_kernels.md and {traffic_path(w.name)}" + (f" and {counters_md}" if counters_md else ""))
+
+
+def _summarize_counters(d, w, cmd, order, traffic):
+    """profiles/<workload>_counters.md: per kernel kind, the launch time (kernel trace),
+    the shader clock and MFMA utilisation implied by GRBM_GUI_ACTIVE, the SQ MFMA-busy
+    ratio, LDS bank conflicts per LDS instruction and HBM GB/s.  Needs the trace run's
+    launch order and the SQ counter pass; returns None when they are absent."""
+    trace_order_path = os.path.join(d, "trace_order.json")
+    sq_csv = glob.glob(os.path.join(d, "sq", "*_counter_collection.csv"))
+    trace_csv = glob.glob(os.path.join(d, "trace", "*_kernel_trace.csv"))
+    if not (os.path.exists(trace_order_path) and sq_csv and trace_csv and "sq" in cmd):
+        return None
+    trace_order = json.load(open(trace_order_path))
+    disp = sorted((int(r["Dispatch_Id"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+                  for r in csv.DictReader(open(trace_csv[0])) if "tpmlp" in r["Kernel_Name"])
+    disp = disp[len(disp) - len(trace_order):]  # the timed launches are the last ones
+    dur = {}
+    for kind, (_, ns) in zip(trace_order, disp):
+        dur.setdefault(kind, []).append(ns)
+    sq = {}
+    for kind, rec in _kernel_kinds_of(sq_csv[0], order):
+        a = sq.setdefault(kind, {"n": 0})
+        a["n"] += 1
+        for c, v in rec["counters"].items():
+            a[c] = a.get(c, 0.0) + v
+    flops = gemm_flops(w)
+    path = os.path.join(PROFILES, f"{w.name}_counters.md")
+    with open(path, "w") as f:
+        f.write(f"# Counters per kernel kind, {w.name} (M={w.M}, H={w.H}, F_i={w.F_i}, t={w.t})\n\n")
+        f.write("Launch times from the kernel trace (the timed steps' dispatches), counters from one "
+                "rocprofv3 --pmc pass over one step:\n\n")
+        f.write("```\n" + cmd["trace"] + "\n" + cmd["sq"] + "\n```\n\n")
+        f.write("- cycles = GRBM_GUI_ACTIVE / 8 (the counter is summed over the 8 XCDs); clock = cycles / launch time "
+                "(launches of 100 us or more only).\n"
+                "- MFMA util = the launch's algorithmic flops / (cycles x 256 CUs x 4096 bf16 flop/clk), i.e. "
+                "the fraction of the MFMA peak at the clock the launch actually ran at.\n"
+                "- SQ MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (cycles x 1024 SIMDs).\n"
+                "- LDS conflicts = SQ_LDS_BANK_CONFLICT / SQ_INSTS_LDS (conflict cycles per LDS instruction).\n"
+                "- HBM GB/s = (FETCH_SIZE + WRITE_SIZE bytes, scaled as in the traffic file) / launch time.\n\n")
+        f.write("| kind | launches | us | clock GHz | MFMA util | SQ MFMA busy | LDS conflicts / inst | HBM GB/s |\n"
+                "|---|---|---|---|---|---|---|---|\n")
+        for kind, a in sq.items():
+            n = a["n"]
+            us = (sum(dur.get(kind, [0])) / max(len(dur.get(kind, [])), 1)) / 1e3
+            cyc = a.get("GRBM_GUI_ACTIVE", 0.0) / n / 8
+            # The counter pass's dispatch is not the timed one; for short launches the two differ
+            # too much for their ratio to be a clock.
+            clock = cyc / (us * 1e3) if us >= 100 else float("nan")
+            util = (flops[kind] / (cyc * 256 * 4096)) if kind in flops and cyc else float("nan")
+            busy = a.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / n / (cyc * 1024) if cyc else float("nan")
+            confl = a.get("SQ_LDS_BANK_CONFLICT", 0.0) / max(a.get("SQ_INSTS_LDS", 0.0), 1.0)
+            t = traffic.get(kind)
+            gbs = ((t["fetch"] + t["write"]) / t["n"]) / (us * 1e-6) / 1e9 if (t and us) else float("nan")
+            f.write(f"| {kind} | {n} | {us:.1f} | {clock:.2f} | {util:.3f} | {busy:.3f} | {confl:.3f} | {gbs:.0f} |\n")
+    return path
 
 
 def main():
