@@ -18,7 +18,7 @@ enum Epi : int {
   EPI_GELU = 1,     // out_bf16[m,n] = GeLU(acc); out2_bf16[m,n] = acc if out2 != null
   EPI_BF16 = 2,     // out_bf16[m,n] = acc
   EPI_DGELU = 3,    // p = aux_bf16[m,n]; out_bf16[m,n] = acc * GeLU'(p); transposed:
-                    //   out2_bf16[n,m] = GeLU(p), out3_bf16[n,m] = acc * GeLU'(p)
+                    //   out2_bf16[n,m] = GeLU(p)
 };
 
 struct GemmArgs {
@@ -29,7 +29,6 @@ struct GemmArgs {
   int k_split;        // K elements per split-K slice (multiple of the K tile); K if none
   void* out;          // float* (EPI_F32) or uint16_t* (bf16 epilogues)
   uint16_t* out2;     // second bf16 output or null
-  uint16_t* out3;     // EPI_DGELU's transposed dP
   const uint16_t* aux;  // EPI_DGELU's pre-activation input
   int64_t ldo;        // leading dimension of out, aux and (EPI_GELU) out2
   int64_t ldt;        // leading dimension of EPI_DGELU's transposed outputs
@@ -54,10 +53,10 @@ hipError_t launch_sum(const float* const* parts, int n_parts, float* out, int64_
                       hipStream_t stream);
 
 // Sum of `splits` float32 slices of an [M][N] product (slice i at part + i*M*N)
-// finished with the epilogue `epi` into out/out2/out3 as the GEMM epilogue
+// finished with the epilogue `epi` into out/out2 as the GEMM epilogue
 // would (aux: the dGeLU pre-activation; ldt: M for the transposed outputs).
 hipError_t launch_splitk_epilogue(Epi epi, const float* part, int splits, int64_t M, int64_t N, void* out,
-                                  uint16_t* out2, uint16_t* out3, const uint16_t* aux, hipStream_t stream);
+                                  uint16_t* out2, const uint16_t* aux, hipStream_t stream);
 
 // out[c][r] = in[r][c] for a bf16 matrix in[R][C] (R, C multiples of 8).
 hipError_t launch_transpose(const uint16_t* in, int64_t R, int64_t C, uint16_t* out, hipStream_t stream);

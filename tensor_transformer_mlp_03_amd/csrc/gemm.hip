@@ -2,16 +2,17 @@
 //
 // C[m,n] = sum_k A[m,k] B[k,n], bf16 operands, float32 accumulation on
 // v_mfma_f32_32x32x16_bf16.  Every product of the tensor-parallel MLP's forward
-// and backward is one launch of this kernel with a different operand layout and
-// epilogue:
+// and backward is one launch with an operand layout and an epilogue (KC: K
+// contiguous; MC: the other dimension contiguous; X^T, dZ^T and, when the
+// planner chooses, A_i^T and B_i^T are transposed copies):
 //
-//   forward   P_i = X A_i          A: KC  B: MC  epilogue GeLU -> G_i (and P_i)
-//             Z_i = G_i B_i        A: KC  B: MC  epilogue float32
-//   backward  P_i = X A_i          A: KC  B: MC  epilogue bf16 (recompute)
-//             dG_i = dZ B_i^T      A: KC  B: KC  epilogue dGeLU -> dP_i, G_i^T, dP_i^T
-//             dB_i = G_i^T dZ      A: KC  B: MC  epilogue float32 (split-K)
-//             dA_i = X^T dP_i      A: MC  B: KC  epilogue float32 (split-K)
-//             dX_i = dP_i A_i^T    A: KC  B: KC  epilogue float32
+//   forward   P_i = X A_i          A: KC  B: MC (A_i) or KC (A_i^T)  epilogue GeLU -> G_i (and P_i)
+//             Z_i = G_i B_i        A: KC  B: MC (B_i) or KC (B_i^T)  epilogue float32
+//   backward  P_i = X A_i          as in the forward, epilogue bf16 (recompute)
+//             dG_i = dZ B_i^T      A: KC  B: KC          epilogue dGeLU -> dP_i, G_i^T
+//             dB_i = G_i^T dZ      A: KC  B: KC (dZ^T)   epilogue float32 (split-K)
+//             dA_i = X^T dP_i      A: KC (X^T)  B: MC    epilogue float32 (split-K)
+//             dX_i = dP_i A_i^T    A: KC  B: KC          epilogue float32
 //
 // (The split of A by columns and B by rows that makes rank i's work exactly
 // these products: "大模型训练" notes §3.1; GeLU between the two GEMMs: QLM page
@@ -19,28 +20,26 @@
 // float32 pre-activation never round-trips through memory: asorrir.com survey,
 // part 三, 算子融合.)
 //
-// Design for CDNA4:
-//  * A block computes a BM x BN output tile with 64-wide waves laid out
-//    WAVES_M x WAVES_N; each wave owns a (BM/WAVES_M) x (BN/WAVES_N) sub-tile of
-//    32 x 32 MFMA fragments held in accumulator registers.
-//  * Every operand tile sits in LDS K-contiguous ([rows][BK]), so every MFMA
-//    operand fragment is one ds_read_b128 per lane (8 consecutive k of one
-//    row).  64-bit LDS reads, the transposing ds_read_b64_tr_b16 included,
-//    move about a third of the bytes per clock that 128-bit reads do on
-//    gfx950, so no operand is read through them.
-//  * A K-contiguous operand goes from memory straight into LDS with
-//    buffer_load ... lds (16 bytes per lane, no staging registers, no LDS write
-//    instructions).  An M/N-contiguous operand is loaded into registers in 8x8
-//    blocks (8 k-rows of 8 contiguous elements), transposed in registers with
-//    v_perm_b32 and written K-contiguous with ds_write_b128.  Buffer
+// Two kernels:
+//  * gemm_kc_kernel: 256 x 256 tiles, A K-contiguous, B either; two groups of
+//    four waves take turns between reading operand fragments from LDS and
+//    running MFMAs (its comment has the schedule).  The main path.
+//  * gemm_kernel: a synchronous two-stage pipeline with 128 x 128 tiles (or
+//    256 x 256), an N-contiguous operand transposed in registers; used for
+//    outputs too small for 256 x 256 tiles.
+// Shared design points:
+//  * A K-contiguous operand tile sits in LDS as [rows][64] (128-byte rows), so
+//    an MFMA operand fragment is one ds_read_b128 per lane (8 consecutive k of
+//    one row); an N-contiguous one in gemm_kc_kernel as [64 k][128 n] halves,
+//    read with two ds_read_b64_tr_b16 per fragment.
+//  * Operands go from memory straight into LDS with buffer_load ... lds (16
+//    bytes per lane, no staging registers, no LDS write instructions).  Buffer
 //    descriptors return zeros for out-of-range chunks, which handles ragged
 //    sizes without branches.
-//  * Two LDS stages: the loads of K step kt+1 are issued right after the
-//    barrier that opens step kt, and land while step kt's MFMAs run.
-//  * 16-byte chunks are XOR-swizzled inside each 128-byte LDS row so that the
-//    rows one read instruction touches fall on distinct banks; the DMA loads
-//    apply the inverse permutation on the memory side, so each DMA still
-//    writes 1 KiB of contiguous LDS.
+//  * 16-byte chunks are XOR-swizzled within LDS rows so that the lanes of one
+//    read instruction fall on distinct banks; the DMA loads apply the inverse
+//    permutation on the memory side, so each DMA still writes 1 KiB of
+//    contiguous LDS.
 //  * The MFMA takes the B fragment as its first operand, so each lane ends with
 //    4 consecutive output columns of one row: epilogues store 8- or 16-byte
 //    vectors.
@@ -62,6 +61,7 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x8_t __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
 constexpr int GROUP_M = 8;
@@ -285,6 +285,81 @@ struct HalfDma {
   }
 };
 
+// The same for an N-contiguous operand (stored [K][ld], n contiguous): one half
+// of a K step is 64 k-rows x 128 n, kept in LDS as [64][128] (256-byte rows),
+// 16 KiB.  The 16-byte chunk holding n .. n+7 of k-row k sits at position
+// (n / 8) ^ (4 * (k % 4)) of the row (mc_off): a transposing fragment read
+// touches 4 consecutive k-rows of 32 columns per 32 lanes, which this spreads
+// over all 64 banks (unswizzled, the 4 rows, 256 bytes apart, hit the same
+// banks).  Instruction i of wave w fills k-rows 4*(4i + w) .. +3 (LDS bytes
+// (4i + w) * 1024 ..); lane q writes position q % 16 of k-row q / 16 and loads
+// the chunk placed there, which depends only on the lane since k % 4 = (q / 16)
+// % 4.  One instruction reads 4 k-rows x 256 bytes.
+__device__ __forceinline__ int mc_off(int k, int n) { return k * 256 + (((n >> 3) ^ (4 * (k & 3))) << 4) + (n & 7) * 2; }
+
+struct HalfDmaMC {
+  static constexpr int PER_WAVE = 4;
+  uint32_t lane_off;  // byte offset of the lane's chunk in instruction 0
+  int lane_k, lane_n;  // the chunk's k-row in instruction 0 and first n
+
+  __device__ __forceinline__ void init(int64_t ld, int w, int lane) {
+    lane_k = 4 * w + (lane >> 4);
+    lane_n = 8 * ((lane & 15) ^ (4 * ((lane >> 4) & 3)));
+    lane_off = (uint32_t)(((int64_t)lane_k * ld + lane_n) * 2);
+  }
+  // base: element (first k of the step, first n of the half).
+  __device__ __forceinline__ void issue(const uint16_t* base, int64_t ld, char* half, int n_left, int k_left,
+                                        int w, int lane) const {
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base);
+    const bool n_ok = lane_n < n_left;
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const bool ok = n_ok && (lane_k + 16 * i < k_left);
+      const uint32_t off = lane_off + (uint32_t)((int64_t)(16 * i) * ld * 2);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(half + (4 * i + w) * 1024), 16, ok ? off : OOB, 0, 0,
+                                               0);
+    }
+  }
+};
+
+// ds_read_b64_tr_b16 from LDS address `p`.  Issued through inline assembly:
+// the builtin makes the compiler wait for every vector-memory load in flight
+// (vmcnt(0)) before it, in case an LDS-DMA load targets the same bytes, which
+// would stall the load pipeline of this kernel on every memory phase.  Callers
+// read only bytes whose loads and writes have already been waited for and made
+// visible by a barrier, and wait for the results themselves (lgkmcnt(0))
+// before using them.
+typedef __attribute__((address_space(3))) char lds_char_t;
+__device__ __forceinline__ i16x4_t ds_read_tr(const char* p) {
+  i16x4_t v;
+  const uint32_t a = (uint32_t)(uintptr_t)(const lds_char_t*)p;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(a));
+  return v;
+}
+// The same, ordered after every earlier memory access of the calling code (for
+// reads of bytes that the same wave has just written with ordinary stores).
+__device__ __forceinline__ i16x4_t ds_read_tr_after_stores(const char* p) {
+  i16x4_t v;
+  const uint32_t a = (uint32_t)(uintptr_t)(const lds_char_t*)p;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(a) : "memory");
+  return v;
+}
+
+// MFMA B fragment of 32 columns (n0 .. n0+31, inside one 128-wide half) at
+// sub-step kk from an N-contiguous [64][128] half: lane l needs k = 16*kk +
+// 8*(l/32) .. +7 of column n0 + l%32.  ds_read_b64_tr_b16 reads, in each
+// 16-lane group, 4 k-rows x 16 columns (lane s: k-row s/4, columns 4*(s%4) ..
+// +3) and hands lane i the 4 k-values of column i; two such reads give 8.
+__device__ __forceinline__ bf16x8_t read_frag_mc(const char* half, int n0, int kk, int lane) {
+  const int g = lane >> 4, sl = lane & 15;
+  const int n = n0 + 16 * (g & 1) + 4 * (sl & 3);
+  const int k = 16 * kk + 8 * (g >> 1) + (sl >> 2);
+  const i16x4_t lo = ds_read_tr(half + mc_off(k, n));
+  const i16x4_t hi = ds_read_tr(half + mc_off(k + 4, n));
+  const i16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
 // Logical tile of workgroup `bid`: XCD-aware renumbering, then grouped order.
 __device__ __forceinline__ void tile_of(int bid, int nblocks, int tiles_m, int tiles_n, int& tm, int& tn,
                                         int& split) {
@@ -410,55 +485,37 @@ __device__ __forceinline__ void store_tile(const f32x16_t (&acc)[FM][FN], const 
             v2[e] = d.g;
           }
           if (ok) *reinterpret_cast<u16x8_t*>(reinterpret_cast<uint16_t*>(args.out) + o) = v1;
-          // Keep dP and G of this row in LDS, in place of its float32 values
-          // (every lane has read its float32 values above): dP in bytes
-          // [0, 128), G in [128, 256), 16-byte chunks swizzled by the row.
-          // Rows and columns outside the output hold values that no
-          // transposed store below reads.
-          *reinterpret_cast<u16x8_t*>(stage + r * ROW_B + ((cp ^ (r & 7)) << 4)) = v1;
-          *reinterpret_cast<u16x8_t*>(stage + r * ROW_B + 128 + ((cp ^ (r & 7)) << 4)) = v2;
+          // Keep G of this row in LDS, in place of its float32 values (every
+          // lane has read its float32 values above), in bytes [0, 128) of the
+          // row, 16-byte chunks swizzled by the row.  Rows and columns outside
+          // the output hold values that no transposed store below reads.
+          *reinterpret_cast<u16x8_t*>(stage + r * ROW_B + ((cp ^ (r & 7)) << 4)) = v2;
         }
       }
       if (EPI == EPI_DGELU) {
-        // Transposed stores G^T and dP^T: ds_read_b64_tr_b16 turns 4 rows x 16
-        // columns of a 16-lane group into one column per lane; two reads give 8
-        // consecutive rows, one 16-byte store into the transposed output.  Four
-        // of the eight steps are read at a time, then stored.
+        // Transposed store of G: ds_read_b64_tr_b16 turns 4 rows x 16 columns
+        // of a 16-lane group into one column per lane; two reads give 8
+        // consecutive rows, one 16-byte store into G^T.  All eight steps are
+        // read first, then stored.
         const int g = lane >> 4, j = lane & 15;
+        i16x4_t lo[8], hi[8];
 #pragma unroll
-        for (int batch = 0; batch < 2; ++batch) {
-          i16x4_t lo[4][2], hi[4][2];
+        for (int it = 0; it < 8; ++it) {
+          const int o0 = 16 * (it & 3), k0 = 8 * ((it >> 2) * 4 + g);
+          const int o = o0 + 4 * (j & 3), c = o >> 3, half = (o & 4) ? 8 : 0;
+          const int ka = k0 + (j >> 2), kb = ka + 4;
+          lo[it] = ds_read_tr_after_stores(stage + ka * ROW_B + ((c ^ (ka & 7)) << 4) + half);
+          hi[it] = ds_read_tr_after_stores(stage + kb * ROW_B + ((c ^ (kb & 7)) << 4) + half);
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the transposed reads above are complete
 #pragma unroll
-          for (int b4 = 0; b4 < 4; ++b4) {
-            const int it = 4 * batch + b4;
-            const int o0 = 16 * (it & 3), k0 = 8 * ((it >> 2) * 4 + g);
-            const int o = o0 + 4 * (j & 3), c = o >> 3, half = (o & 4) ? 8 : 0;
-            const int ka = k0 + (j >> 2), kb = ka + 4;
-#pragma unroll
-            for (int which = 0; which < 2; ++which) {  // 0: dP^T -> out3, 1: G^T -> out2
-              const int region = which * 128;
-              lo[b4][which] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                  (lds_i16x4_t*)(stage + ka * ROW_B + region + ((c ^ (ka & 7)) << 4) + half));
-              hi[b4][which] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                  (lds_i16x4_t*)(stage + kb * ROW_B + region + ((c ^ (kb & 7)) << 4) + half));
-            }
-          }
-#pragma unroll
-          for (int b4 = 0; b4 < 4; ++b4) {
-            const int it = 4 * batch + b4;
-            const int o0 = 16 * (it & 3), k0 = 8 * ((it >> 2) * 4 + g);
-            const int f = col_w + o0 + j, m = row_w + 64 * h + k0;
-            if (f < args.N && m < args.M) {
-#pragma unroll
-              for (int which = 0; which < 2; ++which) {
-                const u16x8_t v = {(uint16_t)lo[b4][which][0], (uint16_t)lo[b4][which][1],
-                                   (uint16_t)lo[b4][which][2], (uint16_t)lo[b4][which][3],
-                                   (uint16_t)hi[b4][which][0], (uint16_t)hi[b4][which][1],
-                                   (uint16_t)hi[b4][which][2], (uint16_t)hi[b4][which][3]};
-                uint16_t* dst = which ? args.out2 : args.out3;
-                *reinterpret_cast<u16x8_t*>(dst + (int64_t)f * args.ldt + m) = v;
-              }
-            }
+        for (int it = 0; it < 8; ++it) {
+          const int o0 = 16 * (it & 3), k0 = 8 * ((it >> 2) * 4 + g);
+          const int f = col_w + o0 + j, m = row_w + 64 * h + k0;
+          if (f < args.N && m < args.M) {
+            const u16x8_t v = {(uint16_t)lo[it][0], (uint16_t)lo[it][1], (uint16_t)lo[it][2], (uint16_t)lo[it][3],
+                               (uint16_t)hi[it][0], (uint16_t)hi[it][1], (uint16_t)hi[it][2], (uint16_t)hi[it][3]};
+            *reinterpret_cast<u16x8_t*>(args.out2 + (int64_t)f * args.ldt + m) = v;
           }
         }
       }
@@ -651,7 +708,7 @@ gemm_kernel(GemmArgs args) {
 // Both groups execute the same number of barriers: group 1's extra barrier at
 // the start is matched by skipping the barrier after its last compute phase.
 // Group 0 stages its epilogue in LDS while group 1 still computes.
-template <int EPI>
+template <int LB, int EPI>
 __global__ void __launch_bounds__(512)
 gemm_kc_kernel(GemmArgs args) {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -680,15 +737,22 @@ gemm_kc_kernel(GemmArgs args) {
   const int nk = (k_end - k_begin + BK - 1) / BK;
 
   HalfDma dma_a, dma_b;
+  HalfDmaMC dma_bm;
   dma_a.init(args.lda, wg, lane);
-  dma_b.init(args.ldb, wg, lane);
+  if (LB == KC) dma_b.init(args.ldb, wg, lane);
+  else dma_bm.init(args.ldb, wg, lane);
   // Issue this group's share of one operand half of K step `step`:
   // is_b selects B (else A), hi the rows 128-255 (else 0-127).
   auto issue = [&](bool is_b, int hi, int step, int b_buf) {
     const int k = k_begin + step * BK;
     if (is_b) {
-      dma_b.issue(args.b + (int64_t)(n0 + 128 * hi) * args.ldb + k, args.ldb, smem + B_BASE + b_buf * BUF_BYTES + hi * HALF_BYTES,
-                  args.N - n0 - 128 * hi, k_end - k, wg, lane);
+      char* dst = smem + B_BASE + b_buf * BUF_BYTES + hi * HALF_BYTES;
+      if (LB == KC)
+        dma_b.issue(args.b + (int64_t)(n0 + 128 * hi) * args.ldb + k, args.ldb, dst, args.N - n0 - 128 * hi, k_end - k,
+                    wg, lane);
+      else
+        dma_bm.issue(args.b + (int64_t)k * args.ldb + n0 + 128 * hi, args.ldb, dst, args.N - n0 - 128 * hi, k_end - k,
+                     wg, lane);
     } else {
       dma_a.issue(args.a + (int64_t)(m0 + 128 * hi) * args.lda + k, args.lda, smem + (step & 1) * BUF_BYTES + hi * HALF_BYTES,
                   args.M - m0 - 128 * hi, k_end - k, wg, lane);
@@ -713,7 +777,14 @@ gemm_kc_kernel(GemmArgs args) {
 #pragma unroll
       for (int i = 0; i < FM; ++i) fa[s2][i] = read_frag(ta, wm * WM + 32 * i, HSUB * h + s2, lane);
 #pragma unroll
-      for (int j = 0; j < FN; ++j) fb[s2][j] = read_frag(tb, wn * WN + 32 * j, HSUB * h + s2, lane);
+      for (int j = 0; j < FN; ++j) {
+        if (LB == KC) {
+          fb[s2][j] = read_frag(tb, wn * WN + 32 * j, HSUB * h + s2, lane);
+        } else {
+          const int n0f = wn * WN + 32 * j;  // the wave's columns lie in one 128-wide half
+          fb[s2][j] = read_frag_mc(tb + (n0f >> 7) * HALF_BYTES, n0f & 127, HSUB * h + s2, lane);
+        }
+      }
     }
   };
   auto mfma_half = [&]() {
@@ -819,8 +890,8 @@ namespace {
 template <int BM, int BN, int WM_, int WN_, int LA, int LB, int EPI>
 hipError_t launch_one(const GemmArgs& a, int splits, hipStream_t s) {
   const int blocks = a.tiles_m * a.tiles_n * splits;
-  if constexpr (BM == 256 && LA == KC && LB == KC)
-    hipLaunchKernelGGL((kern::gemm_kc_kernel<EPI>), dim3(blocks), dim3(512), 0, s, a);
+  if constexpr (BM == 256 && LA == KC)
+    hipLaunchKernelGGL((kern::gemm_kc_kernel<LB, EPI>), dim3(blocks), dim3(512), 0, s, a);
   else
     hipLaunchKernelGGL((kern::gemm_kernel<BM, BN, WM_, WN_, LA, LB, EPI>), dim3(blocks), dim3(64 * WM_ * WN_), 0, s,
                        a);

@@ -8,7 +8,7 @@
 //    that product's epilogue (float32 store, GeLU or bf16 store), so that a
 //    product split along K ends exactly like an unsplit one.
 //  * splitk_dgelu_kernel: the same for the dGeLU epilogue, which also writes G
-//    and dP transposed; it works on 64 x 64 tiles and transposes through LDS.
+//    transposed; it works on 64 x 64 tiles and transposes through LDS.
 //
 //  * transpose_kernel: out[c][r] = in[r][c] for bf16 matrices, so that the
 //    weight-gradient products read both operands K-contiguous.
@@ -84,7 +84,6 @@ struct SplitDGeluArgs {
   int M, N;
   uint16_t* dp;         // [M][N]
   uint16_t* g_t;        // [N][M]
-  uint16_t* dp_t;       // [N][M]
   const uint16_t* p;    // [M][N] pre-activation
 };
 
@@ -92,9 +91,9 @@ typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
 
 // One 64 x 64 tile per block of 256 threads.  Thread t finishes row t/4,
 // columns 16*(t%4) .. +15 (two 8-column vectors), then, after a barrier, writes
-// 16 consecutive rows of one column of the transposed outputs.
+// 16 consecutive rows of one column of the transposed output.
 __global__ void __launch_bounds__(256) splitk_dgelu_kernel(SplitDGeluArgs a) {
-  __shared__ uint16_t s_dp[64][72], s_g[64][72];  // 8 elements of padding per row
+  __shared__ uint16_t s_g[64][72];  // 8 elements of padding per row
   const int tiles_n = (a.N + 63) / 64;
   const int m0 = (blockIdx.x / tiles_n) * 64, n0 = (blockIdx.x % tiles_n) * 64;
   const int t = threadIdx.x;
@@ -119,7 +118,6 @@ __global__ void __launch_bounds__(256) splitk_dgelu_kernel(SplitDGeluArgs a) {
       for (int e = 0; e < 8; ++e) {
         const DGelu d = epi_dgelu(x[e], pb[e]);
         dp[e] = d.dp;
-        s_dp[r][c + e] = d.dp;
         s_g[r][c + e] = d.g;
       }
       *reinterpret_cast<u16x8_t*>(a.dp + o) = dp;
@@ -127,21 +125,17 @@ __global__ void __launch_bounds__(256) splitk_dgelu_kernel(SplitDGeluArgs a) {
   }
   __syncthreads();
   {
-    const int c = t >> 2, col = n0 + c;   // a column of the tile = a row of the transposed outputs
+    const int c = t >> 2, col = n0 + c;   // a column of the tile = a row of the transposed output
     const int r0 = 16 * (t & 3), row = m0 + r0;
     if (col < a.N) {
 #pragma unroll
       for (int v = 0; v < 2; ++v) {
         if (row + 8 * v >= a.M) continue;  // M % 8 == 0
-        u16x8_t gv, dv;
+        u16x8_t gv;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          gv[e] = s_g[r0 + 8 * v + e][c];
-          dv[e] = s_dp[r0 + 8 * v + e][c];
-        }
+        for (int e = 0; e < 8; ++e) gv[e] = s_g[r0 + 8 * v + e][c];
         const int64_t o = (int64_t)col * a.M + row + 8 * v;
         *reinterpret_cast<u16x8_t*>(a.g_t + o) = gv;
-        *reinterpret_cast<u16x8_t*>(a.dp_t + o) = dv;
       }
     }
   }
@@ -222,11 +216,11 @@ hipError_t launch_sum(const float* const* parts, int n_parts, float* out, int64_
 }
 
 hipError_t launch_splitk_epilogue(Epi epi, const float* part, int splits, int64_t M, int64_t N, void* out,
-                                  uint16_t* out2, uint16_t* out3, const uint16_t* aux, hipStream_t stream) {
+                                  uint16_t* out2, const uint16_t* aux, hipStream_t stream) {
   const int64_t n = M * N;
   if (!part || splits < 1 || (n & 3)) return hipErrorInvalidValue;
   if (epi == EPI_DGELU) {
-    SplitDGeluArgs a{part, splits, (int)M, (int)N, static_cast<uint16_t*>(out), out2, out3, aux};
+    SplitDGeluArgs a{part, splits, (int)M, (int)N, static_cast<uint16_t*>(out), out2, aux};
     const int64_t tiles = ((M + 63) / 64) * ((N + 63) / 64);
     hipLaunchKernelGGL(splitk_dgelu_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, a);
     return hipGetLastError();

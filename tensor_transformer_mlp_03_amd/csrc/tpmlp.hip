@@ -96,13 +96,14 @@ size_t part_bytes(const GemmPlan& p, int64_t M, int64_t N) {
 }
 
 // The forward products read A_i and B_i N-contiguous.  Transposing them first
-// (4*H*F bytes of memory traffic at about 5.5 TB/s) lets the products run on
-// the K-contiguous kernel, measured at about 1.2 PFLOP/s against about 1.05 for
-// the register-transposing one.  On two products of 2*M*H*F flops that saves
-// about M*H*F*4.8e-16 s against H*F*7.3e-13 s for the transposes; they are made
-// only when the saving is 1.5 times the cost, which covers the rates' spread
-// over shapes (the long-context chunk, M = 32768, qualifies; M = 2048 does not).
-constexpr double RATE_KC = 1.2e15, RATE_MC = 1.05e15, TRANSPOSE_BW = 5.5e12, TRANSPOSE_MARGIN = 1.5;
+// (4*H*F bytes of memory traffic at about 5.5 TB/s) lets the products run with
+// both operands K-contiguous, measured at about 1.2 PFLOP/s against about 1.14
+// with B read through transposing LDS loads.  On two products of 2*M*H*F flops
+// that saves about M*H*F*1.75e-16 s against H*F*7.3e-13 s for the transposes;
+// they are made only when the saving is 1.5 times the cost, which covers the
+// rates' spread over shapes (M above about 6000: the long-context chunk,
+// M = 32768, qualifies; M = 2048 and 4096 do not).
+constexpr double RATE_KC = 1.2e15, RATE_MC = 1.14e15, TRANSPOSE_BW = 5.5e12, TRANSPOSE_MARGIN = 1.5;
 
 bool transpose_weights(int64_t M, int64_t H, int64_t F) {
   const double saved = 2.0 * 2.0 * double(M) * H * F * (1.0 / RATE_MC - 1.0 / RATE_KC);
@@ -133,7 +134,7 @@ FwdPlan plan_fwd(int64_t M, int64_t H, int64_t F) {
 struct BwdPlan {
   GemmPlan g0, g1, gdb, gda, gdx;
   bool wt;  // the recompute product reads A_i^T from the workspace
-  size_t off_Xt, off_dZt, off_At, off_P, off_Gt, off_dP, off_dPt, off_part, total;
+  size_t off_Xt, off_dZt, off_At, off_P, off_Gt, off_dP, off_part, total;
 };
 
 BwdPlan plan_bwd(int64_t M, int64_t H, int64_t F, bool recompute) {
@@ -152,8 +153,7 @@ BwdPlan plan_bwd(int64_t M, int64_t H, int64_t F, bool recompute) {
   p.off_P = p.off_At + (p.wt ? align_up(size_t(H) * F * 2) : 0);
   p.off_Gt = p.off_P + (recompute ? mf : 0);
   p.off_dP = p.off_Gt + mf;
-  p.off_dPt = p.off_dP + mf;
-  p.off_part = p.off_dPt + mf;
+  p.off_part = p.off_dP + mf;
   size_t part = recompute ? part_bytes(p.g0, M, F) : 0;
   part = std::max({part, part_bytes(p.g1, M, F), part_bytes(p.gdb, F, H), part_bytes(p.gda, H, F),
                    part_bytes(p.gdx, M, H)});
@@ -300,11 +300,10 @@ GemmArgs gemm_args(const void* a, int64_t lda, const void* b, int64_t ldb, int64
 // float32 and the reduction applies the epilogue.
 hipError_t run_gemm(int kind, Layout la, Layout lb, Epi epi, const void* a, int64_t lda, const void* b,
                     int64_t ldb, int64_t M, int64_t N, int64_t K, const GemmPlan& p, void* out, uint16_t* out2,
-                    uint16_t* out3, const uint16_t* aux, float* part, hipStream_t s) {
+                    const uint16_t* aux, float* part, hipStream_t s) {
   if (p.splits == 1) {
     GemmArgs g = gemm_args(a, lda, b, ldb, M, N, K, p, out, N);
     g.out2 = out2;
-    g.out3 = out3;
     g.aux = aux;
     g.ldt = M;
     return timed(kind, s, [&] { return launch_gemm(p.tile, la, lb, epi, g, 1, s); });
@@ -313,7 +312,7 @@ hipError_t run_gemm(int kind, Layout la, Layout lb, Epi epi, const void* a, int6
   hipError_t e = timed(kind, s, [&] { return launch_gemm(p.tile, la, lb, EPI_F32, g, p.splits, s); });
   if (e != hipSuccess) return e;
   return timed(TPMLP_K_SPLITK_REDUCE, s,
-               [&] { return launch_splitk_epilogue(epi, part, p.splits, M, N, out, out2, out3, aux, s); });
+               [&] { return launch_splitk_epilogue(epi, part, p.splits, M, N, out, out2, aux, s); });
 }
 
 char* ws_at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
@@ -333,19 +332,19 @@ hipError_t enqueue_fwd(const tpmlp_bf16* X, const tpmlp_bf16* A, const tpmlp_bf1
     e = timed(TPMLP_K_TRANSPOSE, s, [&] { return launch_transpose(B, F, H, Bt, s); });
     if (e != hipSuccess) return e;
     // P_i = X A_i; G_i = GeLU(P_i)      X: [M][H], A_i^T: [F][H] (both K-contig)
-    e = run_gemm(TPMLP_K_FWD_GEMM1_GELU, KC, KC, EPI_GELU, X, H, At, H, M, F, H, p.g1, G, P_save, nullptr,
+    e = run_gemm(TPMLP_K_FWD_GEMM1_GELU, KC, KC, EPI_GELU, X, H, At, H, M, F, H, p.g1, G, P_save,
                  nullptr, part, s);
     if (e != hipSuccess) return e;
     // Z_i = G_i B_i                    G_i: [M][F], B_i^T: [H][F] (both K-contig)
-    return run_gemm(TPMLP_K_FWD_GEMM2, KC, KC, EPI_F32, G, F, Bt, F, M, H, F, p.g2, Z, nullptr, nullptr, nullptr,
+    return run_gemm(TPMLP_K_FWD_GEMM2, KC, KC, EPI_F32, G, F, Bt, F, M, H, F, p.g2, Z, nullptr, nullptr,
                     part, s);
   }
   // P_i = X A_i; G_i = GeLU(P_i)        X: [M][H] (K-contig), A_i: [H][F] (N-contig)
-  e = run_gemm(TPMLP_K_FWD_GEMM1_GELU, KC, MC, EPI_GELU, X, H, A, F, M, F, H, p.g1, G, P_save, nullptr, nullptr,
+  e = run_gemm(TPMLP_K_FWD_GEMM1_GELU, KC, MC, EPI_GELU, X, H, A, F, M, F, H, p.g1, G, P_save, nullptr,
                part, s);
   if (e != hipSuccess) return e;
   // Z_i = G_i B_i                      G_i: [M][F] (K-contig), B_i: [F][H] (N-contig)
-  return run_gemm(TPMLP_K_FWD_GEMM2, KC, MC, EPI_F32, G, F, B, H, M, H, F, p.g2, Z, nullptr, nullptr, nullptr,
+  return run_gemm(TPMLP_K_FWD_GEMM2, KC, MC, EPI_F32, G, F, B, H, M, H, F, p.g2, Z, nullptr, nullptr,
                   part, s);
 }
 
@@ -372,7 +371,6 @@ hipError_t enqueue_bwd(const tpmlp_bf16* dZ, const tpmlp_bf16* X, const tpmlp_bf
   const uint16_t* dZt = reinterpret_cast<const uint16_t*>(ws_at(ws, p.off_dZt));
   uint16_t* Gt = reinterpret_cast<uint16_t*>(ws_at(ws, p.off_Gt));
   uint16_t* dP = reinterpret_cast<uint16_t*>(ws_at(ws, p.off_dP));
-  uint16_t* dPt = reinterpret_cast<uint16_t*>(ws_at(ws, p.off_dPt));
   float* part = reinterpret_cast<float*>(ws_at(ws, p.off_part));
   const uint16_t* P = P_saved;
   hipError_t e;
@@ -384,26 +382,26 @@ hipError_t enqueue_bwd(const tpmlp_bf16* dZ, const tpmlp_bf16* X, const tpmlp_bf
       e = timed(TPMLP_K_TRANSPOSE, s, [&] { return launch_transpose(A, H, F, At, s); });
       if (e != hipSuccess) return e;
       e = run_gemm(TPMLP_K_BWD_RECOMPUTE, KC, KC, EPI_BF16, X, H, At, H, M, F, H, p.g0, Pw, nullptr, nullptr,
-                   nullptr, part, s);
+                   part, s);
     } else {
       e = run_gemm(TPMLP_K_BWD_RECOMPUTE, KC, MC, EPI_BF16, X, H, A, F, M, F, H, p.g0, Pw, nullptr, nullptr,
-                   nullptr, part, s);
+                   part, s);
     }
     if (e != hipSuccess) return e;
     P = Pw;
   }
-  // dG_i = dZ B_i^T; dP_i = dG_i GeLU'(P_i) -> dP_i [M][F] and dP_i^T [F][M]; G_i^T = GeLU(P_i)^T [F][M]
+  // dG_i = dZ B_i^T; dP_i = dG_i GeLU'(P_i) -> dP_i [M][F]; G_i^T = GeLU(P_i)^T [F][M]
   //   dZ: [M][H] (K-contig), B_i: [F][H] = [N][K] (K-contig)
-  e = run_gemm(TPMLP_K_BWD_DGELU, KC, KC, EPI_DGELU, dZ, H, B, H, M, F, H, p.g1, dP, Gt, dPt, P, part, s);
+  e = run_gemm(TPMLP_K_BWD_DGELU, KC, KC, EPI_DGELU, dZ, H, B, H, M, F, H, p.g1, dP, Gt, P, part, s);
   if (e != hipSuccess) return e;
   // dB_i = G_i^T dZ    G_i^T: [F][M] = [M'][K], dZ^T: [H][M] = [N'][K] (both K-contig)
-  e = run_gemm(TPMLP_K_BWD_DB, KC, KC, EPI_F32, Gt, M, dZt, M, F, H, M, p.gdb, dB, nullptr, nullptr, nullptr, part, s);
+  e = run_gemm(TPMLP_K_BWD_DB, KC, KC, EPI_F32, Gt, M, dZt, M, F, H, M, p.gdb, dB, nullptr, nullptr, part, s);
   if (e != hipSuccess) return e;
-  // dA_i = X^T dP_i    X^T: [H][M] = [M'][K], dP_i^T: [F][M] = [N'][K] (both K-contig)
-  e = run_gemm(TPMLP_K_BWD_DA, KC, KC, EPI_F32, Xt, M, dPt, M, H, F, M, p.gda, dA, nullptr, nullptr, nullptr, part, s);
+  // dA_i = X^T dP_i    X^T: [H][M] = [M'][K] (K-contig), dP_i: [M][F] = [K][N'] (N'-contig)
+  e = run_gemm(TPMLP_K_BWD_DA, KC, MC, EPI_F32, Xt, M, dP, F, H, F, M, p.gda, dA, nullptr, nullptr, part, s);
   if (e != hipSuccess) return e;
   // dX_i = dP_i A_i^T  dP_i: [M][F] (K-contig), A_i: [H][F] = [N][K] (K-contig)
-  return run_gemm(TPMLP_K_BWD_DX, KC, KC, EPI_F32, dP, F, A, F, M, H, F, p.gdx, dX, nullptr, nullptr, nullptr, part,
+  return run_gemm(TPMLP_K_BWD_DX, KC, KC, EPI_F32, dP, F, A, F, M, H, F, p.gdx, dX, nullptr, nullptr, part,
                   s);
 }
 

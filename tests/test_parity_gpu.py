@@ -62,8 +62,10 @@ SMALL = [
     (1032, 1040, 1048, 1, True),
     # M large enough that the forward (and the recompute) transpose the weights
     # first and run every product K-contiguous
-    (4104, 264, 392, 2, False),
-    (4104, 136, 520, 2, True),
+    (8200, 264, 392, 2, False),
+    (8200, 136, 520, 2, True),
+    # enough output tiles for 256 x 256 tiles, with the weights read N-contiguous
+    (4104, 1032, 2056, 2, False),
 ]
 
 
