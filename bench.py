@@ -83,9 +83,9 @@ def gemm_alg_bytes(w, recompute):
         "fwd_gemm1_gelu": 2 * (M * H + H * F) + 2 * M * F * (1 if recompute else 2),  # X, A_i -> G (+P)
         "fwd_gemm2": 2 * (M * F + F * H) + 4 * M * H,                                # G, B_i -> Z_i
         "bwd_recompute": 2 * (M * H + H * F) + 2 * M * F,                             # X, A_i -> P
-        "bwd_dgelu": 2 * (M * H + F * H + M * F) + 6 * M * F,                         # dZ, B_i, P -> dP, dP^T, G^T
+        "bwd_dgelu": 2 * (M * H + F * H + M * F) + 4 * M * F,                         # dZ, B_i, P -> dP, G^T
         "bwd_dB": 2 * (M * F + M * H) + 4 * F * H,                                    # G^T, dZ^T -> dB_i
-        "bwd_dA": 2 * (M * H + M * F) + 4 * H * F,                                    # X^T, dP^T -> dA_i
+        "bwd_dA": 2 * (M * H + M * F) + 4 * H * F,                                    # X^T, dP -> dA_i
         "bwd_dX": 2 * (M * F + H * F) + 4 * M * H,                                    # dP, A_i -> dX_i
         "transpose": 4 * M * H,                                                       # X -> X^T, dZ -> dZ^T
     }
@@ -178,6 +178,12 @@ def summarize(d, config):
         a["fetch"] += f["counters"]["FETCH_SIZE"] * 1024 * f_scale
         a["write"] += wr["counters"]["WRITE_SIZE"] * 1024 * w_scale
     alg = gemm_alg_bytes(w, w.recompute)
+    if "transpose" in agg:
+        # A backward step transposes X and dZ ([M,H]) once each; every further launch
+        # is a weight transpose ([H,F_i] or [F_i,H]).  Per launch: the step's average.
+        n_t, n_x = agg["transpose"]["n"], (2 if w.backward else 0)
+        alg["transpose"] = (n_x * 4 * w.M * w.H + (n_t - n_x) * 4 * w.H * w.F_i) / n_t
+    alg["shard_sum"] = (w.t + 1) * w.M * w.H * 4  # t float32 partials in, their sum out
     os.makedirs(PROFILES, exist_ok=True)
     with open(os.path.join(PROFILES, f"{w.name}_kernels.md"), "w") as f:
         f.write(f"# Kernel times, {w.name} (M={w.M}, H={w.H}, F_i={w.F_i}, t={w.t})\n\n")

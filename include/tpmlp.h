@@ -89,8 +89,9 @@ tpmlp_status tpmlp_fwd(const tpmlp_bf16* X, const tpmlp_bf16* A_i, const tpmlp_b
 
 /* Workspace bytes that tpmlp_bwd needs; `recompute` is 1 when P_saved will be
  * NULL.  0 if the shape is invalid.  The workspace holds the bf16 intermediates
- * [M,F_i] (dP_i, dP_i^T, G_i^T, and P_i when recomputed), the transposes X^T and
- * dZ^T [H,M] in bf16, and float32 split-K slices. */
+ * [M,F_i] (dP_i, G_i^T, and P_i when recomputed), the transposes X^T and dZ^T
+ * [H,M] in bf16, A_i^T [F_i,H] in bf16 when the shape gains from it, and float32
+ * split-K slices. */
 size_t tpmlp_bwd_workspace_bytes(int64_t M, int64_t H, int64_t F_i, int recompute);
 
 /* Rank i's backward, given the output gradient dZ[M,H] (bf16), which every rank
