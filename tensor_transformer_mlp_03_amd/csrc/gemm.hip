@@ -270,18 +270,20 @@ struct HalfDma {
       lane_off[par] = (uint32_t)(((int64_t)(lane >> 3) * ld + 8 * c) * 2);
     }
   }
-  // base: element (first row of the half, first k of the step).
+  // Instruction i of the wave's share; base: element (first row of the half,
+  // first k of the step).
+  __device__ __forceinline__ void issue_one(const uint16_t* base, int64_t ld, char* half, int rows_left, int k_left,
+                                            int w, int lane, int i) const {
+    const int r0 = 8 * (4 * i + w);
+    const bool ok = (kc[i & 1] < k_left) && (r0 + (lane >> 3) < rows_left);
+    const uint32_t off = lane_off[i & 1] + (uint32_t)((int64_t)r0 * ld * 2);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(base), (lds_void_t*)(half + (4 * i + w) * 1024), 16,
+                                             ok ? off : OOB, 0, 0, 0);
+  }
   __device__ __forceinline__ void issue(const uint16_t* base, int64_t ld, char* half, int rows_left, int k_left,
                                         int w, int lane) const {
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base);
 #pragma unroll
-    for (int i = 0; i < PER_WAVE; ++i) {
-      const int r0 = 8 * (4 * i + w);
-      const bool ok = (kc[i & 1] < k_left) && (r0 + (lane >> 3) < rows_left);
-      const uint32_t off = lane_off[i & 1] + (uint32_t)((int64_t)r0 * ld * 2);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(half + (4 * i + w) * 1024), 16, ok ? off : OOB, 0, 0,
-                                               0);
-    }
+    for (int i = 0; i < PER_WAVE; ++i) issue_one(base, ld, half, rows_left, k_left, w, lane, i);
   }
 };
 
@@ -307,18 +309,19 @@ struct HalfDmaMC {
     lane_n = 8 * ((lane & 15) ^ (4 * ((lane >> 4) & 3)));
     lane_off = (uint32_t)(((int64_t)lane_k * ld + lane_n) * 2);
   }
-  // base: element (first k of the step, first n of the half).
+  // Instruction i of the wave's share; base: element (first k of the step,
+  // first n of the half).
+  __device__ __forceinline__ void issue_one(const uint16_t* base, int64_t ld, char* half, int n_left, int k_left,
+                                            int w, int lane, int i) const {
+    const bool ok = lane_n < n_left && (lane_k + 16 * i < k_left);
+    const uint32_t off = lane_off + (uint32_t)((int64_t)(16 * i) * ld * 2);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(base), (lds_void_t*)(half + (4 * i + w) * 1024), 16,
+                                             ok ? off : OOB, 0, 0, 0);
+  }
   __device__ __forceinline__ void issue(const uint16_t* base, int64_t ld, char* half, int n_left, int k_left,
                                         int w, int lane) const {
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base);
-    const bool n_ok = lane_n < n_left;
 #pragma unroll
-    for (int i = 0; i < PER_WAVE; ++i) {
-      const bool ok = n_ok && (lane_k + 16 * i < k_left);
-      const uint32_t off = lane_off + (uint32_t)((int64_t)(16 * i) * ld * 2);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(half + (4 * i + w) * 1024), 16, ok ? off : OOB, 0, 0,
-                                               0);
-    }
+    for (int i = 0; i < PER_WAVE; ++i) issue_one(base, ld, half, n_left, k_left, w, lane, i);
   }
 };
 
@@ -708,6 +711,22 @@ gemm_kernel(GemmArgs args) {
 // Both groups execute the same number of barriers: group 1's extra barrier at
 // the start is matched by skipping the barrier after its last compute phase.
 // Group 0 stages its epilogue in LDS while group 1 still computes.
+//
+// L2 prefetch.  The 32 tiles that run together on one XCD form a block 8
+// tiles tall and 4 wide (tile_of), and run at about the same pace, so the
+// first of them to load a K slice of a shared operand panel waits for the
+// fabric and the others wait for that same miss.  Four phases (a batch's
+// latency budget) are not always enough.  So in phase 4k waves 0-2 of group 0
+// touch, one 4-byte word per 64-byte piece, this tile's share of K step
+// k+4: A rows 64 (tn % 4) .. +63 (waves 0 and 1) and 1/8 of B, selected by
+// tm % 8 (wave 2).  Together the 32 tiles cover both slices, and the DMAs for
+// step k+4, issued from phase 4k+9 on, find them in L2.  The touch is itself an
+// LDS DMA (a load into a register would need one kept free): it lands in the
+// wave's own first 256 bytes of the B rows 128-255 half that the same wave
+// refills from memory in phase 4k+2.  A wave's loads complete in issue order,
+// so the real data lands last, and waiting for that refill also waits for the
+// touch.  The touch is only waited for two memory phases later than a batch
+// of its own phase would be.
 template <int LB, int EPI>
 __global__ void __launch_bounds__(512)
 gemm_kc_kernel(GemmArgs args) {
@@ -759,6 +778,47 @@ gemm_kc_kernel(GemmArgs args) {
     }
   };
 
+  // Group 0's L2 touch of K step `step` < nk (see above): one load per wave,
+  // into the wave's first 256 bytes of B buffer b_buf's rows 128-255, which the
+  // wave refills later.  The lane's piece: waves 0 and 1, A rows
+  // 64 (tn % 4) + 32 wg + lane / 2; waves 2 and 3 (lanes 0-31), B rows
+  // 32 (tm % 8) + 16 (wg - 2) + lane / 2 (K-contiguous B) or k-rows
+  // 8 (tm % 8) + 4 (wg - 2) + lane / 8 (N-contiguous B, 512 bytes per k-row).
+  // Lanes outside the operand load nothing.
+  const uint16_t* pf_base;  // the wave's operand at (tile row 0 or k-row 0, k_begin)
+  int64_t pf_step;          // elements per K step
+  uint32_t pf_off;          // the lane's piece, in bytes from pf_base
+  int pf_k;                 // k_end must reach at least step k + pf_k
+  bool pf_ok;               // the piece's row or column exists
+  if (wg < 2) {
+    const int r = 64 * (tn & 3) + 32 * wg + (lane >> 1), kp = 32 * (lane & 1);
+    pf_base = args.a + (int64_t)m0 * args.lda + k_begin;
+    pf_step = BK;
+    pf_off = (uint32_t)(((int64_t)r * args.lda + kp) * 2);
+    pf_k = kp + 2;
+    pf_ok = m0 + r < args.M;
+  } else if (LB == KC) {
+    const int r = 32 * (tm & 7) + 16 * (wg - 2) + ((lane & 31) >> 1), kp = 32 * (lane & 1);
+    pf_base = args.b + (int64_t)n0 * args.ldb + k_begin;
+    pf_step = BK;
+    pf_off = (uint32_t)(((int64_t)r * args.ldb + kp) * 2);
+    pf_k = kp + 2;
+    pf_ok = lane < 32 && n0 + r < args.N;
+  } else {
+    const int kr = 8 * (tm & 7) + 4 * (wg - 2) + ((lane & 31) >> 3), np = 32 * (lane & 7);
+    pf_base = args.b + (int64_t)k_begin * args.ldb + n0;
+    pf_step = (int64_t)BK * args.ldb;
+    pf_off = (uint32_t)(((int64_t)kr * args.ldb + np) * 2);
+    pf_k = kr + 1;
+    pf_ok = lane < 32 && n0 + np + 2 <= args.N;
+  }
+  auto prefetch = [&](int step, int b_buf) {
+    const bool ok = pf_ok && k_begin + step * BK + pf_k <= k_end;
+    char* dst = smem + B_BASE + b_buf * BUF_BYTES + HALF_BYTES + wg * 1024;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(pf_base + step * pf_step), (lds_void_t*)dst, 4,
+                                             ok ? pf_off : OOB, 0, 0, 0);
+  };
+
   f32x16_t acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -803,18 +863,26 @@ gemm_kc_kernel(GemmArgs args) {
     __builtin_amdgcn_sched_barrier(0);
   };
   auto lds_wait = [&]() { __builtin_amdgcn_s_waitcnt(0xC07F); };  // lgkmcnt(0)
-  // End of a memory phase: at most the batches of this and the previous memory
-  // phase (HalfDma::PER_WAVE loads each) may still be in flight.
-  int prev_issued = 0;
-  auto end_memory_phase = [&](int cur_issued) {
-    static_assert(HalfDma::PER_WAVE == 4, "vmcnt immediates below assume 4 loads per batch");
-    const int newer = prev_issued + cur_issued;
-    if (newer >= 2) __builtin_amdgcn_s_waitcnt(0x0F78);       // vmcnt(8)
-    else if (newer == 1) __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
-    else __builtin_amdgcn_s_waitcnt(0x0F70);                  // vmcnt(0)
-    prev_issued = cur_issued;
+  // End of a memory phase: the batch of the wave's memory phase before the
+  // previous one (and everything older) must have landed; NEWER is the number
+  // of the wave's loads issued after that batch, which may still be in flight.
+  // A larger count than issued is safe where everything older has landed.
+  static_assert(HalfDma::PER_WAVE == 4 && HalfDmaMC::PER_WAVE == 4, "4 loads per batch");
+  auto end_memory_phase = [&](auto newer) {
+    constexpr int N = decltype(newer)::value;
+    static_assert(N >= 0 && N < 16, "vmcnt immediate");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | N);
     lds_wait();
     sync();
+  };
+  // The same with a count known only at run time (the last K steps).
+  auto end_memory_phase_rt = [&](int newer) {
+    if (newer >= 9) end_memory_phase(std::integral_constant<int, 9>{});
+    else if (newer >= 8) end_memory_phase(std::integral_constant<int, 8>{});
+    else if (newer >= 5) end_memory_phase(std::integral_constant<int, 5>{});
+    else if (newer >= 4) end_memory_phase(std::integral_constant<int, 4>{});
+    else if (newer >= 1) end_memory_phase(std::integral_constant<int, 1>{});
+    else end_memory_phase(std::integral_constant<int, 0>{});
   };
 
   if (nk > 0) {
@@ -823,6 +891,10 @@ gemm_kc_kernel(GemmArgs args) {
       issue(false, 0, 0, 0);
       issue(false, 1, 0, 0);
       if (nk > 1) issue(false, 0, 1, 0);
+      if (nk > 3) {  // steps 2 and 3 into B buffer 2, refilled in phase 2
+        prefetch(2, 2);
+        prefetch(3, 2);
+      }
     } else {
       issue(true, 0, 0, 0);
       issue(true, 1, 0, 0);
@@ -834,43 +906,83 @@ gemm_kc_kernel(GemmArgs args) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     sync();
     int bb = 0;  // B buffer of step k: k % 3
+    // The loops are split at the last step with a full set of loads, so the
+    // waits of the steady part are immediates.
+    using C4 = std::integral_constant<int, 4>;
+    using C8 = std::integral_constant<int, 8>;
+    using C9 = std::integral_constant<int, 9>;
+    using C10 = std::integral_constant<int, 10>;
     if (grp == 0) {
-      for (int k = 0; k < nk; ++k) {
+      int k = 0;
+      for (; k + 4 < nk; ++k) {
         const int bb2 = bb == 0 ? 2 : bb - 1;  // (k + 2) % 3
-        // phase 4k: A rows 128-255 of step k+1
-        const bool i0 = k + 1 < nk;
-        if (i0) issue(false, 1, k + 1, 0);
+        // phase 4k: A rows 128-255 of step k+1, then the touch of step k+4, whose
+        // target (B rows 128-255 of step k+2) this wave refills in phase 4k+2.
+        // In flight after A rows 128-255 of step k: the touch of phase 4k-4, the
+        // batch of 4k-2 and this phase's batch and touch.
+        issue(false, 1, k + 1, 0);
+        prefetch(k + 4, bb2);
         read_half(k, bb, 0);
-        end_memory_phase(i0);
+        end_memory_phase(C10{});
         mfma_half();
         sync();
         // phase 4k+2: B rows 128-255 of step k+2
-        const bool i1 = k + 2 < nk;
-        if (i1) issue(true, 1, k + 2, bb2);
+        issue(true, 1, k + 2, bb2);
         read_half(k, bb, 1);
-        end_memory_phase(i1);
+        end_memory_phase(C9{});
         mfma_half();
         sync();
         bb = bb == 2 ? 0 : bb + 1;
       }
+      int pf_last = k > 0 ? 1 : 0, b_last = k > 0 ? 4 : 0;  // the touch of 4k-4, the batch of 4k-2
+      for (; k < nk; ++k) {
+        const int bb2 = bb == 0 ? 2 : bb - 1;
+        const int a_now = k + 1 < nk ? 4 : 0;
+        if (a_now) issue(false, 1, k + 1, 0);
+        read_half(k, bb, 0);
+        end_memory_phase_rt(pf_last + b_last + a_now);
+        mfma_half();
+        sync();
+        const int b_now = k + 2 < nk ? 4 : 0;
+        if (b_now) issue(true, 1, k + 2, bb2);
+        read_half(k, bb, 1);
+        end_memory_phase_rt(a_now + b_now);
+        mfma_half();
+        sync();
+        pf_last = 0;
+        b_last = b_now;
+        bb = bb == 2 ? 0 : bb + 1;
+      }
     } else {
       sync();
-      for (int k = 0; k < nk; ++k) {
+      int k = 0;
+      for (; k + 2 < nk; ++k) {
         const int bb2 = bb == 0 ? 2 : bb - 1;
         // phase 4k+1: B rows 0-127 of step k+2
-        const bool i0 = k + 2 < nk;
-        if (i0) issue(true, 0, k + 2, bb2);
+        issue(true, 0, k + 2, bb2);
         read_half(k, bb, 0);
-        end_memory_phase(i0);
+        end_memory_phase(C8{});
         mfma_half();
         sync();
         // phase 4k+3: A rows 0-127 of step k+2
-        const bool i1 = k + 2 < nk;
-        if (i1) issue(false, 0, k + 2, 0);
+        issue(false, 0, k + 2, 0);
         read_half(k, bb, 1);
-        end_memory_phase(i1);
+        end_memory_phase(C8{});
         mfma_half();
         if (k + 1 < nk) sync();
+        bb = bb == 2 ? 0 : bb + 1;
+      }
+      int a_last = k > 0 ? 4 : 0;  // the batch of phase 4k-1
+      for (; k < nk; ++k) {
+        read_half(k, bb, 0);
+        end_memory_phase_rt(a_last);
+        mfma_half();
+        sync();
+        read_half(k, bb, 1);
+        end_memory_phase(std::integral_constant<int, 0>{});
+        mfma_half();
+        if (k + 1 < nk) sync();
+        a_last = 0;
         bb = bb == 2 ? 0 : bb + 1;
       }
     }
@@ -878,6 +990,282 @@ gemm_kc_kernel(GemmArgs args) {
   }
 
   store_tile<EPI>(acc, args, smem + wave * (64 * ROW_B), m0 + wm * WM, n0 + wn * WN, split, lane);
+#else
+  (void)args;
+#endif
+}
+
+// Orders of the four-wave kernel's fragment reads and MFMAs (see there).
+__device__ constexpr int w4_read(int r) {
+  constexpr int order[8] = {0, 4, 5, 1, 6, 2, 7, 3};  // A0 B0 B1 A1 B2 A2 B3 A3
+  return order[r];
+}
+__device__ constexpr int w4_mi(int m) {
+  constexpr int order[16] = {0, 0, 1, 1, 0, 1, 2, 2, 2, 0, 1, 2, 3, 3, 3, 3};
+  return order[m];
+}
+__device__ constexpr int w4_mj(int m) {
+  constexpr int order[16] = {0, 1, 0, 1, 2, 2, 0, 1, 2, 3, 3, 3, 0, 1, 2, 3};
+  return order[m];
+}
+
+// 256 x 256 tile, A K-contiguous and B either, four waves (one per SIMD) that
+// each compute a 128 x 128 quadrant: wave w owns rows 128 (w / 2) and columns
+// 128 (w % 2) of the tile, its 256 accumulator registers in the AGPRs.  Against
+// eight waves of 128 x 64, a K step reads a third less from LDS (each wave
+// reads 128 rows of A and 128 of B) and needs one barrier instead of four.
+//
+// LDS is a ring of ten 16 KiB slots.  Quarter q of K step s (A rows 0-127,
+// A rows 128-255, B's first 128 columns, B's last 128) lives in slot
+// (4 s + q) mod 10, so steps s and s+1 and half of s+2 fit at once.  Every wave
+// loads a quarter of every quarter-slot (4 LDS-DMA instructions of 1 KiB).
+//
+// A K step is four sub-steps of 16 k.  In each, a wave issues the LDS reads of
+// the next sub-step's operand fragments and one quarter-slot's loads between
+// the current sub-step's 16 MFMAs (sched_group_barrier keeps the MFMA pipe fed
+// while the other instructions issue; with one wave per SIMD nothing else
+// would).  In K step k:
+//   sub-step 0: quarter 3 of step k+1 (into the slot of step k-1's quarter 1)
+//   sub-step 1: quarter 0 of step k+2 (step k-1's quarter 2)
+//   sub-step 2: quarter 1 of step k+2 (step k-1's quarter 3)
+//   then: wait until step k+1 has landed (vmcnt: only the two batches just
+//         issued may be in flight) and until sub-step 3's fragments are in
+//         registers, and barrier: every wave is done with step k's slots and
+//         step k+1 is visible to all
+//   sub-step 3: quarter 2 of step k+2 (step k's quarter 0), and the LDS reads
+//         of step k+1's first sub-step.
+// The loads thus run at an even 16 KiB per sub-step per workgroup; each batch
+// has at least two sub-steps before it is waited for.
+template <int LB, int EPI>
+__global__ void __launch_bounds__(256)
+gemm_w4_kernel(GemmArgs args) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int BK = TILE_BK;
+  constexpr int SLOT = 128 * BK * 2;
+  constexpr int NSLOT = 10;
+  constexpr int FM = 4, FN = 4;  // 32 x 32 fragments per wave: 128 x 128
+  static_assert(BK == 64 && NSLOT * SLOT == 160 * 1024, "ten 16 KiB slots fill the LDS");
+  static_assert(4 * 64 * ROW_B <= NSLOT * SLOT, "epilogue staging fits");
+  __shared__ __attribute__((aligned(1024))) char smem[NSLOT * SLOT];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+
+  int tm, tn, split;
+  tile_of(blockIdx.x, gridDim.x, args.tiles_m, args.tiles_n, tm, tn, split);
+  const int m0 = tm * 256, n0 = tn * 256;
+  const int k_begin = split * args.k_split;
+  const int k_end = min(args.K, k_begin + args.k_split);
+  const int nk = (k_end - k_begin + BK - 1) / BK;
+
+  HalfDma dma_a, dma_b;
+  HalfDmaMC dma_bm;
+  dma_a.init(args.lda, wave, lane);
+  if (LB == KC) dma_b.init(args.ldb, wave, lane);
+  else dma_bm.init(args.ldb, wave, lane);
+
+  // Slot of quarter q of a K step with step % 5 == r (4 * 5 = 20 slots is a
+  // whole number of turns of the ring).  The main loop is unrolled five times so
+  // that r, and every LDS address, is a compile-time constant there.
+  auto slot = [&](int r, int q) -> char* { return smem + ((4 * r + q) % NSLOT) * SLOT; };
+  // Instruction i of this wave's share of quarter q of K step `step` (r = step % 5).
+  auto load = [&](int step, int r, int q, int i) {
+    const int k = k_begin + step * BK;
+    char* dst = slot(r, q);
+    if (q < 2) {
+      dma_a.issue_one(args.a + (int64_t)(m0 + 128 * q) * args.lda + k, args.lda, dst, args.M - m0 - 128 * q,
+                      k_end - k, wave, lane, i);
+    } else if (LB == KC) {
+      dma_b.issue_one(args.b + (int64_t)(n0 + 128 * (q - 2)) * args.ldb + k, args.ldb, dst,
+                      args.N - n0 - 128 * (q - 2), k_end - k, wave, lane, i);
+    } else {
+      dma_bm.issue_one(args.b + (int64_t)k * args.ldb + n0 + 128 * (q - 2), args.ldb, dst,
+                       args.N - n0 - 128 * (q - 2), k_end - k, wave, lane, i);
+    }
+  };
+
+  f32x16_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  bf16x8_t fa[2][FM], fb[2][FN];
+  // The fragments are read, and the MFMAs run, in an order in which the n-th
+  // read is first needed as late as possible: read r fetches A fragment
+  // w4_read(r) (B fragment w4_read(r) - 4 from 4 on); MFMA m updates block
+  // (w4_mi(m), w4_mj(m)).  The first MFMA needs two reads, the last read is
+  // first used by the 13th.
+  // The lane's byte offsets of its fragment reads inside a slot, so that a
+  // read is a register base plus an immediate.  K-contiguous (read_frag): the
+  // fragment of row block f in sub-step kk is at lane_kc[kk][f % 2] + 8192 (f / 2),
+  // because the swizzle of row r + 64 equals that of row r.  N-contiguous
+  // (read_frag_mc): fragment f's low half is at lane_mc[f] + 4096 kk and its
+  // high half 1024 further, because the swizzle depends on k only through k % 4.
+  uint32_t lane_kc[4][2], lane_mc[FN];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+    for (int par = 0; par < 2; ++par) lane_kc[kk][par] = tile_off(32 * par + (lane & 31), 2 * kk + (lane >> 5));
+#pragma unroll
+  for (int f = 0; f < FN; ++f) {
+    const int g = lane >> 4, sl = lane & 15;
+    lane_mc[f] = mc_off(8 * (g >> 1) + (sl >> 2), 32 * f + 16 * (g & 1) + 4 * (sl & 3));
+  }
+  auto read_sub = [&](int buf, int r, int kk) {
+    const char* ta = slot(r, wm);
+    const char* tb = slot(r, 2 + wn);
+#pragma unroll
+    for (int x = 0; x < FM + FN; ++x) {
+      const int f = w4_read(x);
+      if (f < FM) {
+        fa[buf][f] = *reinterpret_cast<const bf16x8_t*>(ta + lane_kc[kk][f & 1] + 8192 * (f >> 1));
+      } else if (LB == KC) {
+        fb[buf][f - FM] = *reinterpret_cast<const bf16x8_t*>(tb + lane_kc[kk][(f - FM) & 1] + 8192 * ((f - FM) >> 1));
+      } else {
+        const char* p = tb + lane_mc[f - FM] + 4096 * kk;
+        const i16x4_t lo = ds_read_tr(p), hi = ds_read_tr(p + 1024);
+        const i16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        fb[buf][f - FM] = __builtin_bit_cast(bf16x8_t, v);
+      }
+    }
+  };
+  auto mfma_sub = [&](int buf) {
+#pragma unroll
+    for (int m = 0; m < FM * FN; ++m) {
+      const int i = w4_mi(m), j = w4_mj(m);
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf][j], fa[buf][i], acc[i][j], 0, 0, 0);
+    }
+  };
+  // Scheduling of one sub-step: its 16 MFMAs, with the 8 LDS reads between the
+  // first eight and the NL loads between the last eight (a load writes LDS, so
+  // the compiler keeps it behind the reads before it).
+  auto interleave = [&](auto nl) {
+    constexpr int NL = decltype(nl)::value;
+    static_assert(NL == 0 || NL == 4 || NL == 8, "loads per sub-step");
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                            // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);                            // up to 3 VALU
+      if (m < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                 // LDS read
+      else if (NL == 8 || (NL == 4 && (m & 1) == 0))
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                          // global load
+    }
+  };
+  auto fence = [&]() { __builtin_amdgcn_sched_barrier(0); };
+  using L0 = std::integral_constant<int, 0>;
+  using L4 = std::integral_constant<int, 4>;
+  using L8 = std::integral_constant<int, 8>;
+
+  // s_waitcnt immediate for vmcnt(n), n < 64, leaving the other counters free.
+  auto vm_wait = [&](auto n) {
+    constexpr int N = decltype(n)::value;
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+  };
+
+  if (nk > 0) {
+    // Prologue: K step 0 and quarters 0-2 of step 1 (slots 0-6); wait for step 0.
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) load(0, 0, q, i);
+    if (nk > 1) {
+#pragma unroll
+      for (int q = 0; q < 3; ++q)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) load(1, 1, q, i);
+      vm_wait(std::integral_constant<int, 12>{});
+    } else {
+      vm_wait(L0{});
+    }
+    __builtin_amdgcn_s_barrier();
+    fence();
+    read_sub(0, 0, 0);
+
+    // One K step; LEFT = min(2, K steps after this one) is known at compile time
+    // (2: every load is issued; 1: the last but one step; 0: the last); r = k % 5.
+    auto k_step = [&](int k, auto left, int r) {
+      const int r1 = r == 4 ? 0 : r + 1, r2 = r >= 3 ? r - 3 : r + 2;
+      constexpr int LEFT = decltype(left)::value;
+      constexpr bool more2 = LEFT >= 2;  // step k+2 exists: load it
+      constexpr bool more1 = LEFT >= 1;  // step k+1 exists: wait for it, read it
+      // sub-step 0
+      fence();
+      read_sub(1, r, 1);
+      if constexpr (more1) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) load(k + 1, r1, 3, i);
+      }
+      mfma_sub(0);
+      if constexpr (more1) interleave(L4{}); else interleave(L0{});
+      fence();
+      // sub-step 1
+      read_sub(0, r, 2);
+      if constexpr (more2) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) load(k + 2, r2, 0, i);
+      }
+      mfma_sub(1);
+      if constexpr (more2) interleave(L4{}); else interleave(L0{});
+      fence();
+      // sub-step 2
+      read_sub(1, r, 3);
+      if constexpr (more2) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) load(k + 2, r2, 1, i);
+      }
+      mfma_sub(0);
+      if constexpr (more2) interleave(L4{}); else interleave(L0{});
+      fence();
+      if constexpr (more1) {
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): sub-step 3's fragments are in registers
+        if constexpr (more2) vm_wait(L8{});  // step k+1 has landed; k+2's first half may be in flight
+        else vm_wait(L0{});
+        __builtin_amdgcn_s_barrier();
+        fence();
+        // sub-step 3
+        read_sub(0, r1, 0);
+        if constexpr (more2) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) load(k + 2, r2, 2, i);
+        }
+        mfma_sub(1);
+        if constexpr (more2) interleave(L4{}); else interleave(L0{});
+        fence();
+      } else {
+        mfma_sub(1);
+        fence();
+      }
+    };
+    using Full = std::integral_constant<int, 2>;
+    int k = 0;
+    for (; k + 7 <= nk; k += 5) {  // steps k .. k+4, each with two more after it
+#pragma unroll
+      for (int u = 0; u < 5; ++u) k_step(k + u, Full{}, u);
+    }
+    for (; k + 2 < nk; ++k) k_step(k, Full{}, k % 5);
+    if (nk >= 2) k_step(nk - 2, std::integral_constant<int, 1>{}, (nk - 2) % 5);
+    k_step(nk - 1, std::integral_constant<int, 0>{}, (nk - 1) % 5);
+    vm_wait(L0{});
+  }
+  __syncthreads();  // every wave is done with the operand slots
+
+  // Epilogue, one 64-column half of the wave's quadrant at a time, staged in the
+  // wave's own 16 KiB of LDS.
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    f32x16_t part[FM][2];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) part[i][j] = acc[i][2 * h + j];
+    store_tile<EPI>(part, args, smem + wave * (64 * ROW_B), m0 + 128 * wm, n0 + 128 * wn + 64 * h, split, lane);
+  }
 #else
   (void)args;
 #endif
@@ -891,7 +1279,7 @@ template <int BM, int BN, int WM_, int WN_, int LA, int LB, int EPI>
 hipError_t launch_one(const GemmArgs& a, int splits, hipStream_t s) {
   const int blocks = a.tiles_m * a.tiles_n * splits;
   if constexpr (BM == 256 && LA == KC)
-    hipLaunchKernelGGL((kern::gemm_kc_kernel<LB, EPI>), dim3(blocks), dim3(512), 0, s, a);
+    hipLaunchKernelGGL((kern::gemm_w4_kernel<LB, EPI>), dim3(blocks), dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL((kern::gemm_kernel<BM, BN, WM_, WN_, LA, LB, EPI>), dim3(blocks), dim3(64 * WM_ * WN_), 0, s,
                        a);
