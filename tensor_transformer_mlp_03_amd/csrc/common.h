@@ -38,7 +38,7 @@ struct GemmArgs {
 
 // Tile shapes the library instantiates.
 enum TileCfg : int {
-  TILE_256x256 = 0,  // 8 waves, 2 x 4, wave tile 128 x 64
+  TILE_256x256 = 0,  // 4 waves, 2 x 2, wave tile 128 x 128
   TILE_128x128 = 1,  // 4 waves, 2 x 2, wave tile 64 x 64
   TILE_COUNT = 2,
 };

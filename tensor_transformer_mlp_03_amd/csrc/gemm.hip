@@ -21,16 +21,17 @@
 // part 三, 算子融合.)
 //
 // Two kernels:
-//  * gemm_kc_kernel: 256 x 256 tiles, A K-contiguous, B either; two groups of
-//    four waves take turns between reading operand fragments from LDS and
-//    running MFMAs (its comment has the schedule).  The main path.
-//  * gemm_kernel: a synchronous two-stage pipeline with 128 x 128 tiles (or
-//    256 x 256), an N-contiguous operand transposed in registers; used for
-//    outputs too small for 256 x 256 tiles.
+//  * gemm_w4_kernel: 256 x 256 tiles, A K-contiguous, B either; four waves,
+//    one per SIMD, each accumulating a 128 x 128 quadrant, with loads and LDS
+//    reads interleaved between its MFMAs (its comment has the schedule).  The
+//    main path.
+//  * gemm_kernel: a synchronous two-stage pipeline with 128 x 128 tiles, an
+//    N-contiguous operand transposed in registers; used for outputs too small
+//    for 256 x 256 tiles.
 // Shared design points:
 //  * A K-contiguous operand tile sits in LDS as [rows][64] (128-byte rows), so
 //    an MFMA operand fragment is one ds_read_b128 per lane (8 consecutive k of
-//    one row); an N-contiguous one in gemm_kc_kernel as [64 k][128 n] halves,
+//    one row); an N-contiguous one in gemm_w4_kernel as [64 k][128 n] halves,
 //    read with two ds_read_b64_tr_b16 per fragment.
 //  * Operands go from memory straight into LDS with buffer_load ... lds (16
 //    bytes per lane, no staging registers, no LDS write instructions).  Buffer
@@ -116,41 +117,6 @@ struct DmaLoader {
   }
 };
 
-// The same for blocks of a multiple of 8 waves, with one register of per-lane
-// state: DMA instruction i of wave w fills rows (i*NWAVES + w)*8 .. +7, and
-// since NWAVES*8 rows is a multiple of 64 the swizzle of a lane's chunk, and so
-// its column, is the same for every i; the instructions differ by a uniform
-// row offset.
-template <int R, int NWAVES>
-struct DmaLoaderW {
-  static_assert(NWAVES % 8 == 0, "row offsets of the instructions keep the swizzle");
-  static constexpr int PER_WAVE = R * 8 / 64 / NWAVES;
-  static_assert(PER_WAVE * 64 * NWAVES == R * 8, "tile must divide evenly over the waves");
-  uint32_t lane_off;  // byte offset of the lane's chunk in instruction 0
-
-  __device__ __forceinline__ static int lane_row(int wave, int lane) { return wave * 8 + (lane >> 3); }
-  __device__ __forceinline__ static int lane_kc(int wave, int lane) {
-    return 8 * ((lane & 7) ^ (((lane >> 3) ^ wave) & 7));
-  }
-  __device__ __forceinline__ void init(int64_t ld, int wave, int lane) {
-    lane_off = (uint32_t)(((int64_t)lane_row(wave, lane) * ld + lane_kc(wave, lane)) * 2);
-  }
-
-  __device__ __forceinline__ void issue(const uint16_t* base, int64_t ld, char* tile, int rows_left, int k_left,
-                                        int wave, int lane) const {
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base);
-    const bool k_ok = lane_kc(wave, lane) < k_left;
-    const int row = lane_row(wave, lane);
-#pragma unroll
-    for (int i = 0; i < PER_WAVE; ++i) {
-      const bool ok = k_ok && (row + i * NWAVES * 8 < rows_left);
-      const uint32_t off = lane_off + (uint32_t)(i * NWAVES * 8 * ld * 2);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(tile + (i * NWAVES + wave) * 1024), 16,
-                                               ok ? off : OOB, 0, 0, 0);
-    }
-  }
-};
-
 // An M/N-contiguous operand's tile of one K step (64 k-rows of R contiguous
 // elements in memory), loaded by R threads as 8x8 blocks into registers and
 // written transposed into the [R][64] LDS tile.
@@ -192,57 +158,6 @@ struct RegLoader {
   }
 };
 
-// The same for the 256-row tile of the 512-thread ping-pong kernel, spread
-// over every thread so that both wave groups do equal work: thread t loads
-// elements 4*(t%64) .. +3 of k-rows 8*(t/64) .. +7 (8-byte loads; a wave reads
-// whole 512-byte k-rows) and writes 4 K-contiguous rows of 8 k-values.  Odd
-// lanes write their 4 rows in the order 1, 0, 3, 2, so that the 16 lanes of one
-// ds_write_b128 cover both row parities and, with the swizzle, 16 distinct
-// bank groups.
-struct RegLoaderH {
-  u32x2_t v[8];  // v[i]: elements (k = 8*kb + i, r = q .. q+3)
-  int q, kb;
-  uint32_t off0, step;
-
-  __device__ __forceinline__ void init(int64_t ld, int t) {
-    const int mq = t & 63;
-    q = 4 * mq;
-    kb = t >> 6;
-    off0 = (uint32_t)(((int64_t)(8 * kb) * ld + q) * 2);
-    step = (uint32_t)(ld * 2);
-  }
-
-  // base: element (k0, r0) of the operand.  r_left is a multiple of 8, so the
-  // 4 elements of a lane are all in range or all out.
-  __device__ __forceinline__ void load(const uint16_t* base, int r_left, int k_left) {
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base);
-    const bool r_ok = q < r_left;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const bool ok = r_ok && (8 * kb + i < k_left);
-      v[i] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rs, ok ? off0 + i * step : OOB, 0, 0));
-    }
-  }
-
-  // Row e = r ^ (mq & 1) of the lane's 4 gets the 8 k-values of element q + e:
-  // dword d packs (k = 2d, k = 2d+1), the halves of v[2d] and v[2d+1] that hold
-  // element q + e (dword e/2 = r/2 of each).
-  // Element q + e sits in the low half of its dword for even e, the high half
-  // for odd e.
-  __device__ __forceinline__ void store(char* tile) const {
-    const int odd = (q >> 2) & 1;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int e = r ^ odd;
-      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-      u32x4_t o;
-#pragma unroll
-      for (int d = 0; d < 4; ++d) o[d] = __builtin_amdgcn_perm(v[2 * d + 1][r >> 1], v[2 * d][r >> 1], sel);
-      *reinterpret_cast<u32x4_t*>(tile + tile_off(q + e, kb)) = o;
-    }
-  }
-};
-
 // MFMA operand fragment of a 32-row slice at sub-step kk (16 wide) of a
 // [rows][64] tile: lane l gets the 8 k-values 16*kk + 8*(l/32) .. +7 of row l%32.
 __device__ __forceinline__ bf16x8_t read_frag(const char* tile, int r0, int kk, int lane) {
@@ -250,13 +165,12 @@ __device__ __forceinline__ bf16x8_t read_frag(const char* tile, int r0, int kk, 
   return *reinterpret_cast<const bf16x8_t*>(tile + tile_off(r, 2 * kk + (lane >> 5)));
 }
 
-// One group's (4 waves') LDS-DMA loads of 128 rows x 64 k of a K-contiguous
-// operand into one half of a [256][64] LDS tile: 16 instructions of 1 KiB, 4
-// per wave.  Instruction i of wave w fills rows 8*(4i + w) .. +7 of the half;
-// lane q writes 16-byte position q & 7 of row q / 8 and loads the chunk that
-// the swizzle places there.  Within a half, a row's swizzle depends on the
-// lane and on (4i + w) & 7, so even and odd i use two lane patterns; the
-// second half's rows are 128 further on, which leaves the swizzle unchanged.
+// Four waves' LDS-DMA loads of 128 rows x 64 k of a K-contiguous operand into
+// one 16 KiB [128][64] LDS slot: 16 instructions of 1 KiB, 4 per wave.
+// Instruction i of wave w fills rows 8*(4i + w) .. +7 of the slot; lane q
+// writes 16-byte position q & 7 of row q / 8 and loads the chunk that the
+// swizzle places there.  A row's swizzle depends on the lane and on
+// (4i + w) & 7, so even and odd i use two lane patterns.
 struct HalfDma {
   static constexpr int PER_WAVE = 4;
   uint32_t lane_off[2];  // byte offset of the lane's chunk for even / odd i
@@ -279,11 +193,6 @@ struct HalfDma {
     const uint32_t off = lane_off[i & 1] + (uint32_t)((int64_t)r0 * ld * 2);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(base), (lds_void_t*)(half + (4 * i + w) * 1024), 16,
                                              ok ? off : OOB, 0, 0, 0);
-  }
-  __device__ __forceinline__ void issue(const uint16_t* base, int64_t ld, char* half, int rows_left, int k_left,
-                                        int w, int lane) const {
-#pragma unroll
-    for (int i = 0; i < PER_WAVE; ++i) issue_one(base, ld, half, rows_left, k_left, w, lane, i);
   }
 };
 
@@ -318,11 +227,6 @@ struct HalfDmaMC {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(base), (lds_void_t*)(half + (4 * i + w) * 1024), 16,
                                              ok ? off : OOB, 0, 0, 0);
   }
-  __device__ __forceinline__ void issue(const uint16_t* base, int64_t ld, char* half, int n_left, int k_left,
-                                        int w, int lane) const {
-#pragma unroll
-    for (int i = 0; i < PER_WAVE; ++i) issue_one(base, ld, half, n_left, k_left, w, lane, i);
-  }
 };
 
 // ds_read_b64_tr_b16 from LDS address `p`.  Issued through inline assembly:
@@ -353,14 +257,12 @@ __device__ __forceinline__ i16x4_t ds_read_tr_after_stores(const char* p) {
 // 8*(l/32) .. +7 of column n0 + l%32.  ds_read_b64_tr_b16 reads, in each
 // 16-lane group, 4 k-rows x 16 columns (lane s: k-row s/4, columns 4*(s%4) ..
 // +3) and hands lane i the 4 k-values of column i; two such reads give 8.
-__device__ __forceinline__ bf16x8_t read_frag_mc(const char* half, int n0, int kk, int lane) {
+// This returns the lane's byte offset of the first read at kk = 0; the
+// second is 4 k-rows (1024 bytes) further, and sub-step kk adds 4096 bytes
+// (the swizzle depends on k only through k % 4).
+__device__ __forceinline__ uint32_t mc_lane_off(int n0, int lane) {
   const int g = lane >> 4, sl = lane & 15;
-  const int n = n0 + 16 * (g & 1) + 4 * (sl & 3);
-  const int k = 16 * kk + 8 * (g >> 1) + (sl >> 2);
-  const i16x4_t lo = ds_read_tr(half + mc_off(k, n));
-  const i16x4_t hi = ds_read_tr(half + mc_off(k + 4, n));
-  const i16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  return __builtin_bit_cast(bf16x8_t, v);
+  return mc_off(8 * (g >> 1) + (sl >> 2), n0 + 16 * (g & 1) + 4 * (sl & 3));
 }
 
 // Logical tile of workgroup `bid`: XCD-aware renumbering, then grouped order.
@@ -677,324 +579,6 @@ gemm_kernel(GemmArgs args) {
 }
 
 
-// 256 x 256 tile, both operands K-contiguous, 8 waves in two groups that take
-// turns on the matrix cores.
-//
-// Waves 0-3 (group 0) own output rows 0-127 of the tile, waves 4-7 (group 1)
-// rows 128-255; each wave a 128 x 64 sub-tile.  The hardware places wave w on
-// SIMD w % 4, so every SIMD holds one wave of each group.  K advances in steps
-// of 64, each read in two halves of 32.  A wave alternates a memory phase
-// (issue one batch of its group's loads, read half a K step's operand
-// fragments from LDS into registers) with a compute phase (that half step's 16
-// MFMAs, from registers only).  Group 1 starts one phase late, so while one
-// group computes the other reads, and block-wide barriers between phases keep
-// the two in step.  Counting phases from 0: group 0 reads K step k in phases
-// 4k and 4k+2, group 1 in 4k+1 and 4k+3; the even phases are group 0's memory
-// phases, the odd ones group 1's.
-//
-// Operand tiles are [rows][64] in LDS (128-byte rows, so every DMA request
-// fetches a whole 128-byte line).  A has two buffers, B three (160 KiB in
-// all).  Group 0 reads only A's rows 0-127 and group 1 only rows 128-255, so
-// the two halves of an A buffer free up one phase apart.  Every memory phase
-// issues one batch: 16 KiB, 4 LDS-DMA instructions per wave of the reading
-// group, in the rotation
-//   phase 4k+1 (group 1): B rows   0-127 of step k+2
-//   phase 4k+2 (group 0): B rows 128-255 of step k+2
-//   phase 4k+3 (group 1): A rows   0-127 of step k+2
-//   phase 4k+4 (group 0): A rows 128-255 of step k+2
-// Each batch lands in a buffer half whose last reader finished in an earlier
-// phase, and is read first at least five phases after it is issued: a wave
-// waits, at the end of each memory phase, until only its batches of this and
-// its previous memory phase are in flight.  The load path thus stays about
-// half busy at an even rate, and the computing group never issues a load.
-//
-// Both groups execute the same number of barriers: group 1's extra barrier at
-// the start is matched by skipping the barrier after its last compute phase.
-// Group 0 stages its epilogue in LDS while group 1 still computes.
-//
-// L2 prefetch.  The 32 tiles that run together on one XCD form a block 8
-// tiles tall and 4 wide (tile_of), and run at about the same pace, so the
-// first of them to load a K slice of a shared operand panel waits for the
-// fabric and the others wait for that same miss.  Four phases (a batch's
-// latency budget) are not always enough.  So in phase 4k waves 0-2 of group 0
-// touch, one 4-byte word per 64-byte piece, this tile's share of K step
-// k+4: A rows 64 (tn % 4) .. +63 (waves 0 and 1) and 1/8 of B, selected by
-// tm % 8 (wave 2).  Together the 32 tiles cover both slices, and the DMAs for
-// step k+4, issued from phase 4k+9 on, find them in L2.  The touch is itself an
-// LDS DMA (a load into a register would need one kept free): it lands in the
-// wave's own first 256 bytes of the B rows 128-255 half that the same wave
-// refills from memory in phase 4k+2.  A wave's loads complete in issue order,
-// so the real data lands last, and waiting for that refill also waits for the
-// touch.  The touch is only waited for two memory phases later than a batch
-// of its own phase would be.
-template <int LB, int EPI>
-__global__ void __launch_bounds__(512)
-gemm_kc_kernel(GemmArgs args) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  constexpr int BM = 256, BN = 256, BK = TILE_BK;
-  constexpr int WM = 128, WN = 64, FM = WM / 32, FN = WN / 32;
-  constexpr int HALF_BYTES = 128 * BK * 2;      // 128 rows of one operand
-  constexpr int BUF_BYTES = 2 * HALF_BYTES;      // one K step of one operand
-  constexpr int B_BASE = 2 * BUF_BYTES;          // A: 2 buffers, then B: 3
-  constexpr int LDS_BYTES = 5 * BUF_BYTES;
-  static_assert(LDS_BYTES == 160 * 1024, "two A and three B buffers fill the LDS");
-  static_assert(8 * 64 * ROW_B <= LDS_BYTES, "staging fits");
-  __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int grp = wave >> 2;
-  const int wg = wave & 3;
-  const int wm = grp, wn = wg;
-
-  int tm, tn, split;
-  tile_of(blockIdx.x, gridDim.x, args.tiles_m, args.tiles_n, tm, tn, split);
-  const int m0 = tm * BM, n0 = tn * BN;
-  const int k_begin = split * args.k_split;
-  const int k_end = min(args.K, k_begin + args.k_split);
-  const int nk = (k_end - k_begin + BK - 1) / BK;
-
-  HalfDma dma_a, dma_b;
-  HalfDmaMC dma_bm;
-  dma_a.init(args.lda, wg, lane);
-  if (LB == KC) dma_b.init(args.ldb, wg, lane);
-  else dma_bm.init(args.ldb, wg, lane);
-  // Issue this group's share of one operand half of K step `step`:
-  // is_b selects B (else A), hi the rows 128-255 (else 0-127).
-  auto issue = [&](bool is_b, int hi, int step, int b_buf) {
-    const int k = k_begin + step * BK;
-    if (is_b) {
-      char* dst = smem + B_BASE + b_buf * BUF_BYTES + hi * HALF_BYTES;
-      if (LB == KC)
-        dma_b.issue(args.b + (int64_t)(n0 + 128 * hi) * args.ldb + k, args.ldb, dst, args.N - n0 - 128 * hi, k_end - k,
-                    wg, lane);
-      else
-        dma_bm.issue(args.b + (int64_t)k * args.ldb + n0 + 128 * hi, args.ldb, dst, args.N - n0 - 128 * hi, k_end - k,
-                     wg, lane);
-    } else {
-      dma_a.issue(args.a + (int64_t)(m0 + 128 * hi) * args.lda + k, args.lda, smem + (step & 1) * BUF_BYTES + hi * HALF_BYTES,
-                  args.M - m0 - 128 * hi, k_end - k, wg, lane);
-    }
-  };
-
-  // Group 0's L2 touch of K step `step` < nk (see above): one load per wave,
-  // into the wave's first 256 bytes of B buffer b_buf's rows 128-255, which the
-  // wave refills later.  The lane's piece: waves 0 and 1, A rows
-  // 64 (tn % 4) + 32 wg + lane / 2; waves 2 and 3 (lanes 0-31), B rows
-  // 32 (tm % 8) + 16 (wg - 2) + lane / 2 (K-contiguous B) or k-rows
-  // 8 (tm % 8) + 4 (wg - 2) + lane / 8 (N-contiguous B, 512 bytes per k-row).
-  // Lanes outside the operand load nothing.
-  const uint16_t* pf_base;  // the wave's operand at (tile row 0 or k-row 0, k_begin)
-  int64_t pf_step;          // elements per K step
-  uint32_t pf_off;          // the lane's piece, in bytes from pf_base
-  int pf_k;                 // k_end must reach at least step k + pf_k
-  bool pf_ok;               // the piece's row or column exists
-  if (wg < 2) {
-    const int r = 64 * (tn & 3) + 32 * wg + (lane >> 1), kp = 32 * (lane & 1);
-    pf_base = args.a + (int64_t)m0 * args.lda + k_begin;
-    pf_step = BK;
-    pf_off = (uint32_t)(((int64_t)r * args.lda + kp) * 2);
-    pf_k = kp + 2;
-    pf_ok = m0 + r < args.M;
-  } else if (LB == KC) {
-    const int r = 32 * (tm & 7) + 16 * (wg - 2) + ((lane & 31) >> 1), kp = 32 * (lane & 1);
-    pf_base = args.b + (int64_t)n0 * args.ldb + k_begin;
-    pf_step = BK;
-    pf_off = (uint32_t)(((int64_t)r * args.ldb + kp) * 2);
-    pf_k = kp + 2;
-    pf_ok = lane < 32 && n0 + r < args.N;
-  } else {
-    const int kr = 8 * (tm & 7) + 4 * (wg - 2) + ((lane & 31) >> 3), np = 32 * (lane & 7);
-    pf_base = args.b + (int64_t)k_begin * args.ldb + n0;
-    pf_step = (int64_t)BK * args.ldb;
-    pf_off = (uint32_t)(((int64_t)kr * args.ldb + np) * 2);
-    pf_k = kr + 1;
-    pf_ok = lane < 32 && n0 + np + 2 <= args.N;
-  }
-  auto prefetch = [&](int step, int b_buf) {
-    const bool ok = pf_ok && k_begin + step * BK + pf_k <= k_end;
-    char* dst = smem + B_BASE + b_buf * BUF_BYTES + HALF_BYTES + wg * 1024;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(pf_base + step * pf_step), (lds_void_t*)dst, 4,
-                                             ok ? pf_off : OOB, 0, 0, 0);
-  };
-
-  f32x16_t acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-  constexpr int HSUB = BK / 32;  // 16-wide sub-steps per phase
-  bf16x8_t fa[HSUB][FM], fb[HSUB][FN];
-  auto read_half = [&](int step, int b_buf, int h) {
-    const char* ta = smem + (step & 1) * BUF_BYTES;
-    const char* tb = smem + B_BASE + b_buf * BUF_BYTES;
-#pragma unroll
-    for (int s2 = 0; s2 < HSUB; ++s2) {
-#pragma unroll
-      for (int i = 0; i < FM; ++i) fa[s2][i] = read_frag(ta, wm * WM + 32 * i, HSUB * h + s2, lane);
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        if (LB == KC) {
-          fb[s2][j] = read_frag(tb, wn * WN + 32 * j, HSUB * h + s2, lane);
-        } else {
-          const int n0f = wn * WN + 32 * j;  // the wave's columns lie in one 128-wide half
-          fb[s2][j] = read_frag_mc(tb + (n0f >> 7) * HALF_BYTES, n0f & 127, HSUB * h + s2, lane);
-        }
-      }
-    }
-  };
-  auto mfma_half = [&]() {
-#pragma unroll
-    for (int s2 = 0; s2 < HSUB; ++s2)
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[s2][j], fa[s2][i], acc[i][j], 0, 0, 0);
-  };
-  // Block-wide barrier that the compiler may not move instructions across.
-  auto sync = [&]() {
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  auto lds_wait = [&]() { __builtin_amdgcn_s_waitcnt(0xC07F); };  // lgkmcnt(0)
-  // End of a memory phase: the batch of the wave's memory phase before the
-  // previous one (and everything older) must have landed; NEWER is the number
-  // of the wave's loads issued after that batch, which may still be in flight.
-  // A larger count than issued is safe where everything older has landed.
-  static_assert(HalfDma::PER_WAVE == 4 && HalfDmaMC::PER_WAVE == 4, "4 loads per batch");
-  auto end_memory_phase = [&](auto newer) {
-    constexpr int N = decltype(newer)::value;
-    static_assert(N >= 0 && N < 16, "vmcnt immediate");
-    __builtin_amdgcn_s_waitcnt(0x0F70 | N);
-    lds_wait();
-    sync();
-  };
-  // The same with a count known only at run time (the last K steps).
-  auto end_memory_phase_rt = [&](int newer) {
-    if (newer >= 9) end_memory_phase(std::integral_constant<int, 9>{});
-    else if (newer >= 8) end_memory_phase(std::integral_constant<int, 8>{});
-    else if (newer >= 5) end_memory_phase(std::integral_constant<int, 5>{});
-    else if (newer >= 4) end_memory_phase(std::integral_constant<int, 4>{});
-    else if (newer >= 1) end_memory_phase(std::integral_constant<int, 1>{});
-    else end_memory_phase(std::integral_constant<int, 0>{});
-  };
-
-  if (nk > 0) {
-    // Prologue: K step 0 entirely, and of step 1 all of B and A's rows 0-127.
-    if (grp == 0) {
-      issue(false, 0, 0, 0);
-      issue(false, 1, 0, 0);
-      if (nk > 1) issue(false, 0, 1, 0);
-      if (nk > 3) {  // steps 2 and 3 into B buffer 2, refilled in phase 2
-        prefetch(2, 2);
-        prefetch(3, 2);
-      }
-    } else {
-      issue(true, 0, 0, 0);
-      issue(true, 1, 0, 0);
-      if (nk > 1) {
-        issue(true, 0, 1, 1);
-        issue(true, 1, 1, 1);
-      }
-    }
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    sync();
-    int bb = 0;  // B buffer of step k: k % 3
-    // The loops are split at the last step with a full set of loads, so the
-    // waits of the steady part are immediates.
-    using C4 = std::integral_constant<int, 4>;
-    using C8 = std::integral_constant<int, 8>;
-    using C9 = std::integral_constant<int, 9>;
-    using C10 = std::integral_constant<int, 10>;
-    if (grp == 0) {
-      int k = 0;
-      for (; k + 4 < nk; ++k) {
-        const int bb2 = bb == 0 ? 2 : bb - 1;  // (k + 2) % 3
-        // phase 4k: A rows 128-255 of step k+1, then the touch of step k+4, whose
-        // target (B rows 128-255 of step k+2) this wave refills in phase 4k+2.
-        // In flight after A rows 128-255 of step k: the touch of phase 4k-4, the
-        // batch of 4k-2 and this phase's batch and touch.
-        issue(false, 1, k + 1, 0);
-        prefetch(k + 4, bb2);
-        read_half(k, bb, 0);
-        end_memory_phase(C10{});
-        mfma_half();
-        sync();
-        // phase 4k+2: B rows 128-255 of step k+2
-        issue(true, 1, k + 2, bb2);
-        read_half(k, bb, 1);
-        end_memory_phase(C9{});
-        mfma_half();
-        sync();
-        bb = bb == 2 ? 0 : bb + 1;
-      }
-      int pf_last = k > 0 ? 1 : 0, b_last = k > 0 ? 4 : 0;  // the touch of 4k-4, the batch of 4k-2
-      for (; k < nk; ++k) {
-        const int bb2 = bb == 0 ? 2 : bb - 1;
-        const int a_now = k + 1 < nk ? 4 : 0;
-        if (a_now) issue(false, 1, k + 1, 0);
-        read_half(k, bb, 0);
-        end_memory_phase_rt(pf_last + b_last + a_now);
-        mfma_half();
-        sync();
-        const int b_now = k + 2 < nk ? 4 : 0;
-        if (b_now) issue(true, 1, k + 2, bb2);
-        read_half(k, bb, 1);
-        end_memory_phase_rt(a_now + b_now);
-        mfma_half();
-        sync();
-        pf_last = 0;
-        b_last = b_now;
-        bb = bb == 2 ? 0 : bb + 1;
-      }
-    } else {
-      sync();
-      int k = 0;
-      for (; k + 2 < nk; ++k) {
-        const int bb2 = bb == 0 ? 2 : bb - 1;
-        // phase 4k+1: B rows 0-127 of step k+2
-        issue(true, 0, k + 2, bb2);
-        read_half(k, bb, 0);
-        end_memory_phase(C8{});
-        mfma_half();
-        sync();
-        // phase 4k+3: A rows 0-127 of step k+2
-        issue(false, 0, k + 2, 0);
-        read_half(k, bb, 1);
-        end_memory_phase(C8{});
-        mfma_half();
-        if (k + 1 < nk) sync();
-        bb = bb == 2 ? 0 : bb + 1;
-      }
-      int a_last = k > 0 ? 4 : 0;  // the batch of phase 4k-1
-      for (; k < nk; ++k) {
-        read_half(k, bb, 0);
-        end_memory_phase_rt(a_last);
-        mfma_half();
-        sync();
-        read_half(k, bb, 1);
-        end_memory_phase(std::integral_constant<int, 0>{});
-        mfma_half();
-        if (k + 1 < nk) sync();
-        a_last = 0;
-        bb = bb == 2 ? 0 : bb + 1;
-      }
-    }
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // nothing is in flight; keeps the staging below safe
-  }
-
-  store_tile<EPI>(acc, args, smem + wave * (64 * ROW_B), m0 + wm * WM, n0 + wn * WN, split, lane);
-#else
-  (void)args;
-#endif
-}
-
 // Orders of the four-wave kernel's fragment reads and MFMAs (see there).
 __device__ constexpr int w4_read(int r) {
   constexpr int order[8] = {0, 4, 5, 1, 6, 2, 7, 3};  // A0 B0 B1 A1 B2 A2 B3 A3
@@ -1104,7 +688,7 @@ gemm_w4_kernel(GemmArgs args) {
   // read is a register base plus an immediate.  K-contiguous (read_frag): the
   // fragment of row block f in sub-step kk is at lane_kc[kk][f % 2] + 8192 (f / 2),
   // because the swizzle of row r + 64 equals that of row r.  N-contiguous
-  // (read_frag_mc): fragment f's low half is at lane_mc[f] + 4096 kk and its
+  // (mc_lane_off): fragment f's low half is at lane_mc[f] + 4096 kk and its
   // high half 1024 further, because the swizzle depends on k only through k % 4.
   uint32_t lane_kc[4][2], lane_mc[FN];
 #pragma unroll
@@ -1112,10 +696,7 @@ gemm_w4_kernel(GemmArgs args) {
 #pragma unroll
     for (int par = 0; par < 2; ++par) lane_kc[kk][par] = tile_off(32 * par + (lane & 31), 2 * kk + (lane >> 5));
 #pragma unroll
-  for (int f = 0; f < FN; ++f) {
-    const int g = lane >> 4, sl = lane & 15;
-    lane_mc[f] = mc_off(8 * (g >> 1) + (sl >> 2), 32 * f + 16 * (g & 1) + 4 * (sl & 3));
-  }
+  for (int f = 0; f < FN; ++f) lane_mc[f] = mc_lane_off(32 * f, lane);
   auto read_sub = [&](int buf, int r, int kk) {
     const char* ta = slot(r, wm);
     const char* tb = slot(r, 2 + wn);
@@ -1315,7 +896,7 @@ int tile_bn(TileCfg t) { return t == TILE_256x256 ? 256 : 128; }
 hipError_t launch_gemm(TileCfg tile, Layout la, Layout lb, Epi epi, const GemmArgs& args, int splits,
                        hipStream_t stream) {
   switch (tile) {
-    case TILE_256x256: return dispatch_layout<256, 256, 2, 4>(la, lb, epi, args, splits, stream);
+    case TILE_256x256: return dispatch_layout<256, 256, 2, 2>(la, lb, epi, args, splits, stream);
     case TILE_128x128: return dispatch_layout<128, 128, 2, 2>(la, lb, epi, args, splits, stream);
     default: return hipErrorInvalidValue;
   }
