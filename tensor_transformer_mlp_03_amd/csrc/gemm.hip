@@ -628,6 +628,9 @@ gemm_w4_kernel(GemmArgs args) {
   constexpr int SLOT = 128 * BK * 2;
   constexpr int NSLOT = 10;
   constexpr int FM = 4, FN = 4;  // 32 x 32 fragments per wave: 128 x 128
+  // A window's 16 loads, four per sub-step: even issue measured best (eight in
+  // one sub-step stall the wave on the address unit).
+  constexpr int LC3 = 4, LC0 = 4, LC1 = 4;
   static_assert(BK == 64 && NSLOT * SLOT == 160 * 1024, "ten 16 KiB slots fill the LDS");
   static_assert(4 * 64 * ROW_B <= NSLOT * SLOT, "epilogue staging fits");
   __shared__ __attribute__((aligned(1024))) char smem[NSLOT * SLOT];
@@ -669,6 +672,19 @@ gemm_w4_kernel(GemmArgs args) {
                        args.N - n0 - 128 * (q - 2), k_end - k, wave, lane, i);
     }
   };
+
+  // The 16 loads of window k, issued between barrier k-1 and barrier k: quarters
+  // 2 and 3 of step k+1 (loads 0-7), then quarters 0 and 1 of step k+2 (8-15),
+  // into the slots of step k-1.  r1, r2: (k+1) % 5, (k+2) % 5.  The first LC3
+  // are issued in sub-step 3 of step k-1, LC0 and LC1 in sub-steps 0 and 1 of
+  // step k, the rest in sub-step 2.
+  auto window_load = [&](int k, int n, int r1, int r2) {
+    const int b = n >> 2, i = n & 3;
+    if (b < 2) load(k + 1, r1, 2 + b, i);
+    else load(k + 2, r2, b - 2, i);
+  };
+  static_assert(LC3 <= 8 && LC0 <= 8 && LC1 <= 8 && 16 - LC3 - LC0 - LC1 <= 8 && LC3 + LC0 + LC1 <= 16,
+                "at most eight loads per sub-step; window k+1's first LC3 exist whenever step k+2 does");
 
   f32x16_t acc[FM][FN];
 #pragma unroll
@@ -723,17 +739,17 @@ gemm_w4_kernel(GemmArgs args) {
     }
   };
   // Scheduling of one sub-step: its 16 MFMAs, with the 8 LDS reads between the
-  // first eight and the NL loads between the last eight (a load writes LDS, so
-  // the compiler keeps it behind the reads before it).
+  // first eight and NL (at most 8) loads spread over the last eight (a load
+  // writes LDS, so the compiler keeps it behind the reads before it).
   auto interleave = [&](auto nl) {
     constexpr int NL = decltype(nl)::value;
-    static_assert(NL == 0 || NL == 4 || NL == 8, "loads per sub-step");
+    static_assert(NL >= 0 && NL <= 8, "loads per sub-step");
 #pragma unroll
     for (int m = 0; m < 16; ++m) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                            // MFMA
       __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);                            // up to 3 VALU
       if (m < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                 // LDS read
-      else if (NL == 8 || (NL == 4 && (m & 1) == 0))
+      else if ((m - 7) * NL / 8 != (m - 8) * NL / 8)
         __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                          // global load
     }
   };
@@ -750,17 +766,20 @@ gemm_w4_kernel(GemmArgs args) {
   };
 
   if (nk > 0) {
-    // Prologue: K step 0 and quarters 0-2 of step 1 (slots 0-6); wait for step 0.
+    // Prologue: K step 0, quarters 0 and 1 of step 1 and the first LC3 loads of
+    // window 0 (slots 0-5 and part of 6); wait for step 0.
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
       for (int i = 0; i < 4; ++i) load(0, 0, q, i);
     if (nk > 1) {
 #pragma unroll
-      for (int q = 0; q < 3; ++q)
+      for (int q = 0; q < 2; ++q)
 #pragma unroll
         for (int i = 0; i < 4; ++i) load(1, 1, q, i);
-      vm_wait(std::integral_constant<int, 12>{});
+#pragma unroll
+      for (int n = 0; n < LC3; ++n) window_load(0, n, 1, 2);
+      vm_wait(std::integral_constant<int, 8 + LC3>{});
     } else {
       vm_wait(L0{});
     }
@@ -775,33 +794,29 @@ gemm_w4_kernel(GemmArgs args) {
       constexpr int LEFT = decltype(left)::value;
       constexpr bool more2 = LEFT >= 2;  // step k+2 exists: load it
       constexpr bool more1 = LEFT >= 1;  // step k+1 exists: wait for it, read it
+      // Loads [lo, hi) of window k that exist (those from 8 on load step k+2).
+      auto window_part = [&](auto lo, auto hi) {
+        constexpr int LO = decltype(lo)::value, HI = decltype(hi)::value;
+        constexpr int END = more2 ? HI : more1 ? (HI < 8 ? HI : 8) : LO;
+#pragma unroll
+        for (int n = LO; n < END; ++n) window_load(k, n, r1, r2);
+        interleave(std::integral_constant<int, (END > LO ? END - LO : 0)>{});
+      };
       // sub-step 0
       fence();
       read_sub(1, r, 1);
-      if constexpr (more1) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) load(k + 1, r1, 3, i);
-      }
       mfma_sub(0);
-      if constexpr (more1) interleave(L4{}); else interleave(L0{});
+      window_part(std::integral_constant<int, LC3>{}, std::integral_constant<int, LC3 + LC0>{});
       fence();
       // sub-step 1
       read_sub(0, r, 2);
-      if constexpr (more2) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) load(k + 2, r2, 0, i);
-      }
       mfma_sub(1);
-      if constexpr (more2) interleave(L4{}); else interleave(L0{});
+      window_part(std::integral_constant<int, LC3 + LC0>{}, std::integral_constant<int, LC3 + LC0 + LC1>{});
       fence();
       // sub-step 2
       read_sub(1, r, 3);
-      if constexpr (more2) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) load(k + 2, r2, 1, i);
-      }
       mfma_sub(0);
-      if constexpr (more2) interleave(L4{}); else interleave(L0{});
+      window_part(std::integral_constant<int, LC3 + LC0 + LC1>{}, std::integral_constant<int, 16>{});
       fence();
       if constexpr (more1) {
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): sub-step 3's fragments are in registers
@@ -809,14 +824,15 @@ gemm_w4_kernel(GemmArgs args) {
         else vm_wait(L0{});
         __builtin_amdgcn_s_barrier();
         fence();
-        // sub-step 3
+        // sub-step 3: the first LC3 loads of window k+1, into step k's slots
         read_sub(0, r1, 0);
+        const int r3 = r2 == 4 ? 0 : r2 + 1;
         if constexpr (more2) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) load(k + 2, r2, 2, i);
+          for (int n = 0; n < LC3; ++n) window_load(k + 1, n, r2, r3);
         }
         mfma_sub(1);
-        if constexpr (more2) interleave(L4{}); else interleave(L0{});
+        if constexpr (more2) interleave(std::integral_constant<int, LC3>{}); else interleave(L0{});
         fence();
       } else {
         mfma_sub(1);
