@@ -52,11 +52,14 @@ hipError_t launch_gemm(TileCfg tile, Layout la, Layout lb, Epi epi, const GemmAr
 hipError_t launch_sum(const float* const* parts, int n_parts, float* out, int64_t n,
                       hipStream_t stream);
 
-// Sum of `splits` float32 slices of an [M][N] product (slice i at part + i*M*N)
-// finished with the epilogue `epi` into out/out2 as the GEMM epilogue
-// would (aux: the dGeLU pre-activation; ldt: M for the transposed outputs).
+// Sum of `splits` float32 slices of an [M][N] product (slice i at part + i*M*N,
+// rows of N) finished with the epilogue `epi` into out/out2 as the GEMM
+// epilogue would.  out, out2 (GeLU's pre-activation) and aux (the dGeLU
+// pre-activation) have rows of ldo elements; dGeLU's transposed out2 has rows
+// of ldt.  The outputs may be a column block of wider matrices.
 hipError_t launch_splitk_epilogue(Epi epi, const float* part, int splits, int64_t M, int64_t N, void* out,
-                                  uint16_t* out2, const uint16_t* aux, hipStream_t stream);
+                                  uint16_t* out2, const uint16_t* aux, int64_t ldo, int64_t ldt,
+                                  hipStream_t stream);
 
 // out[c][r] = in[r][c] for a bf16 matrix in[R][C] (R, C multiples of 8).
 hipError_t launch_transpose(const uint16_t* in, int64_t R, int64_t C, uint16_t* out, hipStream_t stream);

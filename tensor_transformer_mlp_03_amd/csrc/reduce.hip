@@ -43,9 +43,11 @@ __global__ void __launch_bounds__(256) sum_kernel(SumArgs a) {
 }
 
 struct SplitArgs {
-  const float* part;  // splits x n float32, slice i at part + i * n
+  const float* part;  // splits x n float32, slice i at part + i * n ([rows][cols])
   int splits;
   int64_t n;          // elements per slice (multiple of 4)
+  int cols;           // slice row length (multiple of 4)
+  int64_t ldo;        // row stride of out and out2
   void* out;          // float* (EPI_F32) or uint16_t*
   uint16_t* out2;     // second bf16 output or null
   const uint16_t* aux;
@@ -55,11 +57,15 @@ template <int EPI>
 __global__ void __launch_bounds__(256) splitk_kernel(SplitArgs a) {
   const int64_t n4 = a.n / 4;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const bool dense = a.ldo == a.cols;
+  const uint32_t c4n = (uint32_t)a.cols / 4;
   for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < n4; j += stride) {
     f32x4_t s = reinterpret_cast<const f32x4_t*>(a.part)[j];
     for (int i = 1; i < a.splits; ++i) s += reinterpret_cast<const f32x4_t*>(a.part + i * a.n)[j];
+    // Element offset of the 4 values in the outputs (rows of ldo).
+    const int64_t o = dense ? 4 * j : (int64_t)((uint64_t)j / c4n) * a.ldo + 4 * ((uint64_t)j % c4n);
     if (EPI == EPI_F32) {
-      reinterpret_cast<f32x4_t*>(a.out)[j] = s;
+      *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(a.out) + o) = s;
     } else if (EPI == EPI_GELU) {
       u16x4_t g, p;
 #pragma unroll
@@ -67,13 +73,13 @@ __global__ void __launch_bounds__(256) splitk_kernel(SplitArgs a) {
         g[e] = epi_gelu(s[e]);
         p[e] = f32_to_bf16(s[e]);
       }
-      reinterpret_cast<u16x4_t*>(a.out)[j] = g;
-      if (a.out2) reinterpret_cast<u16x4_t*>(a.out2)[j] = p;
+      *reinterpret_cast<u16x4_t*>(reinterpret_cast<uint16_t*>(a.out) + o) = g;
+      if (a.out2) *reinterpret_cast<u16x4_t*>(a.out2 + o) = p;
     } else if (EPI == EPI_BF16) {
       u16x4_t p;
 #pragma unroll
       for (int e = 0; e < 4; ++e) p[e] = f32_to_bf16(s[e]);
-      reinterpret_cast<u16x4_t*>(a.out)[j] = p;
+      *reinterpret_cast<u16x4_t*>(reinterpret_cast<uint16_t*>(a.out) + o) = p;
     }
   }
 }
@@ -82,9 +88,10 @@ struct SplitDGeluArgs {
   const float* part;    // splits x M x N float32
   int splits;
   int M, N;
-  uint16_t* dp;         // [M][N]
-  uint16_t* g_t;        // [N][M]
-  const uint16_t* p;    // [M][N] pre-activation
+  int64_t ldo, ldt;     // row strides of dp and p, and of g_t
+  uint16_t* dp;         // [M][ldo]
+  uint16_t* g_t;        // [N][ldt]
+  const uint16_t* p;    // [M][ldo] pre-activation
 };
 
 typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
@@ -104,7 +111,7 @@ __global__ void __launch_bounds__(256) splitk_dgelu_kernel(SplitDGeluArgs a) {
     for (int v = 0; v < 2; ++v) {
       const int c = 16 * (t & 3) + 8 * v, col = n0 + c;
       if (row >= a.M || col >= a.N) continue;  // N % 8 == 0: 8 columns in or out together
-      const int64_t o = (int64_t)row * a.N + col;
+      const int64_t o = (int64_t)row * a.N + col, oo = (int64_t)row * a.ldo + col;
       f32x4_t s0 = *reinterpret_cast<const f32x4_t*>(a.part + o);
       f32x4_t s1 = *reinterpret_cast<const f32x4_t*>(a.part + o + 4);
       for (int i = 1; i < a.splits; ++i) {
@@ -112,7 +119,7 @@ __global__ void __launch_bounds__(256) splitk_dgelu_kernel(SplitDGeluArgs a) {
         s1 += *reinterpret_cast<const f32x4_t*>(a.part + i * plane + o + 4);
       }
       const float x[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
-      const u16x8_t pb = *reinterpret_cast<const u16x8_t*>(a.p + o);
+      const u16x8_t pb = *reinterpret_cast<const u16x8_t*>(a.p + oo);
       u16x8_t dp;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -120,7 +127,7 @@ __global__ void __launch_bounds__(256) splitk_dgelu_kernel(SplitDGeluArgs a) {
         dp[e] = d.dp;
         s_g[r][c + e] = d.g;
       }
-      *reinterpret_cast<u16x8_t*>(a.dp + o) = dp;
+      *reinterpret_cast<u16x8_t*>(a.dp + oo) = dp;
     }
   }
   __syncthreads();
@@ -134,7 +141,7 @@ __global__ void __launch_bounds__(256) splitk_dgelu_kernel(SplitDGeluArgs a) {
         u16x8_t gv;
 #pragma unroll
         for (int e = 0; e < 8; ++e) gv[e] = s_g[r0 + 8 * v + e][c];
-        const int64_t o = (int64_t)col * a.M + row + 8 * v;
+        const int64_t o = (int64_t)col * a.ldt + row + 8 * v;
         *reinterpret_cast<u16x8_t*>(a.g_t + o) = gv;
       }
     }
@@ -216,16 +223,17 @@ hipError_t launch_sum(const float* const* parts, int n_parts, float* out, int64_
 }
 
 hipError_t launch_splitk_epilogue(Epi epi, const float* part, int splits, int64_t M, int64_t N, void* out,
-                                  uint16_t* out2, const uint16_t* aux, hipStream_t stream) {
+                                  uint16_t* out2, const uint16_t* aux, int64_t ldo, int64_t ldt,
+                                  hipStream_t stream) {
   const int64_t n = M * N;
-  if (!part || splits < 1 || (n & 3)) return hipErrorInvalidValue;
+  if (!part || splits < 1 || (N & 3) || ldo < N) return hipErrorInvalidValue;
   if (epi == EPI_DGELU) {
-    SplitDGeluArgs a{part, splits, (int)M, (int)N, static_cast<uint16_t*>(out), out2, aux};
+    SplitDGeluArgs a{part, splits, (int)M, (int)N, ldo, ldt, static_cast<uint16_t*>(out), out2, aux};
     const int64_t tiles = ((M + 63) / 64) * ((N + 63) / 64);
     hipLaunchKernelGGL(splitk_dgelu_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, a);
     return hipGetLastError();
   }
-  SplitArgs a{part, splits, n, out, out2, aux};
+  SplitArgs a{part, splits, n, (int)N, ldo, out, out2, aux};
   const dim3 grid(grid_for(n / 4)), block(256);
   switch (epi) {
     case EPI_F32: hipLaunchKernelGGL(splitk_kernel<EPI_F32>, grid, block, 0, stream, a); break;

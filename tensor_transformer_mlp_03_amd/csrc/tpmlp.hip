@@ -52,6 +52,10 @@ struct GemmPlan {
   TileCfg tile;
   int splits;
   int k_split;
+  // Hybrid plan (n_full > 0): output columns [0, n_full) are whole waves of
+  // unsplit 256 x 256 tiles with the product's own epilogue; only the tail
+  // columns [n_full, N) are split along K (splits, k_split) and reduced.
+  int n_full = 0;
 };
 
 int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
@@ -88,11 +92,35 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
       }
     }
   }
+  // Hybrid: when the 256 x 256 tiles are not a whole number of waves, run the
+  // largest block of columns that is as whole waves unsplit, and split only the
+  // tail.  The split-K round trip then covers the tail alone.
+  {
+    const int64_t tm = ceil_div(M, 256), tn = ceil_div(N, 256);
+    int64_t c = tn - 1;
+    while (c > 0 && (tm * c) % NUM_CU != 0) --c;
+    if (tm * tn > NUM_CU && c > 0) {
+      const int64_t kfull = (K + TILE_BK - 1) / TILE_BK * TILE_BK, nt = N - c * 256;
+      const double t_full = double(tm * c / NUM_CU) * double(256 * 256 * 2 * kfull) / CU_RATE_256;
+      for (int s = 2; s <= 16; ++s) {
+        const int64_t kslice = ((K + s - 1) / s + TILE_BK - 1) / TILE_BK * TILE_BK;
+        if (ceil_div(K, kslice) != s) continue;
+        if (kslice < 512) break;
+        const int64_t waves = (tm * (tn - c) * s + NUM_CU - 1) / NUM_CU;
+        const double t = t_full + double(waves) * double(256 * 256 * 2 * kslice) / CU_RATE_256 +
+                         double(s) * M * nt * 4 * 2 / SPLIT_BW + 2 * LAUNCH_S;
+        if (t < best_t * (1 - 1e-9)) {
+          best_t = t;
+          best = GemmPlan{TILE_256x256, s, (int)kslice, (int)(c * 256)};
+        }
+      }
+    }
+  }
   return best;
 }
 
 size_t part_bytes(const GemmPlan& p, int64_t M, int64_t N) {
-  return p.splits > 1 ? size_t(p.splits) * M * N * 4 : 0;
+  return p.splits > 1 ? size_t(p.splits) * M * (N - p.n_full) * 4 : 0;
 }
 
 // The forward products read A_i and B_i N-contiguous.  Transposing them first
@@ -308,11 +336,35 @@ hipError_t run_gemm(int kind, Layout la, Layout lb, Epi epi, const void* a, int6
     g.ldt = M;
     return timed(kind, s, [&] { return launch_gemm(p.tile, la, lb, epi, g, 1, s); });
   }
+  if (p.n_full > 0) {
+    // Hybrid: the whole-wave column block with the epilogue, then the tail
+    // columns split into `part` (one timing record for both launches).
+    const int64_t nf = p.n_full, nt = N - nf;
+    const GemmPlan pf{p.tile, 1, (int)((K + TILE_BK - 1) / TILE_BK * TILE_BK)};
+    GemmArgs gf = gemm_args(a, lda, b, ldb, M, nf, K, pf, out, N);
+    gf.out2 = out2;
+    gf.aux = aux;
+    gf.ldt = M;
+    const void* b_tail = static_cast<const uint16_t*>(b) + (lb == KC ? nf * ldb : nf);
+    GemmArgs gt = gemm_args(a, lda, b_tail, ldb, M, nt, K, p, part, nt);
+    hipError_t e = timed(kind, s, [&] {
+      hipError_t r = launch_gemm(p.tile, la, lb, epi, gf, 1, s);
+      return r != hipSuccess ? r : launch_gemm(p.tile, la, lb, EPI_F32, gt, p.splits, s);
+    });
+    if (e != hipSuccess) return e;
+    const size_t esz = epi == EPI_F32 ? 4 : 2;
+    void* out_tail = static_cast<char*>(out) + nf * esz;
+    uint16_t* out2_tail = out2 ? out2 + (epi == EPI_DGELU ? nf * M : nf) : nullptr;
+    const uint16_t* aux_tail = aux ? aux + nf : nullptr;
+    return timed(TPMLP_K_SPLITK_REDUCE, s, [&] {
+      return launch_splitk_epilogue(epi, part, p.splits, M, nt, out_tail, out2_tail, aux_tail, N, M, s);
+    });
+  }
   GemmArgs g = gemm_args(a, lda, b, ldb, M, N, K, p, part, N);
   hipError_t e = timed(kind, s, [&] { return launch_gemm(p.tile, la, lb, EPI_F32, g, p.splits, s); });
   if (e != hipSuccess) return e;
   return timed(TPMLP_K_SPLITK_REDUCE, s,
-               [&] { return launch_splitk_epilogue(epi, part, p.splits, M, N, out, out2, aux, s); });
+               [&] { return launch_splitk_epilogue(epi, part, p.splits, M, N, out, out2, aux, N, M, s); });
 }
 
 char* ws_at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }

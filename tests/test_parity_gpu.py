@@ -66,6 +66,12 @@ SMALL = [
     (8200, 136, 520, 2, True),
     # enough output tiles for 256 x 256 tiles, with the weights read N-contiguous
     (4104, 1032, 2056, 2, False),
+    # 4 x 65 output tiles of 256 x 256 (one wave and 4 more): the products with an
+    # [M, F_i] output run 256 tiles whole and split only the last column block
+    # along K (GeLU epilogue in the forward, dGeLU in the backward) ...
+    (1024, 1032, 16640, 1, True),
+    # ... and with an [M, H] output (float32 epilogue, forward and dX)
+    (1024, 16640, 1032, 1, False),
 ]
 
 
