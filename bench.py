@@ -134,9 +134,16 @@ def cpu_baseline(w, target_s=12.0):
                       f"(H={w.H}, F_i={w.F_i}); {dt:.2f} s"}
 
 
+def _order_entries(order):
+    """Recorded launch order as [(kind, kernel dispatches)]: a timing record covers one
+    dispatch, or two where a product runs as whole-wave tiles plus a split tail."""
+    return [(e, 1) if isinstance(e, str) else (e[0], int(e[1])) for e in order]
+
+
 def _kernel_kinds_of(csv_path, order):
-    """Dispatches of libtpmlp kernels in a rocprofv3 counter CSV, zipped in
-    dispatch order with the launch order that bench recorded for the same run."""
+    """Dispatches of libtpmlp kernels in a rocprofv3 counter CSV, in dispatch order,
+    grouped into the timing records that bench recorded for the same run: one
+    (kind, {"name", "counters"}) per record, counters summed over its dispatches."""
     rows = {}
     for r in csv.DictReader(open(csv_path)):
         if "tpmlp" not in r["Kernel_Name"]:
@@ -146,9 +153,20 @@ def _kernel_kinds_of(csv_path, order):
         rows[d]["counters"][r["Counter_Name"]] = rows[d]["counters"].get(r["Counter_Name"], 0.0) + float(
             r["Counter_Value"])
     disp = [rows[d] for d in sorted(rows)]
-    if len(disp) != len(order):
-        raise SystemExit(f"{csv_path}: {len(disp)} libtpmlp dispatches, {len(order)} recorded launches")
-    return list(zip(order, disp))
+    entries = _order_entries(order)
+    n_disp = sum(n for _, n in entries)
+    if len(disp) != n_disp:
+        raise SystemExit(f"{csv_path}: {len(disp)} libtpmlp dispatches, {n_disp} recorded "
+                         f"({len(entries)} timing records)")
+    out, i = [], 0
+    for kind, n in entries:
+        rec = {"name": disp[i]["name"], "counters": {}}
+        for d in disp[i:i + n]:
+            for c, v in d["counters"].items():
+                rec["counters"][c] = rec["counters"].get(c, 0.0) + v
+        out.append((kind, rec))
+        i += n
+    return out
 
 
 def _copy_scale(csv_path, counter, mib):
@@ -196,7 +214,9 @@ def summarize(d, config):
         f.write(f"# HBM traffic per launch, {w.name} (M={w.M}, H={w.H}, F_i={w.F_i}, t={w.t})\n\n")
         f.write("FETCH_SIZE and WRITE_SIZE (KiB per dispatch, L2-to-fabric traffic) from two rocprofv3 --pmc "
                 "runs of one step, each scaled by what the same counter reads for a plain copy of "
-                f"{mib} MiB through tpmlp_shard_sum (one part): fetch x{f_scale:.3f}, write x{w_scale:.3f}.\n\n")
+                f"{mib} MiB through tpmlp_shard_sum (one part): fetch x{f_scale:.3f}, write x{w_scale:.3f}. "
+                "A launch is one timed call of a kind: one kernel dispatch, or two where a product runs as "
+                "whole waves of unsplit tiles plus a split tail (their bytes are added).\n\n")
         for k in ("fetch", "write", "copy_fetch", "copy_write"):
             f.write(f"```\n{cmd[k]}\n```\n")
         f.write("\n| kind | launches | fetch MB/launch | write MB/launch | algorithmic MB/launch | ratio |\n"
@@ -225,13 +245,14 @@ def _summarize_counters(d, w, cmd, order, traffic):
     trace_csv = glob.glob(os.path.join(d, "trace", "*_kernel_trace.csv"))
     if not (os.path.exists(trace_order_path) and sq_csv and trace_csv and "sq" in cmd):
         return None
-    trace_order = json.load(open(trace_order_path))
+    trace_order = _order_entries(json.load(open(trace_order_path)))
     disp = sorted((int(r["Dispatch_Id"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
                   for r in csv.DictReader(open(trace_csv[0])) if "tpmlp" in r["Kernel_Name"])
-    disp = disp[len(disp) - len(trace_order):]  # the timed launches are the last ones
-    dur = {}
-    for kind, (_, ns) in zip(trace_order, disp):
-        dur.setdefault(kind, []).append(ns)
+    disp = disp[len(disp) - sum(n for _, n in trace_order):]  # the timed launches are the last ones
+    dur, i = {}, 0
+    for kind, n in trace_order:  # a record's time is the sum of its dispatches
+        dur.setdefault(kind, []).append(sum(ns for _, ns in disp[i:i + n]))
+        i += n
     sq = {}
     for kind, rec in _kernel_kinds_of(sq_csv[0], order):
         a = sq.setdefault(kind, {"n": 0})
@@ -243,7 +264,9 @@ def _summarize_counters(d, w, cmd, order, traffic):
     with open(path, "w") as f:
         f.write(f"# Counters per kernel kind, {w.name} (M={w.M}, H={w.H}, F_i={w.F_i}, t={w.t})\n\n")
         f.write("Launch times from the kernel trace (the timed steps' dispatches), counters from one "
-                "rocprofv3 --pmc pass over one step:\n\n")
+                "rocprofv3 --pmc pass over one step. A launch is one timed call of a kind: one kernel "
+                "dispatch, or two where a product runs as whole waves of unsplit tiles plus a split tail "
+                "(their times and counters are added):\n\n")
         f.write("```\n" + cmd["trace"] + "\n" + cmd["sq"] + "\n```\n\n")
         f.write("- cycles = GRBM_GUI_ACTIVE / 8 (the counter is summed over the 8 XCDs); clock = cycles / launch time "
                 "(launches of 100 us or more only).\n"
@@ -278,7 +301,7 @@ def main():
     ap.add_argument("--config", type=int, default=3, help="workload index 0-4 (default 3)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--trace-order", default="",
-                    help="write the kernel kinds of the timed launches, in order, to this JSON file")
+                    help="write [kernel kind, kernel dispatches] of the timed launches, in order, to this JSON file")
     ap.add_argument("--summarize", default="",
                     help="directory of rocprofv3 CSV outputs to summarize into profiles/ (no GPU needed)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -337,7 +360,7 @@ def main():
     log(f"[bench] timed {args.steps} steps in {t1 - t0:.4f} s")
     if args.trace_order:
         with open(args.trace_order, "w") as f:
-            json.dump([k for k, _ in L.tpmlp_timing_records()], f)
+            json.dump([[k, n] for (k, _), n in zip(L.tpmlp_timing_records(), L.tpmlp_timing_dispatches())], f)
 
     ms_per_step = (t1 - t0) * 1e3 / max(args.steps, 1)
     flops_step = w.model_flops_per_shard() * len(shards)

@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define TPMLP_ABI_VERSION 2
+#define TPMLP_ABI_VERSION 3
 #define TPMLP_MAX_SHARDS 64
 
 typedef uint16_t tpmlp_bf16; /* raw bf16 bits */
@@ -193,6 +193,12 @@ tpmlp_status tpmlp_timing_end(int* counts, double* total_ms, int* dropped);
  * of records (or -1 if kinds or ms is NULL).  Valid until the next
  * tpmlp_timing_begin on the calling thread. */
 int tpmlp_timing_records(int* kinds, double* ms, int capacity);
+
+/* Kernel dispatches inside each of those records, in the same order: 1, or 2
+ * for a product planned as whole-wave tiles plus a split tail (one record
+ * spans both launches).  Returns the number of records (or -1 if dispatches is
+ * NULL).  Lets a profiler's per-dispatch list be matched to the records. */
+int tpmlp_timing_dispatches(int* dispatches, int capacity);
 
 #ifdef __cplusplus
 }

@@ -56,6 +56,7 @@ _SIGS = {
     "tpmlp_timing_begin": ([_int], _int),
     "tpmlp_timing_end": ([ctypes.POINTER(_int), ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_int)], _int),
     "tpmlp_timing_records": ([ctypes.POINTER(_int), ctypes.POINTER(ctypes.c_double), _int], _int),
+    "tpmlp_timing_dispatches": ([ctypes.POINTER(_int), _int], _int),
 }
 
 
@@ -236,3 +237,12 @@ def tpmlp_timing_records():
     ms = (ctypes.c_double * max(n, 1))()
     n = lib().tpmlp_timing_records(kinds, ms, n)
     return [(tpmlp_kernel_name(kinds[i]), ms[i]) for i in range(n)]
+
+
+def tpmlp_timing_dispatches():
+    """Kernel dispatches inside each record of the last timing window (1, or 2
+    for a product run as whole-wave tiles plus a split tail)."""
+    n = lib().tpmlp_timing_dispatches((ctypes.c_int * 1)(), 0)
+    out = (ctypes.c_int * max(n, 1))()
+    n = lib().tpmlp_timing_dispatches(out, n)
+    return [out[i] for i in range(n)]

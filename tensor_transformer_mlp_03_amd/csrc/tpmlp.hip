@@ -228,8 +228,9 @@ struct Timing {
   bool on = false;
   int cap = 0, n = 0, dropped = 0;
   std::vector<hipEvent_t> ev;
-  std::vector<int> kind;
+  std::vector<int> kind, disp;   // per record: kernel kind, kernel dispatches inside it
   std::vector<int> last_kind;     // records of the last finished timing window
+  std::vector<int> last_disp;
   std::vector<double> last_ms;
   ~Timing() {
     for (hipEvent_t e : ev) (void)hipEventDestroy(e);
@@ -237,8 +238,10 @@ struct Timing {
 };
 thread_local Timing g_timing;
 
+// One timing record of kind `kind` around `launch`, which enqueues `dispatches`
+// kernels (a hybrid split product is two).
 template <class F>
-hipError_t timed(int kind, hipStream_t s, F&& launch) {
+hipError_t timed(int kind, hipStream_t s, F&& launch, int dispatches = 1) {
   Timing& t = g_timing;
   if (!t.on) return launch();
   if (t.n >= t.cap) {
@@ -251,6 +254,7 @@ hipError_t timed(int kind, hipStream_t s, F&& launch) {
   if (e != hipSuccess) return e;
   e = hipEventRecord(t.ev[2 * t.n + 1], s);
   if (e != hipSuccess) return e;
+  t.disp[t.n] = dispatches;
   t.kind[t.n++] = kind;
   return hipSuccess;
 }
@@ -347,10 +351,13 @@ hipError_t run_gemm(int kind, Layout la, Layout lb, Epi epi, const void* a, int6
     gf.ldt = M;
     const void* b_tail = static_cast<const uint16_t*>(b) + (lb == KC ? nf * ldb : nf);
     GemmArgs gt = gemm_args(a, lda, b_tail, ldb, M, nt, K, p, part, nt);
-    hipError_t e = timed(kind, s, [&] {
-      hipError_t r = launch_gemm(p.tile, la, lb, epi, gf, 1, s);
-      return r != hipSuccess ? r : launch_gemm(p.tile, la, lb, EPI_F32, gt, p.splits, s);
-    });
+    hipError_t e = timed(
+        kind, s,
+        [&] {
+          hipError_t r = launch_gemm(p.tile, la, lb, epi, gf, 1, s);
+          return r != hipSuccess ? r : launch_gemm(p.tile, la, lb, EPI_F32, gt, p.splits, s);
+        },
+        2);
     if (e != hipSuccess) return e;
     const size_t esz = epi == EPI_F32 ? 4 : 2;
     void* out_tail = static_cast<char*>(out) + nf * esz;
@@ -674,6 +681,7 @@ tpmlp_status tpmlp_timing_begin(int capacity) {
   for (hipEvent_t e : t.ev) (void)hipEventDestroy(e);
   t.ev.assign(2 * size_t(capacity), nullptr);
   t.kind.assign(capacity, 0);
+  t.disp.assign(capacity, 1);
   for (auto& e : t.ev) {
     hipError_t r = hipEventCreate(&e);
     if (r != hipSuccess) {
@@ -699,6 +707,7 @@ tpmlp_status tpmlp_timing_end(int* counts, double* total_ms, int* dropped) {
   if (dropped) *dropped = t.dropped;
   t.on = false;
   t.last_kind.clear();
+  t.last_disp.clear();
   t.last_ms.clear();
   for (int i = 0; i < t.n; ++i) {
     hipError_t e = hipEventSynchronize(t.ev[2 * i + 1]);
@@ -709,6 +718,7 @@ tpmlp_status tpmlp_timing_end(int* counts, double* total_ms, int* dropped) {
     counts[t.kind[i]] += 1;
     total_ms[t.kind[i]] += ms;
     t.last_kind.push_back(t.kind[i]);
+    t.last_disp.push_back(t.disp[i]);
     t.last_ms.push_back(ms);
   }
   t.n = 0;
@@ -723,6 +733,14 @@ int tpmlp_timing_records(int* kinds, double* ms, int capacity) {
     kinds[i] = t.last_kind[i];
     ms[i] = t.last_ms[i];
   }
+  return n;
+}
+
+int tpmlp_timing_dispatches(int* dispatches, int capacity) {
+  if (!dispatches) return -1;
+  const Timing& t = g_timing;
+  const int n = (int)t.last_disp.size();
+  for (int i = 0; i < n && i < capacity; ++i) dispatches[i] = t.last_disp[i];
   return n;
 }
 
