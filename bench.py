@@ -343,13 +343,28 @@ def main():
     d = DeviceMLP(inp, store_p=not w.recompute, driver=driver)
     del inp
     torch.cuda.synchronize()
+    per_launch = gemm_flops(w)
+    # Warmup, with every launch timed: the per-kind breakdown and the choice of
+    # the dominant GEMM kind.  A timed launch delays the next kernel by a few
+    # microseconds, so the timed steps below time only the dominant kind (all
+    # kinds when a profiler run needs every launch's kind in order).
     log("[bench] inputs resident; warmup")
-    for _ in range(args.warmup):
-        d.step()
+    warm_stats = None
+    if args.warmup:
+        L.tpmlp_timing_begin(16 * (len(shards) + 1) * args.warmup)
+        for _ in range(args.warmup):
+            d.step()
+        torch.cuda.synchronize()
+        warm_stats, _ = L.tpmlp_timing_end()
     torch.cuda.synchronize()
 
     n_launch = 16 * (len(shards) + 1) * max(args.steps, 1)
-    L.tpmlp_timing_begin(n_launch)
+    dom = None
+    if warm_stats and not args.trace_order:
+        dom = max((n for n in per_launch if warm_stats.get(n, (0, 0))[0]), key=lambda n: warm_stats[n][1])
+        L.tpmlp_timing_begin_kinds(n_launch, [dom])
+    else:
+        L.tpmlp_timing_begin(n_launch)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -357,7 +372,8 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     stats, dropped = L.tpmlp_timing_end()
-    log(f"[bench] timed {args.steps} steps in {t1 - t0:.4f} s")
+    log(f"[bench] timed {args.steps} steps in {t1 - t0:.4f} s"
+        + (f" (launches of {dom} timed)" if dom else " (every launch timed)"))
     if args.trace_order:
         with open(args.trace_order, "w") as f:
             json.dump([[k, n] for (k, _), n in zip(L.tpmlp_timing_records(), L.tpmlp_timing_dispatches())], f)
@@ -366,17 +382,19 @@ def main():
     flops_step = w.model_flops_per_shard() * len(shards)
     value = flops_step / (ms_per_step * 1e-3) / 1e12
 
-    per_launch = gemm_flops(w)
     kernels = {}
-    for name, (count, total_ms) in stats.items():
+    src = warm_stats if dom else stats
+    log(f"[bench] per kernel kind, {'warmup' if dom else 'timed'} steps:")
+    for name, (count, total_ms) in src.items():
         if count:
             kernels[name] = {"launches": count, "avg_us": round(total_ms * 1e3 / count, 2),
-                             "share": round(total_ms / sum(v[1] for v in stats.values()), 4)}
+                             "share": round(total_ms / sum(v[1] for v in src.values()), 4)}
             if name in per_launch:
                 kernels[name]["tflops"] = round(per_launch[name] / (total_ms * 1e-3 / count) / 1e12, 1)
     for name, k in sorted(kernels.items(), key=lambda kv: -kv[1]["share"]):
         log(f"  {name:16s} {k}")
-    dom = max((n for n in kernels if n in per_launch), key=lambda n: stats[n][1])
+    if dom is None:
+        dom = max((n for n in kernels if n in per_launch), key=lambda n: stats[n][1])
     avg_s = stats[dom][1] * 1e-3 / stats[dom][0]
     achieved = per_launch[dom] / avg_s / 1e12
     traffic = read_traffic(w.name)

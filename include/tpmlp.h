@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define TPMLP_ABI_VERSION 3
+#define TPMLP_ABI_VERSION 4
 #define TPMLP_MAX_SHARDS 64
 
 typedef uint16_t tpmlp_bf16; /* raw bf16 bits */
@@ -176,11 +176,21 @@ typedef enum {
 /* Static name of a kernel kind ("?" if out of range). */
 const char* tpmlp_kernel_name(int kind);
 
-/* Start recording a HIP event pair around every kernel the library enqueues on
- * the calling thread, on the stream it is enqueued on, for up to `capacity`
- * launches (events are created here, outside any timed region).  Restarting
- * discards earlier records. */
+/* Start timing every kernel launch the library enqueues on the calling thread,
+ * for up to `capacity` launches, with a HIP event pair per launch (events are
+ * created here, outside any timed region).  The pair is bound to the launch's
+ * kernel dispatches on their stream (hipExtLaunchKernel): it holds the start of
+ * the first and the end of the last, and inserts nothing between kernels.
+ * Restarting discards earlier records. */
 tpmlp_status tpmlp_timing_begin(int capacity);
+
+/* As tpmlp_timing_begin, but only launches of the kinds whose bit (1u << kind)
+ * is set in `kinds` are timed and recorded; the others run as with timing off.
+ * Each timed launch makes its dispatches report their start and end times,
+ * which delays the next kernel by a few microseconds; timing one kind keeps
+ * that cost off the rest.  TPMLP_ERR_SHAPE if capacity < 1 or `kinds` is zero
+ * or has a bit at or above TPMLP_K_COUNT. */
+tpmlp_status tpmlp_timing_begin_kinds(int capacity, unsigned kinds);
 
 /* Stop recording, wait for the recorded events and add up, per kernel kind, the
  * launches (`counts[kind]`) and their total milliseconds (`total_ms[kind]`).

@@ -54,6 +54,7 @@ _SIGS = {
     "tpmlp_tp_bwd": ([_vp, _vp, _PP, _PP, _PP, _PP, _PP, _PP, _vp, _int, _i64, _i64, _i64, _vp, _sz, _vp], _int),
     "tpmlp_shard_sum": ([_PP, _int, _vp, _i64, _vp], _int),
     "tpmlp_timing_begin": ([_int], _int),
+    "tpmlp_timing_begin_kinds": ([_int, ctypes.c_uint], _int),
     "tpmlp_timing_end": ([ctypes.POINTER(_int), ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_int)], _int),
     "tpmlp_timing_records": ([ctypes.POINTER(_int), ctypes.POINTER(ctypes.c_double), _int], _int),
     "tpmlp_timing_dispatches": ([ctypes.POINTER(_int), _int], _int),
@@ -219,6 +220,21 @@ def tpmlp_shard_sum(parts, out, stream=None):
 
 def tpmlp_timing_begin(capacity: int):
     _check(lib().tpmlp_timing_begin(capacity), "tpmlp_timing_begin")
+
+
+def tpmlp_timing_begin_kinds(capacity: int, kinds):
+    """Time only the launches of the named kernel kinds."""
+    mask = 0
+    for name in kinds:
+        mask |= 1 << kernel_kind(name)
+    _check(lib().tpmlp_timing_begin_kinds(capacity, mask), "tpmlp_timing_begin_kinds")
+
+
+def kernel_kind(name: str) -> int:
+    for k in range(KERNEL_COUNT):
+        if tpmlp_kernel_name(k) == name:
+            return k
+    raise ValueError(f"no kernel kind named {name!r}")
 
 
 def tpmlp_timing_end():

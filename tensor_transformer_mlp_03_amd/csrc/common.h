@@ -1,10 +1,38 @@
 // Internal declarations shared by the library's host and kernel sources.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace tpmlp {
+
+// Timing events that the calling thread's next kernel dispatches attach to: the
+// first dispatch takes `start`, the `left`-th takes `stop`.  hipExtLaunchKernel
+// binds them to the dispatch itself, so they hold the kernel's own start and end
+// times and add no marker packets between kernels.  Set by the library's timing
+// wrapper; all null outside a timing window.
+struct LaunchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+  int left = 0;
+};
+extern thread_local LaunchEvents g_launch_events;
+
+// Every kernel of the library takes one argument struct by value and is launched here.
+template <typename T>
+hipError_t launch_kernel(void (*kernel)(T), dim3 grid, dim3 block, hipStream_t s, T arg) {
+  LaunchEvents& le = g_launch_events;
+  hipEvent_t start = nullptr, stop = nullptr;
+  if (le.left > 0) {
+    start = le.start;
+    le.start = nullptr;
+    if (--le.left == 0) stop = le.stop;
+  }
+  void* args[] = {&arg};
+  const hipError_t e = hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, args, 0, s, start,
+                                          stop, 0);
+  return e != hipSuccess ? e : hipGetLastError();
+}
 
 // How an operand sits in memory, seen from the GEMM C[m,n] = sum_k A[m,k] B[k,n].
 //   KC: K is the contiguous dimension (A stored [M][ld], B stored [N][ld]).

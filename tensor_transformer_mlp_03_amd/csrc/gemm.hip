@@ -876,11 +876,9 @@ template <int BM, int BN, int WM_, int WN_, int LA, int LB, int EPI>
 hipError_t launch_one(const GemmArgs& a, int splits, hipStream_t s) {
   const int blocks = a.tiles_m * a.tiles_n * splits;
   if constexpr (BM == 256 && LA == KC)
-    hipLaunchKernelGGL((kern::gemm_w4_kernel<LB, EPI>), dim3(blocks), dim3(256), 0, s, a);
+    return launch_kernel(kern::gemm_w4_kernel<LB, EPI>, dim3(blocks), dim3(256), s, a);
   else
-    hipLaunchKernelGGL((kern::gemm_kernel<BM, BN, WM_, WN_, LA, LB, EPI>), dim3(blocks), dim3(64 * WM_ * WN_), 0, s,
-                       a);
-  return hipGetLastError();
+    return launch_kernel(kern::gemm_kernel<BM, BN, WM_, WN_, LA, LB, EPI>, dim3(blocks), dim3(64 * WM_ * WN_), s, a);
 }
 
 template <int BM, int BN, int WM_, int WN_>

@@ -218,8 +218,7 @@ hipError_t launch_sum(const float* const* parts, int n_parts, float* out, int64_
   a.n_parts = n_parts;
   a.n4 = n / 4;
   a.out = out;
-  hipLaunchKernelGGL(sum_kernel, dim3(grid_for(a.n4)), dim3(256), 0, stream, a);
-  return hipGetLastError();
+  return launch_kernel(sum_kernel, dim3(grid_for(a.n4)), dim3(256), stream, a);
 }
 
 hipError_t launch_splitk_epilogue(Epi epi, const float* part, int splits, int64_t M, int64_t N, void* out,
@@ -230,18 +229,16 @@ hipError_t launch_splitk_epilogue(Epi epi, const float* part, int splits, int64_
   if (epi == EPI_DGELU) {
     SplitDGeluArgs a{part, splits, (int)M, (int)N, ldo, ldt, static_cast<uint16_t*>(out), out2, aux};
     const int64_t tiles = ((M + 63) / 64) * ((N + 63) / 64);
-    hipLaunchKernelGGL(splitk_dgelu_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, a);
-    return hipGetLastError();
+    return launch_kernel(splitk_dgelu_kernel, dim3((unsigned)tiles), dim3(256), stream, a);
   }
   SplitArgs a{part, splits, n, (int)N, ldo, out, out2, aux};
   const dim3 grid(grid_for(n / 4)), block(256);
   switch (epi) {
-    case EPI_F32: hipLaunchKernelGGL(splitk_kernel<EPI_F32>, grid, block, 0, stream, a); break;
-    case EPI_GELU: hipLaunchKernelGGL(splitk_kernel<EPI_GELU>, grid, block, 0, stream, a); break;
-    case EPI_BF16: hipLaunchKernelGGL(splitk_kernel<EPI_BF16>, grid, block, 0, stream, a); break;
+    case EPI_F32: return launch_kernel(splitk_kernel<EPI_F32>, grid, block, stream, a);
+    case EPI_GELU: return launch_kernel(splitk_kernel<EPI_GELU>, grid, block, stream, a);
+    case EPI_BF16: return launch_kernel(splitk_kernel<EPI_BF16>, grid, block, stream, a);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 hipError_t launch_transpose(const uint16_t* in, int64_t R, int64_t C, uint16_t* out, hipStream_t stream) {
@@ -252,8 +249,7 @@ hipError_t launch_transpose(const uint16_t* in, int64_t R, int64_t C, uint16_t* 
   a.C = C;
   a.row_groups = (int)((R + 255) / 256);
   const int64_t blocks = (int64_t)a.row_groups * ((C + 63) / 64);
-  hipLaunchKernelGGL(transpose_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
-  return hipGetLastError();
+  return launch_kernel(transpose_kernel, dim3((unsigned)blocks), dim3(256), stream, a);
 }
 
 }  // namespace tpmlp

@@ -27,6 +27,9 @@
 #include <vector>
 
 namespace tpmlp {
+
+thread_local LaunchEvents g_launch_events;
+
 namespace {
 
 constexpr int64_t MAX_DIM = int64_t(1) << 24;
@@ -222,10 +225,14 @@ tpmlp_status check_device() {
 }
 
 // ---------------------------------------------------------------------------
-// Kernel timing: an event pair around each launch while enabled.
+// Kernel timing: while enabled, an event pair bound to each timed call's first
+// and last kernel dispatch (launch_kernel; g_launch_events is defined at the
+// top of this file).
 // ---------------------------------------------------------------------------
+
 struct Timing {
   bool on = false;
+  unsigned kinds = 0;  // bit k set: launches of kind k are timed
   int cap = 0, n = 0, dropped = 0;
   std::vector<hipEvent_t> ev;
   std::vector<int> kind, disp;   // per record: kernel kind, kernel dispatches inside it
@@ -243,16 +250,21 @@ thread_local Timing g_timing;
 template <class F>
 hipError_t timed(int kind, hipStream_t s, F&& launch, int dispatches = 1) {
   Timing& t = g_timing;
-  if (!t.on) return launch();
+  if (!t.on || !((t.kinds >> kind) & 1u)) return launch();
   if (t.n >= t.cap) {
     ++t.dropped;
     return launch();
   }
-  hipError_t e = hipEventRecord(t.ev[2 * t.n], s);
+  LaunchEvents& le = g_launch_events;
+  le = LaunchEvents{t.ev[2 * t.n], t.ev[2 * t.n + 1], dispatches};
+  hipError_t e = launch();
+  const LaunchEvents rest = le;
+  le = LaunchEvents{};
   if (e != hipSuccess) return e;
-  e = launch();
-  if (e != hipSuccess) return e;
-  e = hipEventRecord(t.ev[2 * t.n + 1], s);
+  // A call that dispatched fewer kernels than it declared leaves an event
+  // unbound: record it on the stream instead.
+  if (rest.start) e = hipEventRecord(rest.start, s);
+  if (e == hipSuccess && rest.left > 0) e = hipEventRecord(rest.stop, s);
   if (e != hipSuccess) return e;
   t.disp[t.n] = dispatches;
   t.kind[t.n++] = kind;
@@ -674,9 +686,13 @@ tpmlp_status tpmlp_tp_bwd(const tpmlp_bf16* dZ, const tpmlp_bf16* X, const tpmlp
   return TPMLP_OK;
 }
 
-tpmlp_status tpmlp_timing_begin(int capacity) {
+tpmlp_status tpmlp_timing_begin(int capacity) { return tpmlp_timing_begin_kinds(capacity, (1u << TPMLP_K_COUNT) - 1); }
+
+tpmlp_status tpmlp_timing_begin_kinds(int capacity, unsigned kinds) {
   g_last_error.clear();
   if (capacity < 1) return fail(TPMLP_ERR_SHAPE, "capacity must be positive");
+  if (kinds == 0 || (kinds >> TPMLP_K_COUNT) != 0)
+    return fail(TPMLP_ERR_SHAPE, "kinds must be a nonzero mask of bits below TPMLP_K_COUNT");
   Timing& t = g_timing;
   for (hipEvent_t e : t.ev) (void)hipEventDestroy(e);
   t.ev.assign(2 * size_t(capacity), nullptr);
@@ -692,6 +708,7 @@ tpmlp_status tpmlp_timing_begin(int capacity) {
   t.cap = capacity;
   t.n = 0;
   t.dropped = 0;
+  t.kinds = kinds;
   t.on = true;
   return TPMLP_OK;
 }

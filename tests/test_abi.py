@@ -43,7 +43,7 @@ def test_exports_every_declared_function():
 
 
 def test_version_and_strings():
-    assert L.tpmlp_abi_version() == 3
+    assert L.tpmlp_abi_version() == 4
     assert L.tpmlp_status_str(0) == "ok"
     assert L.tpmlp_status_str(ALIAS) == "output overlaps another buffer"
     assert L.tpmlp_status_str(99) == "unknown status"
@@ -168,4 +168,7 @@ def test_shard_sum_argument_errors():
 def test_timing_argument_errors():
     lib = L.lib()
     assert lib.tpmlp_timing_begin(0) == SHAPE
+    assert lib.tpmlp_timing_begin_kinds(8, 0) == SHAPE
+    assert lib.tpmlp_timing_begin_kinds(8, 1 << L.KERNEL_COUNT) == SHAPE
+    assert lib.tpmlp_timing_begin_kinds(0, 1) == SHAPE
     assert lib.tpmlp_timing_end(None, None, None) == NULL
