@@ -308,6 +308,32 @@ def test_timing_counts_launches():
     assert stats["bwd_recompute"][0] == 0
     assert stats["transpose"][0] == 2  # X^T and dZ^T once for both shards
     assert all(ms >= 0 for _, ms in stats.values())
+    recs = L.tpmlp_timing_records()
+    assert len(recs) == sum(n for n, _ in stats.values()) and all(ms > 0 for _, ms in recs)
+    # Only the chosen kind is timed; every other launch runs as with timing off.
+    L.tpmlp_timing_begin_kinds(64, ["fwd_gemm2"])
+    d.step()
+    stats, dropped = L.tpmlp_timing_end()
+    assert dropped == 0
+    assert {k: n for k, (n, _) in stats.items() if n} == {"fwd_gemm2": 2}
+    assert [k for k, _ in L.tpmlp_timing_records()] == ["fwd_gemm2"] * 2
+    assert L.tpmlp_timing_dispatches() == [1, 1]
+
+
+def test_timing_spans_hybrid_dispatches():
+    """A product planned as whole-wave tiles plus a split tail is one timing record
+    of two kernel dispatches, with a positive duration."""
+    from tensor_transformer_mlp_03_amd import _lib as L
+    from tensor_transformer_mlp_03_amd.device import DeviceMLP
+    w = I.custom_workload(315, M=1024, H=1032, F_i=16640, t=1)
+    say(f"[timing hybrid] M={w.M} H={w.H} F_i={w.F_i}")
+    d = DeviceMLP(I.make_inputs(w), store_p=True, driver=True)
+    L.tpmlp_timing_begin(64)
+    d.step()
+    L.tpmlp_timing_end()
+    recs, disp = L.tpmlp_timing_records(), L.tpmlp_timing_dispatches()
+    assert len(recs) == len(disp) and set(disp) <= {1, 2} and 2 in disp
+    assert all(ms > 0 for _, ms in recs)
 
 
 @pytest.mark.parametrize("M", [4096, 65536])
