@@ -65,7 +65,9 @@ typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef short i16x8_t __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
-constexpr int GROUP_M = 8;
+// Rows of tiles per group of the grouped order: an XCD's 32 co-resident tiles span
+// 4 rows x 8 columns of tiles (measured 1% faster than 8 x 4 and 2 x 16).
+constexpr int GROUP_M = 4;
 constexpr int NUM_XCD = 8;
 constexpr uint32_t OOB = 0x7FFFFFF0u;  // voffset past num_records: the load returns 0
 
