@@ -72,7 +72,7 @@ def gemm_flops(w):
     M, H, F = w.M, w.H, w.F_i
     f = 2.0 * M * H * F
     return {"fwd_gemm1_gelu": f, "fwd_gemm2": f, "bwd_recompute": f, "bwd_dgelu": f, "bwd_dB": f, "bwd_dA": f,
-            "bwd_dX": f}
+            "bwd_dX": f, "fwd_fused": 2 * f}
 
 
 def gemm_alg_bytes(w, recompute):
@@ -88,6 +88,8 @@ def gemm_alg_bytes(w, recompute):
         "bwd_dA": 2 * (M * H + M * F) + 4 * H * F,                                    # X^T, dP -> dA_i
         "bwd_dX": 2 * (M * F + H * F) + 4 * M * H,                                    # dP, A_i -> dX_i
         "transpose": 4 * M * H,                                                       # X -> X^T, dZ -> dZ^T
+        # X, A_i, B_i -> float32 partials of Z_i, one per chunk of 64 intermediate columns (+P)
+        "fwd_fused": 2 * (M * H + 2 * H * F) + 4 * M * H * (-(-F // 64)) + (0 if recompute else 2 * M * F),
     }
 
 

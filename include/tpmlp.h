@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define TPMLP_ABI_VERSION 4
+#define TPMLP_ABI_VERSION 5
 #define TPMLP_MAX_SHARDS 64
 
 typedef uint16_t tpmlp_bf16; /* raw bf16 bits */
@@ -81,6 +81,11 @@ size_t tpmlp_fwd_workspace_bytes(int64_t M, int64_t H, int64_t F_i);
  *   Z_i = G_i B_i          B_i[F_i,H] bf16 -> Z_i[M,H] float32 (the rank's partial)
  * P_save (nullable): if given, receives P_i[M,F_i] in bf16 (round to nearest even),
  * for a backward that keeps the pre-activation instead of recomputing it.
+ * For small hidden sizes (H a multiple of 64, at most 256) with small M, the
+ * call runs both products and GeLU in one fused launch per chunk of 64
+ * intermediate columns, G_i staying on chip, and adds the chunks' float32
+ * partials in chunk order (blockwise computation of the FFN: sequence-parallel
+ * series, Blockwise Parallel Transformer); G_i is rounded to bf16 either way.
  * Sources: "大模型训练" notes §3.1; QLM page §2.1.2.2 part 3. */
 tpmlp_status tpmlp_fwd(const tpmlp_bf16* X, const tpmlp_bf16* A_i, const tpmlp_bf16* B_i,
                        float* Z_i, tpmlp_bf16* P_save,
@@ -170,7 +175,8 @@ typedef enum {
   TPMLP_K_SPLITK_REDUCE = 7,  /* sum of split-K float32 partials */
   TPMLP_K_SHARD_SUM = 8,      /* tpmlp_shard_sum and the drivers' partial sums */
   TPMLP_K_TRANSPOSE = 9,      /* X^T and dZ^T for the weight-gradient products */
-  TPMLP_K_COUNT = 10
+  TPMLP_K_FWD_FUSED = 10,     /* Z_i chunk partials = GeLU(X A_i) B_i in one launch, G in LDS */
+  TPMLP_K_COUNT = 11
 } tpmlp_kernel_kind;
 
 /* Static name of a kernel kind ("?" if out of range). */

@@ -92,6 +92,30 @@ hipError_t launch_splitk_epilogue(Epi epi, const float* part, int splits, int64_
 // out[c][r] = in[r][c] for a bf16 matrix in[R][C] (R, C multiples of 8).
 hipError_t launch_transpose(const uint16_t* in, int64_t R, int64_t C, uint16_t* out, hipStream_t stream);
 
+// Fused forward for small hidden sizes (ffn.hip): workgroup (row block r,
+// chunk c) computes GeLU(X[r] A_i[:, c]) B_i[c, :] with G kept in LDS and
+// writes that float32 partial [rows][H] to slice c of `part` (slices of M x H,
+// in chunk order); P_save (nullable) receives X A_i in bf16.
+constexpr int FFN_ROWS = 64;    // rows of X per workgroup
+constexpr int FFN_CHUNK = 64;   // intermediate columns per workgroup
+constexpr int FFN_HMAX = 256;   // largest hidden size the fused kernel takes
+
+struct FfnArgs {
+  const uint16_t* x;   // X [M][H]
+  const uint16_t* a;   // A_i [H][lda]
+  const uint16_t* b;   // B_i [F][H]
+  float* part;         // ffn_chunks(F) slices of [M][H] float32
+  uint16_t* p_save;    // P_i [M][ldp] bf16, or null
+  int64_t lda, ldp;
+  int M, H, F;
+};
+
+// H a multiple of 64 and at most FFN_HMAX.
+bool ffn_fused_fits(int64_t H);
+// Number of partial slices (chunks of FFN_CHUNK intermediate columns).
+int ffn_chunks(int64_t F);
+hipError_t launch_ffn_fwd(const FfnArgs& a, hipStream_t stream);
+
 int tile_bm(TileCfg t);
 int tile_bn(TileCfg t);
 constexpr int TILE_BK = 64;

@@ -142,14 +142,34 @@ bool transpose_weights(int64_t M, int64_t H, int64_t F) {
   return saved > TRANSPOSE_MARGIN * cost;
 }
 
+// The fused forward (both products and GeLU in one launch, G kept in LDS) is
+// taken for hidden sizes it holds (H a multiple of 64, at most 256) when its
+// float32 chunk partials, F/64 slices of M x H, stay small: it trades G's trip
+// through memory (4 M F bytes) and a launch for partials of M H F / 16 bytes,
+// which pays only where the shard's time is launch and memory latency.
+constexpr size_t FUSED_PART_MAX = size_t(8) << 20;
+
+bool fused_fwd(int64_t M, int64_t H, int64_t F) {
+  return ffn_fused_fits(H) && size_t(ffn_chunks(F)) * M * H * 4 <= FUSED_PART_MAX;
+}
+
 struct FwdPlan {
   GemmPlan g1, g2;
-  bool wt;  // products read A_i^T and B_i^T from the workspace
+  bool wt;     // products read A_i^T and B_i^T from the workspace
+  bool fused;  // one fused launch (chunk partials at off_part) and their sum
   size_t off_G, off_At, off_Bt, off_part, total;
 };
 
 FwdPlan plan_fwd(int64_t M, int64_t H, int64_t F) {
   FwdPlan p;
+  p.fused = fused_fwd(M, H, F);
+  if (p.fused) {
+    p.g1 = p.g2 = GemmPlan{TILE_128x128, 1, 0};
+    p.wt = false;
+    p.off_G = p.off_At = p.off_Bt = p.off_part = 0;
+    p.total = ffn_chunks(F) > 1 ? align_up(size_t(ffn_chunks(F)) * M * H * 4) : WS_ALIGN;
+    return p;
+  }
   p.g1 = plan_gemm(M, F, H);
   p.g2 = plan_gemm(M, H, F);
   p.wt = transpose_weights(M, H, F);
@@ -395,6 +415,27 @@ hipError_t enqueue_fwd(const tpmlp_bf16* X, const tpmlp_bf16* A, const tpmlp_bf1
   uint16_t* G = reinterpret_cast<uint16_t*>(ws_at(ws, p.off_G));
   float* part = reinterpret_cast<float*>(ws_at(ws, p.off_part));
   hipError_t e;
+  if (p.fused) {
+    // Z_i = GeLU(X A_i) B_i per chunk of 64 intermediate columns, G in LDS;
+    // a single chunk writes Z_i itself, more are added in chunk order.
+    const int chunks = ffn_chunks(F);
+    FfnArgs fa{};
+    fa.x = X;
+    fa.a = A;
+    fa.b = B;
+    fa.part = chunks > 1 ? part : Z;
+    fa.p_save = P_save;
+    fa.lda = F;
+    fa.ldp = F;
+    fa.M = (int)M;
+    fa.H = (int)H;
+    fa.F = (int)F;
+    e = timed(TPMLP_K_FWD_FUSED, s, [&] { return launch_ffn_fwd(fa, s); });
+    if (e != hipSuccess || chunks == 1) return e;
+    return timed(TPMLP_K_SPLITK_REDUCE, s, [&] {
+      return launch_splitk_epilogue(EPI_F32, part, chunks, M, H, Z, nullptr, nullptr, H, M, s);
+    });
+  }
   if (p.wt) {
     uint16_t* At = reinterpret_cast<uint16_t*>(ws_at(ws, p.off_At));
     uint16_t* Bt = reinterpret_cast<uint16_t*>(ws_at(ws, p.off_Bt));
@@ -504,7 +545,7 @@ const char* tpmlp_last_error(void) { return g_last_error.c_str(); }
 
 const char* tpmlp_kernel_name(int kind) {
   static const char* names[TPMLP_K_COUNT] = {"fwd_gemm1_gelu", "fwd_gemm2", "bwd_recompute", "bwd_dgelu",
-                                             "bwd_dB", "bwd_dA", "bwd_dX", "splitk_reduce", "shard_sum", "transpose"};
+                                             "bwd_dB", "bwd_dA", "bwd_dX", "splitk_reduce", "shard_sum", "transpose", "fwd_fused"};
   return (kind >= 0 && kind < TPMLP_K_COUNT) ? names[kind] : "?";
 }
 

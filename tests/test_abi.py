@@ -43,7 +43,7 @@ def test_exports_every_declared_function():
 
 
 def test_version_and_strings():
-    assert L.tpmlp_abi_version() == 4
+    assert L.tpmlp_abi_version() == 5
     assert L.tpmlp_status_str(0) == "ok"
     assert L.tpmlp_status_str(ALIAS) == "output overlaps another buffer"
     assert L.tpmlp_status_str(99) == "unknown status"

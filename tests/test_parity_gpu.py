@@ -72,6 +72,14 @@ SMALL = [
     (1024, 1032, 16640, 1, True),
     # ... and with an [M, H] output (float32 epilogue, forward and dX)
     (1024, 16640, 1032, 1, False),
+    # fused forward (H a multiple of 64, at most 256): ragged rows and a ragged last
+    # chunk of intermediate columns, with the pre-activation kept from it ...
+    (200, 192, 392, 2, True),
+    # ... one chunk (the kernel writes Z_i itself), the smallest hidden size ...
+    (8, 64, 8, 1, True),
+    # ... many chunks and row blocks, backward recomputing
+    (520, 128, 1032, 2, False),
+    (72, 256, 2056, 2, True),
 ]
 
 
@@ -295,7 +303,7 @@ def test_shard_sum_kernel_exact():
 
 def test_timing_counts_launches():
     from tensor_transformer_mlp_03_amd import _lib as L
-    w = I.custom_workload(314, M=256, H=256, F_i=256, t=2)
+    w = I.custom_workload(314, M=256, H=264, F_i=256, t=2)
     inp = I.make_inputs(w)
     from tensor_transformer_mlp_03_amd.device import DeviceMLP
     d = DeviceMLP(inp, store_p=True, driver=True)
@@ -318,6 +326,41 @@ def test_timing_counts_launches():
     assert {k: n for k, (n, _) in stats.items() if n} == {"fwd_gemm2": 2}
     assert [k for k, _ in L.tpmlp_timing_records()] == ["fwd_gemm2"] * 2
     assert L.tpmlp_timing_dispatches() == [1, 1]
+
+
+@pytest.mark.parametrize("shape", [(64, 256, 512), (200, 192, 392), (8, 64, 8)])
+def test_fused_forward_is_taken(shape):
+    """Small hidden sizes run the forward as one fused launch per shard (plus the
+    chunk sum when F_i spans more than one chunk of 64), never the two products."""
+    from tensor_transformer_mlp_03_amd import _lib as L
+    from tensor_transformer_mlp_03_amd.device import DeviceMLP
+    M, H, F = shape
+    say(f"[fused taken] M={M} H={H} F_i={F}")
+    w = I.custom_workload(316, M=M, H=H, F_i=F, t=2)
+    d = DeviceMLP(I.make_inputs(w), store_p=True, driver=True)
+    L.tpmlp_timing_begin(64)
+    d.forward()
+    stats, dropped = L.tpmlp_timing_end()
+    assert dropped == 0
+    counts = {k: n for k, (n, _) in stats.items() if n}
+    want = {"fwd_fused": 2, "shard_sum": 1}
+    if F > 64:
+        want["splitk_reduce"] = 2
+    assert counts == want
+
+
+def test_fused_forward_pre_activation():
+    """P_save written by the fused kernel is X A_i rounded once to bf16: within half
+    a bf16 ulp of the float64 product, plus float32 accumulation error."""
+    M, H, F = 136, 256, 520
+    say(f"[fused P_save] M={M} H={H} F_i={F}")
+    w = I.custom_workload(317, M=M, H=H, F_i=F, t=1)
+    inp = I.make_inputs(w)
+    d = run_device(inp, store_p=True)
+    P = O.decode_bf16(d.P[0].cpu().numpy().view(np.uint16))
+    ref = dec(inp.X) @ dec(inp.A[0])
+    bound = 2.0 ** -8 * np.abs(ref) + 1e-5 * np.abs(ref).max()
+    assert np.all(np.abs(P - ref) <= bound)
 
 
 def test_timing_spans_hybrid_dispatches():
