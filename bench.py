@@ -302,6 +302,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=3, help="workload index 0-4 (default 3)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--full-weights", action="store_true",
+                    help="run the t-shard driver over the whole weights A[H, t F_i], B[t F_i, H] (shards as views)")
     ap.add_argument("--trace-order", default="",
                     help="write [kernel kind, kernel dispatches] of the timed launches, in order, to this JSON file")
     ap.add_argument("--summarize", default="",
@@ -342,7 +344,10 @@ def main():
     log(f"[bench] workload {w.name}: M={w.M} H={w.H} F_i={w.F_i} t={w.t} shards={shards} "
         f"{'recompute' if w.recompute else 'store P'}; generating inputs")
     inp = I.make_inputs(w, shards=shards)
-    d = DeviceMLP(inp, store_p=not w.recompute, driver=driver)
+    if args.full_weights and not driver:
+        print("--full-weights needs every shard of the workload", file=sys.stderr)
+        sys.exit(2)
+    d = DeviceMLP(inp, store_p=not w.recompute, driver=driver, full_weights=args.full_weights)
     del inp
     torch.cuda.synchronize()
     per_launch = gemm_flops(w)
@@ -424,6 +429,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "M": w.M, "H": w.H, "F": w.F, "t": w.t, "F_i": w.F_i,
                    "shards_per_step": len(shards), "pre_activation": "recompute" if w.recompute else "stored",
+                   "weights": "whole (shard views)" if args.full_weights else "per-shard buffers",
                    "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4), "timing_dropped": dropped},
         "roofline": roofline,
         "cpu_baseline": None,

@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define TPMLP_ABI_VERSION 5
+#define TPMLP_ABI_VERSION 6
 #define TPMLP_MAX_SHARDS 64
 
 typedef uint16_t tpmlp_bf16; /* raw bf16 bits */
@@ -151,6 +151,31 @@ tpmlp_status tpmlp_tp_bwd(const tpmlp_bf16* dZ, const tpmlp_bf16* X,
                           float* const* dA_sh, float* const* dB_sh, float* const* dX_sh,
                           float* dX, int t, int64_t M, int64_t H, int64_t F_i,
                           void* ws, size_t ws_bytes, void* stream);
+
+/* The t-shard driver over unsharded weights, with no copy of the shards.  A is
+ * the whole first weight [H, t F_i] and B the whole second weight [t F_i, H];
+ * shard i reads A_i = columns [i F_i, (i+1) F_i) of A (a strided view, rows of
+ * t F_i elements) and B_i = rows [i F_i, (i+1) F_i) of B, which is exactly the
+ * column split of A and row split of B that makes the shards independent
+ * ("大模型训练" notes §3.1, A = [A_1 | A_2], B = [B_1; B_2]).
+ * P (nullable): t consecutive blocks [M, F_i] of bf16, block i receiving shard
+ * i's pre-activation as tpmlp_fwd's P_save.  Z[M,H] float32: the rank-order sum
+ * of the shards' partials (shards one after another, as tpmlp_tp_fwd).
+ * Workspace: tpmlp_tp_workspace_bytes(t, M, H, F_i).  t * F_i must be at most
+ * 2^24 (TPMLP_ERR_SHAPE). */
+tpmlp_status tpmlp_tp_fwd_full(const tpmlp_bf16* X, const tpmlp_bf16* A, const tpmlp_bf16* B,
+                               tpmlp_bf16* P, float* Z, int t, int64_t M, int64_t H, int64_t F_i,
+                               void* ws, size_t ws_bytes, void* stream);
+
+/* Backward over unsharded weights: dA[H, t F_i] and dB[t F_i, H] (float32) are
+ * the whole weight gradients, shard i writing its column block of dA (rows of
+ * t F_i elements) and its row block of dB; dX[M,H] is the rank-order sum of the
+ * shards' partial input gradients.  P: NULL => every shard recomputes its
+ * pre-activation; otherwise the t blocks written by tpmlp_tp_fwd_full. */
+tpmlp_status tpmlp_tp_bwd_full(const tpmlp_bf16* dZ, const tpmlp_bf16* X, const tpmlp_bf16* A,
+                               const tpmlp_bf16* B, const tpmlp_bf16* P,
+                               float* dA, float* dB, float* dX, int t, int64_t M, int64_t H, int64_t F_i,
+                               void* ws, size_t ws_bytes, void* stream);
 
 /* out[j] = parts[0][j] + parts[1][j] + ... + parts[t-1][j] (float32, left to right)
  * for j < n: the local stand-in for a sum all-reduce across t ranks

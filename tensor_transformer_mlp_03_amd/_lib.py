@@ -52,6 +52,8 @@ _SIGS = {
     "tpmlp_bwd": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _sz, _vp], _int),
     "tpmlp_tp_fwd": ([_vp, _PP, _PP, _PP, _PP, _vp, _int, _i64, _i64, _i64, _vp, _sz, _vp], _int),
     "tpmlp_tp_bwd": ([_vp, _vp, _PP, _PP, _PP, _PP, _PP, _PP, _vp, _int, _i64, _i64, _i64, _vp, _sz, _vp], _int),
+    "tpmlp_tp_fwd_full": ([_vp, _vp, _vp, _vp, _vp, _int, _i64, _i64, _i64, _vp, _sz, _vp], _int),
+    "tpmlp_tp_bwd_full": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _i64, _i64, _i64, _vp, _sz, _vp], _int),
     "tpmlp_shard_sum": ([_PP, _int, _vp, _i64, _vp], _int),
     "tpmlp_timing_begin": ([_int], _int),
     "tpmlp_timing_begin_kinds": ([_int, ctypes.c_uint], _int),
@@ -209,6 +211,26 @@ def tpmlp_tp_bwd(dZ, X, A_sh, B_sh, P_sh, dA_sh, dB_sh, dX_sh, dX, ws, stream=No
                             _ptr_array(dA_sh, t), _ptr_array(dB_sh, t), _ptr_array(dX_sh, t), _ptr(dX), t, M,
                             H, F, _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     _check(st, "tpmlp_tp_bwd")
+
+
+def tpmlp_tp_fwd_full(X, A, B, P, Z, t, ws, stream=None):
+    """All t shards' forward over the whole weights A[H, t F_i], B[t F_i, H] (no shard
+    copies); P: None or t blocks [M, F_i] of bf16; Z[M,H] float32 the summed output."""
+    M, H = X.shape
+    F = A.shape[1] // t
+    st = lib().tpmlp_tp_fwd_full(_ptr(X), _ptr(A), _ptr(B), _ptr(P), _ptr(Z), t, M, H, F, _ptr(ws),
+                                 ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "tpmlp_tp_fwd_full")
+
+
+def tpmlp_tp_bwd_full(dZ, X, A, B, P, dA, dB, dX, t, ws, stream=None):
+    """All t shards' backward over the whole weights; dA[H, t F_i] and dB[t F_i, H] are
+    the whole float32 weight gradients, dX the sum of the shards' partials."""
+    M, H = X.shape
+    F = A.shape[1] // t
+    st = lib().tpmlp_tp_bwd_full(_ptr(dZ), _ptr(X), _ptr(A), _ptr(B), _ptr(P), _ptr(dA), _ptr(dB), _ptr(dX), t,
+                                 M, H, F, _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "tpmlp_tp_bwd_full")
 
 
 def tpmlp_shard_sum(parts, out, stream=None):

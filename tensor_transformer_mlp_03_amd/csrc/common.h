@@ -89,8 +89,10 @@ hipError_t launch_splitk_epilogue(Epi epi, const float* part, int splits, int64_
                                   uint16_t* out2, const uint16_t* aux, int64_t ldo, int64_t ldt,
                                   hipStream_t stream);
 
-// out[c][r] = in[r][c] for a bf16 matrix in[R][C] (R, C multiples of 8).
-hipError_t launch_transpose(const uint16_t* in, int64_t R, int64_t C, uint16_t* out, hipStream_t stream);
+// out[c][r] = in[r][c] for a bf16 matrix in[R][C] with rows of ld_in >= C
+// elements (R, C, ld_in multiples of 8).
+hipError_t launch_transpose(const uint16_t* in, int64_t R, int64_t C, int64_t ld_in, uint16_t* out,
+                            hipStream_t stream);
 
 // Fused forward for small hidden sizes (ffn.hip): workgroup (row block r,
 // chunk c) computes GeLU(X[r] A_i[:, c]) B_i[c, :] with G kept in LDS and

@@ -169,7 +169,8 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 struct TransposeArgs {
   const uint16_t* in;
   uint16_t* out;
-  int64_t R, C;  // in is [R][C], out is [C][R]
+  int64_t R, C;  // in is [R][C] (rows of ld_in elements), out is [C][R]
+  int64_t ld_in;
   int row_groups;  // groups of four 64-row tiles
 };
 
@@ -187,12 +188,12 @@ __global__ void __launch_bounds__(256) transpose_kernel(TransposeArgs a) {
   const int64_t r0 = tr + lr, c0 = tc + lc;
   if (r0 >= a.R || c0 >= a.C) return;
   const __amdgpu_buffer_rsrc_t rs =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.in + tr * a.C + tc), (short)0, 0x7FFFFFF0, 0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.in + tr * a.ld_in + tc), (short)0, 0x7FFFFFF0, 0x00020000);
   u32x4_t v[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
     v[i] = __builtin_bit_cast(u32x4_t,
-                              __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)(((lr + i) * a.C + lc) * 2), 0, 0));
+                              __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)(((lr + i) * a.ld_in + lc) * 2), 0, 0));
   // Output row c0 + j takes element j of each of the 8 input rows: dword e
   // packs input rows 2e and 2e+1, i.e. the halves of v[2e] and v[2e+1] that
   // hold column j (low halves for even j, high halves for odd j).
@@ -241,12 +242,15 @@ hipError_t launch_splitk_epilogue(Epi epi, const float* part, int splits, int64_
   }
 }
 
-hipError_t launch_transpose(const uint16_t* in, int64_t R, int64_t C, uint16_t* out, hipStream_t stream) {
+hipError_t launch_transpose(const uint16_t* in, int64_t R, int64_t C, int64_t ld_in, uint16_t* out,
+                            hipStream_t stream) {
+  if (ld_in < C || (ld_in & 7)) return hipErrorInvalidValue;
   TransposeArgs a;
   a.in = in;
   a.out = out;
   a.R = R;
   a.C = C;
+  a.ld_in = ld_in;
   a.row_groups = (int)((R + 255) / 256);
   const int64_t blocks = (int64_t)a.row_groups * ((C + 63) / 64);
   return launch_kernel(transpose_kernel, dim3((unsigned)blocks), dim3(256), stream, a);

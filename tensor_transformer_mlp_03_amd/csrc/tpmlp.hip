@@ -364,9 +364,12 @@ GemmArgs gemm_args(const void* a, int64_t lda, const void* b, int64_t ldb, int64
 // float32 and the reduction applies the epilogue.
 hipError_t run_gemm(int kind, Layout la, Layout lb, Epi epi, const void* a, int64_t lda, const void* b,
                     int64_t ldb, int64_t M, int64_t N, int64_t K, const GemmPlan& p, void* out, uint16_t* out2,
-                    const uint16_t* aux, float* part, hipStream_t s) {
+                    const uint16_t* aux, float* part, hipStream_t s, int64_t ldo = 0) {
+  // ldo: row stride of out (and of out2 and aux for the GeLU and dGeLU
+  // epilogues); 0 means N.
+  if (ldo == 0) ldo = N;
   if (p.splits == 1) {
-    GemmArgs g = gemm_args(a, lda, b, ldb, M, N, K, p, out, N);
+    GemmArgs g = gemm_args(a, lda, b, ldb, M, N, K, p, out, ldo);
     g.out2 = out2;
     g.aux = aux;
     g.ldt = M;
@@ -377,7 +380,7 @@ hipError_t run_gemm(int kind, Layout la, Layout lb, Epi epi, const void* a, int6
     // columns split into `part` (one timing record for both launches).
     const int64_t nf = p.n_full, nt = N - nf;
     const GemmPlan pf{p.tile, 1, (int)((K + TILE_BK - 1) / TILE_BK * TILE_BK)};
-    GemmArgs gf = gemm_args(a, lda, b, ldb, M, nf, K, pf, out, N);
+    GemmArgs gf = gemm_args(a, lda, b, ldb, M, nf, K, pf, out, ldo);
     gf.out2 = out2;
     gf.aux = aux;
     gf.ldt = M;
@@ -396,20 +399,21 @@ hipError_t run_gemm(int kind, Layout la, Layout lb, Epi epi, const void* a, int6
     uint16_t* out2_tail = out2 ? out2 + (epi == EPI_DGELU ? nf * M : nf) : nullptr;
     const uint16_t* aux_tail = aux ? aux + nf : nullptr;
     return timed(TPMLP_K_SPLITK_REDUCE, s, [&] {
-      return launch_splitk_epilogue(epi, part, p.splits, M, nt, out_tail, out2_tail, aux_tail, N, M, s);
+      return launch_splitk_epilogue(epi, part, p.splits, M, nt, out_tail, out2_tail, aux_tail, ldo, M, s);
     });
   }
   GemmArgs g = gemm_args(a, lda, b, ldb, M, N, K, p, part, N);
   hipError_t e = timed(kind, s, [&] { return launch_gemm(p.tile, la, lb, EPI_F32, g, p.splits, s); });
   if (e != hipSuccess) return e;
   return timed(TPMLP_K_SPLITK_REDUCE, s,
-               [&] { return launch_splitk_epilogue(epi, part, p.splits, M, N, out, out2, aux, N, M, s); });
+               [&] { return launch_splitk_epilogue(epi, part, p.splits, M, N, out, out2, aux, ldo, M, s); });
 }
 
 char* ws_at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
 
 // Enqueue rank i's forward (arguments already checked).
-hipError_t enqueue_fwd(const tpmlp_bf16* X, const tpmlp_bf16* A, const tpmlp_bf16* B, float* Z,
+// A (A_i) has rows of lda >= F elements: a column block of a wider weight.
+hipError_t enqueue_fwd(const tpmlp_bf16* X, const tpmlp_bf16* A, int64_t lda, const tpmlp_bf16* B, float* Z,
                        tpmlp_bf16* P_save, int64_t M, int64_t H, int64_t F, void* ws, hipStream_t s) {
   const FwdPlan p = plan_fwd(M, H, F);
   uint16_t* G = reinterpret_cast<uint16_t*>(ws_at(ws, p.off_G));
@@ -425,7 +429,7 @@ hipError_t enqueue_fwd(const tpmlp_bf16* X, const tpmlp_bf16* A, const tpmlp_bf1
     fa.b = B;
     fa.part = chunks > 1 ? part : Z;
     fa.p_save = P_save;
-    fa.lda = F;
+    fa.lda = lda;
     fa.ldp = F;
     fa.M = (int)M;
     fa.H = (int)H;
@@ -439,9 +443,9 @@ hipError_t enqueue_fwd(const tpmlp_bf16* X, const tpmlp_bf16* A, const tpmlp_bf1
   if (p.wt) {
     uint16_t* At = reinterpret_cast<uint16_t*>(ws_at(ws, p.off_At));
     uint16_t* Bt = reinterpret_cast<uint16_t*>(ws_at(ws, p.off_Bt));
-    e = timed(TPMLP_K_TRANSPOSE, s, [&] { return launch_transpose(A, H, F, At, s); });
+    e = timed(TPMLP_K_TRANSPOSE, s, [&] { return launch_transpose(A, H, F, lda, At, s); });
     if (e != hipSuccess) return e;
-    e = timed(TPMLP_K_TRANSPOSE, s, [&] { return launch_transpose(B, F, H, Bt, s); });
+    e = timed(TPMLP_K_TRANSPOSE, s, [&] { return launch_transpose(B, F, H, H, Bt, s); });
     if (e != hipSuccess) return e;
     // P_i = X A_i; G_i = GeLU(P_i)      X: [M][H], A_i^T: [F][H] (both K-contig)
     e = run_gemm(TPMLP_K_FWD_GEMM1_GELU, KC, KC, EPI_GELU, X, H, At, H, M, F, H, p.g1, G, P_save,
@@ -452,7 +456,7 @@ hipError_t enqueue_fwd(const tpmlp_bf16* X, const tpmlp_bf16* A, const tpmlp_bf1
                     part, s);
   }
   // P_i = X A_i; G_i = GeLU(P_i)        X: [M][H] (K-contig), A_i: [H][F] (N-contig)
-  e = run_gemm(TPMLP_K_FWD_GEMM1_GELU, KC, MC, EPI_GELU, X, H, A, F, M, F, H, p.g1, G, P_save, nullptr,
+  e = run_gemm(TPMLP_K_FWD_GEMM1_GELU, KC, MC, EPI_GELU, X, H, A, lda, M, F, H, p.g1, G, P_save, nullptr,
                part, s);
   if (e != hipSuccess) return e;
   // Z_i = G_i B_i                      G_i: [M][F] (K-contig), B_i: [F][H] (N-contig)
@@ -467,16 +471,17 @@ hipError_t enqueue_transposes(const tpmlp_bf16* dZ, const tpmlp_bf16* X, int64_t
   const BwdPlan p = plan_bwd(M, H, 8, false);  // the transposes' offsets do not depend on F or recompute
   uint16_t* Xt = reinterpret_cast<uint16_t*>(ws_at(ws, p.off_Xt));
   uint16_t* dZt = reinterpret_cast<uint16_t*>(ws_at(ws, p.off_dZt));
-  hipError_t e = timed(TPMLP_K_TRANSPOSE, s, [&] { return launch_transpose(X, M, H, Xt, s); });
+  hipError_t e = timed(TPMLP_K_TRANSPOSE, s, [&] { return launch_transpose(X, M, H, H, Xt, s); });
   if (e != hipSuccess) return e;
-  return timed(TPMLP_K_TRANSPOSE, s, [&] { return launch_transpose(dZ, M, H, dZt, s); });
+  return timed(TPMLP_K_TRANSPOSE, s, [&] { return launch_transpose(dZ, M, H, H, dZt, s); });
 }
 
 // Enqueue rank i's backward (arguments already checked; X^T and dZ^T already
 // in the workspace).
-hipError_t enqueue_bwd(const tpmlp_bf16* dZ, const tpmlp_bf16* X, const tpmlp_bf16* A, const tpmlp_bf16* B,
-                       const tpmlp_bf16* P_saved, float* dX, float* dA, float* dB, int64_t M, int64_t H,
-                       int64_t F, void* ws, hipStream_t s) {
+// A (A_i) has rows of lda >= F elements and dA (dA_i) rows of ldda >= F.
+hipError_t enqueue_bwd(const tpmlp_bf16* dZ, const tpmlp_bf16* X, const tpmlp_bf16* A, int64_t lda,
+                       const tpmlp_bf16* B, const tpmlp_bf16* P_saved, float* dX, float* dA, int64_t ldda,
+                       float* dB, int64_t M, int64_t H, int64_t F, void* ws, hipStream_t s) {
   const bool recompute = P_saved == nullptr;
   const BwdPlan p = plan_bwd(M, H, F, recompute);
   const uint16_t* Xt = reinterpret_cast<const uint16_t*>(ws_at(ws, p.off_Xt));
@@ -491,12 +496,12 @@ hipError_t enqueue_bwd(const tpmlp_bf16* dZ, const tpmlp_bf16* X, const tpmlp_bf
     uint16_t* Pw = reinterpret_cast<uint16_t*>(ws_at(ws, p.off_P));
     if (p.wt) {
       uint16_t* At = reinterpret_cast<uint16_t*>(ws_at(ws, p.off_At));
-      e = timed(TPMLP_K_TRANSPOSE, s, [&] { return launch_transpose(A, H, F, At, s); });
+      e = timed(TPMLP_K_TRANSPOSE, s, [&] { return launch_transpose(A, H, F, lda, At, s); });
       if (e != hipSuccess) return e;
       e = run_gemm(TPMLP_K_BWD_RECOMPUTE, KC, KC, EPI_BF16, X, H, At, H, M, F, H, p.g0, Pw, nullptr, nullptr,
                    part, s);
     } else {
-      e = run_gemm(TPMLP_K_BWD_RECOMPUTE, KC, MC, EPI_BF16, X, H, A, F, M, F, H, p.g0, Pw, nullptr, nullptr,
+      e = run_gemm(TPMLP_K_BWD_RECOMPUTE, KC, MC, EPI_BF16, X, H, A, lda, M, F, H, p.g0, Pw, nullptr, nullptr,
                    part, s);
     }
     if (e != hipSuccess) return e;
@@ -510,10 +515,11 @@ hipError_t enqueue_bwd(const tpmlp_bf16* dZ, const tpmlp_bf16* X, const tpmlp_bf
   e = run_gemm(TPMLP_K_BWD_DB, KC, KC, EPI_F32, Gt, M, dZt, M, F, H, M, p.gdb, dB, nullptr, nullptr, part, s);
   if (e != hipSuccess) return e;
   // dA_i = X^T dP_i    X^T: [H][M] = [M'][K] (K-contig), dP_i: [M][F] = [K][N'] (N'-contig)
-  e = run_gemm(TPMLP_K_BWD_DA, KC, MC, EPI_F32, Xt, M, dP, F, H, F, M, p.gda, dA, nullptr, nullptr, part, s);
+  e = run_gemm(TPMLP_K_BWD_DA, KC, MC, EPI_F32, Xt, M, dP, F, H, F, M, p.gda, dA, nullptr, nullptr, part, s,
+               ldda);
   if (e != hipSuccess) return e;
   // dX_i = dP_i A_i^T  dP_i: [M][F] (K-contig), A_i: [H][F] = [N][K] (K-contig)
-  return run_gemm(TPMLP_K_BWD_DX, KC, KC, EPI_F32, dP, F, A, F, M, H, F, p.gdx, dX, nullptr, nullptr, part,
+  return run_gemm(TPMLP_K_BWD_DX, KC, KC, EPI_F32, dP, F, A, lda, M, H, F, p.gdx, dX, nullptr, nullptr, part,
                   s);
 }
 
@@ -574,7 +580,7 @@ tpmlp_status tpmlp_fwd(const tpmlp_bf16* X, const tpmlp_bf16* A_i, const tpmlp_b
   std::vector<Range> outs = {{Z_i, mh * 4, "Z_i"}, {P_save, P_save ? mf * 2 : 0, "P_save"}, {ws, need, "ws"}};
   if ((st = check_alias(outs, ins))) return st;
   if ((st = check_device())) return st;
-  hipError_t e = enqueue_fwd(X, A_i, B_i, Z_i, P_save, M, H, F_i, ws, static_cast<hipStream_t>(stream));
+  hipError_t e = enqueue_fwd(X, A_i, F_i, B_i, Z_i, P_save, M, H, F_i, ws, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? TPMLP_OK : hip_fail(e, "tpmlp_fwd launch");
 }
 
@@ -597,7 +603,7 @@ tpmlp_status tpmlp_bwd(const tpmlp_bf16* dZ, const tpmlp_bf16* X, const tpmlp_bf
   if ((st = check_device())) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = enqueue_transposes(dZ, X, M, H, ws, s);
-  if (e == hipSuccess) e = enqueue_bwd(dZ, X, A_i, B_i, P_saved, dX_i, dA_i, dB_i, M, H, F_i, ws, s);
+  if (e == hipSuccess) e = enqueue_bwd(dZ, X, A_i, F_i, B_i, P_saved, dX_i, dA_i, F_i, dB_i, M, H, F_i, ws, s);
   return e == hipSuccess ? TPMLP_OK : hip_fail(e, "tpmlp_bwd launch");
 }
 
@@ -663,7 +669,7 @@ tpmlp_status tpmlp_tp_fwd(const tpmlp_bf16* X, const tpmlp_bf16* const* A_sh, co
   for (int i = 0; i < t; ++i) {
     float* Zi = direct ? Z : (Z_sh && Z_sh[i]) ? Z_sh[i] : partials + size_t(i) * mh;
     parts[i] = Zi;
-    hipError_t e = enqueue_fwd(X, A_sh[i], B_sh[i], Zi, P_sh ? P_sh[i] : nullptr, M, H, F_i, ws, s);
+    hipError_t e = enqueue_fwd(X, A_sh[i], F_i, B_sh[i], Zi, P_sh ? P_sh[i] : nullptr, M, H, F_i, ws, s);
     if (e != hipSuccess) return hip_fail(e, "tpmlp_tp_fwd launch");
   }
   if (!direct) {
@@ -716,13 +722,90 @@ tpmlp_status tpmlp_tp_bwd(const tpmlp_bf16* dZ, const tpmlp_bf16* X, const tpmlp
   for (int i = 0; i < t; ++i) {
     float* dXi = direct ? dX : (dX_sh && dX_sh[i]) ? dX_sh[i] : partials + size_t(i) * mh;
     parts[i] = dXi;
-    hipError_t e = enqueue_bwd(dZ, X, A_sh[i], B_sh[i], P_sh ? P_sh[i] : nullptr, dXi, dA_sh[i], dB_sh[i], M, H,
-                               F_i, ws, s);
+    hipError_t e = enqueue_bwd(dZ, X, A_sh[i], F_i, B_sh[i], P_sh ? P_sh[i] : nullptr, dXi, dA_sh[i], F_i,
+                               dB_sh[i], M, H, F_i, ws, s);
     if (e != hipSuccess) return hip_fail(e, "tpmlp_tp_bwd launch");
   }
   if (!direct) {
     hipError_t e = timed(TPMLP_K_SHARD_SUM, s, [&] { return launch_sum(parts, t, dX, int64_t(mh), s); });
     if (e != hipSuccess) return hip_fail(e, "tpmlp_tp_bwd sum");
+  }
+  return TPMLP_OK;
+}
+
+tpmlp_status tpmlp_tp_fwd_full(const tpmlp_bf16* X, const tpmlp_bf16* A, const tpmlp_bf16* B, tpmlp_bf16* P,
+                               float* Z, int t, int64_t M, int64_t H, int64_t F_i, void* ws, size_t ws_bytes,
+                               void* stream) {
+  g_last_error.clear();
+  if (t < 1 || t > TPMLP_MAX_SHARDS) return fail(TPMLP_ERR_SHARDS, "t outside 1..TPMLP_MAX_SHARDS");
+  tpmlp_status st = check_ptrs({{X, "X"}, {A, "A"}, {B, "B"}, {Z, "Z"}, {ws, "ws"}});
+  if (st) return st;
+  if (P && !aligned16(P)) return fail(TPMLP_ERR_ALIGN, "P is not 16-byte aligned");
+  if ((st = check_shape(M, H, F_i))) return st;
+  if (int64_t(t) * F_i > MAX_DIM) return fail(TPMLP_ERR_SHAPE, "t * F_i is above 2^24");
+  const size_t need = tpmlp_tp_workspace_bytes(t, M, H, F_i);
+  if (ws_bytes < need) return fail(TPMLP_ERR_WORKSPACE, "ws_bytes below tpmlp_tp_workspace_bytes");
+  const int64_t F = int64_t(t) * F_i;
+  const size_t mh = size_t(M) * H, hf = size_t(H) * F, mf = size_t(M) * F_i;
+  std::vector<Range> ins = {{X, mh * 2, "X"}, {A, hf * 2, "A"}, {B, hf * 2, "B"}};
+  std::vector<Range> outs = {{Z, mh * 4, "Z"}, {P, P ? mf * t * 2 : 0, "P"}, {ws, need, "ws"}};
+  if ((st = check_alias(outs, ins))) return st;
+  if ((st = check_device())) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* partials = reinterpret_cast<float*>(ws_at(ws, shard_ws_bytes(M, H, F_i)));
+  const float* parts[TPMLP_MAX_SHARDS];
+  for (int i = 0; i < t; ++i) {
+    float* Zi = t == 1 ? Z : partials + size_t(i) * mh;
+    parts[i] = Zi;
+    // Shard i: columns [i F_i, (i+1) F_i) of A (rows of F elements), rows of B.
+    hipError_t e = enqueue_fwd(X, A + int64_t(i) * F_i, F, B + int64_t(i) * F_i * H, Zi,
+                               P ? P + size_t(i) * mf : nullptr, M, H, F_i, ws, s);
+    if (e != hipSuccess) return hip_fail(e, "tpmlp_tp_fwd_full launch");
+  }
+  if (t > 1) {
+    hipError_t e = timed(TPMLP_K_SHARD_SUM, s, [&] { return launch_sum(parts, t, Z, int64_t(mh), s); });
+    if (e != hipSuccess) return hip_fail(e, "tpmlp_tp_fwd_full sum");
+  }
+  return TPMLP_OK;
+}
+
+tpmlp_status tpmlp_tp_bwd_full(const tpmlp_bf16* dZ, const tpmlp_bf16* X, const tpmlp_bf16* A,
+                               const tpmlp_bf16* B, const tpmlp_bf16* P, float* dA, float* dB, float* dX, int t,
+                               int64_t M, int64_t H, int64_t F_i, void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  if (t < 1 || t > TPMLP_MAX_SHARDS) return fail(TPMLP_ERR_SHARDS, "t outside 1..TPMLP_MAX_SHARDS");
+  tpmlp_status st =
+      check_ptrs({{dZ, "dZ"}, {X, "X"}, {A, "A"}, {B, "B"}, {dA, "dA"}, {dB, "dB"}, {dX, "dX"}, {ws, "ws"}});
+  if (st) return st;
+  if (P && !aligned16(P)) return fail(TPMLP_ERR_ALIGN, "P is not 16-byte aligned");
+  if ((st = check_shape(M, H, F_i))) return st;
+  if (int64_t(t) * F_i > MAX_DIM) return fail(TPMLP_ERR_SHAPE, "t * F_i is above 2^24");
+  const size_t need = tpmlp_tp_workspace_bytes(t, M, H, F_i);
+  if (ws_bytes < need) return fail(TPMLP_ERR_WORKSPACE, "ws_bytes below tpmlp_tp_workspace_bytes");
+  const int64_t F = int64_t(t) * F_i;
+  const size_t mh = size_t(M) * H, hf = size_t(H) * F, mf = size_t(M) * F_i;
+  std::vector<Range> ins = {{dZ, mh * 2, "dZ"}, {X, mh * 2, "X"}, {A, hf * 2, "A"}, {B, hf * 2, "B"},
+                            {P, P ? mf * t * 2 : 0, "P"}};
+  std::vector<Range> outs = {{dX, mh * 4, "dX"}, {dA, hf * 4, "dA"}, {dB, hf * 4, "dB"}, {ws, need, "ws"}};
+  if ((st = check_alias(outs, ins))) return st;
+  if ((st = check_device())) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* partials = reinterpret_cast<float*>(ws_at(ws, shard_ws_bytes(M, H, F_i)));
+  const float* parts[TPMLP_MAX_SHARDS];
+  hipError_t et = enqueue_transposes(dZ, X, M, H, ws, s);
+  if (et != hipSuccess) return hip_fail(et, "tpmlp_tp_bwd_full transpose");
+  for (int i = 0; i < t; ++i) {
+    float* dXi = t == 1 ? dX : partials + size_t(i) * mh;
+    parts[i] = dXi;
+    // Shard i: columns [i F_i, (i+1) F_i) of A and dA (rows of F elements), rows of B and dB.
+    const int64_t c = int64_t(i) * F_i;
+    hipError_t e = enqueue_bwd(dZ, X, A + c, F, B + c * H, P ? P + size_t(i) * mf : nullptr, dXi, dA + c, F,
+                               dB + c * H, M, H, F_i, ws, s);
+    if (e != hipSuccess) return hip_fail(e, "tpmlp_tp_bwd_full launch");
+  }
+  if (t > 1) {
+    hipError_t e = timed(TPMLP_K_SHARD_SUM, s, [&] { return launch_sum(parts, t, dX, int64_t(mh), s); });
+    if (e != hipSuccess) return hip_fail(e, "tpmlp_tp_bwd_full sum");
   }
   return TPMLP_OK;
 }

@@ -37,10 +37,13 @@ class DeviceMLP:
     """
 
     def __init__(self, inputs: Inputs, store_p: bool = True, driver: bool = True, shards=None,
-                 keep_partials: bool = False, device="cuda"):
+                 keep_partials: bool = False, device="cuda", full_weights: bool = False):
         import torch
         w = inputs.workload
         self.w, self.device, self.store_p, self.driver = w, device, store_p, driver
+        self.full = full_weights
+        if full_weights and (not driver or keep_partials):
+            raise ValueError("full_weights runs the t-shard driver over whole weights, without per-shard partials")
         self.M, self.H, self.F = w.M, w.H, w.F_i
         self.shards = [i for i in range(w.t) if inputs.A[i] is not None] if shards is None else list(shards)
         if driver and len(self.shards) != w.t:
@@ -61,6 +64,21 @@ class DeviceMLP:
             self.dB = [torch.empty((F, H), **f32) for _ in range(n)]
             self.dX_sh = [torch.empty((M, H), **f32) for _ in range(n)] if (keep_partials or not driver) else None
             self.dX = torch.empty((M, H), **f32) if driver else None
+        if full_weights:
+            # The whole weights A[H, t F_i] and B[t F_i, H]; the per-shard lists become
+            # views into them (and into the whole P, dA and dB).
+            self.Af = torch.cat(self.A, 1).contiguous()
+            self.Bf = torch.cat(self.B, 0).contiguous()
+            self.A = [self.Af[:, j * F:(j + 1) * F] for j in range(n)]
+            self.B = [self.Bf[j * F:(j + 1) * F] for j in range(n)]
+            if store_p:
+                self.Pf = torch.empty((n, M, F), **bf)
+                self.P = [self.Pf[j] for j in range(n)]
+            if w.backward:
+                self.dAf = torch.empty((H, n * F), **f32)
+                self.dBf = torch.empty((n * F, H), **f32)
+                self.dA = [self.dAf[:, j * F:(j + 1) * F] for j in range(n)]
+                self.dB = [self.dBf[j * F:(j + 1) * F] for j in range(n)]
         if driver:
             ws = L.tpmlp_tp_workspace_bytes(n, M, H, F)
         else:
@@ -68,7 +86,10 @@ class DeviceMLP:
         self.ws = torch.empty(ws, dtype=torch.uint8, device=device)
 
     def forward(self, stream=None):
-        if self.driver:
+        if self.full:
+            L.tpmlp_tp_fwd_full(self.X, self.Af, self.Bf, self.Pf if self.store_p else None, self.Z,
+                                len(self.shards), self.ws, stream)
+        elif self.driver:
             L.tpmlp_tp_fwd(self.X, self.A, self.B, self.P, self.Z_sh, self.Z, self.ws, stream)
         else:
             for j in range(len(self.shards)):
@@ -76,7 +97,10 @@ class DeviceMLP:
                             stream)
 
     def backward(self, stream=None):
-        if self.driver:
+        if self.full:
+            L.tpmlp_tp_bwd_full(self.dZ, self.X, self.Af, self.Bf, self.Pf if self.store_p else None, self.dAf,
+                                self.dBf, self.dX, len(self.shards), self.ws, stream)
+        elif self.driver:
             L.tpmlp_tp_bwd(self.dZ, self.X, self.A, self.B, self.P, self.dA, self.dB, self.dX_sh, self.dX, self.ws,
                            stream)
         else:

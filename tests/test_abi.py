@@ -43,7 +43,7 @@ def test_exports_every_declared_function():
 
 
 def test_version_and_strings():
-    assert L.tpmlp_abi_version() == 5
+    assert L.tpmlp_abi_version() == 6
     assert L.tpmlp_status_str(0) == "ok"
     assert L.tpmlp_status_str(ALIAS) == "output overlaps another buffer"
     assert L.tpmlp_status_str(99) == "unknown status"
@@ -153,6 +153,29 @@ def test_tp_argument_errors():
     assert lib.tpmlp_tp_bwd(_p(0), _p(3), A, B, Pbad, dA, dB, None, _p(1), t, M, H, F, _p(2), need, None) == NULL
     dBov = _arr([_p(40)] + [_p(51 + i) for i in range(t - 1)])       # dB_0 on dA_0
     assert lib.tpmlp_tp_bwd(_p(0), _p(3), A, B, None, dA, dBov, None, _p(1), t, M, H, F, _p(2), need, None) == ALIAS
+
+
+def test_tp_full_argument_errors():
+    """The whole-weight drivers check their arguments before any HIP call."""
+    lib = L.lib()
+    t, M, H, F = 4, 64, 256, 128
+    need = L.tpmlp_tp_workspace_bytes(t, M, H, F)
+    X, A, B, Z, ws = _p(0), _p(1), _p(2), _p(3), _p(4)
+    assert lib.tpmlp_tp_fwd_full(X, None, B, None, Z, t, M, H, F, ws, need, None) == NULL
+    assert lib.tpmlp_tp_fwd_full(X, A, B, None, Z, 0, M, H, F, ws, need, None) == SHARDS
+    assert lib.tpmlp_tp_fwd_full(X, A, B, None, Z, t, M, H, 12, ws, need, None) == SHAPE
+    assert lib.tpmlp_tp_fwd_full(X, A, B, None, Z, 8, M, H, 1 << 22, ws, 1 << 62, None) == SHAPE  # t F_i > 2^24
+    assert lib.tpmlp_tp_fwd_full(X, A, B, None, Z, t, M, H, F, ws, need - 1, None) == WS
+    assert lib.tpmlp_tp_fwd_full(X, A + 8, B, None, Z, t, M, H, F, ws, need, None) == ALIGN
+    # Z inside the whole A (H t F_i bf16 elements from A): overlap
+    assert lib.tpmlp_tp_fwd_full(X, A, B, None, A + 1024 * 16, t, M, H, F, ws, need, None) == ALIAS
+    dA, dB, dX = _p(5), _p(6), _p(7)
+    assert lib.tpmlp_tp_bwd_full(X, X, A, B, None, None, dB, dX, t, M, H, F, ws, need, None) == NULL
+    assert lib.tpmlp_tp_bwd_full(X, X, A, B, None, dA, dB, dX, 65, M, H, F, ws, need, None) == SHARDS
+    # dB starting inside dA (H t F_i float32 elements): overlap
+    assert lib.tpmlp_tp_bwd_full(X, X, A, B, None, dA, dA + 4096, dX, t, M, H, F, ws, need, None) == ALIAS
+    # P inside dA: an input overlapping an output
+    assert lib.tpmlp_tp_bwd_full(X, X, A, B, dA + 4096, dA, dB, dX, t, M, H, F, ws, need, None) == ALIAS
 
 
 def test_shard_sum_argument_errors():

@@ -227,6 +227,56 @@ def test_store_equals_recompute_bitwise():
         assert torch.equal(x, y)
 
 
+@pytest.mark.parametrize("case", [(200, 264, 392, 3, True), (520, 128, 1032, 2, False), (8200, 136, 520, 2, True),
+                                  (1024, 1032, 16640, 1, False)],
+                         ids=lambda c: "x".join(map(str, c[:4])) + ("_store" if c[4] else "_recompute"))
+def test_full_weights_equal_shards_bitwise(case):
+    """The whole-weight drivers (A_i a strided column view of A, dA_i of dA) give the
+    bits of the per-shard drivers on contiguous copies of the same shards: the
+    plans and kernels are the same, only the row strides differ.  Covers the
+    fused forward, the weight transposes (M = 8200) and split products."""
+    from tensor_transformer_mlp_03_amd.device import DeviceMLP
+    M, H, F, t, store = case
+    say(f"[full weights] M={M} H={H} F_i={F} t={t} store_p={store}")
+    w = I.custom_workload(318, M=M, H=H, F_i=F, t=t, w_std=0.05)
+    inp = I.make_inputs(w)
+    a = DeviceMLP(inp, store_p=store, driver=True)
+    b = DeviceMLP(inp, store_p=store, driver=True, full_weights=True)
+    a.step()
+    b.step()
+    torch.cuda.synchronize()
+    assert torch.equal(a.Z, b.Z) and torch.equal(a.dX, b.dX)
+    for x, y in list(zip(a.dA, b.dA)) + list(zip(a.dB, b.dB)):
+        assert torch.equal(x, y)
+    if store:
+        for x, y in zip(a.P, b.P):
+            assert torch.equal(x, y)
+
+
+def test_full_weights_oracle():
+    """Whole-weight drivers against the oracle on the unsharded MLP: Z = GeLU(X A) B
+    and its gradients, with dA and dB compared whole."""
+    from tensor_transformer_mlp_03_amd.device import DeviceMLP
+    M, H, F, t = 136, 520, 264, 4
+    say(f"[full weights oracle] M={M} H={H} F_i={F} t={t}")
+    w = I.custom_workload(319, M=M, H=H, F_i=F, t=t, w_std=0.05)
+    inp = I.make_inputs(w)
+    d = DeviceMLP(inp, store_p=False, driver=True, full_weights=True)
+    d.step()
+    torch.cuda.synchronize()
+    X, dZ = dec(inp.X), dec(inp.dZ)
+    A = np.concatenate([dec(a) for a in inp.A], 1)
+    B = np.concatenate([dec(b) for b in inp.B], 0)
+    fwd = O.mlp_forward(X, A, B)
+    bwd = O.mlp_backward(dZ, X, A, B)
+    r = {}
+    check("Z", d.Z.cpu().numpy(), fwd["Z"], r)
+    for name in ("dX", "dA", "dB"):
+        got = {"dX": d.dX, "dA": d.dAf, "dB": d.dBf}[name]
+        check(name, got.cpu().numpy(), bwd[name], r)
+    say("  err/tol:", {k: round(v, 3) for k, v in r.items()})
+
+
 def test_deterministic():
     w = I.custom_workload(311, M=768, H=1024, F_i=1536, t=2)
     say(f"[determinism] {w}")
