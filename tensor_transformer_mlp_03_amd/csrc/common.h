@@ -47,7 +47,13 @@ enum Epi : int {
   EPI_BF16 = 2,     // out_bf16[m,n] = acc
   EPI_DGELU = 3,    // p = aux_bf16[m,n]; out_bf16[m,n] = acc * GeLU'(p); transposed:
                     //   out2_bf16[n,m] = GeLU(p)
+  EPI_F32_ACC = 4,  // out_f32[m,n] = out_f32[m,n] + acc: adds the product to a running
+                    //   float32 sum (no split-K slices; the reduction applies it instead)
 };
+
+// Largest output row stride of an EPI_F32_ACC product (its loads of the running
+// sum take 32-bit byte offsets within a 64-row band).
+constexpr int64_t ACC_MAX_LDO = int64_t(1) << 22;
 
 struct GemmArgs {
   const uint16_t* a;  // A operand base (bf16 bits)

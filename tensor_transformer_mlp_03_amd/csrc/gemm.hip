@@ -310,6 +310,21 @@ __device__ __forceinline__ void store_tile(const f32x16_t (&acc)[FM][FN], const 
   // columns outside the output read as zero without a branch.
   u16x8_t pre[2][8];
   __amdgpu_buffer_rsrc_t pre_rs;
+  // EPI_F32_ACC: the running sum under a 64-row half, loaded before the half is
+  // staged so that the loads overlap the staging (descriptor on the half's first
+  // row and column; rows and columns outside the output read as zero).
+  f32x4_t old[16];
+  auto load_old = [&](int h) {
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(reinterpret_cast<const float*>(args.out) + (int64_t)(row_w + 64 * h) * args.ldo + col_w);
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+      const int q = it * 64 + lane, r = q >> 4, c = q & 15;
+      const bool ok = row_w + 64 * h + r < args.M && col_w + 4 * c < args.N;
+      const uint32_t off = (uint32_t)(((int64_t)r * args.ldo + 4 * c) * 4);
+      old[it] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, ok ? off : OOB, 0, 0));
+    }
+  };
   auto load_pre = [&](int h) {
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
@@ -326,6 +341,7 @@ __device__ __forceinline__ void store_tile(const f32x16_t (&acc)[FM][FN], const 
   }
 #pragma unroll
   for (int h = 0; h < NH; ++h) {
+    if (EPI == EPI_F32_ACC) load_old(h);
 #pragma unroll
     for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
@@ -339,7 +355,7 @@ __device__ __forceinline__ void store_tile(const f32x16_t (&acc)[FM][FN], const 
           *reinterpret_cast<f32x4_t*>(stage + r * ROW_B + ((c ^ (r & 15)) << 4)) = x;
         }
     if (EPI == EPI_DGELU && h + 1 < NH) load_pre(h + 1);
-    if (EPI == EPI_F32) {
+    if (EPI == EPI_F32 || EPI == EPI_F32_ACC) {
       float* out = reinterpret_cast<float*>(args.out) + (int64_t)split * args.split_stride;
       f32x4_t xs[16];
 #pragma unroll
@@ -351,6 +367,7 @@ __device__ __forceinline__ void store_tile(const f32x16_t (&acc)[FM][FN], const 
       for (int it = 0; it < 16; ++it) {
         const int q = it * 64 + lane, r = q >> 4, c = q & 15;
         const int row = row_w + 64 * h + r, col = col_w + 4 * c;
+        if (EPI == EPI_F32_ACC) xs[it] += old[it];
         if (row < args.M && col < args.N) *reinterpret_cast<f32x4_t*>(out + (int64_t)row * args.ldo + col) = xs[it];
       }
     } else {
@@ -889,6 +906,7 @@ hipError_t dispatch_layout(Layout la, Layout lb, Epi epi, const GemmArgs& a, int
     switch (epi) {
       case EPI_GELU: return launch_one<BM, BN, WM_, WN_, KC, MC, EPI_GELU>(a, splits, s);
       case EPI_F32: return launch_one<BM, BN, WM_, WN_, KC, MC, EPI_F32>(a, splits, s);
+      case EPI_F32_ACC: return launch_one<BM, BN, WM_, WN_, KC, MC, EPI_F32_ACC>(a, splits, s);
       case EPI_BF16: return launch_one<BM, BN, WM_, WN_, KC, MC, EPI_BF16>(a, splits, s);
       default: break;
     }
@@ -896,6 +914,7 @@ hipError_t dispatch_layout(Layout la, Layout lb, Epi epi, const GemmArgs& a, int
     switch (epi) {
       case EPI_DGELU: return launch_one<BM, BN, WM_, WN_, KC, KC, EPI_DGELU>(a, splits, s);
       case EPI_F32: return launch_one<BM, BN, WM_, WN_, KC, KC, EPI_F32>(a, splits, s);
+      case EPI_F32_ACC: return launch_one<BM, BN, WM_, WN_, KC, KC, EPI_F32_ACC>(a, splits, s);
       case EPI_GELU: return launch_one<BM, BN, WM_, WN_, KC, KC, EPI_GELU>(a, splits, s);
       case EPI_BF16: return launch_one<BM, BN, WM_, WN_, KC, KC, EPI_BF16>(a, splits, s);
       default: break;

@@ -66,6 +66,10 @@ __global__ void __launch_bounds__(256) splitk_kernel(SplitArgs a) {
     const int64_t o = dense ? 4 * j : (int64_t)((uint64_t)j / c4n) * a.ldo + 4 * ((uint64_t)j % c4n);
     if (EPI == EPI_F32) {
       *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(a.out) + o) = s;
+    } else if (EPI == EPI_F32_ACC) {
+      // The product (its slices summed first) is added to the running sum.
+      f32x4_t* p = reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(a.out) + o);
+      *p = *p + s;
     } else if (EPI == EPI_GELU) {
       u16x4_t g, p;
 #pragma unroll
@@ -236,6 +240,7 @@ hipError_t launch_splitk_epilogue(Epi epi, const float* part, int splits, int64_
   const dim3 grid(grid_for(n / 4)), block(256);
   switch (epi) {
     case EPI_F32: return launch_kernel(splitk_kernel<EPI_F32>, grid, block, stream, a);
+    case EPI_F32_ACC: return launch_kernel(splitk_kernel<EPI_F32_ACC>, grid, block, stream, a);
     case EPI_GELU: return launch_kernel(splitk_kernel<EPI_GELU>, grid, block, stream, a);
     case EPI_BF16: return launch_kernel(splitk_kernel<EPI_BF16>, grid, block, stream, a);
     default: return hipErrorInvalidValue;

@@ -394,7 +394,7 @@ hipError_t run_gemm(int kind, Layout la, Layout lb, Epi epi, const void* a, int6
         },
         2);
     if (e != hipSuccess) return e;
-    const size_t esz = epi == EPI_F32 ? 4 : 2;
+    const size_t esz = (epi == EPI_F32 || epi == EPI_F32_ACC) ? 4 : 2;
     void* out_tail = static_cast<char*>(out) + nf * esz;
     uint16_t* out2_tail = out2 ? out2 + (epi == EPI_DGELU ? nf * M : nf) : nullptr;
     const uint16_t* aux_tail = aux ? aux + nf : nullptr;
@@ -413,9 +413,13 @@ char* ws_at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
 
 // Enqueue rank i's forward (arguments already checked).
 // A (A_i) has rows of lda >= F elements: a column block of a wider weight.
+// acc: Z already holds the sum of earlier shards' partials and this shard's is
+// added to it (Z = Z + Z_i, in float32) instead of overwriting it.
 hipError_t enqueue_fwd(const tpmlp_bf16* X, const tpmlp_bf16* A, int64_t lda, const tpmlp_bf16* B, float* Z,
-                       tpmlp_bf16* P_save, int64_t M, int64_t H, int64_t F, void* ws, hipStream_t s) {
+                       tpmlp_bf16* P_save, int64_t M, int64_t H, int64_t F, void* ws, hipStream_t s,
+                       bool acc = false) {
   const FwdPlan p = plan_fwd(M, H, F);
+  const Epi out_epi = acc ? EPI_F32_ACC : EPI_F32;
   uint16_t* G = reinterpret_cast<uint16_t*>(ws_at(ws, p.off_G));
   float* part = reinterpret_cast<float*>(ws_at(ws, p.off_part));
   hipError_t e;
@@ -427,7 +431,8 @@ hipError_t enqueue_fwd(const tpmlp_bf16* X, const tpmlp_bf16* A, int64_t lda, co
     fa.x = X;
     fa.a = A;
     fa.b = B;
-    fa.part = chunks > 1 ? part : Z;
+    const bool direct = chunks == 1 && !acc;
+    fa.part = direct ? Z : part;
     fa.p_save = P_save;
     fa.lda = lda;
     fa.ldp = F;
@@ -435,9 +440,9 @@ hipError_t enqueue_fwd(const tpmlp_bf16* X, const tpmlp_bf16* A, int64_t lda, co
     fa.H = (int)H;
     fa.F = (int)F;
     e = timed(TPMLP_K_FWD_FUSED, s, [&] { return launch_ffn_fwd(fa, s); });
-    if (e != hipSuccess || chunks == 1) return e;
+    if (e != hipSuccess || direct) return e;
     return timed(TPMLP_K_SPLITK_REDUCE, s, [&] {
-      return launch_splitk_epilogue(EPI_F32, part, chunks, M, H, Z, nullptr, nullptr, H, M, s);
+      return launch_splitk_epilogue(out_epi, part, chunks, M, H, Z, nullptr, nullptr, H, M, s);
     });
   }
   if (p.wt) {
@@ -452,7 +457,7 @@ hipError_t enqueue_fwd(const tpmlp_bf16* X, const tpmlp_bf16* A, int64_t lda, co
                  nullptr, part, s);
     if (e != hipSuccess) return e;
     // Z_i = G_i B_i                    G_i: [M][F], B_i^T: [H][F] (both K-contig)
-    return run_gemm(TPMLP_K_FWD_GEMM2, KC, KC, EPI_F32, G, F, Bt, F, M, H, F, p.g2, Z, nullptr, nullptr,
+    return run_gemm(TPMLP_K_FWD_GEMM2, KC, KC, out_epi, G, F, Bt, F, M, H, F, p.g2, Z, nullptr, nullptr,
                     part, s);
   }
   // P_i = X A_i; G_i = GeLU(P_i)        X: [M][H] (K-contig), A_i: [H][F] (N-contig)
@@ -460,12 +465,26 @@ hipError_t enqueue_fwd(const tpmlp_bf16* X, const tpmlp_bf16* A, int64_t lda, co
                part, s);
   if (e != hipSuccess) return e;
   // Z_i = G_i B_i                      G_i: [M][F] (K-contig), B_i: [F][H] (N-contig)
-  return run_gemm(TPMLP_K_FWD_GEMM2, KC, MC, EPI_F32, G, F, B, H, M, H, F, p.g2, Z, nullptr, nullptr,
+  return run_gemm(TPMLP_K_FWD_GEMM2, KC, MC, out_epi, G, F, B, H, M, H, F, p.g2, Z, nullptr, nullptr,
                   part, s);
 }
 
 // Enqueue rank i's backward (arguments already checked).
 // X^T and dZ^T [H][M] into the backward workspace (shared by all shards).
+// The drivers fold the rank-order sum of the shards' partials into the
+// products that make them when no per-shard partial is asked for: shard 0's
+// row-parallel product (forward) or input-gradient product (backward) writes
+// the output, and shard i > 0's adds its partial to it in its epilogue.  The
+// additions are the float32 ones of the separate sum, in the same order
+// (((p_0 + p_1) + p_2) + ...), so the result has the same bits, and the t
+// partial buffers are neither written nor read back.
+bool fold_sum(float* const* per_shard, int t, int64_t H) {
+  if (t < 2 || H > ACC_MAX_LDO) return false;
+  for (int i = 0; per_shard && i < t; ++i)
+    if (per_shard[i]) return false;
+  return true;
+}
+
 hipError_t enqueue_transposes(const tpmlp_bf16* dZ, const tpmlp_bf16* X, int64_t M, int64_t H, void* ws,
                               hipStream_t s) {
   const BwdPlan p = plan_bwd(M, H, 8, false);  // the transposes' offsets do not depend on F or recompute
@@ -479,9 +498,10 @@ hipError_t enqueue_transposes(const tpmlp_bf16* dZ, const tpmlp_bf16* X, int64_t
 // Enqueue rank i's backward (arguments already checked; X^T and dZ^T already
 // in the workspace).
 // A (A_i) has rows of lda >= F elements and dA (dA_i) rows of ldda >= F.
+// acc: this shard's partial input gradient is added to dX (dX = dX + dX_i).
 hipError_t enqueue_bwd(const tpmlp_bf16* dZ, const tpmlp_bf16* X, const tpmlp_bf16* A, int64_t lda,
                        const tpmlp_bf16* B, const tpmlp_bf16* P_saved, float* dX, float* dA, int64_t ldda,
-                       float* dB, int64_t M, int64_t H, int64_t F, void* ws, hipStream_t s) {
+                       float* dB, int64_t M, int64_t H, int64_t F, void* ws, hipStream_t s, bool acc = false) {
   const bool recompute = P_saved == nullptr;
   const BwdPlan p = plan_bwd(M, H, F, recompute);
   const uint16_t* Xt = reinterpret_cast<const uint16_t*>(ws_at(ws, p.off_Xt));
@@ -519,8 +539,8 @@ hipError_t enqueue_bwd(const tpmlp_bf16* dZ, const tpmlp_bf16* X, const tpmlp_bf
                ldda);
   if (e != hipSuccess) return e;
   // dX_i = dP_i A_i^T  dP_i: [M][F] (K-contig), A_i: [H][F] = [N][K] (K-contig)
-  return run_gemm(TPMLP_K_BWD_DX, KC, KC, EPI_F32, dP, F, A, lda, M, H, F, p.gdx, dX, nullptr, nullptr, part,
-                  s);
+  return run_gemm(TPMLP_K_BWD_DX, KC, KC, acc ? EPI_F32_ACC : EPI_F32, dP, F, A, lda, M, H, F, p.gdx, dX,
+                  nullptr, nullptr, part, s);
 }
 
 }  // namespace
@@ -665,14 +685,16 @@ tpmlp_status tpmlp_tp_fwd(const tpmlp_bf16* X, const tpmlp_bf16* const* A_sh, co
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* partials = reinterpret_cast<float*>(ws_at(ws, shard_ws_bytes(M, H, F_i)));
   const bool direct = (t == 1) && !(Z_sh && Z_sh[0]);
+  const bool fold = fold_sum(Z_sh, t, H);
   const float* parts[TPMLP_MAX_SHARDS];
   for (int i = 0; i < t; ++i) {
-    float* Zi = direct ? Z : (Z_sh && Z_sh[i]) ? Z_sh[i] : partials + size_t(i) * mh;
+    float* Zi = (direct || fold) ? Z : (Z_sh && Z_sh[i]) ? Z_sh[i] : partials + size_t(i) * mh;
     parts[i] = Zi;
-    hipError_t e = enqueue_fwd(X, A_sh[i], F_i, B_sh[i], Zi, P_sh ? P_sh[i] : nullptr, M, H, F_i, ws, s);
+    hipError_t e =
+        enqueue_fwd(X, A_sh[i], F_i, B_sh[i], Zi, P_sh ? P_sh[i] : nullptr, M, H, F_i, ws, s, fold && i > 0);
     if (e != hipSuccess) return hip_fail(e, "tpmlp_tp_fwd launch");
   }
-  if (!direct) {
+  if (!direct && !fold) {
     hipError_t e = timed(TPMLP_K_SHARD_SUM, s, [&] { return launch_sum(parts, t, Z, int64_t(mh), s); });
     if (e != hipSuccess) return hip_fail(e, "tpmlp_tp_fwd sum");
   }
@@ -716,17 +738,18 @@ tpmlp_status tpmlp_tp_bwd(const tpmlp_bf16* dZ, const tpmlp_bf16* X, const tpmlp
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* partials = reinterpret_cast<float*>(ws_at(ws, shard_ws_bytes(M, H, F_i)));
   const bool direct = (t == 1) && !(dX_sh && dX_sh[0]);
+  const bool fold = fold_sum(dX_sh, t, H);
   const float* parts[TPMLP_MAX_SHARDS];
   hipError_t et = enqueue_transposes(dZ, X, M, H, ws, s);
   if (et != hipSuccess) return hip_fail(et, "tpmlp_tp_bwd transpose");
   for (int i = 0; i < t; ++i) {
-    float* dXi = direct ? dX : (dX_sh && dX_sh[i]) ? dX_sh[i] : partials + size_t(i) * mh;
+    float* dXi = (direct || fold) ? dX : (dX_sh && dX_sh[i]) ? dX_sh[i] : partials + size_t(i) * mh;
     parts[i] = dXi;
     hipError_t e = enqueue_bwd(dZ, X, A_sh[i], F_i, B_sh[i], P_sh ? P_sh[i] : nullptr, dXi, dA_sh[i], F_i,
-                               dB_sh[i], M, H, F_i, ws, s);
+                               dB_sh[i], M, H, F_i, ws, s, fold && i > 0);
     if (e != hipSuccess) return hip_fail(e, "tpmlp_tp_bwd launch");
   }
-  if (!direct) {
+  if (!direct && !fold) {
     hipError_t e = timed(TPMLP_K_SHARD_SUM, s, [&] { return launch_sum(parts, t, dX, int64_t(mh), s); });
     if (e != hipSuccess) return hip_fail(e, "tpmlp_tp_bwd sum");
   }
@@ -754,15 +777,16 @@ tpmlp_status tpmlp_tp_fwd_full(const tpmlp_bf16* X, const tpmlp_bf16* A, const t
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* partials = reinterpret_cast<float*>(ws_at(ws, shard_ws_bytes(M, H, F_i)));
   const float* parts[TPMLP_MAX_SHARDS];
+  const bool fold = fold_sum(nullptr, t, H);
   for (int i = 0; i < t; ++i) {
-    float* Zi = t == 1 ? Z : partials + size_t(i) * mh;
+    float* Zi = (t == 1 || fold) ? Z : partials + size_t(i) * mh;
     parts[i] = Zi;
     // Shard i: columns [i F_i, (i+1) F_i) of A (rows of F elements), rows of B.
     hipError_t e = enqueue_fwd(X, A + int64_t(i) * F_i, F, B + int64_t(i) * F_i * H, Zi,
-                               P ? P + size_t(i) * mf : nullptr, M, H, F_i, ws, s);
+                               P ? P + size_t(i) * mf : nullptr, M, H, F_i, ws, s, fold && i > 0);
     if (e != hipSuccess) return hip_fail(e, "tpmlp_tp_fwd_full launch");
   }
-  if (t > 1) {
+  if (t > 1 && !fold) {
     hipError_t e = timed(TPMLP_K_SHARD_SUM, s, [&] { return launch_sum(parts, t, Z, int64_t(mh), s); });
     if (e != hipSuccess) return hip_fail(e, "tpmlp_tp_fwd_full sum");
   }
@@ -794,16 +818,17 @@ tpmlp_status tpmlp_tp_bwd_full(const tpmlp_bf16* dZ, const tpmlp_bf16* X, const 
   const float* parts[TPMLP_MAX_SHARDS];
   hipError_t et = enqueue_transposes(dZ, X, M, H, ws, s);
   if (et != hipSuccess) return hip_fail(et, "tpmlp_tp_bwd_full transpose");
+  const bool fold = fold_sum(nullptr, t, H);
   for (int i = 0; i < t; ++i) {
-    float* dXi = t == 1 ? dX : partials + size_t(i) * mh;
+    float* dXi = (t == 1 || fold) ? dX : partials + size_t(i) * mh;
     parts[i] = dXi;
     // Shard i: columns [i F_i, (i+1) F_i) of A and dA (rows of F elements), rows of B and dB.
     const int64_t c = int64_t(i) * F_i;
     hipError_t e = enqueue_bwd(dZ, X, A + c, F, B + c * H, P ? P + size_t(i) * mf : nullptr, dXi, dA + c, F,
-                               dB + c * H, M, H, F_i, ws, s);
+                               dB + c * H, M, H, F_i, ws, s, fold && i > 0);
     if (e != hipSuccess) return hip_fail(e, "tpmlp_tp_bwd_full launch");
   }
-  if (t > 1) {
+  if (t > 1 && !fold) {
     hipError_t e = timed(TPMLP_K_SHARD_SUM, s, [&] { return launch_sum(parts, t, dX, int64_t(mh), s); });
     if (e != hipSuccess) return hip_fail(e, "tpmlp_tp_bwd_full sum");
   }

@@ -277,6 +277,33 @@ def test_full_weights_oracle():
     say("  err/tol:", {k: round(v, 3) for k, v in r.items()})
 
 
+@pytest.mark.parametrize("case", [(200, 264, 392, 3, True), (200, 192, 392, 2, False), (8, 64, 8, 2, True),
+                                  (1024, 16640, 1032, 2, False), (2048, 4096, 2048, 4, True)],
+                         ids=lambda c: "x".join(map(str, c[:4])) + ("_store" if c[4] else "_recompute"))
+def test_folded_sum_equals_separate_sum_bitwise(case):
+    """Without per-shard partials the drivers add each shard's partial to Z and dX in
+    its product's epilogue (or its split reduction); the float32 additions are those
+    of the separate rank-order sum, so the bits are the same.  Covers the fused
+    forward (one and several chunks), hybrid split products ([M, H] outputs with a
+    split tail: H = 16640) and the 128 x 128 kernel (7B-class shard shapes)."""
+    from tensor_transformer_mlp_03_amd.device import DeviceMLP
+    M, H, F, t, store = case
+    say(f"[folded sum] M={M} H={H} F_i={F} t={t} store_p={store}")
+    w = I.custom_workload(320, M=M, H=H, F_i=F, t=t, w_std=0.05)
+    inp = I.make_inputs(w)
+    a = DeviceMLP(inp, store_p=store, driver=True, keep_partials=True)   # partials + separate sum
+    b = DeviceMLP(inp, store_p=store, driver=True, keep_partials=False)  # folded
+    c = DeviceMLP(inp, store_p=store, driver=True, full_weights=True)    # folded, whole weights
+    for d in (a, b, c):
+        d.step()
+    torch.cuda.synchronize()
+    for d in (b, c):
+        assert torch.equal(a.Z, d.Z) and torch.equal(a.dX, d.dX)
+    # and the sum is the sum of the partials, to float32 rounding of t - 1 additions
+    Z = sum(z.double() for z in a.Z_sh)
+    assert (a.Z.double() - Z).abs().max() <= t * 2.0 ** -23 * Z.abs().max()
+
+
 def test_deterministic():
     w = I.custom_workload(311, M=768, H=1024, F_i=1536, t=2)
     say(f"[determinism] {w}")
@@ -362,7 +389,8 @@ def test_timing_counts_launches():
     stats, dropped = L.tpmlp_timing_end()
     assert dropped == 0
     assert stats["fwd_gemm1_gelu"][0] == 2 and stats["fwd_gemm2"][0] == 2
-    assert stats["bwd_dgelu"][0] == 2 and stats["bwd_dX"][0] == 2 and stats["shard_sum"][0] == 2
+    # no per-shard partials asked for: the sums are folded into the products' epilogues
+    assert stats["bwd_dgelu"][0] == 2 and stats["bwd_dX"][0] == 2 and stats["shard_sum"][0] == 0
     assert stats["bwd_recompute"][0] == 0
     assert stats["transpose"][0] == 2  # X^T and dZ^T once for both shards
     assert all(ms >= 0 for _, ms in stats.values())
@@ -393,9 +421,9 @@ def test_fused_forward_is_taken(shape):
     stats, dropped = L.tpmlp_timing_end()
     assert dropped == 0
     counts = {k: n for k, (n, _) in stats.items() if n}
-    want = {"fwd_fused": 2, "shard_sum": 1}
-    if F > 64:
-        want["splitk_reduce"] = 2
+    # Shard 1's chunk sum also adds its partial to Z (no separate shard sum); with
+    # a single chunk, shard 0 writes Z from the fused kernel itself.
+    want = {"fwd_fused": 2, "splitk_reduce": 2 if F > 64 else 1}
     assert counts == want
 
 
