@@ -75,22 +75,31 @@ def gemm_flops(w):
             "bwd_dX": f, "fwd_fused": 2 * f}
 
 
-def gemm_alg_bytes(w, recompute):
+def gemm_alg_bytes(w, recompute, fold=False):
     """Algorithmic HBM bytes of one launch of each GEMM kind (operands read once,
-    outputs written once; bf16 = 2 bytes, float32 = 4)."""
+    outputs written once; bf16 = 2 bytes, float32 = 4).  fold: the t-shard driver adds
+    the partials of Z and dX in the products' epilogues, so t - 1 of every t launches
+    of those kinds also read the running sum (counted as its average per launch)."""
     M, H, F = w.M, w.H, w.F_i
+    acc = 4 * M * H * (w.t - 1) / w.t if fold else 0
     return {
         "fwd_gemm1_gelu": 2 * (M * H + H * F) + 2 * M * F * (1 if recompute else 2),  # X, A_i -> G (+P)
-        "fwd_gemm2": 2 * (M * F + F * H) + 4 * M * H,                                # G, B_i -> Z_i
+        "fwd_gemm2": 2 * (M * F + F * H) + 4 * M * H + acc,                          # G, B_i (+Z) -> Z
         "bwd_recompute": 2 * (M * H + H * F) + 2 * M * F,                             # X, A_i -> P
         "bwd_dgelu": 2 * (M * H + F * H + M * F) + 4 * M * F,                         # dZ, B_i, P -> dP, G^T
         "bwd_dB": 2 * (M * F + M * H) + 4 * F * H,                                    # G^T, dZ^T -> dB_i
         "bwd_dA": 2 * (M * H + M * F) + 4 * H * F,                                    # X^T, dP -> dA_i
-        "bwd_dX": 2 * (M * F + H * F) + 4 * M * H,                                    # dP, A_i -> dX_i
+        "bwd_dX": 2 * (M * F + H * F) + 4 * M * H + acc,                              # dP, A_i (+dX) -> dX
         "transpose": 4 * M * H,                                                       # X -> X^T, dZ -> dZ^T
         # X, A_i, B_i -> float32 partials of Z_i, one per chunk of 64 intermediate columns (+P)
         "fwd_fused": 2 * (M * H + 2 * H * F) + 4 * M * H * (-(-F // 64)) + (0 if recompute else 2 * M * F),
     }
+
+
+def folds(w):
+    """Whether bench's step folds the partial sums into the products: it runs the
+    t-shard driver (every shard) without per-shard partials."""
+    return len(w.shards_timed) == w.t and w.t > 1
 
 
 def cpu_baseline(w, target_s=12.0):
@@ -197,7 +206,7 @@ def summarize(d, config):
         a["n"] += 1
         a["fetch"] += f["counters"]["FETCH_SIZE"] * 1024 * f_scale
         a["write"] += wr["counters"]["WRITE_SIZE"] * 1024 * w_scale
-    alg = gemm_alg_bytes(w, w.recompute)
+    alg = gemm_alg_bytes(w, w.recompute, fold=folds(w))
     if "transpose" in agg:
         # A backward step transposes X and dZ ([M,H]) once each; every further launch
         # is a weight transpose ([H,F_i] or [F_i,H]).  Per launch: the step's average.
@@ -408,7 +417,7 @@ def main():
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": None, "avg_launch_us": round(avg_s * 1e6, 2),
-                "alg_bytes": gemm_alg_bytes(w, w.recompute)[dom]}
+                "alg_bytes": gemm_alg_bytes(w, w.recompute, fold=folds(w))[dom]}
     if traffic and dom in traffic:
         fetch, write = traffic[dom]
         roofline["traffic"] = int(fetch + write)
