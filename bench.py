@@ -439,6 +439,7 @@ def main():
         "config": {"workload": w.name, "M": w.M, "H": w.H, "F": w.F, "t": w.t, "F_i": w.F_i,
                    "shards_per_step": len(shards), "pre_activation": "recompute" if w.recompute else "stored",
                    "weights": "whole (shard views)" if args.full_weights else "per-shard buffers",
+                   "saved_activation_bytes_per_rank": L.tpmlp_saved_activation_bytes(w.M, w.H, w.F_i, w.recompute),
                    "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4), "timing_dropped": dropped},
         "roofline": roofline,
         "cpu_baseline": None,

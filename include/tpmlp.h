@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define TPMLP_ABI_VERSION 6
+#define TPMLP_ABI_VERSION 7
 #define TPMLP_MAX_SHARDS 64
 
 typedef uint16_t tpmlp_bf16; /* raw bf16 bits */
@@ -116,6 +116,22 @@ tpmlp_status tpmlp_bwd(const tpmlp_bf16* dZ, const tpmlp_bf16* X, const tpmlp_bf
                        float* dX_i, float* dA_i, float* dB_i,
                        int64_t M, int64_t H, int64_t F_i,
                        void* ws, size_t ws_bytes, void* stream);
+
+/* Activation memory that one rank keeps from its forward to its backward, in
+ * bytes: X[M,H] in bf16, which the backward reads either way (its weight
+ * gradient dA_i = X^T dP_i needs it), plus the pre-activation P_i[M,F_i] in bf16
+ * unless it is recomputed.  Recomputing saves those M F_i 2 bytes at the cost of
+ * one more product of 2 M H F_i flops, a sixth of the shard's model FLOPs
+ * (products need their inputs for their gradients, recomputation trades compute
+ * for memory: asorrir.com survey, part 二, Checkpoint 技术; "大模型训练" notes §7).
+ * 0 if the shape is invalid. */
+size_t tpmlp_saved_activation_bytes(int64_t M, int64_t H, int64_t F_i, int recompute);
+
+/* Store-or-recompute choice for one rank's shard under an activation budget of
+ * `budget_bytes` per rank: 0 = keep P_i (no extra work) when that fits, 1 =
+ * recompute P_i when only the smaller footprint fits, -1 when neither fits or the
+ * shape is invalid.  Storing is preferred because it costs no FLOPs. */
+int tpmlp_recompute_policy(int64_t M, int64_t H, int64_t F_i, size_t budget_bytes);
 
 /* ------------------------------------------------------------------------ */
 /* The t-shard driver: all t ranks' shards run one after another on one GPU and */

@@ -48,6 +48,8 @@ _SIGS = {
     "tpmlp_fwd_workspace_bytes": ([_i64, _i64, _i64], _sz),
     "tpmlp_bwd_workspace_bytes": ([_i64, _i64, _i64, _int], _sz),
     "tpmlp_tp_workspace_bytes": ([_int, _i64, _i64, _i64], _sz),
+    "tpmlp_saved_activation_bytes": ([_i64, _i64, _i64, _int], _sz),
+    "tpmlp_recompute_policy": ([_i64, _i64, _i64, _sz], _int),
     "tpmlp_fwd": ([_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _sz, _vp], _int),
     "tpmlp_bwd": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _sz, _vp], _int),
     "tpmlp_tp_fwd": ([_vp, _PP, _PP, _PP, _PP, _vp, _int, _i64, _i64, _i64, _vp, _sz, _vp], _int),
@@ -231,6 +233,15 @@ def tpmlp_tp_bwd_full(dZ, X, A, B, P, dA, dB, dX, t, ws, stream=None):
     st = lib().tpmlp_tp_bwd_full(_ptr(dZ), _ptr(X), _ptr(A), _ptr(B), _ptr(P), _ptr(dA), _ptr(dB), _ptr(dX), t,
                                  M, H, F, _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     _check(st, "tpmlp_tp_bwd_full")
+
+
+def tpmlp_saved_activation_bytes(M: int, H: int, F: int, recompute: bool) -> int:
+    return lib().tpmlp_saved_activation_bytes(M, H, F, int(recompute))
+
+
+def tpmlp_recompute_policy(M: int, H: int, F: int, budget_bytes: int) -> int:
+    """0: keep the pre-activation, 1: recompute it, -1: neither fits the budget."""
+    return lib().tpmlp_recompute_policy(M, H, F, budget_bytes)
 
 
 def tpmlp_shard_sum(parts, out, stream=None):

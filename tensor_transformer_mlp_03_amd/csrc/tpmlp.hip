@@ -627,6 +627,18 @@ tpmlp_status tpmlp_bwd(const tpmlp_bf16* dZ, const tpmlp_bf16* X, const tpmlp_bf
   return e == hipSuccess ? TPMLP_OK : hip_fail(e, "tpmlp_bwd launch");
 }
 
+size_t tpmlp_saved_activation_bytes(int64_t M, int64_t H, int64_t F_i, int recompute) {
+  if (!shape_ok(M) || !shape_ok(H) || !shape_ok(F_i)) return 0;
+  return size_t(M) * H * 2 + (recompute ? 0 : size_t(M) * F_i * 2);
+}
+
+int tpmlp_recompute_policy(int64_t M, int64_t H, int64_t F_i, size_t budget_bytes) {
+  if (!shape_ok(M) || !shape_ok(H) || !shape_ok(F_i)) return -1;
+  if (tpmlp_saved_activation_bytes(M, H, F_i, 0) <= budget_bytes) return 0;
+  if (tpmlp_saved_activation_bytes(M, H, F_i, 1) <= budget_bytes) return 1;
+  return -1;
+}
+
 size_t tpmlp_tp_workspace_bytes(int t, int64_t M, int64_t H, int64_t F_i) {
   if (t < 1 || t > TPMLP_MAX_SHARDS || !shape_ok(M) || !shape_ok(H) || !shape_ok(F_i)) return 0;
   return shard_ws_bytes(M, H, F_i) + align_up(size_t(t) * M * H * 4);

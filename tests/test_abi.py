@@ -43,7 +43,7 @@ def test_exports_every_declared_function():
 
 
 def test_version_and_strings():
-    assert L.tpmlp_abi_version() == 6
+    assert L.tpmlp_abi_version() == 7
     assert L.tpmlp_status_str(0) == "ok"
     assert L.tpmlp_status_str(ALIAS) == "output overlaps another buffer"
     assert L.tpmlp_status_str(99) == "unknown status"
@@ -153,6 +153,21 @@ def test_tp_argument_errors():
     assert lib.tpmlp_tp_bwd(_p(0), _p(3), A, B, Pbad, dA, dB, None, _p(1), t, M, H, F, _p(2), need, None) == NULL
     dBov = _arr([_p(40)] + [_p(51 + i) for i in range(t - 1)])       # dB_0 on dA_0
     assert lib.tpmlp_tp_bwd(_p(0), _p(3), A, B, None, dA, dBov, None, _p(1), t, M, H, F, _p(2), need, None) == ALIAS
+
+
+def test_activation_accounting_and_policy():
+    """Saved activations per rank: X always, P_i unless recomputed; the policy keeps
+    P_i when it fits and recomputes only when the smaller footprint alone fits."""
+    M, H, F = 2048, 20480, 10240  # a 530B-class rank shard
+    x, p = M * H * 2, M * F * 2
+    assert L.tpmlp_saved_activation_bytes(M, H, F, False) == x + p
+    assert L.tpmlp_saved_activation_bytes(M, H, F, True) == x
+    assert L.tpmlp_saved_activation_bytes(M, H, 12, True) == 0
+    assert L.tpmlp_recompute_policy(M, H, F, x + p) == 0
+    assert L.tpmlp_recompute_policy(M, H, F, x + p - 1) == 1
+    assert L.tpmlp_recompute_policy(M, H, F, x) == 1
+    assert L.tpmlp_recompute_policy(M, H, F, x - 1) == -1
+    assert L.tpmlp_recompute_policy(0, H, F, 1 << 60) == -1
 
 
 def test_tp_full_argument_errors():
