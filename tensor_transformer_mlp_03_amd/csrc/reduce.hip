@@ -100,9 +100,11 @@ struct SplitDGeluArgs {
 
 typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
 
-// One 64 x 64 tile per block of 256 threads.  Thread t finishes row t/4,
-// columns 16*(t%4) .. +15 (two 8-column vectors), then, after a barrier, writes
-// 16 consecutive rows of one column of the transposed output.
+// One 64 x 64 tile per block of 256 threads.  Thread t finishes columns
+// 8*(t%8) .. +7 of rows t/8 and t/8 + 32 (eight threads cover a row's 256 bytes
+// of each float32 slice), issuing the pre-activation loads and the slices'
+// loads before it adds, then, after a barrier, writes 16 consecutive rows of
+// one column of the transposed output.
 __global__ void __launch_bounds__(256) splitk_dgelu_kernel(SplitDGeluArgs a) {
   __shared__ uint16_t s_g[64][72];  // 8 elements of padding per row
   const int tiles_n = (a.N + 63) / 64;
@@ -110,28 +112,42 @@ __global__ void __launch_bounds__(256) splitk_dgelu_kernel(SplitDGeluArgs a) {
   const int t = threadIdx.x;
   const int64_t plane = (int64_t)a.M * a.N;
   {
-    const int r = t >> 2, row = m0 + r;
+    const int rq = t >> 3, c = 8 * (t & 7), col = n0 + c;
+    bool ok[2];
+    int64_t o[2];
+    u16x8_t pb[2];
+    f32x4_t s0[2], s1[2];
 #pragma unroll
     for (int v = 0; v < 2; ++v) {
-      const int c = 16 * (t & 3) + 8 * v, col = n0 + c;
-      if (row >= a.M || col >= a.N) continue;  // N % 8 == 0: 8 columns in or out together
-      const int64_t o = (int64_t)row * a.N + col, oo = (int64_t)row * a.ldo + col;
-      f32x4_t s0 = *reinterpret_cast<const f32x4_t*>(a.part + o);
-      f32x4_t s1 = *reinterpret_cast<const f32x4_t*>(a.part + o + 4);
-      for (int i = 1; i < a.splits; ++i) {
-        s0 += *reinterpret_cast<const f32x4_t*>(a.part + i * plane + o);
-        s1 += *reinterpret_cast<const f32x4_t*>(a.part + i * plane + o + 4);
+      const int row = m0 + rq + 32 * v;
+      ok[v] = row < a.M && col < a.N;  // N % 8 == 0: 8 columns in or out together
+      o[v] = ok[v] ? (int64_t)row * a.N + col : 0;
+      const int64_t oo = ok[v] ? (int64_t)row * a.ldo + col : 0;
+      pb[v] = *reinterpret_cast<const u16x8_t*>(a.p + oo);
+      s0[v] = *reinterpret_cast<const f32x4_t*>(a.part + o[v]);
+      s1[v] = *reinterpret_cast<const f32x4_t*>(a.part + o[v] + 4);
+    }
+#pragma unroll 2
+    for (int i = 1; i < a.splits; ++i) {
+#pragma unroll
+      for (int v = 0; v < 2; ++v) {
+        s0[v] += *reinterpret_cast<const f32x4_t*>(a.part + i * plane + o[v]);
+        s1[v] += *reinterpret_cast<const f32x4_t*>(a.part + i * plane + o[v] + 4);
       }
-      const float x[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
-      const u16x8_t pb = *reinterpret_cast<const u16x8_t*>(a.p + oo);
+    }
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+      if (!ok[v]) continue;
+      const int r = rq + 32 * v;
+      const float x[8] = {s0[v][0], s0[v][1], s0[v][2], s0[v][3], s1[v][0], s1[v][1], s1[v][2], s1[v][3]};
       u16x8_t dp;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const DGelu d = epi_dgelu(x[e], pb[e]);
+        const DGelu d = epi_dgelu(x[e], pb[v][e]);
         dp[e] = d.dp;
         s_g[r][c + e] = d.g;
       }
-      *reinterpret_cast<u16x8_t*>(a.dp + oo) = dp;
+      *reinterpret_cast<u16x8_t*>(a.dp + (int64_t)(m0 + r) * a.ldo + col) = dp;
     }
   }
   __syncthreads();

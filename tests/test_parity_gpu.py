@@ -216,10 +216,13 @@ def test_gpu_shard_sum_identity(t):
     say("  err/tol:", {k: round(v, 3) for k, v in r.items()})
 
 
-def test_store_equals_recompute_bitwise():
+@pytest.mark.parametrize("shape", [(1000, 520, 776), (200, 192, 392)], ids=["two_products", "fused_forward"])
+def test_store_equals_recompute_bitwise(shape):
     """Keeping the bf16 pre-activation or recomputing it gives identical bits: both
-    come from the same GEMM with the same tile and accumulation order."""
-    w = I.custom_workload(310, M=1000, H=520, F_i=776, t=2)
+    come from a chain of MFMAs over k in the same order (the fused forward's P_i
+    included, H = 192)."""
+    M, H, F = shape
+    w = I.custom_workload(310, M=M, H=H, F_i=F, t=2)
     say(f"[store vs recompute] {w}")
     inp = I.make_inputs(w)
     a, b = run_device(inp, store_p=True), run_device(inp, store_p=False)
