@@ -174,7 +174,6 @@ __device__ __forceinline__ bf16x8_t read_frag(const char* tile, int r0, int kk, 
 // swizzle places there.  A row's swizzle depends on the lane and on
 // (4i + w) & 7, so even and odd i use two lane patterns.
 struct HalfDma {
-  static constexpr int PER_WAVE = 4;
   uint32_t lane_off[2];  // byte offset of the lane's chunk for even / odd i
   int kc[2];             // its first k inside the K step
 
@@ -211,7 +210,6 @@ struct HalfDma {
 __device__ __forceinline__ int mc_off(int k, int n) { return k * 256 + (((n >> 3) ^ (4 * (k & 3))) << 4) + (n & 7) * 2; }
 
 struct HalfDmaMC {
-  static constexpr int PER_WAVE = 4;
   uint32_t lane_off;  // byte offset of the lane's chunk in instruction 0
   int lane_k, lane_n;  // the chunk's k-row in instruction 0 and first n
 
@@ -774,7 +772,6 @@ gemm_w4_kernel(GemmArgs args) {
   };
   auto fence = [&]() { __builtin_amdgcn_sched_barrier(0); };
   using L0 = std::integral_constant<int, 0>;
-  using L4 = std::integral_constant<int, 4>;
   using L8 = std::integral_constant<int, 8>;
 
   // s_waitcnt immediate for vmcnt(n), n < 64, leaving the other counters free.

@@ -187,6 +187,15 @@ def test_config_sampled(cfg):
     if driver:
         check("Z[rows]", d.Z[rows].cpu().numpy(), Zs, r)
         check("dX[rows]", d.dX[rows].cpu().numpy(), dXs, r)
+        # The launch configuration the benchmark times: no per-shard partials, the
+        # sums folded into the products.  Same bits as the run checked above.
+        b = DeviceMLP(inp, store_p=not w.recompute, driver=True, keep_partials=False)
+        b.step()
+        torch.cuda.synchronize()
+        assert torch.equal(b.Z, d.Z) and torch.equal(b.dX, d.dX)
+        for x, y in list(zip(b.dA, d.dA)) + list(zip(b.dB, d.dB)):
+            assert torch.equal(x, y)
+        del b
     say("  err/tol:", {k: round(v, 3) for k, v in r.items()})
 
 
