@@ -74,7 +74,8 @@ struct GemmArgs {
 enum TileCfg : int {
   TILE_256x256 = 0,  // 4 waves, 2 x 2, wave tile 128 x 128
   TILE_128x128 = 1,  // 4 waves, 2 x 2, wave tile 64 x 64
-  TILE_COUNT = 2,
+  TILE_256x128 = 2,  // 4 waves, 2 x 2, wave tile 128 x 64 (the 256 x 256 kernel's ring)
+  TILE_COUNT = 3,
 };
 
 // Launches C = A B with the given layouts and epilogue on `stream`.

@@ -609,6 +609,12 @@ __device__ constexpr int w4_mj(int m) {
   constexpr int order[16] = {0, 1, 0, 1, 2, 2, 0, 1, 2, 3, 3, 3, 0, 1, 2, 3};
   return order[m];
 }
+// The same for a 128 x 64 wave tile (256 x 128 workgroup tile): reads A0 B0 B1
+// A1 A2 A3, MFMAs row by row.
+__device__ constexpr int w4n_read(int r) {
+  constexpr int order[6] = {0, 4, 5, 1, 2, 3};
+  return order[r];
+}
 
 // 256 x 256 tile, A K-contiguous and B either, four waves (one per SIMD) that
 // each compute a 128 x 128 quadrant: wave w owns rows 128 (w / 2) and columns
@@ -637,14 +643,21 @@ __device__ constexpr int w4_mj(int m) {
 //         of step k+1's first sub-step.
 // The loads thus run at an even 16 KiB per sub-step per workgroup; each batch
 // has at least two sub-steps before it is waited for.
-template <int LB, int EPI>
+//
+// BN = 128 (256 x 128 tiles) keeps the ring and the schedule: a K step has no
+// fourth quarter (B's 128 columns are quarter 2, read by both column waves,
+// each a 128 x 64 sub-tile), so its loads are simply not issued and every
+// vmcnt wait above still counts the loads that follow the ones it needs.
+template <int LB, int EPI, int BN>
 __global__ void __launch_bounds__(256)
 gemm_w4_kernel(GemmArgs args) {
 #if defined(__HIP_DEVICE_COMPILE__)
+  static_assert(BN == 256 || BN == 128, "tile widths");
   constexpr int BK = TILE_BK;
   constexpr int SLOT = 128 * BK * 2;
   constexpr int NSLOT = 10;
-  constexpr int FM = 4, FN = 4;  // 32 x 32 fragments per wave: 128 x 128
+  constexpr int FM = 4, FN = BN / 64;  // 32 x 32 fragments per wave: 128 x BN/2
+  constexpr int NQ = BN == 256 ? 4 : 3;  // quarters loaded per K step
   // A window's 16 loads, four per sub-step: even issue measured best (eight in
   // one sub-step stall the wave on the address unit).
   constexpr int LC3 = 4, LC0 = 4, LC1 = 4;
@@ -659,7 +672,7 @@ gemm_w4_kernel(GemmArgs args) {
 
   int tm, tn, split;
   tile_of(blockIdx.x, gridDim.x, args.tiles_m, args.tiles_n, tm, tn, split);
-  const int m0 = tm * 256, n0 = tn * 256;
+  const int m0 = tm * 256, n0 = tn * BN;
   const int k_begin = split * args.k_split;
   const int k_end = min(args.K, k_begin + args.k_split);
   const int nk = (k_end - k_begin + BK - 1) / BK;
@@ -676,6 +689,7 @@ gemm_w4_kernel(GemmArgs args) {
   auto slot = [&](int r, int q) -> char* { return smem + ((4 * r + q) % NSLOT) * SLOT; };
   // Instruction i of this wave's share of quarter q of K step `step` (r = step % 5).
   auto load = [&](int step, int r, int q, int i) {
+    if (q >= NQ) return;
     const int k = k_begin + step * BK;
     char* dst = slot(r, q);
     if (q < 2) {
@@ -728,18 +742,21 @@ gemm_w4_kernel(GemmArgs args) {
   for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
     for (int par = 0; par < 2; ++par) lane_kc[kk][par] = tile_off(32 * par + (lane & 31), 2 * kk + (lane >> 5));
+  // BN = 128: the wave's columns are 64 wn .. +63 of the one B quarter.
+  const int wcol = BN == 256 ? 0 : 64 * wn;
 #pragma unroll
-  for (int f = 0; f < FN; ++f) lane_mc[f] = mc_lane_off(32 * f, lane);
+  for (int f = 0; f < FN; ++f) lane_mc[f] = mc_lane_off(wcol + 32 * f, lane);
   auto read_sub = [&](int buf, int r, int kk) {
     const char* ta = slot(r, wm);
-    const char* tb = slot(r, 2 + wn);
+    const char* tb = slot(r, BN == 256 ? 2 + wn : 2);
 #pragma unroll
     for (int x = 0; x < FM + FN; ++x) {
-      const int f = w4_read(x);
+      const int f = BN == 256 ? w4_read(x) : w4n_read(x);
       if (f < FM) {
         fa[buf][f] = *reinterpret_cast<const bf16x8_t*>(ta + lane_kc[kk][f & 1] + 8192 * (f >> 1));
       } else if (LB == KC) {
-        fb[buf][f - FM] = *reinterpret_cast<const bf16x8_t*>(tb + lane_kc[kk][(f - FM) & 1] + 8192 * ((f - FM) >> 1));
+        const int rb = (BN == 256 ? 0 : 2 * wn) + (f - FM);  // 32-row block of the B quarter
+        fb[buf][f - FM] = *reinterpret_cast<const bf16x8_t*>(tb + lane_kc[kk][rb & 1] + 8192 * (rb >> 1));
       } else {
         const char* p = tb + lane_mc[f - FM] + 4096 * kk;
         const i16x4_t lo = ds_read_tr(p), hi = ds_read_tr(p + 1024);
@@ -751,7 +768,7 @@ gemm_w4_kernel(GemmArgs args) {
   auto mfma_sub = [&](int buf) {
 #pragma unroll
     for (int m = 0; m < FM * FN; ++m) {
-      const int i = w4_mi(m), j = w4_mj(m);
+      const int i = BN == 256 ? w4_mi(m) : m >> 1, j = BN == 256 ? w4_mj(m) : m & 1;
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf][j], fa[buf][i], acc[i][j], 0, 0, 0);
     }
   };
@@ -760,14 +777,19 @@ gemm_w4_kernel(GemmArgs args) {
   // writes LDS, so the compiler keeps it behind the reads before it).
   auto interleave = [&](auto nl) {
     constexpr int NL = decltype(nl)::value;
+    constexpr int NM = FM * FN, NR = FM + FN, S = NM - NR;  // MFMAs, reads, MFMAs after the reads
     static_assert(NL >= 0 && NL <= 8, "loads per sub-step");
 #pragma unroll
-    for (int m = 0; m < 16; ++m) {
+    for (int m = 0; m < NM; ++m) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                            // MFMA
       __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);                            // up to 3 VALU
-      if (m < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                 // LDS read
-      else if ((m - 7) * NL / 8 != (m - 8) * NL / 8)
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                          // global load
+      if (m < NR) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                          // LDS read
+      } else {
+#pragma unroll
+        for (int u = (m - NR) * NL / S; u < (m - NR + 1) * NL / S; ++u)
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                        // global load
+      }
     }
   };
   auto fence = [&]() { __builtin_amdgcn_sched_barrier(0); };
@@ -868,16 +890,17 @@ gemm_w4_kernel(GemmArgs args) {
   }
   __syncthreads();  // every wave is done with the operand slots
 
-  // Epilogue, one 64-column half of the wave's quadrant at a time, staged in the
+  // Epilogue, one 64-column half of the wave's sub-tile at a time, staged in the
   // wave's own 16 KiB of LDS.
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
+  for (int h = 0; h < FN / 2; ++h) {
     f32x16_t part[FM][2];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j) part[i][j] = acc[i][2 * h + j];
-    store_tile<EPI>(part, args, smem + wave * (64 * ROW_B), m0 + 128 * wm, n0 + 128 * wn + 64 * h, split, lane);
+    store_tile<EPI>(part, args, smem + wave * (64 * ROW_B), m0 + 128 * wm, n0 + (BN / 2) * wn + 64 * h, split,
+                    lane);
   }
 #else
   (void)args;
@@ -892,7 +915,7 @@ template <int BM, int BN, int WM_, int WN_, int LA, int LB, int EPI>
 hipError_t launch_one(const GemmArgs& a, int splits, hipStream_t s) {
   const int blocks = a.tiles_m * a.tiles_n * splits;
   if constexpr (BM == 256 && LA == KC)
-    return launch_kernel(kern::gemm_w4_kernel<LB, EPI>, dim3(blocks), dim3(256), s, a);
+    return launch_kernel(kern::gemm_w4_kernel<LB, EPI, BN>, dim3(blocks), dim3(256), s, a);
   else
     return launch_kernel(kern::gemm_kernel<BM, BN, WM_, WN_, LA, LB, EPI>, dim3(blocks), dim3(64 * WM_ * WN_), s, a);
 }
@@ -922,7 +945,7 @@ hipError_t dispatch_layout(Layout la, Layout lb, Epi epi, const GemmArgs& a, int
 
 }  // namespace
 
-int tile_bm(TileCfg t) { return t == TILE_256x256 ? 256 : 128; }
+int tile_bm(TileCfg t) { return t == TILE_128x128 ? 128 : 256; }
 int tile_bn(TileCfg t) { return t == TILE_256x256 ? 256 : 128; }
 
 hipError_t launch_gemm(TileCfg tile, Layout la, Layout lb, Epi epi, const GemmArgs& args, int splits,
@@ -930,6 +953,7 @@ hipError_t launch_gemm(TileCfg tile, Layout la, Layout lb, Epi epi, const GemmAr
   switch (tile) {
     case TILE_256x256: return dispatch_layout<256, 256, 2, 2>(la, lb, epi, args, splits, stream);
     case TILE_128x128: return dispatch_layout<128, 128, 2, 2>(la, lb, epi, args, splits, stream);
+    case TILE_256x128: return dispatch_layout<256, 128, 2, 2>(la, lb, epi, args, splits, stream);
     default: return hipErrorInvalidValue;
   }
 }

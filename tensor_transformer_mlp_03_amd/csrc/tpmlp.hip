@@ -69,6 +69,7 @@ int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 // tile; split-K adds a float32 round trip of the slices through memory and
 // one reduction launch.  Splits keep at least 512 of K each.
 constexpr double CU_RATE_256 = 4.3e12;   // flop/s per CU, 256x256 tile
+constexpr double CU_RATE_256x128 = 3.8e12;  // flop/s per CU, 256x128 tile (same kernel, half the MFMAs per load)
 constexpr double CU_RATE_128 = 1.3e12;   // flop/s per 128x128 block, two per CU
 constexpr double SPLIT_BW = 4.0e12;      // bytes/s for the slices' write and re-read
 constexpr double LAUNCH_S = 5e-6;
@@ -76,11 +77,11 @@ constexpr double LAUNCH_S = 5e-6;
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
   GemmPlan best{TILE_256x256, 1, (int)((K + TILE_BK - 1) / TILE_BK * TILE_BK)};
   double best_t = 1e30;
-  for (TileCfg tile : {TILE_256x256, TILE_128x128}) {
+  for (TileCfg tile : {TILE_256x256, TILE_256x128, TILE_128x128}) {
     const int64_t bm = tile_bm(tile), bn = tile_bn(tile);
     const int64_t tiles = (int64_t)ceil_div(M, bm) * ceil_div(N, bn);
-    const int64_t slots = tile == TILE_256x256 ? NUM_CU : 2 * NUM_CU;
-    const double rate = tile == TILE_256x256 ? CU_RATE_256 : CU_RATE_128;
+    const int64_t slots = tile == TILE_128x128 ? 2 * NUM_CU : NUM_CU;
+    const double rate = tile == TILE_256x256 ? CU_RATE_256 : tile == TILE_256x128 ? CU_RATE_256x128 : CU_RATE_128;
     for (int s = 1; s <= 16; ++s) {
       const int64_t kslice = ((K + s - 1) / s + TILE_BK - 1) / TILE_BK * TILE_BK;
       const int splits = ceil_div(K, kslice);

@@ -66,12 +66,16 @@ SMALL = [
     (8200, 136, 520, 2, True),
     # enough output tiles for 256 x 256 tiles, with the weights read N-contiguous
     (4104, 1032, 2056, 2, False),
+    # 256 x 128 tiles, unsplit for [M, F_i] and split 7 ways for [M, H] (and the
+    # other way round)
+    (1024, 1032, 16640, 1, True),
+    (1024, 16640, 1032, 1, False),
     # 4 x 65 output tiles of 256 x 256 (one wave and 4 more): the products with an
     # [M, F_i] output run 256 tiles whole and split only the last column block
     # along K (GeLU epilogue in the forward, dGeLU in the backward) ...
-    (1024, 1032, 16640, 1, True),
+    (1024, 2056, 16640, 1, True),
     # ... and with an [M, H] output (float32 epilogue, forward and dX)
-    (1024, 16640, 1032, 1, False),
+    (1024, 16640, 2056, 1, False),
     # fused forward (H a multiple of 64, at most 256): ragged rows and a ragged last
     # chunk of intermediate columns, with the pre-activation kept from it ...
     (200, 192, 392, 2, True),
@@ -290,14 +294,16 @@ def test_full_weights_oracle():
 
 
 @pytest.mark.parametrize("case", [(200, 264, 392, 3, True), (200, 192, 392, 2, False), (8, 64, 8, 2, True),
-                                  (1024, 16640, 1032, 2, False), (2048, 4096, 2048, 4, True)],
+                                  (1024, 16640, 2056, 2, False), (1024, 16640, 1032, 2, True),
+                                  (2048, 4096, 2048, 4, True)],
                          ids=lambda c: "x".join(map(str, c[:4])) + ("_store" if c[4] else "_recompute"))
 def test_folded_sum_equals_separate_sum_bitwise(case):
     """Without per-shard partials the drivers add each shard's partial to Z and dX in
     its product's epilogue (or its split reduction); the float32 additions are those
     of the separate rank-order sum, so the bits are the same.  Covers the fused
     forward (one and several chunks), hybrid split products ([M, H] outputs with a
-    split tail: H = 16640) and the 128 x 128 kernel (7B-class shard shapes)."""
+    split tail: H = 16640, F_i = 2056), split 256 x 128 products (F_i = 1032) and
+    256 x 128 tiles at 7B-class shard shapes."""
     from tensor_transformer_mlp_03_amd.device import DeviceMLP
     M, H, F, t, store = case
     say(f"[folded sum] M={M} H={H} F_i={F} t={t} store_p={store}")
@@ -458,7 +464,7 @@ def test_timing_spans_hybrid_dispatches():
     of two kernel dispatches, with a positive duration."""
     from tensor_transformer_mlp_03_amd import _lib as L
     from tensor_transformer_mlp_03_amd.device import DeviceMLP
-    w = I.custom_workload(315, M=1024, H=1032, F_i=16640, t=1)
+    w = I.custom_workload(315, M=1024, H=2056, F_i=16640, t=1)
     say(f"[timing hybrid] M={w.M} H={w.H} F_i={w.F_i}")
     d = DeviceMLP(I.make_inputs(w), store_p=True, driver=True)
     L.tpmlp_timing_begin(64)
