@@ -311,6 +311,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=3, help="workload index 0-4 (default 3)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of one step captured into a HIP graph (for launch-latency-bound "
+                         "workloads); per-kernel times then come from the eager warmup steps")
     ap.add_argument("--full-weights", action="store_true",
                     help="run the t-shard driver over the whole weights A[H, t F_i], B[t F_i, H] (shards as views)")
     ap.add_argument("--trace-order", default="",
@@ -376,7 +379,17 @@ def main():
 
     n_launch = 16 * (len(shards) + 1) * max(args.steps, 1)
     dom = None
-    if warm_stats and not args.trace_order:
+    graph = None
+    if args.graph:
+        if not warm_stats or args.trace_order:
+            print("--graph needs warmup steps (their events give the per-kernel times) and no --trace-order",
+                  file=sys.stderr)
+            sys.exit(2)
+        graph = d.capture()
+        graph.replay()
+        torch.cuda.synchronize()
+        dom = max((n for n in per_launch if warm_stats.get(n, (0, 0))[0]), key=lambda n: warm_stats[n][1])
+    elif warm_stats and not args.trace_order:
         dom = max((n for n in per_launch if warm_stats.get(n, (0, 0))[0]), key=lambda n: warm_stats[n][1])
         L.tpmlp_timing_begin_kinds(n_launch, [dom])
     else:
@@ -384,12 +397,19 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        d.step()
+        if graph is not None:
+            graph.replay()
+        else:
+            d.step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    stats, dropped = L.tpmlp_timing_end()
+    if graph is not None:
+        stats, dropped = warm_stats, 0
+    else:
+        stats, dropped = L.tpmlp_timing_end()
     log(f"[bench] timed {args.steps} steps in {t1 - t0:.4f} s"
-        + (f" (launches of {dom} timed)" if dom else " (every launch timed)"))
+        + (" (graph replays; kernel times from the warmup)" if graph is not None
+           else f" (launches of {dom} timed)" if dom else " (every launch timed)"))
     if args.trace_order:
         with open(args.trace_order, "w") as f:
             json.dump([[k, n] for (k, _), n in zip(L.tpmlp_timing_records(), L.tpmlp_timing_dispatches())], f)
@@ -399,7 +419,7 @@ def main():
     value = flops_step / (ms_per_step * 1e-3) / 1e12
 
     kernels = {}
-    src = warm_stats if dom else stats
+    src = warm_stats if (dom or graph is not None) else stats
     log(f"[bench] per kernel kind, {'warmup' if dom else 'timed'} steps:")
     for name, (count, total_ms) in src.items():
         if count:
@@ -439,6 +459,7 @@ def main():
         "config": {"workload": w.name, "M": w.M, "H": w.H, "F": w.F, "t": w.t, "F_i": w.F_i,
                    "shards_per_step": len(shards), "pre_activation": "recompute" if w.recompute else "stored",
                    "weights": "whole (shard views)" if args.full_weights else "per-shard buffers",
+                   "launch": "HIP graph replay" if args.graph else "eager",
                    "saved_activation_bytes_per_rank": L.tpmlp_saved_activation_bytes(w.M, w.H, w.F_i, w.recompute),
                    "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4), "timing_dropped": dropped},
         "roofline": roofline,

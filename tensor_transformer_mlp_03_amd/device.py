@@ -112,3 +112,18 @@ class DeviceMLP:
         self.forward(stream)
         if self.w.backward:
             self.backward(stream)
+
+    def capture(self):
+        """One step captured into a HIP graph (torch.cuda.CUDAGraph) on a side stream
+        of default priority.  Replaying it reruns the step's kernel launches on the
+        same buffers with no host work per launch, for workloads whose step time is
+        launch latency.  The library's calls enqueue kernels only (no memset, no
+        allocation, no host synchronisation), so the whole step can be captured."""
+        import torch
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            self.step()
+        torch.cuda.current_stream().wait_stream(s)
+        return g

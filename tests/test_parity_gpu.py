@@ -322,6 +322,31 @@ def test_folded_sum_equals_separate_sum_bitwise(case):
     assert (a.Z.double() - Z).abs().max() <= t * 2.0 ** -23 * Z.abs().max()
 
 
+@pytest.mark.parametrize("shape", [(200, 192, 392, 2), (1000, 520, 776, 2)], ids=["fused_forward", "two_products"])
+def test_graph_replay_matches_eager(shape):
+    """A step captured into a HIP graph gives, on every replay, the bits of the eager
+    step; between replays the outputs are overwritten by eager work and the
+    program synchronises, so each replay recomputes them."""
+    from tensor_transformer_mlp_03_amd.device import DeviceMLP
+    M, H, F, t = shape
+    say(f"[graph replay] M={M} H={H} F_i={F} t={t}")
+    w = I.custom_workload(321, M=M, H=H, F_i=F, t=t, w_std=0.05)
+    d = DeviceMLP(I.make_inputs(w), store_p=True, driver=True)
+    d.step()
+    torch.cuda.synchronize()
+    outs = lambda: [d.Z, d.dX] + list(d.dA) + list(d.dB) + list(d.P)
+    ref = [x.clone() for x in outs()]
+    g = d.capture()
+    for rep in range(3):
+        for x in outs():
+            x.fill_(float("nan") if x.dtype == torch.float32 else -1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for x, y in zip(outs(), ref):
+            assert torch.equal(x, y), f"replay {rep} differs"
+
+
 def test_deterministic():
     w = I.custom_workload(311, M=768, H=1024, F_i=1536, t=2)
     say(f"[determinism] {w}")
