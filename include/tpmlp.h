@@ -25,7 +25,7 @@
  *    does not synchronise.  Argument errors are reported before any HIP call is
  *    made and nothing is enqueued then.
  *  - M (token rows), H (hidden size) and F_i (the rank's slice of the intermediate
- *    size) must be positive multiples of 8 and at most 2^24; pointers must be
+ *    size) must be positive multiples of 8 and at most 2^23; pointers must be
  *    16-byte aligned.  Sizes need not be multiples of any tile size.
  *  - Only gfx950 devices are supported (TPMLP_ERR_UNSUPPORTED otherwise).
  *  - All entry points are thread-safe; calls that share a workspace must not
@@ -49,7 +49,7 @@ typedef uint16_t tpmlp_bf16; /* raw bf16 bits */
 typedef enum {
   TPMLP_OK = 0,
   TPMLP_ERR_NULL = 1,        /* a required pointer is NULL */
-  TPMLP_ERR_SHAPE = 2,       /* M, H or F_i not a positive multiple of 8, or above 2^24 */
+  TPMLP_ERR_SHAPE = 2,       /* M, H or F_i not a positive multiple of 8, or above 2^23 */
   TPMLP_ERR_ALIGN = 3,       /* a pointer is not 16-byte aligned */
   TPMLP_ERR_WORKSPACE = 4,   /* ws_bytes is below the workspace query's result */
   TPMLP_ERR_SHARDS = 5,      /* t outside 1..TPMLP_MAX_SHARDS */
@@ -178,7 +178,7 @@ tpmlp_status tpmlp_tp_bwd(const tpmlp_bf16* dZ, const tpmlp_bf16* X,
  * i's pre-activation as tpmlp_fwd's P_save.  Z[M,H] float32: the rank-order sum
  * of the shards' partials (shards one after another, as tpmlp_tp_fwd).
  * Workspace: tpmlp_tp_workspace_bytes(t, M, H, F_i).  t * F_i must be at most
- * 2^24 (TPMLP_ERR_SHAPE). */
+ * 2^23 (TPMLP_ERR_SHAPE). */
 tpmlp_status tpmlp_tp_fwd_full(const tpmlp_bf16* X, const tpmlp_bf16* A, const tpmlp_bf16* B,
                                tpmlp_bf16* P, float* Z, int t, int64_t M, int64_t H, int64_t F_i,
                                void* ws, size_t ws_bytes, void* stream);

@@ -70,7 +70,7 @@ __global__ void __launch_bounds__(256) ffn_fwd_kernel(FfnArgs g) {
   __shared__ __attribute__((aligned(16))) uint16_t bt[HMAX][CL];  // B_i chunk transposed [n][f]
   __shared__ __attribute__((aligned(16))) uint16_t gs[RB][CL];    // G chunk [m][f]
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int m0 = blockIdx.x * RB, f0 = blockIdx.y * FC;
   const int H = g.H, hv = H >> 3;  // 16-byte vectors per row of X and of B_i
 
@@ -84,7 +84,9 @@ __global__ void __launch_bounds__(256) ffn_fwd_kernel(FfnArgs g) {
   // branch per load would let the compiler wait on earlier loads inside it).
   u16x8_t xr[VPT], ar[8], br[8];
   const __amdgpu_buffer_rsrc_t xrs = make_rsrc(g.x + (int64_t)m0 * H);
-  const __amdgpu_buffer_rsrc_t ars = make_rsrc(g.a + f0);
+  // A_i rows of this wave's threads (64 w .. 64 w + 63) from a wave-uniform base,
+  // so that offsets stay within 64 rows of lda elements.
+  const __amdgpu_buffer_rsrc_t ars = make_rsrc(g.a + f0 + (int64_t)(64 * wave) * g.lda);
   const __amdgpu_buffer_rsrc_t brs = make_rsrc(g.b + (int64_t)f0 * H);
 #pragma unroll
   for (int i = 0; i < VPT; ++i) {
@@ -97,7 +99,7 @@ __global__ void __launch_bounds__(256) ffn_fwd_kernel(FfnArgs g) {
   const bool a_ok = tid < H && f0 + 8 * av < g.F;  // F % 8 == 0: a vector is in or out whole
 #pragma unroll
   for (int i = 0; i < 8; ++i)
-    ar[i] = load16(ars, a_ok ? (uint32_t)((8 * akb + i) * g.lda + 8 * av) * 2 : OOB);
+    ar[i] = load16(ars, a_ok ? (uint32_t)(((8 * akb + i - 64 * wave) * g.lda + 8 * av) * 2) : OOB);
   // B_i rows f0 + 8 (t % 8) + i, columns 8 (t / 8) .. +7.
   const int bv = tid >> 3, bfb = tid & 7;
 #pragma unroll

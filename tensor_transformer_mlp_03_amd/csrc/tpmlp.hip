@@ -32,7 +32,11 @@ thread_local LaunchEvents g_launch_events;
 
 namespace {
 
-constexpr int64_t MAX_DIM = int64_t(1) << 24;
+// Largest M, H, F_i (and t * F_i for the whole-weight drivers).  The kernels
+// address operands through buffer descriptors with 32-bit byte offsets from a
+// wave-uniform base, spanning at most 128 rows of a row-major operand:
+// 127 * 2^23 * 2 bytes stays below the descriptors' 2^31-byte range.
+constexpr int64_t MAX_DIM = int64_t(1) << 23;
 constexpr int NUM_CU = 256;  // MI355X compute units, used to size split-K
 constexpr size_t WS_ALIGN = 256;
 
@@ -323,7 +327,7 @@ tpmlp_status check_alias(const std::vector<Range>& outs, const std::vector<Range
 
 tpmlp_status check_shape(int64_t M, int64_t H, int64_t F) {
   if (!shape_ok(M) || !shape_ok(H) || !shape_ok(F))
-    return fail(TPMLP_ERR_SHAPE, "M, H and F_i must be positive multiples of 8, at most 2^24");
+    return fail(TPMLP_ERR_SHAPE, "M, H and F_i must be positive multiples of 8, at most 2^23");
   return TPMLP_OK;
 }
 
@@ -778,7 +782,7 @@ tpmlp_status tpmlp_tp_fwd_full(const tpmlp_bf16* X, const tpmlp_bf16* A, const t
   if (st) return st;
   if (P && !aligned16(P)) return fail(TPMLP_ERR_ALIGN, "P is not 16-byte aligned");
   if ((st = check_shape(M, H, F_i))) return st;
-  if (int64_t(t) * F_i > MAX_DIM) return fail(TPMLP_ERR_SHAPE, "t * F_i is above 2^24");
+  if (int64_t(t) * F_i > MAX_DIM) return fail(TPMLP_ERR_SHAPE, "t * F_i is above 2^23");
   const size_t need = tpmlp_tp_workspace_bytes(t, M, H, F_i);
   if (ws_bytes < need) return fail(TPMLP_ERR_WORKSPACE, "ws_bytes below tpmlp_tp_workspace_bytes");
   const int64_t F = int64_t(t) * F_i;
@@ -816,7 +820,7 @@ tpmlp_status tpmlp_tp_bwd_full(const tpmlp_bf16* dZ, const tpmlp_bf16* X, const 
   if (st) return st;
   if (P && !aligned16(P)) return fail(TPMLP_ERR_ALIGN, "P is not 16-byte aligned");
   if ((st = check_shape(M, H, F_i))) return st;
-  if (int64_t(t) * F_i > MAX_DIM) return fail(TPMLP_ERR_SHAPE, "t * F_i is above 2^24");
+  if (int64_t(t) * F_i > MAX_DIM) return fail(TPMLP_ERR_SHAPE, "t * F_i is above 2^23");
   const size_t need = tpmlp_tp_workspace_bytes(t, M, H, F_i);
   if (ws_bytes < need) return fail(TPMLP_ERR_WORKSPACE, "ws_bytes below tpmlp_tp_workspace_bytes");
   const int64_t F = int64_t(t) * F_i;

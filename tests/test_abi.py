@@ -155,6 +155,15 @@ def test_tp_argument_errors():
     assert lib.tpmlp_tp_bwd(_p(0), _p(3), A, B, None, dA, dBov, None, _p(1), t, M, H, F, _p(2), need, None) == ALIAS
 
 
+def test_dimension_limit():
+    """Dimensions up to 2^23 are accepted (workspace queries answer), one step more is
+    not: operand offsets of up to 128 rows must fit the 2^31-byte buffer range."""
+    assert L.tpmlp_fwd_workspace_bytes(8, 8, 1 << 23) > 0
+    assert L.tpmlp_fwd_workspace_bytes(8, 8, (1 << 23) + 8) == 0
+    assert L.tpmlp_bwd_workspace_bytes((1 << 23) + 8, 8, 8, 1) == 0
+    assert _fwd(H=(1 << 23) + 8)[0] == SHAPE
+
+
 def test_activation_accounting_and_policy():
     """Saved activations per rank: X always, P_i unless recomputed; the policy keeps
     P_i when it fits and recomputes only when the smaller footprint alone fits."""
@@ -179,7 +188,7 @@ def test_tp_full_argument_errors():
     assert lib.tpmlp_tp_fwd_full(X, None, B, None, Z, t, M, H, F, ws, need, None) == NULL
     assert lib.tpmlp_tp_fwd_full(X, A, B, None, Z, 0, M, H, F, ws, need, None) == SHARDS
     assert lib.tpmlp_tp_fwd_full(X, A, B, None, Z, t, M, H, 12, ws, need, None) == SHAPE
-    assert lib.tpmlp_tp_fwd_full(X, A, B, None, Z, 8, M, H, 1 << 22, ws, 1 << 62, None) == SHAPE  # t F_i > 2^24
+    assert lib.tpmlp_tp_fwd_full(X, A, B, None, Z, 8, M, H, 1 << 21, ws, 1 << 62, None) == SHAPE  # t F_i > 2^23
     assert lib.tpmlp_tp_fwd_full(X, A, B, None, Z, t, M, H, F, ws, need - 1, None) == WS
     assert lib.tpmlp_tp_fwd_full(X, A + 8, B, None, Z, t, M, H, F, ws, need, None) == ALIGN
     # Z inside the whole A (H t F_i bf16 elements from A): overlap
