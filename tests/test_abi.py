@@ -5,6 +5,7 @@ Every call here with made-up device addresses is invalid in at least one way
 that the library checks before any HIP call, so none of them can reach a kernel.
 """
 import ctypes
+import os
 import subprocess
 
 import pytest
@@ -40,6 +41,37 @@ def test_exports_every_declared_function():
     for f in declared:
         assert hasattr(lib, f)
     assert set(declared) == set(L._SIGS)
+
+
+def test_header_is_plain_c_and_links(tmp_path):
+    """include/tpmlp.h compiles as C99 with no HIP or torch header, and a C program
+    that calls the host-only entry points links against the library and runs (no
+    GPU needed: workspace queries, names, argument errors)."""
+    import shutil
+    cc = shutil.which("gcc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    src = tmp_path / "abi.c"
+    src.write_text(r"""
+#include <stdio.h>
+#include "tpmlp.h"
+int main(void) {
+  if (tpmlp_abi_version() != TPMLP_ABI_VERSION) return 1;
+  if (tpmlp_fwd_workspace_bytes(64, 256, 512) == 0) return 2;
+  if (tpmlp_fwd_workspace_bytes(60, 256, 512) != 0) return 3;
+  if (tpmlp_fwd(0, 0, 0, 0, 0, 64, 256, 512, 0, 0, 0) != TPMLP_ERR_NULL) return 4;
+  if (tpmlp_recompute_policy(2048, 20480, 10240, (size_t)1 << 40) != 0) return 5;
+  printf("%s|%s\n", tpmlp_status_str(TPMLP_ERR_ALIAS), tpmlp_kernel_name(TPMLP_K_FWD_FUSED));
+  return 0;
+}
+""")
+    exe = tmp_path / "abi"
+    lib_dir = os.path.dirname(L.LIB_PATH)
+    subprocess.run([cc, "-std=c99", "-Wall", "-Werror", "-I", os.path.dirname(L.HEADER), str(src), "-o", str(exe),
+                    "-L", lib_dir, "-ltpmlp", "-Wl,-rpath," + lib_dir], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert out.returncode == 0, (out.returncode, out.stderr)
+    assert out.stdout.strip() == f"{L.tpmlp_status_str(8)}|fwd_fused"
 
 
 def test_version_and_strings():
