@@ -203,6 +203,37 @@ def test_config_sampled(cfg):
     say("  err/tol:", {k: round(v, 3) for k, v in r.items()})
 
 
+def test_largest_hidden_size():
+    """H at the library's limit, 2^23: a 256-row tile's operand rows are 2^24 bytes
+    apart, so the loaders' 32-bit offsets within 128-row bands reach 2.1e9 bytes (X,
+    dZ and B_i read with row stride H, the transposes of X and dZ).  M = 136 gives
+    tiles with rows past 128.  Sampled rows of Z and dX and rows of dB are checked
+    against the oracle (tokens are independent: a row needs only its own X and dZ)."""
+    from tensor_transformer_mlp_03_amd.device import DeviceMLP
+    M, H, F = 136, 1 << 23, 64
+    say(f"[largest H] M={M} H={H} F_i={F}: generating inputs")
+    w = I.custom_workload(322, M=M, H=H, F_i=F, t=1, w_std=0.02)
+    inp = I.make_inputs(w)
+    say("  running")
+    d = DeviceMLP(inp, store_p=True, driver=False)
+    d.step()
+    torch.cuda.synchronize()
+    say("  checking")
+    rng = np.random.default_rng(322)
+    rows = _sample(M, 6, rng, must=[0, 127, 128, M - 1])
+    A, B = dec(inp.A[0]), dec(inp.B[0])
+    Xr, dZr = dec(inp.X[rows]), dec(inp.dZ[rows])
+    sub = np.arange(len(rows))
+    r = {}
+    check("Z[rows]", d.Z_sh[0][rows].cpu().numpy(), O.forward_rows(Xr, A, B, sub), r)
+    check("dX[rows]", d.dX_sh[0][rows].cpu().numpy(), O.backward_dX_rows(dZr, Xr, A, B, sub), r)
+    del Xr, dZr
+    frows = np.array([0, F - 1])
+    X, dZ = dec(inp.X), dec(inp.dZ)
+    check("dB[frows]", d.dB[0][frows].cpu().numpy(), O.backward_dB_rows(dZ, X, A, B, frows), r)
+    say("  err/tol:", {k: round(v, 3) for k, v in r.items()})
+
+
 @pytest.mark.parametrize("t", [2, 4, 8])
 def test_gpu_shard_sum_identity(t):
     """The t-shard driver's sum equals one unsharded run (t = 1) of the same A, B."""
