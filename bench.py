@@ -461,7 +461,10 @@ def main():
                    "weights": "whole (shard views)" if args.full_weights else "per-shard buffers",
                    "launch": "HIP graph replay" if args.graph else "eager",
                    "saved_activation_bytes_per_rank": L.tpmlp_saved_activation_bytes(w.M, w.H, w.F_i, w.recompute),
-                   "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4), "timing_dropped": dropped},
+                   "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
+                   # hardware FLOPs: the recomputed product of the pre-activation counted too
+                   "hfu_tflops": round(value * (14.0 if w.recompute else 12.0) / 12.0, 2) if w.backward else round(value, 2),
+                   "timing_dropped": dropped},
         "roofline": roofline,
         "cpu_baseline": None,
     }
