@@ -96,6 +96,14 @@ def gemm_alg_bytes(w, recompute, fold=False):
     }
 
 
+def dp_transposed(w):
+    """Whether the library transposes dP_i before dA_i = X^T dP_i for this shape: the
+    saving on one product, 2 M H F_i (1/1.14e15 - 1/1.2e15) s, is 1.5 times the
+    transpose, 4 M F_i / 5.5e12 s (the planner's rates), i.e. for H above ~12400."""
+    saved = 2.0 * w.M * w.H * w.F_i * (1.0 / 1.14e15 - 1.0 / 1.2e15)
+    return saved > 1.5 * 4.0 * w.M * w.F_i / 5.5e12
+
+
 def folds(w):
     """Whether bench's step folds the partial sums into the products: it runs the
     t-shard driver (every shard) without per-shard partials."""
@@ -208,10 +216,15 @@ def summarize(d, config):
         a["write"] += wr["counters"]["WRITE_SIZE"] * 1024 * w_scale
     alg = gemm_alg_bytes(w, w.recompute, fold=folds(w))
     if "transpose" in agg:
-        # A backward step transposes X and dZ ([M,H]) once each; every further launch
-        # is a weight transpose ([H,F_i] or [F_i,H]).  Per launch: the step's average.
-        n_t, n_x = agg["transpose"]["n"], (2 if w.backward else 0)
-        alg["transpose"] = (n_x * 4 * w.M * w.H + (n_t - n_x) * 4 * w.H * w.F_i) / n_t
+        # A backward step transposes X and dZ ([M,H]) once each, and dP ([M,F_i]) once per
+        # shard when the planner transposes it for dA (large H: the library's rule is
+        # restated in dp_transposed); every further launch is a weight transpose
+        # ([H,F_i] or [F_i,H]).  Per launch: the step's average.
+        n_t = agg["transpose"]["n"]
+        n_x = 2 if w.backward else 0
+        n_p = len(w.shards_timed) if (w.backward and dp_transposed(w)) else 0
+        alg["transpose"] = (n_x * 4 * w.M * w.H + n_p * 4 * w.M * w.F_i
+                            + (n_t - n_x - n_p) * 4 * w.H * w.F_i) / n_t
     alg["shard_sum"] = (w.t + 1) * w.M * w.H * 4  # t float32 partials in, their sum out
     os.makedirs(PROFILES, exist_ok=True)
     with open(os.path.join(PROFILES, f"{w.name}_kernels.md"), "w") as f:

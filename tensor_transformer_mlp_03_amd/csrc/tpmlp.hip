@@ -187,10 +187,20 @@ FwdPlan plan_fwd(int64_t M, int64_t H, int64_t F) {
   return p;
 }
 
+// dA_i = X^T dP_i reads dP_i N-contiguous unless dP_i is transposed first; the
+// transpose (4 M F bytes) pays when the one product's saving, at the rates above,
+// is 1.5 times its cost, i.e. for H above about 12400 (the 530B-class shard).
+bool transpose_dp(int64_t M, int64_t H, int64_t F) {
+  const double saved = 2.0 * double(M) * H * F * (1.0 / RATE_MC - 1.0 / RATE_KC);
+  const double cost = 4.0 * double(M) * F / TRANSPOSE_BW;
+  return saved > TRANSPOSE_MARGIN * cost;
+}
+
 struct BwdPlan {
   GemmPlan g0, g1, gdb, gda, gdx;
-  bool wt;  // the recompute product reads A_i^T from the workspace
-  size_t off_Xt, off_dZt, off_At, off_P, off_Gt, off_dP, off_part, total;
+  bool wt;   // the recompute product reads A_i^T from the workspace
+  bool tdp;  // dA reads dP_i^T from the workspace
+  size_t off_Xt, off_dZt, off_At, off_P, off_Gt, off_dP, off_dPt, off_part, total;
 };
 
 BwdPlan plan_bwd(int64_t M, int64_t H, int64_t F, bool recompute) {
@@ -208,8 +218,10 @@ BwdPlan plan_bwd(int64_t M, int64_t H, int64_t F, bool recompute) {
   p.off_At = 2 * mh;
   p.off_P = p.off_At + (p.wt ? align_up(size_t(H) * F * 2) : 0);
   p.off_Gt = p.off_P + (recompute ? mf : 0);
+  p.tdp = transpose_dp(M, H, F);
   p.off_dP = p.off_Gt + mf;
-  p.off_part = p.off_dP + mf;
+  p.off_dPt = p.off_dP + mf;
+  p.off_part = p.off_dPt + (p.tdp ? mf : 0);
   size_t part = recompute ? part_bytes(p.g0, M, F) : 0;
   part = std::max({part, part_bytes(p.g1, M, F), part_bytes(p.gdb, F, H), part_bytes(p.gda, H, F),
                    part_bytes(p.gdx, M, H)});
@@ -539,9 +551,18 @@ hipError_t enqueue_bwd(const tpmlp_bf16* dZ, const tpmlp_bf16* X, const tpmlp_bf
   // dB_i = G_i^T dZ    G_i^T: [F][M] = [M'][K], dZ^T: [H][M] = [N'][K] (both K-contig)
   e = run_gemm(TPMLP_K_BWD_DB, KC, KC, EPI_F32, Gt, M, dZt, M, F, H, M, p.gdb, dB, nullptr, nullptr, part, s);
   if (e != hipSuccess) return e;
-  // dA_i = X^T dP_i    X^T: [H][M] = [M'][K] (K-contig), dP_i: [M][F] = [K][N'] (N'-contig)
-  e = run_gemm(TPMLP_K_BWD_DA, KC, MC, EPI_F32, Xt, M, dP, F, H, F, M, p.gda, dA, nullptr, nullptr, part, s,
-               ldda);
+  if (p.tdp) {
+    uint16_t* dPt = reinterpret_cast<uint16_t*>(ws_at(ws, p.off_dPt));
+    e = timed(TPMLP_K_TRANSPOSE, s, [&] { return launch_transpose(dP, M, F, F, dPt, s); });
+    if (e != hipSuccess) return e;
+    // dA_i = X^T dP_i  X^T: [H][M] = [M'][K], dP_i^T: [F][M] = [N'][K] (both K-contig)
+    e = run_gemm(TPMLP_K_BWD_DA, KC, KC, EPI_F32, Xt, M, dPt, M, H, F, M, p.gda, dA, nullptr, nullptr, part, s,
+                 ldda);
+  } else {
+    // dA_i = X^T dP_i  X^T: [H][M] = [M'][K] (K-contig), dP_i: [M][F] = [K][N'] (N'-contig)
+    e = run_gemm(TPMLP_K_BWD_DA, KC, MC, EPI_F32, Xt, M, dP, F, H, F, M, p.gda, dA, nullptr, nullptr, part, s,
+                 ldda);
+  }
   if (e != hipSuccess) return e;
   // dX_i = dP_i A_i^T  dP_i: [M][F] (K-contig), A_i: [H][F] = [N][K] (K-contig)
   return run_gemm(TPMLP_K_BWD_DX, KC, KC, acc ? EPI_F32_ACC : EPI_F32, dP, F, A, lda, M, H, F, p.gdx, dX,
