@@ -325,8 +325,8 @@ def test_full_weights_oracle():
 
 
 @pytest.mark.parametrize("case", [(200, 264, 392, 3, True), (200, 192, 392, 2, False), (8, 64, 8, 2, True),
-                                  (1024, 16640, 2056, 2, False), (1024, 16640, 1032, 2, True),
-                                  (2048, 4096, 2048, 4, True)],
+                                  (64, 256, 512, 2, True), (1024, 16640, 2056, 2, False),
+                                  (1024, 16640, 1032, 2, True), (2048, 4096, 2048, 4, True)],
                          ids=lambda c: "x".join(map(str, c[:4])) + ("_store" if c[4] else "_recompute"))
 def test_folded_sum_equals_separate_sum_bitwise(case):
     """Without per-shard partials the drivers add each shard's partial to Z and dX in
