@@ -6,17 +6,19 @@
 // kernels are enqueued on the caller's stream.
 //
 // Rank i's forward is two launches (the column-parallel GEMM with the GeLU
-// epilogue, the row-parallel GEMM writing the float32 partial); its backward is
-// four or five (optional recompute of the pre-activation, the dGeLU GEMM, the
-// two weight-gradient GEMMs, the input-gradient GEMM), plus split-K reductions
-// where an output has too few tiles to fill the chip.  The weight-gradient
-// GEMMs read X and dZ transposed, so that every operand of the backward is
-// K-contiguous; the transposes are made once per backward call (once for all
-// shards in the t-shard driver).  The t-shard drivers run
-// the shards one after another and add the partials in rank order, standing in
-// for the all-reduces of the row-parallel output (forward) and of the
-// column-parallel input gradient (backward) ("大模型训练" notes §3.1; QLM page
-// §2.1.2.2 parts 1-3).
+// epilogue, the row-parallel GEMM writing the float32 partial), or, for small
+// hidden sizes, one fused launch and its chunk sum; its backward is four or five
+// (optional recompute of the pre-activation, the dGeLU GEMM, the two
+// weight-gradient GEMMs, the input-gradient GEMM), plus split-K reductions where
+// an output has too few tiles to fill the chip.  The weight-gradient GEMMs read
+// X and dZ transposed (and dP for large H), so that their operands are
+// K-contiguous; the transposes of X and dZ are made once per backward call (once
+// for all shards in the t-shard driver).  The t-shard drivers run the shards one
+// after another and add the partials in rank order, standing in for the
+// all-reduces of the row-parallel output (forward) and of the column-parallel
+// input gradient (backward) ("大模型训练" notes §3.1; QLM page §2.1.2.2 parts
+// 1-3); without per-shard outputs the additions happen in the epilogues of the
+// products that make the partials.
 
 #include "../../include/tpmlp.h"
 #include "common.h"
