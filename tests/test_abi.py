@@ -74,6 +74,30 @@ int main(void) {
     assert out.stdout.strip() == f"{L.tpmlp_status_str(8)}|fwd_fused"
 
 
+def test_last_error_is_per_thread():
+    """Argument errors from concurrent threads each leave their own detail in
+    tpmlp_last_error (thread-local), never another thread's."""
+    import threading
+    bad = {"X": dict(X=None), "ws": dict(ws=None), "shape": dict(M=60), "align": dict(A=_p(1) + 2)}
+    want = {"X": (NULL, "X"), "ws": (NULL, "ws"), "shape": (SHAPE, "multiples of 8"), "align": (ALIGN, "A_i")}
+    errors = []
+
+    def run(name):
+        for _ in range(200):
+            st, msg = _fwd(**bad[name])
+            code, text = want[name]
+            if st != code or text not in msg:
+                errors.append((name, st, msg))
+                return
+
+    threads = [threading.Thread(target=run, args=(n,)) for n in bad for _ in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors[:3]
+
+
 def test_version_and_strings():
     assert L.tpmlp_abi_version() == 7
     assert L.tpmlp_status_str(0) == "ok"
