@@ -148,9 +148,19 @@ def cpu_baseline(w, target_s=12.0):
             done.append(i)
     flops = 12.0 * rows * w.H * w.F_i * len(done)
     what = f"shards {done}" if len(done) > 1 else f"shard {done[0]}"
+    cpu, blas = "unknown CPU", "unknown BLAS"
+    try:
+        cpu = next(l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo") if l.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
+    try:
+        from threadpoolctl import threadpool_info
+        blas = ", ".join(sorted({p.get("internal_api", "?") for p in threadpool_info() if p.get("user_api") == "blas"}))
+    except Exception:
+        pass
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"float64 oracle forward+backward of {what} on the first {rows} of {w.M} token rows "
-                      f"(H={w.H}, F_i={w.F_i}); {dt:.2f} s"}
+                      f"(H={w.H}, F_i={w.F_i}); {dt:.2f} s on {cpu}, numpy BLAS {blas}"}
 
 
 def _order_entries(order):
