@@ -294,6 +294,12 @@ __device__ __forceinline__ void tile_of(int bid, int nblocks, int tiles_m, int t
 // are the first output row and column of the wave's (32 FM) x 64 tile.
 constexpr int ROW_B = 256;  // staged row stride in bytes (64 float32)
 
+// Chunk swizzle of the bf16 G rows that the dGeLU epilogue keeps in staging
+// rows.  A transposing read of a 16-lane group takes rows b + 8 q + r (q, r < 4)
+// at one column chunk; shifting the chunk by r + 4 q spreads them over 8
+// positions, two lanes per bank pair (the same as the row-contiguous reads).
+__device__ __forceinline__ int gt_swz(int r) { return (r + 4 * (r >> 3)) & 7; }
+
 template <int EPI, int FM, int FN>
 __device__ __forceinline__ void store_tile(const f32x16_t (&acc)[FM][FN], const GemmArgs& args, char* stage,
                                            int row_w, int col_w, int split, int lane) {
@@ -409,31 +415,35 @@ __device__ __forceinline__ void store_tile(const f32x16_t (&acc)[FM][FN], const 
           if (ok) *reinterpret_cast<u16x8_t*>(reinterpret_cast<uint16_t*>(args.out) + o) = v1;
           // Keep G of this row in LDS, in place of its float32 values (every
           // lane has read its float32 values above), in bytes [0, 128) of the
-          // row, 16-byte chunks swizzled by the row.  Rows and columns outside
-          // the output hold values that no transposed store below reads.
-          *reinterpret_cast<u16x8_t*>(stage + r * ROW_B + ((cp ^ (r & 7)) << 4)) = v2;
+          // row, 16-byte chunks swizzled by the row (gt_swz).  Rows and columns
+          // outside the output hold values that no transposed store below reads.
+          *reinterpret_cast<u16x8_t*>(stage + r * ROW_B + ((cp ^ gt_swz(r)) << 4)) = v2;
         }
       }
       if (EPI == EPI_DGELU) {
-        // Transposed store of G: ds_read_b64_tr_b16 turns 4 rows x 16 columns
-        // of a 16-lane group into one column per lane; two reads give 8
-        // consecutive rows, one 16-byte store into G^T.  All eight steps are
-        // read first, then stored.
-        const int g = lane >> 4, j = lane & 15;
+        // Transposed store of G in whole 128-byte lines.  ds_read_b64_tr_b16
+        // takes, in each 16-lane group, 4 rows x 16 columns (source lane 4 r + q:
+        // row r, columns 4 q .. +3) and hands lane i column i.  Source lane
+        // 4 r + q reads the 4 columns 8 it + 4 (g / 2) .. +3 of G row
+        // m0(q) + r, with m0(q) = 32 (g % 2) + 8 q, so lane 4 q + e receives
+        // rows m0(q) .. +3 of column 8 it + 4 (g / 2) + e; a second read gives
+        // rows +4 .. +7.  The 8 lanes (g % 2, q) of a column then hold its 64
+        // rows: one store instruction writes 8 columns x 128 bytes of G^T.  All
+        // eight steps are read first, then stored.
+        const int g = lane >> 4, j = lane & 15, jq = j & 3, jr = j >> 2;
+        const int half = (g >> 1) ? 8 : 0;
         i16x4_t lo[8], hi[8];
 #pragma unroll
         for (int it = 0; it < 8; ++it) {
-          const int o0 = 16 * (it & 3), k0 = 8 * ((it >> 2) * 4 + g);
-          const int o = o0 + 4 * (j & 3), c = o >> 3, half = (o & 4) ? 8 : 0;
-          const int ka = k0 + (j >> 2), kb = ka + 4;
-          lo[it] = ds_read_tr_after_stores(stage + ka * ROW_B + ((c ^ (ka & 7)) << 4) + half);
-          hi[it] = ds_read_tr_after_stores(stage + kb * ROW_B + ((c ^ (kb & 7)) << 4) + half);
+          const int ka = 32 * (g & 1) + 8 * jq + jr, kb = ka + 4;  // source role: q = jq, r = jr
+          lo[it] = ds_read_tr_after_stores(stage + ka * ROW_B + ((it ^ gt_swz(ka)) << 4) + half);
+          hi[it] = ds_read_tr_after_stores(stage + kb * ROW_B + ((it ^ gt_swz(kb)) << 4) + half);
         }
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the transposed reads above are complete
 #pragma unroll
         for (int it = 0; it < 8; ++it) {
-          const int o0 = 16 * (it & 3), k0 = 8 * ((it >> 2) * 4 + g);
-          const int f = col_w + o0 + j, m = row_w + 64 * h + k0;
+          // destination role: lane 4 q + e with q = jr, e = jq
+          const int f = col_w + 8 * it + 4 * (g >> 1) + jq, m = row_w + 64 * h + 32 * (g & 1) + 8 * jr;
           if (f < args.N && m < args.M) {
             const u16x8_t v = {(uint16_t)lo[it][0], (uint16_t)lo[it][1], (uint16_t)lo[it][2], (uint16_t)lo[it][3],
                                (uint16_t)hi[it][0], (uint16_t)hi[it][1], (uint16_t)hi[it][2], (uint16_t)hi[it][3]};
