@@ -327,53 +327,8 @@ def _summarize_counters(d, w, cmd, order, traffic):
     return path
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=3, help="workload index 0-4 (default 3)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--graph", action="store_true",
-                    help="time replays of one step captured into a HIP graph (for launch-latency-bound "
-                         "workloads); per-kernel times then come from the eager warmup steps")
-    ap.add_argument("--full-weights", action="store_true",
-                    help="run the t-shard driver over the whole weights A[H, t F_i], B[t F_i, H] (shards as views)")
-    ap.add_argument("--trace-order", default="",
-                    help="write [kernel kind, kernel dispatches] of the timed launches, in order, to this JSON file")
-    ap.add_argument("--summarize", default="",
-                    help="directory of rocprofv3 CSV outputs to summarize into profiles/ (no GPU needed)")
-    ap.add_argument("--copy-probe-mib", type=int, default=0,
-                    help="only run a plain copy of this many MiB through tpmlp_shard_sum with one part "
-                         "(reference dispatch for scaling HBM byte counters), then exit")
-    args = ap.parse_args()
-    if args.summarize:
-        summarize(args.summarize, args.config)
-        return
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the tensor-parallel "
-              "ranks' shards run one after another on a single GPU).", file=sys.stderr)
-        sys.exit(2)
-
-    import torch
-    from tensor_transformer_mlp_03_amd import _lib as L
-    from tensor_transformer_mlp_03_amd import inputs as I
-    from tensor_transformer_mlp_03_amd.device import DeviceMLP
-
-    if not torch.cuda.is_available():
-        print("no GPU visible", file=sys.stderr)
-        sys.exit(1)
-    L.lib()
-    if args.copy_probe_mib:
-        n = args.copy_probe_mib * (1 << 20) // 4
-        src = torch.ones(n, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            L.tpmlp_shard_sum([src], dst)
-        torch.cuda.synchronize()
-        log(f"[bench] copy probe: 3 dispatches, each reads and writes {args.copy_probe_mib} MiB")
-        return
-    w = I.CONFIGS[args.config]
+def measure(w, args, L, I, DeviceMLP, torch):
+    """Warmup and timed steps of one workload; returns its numbers."""
     shards = list(w.shards_timed)
     driver = len(shards) == w.t
     log(f"[bench] workload {w.name}: M={w.M} H={w.H} F_i={w.F_i} t={w.t} shards={shards} "
@@ -443,7 +398,7 @@ def main():
 
     kernels = {}
     src = warm_stats if (dom or graph is not None) else stats
-    log(f"[bench] per kernel kind, {'warmup' if dom else 'timed'} steps:")
+    log(f"[bench] {w.name} per kernel kind, {'warmup' if dom else 'timed'} steps:")
     for name, (count, total_ms) in src.items():
         if count:
             kernels[name] = {"launches": count, "avg_us": round(total_ms * 1e3 / count, 2),
@@ -465,6 +420,80 @@ def main():
         fetch, write = traffic[dom]
         roofline["traffic"] = int(fetch + write)
         roofline["traffic_fetch"], roofline["traffic_write"] = int(fetch), int(write)
+    log(f"[bench] {w.name}: {ms_per_step:.4f} ms per step, {value:.1f} TFLOP/s")
+    del d
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return {"shards": len(shards), "ms_per_step": ms_per_step, "value": value, "roofline": roofline,
+            "dropped": dropped}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=3, help="workload index 0-4 (default 3)")
+    ap.add_argument("--also", type=int, default=4,
+                    help="second workload timed in the same run and reported under \"workloads\" (default 4, "
+                         "the 530B-class shard; -1 for none; skipped with --graph or --trace-order)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of one step captured into a HIP graph (for launch-latency-bound "
+                         "workloads); per-kernel times then come from the eager warmup steps")
+    ap.add_argument("--full-weights", action="store_true",
+                    help="run the t-shard driver over the whole weights A[H, t F_i], B[t F_i, H] (shards as views)")
+    ap.add_argument("--trace-order", default="",
+                    help="write [kernel kind, kernel dispatches] of the timed launches, in order, to this JSON file")
+    ap.add_argument("--summarize", default="",
+                    help="directory of rocprofv3 CSV outputs to summarize into profiles/ (no GPU needed)")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a plain copy of this many MiB through tpmlp_shard_sum with one part "
+                         "(reference dispatch for scaling HBM byte counters), then exit")
+    args = ap.parse_args()
+    if args.summarize:
+        summarize(args.summarize, args.config)
+        return
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the tensor-parallel "
+              "ranks' shards run one after another on a single GPU).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from tensor_transformer_mlp_03_amd import _lib as L
+    from tensor_transformer_mlp_03_amd import inputs as I
+    from tensor_transformer_mlp_03_amd.device import DeviceMLP
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    L.lib()
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            L.tpmlp_shard_sum([src], dst)
+        torch.cuda.synchronize()
+        log(f"[bench] copy probe: 3 dispatches, each reads and writes {args.copy_probe_mib} MiB")
+        return
+    w = I.CONFIGS[args.config]
+    m = measure(w, args, L, I, DeviceMLP, torch)
+    extra = {}
+    if args.also >= 0 and args.also != args.config and not (args.graph or args.trace_order or args.full_weights):
+        # The second target workload, timed the same way in the same run, reported
+        # in its own object; the headline stays the first.
+        w2 = I.CONFIGS[args.also]
+        m2 = measure(w2, args, L, I, DeviceMLP, torch)
+        extra[w2.name] = {
+            "workload": w2.name, "M": w2.M, "H": w2.H, "F_i": w2.F_i, "t": w2.t,
+            "shards_per_step": m2["shards"], "pre_activation": "recompute" if w2.recompute else "stored",
+            "ms_per_step": round(m2["ms_per_step"], 4), "value": round(m2["value"], 2), "unit": "TFLOP/s",
+            "frac_of_peak": round(m2["value"] / PEAK_BF16_TFLOPS, 4),
+            "hfu_tflops": round(m2["value"] * (14.0 if w2.recompute else 12.0) / 12.0, 2),
+            "roofline": m2["roofline"], "timing_dropped": m2["dropped"]}
+    shards, ms_per_step, value, roofline, dropped = m["shards"], m["ms_per_step"], m["value"], m["roofline"], \
+        m["dropped"]
 
     result = {
         "metric": METRIC,
@@ -480,7 +509,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "M": w.M, "H": w.H, "F": w.F, "t": w.t, "F_i": w.F_i,
-                   "shards_per_step": len(shards), "pre_activation": "recompute" if w.recompute else "stored",
+                   "shards_per_step": shards, "pre_activation": "recompute" if w.recompute else "stored",
                    "weights": "whole (shard views)" if args.full_weights else "per-shard buffers",
                    "launch": "HIP graph replay" if args.graph else "eager",
                    "saved_activation_bytes_per_rank": L.tpmlp_saved_activation_bytes(w.M, w.H, w.F_i, w.recompute),
@@ -491,6 +520,8 @@ def main():
         "roofline": roofline,
         "cpu_baseline": None,
     }
+    if extra:
+        result["workloads"] = extra
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a row sample")
         result["cpu_baseline"] = cpu_baseline(w)

@@ -171,8 +171,9 @@ def tpmlp_fwd(X, A_i, B_i, Z_i, P_save, ws, stream=None):
     M, H = X.shape
     F = A_i.shape[1]
     _bf16(X, "X"), _bf16(A_i, "A_i"), _bf16(B_i, "B_i"), _f32(Z_i, "Z_i")
+    _shape(B_i, (F, H), "B_i"), _shape(Z_i, (M, H), "Z_i")
     if P_save is not None:
-        _bf16(P_save, "P_save")
+        _bf16(P_save, "P_save"), _shape(P_save, (M, F), "P_save")
     st = lib().tpmlp_fwd(_ptr(X), _ptr(A_i), _ptr(B_i), _ptr(Z_i), _ptr(P_save), M, H, F,
                          _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     _check(st, "tpmlp_fwd")
@@ -186,11 +187,44 @@ def tpmlp_bwd(dZ, X, A_i, B_i, P_saved, dX_i, dA_i, dB_i, ws, stream=None):
         _bf16(t, n)
     for t, n in ((dX_i, "dX_i"), (dA_i, "dA_i"), (dB_i, "dB_i")):
         _f32(t, n)
+    for t, n, shp in ((dZ, "dZ", (M, H)), (A_i, "A_i", (H, F)), (B_i, "B_i", (F, H)), (dX_i, "dX_i", (M, H)),
+                      (dA_i, "dA_i", (H, F)), (dB_i, "dB_i", (F, H))):
+        _shape(t, shp, n)
     if P_saved is not None:
-        _bf16(P_saved, "P_saved")
+        _bf16(P_saved, "P_saved"), _shape(P_saved, (M, F), "P_saved")
     st = lib().tpmlp_bwd(_ptr(dZ), _ptr(X), _ptr(A_i), _ptr(B_i), _ptr(P_saved), _ptr(dX_i), _ptr(dA_i),
                          _ptr(dB_i), M, H, F, _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     _check(st, "tpmlp_bwd")
+
+
+def _shape(t, shape, name):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t
+
+
+def _shards(items, t, shape, name, check, nullable=False):
+    """Checks a list of t per-shard tensors (entries None allowed if nullable)."""
+    if items is None:
+        return
+    if len(items) != t:
+        raise ValueError(f"{name} has {len(items)} entries, expected t = {t}")
+    for i, x in enumerate(items):
+        if x is None:
+            if not nullable:
+                raise ValueError(f"{name}[{i}] is None")
+            continue
+        check(x, f"{name}[{i}]")
+        _shape(x, shape, f"{name}[{i}]")
+
+
+def _whole(A, B, t, H):
+    """F_i of the whole weights A[H, t F_i], B[t F_i, H]."""
+    if t < 1 or A.shape[1] % t:
+        raise ValueError(f"A has {A.shape[1]} columns, not a multiple of t = {t}")
+    _shape(A, (H, A.shape[1]), "A")
+    _shape(B, (A.shape[1], H), "B")
+    return A.shape[1] // t
 
 
 def tpmlp_tp_fwd(X, A_sh, B_sh, P_sh, Z_sh, Z, ws, stream=None):
@@ -198,6 +232,11 @@ def tpmlp_tp_fwd(X, A_sh, B_sh, P_sh, Z_sh, Z, ws, stream=None):
     t = len(A_sh)
     M, H = X.shape
     F = A_sh[0].shape[1]
+    _bf16(X, "X"), _f32(Z, "Z"), _shape(Z, (M, H), "Z")
+    _shards(A_sh, t, (H, F), "A_sh", _bf16)
+    _shards(B_sh, t, (F, H), "B_sh", _bf16)
+    _shards(P_sh, t, (M, F), "P_sh", _bf16, nullable=True)
+    _shards(Z_sh, t, (M, H), "Z_sh", _f32, nullable=True)
     st = lib().tpmlp_tp_fwd(_ptr(X), _ptr_array(A_sh, t), _ptr_array(B_sh, t), _ptr_array(P_sh, t),
                             _ptr_array(Z_sh, t), _ptr(Z), t, M, H, F, _ptr(ws),
                             ws.numel() * ws.element_size(), _stream(stream))
@@ -209,6 +248,13 @@ def tpmlp_tp_bwd(dZ, X, A_sh, B_sh, P_sh, dA_sh, dB_sh, dX_sh, dX, ws, stream=No
     t = len(A_sh)
     M, H = X.shape
     F = A_sh[0].shape[1]
+    _bf16(dZ, "dZ"), _shape(dZ, (M, H), "dZ"), _bf16(X, "X"), _f32(dX, "dX"), _shape(dX, (M, H), "dX")
+    _shards(A_sh, t, (H, F), "A_sh", _bf16)
+    _shards(B_sh, t, (F, H), "B_sh", _bf16)
+    _shards(P_sh, t, (M, F), "P_sh", _bf16)
+    _shards(dA_sh, t, (H, F), "dA_sh", _f32)
+    _shards(dB_sh, t, (F, H), "dB_sh", _f32)
+    _shards(dX_sh, t, (M, H), "dX_sh", _f32, nullable=True)
     st = lib().tpmlp_tp_bwd(_ptr(dZ), _ptr(X), _ptr_array(A_sh, t), _ptr_array(B_sh, t), _ptr_array(P_sh, t),
                             _ptr_array(dA_sh, t), _ptr_array(dB_sh, t), _ptr_array(dX_sh, t), _ptr(dX), t, M,
                             H, F, _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
@@ -219,7 +265,12 @@ def tpmlp_tp_fwd_full(X, A, B, P, Z, t, ws, stream=None):
     """All t shards' forward over the whole weights A[H, t F_i], B[t F_i, H] (no shard
     copies); P: None or t blocks [M, F_i] of bf16; Z[M,H] float32 the summed output."""
     M, H = X.shape
-    F = A.shape[1] // t
+    F = _whole(A, B, t, H)
+    _bf16(X, "X"), _bf16(A, "A"), _bf16(B, "B"), _f32(Z, "Z"), _shape(Z, (M, H), "Z")
+    if P is not None:
+        _bf16(P, "P")
+        if P.numel() != t * M * F:
+            raise ValueError(f"P holds {P.numel()} elements, expected t * M * F_i = {t * M * F}")
     st = lib().tpmlp_tp_fwd_full(_ptr(X), _ptr(A), _ptr(B), _ptr(P), _ptr(Z), t, M, H, F, _ptr(ws),
                                  ws.numel() * ws.element_size(), _stream(stream))
     _check(st, "tpmlp_tp_fwd_full")
@@ -229,7 +280,16 @@ def tpmlp_tp_bwd_full(dZ, X, A, B, P, dA, dB, dX, t, ws, stream=None):
     """All t shards' backward over the whole weights; dA[H, t F_i] and dB[t F_i, H] are
     the whole float32 weight gradients, dX the sum of the shards' partials."""
     M, H = X.shape
-    F = A.shape[1] // t
+    F = _whole(A, B, t, H)
+    for x, n in ((dZ, "dZ"), (X, "X"), (A, "A"), (B, "B")):
+        _bf16(x, n)
+    _shape(dZ, (M, H), "dZ")
+    for x, n, shp in ((dA, "dA", (H, t * F)), (dB, "dB", (t * F, H)), (dX, "dX", (M, H))):
+        _f32(x, n), _shape(x, shp, n)
+    if P is not None:
+        _bf16(P, "P")
+        if P.numel() != t * M * F:
+            raise ValueError(f"P holds {P.numel()} elements, expected t * M * F_i = {t * M * F}")
     st = lib().tpmlp_tp_bwd_full(_ptr(dZ), _ptr(X), _ptr(A), _ptr(B), _ptr(P), _ptr(dA), _ptr(dB), _ptr(dX), t,
                                  M, H, F, _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     _check(st, "tpmlp_tp_bwd_full")
@@ -247,6 +307,11 @@ def tpmlp_recompute_policy(M: int, H: int, F: int, budget_bytes: int) -> int:
 def tpmlp_shard_sum(parts, out, stream=None):
     """out = parts[0] + ... + parts[t-1] (float32, in order)."""
     t = len(parts)
+    _f32(out, "out")
+    for i, p in enumerate(parts):
+        _f32(p, f"parts[{i}]")
+        if p.numel() != out.numel():
+            raise ValueError(f"parts[{i}] holds {p.numel()} elements, out {out.numel()}")
     st = lib().tpmlp_shard_sum(_ptr_array(parts, t), t, _ptr(out), out.numel(), _stream(stream))
     _check(st, "tpmlp_shard_sum")
 

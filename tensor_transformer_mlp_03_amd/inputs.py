@@ -173,14 +173,18 @@ def make_dZ(w: Workload, seed: int = 0) -> np.ndarray:
     return normal_bf16(seed, w.key, TID_DZ, 0, (w.M, w.H), 1.0)
 
 
-def make_inputs(w: Workload, seed: int = 0, shards=None) -> Inputs:
+def make_inputs(w: Workload, seed: int = 0, shards=None, workers: int = 8) -> Inputs:
     """Generate the workload's tensors.  ``shards`` limits which weight shards are
-    generated (others are None); default: all ``t``."""
-    shards = range(w.t) if shards is None else shards
+    generated (others are None); default: all ``t``.  Shards are drawn on up to
+    ``workers`` threads (each has its own stream, so the values do not depend on
+    the number of threads)."""
+    from concurrent.futures import ThreadPoolExecutor
+    shards = list(range(w.t) if shards is None else shards)
     A: List[Optional[np.ndarray]] = [None] * w.t
     B: List[Optional[np.ndarray]] = [None] * w.t
-    for i in shards:
-        A[i] = make_A_shard(w, i, seed)
-        B[i] = make_B_shard(w, i, seed)
+    jobs = [(A, make_A_shard, i) for i in shards] + [(B, make_B_shard, i) for i in shards]
+    with ThreadPoolExecutor(max_workers=max(1, min(workers, len(jobs)))) as ex:
+        for (dst, _, i), arr in zip(jobs, ex.map(lambda j: j[1](w, j[2], seed), jobs)):
+            dst[i] = arr
     dZ = make_dZ(w, seed) if w.backward else None
     return Inputs(w, make_X(w, seed), A, B, dZ, outlier_rows(w, seed))

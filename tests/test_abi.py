@@ -158,6 +158,36 @@ def test_fwd_argument_errors():
     assert st == ALIAS and "Z_i" in msg
 
 
+def test_python_wrappers_check_tensors():
+    """The binding rejects tensors of the wrong dtype, layout or shape before it
+    calls the library (CPU tensors; nothing reaches a C entry point)."""
+    torch = pytest.importorskip("torch")
+    bf = dict(dtype=torch.bfloat16)
+    M, H, F, t = 16, 32, 24, 2
+    X = torch.zeros((M, H), **bf)
+    A = torch.zeros((H, t * F), **bf)
+    B = torch.zeros((t * F, H), **bf)
+    Z = torch.zeros((M, H))
+    ws = torch.zeros(8, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="multiple of t"):
+        L.tpmlp_tp_fwd_full(X, A[:, :t * F - 1], B, None, Z, t, ws, stream=0)
+    with pytest.raises(ValueError, match="shape"):
+        L.tpmlp_tp_fwd_full(X, A, B[:-8], None, Z, t, ws, stream=0)
+    with pytest.raises(TypeError, match="float32"):
+        L.tpmlp_tp_fwd_full(X, A, B, None, Z.double(), t, ws, stream=0)
+    shards_A = [A[:, i * F:(i + 1) * F] for i in range(t)]  # strided views
+    shards_B = [B[i * F:(i + 1) * F] for i in range(t)]
+    with pytest.raises(ValueError, match="contiguous"):
+        L.tpmlp_tp_fwd(X, shards_A, shards_B, None, None, Z, ws, stream=0)
+    shards_A = [a.contiguous() for a in shards_A]
+    with pytest.raises(ValueError, match="shape"):
+        L.tpmlp_tp_fwd(X, shards_A, [shards_B[0], shards_B[1][:8]], None, None, Z, ws, stream=0)
+    with pytest.raises(ValueError, match="entries"):
+        L.tpmlp_tp_fwd(X, shards_A, shards_B, [None], None, Z, ws, stream=0)
+    with pytest.raises(ValueError, match="shape"):
+        L.tpmlp_fwd(X, shards_A[0], shards_B[0], torch.zeros((M, H + 8)), None, ws, stream=0)
+
+
 def _bwd(**kw):
     a = dict(dZ=_p(0), X=_p(1), A=_p(2), B=_p(3), P=None, dX=_p(4), dA=_p(5), dB=_p(6), M=64, H=256, F=512,
              ws=_p(7), wsb=1 << 30)

@@ -11,6 +11,7 @@ import sys
 import numpy as np
 import pytest
 
+import margins
 from oracle import oracle as O
 from tensor_transformer_mlp_03_amd import inputs as I
 
@@ -40,8 +41,20 @@ def check(name, got, ref, ratios):
     err = O.max_abs_err(got, ref)
     tol = O.tolerance(ref)
     ratios[name] = err / tol
+    margins.record(name, err / tol)
     assert np.all(np.isfinite(got)), f"{name}: non-finite values"
-    assert err <= tol, f"{name}: max err {err:.3e} > tol {tol:.3e}"
+    assert err <= tol, f"{name}: max err {err:.3e} > tol {tol:.3e} (err/tol {err / tol:.3f})"
+
+
+def check_dev(name, got, ref, ratios):
+    """check() on two device tensors of the same shape, reduced on the GPU (for
+    outputs too large to copy back whole); ref is the reference side."""
+    err = (got.double() - ref.double()).abs().max().item()
+    tol = 1e-2 * ref.double().abs().max().item() + 1e-3
+    ratios[name] = err / tol
+    margins.record(name, err / tol)
+    assert bool(torch.isfinite(got).all()), f"{name}: non-finite values"
+    assert err <= tol, f"{name}: max err {err:.3e} > tol {tol:.3e} (err/tol {err / tol:.3f})"
 
 
 def run_device(inp, store_p=True, keep_partials=True):
@@ -159,47 +172,153 @@ def _sample(n, k, rng, must=()):
     return np.array(sorted(idx))
 
 
-@pytest.mark.parametrize("cfg", [3, 4])
-def test_config_sampled(cfg):
-    """Full-size runs; rows of Z/dX and columns of dA_i / rows of dB_i compared."""
-    w = I.CONFIGS[cfg]
-    say(f"[parity config{cfg} sampled] {w}")
-    shards = list(w.shards_timed)
-    inp = I.make_inputs(w, shards=shards)
+def _per_block(n, block, per_block, rng, exclude=()):
+    """per_block distinct seeded indices from every block of `block` consecutive
+    indices of range(n) (the last block may be short), none of them in `exclude`:
+    every output tile row (or column) block is touched."""
+    ex = np.zeros(n, dtype=bool)
+    ex[np.asarray(exclude, dtype=np.int64)] = True
+    out = []
+    for b0 in range(0, n, block):
+        cand = np.nonzero(~ex[b0:b0 + block])[0] + b0
+        out.extend(rng.choice(cand, size=min(per_block, cand.size), replace=False).tolist())
+    return np.array(sorted(out), dtype=np.int64)
+
+
+def test_config3_sampled():
+    """Long-context chunk at full size, all four shards, per-shard partials kept.
+
+    Rows of Z_i, dX_i, Z and dX are compared in two classes, each against a
+    tolerance from its own max|oracle|: two seeded rows from every 256-row tile of
+    rows that are not outliers, and 32 of the 328 outlier rows (X scaled x8).  The
+    outliers dominate max|oracle| of a mixed sample, so a mixed check would judge
+    the normal rows at about 8x the stated tolerance.  Columns of dA_i and rows of
+    dB_i: two from every 256-wide block of F_i (the split-K products' tiles)."""
+    w = I.CONFIGS[3]
+    say(f"[parity config3 sampled] {w}")
+    inp = I.make_inputs(w)
     from tensor_transformer_mlp_03_amd.device import DeviceMLP
-    driver = len(shards) == w.t
-    d = DeviceMLP(inp, store_p=not w.recompute, driver=driver, keep_partials=True)
+    d = DeviceMLP(inp, store_p=True, driver=True, keep_partials=True)
     d.step()
     torch.cuda.synchronize()
-    rng = np.random.default_rng(1234 + cfg)
-    rows = _sample(w.M, 24, rng, must=inp.outliers[:8])
+    rng = np.random.default_rng(1234 + 3)
+    normal = _per_block(w.M, 256, 2, rng, exclude=inp.outliers)
+    outl = np.sort(rng.choice(inp.outliers, size=32, replace=False))
+    cols = _per_block(w.F_i, 256, 2, rng)
+    say(f"  {normal.size} normal rows, {outl.size} outlier rows, {cols.size} dA columns / dB rows")
     X, dZ = dec(inp.X), dec(inp.dZ)
     r = {}
-    Zs, dXs = None, None
-    for j, i in enumerate(shards):
+    sums = {}
+    for i in range(w.t):
         A, B = dec(inp.A[i]), dec(inp.B[i])
-        z = O.forward_rows(X, A, B, rows)
-        dx = O.backward_dX_rows(dZ, X, A, B, rows)
-        Zs = z if Zs is None else Zs + z
-        dXs = dx if dXs is None else dXs + dx
-        check(f"Z_{i}[rows]", d.Z_sh[j][rows].cpu().numpy(), z, r)
-        check(f"dX_{i}[rows]", d.dX_sh[j][rows].cpu().numpy(), dx, r)
-        cols = _sample(w.F_i, 6, rng, must=[0, w.F_i - 1])
-        check(f"dA_{i}[:,cols]", d.dA[j][:, cols].cpu().numpy(), O.backward_dA_cols(dZ, X, A, B, cols), r)
-        check(f"dB_{i}[cols,:]", d.dB[j][cols, :].cpu().numpy(), O.backward_dB_rows(dZ, X, A, B, cols), r)
+        for cls, rows in (("normal", normal), ("outlier", outl)):
+            z = O.forward_rows(X, A, B, rows)
+            dx = O.backward_dX_rows(dZ, X, A, B, rows)
+            check(f"Z_{i}[{cls}]", d.Z_sh[i][rows].cpu().numpy(), z, r)
+            check(f"dX_{i}[{cls}]", d.dX_sh[i][rows].cpu().numpy(), dx, r)
+            zs, dxs = sums.get(cls, (0.0, 0.0))
+            sums[cls] = (zs + z, dxs + dx)
+        check(f"dA_{i}[:,cols]", d.dA[i][:, cols].cpu().numpy(), O.backward_dA_cols(dZ, X, A, B, cols), r)
+        check(f"dB_{i}[cols,:]", d.dB[i][cols, :].cpu().numpy(), O.backward_dB_rows(dZ, X, A, B, cols), r)
         del A, B
-    if driver:
-        check("Z[rows]", d.Z[rows].cpu().numpy(), Zs, r)
-        check("dX[rows]", d.dX[rows].cpu().numpy(), dXs, r)
-        # The launch configuration the benchmark times: no per-shard partials, the
-        # sums folded into the products.  Same bits as the run checked above.
-        b = DeviceMLP(inp, store_p=not w.recompute, driver=True, keep_partials=False)
-        b.step()
-        torch.cuda.synchronize()
-        assert torch.equal(b.Z, d.Z) and torch.equal(b.dX, d.dX)
-        for x, y in list(zip(b.dA, d.dA)) + list(zip(b.dB, d.dB)):
-            assert torch.equal(x, y)
-        del b
+    for cls, rows in (("normal", normal), ("outlier", outl)):
+        check(f"Z[{cls}]", d.Z[rows].cpu().numpy(), sums[cls][0], r)
+        check(f"dX[{cls}]", d.dX[rows].cpu().numpy(), sums[cls][1], r)
+    # The launch configuration the benchmark times: no per-shard partials, the
+    # sums folded into the products.  Same bits as the run checked above.
+    b = DeviceMLP(inp, store_p=True, driver=True, keep_partials=False)
+    b.step()
+    torch.cuda.synchronize()
+    assert torch.equal(b.Z, d.Z) and torch.equal(b.dX, d.dX)
+    for x, y in list(zip(b.dA, d.dA)) + list(zip(b.dB, d.dB)):
+        assert torch.equal(x, y)
+    del b
+    say("  err/tol:", {k: round(v, 3) for k, v in r.items()})
+
+
+def test_config4_shard0_sampled():
+    """530B-class shard 0 at full size in the launch configuration the benchmark
+    times (one rank's tpmlp_fwd and tpmlp_bwd, pre-activation recomputed): two
+    seeded rows from every 256-row tile plus the first and last rows, and two
+    dA_0 columns / dB_0 rows from every 256-wide block of F_i (the hybrid
+    products' whole-wave columns and their split tail, columns 8192 on)."""
+    w = I.CONFIGS[4]
+    say(f"[parity config4 shard 0 sampled] {w}")
+    inp = I.make_inputs(w, shards=[0])
+    from tensor_transformer_mlp_03_amd.device import DeviceMLP
+    d = DeviceMLP(inp, store_p=False, driver=False, shards=[0])
+    d.step()
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(1234 + 4)
+    rows = np.union1d(_per_block(w.M, 256, 2, rng), [0, w.M - 1])
+    cols = _per_block(w.F_i, 256, 2, rng)
+    X, dZ = dec(inp.X), dec(inp.dZ)
+    A, B = dec(inp.A[0]), dec(inp.B[0])
+    r = {}
+    check("Z_0[rows]", d.Z_sh[0][rows].cpu().numpy(), O.forward_rows(X, A, B, rows), r)
+    check("dX_0[rows]", d.dX_sh[0][rows].cpu().numpy(), O.backward_dX_rows(dZ, X, A, B, rows), r)
+    check("dA_0[:,cols]", d.dA[0][:, cols].cpu().numpy(), O.backward_dA_cols(dZ, X, A, B, cols), r)
+    check("dB_0[cols,:]", d.dB[0][cols, :].cpu().numpy(), O.backward_dB_rows(dZ, X, A, B, cols), r)
+    say("  err/tol:", {k: round(v, 3) for k, v in r.items()})
+
+
+def test_config4_shard_sum_identity():
+    """530B-class workload with all eight shards: the t-shard driver (sums folded
+    into the products, pre-activation recomputed) against the unsharded MLP.
+
+    * Z and dX on 64 seeded rows against the oracle of the unsharded weights
+      A = [A_0 | ... | A_7], B = [B_0; ...; B_7] (each decoded whole, 13.4 GB of
+      float64), so the identity sum_i GeLU(X A_i) B_i = GeLU(X A) B is checked at
+      H = 20480, F = 81920;
+    * Z, dX and the weight-gradient blocks against one GPU run with t = 1 on the
+      whole weights (F_i = 81920);
+    * the whole-weight driver (shards as strided views of A and B) gives the bits
+      of the per-shard driver."""
+    from tensor_transformer_mlp_03_amd.device import DeviceMLP
+    w = I.CONFIGS[4]
+    say(f"[identity config4] {w}: generating all {w.t} shards")
+    inp = I.make_inputs(w)
+    say("  t = 8 driver")
+    d = DeviceMLP(inp, store_p=False, driver=True, keep_partials=False)
+    d.step()
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(4321)
+    rows = np.union1d(rng.choice(w.M, size=62, replace=False), [0, w.M - 1])
+    say("  oracle of the unsharded MLP on 64 rows")
+    Xr, dZr = dec(inp.X[rows]), dec(inp.dZ[rows])
+    Af = dec(np.concatenate(inp.A, axis=1))          # [H, F] float64
+    P = Xr @ Af
+    Bf = dec(np.concatenate(inp.B, axis=0))          # [F, H]
+    Z = O.gelu(P) @ Bf
+    dP = (dZr @ Bf.T) * O.gelu_grad(P)
+    del Bf
+    dX = dP @ Af.T
+    del Af, P, dP
+    r = {}
+    check("Z[rows]_vs_unsharded", d.Z[rows].cpu().numpy(), Z, r)
+    check("dX[rows]_vs_unsharded", d.dX[rows].cpu().numpy(), dX, r)
+    say("  t = 1 run on the whole weights")
+    one = I.Inputs(I.custom_workload(340, M=w.M, H=w.H, F_i=w.F, t=1, w_std=w.w_std, recompute=True), inp.X,
+                   [np.concatenate(inp.A, axis=1)], [np.concatenate(inp.B, axis=0)], inp.dZ)
+    d1 = DeviceMLP(one, store_p=False, driver=True)
+    del one
+    d1.step()
+    torch.cuda.synchronize()
+    check_dev("Z_t8_vs_t1", d.Z, d1.Z, r)
+    check_dev("dX_t8_vs_t1", d.dX, d1.dX, r)
+    F = w.F_i
+    for i in range(w.t):
+        check_dev(f"dA_{i}_vs_t1_block", d.dA[i], d1.dA[0][:, i * F:(i + 1) * F], r)
+        check_dev(f"dB_{i}_vs_t1_block", d.dB[i], d1.dB[0][i * F:(i + 1) * F], r)
+    del d1
+    torch.cuda.empty_cache()
+    say("  whole-weight driver")
+    f = DeviceMLP(inp, store_p=False, driver=True, full_weights=True)
+    f.step()
+    torch.cuda.synchronize()
+    assert torch.equal(f.Z, d.Z) and torch.equal(f.dX, d.dX)
+    for x, y in list(zip(f.dA, d.dA)) + list(zip(f.dB, d.dB)):
+        assert torch.equal(x, y)
     say("  err/tol:", {k: round(v, 3) for k, v in r.items()})
 
 
@@ -404,37 +523,119 @@ def test_zero_input_gives_exact_zeros():
     check("dX", d.dX.cpu().numpy(), ref, r)
 
 
-def test_no_writes_outside_outputs():
-    """Outputs are views into larger buffers filled with a canary; after a forward and
-    backward at a ragged shape the canary bands are untouched."""
+CANARY_F32 = float("nan")
+CANARY_I16 = -12345
+CANARY_U8 = 77
+PAD = 4096  # canary elements on each side of every output
+
+
+def _padded(n, dtype):
+    """A buffer of n + 2 PAD elements filled with the canary, and its middle n."""
+    fill = CANARY_F32 if dtype == torch.float32 else CANARY_I16 if dtype == torch.int16 else CANARY_U8
+    buf = torch.full((n + 2 * PAD,), fill, dtype=dtype, device="cuda")
+    return buf, buf[PAD:PAD + n]
+
+
+def _canary_intact(buf, n, name):
+    lo, hi = buf[:PAD], buf[PAD + n:]
+    if buf.dtype == torch.float32:
+        ok = bool(torch.isnan(lo).all()) and bool(torch.isnan(hi).all())
+        assert bool(torch.isfinite(buf[PAD:PAD + n]).all()), f"{name}: unwritten or non-finite values inside"
+    else:
+        fill = CANARY_I16 if buf.dtype == torch.int16 else CANARY_U8
+        ok = bool((lo == fill).all()) and bool((hi == fill).all())
+    assert ok, f"{name}: a write landed outside the buffer"
+
+
+CANARY_CASES = [
+    # (M, H, F_i, t, store_p, mode): mode "rank" = tpmlp_fwd/tpmlp_bwd per shard,
+    # "driver" = t-shard driver with the sums folded into the products, "whole" =
+    # the whole-weight driver (A_i, dA_i strided column views)
+    (136, 264, 200, 1, True, "rank"),        # plain ragged products, unsplit
+    (1024, 2056, 16640, 1, True, "rank"),    # [M, F_i] products as whole waves + split tail (GeLU, dGeLU)
+    (1024, 16640, 2056, 1, False, "rank"),   # [M, H] products as whole waves + split tail (float32, dX)
+    (200, 192, 392, 1, True, "rank"),        # fused small-H forward: chunk partials, P_save from the fused kernel
+    (200, 264, 392, 3, True, "driver"),      # folded sums: shards 1, 2 add into Z and dX in their epilogues
+    (1024, 16640, 1032, 2, False, "driver"), # folded sums in split reductions
+    (200, 264, 392, 3, True, "whole"),       # strided column blocks of A, P, dA
+    (1024, 1032, 2056, 2, True, "whole"),    # the same with 256 x 128 tiles and splits
+]
+
+
+@pytest.mark.parametrize("case", CANARY_CASES, ids=lambda c: "x".join(map(str, c[:4])) + "_" + c[5])
+def test_no_writes_outside_outputs(case):
+    """Every output and the workspace sit inside larger buffers filled with a
+    canary; after a forward and backward the canary bands are untouched and the
+    outputs are finite.  For the whole-weight driver, shard i's column blocks of
+    P, dA and dB sit between other shards' blocks: the results must also equal,
+    bit for bit, those of the per-shard driver on separate buffers, so a shard
+    that wrote into an earlier shard's block would show there (a write into a
+    later block is overwritten by that shard, but every shard runs the same code
+    with a different base, and the last shard's overrun would hit the canary or
+    the next row's first block)."""
     from tensor_transformer_mlp_03_amd import _lib as L
-    M, H, F = 136, 264, 200
-    say(f"[canary] M={M} H={H} F_i={F}")
-    w = I.custom_workload(313, M=M, H=H, F_i=F, t=1)
+    from tensor_transformer_mlp_03_amd.device import DeviceMLP, to_device
+    M, H, F, t, store, mode = case
+    say(f"[canary] M={M} H={H} F_i={F} t={t} store_p={store} {mode}")
+    w = I.custom_workload(313, M=M, H=H, F_i=F, t=t, w_std=0.05)
     inp = I.make_inputs(w)
-    from tensor_transformer_mlp_03_amd.device import to_device
-    X, dZ, A, B = (to_device(v) for v in (inp.X, inp.dZ, inp.A[0], inp.B[0]))
-    pad = 4096
-    canary = float("nan")
+    X, dZ = to_device(inp.X), to_device(inp.dZ)
+    A = [to_device(a) for a in inp.A]
+    B = [to_device(b) for b in inp.B]
+    bufs = []
 
-    def padded(n, dtype):
-        buf = torch.full((n + 2 * pad,), canary, dtype=torch.float32, device="cuda") if dtype == torch.float32 \
-            else torch.full((n + 2 * pad,), -12345, dtype=torch.int16, device="cuda")
-        return buf, buf[pad:pad + n]
+    def out(n, dtype, name, shape):
+        buf, v = _padded(n, dtype)
+        bufs.append((buf, n, name))
+        return v.view(*shape)
 
-    (Zb, Z), (Pb, P) = padded(M * H, torch.float32), padded(M * F, torch.int16)
-    (dXb, dX), (dAb, dA), (dBb, dB) = padded(M * H, torch.float32), padded(H * F, torch.float32), padded(F * H, torch.float32)
-    wsn = max(L.tpmlp_fwd_workspace_bytes(M, H, F), L.tpmlp_bwd_workspace_bytes(M, H, F, False))
-    wsb = torch.full((wsn + 2 * 4096,), 77, dtype=torch.uint8, device="cuda")
-    ws = wsb[4096:4096 + wsn]
-    L.tpmlp_fwd(X, A, B, Z.view(M, H), P.view(M, F), ws)
-    L.tpmlp_bwd(dZ, X, A, B, P.view(M, F), dX.view(M, H), dA.view(H, F), dB.view(F, H), ws)
+    f32, i16 = torch.float32, torch.int16
+    if mode == "rank":
+        wsn = max(L.tpmlp_fwd_workspace_bytes(M, H, F), L.tpmlp_bwd_workspace_bytes(M, H, F, not store))
+        ws = out(wsn, torch.uint8, "ws", (wsn,))
+        for i in range(t):
+            Z = out(M * H, f32, f"Z_{i}", (M, H))
+            P = out(M * F, i16, f"P_{i}", (M, F)) if store else None
+            dX = out(M * H, f32, f"dX_{i}", (M, H))
+            dA = out(H * F, f32, f"dA_{i}", (H, F))
+            dB = out(F * H, f32, f"dB_{i}", (F, H))
+            L.tpmlp_fwd(X, A[i], B[i], Z, P, ws)
+            L.tpmlp_bwd(dZ, X, A[i], B[i], P, dX, dA, dB, ws)
+    elif mode == "driver":
+        wsn = L.tpmlp_tp_workspace_bytes(t, M, H, F)
+        ws = out(wsn, torch.uint8, "ws", (wsn,))
+        Z, dX = out(M * H, f32, "Z", (M, H)), out(M * H, f32, "dX", (M, H))
+        P = [out(M * F, i16, f"P_{i}", (M, F)) for i in range(t)] if store else None
+        dA = [out(H * F, f32, f"dA_{i}", (H, F)) for i in range(t)]
+        dB = [out(F * H, f32, f"dB_{i}", (F, H)) for i in range(t)]
+        L.tpmlp_tp_fwd(X, A, B, P, None, Z, ws)
+        L.tpmlp_tp_bwd(dZ, X, A, B, P, dA, dB, None, dX, ws)
+    else:
+        wsn = L.tpmlp_tp_workspace_bytes(t, M, H, F)
+        ws = out(wsn, torch.uint8, "ws", (wsn,))
+        Af, Bf = torch.cat(A, 1).contiguous(), torch.cat(B, 0).contiguous()
+        Z, dX = out(M * H, f32, "Z", (M, H)), out(M * H, f32, "dX", (M, H))
+        P = out(t * M * F, i16, "P", (t, M, F)) if store else None
+        dA = out(H * t * F, f32, "dA", (H, t * F))
+        dB = out(t * F * H, f32, "dB", (t * F, H))
+        L.tpmlp_tp_fwd_full(X, Af, Bf, P, Z, t, ws)
+        L.tpmlp_tp_bwd_full(dZ, X, Af, Bf, P, dA, dB, dX, t, ws)
+        ref = DeviceMLP(inp, store_p=store, driver=True)
+        ref.step()
+        torch.cuda.synchronize()
+        assert torch.equal(Z, ref.Z) and torch.equal(dX, ref.dX)
+        for i in range(t):
+            assert torch.equal(dA[:, i * F:(i + 1) * F], ref.dA[i]), f"dA block {i}"
+            assert torch.equal(dB[i * F:(i + 1) * F], ref.dB[i]), f"dB block {i}"
+            if store:
+                assert torch.equal(P[i], ref.P[i]), f"P block {i}"
     torch.cuda.synchronize()
-    for buf, n in ((Zb, M * H), (dXb, M * H), (dAb, H * F), (dBb, F * H)):
-        assert torch.isnan(buf[:pad]).all() and torch.isnan(buf[pad + n:]).all()
-        assert torch.isfinite(buf[pad:pad + n]).all()
-    assert (Pb[:pad] == -12345).all() and (Pb[pad + M * F:] == -12345).all()
-    assert (wsb[:4096] == 77).all() and (wsb[4096 + wsn:] == 77).all()
+    for buf, n, name in bufs:
+        if name == "ws":
+            fill_ok = bool((buf[:PAD] == CANARY_U8).all()) and bool((buf[PAD + n:] == CANARY_U8).all())
+            assert fill_ok, "workspace: a write landed outside it"
+        else:
+            _canary_intact(buf, n, name)
 
 
 def test_shard_sum_kernel_exact():
