@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define TPMLP_ABI_VERSION 7
+#define TPMLP_ABI_VERSION 8
 #define TPMLP_MAX_SHARDS 64
 
 typedef uint16_t tpmlp_bf16; /* raw bf16 bits */
@@ -199,6 +199,31 @@ tpmlp_status tpmlp_tp_bwd_full(const tpmlp_bf16* dZ, const tpmlp_bf16* X, const 
  * array of t device pointers; n must be a positive multiple of 4.  `out` may not
  * overlap any part. */
 tpmlp_status tpmlp_shard_sum(const float* const* parts, int t, float* out, int64_t n, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Forward without allocation or workspace                                  */
+/* ------------------------------------------------------------------------ */
+
+/* Bytes of the library's own device scratch array that tpmlp_fwd_noalloc
+ * uses in place of a workspace: 64 MiB per GPU, reserved when the library's
+ * code is loaded on that GPU and held until the process ends. */
+#define TPMLP_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* tpmlp_fwd with no workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  Same kernels, same launches and the same bits as
+ * tpmlp_fwd; the intermediate G_i and any split-K slices live in a file-scope
+ * device array of TPMLP_NOALLOC_SCRATCH_BYTES, one per GPU, whose address is
+ * looked up once per device (hipGetSymbolAddress) on the first call there.
+ * The call allocates nothing and frees nothing.  Nothing in the array has to
+ * start at zero: every byte a launch reads was written earlier in the call.
+ * Returns TPMLP_ERR_WORKSPACE when tpmlp_fwd_workspace_bytes(M, H, F_i)
+ * exceeds TPMLP_NOALLOC_SCRATCH_BYTES.  All calls on one GPU share its array:
+ * calls that overlap in time on one GPU (different streams, or different host
+ * threads) race and must not be made. */
+tpmlp_status tpmlp_fwd_noalloc(const tpmlp_bf16* X, const tpmlp_bf16* A_i, const tpmlp_bf16* B_i,
+                               float* Z_i, tpmlp_bf16* P_save,
+                               int64_t M, int64_t H, int64_t F_i, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Kernel timing (measurement aid; not needed to compute anything)           */

@@ -57,6 +57,7 @@ _SIGS = {
     "tpmlp_tp_fwd_full": ([_vp, _vp, _vp, _vp, _vp, _int, _i64, _i64, _i64, _vp, _sz, _vp], _int),
     "tpmlp_tp_bwd_full": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _i64, _i64, _i64, _vp, _sz, _vp], _int),
     "tpmlp_shard_sum": ([_PP, _int, _vp, _i64, _vp], _int),
+    "tpmlp_fwd_noalloc": ([_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp], _int),
     "tpmlp_timing_begin": ([_int], _int),
     "tpmlp_timing_begin_kinds": ([_int, ctypes.c_uint], _int),
     "tpmlp_timing_end": ([ctypes.POINTER(_int), ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_int)], _int),
@@ -177,6 +178,23 @@ def tpmlp_fwd(X, A_i, B_i, Z_i, P_save, ws, stream=None):
     st = lib().tpmlp_fwd(_ptr(X), _ptr(A_i), _ptr(B_i), _ptr(Z_i), _ptr(P_save), M, H, F,
                          _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     _check(st, "tpmlp_fwd")
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # TPMLP_NOALLOC_SCRATCH_BYTES
+
+
+def tpmlp_fwd_noalloc(X, A_i, B_i, Z_i, P_save, stream=None):
+    """tpmlp_fwd with the library's own device scratch array as its workspace (no
+    allocation); shapes whose forward workspace exceeds NOALLOC_SCRATCH_BYTES are
+    rejected with TPMLP_ERR_WORKSPACE."""
+    M, H = X.shape
+    F = A_i.shape[1]
+    _bf16(X, "X"), _bf16(A_i, "A_i"), _bf16(B_i, "B_i"), _f32(Z_i, "Z_i")
+    _shape(B_i, (F, H), "B_i"), _shape(Z_i, (M, H), "Z_i")
+    if P_save is not None:
+        _bf16(P_save, "P_save"), _shape(P_save, (M, F), "P_save")
+    st = lib().tpmlp_fwd_noalloc(_ptr(X), _ptr(A_i), _ptr(B_i), _ptr(Z_i), _ptr(P_save), M, H, F, _stream(stream))
+    _check(st, "tpmlp_fwd_noalloc")
 
 
 def tpmlp_bwd(dZ, X, A_i, B_i, P_saved, dX_i, dA_i, dB_i, ws, stream=None):

@@ -34,6 +34,11 @@ thread_local LaunchEvents g_launch_events;
 
 namespace {
 
+// The no-allocation forward's workspace: one array per GPU, reserved with the
+// library's code object.  In host code its name is only a stand-in for the
+// symbol; the device address comes from hipGetSymbolAddress (noalloc_scratch).
+__device__ __align__(256) unsigned char scratch[TPMLP_NOALLOC_SCRATCH_BYTES];
+
 // Largest M, H, F_i (and t * F_i for the whole-weight drivers).  The kernels
 // address operands through buffer descriptors with 32-bit byte offsets from a
 // wave-uniform base, spanning at most 128 rows of a row-major operand:
@@ -571,6 +576,27 @@ hipError_t enqueue_bwd(const tpmlp_bf16* dZ, const tpmlp_bf16* X, const tpmlp_bf
                   nullptr, nullptr, part, s);
 }
 
+// Device address of `scratch` on the current device, looked up once per device.
+std::mutex g_scratch_mu;
+std::vector<void*> g_scratch_ptr;
+
+tpmlp_status noalloc_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(TPMLP_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if ((int)g_scratch_ptr.size() <= dev) g_scratch_ptr.resize(dev + 1, nullptr);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(TPMLP_ERR_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return TPMLP_OK;
+}
+
 }  // namespace
 }  // namespace tpmlp
 
@@ -630,6 +656,30 @@ tpmlp_status tpmlp_fwd(const tpmlp_bf16* X, const tpmlp_bf16* A_i, const tpmlp_b
   if ((st = check_device())) return st;
   hipError_t e = enqueue_fwd(X, A_i, F_i, B_i, Z_i, P_save, M, H, F_i, ws, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? TPMLP_OK : hip_fail(e, "tpmlp_fwd launch");
+}
+
+
+tpmlp_status tpmlp_fwd_noalloc(const tpmlp_bf16* X, const tpmlp_bf16* A_i, const tpmlp_bf16* B_i,
+                               float* Z_i, tpmlp_bf16* P_save, int64_t M, int64_t H, int64_t F_i,
+                               void* stream) {
+  g_last_error.clear();
+  tpmlp_status st = check_ptrs({{X, "X"}, {A_i, "A_i"}, {B_i, "B_i"}, {Z_i, "Z_i"}});
+  if (st) return st;
+  if (P_save && !aligned16(P_save)) return fail(TPMLP_ERR_ALIGN, "P_save is not 16-byte aligned");
+  if ((st = check_shape(M, H, F_i))) return st;
+  const size_t need = tpmlp_fwd_workspace_bytes(M, H, F_i);
+  if (need > TPMLP_NOALLOC_SCRATCH_BYTES)
+    return fail(TPMLP_ERR_WORKSPACE, "the shape needs " + std::to_string(need) +
+                                         " bytes of workspace, above TPMLP_NOALLOC_SCRATCH_BYTES");
+  const size_t mh = size_t(M) * H, hf = size_t(H) * F_i, mf = size_t(M) * F_i;
+  std::vector<Range> ins = {{X, mh * 2, "X"}, {A_i, hf * 2, "A_i"}, {B_i, hf * 2, "B_i"}};
+  std::vector<Range> outs = {{Z_i, mh * 4, "Z_i"}, {P_save, P_save ? mf * 2 : 0, "P_save"}};
+  if ((st = check_alias(outs, ins))) return st;
+  if ((st = check_device())) return st;
+  void* ws = nullptr;
+  if ((st = noalloc_scratch(&ws))) return st;
+  hipError_t e = enqueue_fwd(X, A_i, F_i, B_i, Z_i, P_save, M, H, F_i, ws, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TPMLP_OK : hip_fail(e, "tpmlp_fwd_noalloc launch");
 }
 
 tpmlp_status tpmlp_bwd(const tpmlp_bf16* dZ, const tpmlp_bf16* X, const tpmlp_bf16* A_i, const tpmlp_bf16* B_i,

@@ -99,7 +99,7 @@ def test_last_error_is_per_thread():
 
 
 def test_version_and_strings():
-    assert L.tpmlp_abi_version() == 7
+    assert L.tpmlp_abi_version() == 8
     assert L.tpmlp_status_str(0) == "ok"
     assert L.tpmlp_status_str(ALIAS) == "output overlaps another buffer"
     assert L.tpmlp_status_str(99) == "unknown status"
@@ -156,6 +156,30 @@ def test_fwd_argument_errors():
     assert _fwd(P=_p(2))[0] == ALIAS                 # P_save on B_i
     st, msg = _fwd(Z=_p(1))
     assert st == ALIAS and "Z_i" in msg
+
+
+def _fwd_noalloc(**kw):
+    a = dict(X=_p(0), A=_p(1), B=_p(2), Z=_p(3), P=None, M=64, H=256, F=512)
+    a.update(kw)
+    st = L.lib().tpmlp_fwd_noalloc(a["X"], a["A"], a["B"], a["Z"], a["P"], a["M"], a["H"], a["F"], None)
+    return st, L.lib().tpmlp_last_error().decode()
+
+
+def test_fwd_noalloc_argument_errors():
+    """The no-allocation forward checks its arguments as tpmlp_fwd does, and rejects
+    shapes whose forward workspace exceeds the scratch array's fixed size before
+    any HIP call; a valid small shape gets as far as the device check."""
+    assert _fwd_noalloc(X=None)[0] == NULL
+    assert _fwd_noalloc(Z=_p(3) + 4)[0] == ALIGN
+    assert _fwd_noalloc(M=60)[0] == SHAPE
+    assert _fwd_noalloc(Z=_p(0) + 64)[0] == ALIAS
+    for M, H, F in ((32768, 3584, 3584), (2048, 20480, 10240)):
+        assert L.tpmlp_fwd_workspace_bytes(M, H, F) > L.NOALLOC_SCRATCH_BYTES
+        st, msg = _fwd_noalloc(M=M, H=H, F=F)
+        assert st == WS and "TPMLP_NOALLOC_SCRATCH_BYTES" in msg
+    # the largest of the benchmark shapes that fits uses all of it
+    assert L.tpmlp_fwd_workspace_bytes(4096, 1024, 4096) == L.NOALLOC_SCRATCH_BYTES
+    assert _fwd_noalloc(M=4096, H=1024, F=4096)[0] in (HIP, UNSUP)  # no GPU here
 
 
 def test_python_wrappers_check_tensors():
