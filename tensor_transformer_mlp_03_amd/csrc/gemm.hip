@@ -1,7 +1,7 @@
 // bf16 MFMA GEMM core for gfx950 with the MLP's fused epilogues.
 //
-// C[m,n] = sum_k A[m,k] B[k,n], bf16 operands, float32 accumulation on
-// v_mfma_f32_32x32x16_bf16.  Every product of the tensor-parallel MLP's forward
+// C[m,n] = sum_k A[m,k] B[k,n], bf16 operands, float32 accumulation on the
+// bf16 MFMA instructions.  Every product of the tensor-parallel MLP's forward
 // and backward is one launch with an operand layout and an epilogue (KC: K
 // contiguous; MC: the other dimension contiguous; X^T, dZ^T and, when the
 // planner chooses, A_i^T and B_i^T are transposed copies):
@@ -21,17 +21,18 @@
 // part 三, 算子融合.)
 //
 // Two kernels:
-//  * gemm_w4_kernel: 256 x 256 tiles, A K-contiguous, B either; four waves,
-//    one per SIMD, each accumulating a 128 x 128 quadrant, with loads and LDS
-//    reads interleaved between its MFMAs (its comment has the schedule).  The
-//    main path.
-//  * gemm_kernel: a synchronous two-stage pipeline with 128 x 128 tiles, an
-//    N-contiguous operand transposed in registers; used for outputs too small
-//    for 256 x 256 tiles.
+//  * gemm_x16_kernel: 256 x 256 or 256 x 128 tiles, A K-contiguous, B either;
+//    four waves, one per SIMD, each accumulating a 128 x 128 (or 128 x 64)
+//    sub-tile as 16 x 16 blocks on v_mfma_f32_16x16x32_bf16, with loads and LDS
+//    reads placed between its MFMAs (its comment has the schedule).  The main
+//    path.
+//  * gemm_kernel: a synchronous two-stage pipeline with 128 x 128 tiles on
+//    v_mfma_f32_32x32x16_bf16, an N-contiguous operand transposed in registers;
+//    used for outputs too small for 256-row tiles.
 // Shared design points:
 //  * A K-contiguous operand tile sits in LDS as [rows][64] (128-byte rows), so
 //    an MFMA operand fragment is one ds_read_b128 per lane (8 consecutive k of
-//    one row); an N-contiguous one in gemm_w4_kernel as [64 k][128 n] halves,
+//    one row); an N-contiguous one in gemm_x16_kernel as [64 k][128 n] slots,
 //    read with two ds_read_b64_tr_b16 per fragment.
 //  * Operands go from memory straight into LDS with buffer_load ... lds (16
 //    bytes per lane, no staging registers, no LDS write instructions).  Buffer
@@ -45,7 +46,7 @@
 //    4 consecutive output columns of one row: epilogues store 8- or 16-byte
 //    vectors.
 //  * Workgroups are renumbered so that consecutive output tiles (which share
-//    operand panels) run on the same XCD and its L2, then grouped 8 tiles tall.
+//    operand panels) run on the same XCD and its L2, then grouped 4 tiles tall.
 
 #include "common.h"
 #include "epilogue.h"
@@ -167,68 +168,6 @@ __device__ __forceinline__ bf16x8_t read_frag(const char* tile, int r0, int kk, 
   return *reinterpret_cast<const bf16x8_t*>(tile + tile_off(r, 2 * kk + (lane >> 5)));
 }
 
-// Four waves' LDS-DMA loads of 128 rows x 64 k of a K-contiguous operand into
-// one 16 KiB [128][64] LDS slot: 16 instructions of 1 KiB, 4 per wave.
-// Instruction i of wave w fills rows 8*(4i + w) .. +7 of the slot; lane q
-// writes 16-byte position q & 7 of row q / 8 and loads the chunk that the
-// swizzle places there.  A row's swizzle depends on the lane and on
-// (4i + w) & 7, so even and odd i use two lane patterns.
-struct HalfDma {
-  uint32_t lane_off[2];  // byte offset of the lane's chunk for even / odd i
-  int kc[2];             // its first k inside the K step
-
-  __device__ __forceinline__ void init(int64_t ld, int w, int lane) {
-#pragma unroll
-    for (int par = 0; par < 2; ++par) {
-      const int c = (lane & 7) ^ (((lane >> 3) ^ (4 * par + w)) & 7);
-      kc[par] = 8 * c;
-      lane_off[par] = (uint32_t)(((int64_t)(lane >> 3) * ld + 8 * c) * 2);
-    }
-  }
-  // Instruction i of the wave's share; base: element (first row of the half,
-  // first k of the step).
-  __device__ __forceinline__ void issue_one(const uint16_t* base, int64_t ld, char* half, int rows_left, int k_left,
-                                            int w, int lane, int i) const {
-    const int r0 = 8 * (4 * i + w);
-    const bool ok = (kc[i & 1] < k_left) && (r0 + (lane >> 3) < rows_left);
-    const uint32_t off = lane_off[i & 1] + (uint32_t)((int64_t)r0 * ld * 2);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(base), (lds_void_t*)(half + (4 * i + w) * 1024), 16,
-                                             ok ? off : OOB, 0, 0, 0);
-  }
-};
-
-// The same for an N-contiguous operand (stored [K][ld], n contiguous): one half
-// of a K step is 64 k-rows x 128 n, kept in LDS as [64][128] (256-byte rows),
-// 16 KiB.  The 16-byte chunk holding n .. n+7 of k-row k sits at position
-// (n / 8) ^ (4 * (k % 4)) of the row (mc_off): a transposing fragment read
-// touches 4 consecutive k-rows of 32 columns per 32 lanes, which this spreads
-// over all 64 banks (unswizzled, the 4 rows, 256 bytes apart, hit the same
-// banks).  Instruction i of wave w fills k-rows 4*(4i + w) .. +3 (LDS bytes
-// (4i + w) * 1024 ..); lane q writes position q % 16 of k-row q / 16 and loads
-// the chunk placed there, which depends only on the lane since k % 4 = (q / 16)
-// % 4.  One instruction reads 4 k-rows x 256 bytes.
-__device__ __forceinline__ int mc_off(int k, int n) { return k * 256 + (((n >> 3) ^ (4 * (k & 3))) << 4) + (n & 7) * 2; }
-
-struct HalfDmaMC {
-  uint32_t lane_off;  // byte offset of the lane's chunk in instruction 0
-  int lane_k, lane_n;  // the chunk's k-row in instruction 0 and first n
-
-  __device__ __forceinline__ void init(int64_t ld, int w, int lane) {
-    lane_k = 4 * w + (lane >> 4);
-    lane_n = 8 * ((lane & 15) ^ (4 * ((lane >> 4) & 3)));
-    lane_off = (uint32_t)(((int64_t)lane_k * ld + lane_n) * 2);
-  }
-  // Instruction i of the wave's share; base: element (first k of the step,
-  // first n of the half).
-  __device__ __forceinline__ void issue_one(const uint16_t* base, int64_t ld, char* half, int n_left, int k_left,
-                                            int w, int lane, int i) const {
-    const bool ok = lane_n < n_left && (lane_k + 16 * i < k_left);
-    const uint32_t off = lane_off + (uint32_t)((int64_t)(16 * i) * ld * 2);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(base), (lds_void_t*)(half + (4 * i + w) * 1024), 16,
-                                             ok ? off : OOB, 0, 0, 0);
-  }
-};
-
 // ds_read_b64_tr_b16 from LDS address `p`.  Issued through inline assembly:
 // the builtin makes the compiler wait for every vector-memory load in flight
 // (vmcnt(0)) before it, in case an LDS-DMA load targets the same bytes, which
@@ -252,17 +191,86 @@ __device__ __forceinline__ i16x4_t ds_read_tr_after_stores(const char* p) {
   return v;
 }
 
-// MFMA B fragment of 32 columns (n0 .. n0+31, inside one 128-wide half) at
-// sub-step kk from an N-contiguous [64][128] half: lane l needs k = 16*kk +
-// 8*(l/32) .. +7 of column n0 + l%32.  ds_read_b64_tr_b16 reads, in each
-// 16-lane group, 4 k-rows x 16 columns (lane s: k-row s/4, columns 4*(s%4) ..
-// +3) and hands lane i the 4 k-values of column i; two such reads give 8.
-// This returns the lane's byte offset of the first read at kk = 0; the
-// second is 4 k-rows (1024 bytes) further, and sub-step kk adds 4096 bytes
-// (the swizzle depends on k only through k % 4).
-__device__ __forceinline__ uint32_t mc_lane_off(int n0, int lane) {
+// ---------------------------------------------------------------------------
+// Pieces of the 16 x 16 x 32 kernel (gemm_x16_kernel)
+// ---------------------------------------------------------------------------
+
+// N-contiguous slot of the 16 x 16 x 32 kernel: 64 k-rows of 128 n, 256-byte rows.
+// The 16-byte chunk holding n .. n+7 of k-row k sits at (n / 8) ^ (4 (k % 4) + 2
+// ((k / 8) % 2)).  A transposing fragment read takes, per 16-lane group, 4
+// consecutive k-rows x 32 bytes, and the LDS serves two groups per cycle whose
+// k-rows lie 8 apart: the first term puts a group's 4 rows on distinct banks
+// (unswizzled, rows 256 bytes apart hit the same ones), the second moves the
+// other group's to the remaining banks.
+__device__ __forceinline__ int mc16_x(int k) { return 4 * (k & 3) + 2 * ((k >> 3) & 1); }
+__device__ __forceinline__ int mc16_off(int k, int n) { return k * 256 + (((n >> 3) ^ mc16_x(k)) << 4) + (n & 7) * 2; }
+
+// K-contiguous [128 rows][64 k] slot of the 16 x 16 x 32 kernel: the 16-byte chunk c
+// of row r sits at position c ^ ((r / 2) % 8).  The XOR depends on r % 16 only, so
+// the 16-row fragments of a slot differ by a constant 2048 bytes (one base register
+// per lane serves all of them), and the 16 rows of a fragment read at one chunk
+// land on distinct 16-byte bank groups (even rows on 8 positions in one half of
+// the banks, odd rows on 8 in the other).
+__device__ __forceinline__ int swz16(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int tile16_off(int r, int c) { return r * 128 + ((c ^ swz16(r)) << 4); }
+
+// LDS-DMA loads of one 128-row K-contiguous quarter of a K step: 4 instructions per
+// wave of 1 KiB, instruction i of wave w filling rows 8 (4i + w) .. +7 of the slot;
+// lane q writes position q % 8 of row q / 8 and loads the chunk the swizzle places
+// there, which depends on the lane and w % 2 only.  Each lane's byte offset from
+// the quarter's (first row, first k of the step) is computed once per tile, with
+// lanes whose row is outside the operand set to OOB, so the only per-step masking
+// left is that of a K tail.
+struct QuarterKC {
+  uint32_t voff[4];  // instruction i
+  int kc;            // first k of the lane's chunk inside the K step
+
+  __device__ __forceinline__ void init(int64_t ld, int rows_left, int w, int lane) {
+    kc = 8 * ((lane & 7) ^ swz16(8 * w + (lane >> 3)));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 8 * (4 * i + w) + (lane >> 3);
+      voff[i] = r < rows_left ? (uint32_t)(((int64_t)r * ld + kc) * 2) : OOB;
+    }
+  }
+  // rs: descriptor based at the quarter's (first row, first k of the step); k_left:
+  // elements of K from the step's first k (64 or more: no tail).
+  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, char* slot, int k_left, int w, int i) const {
+    const uint32_t off = kc < k_left ? voff[i] : OOB;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(slot + (4 * i + w) * 1024), 16, off, 0, 0, 0);
+  }
+};
+
+// The same for an N-contiguous quarter (64 k-rows x 128 n, mc16_off layout):
+// instruction i of wave w fills k-rows 4 (4i + w) .. +3; lane q writes position
+// q % 16 of k-row q / 16 and loads the chunk placed there, which depends on the
+// lane and on w / 2 only.
+struct QuarterMC {
+  uint32_t voff[4];
+  int lane_k;  // k-row of the lane's chunk in instruction 0
+
+  __device__ __forceinline__ void init(int64_t ld, int n_left, int w, int lane) {
+    lane_k = 4 * w + (lane >> 4);
+    const int n = 8 * ((lane & 15) ^ mc16_x(lane_k));
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      voff[i] = n < n_left ? (uint32_t)(((int64_t)(lane_k + 16 * i) * ld + n) * 2) : OOB;
+  }
+  // rs: descriptor based at the quarter's (first k of the step, first n).
+  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, char* slot, int k_left, int w, int i) const {
+    const uint32_t off = lane_k + 16 * i < k_left ? voff[i] : OOB;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(slot + (4 * i + w) * 1024), 16, off, 0, 0, 0);
+  }
+};
+
+// Byte offset of lane `lane`'s first transposing read of the 16 x 16 x 32 B
+// fragment at columns n0 .. n0+15 of an N-contiguous half, sub-step 0: in 16-lane
+// group g, source lane s reads k-row 8g + s / 4, columns n0 + 4 (s % 4) .. +3, and
+// ds_read_b64_tr_b16 hands lane i of the group the 4 k-values of column n0 + i.
+// The second read (k-rows + 4) is 1024 bytes further, sub-step 1 (k + 32) 8192.
+__device__ __forceinline__ uint32_t mc16_lane_off(int n0, int lane) {
   const int g = lane >> 4, sl = lane & 15;
-  return mc_off(8 * (g >> 1) + (sl >> 2), n0 + 16 * (g & 1) + 4 * (sl & 3));
+  return mc16_off(8 * g + (sl >> 2), n0 + 4 * (sl & 3));
 }
 
 // Logical tile of workgroup `bid`: XCD-aware renumbering, then grouped order.
@@ -300,11 +308,13 @@ constexpr int ROW_B = 256;  // staged row stride in bytes (64 float32)
 // positions, two lanes per bank pair (the same as the row-contiguous reads).
 __device__ __forceinline__ int gt_swz(int r) { return (r + 4 * (r >> 3)) & 7; }
 
-template <int EPI, int FM, int FN>
-__device__ __forceinline__ void store_tile(const f32x16_t (&acc)[FM][FN], const GemmArgs& args, char* stage,
-                                           int row_w, int col_w, int split, int lane) {
-  static_assert(FN == 2 && FM % 2 == 0, "staging layout: 64 columns, 64-row halves");
-  constexpr int NH = FM / 2;
+// The epilogue proper, independent of the MFMA accumulator layout: for each of
+// NH 64-row halves of the wave's (64 NH) x 64 region, stage_half(h) writes the
+// half's float32 values into `stage` (row r in 0..63 at r * ROW_B, 16-byte chunk c
+// in 0..15 at position c ^ (r & 15)), and the half is finished from there.
+template <int EPI, int NH, class StageHalf>
+__device__ __forceinline__ void store_staged(StageHalf&& stage_half, const GemmArgs& args, char* stage, int row_w,
+                                             int col_w, int split, int lane) {
   // Each phase below issues all of its memory operations before it waits for
   // any: the dGeLU pre-activations of a 64-row half are loaded together (one
   // memory latency instead of one per vector; the next half's are in flight
@@ -346,18 +356,7 @@ __device__ __forceinline__ void store_tile(const f32x16_t (&acc)[FM][FN], const 
 #pragma unroll
   for (int h = 0; h < NH; ++h) {
     if (EPI == EPI_F32_ACC) load_old(h);
-#pragma unroll
-    for (int ii = 0; ii < 2; ++ii)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int r = 32 * ii + (lane & 31);
-          const int c = 8 * j + 2 * g + (lane >> 5);  // 16-byte chunk (4 columns) of the row
-          const f32x4_t x = {acc[2 * h + ii][j][4 * g], acc[2 * h + ii][j][4 * g + 1], acc[2 * h + ii][j][4 * g + 2],
-                             acc[2 * h + ii][j][4 * g + 3]};
-          *reinterpret_cast<f32x4_t*>(stage + r * ROW_B + ((c ^ (r & 15)) << 4)) = x;
-        }
+    stage_half(h);
     if (EPI == EPI_DGELU && h + 1 < NH) load_pre(h + 1);
     if (EPI == EPI_F32 || EPI == EPI_F32_ACC) {
       float* out = reinterpret_cast<float*>(args.out) + (int64_t)split * args.split_stride;
@@ -453,6 +452,30 @@ __device__ __forceinline__ void store_tile(const f32x16_t (&acc)[FM][FN], const 
       }
     }
   }
+}
+
+// Epilogue of a (32 FM) x 64 region held as 32 x 32 MFMA accumulators: register
+// r of fragment (i, j) holds C[32i + lane%32][32j + 8(r/4) + 4(lane/32) + r%4].
+template <int EPI, int FM, int FN>
+__device__ __forceinline__ void store_tile(const f32x16_t (&acc)[FM][FN], const GemmArgs& args, char* stage,
+                                           int row_w, int col_w, int split, int lane) {
+  static_assert(FN == 2 && FM % 2 == 0, "staging layout: 64 columns, 64-row halves");
+  store_staged<EPI, FM / 2>(
+      [&](int h) {
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const int r = 32 * ii + (lane & 31);
+              const int c = 8 * j + 2 * g + (lane >> 5);  // 16-byte chunk (4 columns) of the row
+              const f32x4_t x = {acc[2 * h + ii][j][4 * g], acc[2 * h + ii][j][4 * g + 1],
+                                 acc[2 * h + ii][j][4 * g + 2], acc[2 * h + ii][j][4 * g + 3]};
+              *reinterpret_cast<f32x4_t*>(stage + r * ROW_B + ((c ^ (r & 15)) << 4)) = x;
+            }
+      },
+      args, stage, row_w, col_w, split, lane);
 }
 
 }  // namespace
@@ -606,73 +629,32 @@ gemm_kernel(GemmArgs args) {
 }
 
 
-// Orders of the four-wave kernel's fragment reads and MFMAs (see there).
-__device__ constexpr int w4_read(int r) {
-  constexpr int order[8] = {0, 4, 5, 1, 6, 2, 7, 3};  // A0 B0 B1 A1 B2 A2 B3 A3
-  return order[r];
-}
-__device__ constexpr int w4_mi(int m) {
-  constexpr int order[16] = {0, 0, 1, 1, 0, 1, 2, 2, 2, 0, 1, 2, 3, 3, 3, 3};
-  return order[m];
-}
-__device__ constexpr int w4_mj(int m) {
-  constexpr int order[16] = {0, 1, 0, 1, 2, 2, 0, 1, 2, 3, 3, 3, 0, 1, 2, 3};
-  return order[m];
-}
-// The same for a 128 x 64 wave tile (256 x 128 workgroup tile): reads A0 B0 B1
-// A1 A2 A3, MFMAs row by row.
-__device__ constexpr int w4n_read(int r) {
-  constexpr int order[6] = {0, 4, 5, 1, 2, 3};
-  return order[r];
-}
-
-// 256 x 256 tile, A K-contiguous and B either, four waves (one per SIMD) that
-// each compute a 128 x 128 quadrant: wave w owns rows 128 (w / 2) and columns
-// 128 (w % 2) of the tile, its 256 accumulator registers in the AGPRs.  Against
-// eight waves of 128 x 64, a K step reads a third less from LDS (each wave
-// reads 128 rows of A and 128 of B) and needs one barrier instead of four.
-//
-// LDS is a ring of ten 16 KiB slots.  Quarter q of K step s (A rows 0-127,
-// A rows 128-255, B's first 128 columns, B's last 128) lives in slot
-// (4 s + q) mod 10, so steps s and s+1 and half of s+2 fit at once.  Every wave
-// loads a quarter of every quarter-slot (4 LDS-DMA instructions of 1 KiB).
-//
-// A K step is four sub-steps of 16 k.  In each, a wave issues the LDS reads of
-// the next sub-step's operand fragments and one quarter-slot's loads between
-// the current sub-step's 16 MFMAs (sched_group_barrier keeps the MFMA pipe fed
-// while the other instructions issue; with one wave per SIMD nothing else
-// would).  In K step k:
-//   sub-step 0: quarter 3 of step k+1 (into the slot of step k-1's quarter 1)
-//   sub-step 1: quarter 0 of step k+2 (step k-1's quarter 2)
-//   sub-step 2: quarter 1 of step k+2 (step k-1's quarter 3)
-//   then: wait until step k+1 has landed (vmcnt: only the two batches just
-//         issued may be in flight) and until sub-step 3's fragments are in
-//         registers, and barrier: every wave is done with step k's slots and
-//         step k+1 is visible to all
-//   sub-step 3: quarter 2 of step k+2 (step k's quarter 0), and the LDS reads
-//         of step k+1's first sub-step.
-// The loads thus run at an even 16 KiB per sub-step per workgroup; each batch
-// has at least two sub-steps before it is waited for.
-//
-// BN = 128 (256 x 128 tiles) keeps the ring and the schedule: a K step has no
-// fourth quarter (B's 128 columns are quarter 2, read by both column waves,
-// each a 128 x 64 sub-tile), so its loads are simply not issued and every
-// vmcnt wait above still counts the loads that follow the ones it needs.
+// 256 x BN tile (BN = 256 or 128) on v_mfma_f32_16x16x32_bf16: the four-wave
+// kernel's ring of ten 16 KiB slots, LDS layouts and loads, with 16 x 16
+// accumulator blocks.  Wave (wm, wn) computes a 128 x (BN / 2) sub-tile as 8 x FJ
+// blocks (FJ = 8 or 4, 256 or 128 accumulator registers).  A K step (64) is two
+// sub-steps of 32 k; in each a wave issues 8 FJ MFMAs of 16 cycles and, between
+// them, the LDS reads of the next sub-step's fragments and one batch of loads:
+//   sub-step 0 of step k: quarters 0 and 1 of step k+2 (into step k-1's slots 2, 3)
+//   then: wait until the next sub-step's fragments are in registers and step k+1
+//         has landed (vmcnt: only the batch just issued may be in flight); barrier
+//   sub-step 1 of step k: quarters 2 and 3 of step k+2 (into step k's slots 0, 1,
+//         which no wave reads any more), and the reads of step k+1's sub-step 0.
+// The next sub-step's B fragments go to the other half of a double buffer; an A
+// fragment is reloaded as soon as its row of MFMAs has been issued (MFMAs run
+// row by row), so A needs no second buffer.
 template <int LB, int EPI, int BN>
 __global__ void __launch_bounds__(256)
-gemm_w4_kernel(GemmArgs args) {
+gemm_x16_kernel(GemmArgs args) {
 #if defined(__HIP_DEVICE_COMPILE__)
   static_assert(BN == 256 || BN == 128, "tile widths");
   constexpr int BK = TILE_BK;
   constexpr int SLOT = 128 * BK * 2;
   constexpr int NSLOT = 10;
-  constexpr int FM = 4, FN = BN / 64;  // 32 x 32 fragments per wave: 128 x BN/2
-  constexpr int NQ = BN == 256 ? 4 : 3;  // quarters loaded per K step
-  // A window's 16 loads, four per sub-step: even issue measured best (eight in
-  // one sub-step stall the wave on the address unit).
-  constexpr int LC3 = 4, LC0 = 4, LC1 = 4;
+  constexpr int FI = 8, FJ = BN / 32;     // 16 x 16 blocks per wave: 8 x FJ
+  constexpr int NQ = BN == 256 ? 4 : 3;   // quarters loaded per K step
+  constexpr int NM = FI * FJ;             // MFMAs per sub-step
   static_assert(BK == 64 && NSLOT * SLOT == 160 * 1024, "ten 16 KiB slots fill the LDS");
-  static_assert(4 * 64 * ROW_B <= NSLOT * SLOT, "epilogue staging fits");
   __shared__ __attribute__((aligned(1024))) char smem[NSLOT * SLOT];
 
   const int tid = threadIdx.x;
@@ -687,15 +669,16 @@ gemm_w4_kernel(GemmArgs args) {
   const int k_end = min(args.K, k_begin + args.k_split);
   const int nk = (k_end - k_begin + BK - 1) / BK;
 
-  HalfDma dma_a, dma_b;
-  HalfDmaMC dma_bm;
-  dma_a.init(args.lda, wave, lane);
-  if (LB == KC) dma_b.init(args.ldb, wave, lane);
-  else dma_bm.init(args.ldb, wave, lane);
+  QuarterKC qa[2], qb[2];
+  QuarterMC qm[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) qa[q].init(args.lda, args.M - m0 - 128 * q, wave, lane);
+#pragma unroll
+  for (int q = 0; q < NQ - 2; ++q) {
+    if (LB == KC) qb[q].init(args.ldb, args.N - n0 - 128 * q, wave, lane);
+    else qm[q].init(args.ldb, args.N - n0 - 128 * q, wave, lane);
+  }
 
-  // Slot of quarter q of a K step with step % 5 == r (4 * 5 = 20 slots is a
-  // whole number of turns of the ring).  The main loop is unrolled five times so
-  // that r, and every LDS address, is a compile-time constant there.
   auto slot = [&](int r, int q) -> char* { return smem + ((4 * r + q) % NSLOT) * SLOT; };
   // Instruction i of this wave's share of quarter q of K step `step` (r = step % 5).
   auto load = [&](int step, int r, int q, int i) {
@@ -703,189 +686,138 @@ gemm_w4_kernel(GemmArgs args) {
     const int k = k_begin + step * BK;
     char* dst = slot(r, q);
     if (q < 2) {
-      dma_a.issue_one(args.a + (int64_t)(m0 + 128 * q) * args.lda + k, args.lda, dst, args.M - m0 - 128 * q,
-                      k_end - k, wave, lane, i);
+      qa[q].issue(make_rsrc(args.a + (int64_t)(m0 + 128 * q) * args.lda + k), dst, k_end - k, wave, i);
     } else if (LB == KC) {
-      dma_b.issue_one(args.b + (int64_t)(n0 + 128 * (q - 2)) * args.ldb + k, args.ldb, dst,
-                      args.N - n0 - 128 * (q - 2), k_end - k, wave, lane, i);
+      qb[q - 2].issue(make_rsrc(args.b + (int64_t)(n0 + 128 * (q - 2)) * args.ldb + k), dst, k_end - k, wave, i);
     } else {
-      dma_bm.issue_one(args.b + (int64_t)k * args.ldb + n0 + 128 * (q - 2), args.ldb, dst,
-                       args.N - n0 - 128 * (q - 2), k_end - k, wave, lane, i);
+      qm[q - 2].issue(make_rsrc(args.b + (int64_t)k * args.ldb + n0 + 128 * (q - 2)), dst, k_end - k, wave, i);
     }
   };
 
-  // The 16 loads of window k, issued between barrier k-1 and barrier k: quarters
-  // 2 and 3 of step k+1 (loads 0-7), then quarters 0 and 1 of step k+2 (8-15),
-  // into the slots of step k-1.  r1, r2: (k+1) % 5, (k+2) % 5.  The first LC3
-  // are issued in sub-step 3 of step k-1, LC0 and LC1 in sub-steps 0 and 1 of
-  // step k, the rest in sub-step 2.
-  auto window_load = [&](int k, int n, int r1, int r2) {
-    const int b = n >> 2, i = n & 3;
-    if (b < 2) load(k + 1, r1, 2 + b, i);
-    else load(k + 2, r2, b - 2, i);
+  f32x4_t acc[FI][FJ];
+#pragma unroll
+  for (int i = 0; i < FI; ++i)
+#pragma unroll
+    for (int j = 0; j < FJ; ++j) acc[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  bf16x8_t fa[FI], fb[2][FJ];
+  // K-contiguous fragment f (rows 16f .. +15 of a 128-row quarter) in sub-step kk:
+  // lane l reads row 16f + l % 16, 16-byte chunk 4kk + l / 16, at lane_kc[kk] + 2048 f.
+  uint32_t lane_kc[2], lane_mc[FJ];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) lane_kc[kk] = tile16_off(lane & 15, 4 * kk + (lane >> 4));
+  const int wcol = BN == 256 ? 0 : 64 * wn;  // the wave's first column inside its B quarter
+#pragma unroll
+  for (int j = 0; j < FJ; ++j) lane_mc[j] = mc16_lane_off(wcol + 16 * j, lane);
+  auto read_a = [&](int r, int kk, int f) {
+    fa[f] = *reinterpret_cast<const bf16x8_t*>(slot(r, wm) + lane_kc[kk] + 2048 * f);
   };
-  static_assert(LC3 <= 8 && LC0 <= 8 && LC1 <= 8 && 16 - LC3 - LC0 - LC1 <= 8 && LC3 + LC0 + LC1 <= 16,
-                "at most eight loads per sub-step; window k+1's first LC3 exist whenever step k+2 does");
-
-  f32x16_t acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-  bf16x8_t fa[2][FM], fb[2][FN];
-  // The fragments are read, and the MFMAs run, in an order in which the n-th
-  // read is first needed as late as possible: read r fetches A fragment
-  // w4_read(r) (B fragment w4_read(r) - 4 from 4 on); MFMA m updates block
-  // (w4_mi(m), w4_mj(m)).  The first MFMA needs two reads, the last read is
-  // first used by the 13th.
-  // The lane's byte offsets of its fragment reads inside a slot, so that a
-  // read is a register base plus an immediate.  K-contiguous (read_frag): the
-  // fragment of row block f in sub-step kk is at lane_kc[kk][f % 2] + 8192 (f / 2),
-  // because the swizzle of row r + 64 equals that of row r.  N-contiguous
-  // (mc_lane_off): fragment f's low half is at lane_mc[f] + 4096 kk and its
-  // high half 1024 further, because the swizzle depends on k only through k % 4.
-  uint32_t lane_kc[4][2], lane_mc[FN];
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-    for (int par = 0; par < 2; ++par) lane_kc[kk][par] = tile_off(32 * par + (lane & 31), 2 * kk + (lane >> 5));
-  // BN = 128: the wave's columns are 64 wn .. +63 of the one B quarter.
-  const int wcol = BN == 256 ? 0 : 64 * wn;
-#pragma unroll
-  for (int f = 0; f < FN; ++f) lane_mc[f] = mc_lane_off(wcol + 32 * f, lane);
-  auto read_sub = [&](int buf, int r, int kk) {
-    const char* ta = slot(r, wm);
+  auto read_b = [&](int buf, int r, int kk, int j) {
     const char* tb = slot(r, BN == 256 ? 2 + wn : 2);
-#pragma unroll
-    for (int x = 0; x < FM + FN; ++x) {
-      const int f = BN == 256 ? w4_read(x) : w4n_read(x);
-      if (f < FM) {
-        fa[buf][f] = *reinterpret_cast<const bf16x8_t*>(ta + lane_kc[kk][f & 1] + 8192 * (f >> 1));
-      } else if (LB == KC) {
-        const int rb = (BN == 256 ? 0 : 2 * wn) + (f - FM);  // 32-row block of the B quarter
-        fb[buf][f - FM] = *reinterpret_cast<const bf16x8_t*>(tb + lane_kc[kk][rb & 1] + 8192 * (rb >> 1));
-      } else {
-        const char* p = tb + lane_mc[f - FM] + 4096 * kk;
-        const i16x4_t lo = ds_read_tr(p), hi = ds_read_tr(p + 1024);
-        const i16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        fb[buf][f - FM] = __builtin_bit_cast(bf16x8_t, v);
-      }
+    if (LB == KC) {
+      const int f = (BN == 256 ? 0 : 4 * wn) + j;  // 16-row block of the B quarter
+      fb[buf][j] = *reinterpret_cast<const bf16x8_t*>(tb + lane_kc[kk] + 2048 * f);
+    } else {
+      const char* p = tb + lane_mc[j] + 8192 * kk;
+      const i16x4_t lo = ds_read_tr(p), hi = ds_read_tr(p + 1024);
+      const i16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      fb[buf][j] = __builtin_bit_cast(bf16x8_t, v);
     }
   };
-  auto mfma_sub = [&](int buf) {
-#pragma unroll
-    for (int m = 0; m < FM * FN; ++m) {
-      const int i = BN == 256 ? w4_mi(m) : m >> 1, j = BN == 256 ? w4_mj(m) : m & 1;
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf][j], fa[buf][i], acc[i][j], 0, 0, 0);
-    }
+  constexpr int NB = LB == KC ? FJ : 2 * FJ;  // LDS read instructions for the B fragments
+  // acc += A B for one 16 x 16 block, the B fragment as the first operand.  Inline
+  // assembly ties the accumulator to one AGPR quadruple for the whole K loop (the
+  // builtin's results were moved between registers every iteration at this
+  // register pressure).  The compiler still waits for the LDS reads that produce
+  // the operands; the accumulators are next read by the epilogue, after explicit
+  // wait states.
+  auto mfma16 = [](f32x4_t& c, const bf16x8_t& b, const bf16x8_t& a) {
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(b), "v"(a));
   };
-  // Scheduling of one sub-step: its 16 MFMAs, with the 8 LDS reads between the
-  // first eight and NL (at most 8) loads spread over the last eight (a load
-  // writes LDS, so the compiler keeps it behind the reads before it).
-  auto interleave = [&](auto nl) {
-    constexpr int NL = decltype(nl)::value;
-    constexpr int NM = FM * FN, NR = FM + FN, S = NM - NR;  // MFMAs, reads, MFMAs after the reads
-    static_assert(NL >= 0 && NL <= 8, "loads per sub-step");
-#pragma unroll
-    for (int m = 0; m < NM; ++m) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                            // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);                            // up to 3 VALU
-      if (m < NR) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                          // LDS read
-      } else {
-#pragma unroll
-        for (int u = (m - NR) * NL / S; u < (m - NR + 1) * NL / S; ++u)
-          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                        // global load
-      }
-    }
-  };
-  auto fence = [&]() { __builtin_amdgcn_sched_barrier(0); };
-  using L0 = std::integral_constant<int, 0>;
-  using L8 = std::integral_constant<int, 8>;
 
-  // s_waitcnt immediate for vmcnt(n), n < 64, leaving the other counters free.
+  // One sub-step: the MFMAs on fa and fb[cur], row by row; with `reads`, the next
+  // sub-step's fragments (ring position rn, sub-step kn): B into fb[1 - cur] during
+  // row 0, A fragment f right after row f's MFMAs (its old value has then fed its
+  // last MFMA).  Load n of the sub-step's NL goes after MFMA 1 (and FJ/2 + 1 for a
+  // second) of row n * FI / NL.  Every MFMA with the reads and loads placed after it
+  // is its own scheduling region, so the order is exactly this one.
+  auto sub_step = [&](int cur, bool reads, int rn, int kn, auto nl, auto&& issue_load) {
+    constexpr int NL = decltype(nl)::value;
+#pragma unroll
+    for (int i = 0; i < FI; ++i) {
+      int n_row = 0, n_first = 0;  // loads of this row and the first one's index
+#pragma unroll
+      for (int n = NL - 1; n >= 0; --n)
+        if (n * FI / NL == i) {
+          ++n_row;
+          n_first = n;
+        }
+#pragma unroll
+      for (int j = 0; j < FJ; ++j) {
+        mfma16(acc[i][j], fb[cur][j], fa[i]);
+        if (reads && i == 0) {
+#pragma unroll
+          for (int u = 0; u < NB / FJ; ++u) {
+            const int jb = j * (NB / FJ) + u;  // B read jb: fragment jb / (NB / FJ), half jb % (NB / FJ)
+            if (NB == FJ || u == NB / FJ - 1) read_b(1 - cur, rn, kn, jb / (NB / FJ));
+          }
+        }
+        if (j == 1 && n_row >= 1) issue_load(n_first);
+        if (j == FJ / 2 + 1 && n_row >= 2) issue_load(n_first + 1);
+        if (j == FJ - 1 && reads) read_a(rn, kn, i);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
   auto vm_wait = [&](auto n) {
     constexpr int N = decltype(n)::value;
     static_assert(N >= 0 && N < 64, "vmcnt");
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
   };
+  using L0 = std::integral_constant<int, 0>;
+  constexpr int HALF_LOADS = 8;                 // quarters 0 and 1: 4 instructions each
+  constexpr int TAIL_LOADS = 4 * (NQ - 2);      // quarters 2 (and 3)
 
   if (nk > 0) {
-    // Prologue: K step 0, quarters 0 and 1 of step 1 and the first LC3 loads of
-    // window 0 (slots 0-5 and part of 6); wait for step 0.
+    // Prologue: steps 0 and 1 (slots 0-7); wait for step 0.
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
       for (int i = 0; i < 4; ++i) load(0, 0, q, i);
     if (nk > 1) {
 #pragma unroll
-      for (int q = 0; q < 2; ++q)
+      for (int q = 0; q < 4; ++q)
 #pragma unroll
         for (int i = 0; i < 4; ++i) load(1, 1, q, i);
-#pragma unroll
-      for (int n = 0; n < LC3; ++n) window_load(0, n, 1, 2);
-      vm_wait(std::integral_constant<int, 8 + LC3>{});
+      vm_wait(std::integral_constant<int, HALF_LOADS + TAIL_LOADS>{});
     } else {
       vm_wait(L0{});
     }
     __builtin_amdgcn_s_barrier();
-    fence();
-    read_sub(0, 0, 0);
-
-    // One K step; LEFT = min(2, K steps after this one) is known at compile time
-    // (2: every load is issued; 1: the last but one step; 0: the last); r = k % 5.
-    auto k_step = [&](int k, auto left, int r) {
-      const int r1 = r == 4 ? 0 : r + 1, r2 = r >= 3 ? r - 3 : r + 2;
-      constexpr int LEFT = decltype(left)::value;
-      constexpr bool more2 = LEFT >= 2;  // step k+2 exists: load it
-      constexpr bool more1 = LEFT >= 1;  // step k+1 exists: wait for it, read it
-      // Loads [lo, hi) of window k that exist (those from 8 on load step k+2).
-      auto window_part = [&](auto lo, auto hi) {
-        constexpr int LO = decltype(lo)::value, HI = decltype(hi)::value;
-        constexpr int END = more2 ? HI : more1 ? (HI < 8 ? HI : 8) : LO;
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int n = LO; n < END; ++n) window_load(k, n, r1, r2);
-        interleave(std::integral_constant<int, (END > LO ? END - LO : 0)>{});
-      };
-      // sub-step 0
-      fence();
-      read_sub(1, r, 1);
-      mfma_sub(0);
-      window_part(std::integral_constant<int, LC3>{}, std::integral_constant<int, LC3 + LC0>{});
-      fence();
-      // sub-step 1
-      read_sub(0, r, 2);
-      mfma_sub(1);
-      window_part(std::integral_constant<int, LC3 + LC0>{}, std::integral_constant<int, LC3 + LC0 + LC1>{});
-      fence();
-      // sub-step 2
-      read_sub(1, r, 3);
-      mfma_sub(0);
-      window_part(std::integral_constant<int, LC3 + LC0 + LC1>{}, std::integral_constant<int, 16>{});
-      fence();
-      if constexpr (more1) {
-        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): sub-step 3's fragments are in registers
-        if constexpr (more2) vm_wait(L8{});  // step k+1 has landed; k+2's first half may be in flight
+    for (int j = 0; j < FJ; ++j) read_b(0, 0, 0, j);
+#pragma unroll
+    for (int f = 0; f < FI; ++f) read_a(0, 0, f);
+
+    // K step k with LEFT = min(2, steps after it) known at compile time; r = k % 5.
+    auto k_step = [&](int k, auto left, int r) {
+      constexpr int LEFT = decltype(left)::value;
+      const int r1 = r == 4 ? 0 : r + 1, r2 = r >= 3 ? r - 3 : r + 2;
+      // sub-step 0: reads sub-step 1 of this step; loads quarters 0, 1 of step k+2
+      sub_step(0, true, r, 1, std::integral_constant<int, LEFT >= 2 ? HALF_LOADS : 0>{},
+               [&](int n) { load(k + 2, r2, n >> 2, n & 3); });
+      if constexpr (LEFT >= 1) {
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): sub-step 1's fragments are in registers
+        if constexpr (LEFT >= 2) vm_wait(std::integral_constant<int, HALF_LOADS>{});  // step k+1 has landed
         else vm_wait(L0{});
         __builtin_amdgcn_s_barrier();
-        fence();
-        // sub-step 3: the first LC3 loads of window k+1, into step k's slots
-        read_sub(0, r1, 0);
-        const int r3 = r2 == 4 ? 0 : r2 + 1;
-        if constexpr (more2) {
-#pragma unroll
-          for (int n = 0; n < LC3; ++n) window_load(k + 1, n, r2, r3);
-        }
-        mfma_sub(1);
-        if constexpr (more2) interleave(std::integral_constant<int, LC3>{}); else interleave(L0{});
-        fence();
-      } else {
-        mfma_sub(1);
-        fence();
+        __builtin_amdgcn_sched_barrier(0);
       }
+      // sub-step 1: reads sub-step 0 of step k+1; loads quarters 2, 3 of step k+2
+      sub_step(1, LEFT >= 1, r1, 0, std::integral_constant<int, LEFT >= 2 ? TAIL_LOADS : 0>{},
+               [&](int n) { load(k + 2, r2, 2 + (n >> 2), n & 3); });
     };
     using Full = std::integral_constant<int, 2>;
     int k = 0;
@@ -898,19 +830,29 @@ gemm_w4_kernel(GemmArgs args) {
     k_step(nk - 1, std::integral_constant<int, 0>{}, (nk - 1) % 5);
     vm_wait(L0{});
   }
+  // The last MFMAs' results are read below; 32 wait states cover the longest
+  // write-to-read distance of a 16 x 16 x 32 MFMA (issued as inline assembly, so
+  // the compiler does not insert them).
+  asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
   __syncthreads();  // every wave is done with the operand slots
 
   // Epilogue, one 64-column half of the wave's sub-tile at a time, staged in the
-  // wave's own 16 KiB of LDS.
+  // wave's own 16 KiB of LDS.  Block (i, j) register e holds C[16i + lane%16][16j +
+  // 4 (lane/16) + e] of the wave's sub-tile.
 #pragma unroll
-  for (int h = 0; h < FN / 2; ++h) {
-    f32x16_t part[FM][2];
+  for (int hc = 0; hc < FJ / 4; ++hc) {
+    store_staged<EPI, 2>(
+        [&](int h) {
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+          for (int ii = 0; ii < 4; ++ii)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) part[i][j] = acc[i][2 * h + j];
-    store_tile<EPI>(part, args, smem + wave * (64 * ROW_B), m0 + 128 * wm, n0 + (BN / 2) * wn + 64 * h, split,
-                    lane);
+            for (int jj = 0; jj < 4; ++jj) {
+              const int r = 16 * ii + (lane & 15), c = 4 * jj + (lane >> 4);
+              *reinterpret_cast<f32x4_t*>(smem + wave * (64 * ROW_B) + r * ROW_B + ((c ^ (r & 15)) << 4)) =
+                  acc[4 * h + ii][4 * hc + jj];
+            }
+        },
+        args, smem + wave * (64 * ROW_B), m0 + 128 * wm, n0 + (BN / 2) * wn + 64 * hc, split, lane);
   }
 #else
   (void)args;
@@ -925,7 +867,7 @@ template <int BM, int BN, int WM_, int WN_, int LA, int LB, int EPI>
 hipError_t launch_one(const GemmArgs& a, int splits, hipStream_t s) {
   const int blocks = a.tiles_m * a.tiles_n * splits;
   if constexpr (BM == 256 && LA == KC)
-    return launch_kernel(kern::gemm_w4_kernel<LB, EPI, BN>, dim3(blocks), dim3(256), s, a);
+    return launch_kernel(kern::gemm_x16_kernel<LB, EPI, BN>, dim3(blocks), dim3(256), s, a);
   else
     return launch_kernel(kern::gemm_kernel<BM, BN, WM_, WN_, LA, LB, EPI>, dim3(blocks), dim3(64 * WM_ * WN_), s, a);
 }
