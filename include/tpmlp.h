@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define TPMLP_ABI_VERSION 8
+#define TPMLP_ABI_VERSION 9
 #define TPMLP_MAX_SHARDS 64
 
 typedef uint16_t tpmlp_bf16; /* raw bf16 bits */
@@ -199,6 +199,58 @@ tpmlp_status tpmlp_tp_bwd_full(const tpmlp_bf16* dZ, const tpmlp_bf16* X, const 
  * array of t device pointers; n must be a positive multiple of 4.  `out` may not
  * overlap any part. */
 tpmlp_status tpmlp_shard_sum(const float* const* parts, int t, float* out, int64_t n, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* The t-shard driver at the sequence-parallel boundary                       */
+/* ------------------------------------------------------------------------ */
+/* With sequence parallelism the tokens outside the MLP are split by rank: rank
+ * r holds the rows [r M/t, (r+1) M/t) of X.  Before the column-parallel product
+ * an all-gather gives every rank all M rows, and after the row-parallel product
+ * a reduce-scatter leaves rank r the sum over ranks of its own rows of Z; the
+ * backward runs the reverse (all-gather of dZ, reduce-scatter of dX).  An
+ * all-reduce is a reduce-scatter plus an all-gather, so this costs no extra
+ * communication (QLM page §2.1.3 顺序并行; "大模型训练" notes §3.2 序列并行, the
+ * all-reduce replaced by all-gather + reduce-scatter; sequence-parallel series
+ * §3.2, Megatron's split of the token-wise operations across ranks).
+ *
+ * These calls take and return the ranks' row slices.  On one GPU the gather is
+ * never materialised: each product whose rows are tokens runs once per rank row
+ * block, reading that rank's slice directly, and each rank's output slice
+ * receives the rank-order sum of the shards' rows in the products' epilogues
+ * (shard 0 writes, shards 1 .. t-1 add), which is the reduce-scatter's result.
+ * The weight-gradient products contract over all M tokens and read X^T and dZ^T,
+ * which are assembled from the slices by the transposes.
+ *
+ * M must split into t slices of S = M / t rows, S a positive multiple of 8, and
+ * H must be at most 2^22 when t > 1 (TPMLP_ERR_SHAPE). */
+
+/* Workspace bytes for tpmlp_sp_fwd and tpmlp_sp_bwd (either backward mode); 0 if
+ * the arguments are invalid. */
+size_t tpmlp_sp_workspace_bytes(int t, int64_t M, int64_t H, int64_t F_i);
+
+/* Z_sl[r] = rows [r S, (r+1) S) of sum_i GeLU(X A_sh[i]) B_sh[i], for each rank r.
+ * X_sl: host array of t device pointers, rank r's tokens X_r[S, H] (bf16).
+ * A_sh, B_sh: host arrays of t device pointers (shard i's A_i[H,F_i], B_i[F_i,H]).
+ * P_sh (nullable host array; entries nullable): shard i's pre-activation over all
+ * M tokens, [M, F_i] bf16 (row block r from rank r's tokens), for a backward that
+ * keeps it.
+ * Z_sl: host array of t device pointers, rank r's output rows [S, H] float32. */
+tpmlp_status tpmlp_sp_fwd(const tpmlp_bf16* const* X_sl, const tpmlp_bf16* const* A_sh,
+                          const tpmlp_bf16* const* B_sh, tpmlp_bf16* const* P_sh, float* const* Z_sl,
+                          int t, int64_t M, int64_t H, int64_t F_i,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/* Backward at the sequence-parallel boundary: dZ_sl[r] and X_sl[r] are rank r's
+ * rows [S, H] (bf16); dX_sl[r] receives rank r's rows [S, H] of sum_i dX_i
+ * (float32); dA_sh[i], dB_sh[i] are shard i's weight gradients over all M tokens
+ * (float32).  P_sh: NULL host array => every shard recomputes P_i; otherwise t
+ * device pointers written by tpmlp_sp_fwd (no NULL entries). */
+tpmlp_status tpmlp_sp_bwd(const tpmlp_bf16* const* dZ_sl, const tpmlp_bf16* const* X_sl,
+                          const tpmlp_bf16* const* A_sh, const tpmlp_bf16* const* B_sh,
+                          const tpmlp_bf16* const* P_sh,
+                          float* const* dA_sh, float* const* dB_sh, float* const* dX_sl,
+                          int t, int64_t M, int64_t H, int64_t F_i,
+                          void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Forward without allocation or workspace                                  */

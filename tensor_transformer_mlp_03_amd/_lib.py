@@ -58,6 +58,9 @@ _SIGS = {
     "tpmlp_tp_bwd_full": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _i64, _i64, _i64, _vp, _sz, _vp], _int),
     "tpmlp_shard_sum": ([_PP, _int, _vp, _i64, _vp], _int),
     "tpmlp_fwd_noalloc": ([_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp], _int),
+    "tpmlp_sp_workspace_bytes": ([_int, _i64, _i64, _i64], _sz),
+    "tpmlp_sp_fwd": ([_PP, _PP, _PP, _PP, _PP, _int, _i64, _i64, _i64, _vp, _sz, _vp], _int),
+    "tpmlp_sp_bwd": ([_PP, _PP, _PP, _PP, _PP, _PP, _PP, _PP, _int, _i64, _i64, _i64, _vp, _sz, _vp], _int),
     "tpmlp_timing_begin": ([_int], _int),
     "tpmlp_timing_begin_kinds": ([_int, ctypes.c_uint], _int),
     "tpmlp_timing_end": ([ctypes.POINTER(_int), ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_int)], _int),
@@ -311,6 +314,47 @@ def tpmlp_tp_bwd_full(dZ, X, A, B, P, dA, dB, dX, t, ws, stream=None):
     st = lib().tpmlp_tp_bwd_full(_ptr(dZ), _ptr(X), _ptr(A), _ptr(B), _ptr(P), _ptr(dA), _ptr(dB), _ptr(dX), t,
                                  M, H, F, _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     _check(st, "tpmlp_tp_bwd_full")
+
+
+def tpmlp_sp_workspace_bytes(t: int, M: int, H: int, F_i: int) -> int:
+    return lib().tpmlp_sp_workspace_bytes(t, M, H, F_i)
+
+
+def tpmlp_sp_fwd(X_sl, A_sh, B_sh, P_sh, Z_sl, ws, stream=None):
+    """Forward at the sequence-parallel boundary: X_sl[r] and Z_sl[r] are rank r's
+    token rows [M/t, H] (bf16 in, float32 out); P_sh: None or t tensors [M, F_i]."""
+    t = len(A_sh)
+    S, H = X_sl[0].shape
+    F = A_sh[0].shape[1]
+    _shards(X_sl, t, (S, H), "X_sl", _bf16)
+    _shards(Z_sl, t, (S, H), "Z_sl", _f32)
+    _shards(A_sh, t, (H, F), "A_sh", _bf16)
+    _shards(B_sh, t, (F, H), "B_sh", _bf16)
+    _shards(P_sh, t, (S * t, F), "P_sh", _bf16, nullable=True)
+    st = lib().tpmlp_sp_fwd(_ptr_array(X_sl, t), _ptr_array(A_sh, t), _ptr_array(B_sh, t), _ptr_array(P_sh, t),
+                            _ptr_array(Z_sl, t), t, S * t, H, F, _ptr(ws), ws.numel() * ws.element_size(),
+                            _stream(stream))
+    _check(st, "tpmlp_sp_fwd")
+
+
+def tpmlp_sp_bwd(dZ_sl, X_sl, A_sh, B_sh, P_sh, dA_sh, dB_sh, dX_sl, ws, stream=None):
+    """Backward at the sequence-parallel boundary; P_sh None recomputes the
+    pre-activations."""
+    t = len(A_sh)
+    S, H = X_sl[0].shape
+    F = A_sh[0].shape[1]
+    _shards(dZ_sl, t, (S, H), "dZ_sl", _bf16)
+    _shards(X_sl, t, (S, H), "X_sl", _bf16)
+    _shards(dX_sl, t, (S, H), "dX_sl", _f32)
+    _shards(A_sh, t, (H, F), "A_sh", _bf16)
+    _shards(B_sh, t, (F, H), "B_sh", _bf16)
+    _shards(P_sh, t, (S * t, F), "P_sh", _bf16)
+    _shards(dA_sh, t, (H, F), "dA_sh", _f32)
+    _shards(dB_sh, t, (F, H), "dB_sh", _f32)
+    st = lib().tpmlp_sp_bwd(_ptr_array(dZ_sl, t), _ptr_array(X_sl, t), _ptr_array(A_sh, t), _ptr_array(B_sh, t),
+                            _ptr_array(P_sh, t), _ptr_array(dA_sh, t), _ptr_array(dB_sh, t), _ptr_array(dX_sl, t),
+                            t, S * t, H, F, _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "tpmlp_sp_bwd")
 
 
 def tpmlp_saved_activation_bytes(M: int, H: int, F: int, recompute: bool) -> int:

@@ -97,9 +97,11 @@ hipError_t launch_splitk_epilogue(Epi epi, const float* part, int splits, int64_
                                   hipStream_t stream);
 
 // out[c][r] = in[r][c] for a bf16 matrix in[R][C] with rows of ld_in >= C
-// elements (R, C, ld_in multiples of 8).
+// elements, into out with rows of ld_out >= R elements (0: R), so that the
+// transpose can be a column block of a wider matrix (R, C, ld_in, ld_out
+// multiples of 8).
 hipError_t launch_transpose(const uint16_t* in, int64_t R, int64_t C, int64_t ld_in, uint16_t* out,
-                            hipStream_t stream);
+                            hipStream_t stream, int64_t ld_out = 0);
 
 // Fused forward for small hidden sizes (ffn.hip): workgroup (row block r,
 // chunk c) computes GeLU(X[r] A_i[:, c]) B_i[c, :] with G kept in LDS and

@@ -189,8 +189,8 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 struct TransposeArgs {
   const uint16_t* in;
   uint16_t* out;
-  int64_t R, C;  // in is [R][C] (rows of ld_in elements), out is [C][R]
-  int64_t ld_in;
+  int64_t R, C;  // in is [R][C] (rows of ld_in elements), out is [C][R] (rows of ld_out)
+  int64_t ld_in, ld_out;
   int row_groups;  // groups of four 64-row tiles
 };
 
@@ -223,7 +223,7 @@ __global__ void __launch_bounds__(256) transpose_kernel(TransposeArgs a) {
     u32x4_t o;
 #pragma unroll
     for (int e = 0; e < 4; ++e) o[e] = __builtin_amdgcn_perm(v[2 * e + 1][j >> 1], v[2 * e][j >> 1], sel);
-    *reinterpret_cast<u32x4_t*>(a.out + (c0 + j) * a.R + r0) = o;
+    *reinterpret_cast<u32x4_t*>(a.out + (c0 + j) * a.ld_out + r0) = o;
   }
 #else
   (void)a;
@@ -264,14 +264,16 @@ hipError_t launch_splitk_epilogue(Epi epi, const float* part, int splits, int64_
 }
 
 hipError_t launch_transpose(const uint16_t* in, int64_t R, int64_t C, int64_t ld_in, uint16_t* out,
-                            hipStream_t stream) {
-  if (ld_in < C || (ld_in & 7)) return hipErrorInvalidValue;
+                            hipStream_t stream, int64_t ld_out) {
+  if (ld_out == 0) ld_out = R;
+  if (ld_in < C || (ld_in & 7) || ld_out < R || (ld_out & 7)) return hipErrorInvalidValue;
   TransposeArgs a;
   a.in = in;
   a.out = out;
   a.R = R;
   a.C = C;
   a.ld_in = ld_in;
+  a.ld_out = ld_out;
   a.row_groups = (int)((R + 255) / 256);
   const int64_t blocks = (int64_t)a.row_groups * ((C + 63) / 64);
   return launch_kernel(transpose_kernel, dim3((unsigned)blocks), dim3(256), stream, a);

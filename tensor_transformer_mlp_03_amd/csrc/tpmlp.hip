@@ -388,15 +388,17 @@ GemmArgs gemm_args(const void* a, int64_t lda, const void* b, int64_t ldb, int64
 // float32 and the reduction applies the epilogue.
 hipError_t run_gemm(int kind, Layout la, Layout lb, Epi epi, const void* a, int64_t lda, const void* b,
                     int64_t ldb, int64_t M, int64_t N, int64_t K, const GemmPlan& p, void* out, uint16_t* out2,
-                    const uint16_t* aux, float* part, hipStream_t s, int64_t ldo = 0) {
+                    const uint16_t* aux, float* part, hipStream_t s, int64_t ldo = 0, int64_t ldt = 0) {
   // ldo: row stride of out (and of out2 and aux for the GeLU and dGeLU
-  // epilogues); 0 means N.
+  // epilogues); 0 means N.  ldt: row stride of the dGeLU epilogue's transposed
+  // out2; 0 means M (the product's rows can be a row block of a taller one).
   if (ldo == 0) ldo = N;
+  if (ldt == 0) ldt = M;
   if (p.splits == 1) {
     GemmArgs g = gemm_args(a, lda, b, ldb, M, N, K, p, out, ldo);
     g.out2 = out2;
     g.aux = aux;
-    g.ldt = M;
+    g.ldt = ldt;
     return timed(kind, s, [&] { return launch_gemm(p.tile, la, lb, epi, g, 1, s); });
   }
   if (p.n_full > 0) {
@@ -407,7 +409,7 @@ hipError_t run_gemm(int kind, Layout la, Layout lb, Epi epi, const void* a, int6
     GemmArgs gf = gemm_args(a, lda, b, ldb, M, nf, K, pf, out, ldo);
     gf.out2 = out2;
     gf.aux = aux;
-    gf.ldt = M;
+    gf.ldt = ldt;
     const void* b_tail = static_cast<const uint16_t*>(b) + (lb == KC ? nf * ldb : nf);
     GemmArgs gt = gemm_args(a, lda, b_tail, ldb, M, nt, K, p, part, nt);
     hipError_t e = timed(
@@ -420,17 +422,17 @@ hipError_t run_gemm(int kind, Layout la, Layout lb, Epi epi, const void* a, int6
     if (e != hipSuccess) return e;
     const size_t esz = (epi == EPI_F32 || epi == EPI_F32_ACC) ? 4 : 2;
     void* out_tail = static_cast<char*>(out) + nf * esz;
-    uint16_t* out2_tail = out2 ? out2 + (epi == EPI_DGELU ? nf * M : nf) : nullptr;
+    uint16_t* out2_tail = out2 ? out2 + (epi == EPI_DGELU ? nf * ldt : nf) : nullptr;
     const uint16_t* aux_tail = aux ? aux + nf : nullptr;
     return timed(TPMLP_K_SPLITK_REDUCE, s, [&] {
-      return launch_splitk_epilogue(epi, part, p.splits, M, nt, out_tail, out2_tail, aux_tail, ldo, M, s);
+      return launch_splitk_epilogue(epi, part, p.splits, M, nt, out_tail, out2_tail, aux_tail, ldo, ldt, s);
     });
   }
   GemmArgs g = gemm_args(a, lda, b, ldb, M, N, K, p, part, N);
   hipError_t e = timed(kind, s, [&] { return launch_gemm(p.tile, la, lb, EPI_F32, g, p.splits, s); });
   if (e != hipSuccess) return e;
   return timed(TPMLP_K_SPLITK_REDUCE, s,
-               [&] { return launch_splitk_epilogue(epi, part, p.splits, M, N, out, out2, aux, ldo, M, s); });
+               [&] { return launch_splitk_epilogue(epi, part, p.splits, M, N, out, out2, aux, ldo, ldt, s); });
 }
 
 char* ws_at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
@@ -439,9 +441,11 @@ char* ws_at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
 // A (A_i) has rows of lda >= F elements: a column block of a wider weight.
 // acc: Z already holds the sum of earlier shards' partials and this shard's is
 // added to it (Z = Z + Z_i, in float32) instead of overwriting it.
+// weights_ready: A_i^T and B_i^T are already in the workspace (an earlier call
+// for the same shard and plan made them).
 hipError_t enqueue_fwd(const tpmlp_bf16* X, const tpmlp_bf16* A, int64_t lda, const tpmlp_bf16* B, float* Z,
                        tpmlp_bf16* P_save, int64_t M, int64_t H, int64_t F, void* ws, hipStream_t s,
-                       bool acc = false) {
+                       bool acc = false, bool weights_ready = false) {
   const FwdPlan p = plan_fwd(M, H, F);
   const Epi out_epi = acc ? EPI_F32_ACC : EPI_F32;
   uint16_t* G = reinterpret_cast<uint16_t*>(ws_at(ws, p.off_G));
@@ -472,10 +476,12 @@ hipError_t enqueue_fwd(const tpmlp_bf16* X, const tpmlp_bf16* A, int64_t lda, co
   if (p.wt) {
     uint16_t* At = reinterpret_cast<uint16_t*>(ws_at(ws, p.off_At));
     uint16_t* Bt = reinterpret_cast<uint16_t*>(ws_at(ws, p.off_Bt));
-    e = timed(TPMLP_K_TRANSPOSE, s, [&] { return launch_transpose(A, H, F, lda, At, s); });
-    if (e != hipSuccess) return e;
-    e = timed(TPMLP_K_TRANSPOSE, s, [&] { return launch_transpose(B, F, H, H, Bt, s); });
-    if (e != hipSuccess) return e;
+    if (!weights_ready) {
+      e = timed(TPMLP_K_TRANSPOSE, s, [&] { return launch_transpose(A, H, F, lda, At, s); });
+      if (e != hipSuccess) return e;
+      e = timed(TPMLP_K_TRANSPOSE, s, [&] { return launch_transpose(B, F, H, H, Bt, s); });
+      if (e != hipSuccess) return e;
+    }
     // P_i = X A_i; G_i = GeLU(P_i)      X: [M][H], A_i^T: [F][H] (both K-contig)
     e = run_gemm(TPMLP_K_FWD_GEMM1_GELU, KC, KC, EPI_GELU, X, H, At, H, M, F, H, p.g1, G, P_save,
                  nullptr, part, s);
@@ -594,6 +600,141 @@ tpmlp_status noalloc_scratch(void** out) {
     g_scratch_ptr[dev] = p;
   }
   *out = g_scratch_ptr[dev];
+  return TPMLP_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Sequence-parallel boundary (one GPU): every rank's tokens arrive as its own
+// row slice [M/t, H], and every rank's output and input gradient leave as its
+// own row slice.  The products whose rows are tokens run once per rank row
+// block, reading that rank's X or dZ slice and writing that rank's Z or dX slice
+// (the rank-order sum folded into the epilogues), so the gathered X and dZ and
+// the t per-shard partials are never materialised; the weight-gradient products
+// contract over all tokens and read X^T and dZ^T, which the transpose assembles
+// column block by column block from the slices.
+// ---------------------------------------------------------------------------
+struct SpBwdLayout {
+  int64_t S;               // rows per rank
+  GemmPlan g0, g1, gdx;    // recompute, dGeLU and dX products, per row block (S rows)
+  GemmPlan gdb, gda;       // weight-gradient products over all M tokens
+  bool wt;                 // the recompute reads A_i^T
+  bool tdp;                // dA reads dP_i^T
+  size_t off_Xt, off_dZt, off_At, off_P, off_Gt, off_dP, off_dPt, off_part, total;
+};
+
+SpBwdLayout sp_bwd_layout(int t, int64_t M, int64_t H, int64_t F, bool recompute) {
+  SpBwdLayout L;
+  L.S = M / t;
+  L.g0 = plan_gemm(L.S, F, H);
+  L.g1 = plan_gemm(L.S, F, H);
+  L.gdx = plan_gemm(L.S, H, F);
+  L.gdb = plan_gemm(F, H, M);
+  L.gda = plan_gemm(H, F, M);
+  const size_t mf = align_up(size_t(M) * F * 2), mh = align_up(size_t(M) * H * 2);
+  L.wt = recompute && transpose_weights(L.S, H, F);
+  L.tdp = transpose_dp(M, H, F);
+  L.off_Xt = 0;
+  L.off_dZt = mh;
+  L.off_At = 2 * mh;
+  L.off_P = L.off_At + (L.wt ? align_up(size_t(H) * F * 2) : 0);
+  L.off_Gt = L.off_P + (recompute ? mf : 0);
+  L.off_dP = L.off_Gt + mf;
+  L.off_dPt = L.off_dP + mf;
+  L.off_part = L.off_dPt + (L.tdp ? mf : 0);
+  size_t part = recompute ? part_bytes(L.g0, L.S, F) : 0;
+  part = std::max({part, part_bytes(L.g1, L.S, F), part_bytes(L.gdb, F, H), part_bytes(L.gda, H, F),
+                   part_bytes(L.gdx, L.S, H)});
+  L.total = L.off_part + align_up(part);
+  return L;
+}
+
+size_t sp_ws_bytes(int t, int64_t M, int64_t H, int64_t F) {
+  return align_up(std::max({plan_fwd(M / t, H, F).total, sp_bwd_layout(t, M, H, F, true).total,
+                            sp_bwd_layout(t, M, H, F, false).total}));
+}
+
+// X^T and dZ^T [H][M] from the ranks' slices: slice r fills columns [r S, (r+1) S).
+hipError_t enqueue_sp_transposes(const tpmlp_bf16* const* dZ_sl, const tpmlp_bf16* const* X_sl, int t, int64_t M,
+                                 int64_t H, void* ws, hipStream_t s) {
+  const SpBwdLayout L = sp_bwd_layout(t, M, H, 8, false);  // the transposes' offsets depend on M and H only
+  uint16_t* Xt = reinterpret_cast<uint16_t*>(ws_at(ws, L.off_Xt));
+  uint16_t* dZt = reinterpret_cast<uint16_t*>(ws_at(ws, L.off_dZt));
+  for (int r = 0; r < t; ++r) {
+    hipError_t e = timed(TPMLP_K_TRANSPOSE, s, [&] { return launch_transpose(X_sl[r], L.S, H, H, Xt + r * L.S, s, M); });
+    if (e != hipSuccess) return e;
+    e = timed(TPMLP_K_TRANSPOSE, s, [&] { return launch_transpose(dZ_sl[r], L.S, H, H, dZt + r * L.S, s, M); });
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// Shard i's backward over the ranks' slices (arguments checked, transposes made).
+// acc: add this shard's partial input gradient to the dX slices.
+hipError_t enqueue_bwd_sp(const tpmlp_bf16* const* dZ_sl, const tpmlp_bf16* const* X_sl, const tpmlp_bf16* A,
+                          const tpmlp_bf16* B, const tpmlp_bf16* P_saved, float* const* dX_sl, float* dA, float* dB,
+                          int t, int64_t M, int64_t H, int64_t F, void* ws, hipStream_t s, bool acc) {
+  const bool recompute = P_saved == nullptr;
+  const SpBwdLayout L = sp_bwd_layout(t, M, H, F, recompute);
+  const int64_t S = L.S;
+  const uint16_t* Xt = reinterpret_cast<const uint16_t*>(ws_at(ws, L.off_Xt));
+  const uint16_t* dZt = reinterpret_cast<const uint16_t*>(ws_at(ws, L.off_dZt));
+  uint16_t* Gt = reinterpret_cast<uint16_t*>(ws_at(ws, L.off_Gt));
+  uint16_t* dP = reinterpret_cast<uint16_t*>(ws_at(ws, L.off_dP));
+  float* part = reinterpret_cast<float*>(ws_at(ws, L.off_part));
+  const uint16_t* P = P_saved;
+  hipError_t e;
+  if (recompute) {
+    // P_i = X A_i again, one rank row block at a time
+    uint16_t* Pw = reinterpret_cast<uint16_t*>(ws_at(ws, L.off_P));
+    uint16_t* At = reinterpret_cast<uint16_t*>(ws_at(ws, L.off_At));
+    if (L.wt) {
+      e = timed(TPMLP_K_TRANSPOSE, s, [&] { return launch_transpose(A, H, F, F, At, s); });
+      if (e != hipSuccess) return e;
+    }
+    for (int r = 0; r < t; ++r) {
+      e = L.wt ? run_gemm(TPMLP_K_BWD_RECOMPUTE, KC, KC, EPI_BF16, X_sl[r], H, At, H, S, F, H, L.g0, Pw + r * S * F,
+                          nullptr, nullptr, part, s)
+               : run_gemm(TPMLP_K_BWD_RECOMPUTE, KC, MC, EPI_BF16, X_sl[r], H, A, F, S, F, H, L.g0, Pw + r * S * F,
+                          nullptr, nullptr, part, s);
+      if (e != hipSuccess) return e;
+    }
+    P = Pw;
+  }
+  // dG_i = dZ B_i^T and the dGeLU epilogue, per rank row block: dP_i rows and
+  // G_i^T columns of that block (G_i^T rows of M elements)
+  for (int r = 0; r < t; ++r) {
+    e = run_gemm(TPMLP_K_BWD_DGELU, KC, KC, EPI_DGELU, dZ_sl[r], H, B, H, S, F, H, L.g1, dP + r * S * F, Gt + r * S,
+                 P + r * S * F, part, s, 0, M);
+    if (e != hipSuccess) return e;
+  }
+  // dB_i = G_i^T dZ and dA_i = X^T dP_i over all tokens
+  e = run_gemm(TPMLP_K_BWD_DB, KC, KC, EPI_F32, Gt, M, dZt, M, F, H, M, L.gdb, dB, nullptr, nullptr, part, s);
+  if (e != hipSuccess) return e;
+  if (L.tdp) {
+    uint16_t* dPt = reinterpret_cast<uint16_t*>(ws_at(ws, L.off_dPt));
+    e = timed(TPMLP_K_TRANSPOSE, s, [&] { return launch_transpose(dP, M, F, F, dPt, s); });
+    if (e != hipSuccess) return e;
+    e = run_gemm(TPMLP_K_BWD_DA, KC, KC, EPI_F32, Xt, M, dPt, M, H, F, M, L.gda, dA, nullptr, nullptr, part, s);
+  } else {
+    e = run_gemm(TPMLP_K_BWD_DA, KC, MC, EPI_F32, Xt, M, dP, F, H, F, M, L.gda, dA, nullptr, nullptr, part, s);
+  }
+  if (e != hipSuccess) return e;
+  // dX_i = dP_i A_i^T, per rank row block, into (or added to) that rank's slice
+  for (int r = 0; r < t; ++r) {
+    e = run_gemm(TPMLP_K_BWD_DX, KC, KC, acc ? EPI_F32_ACC : EPI_F32, dP + r * S * F, F, A, F, S, H, F, L.gdx,
+                 dX_sl[r], nullptr, nullptr, part, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// Shape checks shared by the sequence-parallel entry points.
+tpmlp_status check_sp_shape(int t, int64_t M, int64_t H, int64_t F) {
+  tpmlp_status st = check_shape(M, H, F);
+  if (st) return st;
+  if (M % t || !shape_ok(M / t))
+    return fail(TPMLP_ERR_SHAPE, "M must split into t row slices of a positive multiple of 8 rows");
+  if (t > 1 && H > ACC_MAX_LDO) return fail(TPMLP_ERR_SHAPE, "H is above 2^22 (the folded rank sums' limit)");
   return TPMLP_OK;
 }
 
@@ -921,6 +1062,103 @@ tpmlp_status tpmlp_tp_bwd_full(const tpmlp_bf16* dZ, const tpmlp_bf16* X, const 
   if (t > 1 && !fold) {
     hipError_t e = timed(TPMLP_K_SHARD_SUM, s, [&] { return launch_sum(parts, t, dX, int64_t(mh), s); });
     if (e != hipSuccess) return hip_fail(e, "tpmlp_tp_bwd_full sum");
+  }
+  return TPMLP_OK;
+}
+
+size_t tpmlp_sp_workspace_bytes(int t, int64_t M, int64_t H, int64_t F_i) {
+  if (t < 1 || t > TPMLP_MAX_SHARDS || !shape_ok(M) || !shape_ok(H) || !shape_ok(F_i) || M % t || !shape_ok(M / t))
+    return 0;
+  return sp_ws_bytes(t, M, H, F_i);
+}
+
+tpmlp_status tpmlp_sp_fwd(const tpmlp_bf16* const* X_sl, const tpmlp_bf16* const* A_sh, const tpmlp_bf16* const* B_sh,
+                          tpmlp_bf16* const* P_sh, float* const* Z_sl, int t, int64_t M, int64_t H, int64_t F_i,
+                          void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  if (!X_sl || !A_sh || !B_sh || !Z_sl) return fail(TPMLP_ERR_NULL, "a slice or shard array is NULL");
+  if (t < 1 || t > TPMLP_MAX_SHARDS) return fail(TPMLP_ERR_SHARDS, "t outside 1..TPMLP_MAX_SHARDS");
+  tpmlp_status st = check_ptrs({{ws, "ws"}});
+  if (st) return st;
+  if ((st = check_sp_shape(t, M, H, F_i))) return st;
+  const size_t need = tpmlp_sp_workspace_bytes(t, M, H, F_i);
+  if (ws_bytes < need) return fail(TPMLP_ERR_WORKSPACE, "ws_bytes below tpmlp_sp_workspace_bytes");
+  const int64_t S = M / t;
+  const size_t sh = size_t(S) * H, hf = size_t(H) * F_i, mf = size_t(M) * F_i;
+  std::vector<Range> ins, outs = {{ws, need, "ws"}};
+  for (int i = 0; i < t; ++i) {
+    const std::string idx = "[" + std::to_string(i) + "]";
+    if (!X_sl[i] || !Z_sl[i] || !A_sh[i] || !B_sh[i]) return fail(TPMLP_ERR_NULL, "a slice or shard pointer" + idx + " is NULL");
+    for (const void* p : {(const void*)X_sl[i], (const void*)Z_sl[i], (const void*)A_sh[i], (const void*)B_sh[i]})
+      if (!aligned16(p)) return fail(TPMLP_ERR_ALIGN, "a slice or shard pointer" + idx + " is not 16-byte aligned");
+    ins.push_back({X_sl[i], sh * 2, "X_sl[i]"});
+    ins.push_back({A_sh[i], hf * 2, "A_sh[i]"});
+    ins.push_back({B_sh[i], hf * 2, "B_sh[i]"});
+    outs.push_back({Z_sl[i], sh * 4, "Z_sl[i]"});
+    if (P_sh && P_sh[i]) {
+      if (!aligned16(P_sh[i])) return fail(TPMLP_ERR_ALIGN, "P_sh" + idx + " is not 16-byte aligned");
+      outs.push_back({P_sh[i], mf * 2, "P_sh[i]"});
+    }
+  }
+  if ((st = check_alias(outs, ins))) return st;
+  if ((st = check_device())) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // Shard i over the ranks' row blocks: block r reads rank r's tokens and writes
+  // (shard 0) or adds to (shards 1 ..) rank r's output slice, so each slice ends
+  // as the rank-order sum of the shards' rows: the reduce-scatter's result.
+  for (int i = 0; i < t; ++i) {
+    for (int r = 0; r < t; ++r) {
+      tpmlp_bf16* Pi = (P_sh && P_sh[i]) ? P_sh[i] + size_t(r) * S * F_i : nullptr;
+      hipError_t e = enqueue_fwd(X_sl[r], A_sh[i], F_i, B_sh[i], Z_sl[r], Pi, S, H, F_i, ws, s, i > 0, r > 0);
+      if (e != hipSuccess) return hip_fail(e, "tpmlp_sp_fwd launch");
+    }
+  }
+  return TPMLP_OK;
+}
+
+tpmlp_status tpmlp_sp_bwd(const tpmlp_bf16* const* dZ_sl, const tpmlp_bf16* const* X_sl,
+                          const tpmlp_bf16* const* A_sh, const tpmlp_bf16* const* B_sh, const tpmlp_bf16* const* P_sh,
+                          float* const* dA_sh, float* const* dB_sh, float* const* dX_sl, int t, int64_t M, int64_t H,
+                          int64_t F_i, void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  if (!dZ_sl || !X_sl || !A_sh || !B_sh || !dA_sh || !dB_sh || !dX_sl)
+    return fail(TPMLP_ERR_NULL, "a slice or shard array is NULL");
+  if (t < 1 || t > TPMLP_MAX_SHARDS) return fail(TPMLP_ERR_SHARDS, "t outside 1..TPMLP_MAX_SHARDS");
+  tpmlp_status st = check_ptrs({{ws, "ws"}});
+  if (st) return st;
+  if ((st = check_sp_shape(t, M, H, F_i))) return st;
+  const size_t need = tpmlp_sp_workspace_bytes(t, M, H, F_i);
+  if (ws_bytes < need) return fail(TPMLP_ERR_WORKSPACE, "ws_bytes below tpmlp_sp_workspace_bytes");
+  const int64_t S = M / t;
+  const size_t sh = size_t(S) * H, hf = size_t(H) * F_i, mf = size_t(M) * F_i;
+  std::vector<Range> ins, outs = {{ws, need, "ws"}};
+  for (int i = 0; i < t; ++i) {
+    const std::string idx = "[" + std::to_string(i) + "]";
+    const void* ptrs[] = {dZ_sl[i], X_sl[i], A_sh[i], B_sh[i], dA_sh[i], dB_sh[i], dX_sl[i]};
+    for (const void* p : ptrs) {
+      if (!p) return fail(TPMLP_ERR_NULL, "a slice or shard pointer" + idx + " is NULL");
+      if (!aligned16(p)) return fail(TPMLP_ERR_ALIGN, "a slice or shard pointer" + idx + " is not 16-byte aligned");
+    }
+    if (P_sh && !P_sh[i]) return fail(TPMLP_ERR_NULL, "P_sh" + idx + " is NULL");
+    if (P_sh && !aligned16(P_sh[i])) return fail(TPMLP_ERR_ALIGN, "P_sh" + idx + " is not 16-byte aligned");
+    ins.push_back({dZ_sl[i], sh * 2, "dZ_sl[i]"});
+    ins.push_back({X_sl[i], sh * 2, "X_sl[i]"});
+    ins.push_back({A_sh[i], hf * 2, "A_sh[i]"});
+    ins.push_back({B_sh[i], hf * 2, "B_sh[i]"});
+    if (P_sh) ins.push_back({P_sh[i], mf * 2, "P_sh[i]"});
+    outs.push_back({dA_sh[i], hf * 4, "dA_sh[i]"});
+    outs.push_back({dB_sh[i], hf * 4, "dB_sh[i]"});
+    outs.push_back({dX_sl[i], sh * 4, "dX_sl[i]"});
+  }
+  if ((st = check_alias(outs, ins))) return st;
+  if ((st = check_device())) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = enqueue_sp_transposes(dZ_sl, X_sl, t, M, H, ws, s);
+  if (e != hipSuccess) return hip_fail(e, "tpmlp_sp_bwd transpose");
+  for (int i = 0; i < t; ++i) {
+    e = enqueue_bwd_sp(dZ_sl, X_sl, A_sh[i], B_sh[i], P_sh ? P_sh[i] : nullptr, dX_sl, dA_sh[i], dB_sh[i], t, M, H,
+                       F_i, ws, s, i > 0);
+    if (e != hipSuccess) return hip_fail(e, "tpmlp_sp_bwd launch");
   }
   return TPMLP_OK;
 }

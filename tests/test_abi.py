@@ -99,7 +99,7 @@ def test_last_error_is_per_thread():
 
 
 def test_version_and_strings():
-    assert L.tpmlp_abi_version() == 8
+    assert L.tpmlp_abi_version() == 9
     assert L.tpmlp_status_str(0) == "ok"
     assert L.tpmlp_status_str(ALIAS) == "output overlaps another buffer"
     assert L.tpmlp_status_str(99) == "unknown status"
@@ -329,3 +329,48 @@ def test_timing_argument_errors():
     assert lib.tpmlp_timing_begin_kinds(8, 1 << L.KERNEL_COUNT) == SHAPE
     assert lib.tpmlp_timing_begin_kinds(0, 1) == SHAPE
     assert lib.tpmlp_timing_end(None, None, None) == NULL
+
+
+def _sp(fn, t=2, M=128, H=64, F=64, **kw):
+    arr = lambda base: L._ptr_array([_p(base + i) for i in range(t)], t)
+    ws = kw.pop("ws", _p(40))
+    wsb = kw.pop("wsb", 1 << 30)
+    if fn == "fwd":
+        a = dict(X=arr(0), A=arr(10), B=arr(20), P=None, Z=arr(30))
+        a.update(kw)
+        st = L.lib().tpmlp_sp_fwd(a["X"], a["A"], a["B"], a["P"], a["Z"], t, M, H, F, ws, wsb, None)
+    else:
+        a = dict(dZ=arr(0), X=arr(8), A=arr(16), B=arr(24), P=None, dA=arr(32), dB=arr(44), dX=arr(52))
+        a.update(kw)
+        st = L.lib().tpmlp_sp_bwd(a["dZ"], a["X"], a["A"], a["B"], a["P"], a["dA"], a["dB"], a["dX"], t, M, H, F,
+                                  ws, wsb, None)
+    return st, L.lib().tpmlp_last_error().decode()
+
+
+def test_sp_argument_errors():
+    """The sequence-parallel calls reject bad slices before any HIP call: NULL
+    arrays and entries, token counts that do not split into slices of multiples
+    of 8 rows, a short workspace, and overlapping outputs."""
+    for fn in ("fwd", "bwd"):
+        key = "X" if fn == "fwd" else "dZ"
+        assert _sp(fn, **{key: None})[0] == NULL
+        st, msg = _sp(fn, M=120, t=4)   # 30 rows per slice
+        assert st == SHAPE and "row slices" in msg
+        assert _sp(fn, M=96, t=4)[0] in (HIP, UNSUP)  # 24 rows per slice: valid, reaches the device check
+        assert _sp(fn, t=0)[0] == SHARDS
+        need = L.tpmlp_sp_workspace_bytes(2, 128, 64, 64)
+        assert _sp(fn, wsb=need - 1)[0] == WS
+    # an output slice on top of an input slice
+    arr = L._ptr_array([_p(0), _p(30)], 2)
+    st, msg = _sp("fwd", Z=arr)
+    assert st == ALIAS and "Z_sl" in msg
+    st, _ = _sp("fwd", H=(1 << 22) + 8)
+    assert st == SHAPE
+
+
+def test_sp_workspace_query():
+    assert L.tpmlp_sp_workspace_bytes(4, 32768, 3584, 3584) > 0
+    assert L.tpmlp_sp_workspace_bytes(4, 32768 + 8, 3584, 3584) == 0  # not a multiple of t
+    assert L.tpmlp_sp_workspace_bytes(4, 96, 64, 64) > 0
+    assert L.tpmlp_sp_workspace_bytes(3, 96, 64, 64) > 0     # 32 rows per slice
+    assert L.tpmlp_sp_workspace_bytes(4, 48, 64, 64) == 0     # 12 rows per slice 

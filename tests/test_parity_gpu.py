@@ -497,6 +497,81 @@ def test_graph_replay_matches_eager(shape):
             assert torch.equal(x, y), f"replay {rep} differs"
 
 
+SP_CASES = [
+    # (M, H, F_i, t, store_p): rows per rank slice a multiple of 8, ragged tiles
+    (528, 264, 392, 2, True),
+    (1056, 520, 264, 4, False),
+    (208, 192, 392, 2, True),      # fused small-H forward per slice
+    (16400, 136, 520, 2, False),   # 8200-row slices: the forward transposes the weights
+    (2048, 1032, 2056, 8, True),   # 256-row slices, split and hybrid products
+]
+
+
+@pytest.mark.parametrize("case", SP_CASES, ids=lambda c: "x".join(map(str, c[:4])) + ("_store" if c[4] else "_recompute"))
+def test_sequence_parallel_boundary(case):
+    """tpmlp_sp_fwd / tpmlp_sp_bwd take every rank's token rows as a separate
+    slice and return every rank's rows of Z and dX: rank r's output slice must be
+    rows [r S, (r+1) S) of sum_i GeLU(X A_i) B_i (the reduce-scatter of the
+    shards' partials), its dX slice the same rows of sum_i dX_i, and dA_i, dB_i the
+    shard gradients over all tokens.  Each slice is its own allocation with a
+    canary band on both sides.  The results also match the t-shard driver's on
+    the gathered X within the tolerance."""
+    from tensor_transformer_mlp_03_amd import _lib as L
+    from tensor_transformer_mlp_03_amd.device import DeviceMLP, to_device
+    M, H, F, t, store = case
+    S = M // t
+    say(f"[sp boundary] M={M} H={H} F_i={F} t={t} ({S} rows per rank) store_p={store}")
+    w = I.custom_workload(350 + t, M=M, H=H, F_i=F, t=t, w_std=0.05)
+    inp = I.make_inputs(w)
+    bufs = []
+
+    def slice_buf(n, dtype, src=None):
+        fill = float("nan") if dtype == torch.float32 else -12345
+        buf = torch.full((n + 2 * PAD,), fill, dtype=dtype, device="cuda")
+        v = buf[PAD:PAD + n]
+        if src is not None:
+            v.copy_(src.reshape(-1))
+        bufs.append((buf, n))
+        return v
+
+    Xd, dZd = to_device(inp.X), to_device(inp.dZ)
+    X_sl = [slice_buf(S * H, torch.int16, Xd[r * S:(r + 1) * S]).view(S, H) for r in range(t)]
+    dZ_sl = [slice_buf(S * H, torch.int16, dZd[r * S:(r + 1) * S]).view(S, H) for r in range(t)]
+    Z_sl = [slice_buf(S * H, torch.float32).view(S, H) for _ in range(t)]
+    dX_sl = [slice_buf(S * H, torch.float32).view(S, H) for _ in range(t)]
+    A = [to_device(a) for a in inp.A]
+    B = [to_device(b) for b in inp.B]
+    P = [torch.empty((M, F), dtype=torch.int16, device="cuda") for _ in range(t)] if store else None
+    dA = [torch.empty((H, F), dtype=torch.float32, device="cuda") for _ in range(t)]
+    dB = [torch.empty((F, H), dtype=torch.float32, device="cuda") for _ in range(t)]
+    ws = torch.empty(L.tpmlp_sp_workspace_bytes(t, M, H, F), dtype=torch.uint8, device="cuda")
+    L.tpmlp_sp_fwd(X_sl, A, B, P, Z_sl, ws)
+    L.tpmlp_sp_bwd(dZ_sl, X_sl, A, B, P, dA, dB, dX_sl, ws)
+    torch.cuda.synchronize()
+    for buf, n in bufs:
+        _canary_intact(buf, n, "slice") if buf.dtype == torch.float32 else None
+        if buf.dtype == torch.int16:
+            assert bool((buf[:PAD] == -12345).all()) and bool((buf[PAD + n:] == -12345).all())
+    Xo, dZo = dec(inp.X), dec(inp.dZ)
+    Ao, Bo = [dec(a) for a in inp.A], [dec(b) for b in inp.B]
+    Z, _ = O.tp_forward(Xo, Ao, Bo)
+    dX, _, dAo, dBo = O.tp_backward(dZo, Xo, Ao, Bo)
+    r_ = {}
+    for r in range(t):
+        check(f"Z_sl[{r}]", Z_sl[r].cpu().numpy(), Z[r * S:(r + 1) * S], r_)
+        check(f"dX_sl[{r}]", dX_sl[r].cpu().numpy(), dX[r * S:(r + 1) * S], r_)
+    for i in range(t):
+        check(f"dA_{i}", dA[i].cpu().numpy(), dAo[i], r_)
+        check(f"dB_{i}", dB[i].cpu().numpy(), dBo[i], r_)
+    # the t-shard driver on the gathered tokens gives the same outputs within tolerance
+    d = DeviceMLP(inp, store_p=store, driver=True)
+    d.step()
+    torch.cuda.synchronize()
+    check_dev("Z_sl_vs_driver", torch.cat(Z_sl, 0), d.Z, r_)
+    check_dev("dX_sl_vs_driver", torch.cat(dX_sl, 0), d.dX, r_)
+    say("  err/tol:", {k: round(v, 3) for k, v in r_.items()})
+
+
 def test_deterministic():
     w = I.custom_workload(311, M=768, H=1024, F_i=1536, t=2)
     say(f"[determinism] {w}")
