@@ -20,19 +20,13 @@
 // float32 pre-activation never round-trips through memory: asorrir.com survey,
 // part 三, 算子融合.)
 //
-// Two kernels:
-//  * gemm_x16_kernel: 256 x 256 or 256 x 128 tiles, A K-contiguous, B either;
-//    four waves, one per SIMD, each accumulating a 128 x 128 (or 128 x 64)
-//    sub-tile as 16 x 16 blocks on v_mfma_f32_16x16x32_bf16, with loads and LDS
-//    reads placed between its MFMAs (its comment has the schedule).  The main
-//    path.
-//  * gemm_kernel: a synchronous two-stage pipeline with 128 x 128 tiles on
-//    v_mfma_f32_32x32x16_bf16, an N-contiguous operand transposed in registers;
-//    used for outputs too small for 256-row tiles.
-// Shared design points:
-//  * A K-contiguous operand tile sits in LDS as [rows][64] (128-byte rows), so
-//    an MFMA operand fragment is one ds_read_b128 per lane (8 consecutive k of
-//    one row); an N-contiguous one in gemm_x16_kernel as [64 k][128 n] slots,
+// One kernel, gemm_x16_kernel, in three tile shapes (256 x 256, 256 x 128, 128 x
+// 128): four waves, one per SIMD, each accumulating its sub-tile as 16 x 16
+// blocks on v_mfma_f32_16x16x32_bf16, with loads and LDS reads placed between
+// its MFMAs (its comment has the schedule).  Design points:
+//  * A K-contiguous operand sits in LDS as 128-row slots of [rows][64 k]
+//    (128-byte rows), so an MFMA operand fragment is one ds_read_b128 per lane
+//    (8 consecutive k of one row); an N-contiguous one as [64 k][128 n] slots,
 //    read with two ds_read_b64_tr_b16 per fragment.
 //  * Operands go from memory straight into LDS with buffer_load ... lds (16
 //    bytes per lane, no staging registers, no LDS write instructions).  Buffer
@@ -43,8 +37,8 @@
 //    permutation on the memory side, so each DMA still writes 1 KiB of
 //    contiguous LDS.
 //  * The MFMA takes the B fragment as its first operand, so each lane ends with
-//    4 consecutive output columns of one row: epilogues store 8- or 16-byte
-//    vectors.
+//    4 consecutive output columns of one row; the epilogue restages them
+//    through LDS and stores whole 128-byte lines.
 //  * Workgroups are renumbered so that consecutive output tiles (which share
 //    operand panels) run on the same XCD and its L2, then grouped 4 tiles tall.
 
@@ -72,100 +66,8 @@ constexpr int GROUP_M = 4;
 constexpr int NUM_XCD = 8;
 constexpr uint32_t OOB = 0x7FFFFFF0u;  // voffset past num_records: the load returns 0
 
-// Swizzle of the 16-byte chunk index inside a 128-byte row of a K-contiguous
-// tile ([rows][64]): rows r .. r+15 read at one chunk land on 16 distinct
-// (row parity, chunk) bank groups, and rows r .. r+7 on 8 distinct chunks.
-__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
-
-// Byte offset of 16-byte chunk c (k = 8c .. 8c+7) of row r in a [rows][64] tile.
-__device__ __forceinline__ int tile_off(int r, int c) { return r * 128 + ((c ^ swz(r)) << 4); }
-
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)OOB, 0x00020000);
-}
-
-// A K-contiguous operand's [R][64] tile of one K step, loaded straight into LDS.
-// DMA instruction i of wave w writes LDS chunks (i*NWAVES + w)*64 + lane of the
-// tile; each lane loads the memory chunk that the swizzle places there.
-template <int R, int NWAVES>
-struct DmaLoader {
-  static constexpr int CHUNKS = R * 8;
-  static constexpr int PER_WAVE = CHUNKS / 64 / NWAVES;
-  static_assert(CHUNKS % (64 * NWAVES) == 0, "tile must divide evenly over the waves");
-  uint32_t off[PER_WAVE];  // byte offset of the lane's chunk from the K step's base
-  int row[PER_WAVE];       // the chunk's row inside the tile
-  int kc[PER_WAVE];        // the chunk's first k inside the K step
-
-  __device__ __forceinline__ void init(int64_t ld, int wave, int lane) {
-#pragma unroll
-    for (int i = 0; i < PER_WAVE; ++i) {
-      const int q = (i * NWAVES + wave) * 64 + lane;
-      const int r = q >> 3, c = (q & 7) ^ swz(r);
-      row[i] = r;
-      kc[i] = 8 * c;
-      off[i] = (uint32_t)(((int64_t)r * ld + 8 * c) * 2);
-    }
-  }
-
-  // base: element (row0, k0) of the operand.
-  __device__ __forceinline__ void issue(const uint16_t* base, char* tile, int rows_left, int k_left,
-                                        int wave) const {
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base);
-#pragma unroll
-    for (int i = 0; i < PER_WAVE; ++i) {
-      const bool ok = (row[i] < rows_left) && (kc[i] < k_left);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(tile + (i * NWAVES + wave) * 1024), 16,
-                                               ok ? off[i] : OOB, 0, 0, 0);
-    }
-  }
-};
-
-// An M/N-contiguous operand's tile of one K step (64 k-rows of R contiguous
-// elements in memory), loaded by R threads as 8x8 blocks into registers and
-// written transposed into the [R][64] LDS tile.
-template <int R>
-struct RegLoader {
-  u32x4_t v[8];  // v[i]: elements (k = 8*kb + i, r = 8*mb .. 8*mb+7)
-  int mb, kb;
-  uint32_t off0, step;
-
-  __device__ __forceinline__ void init(int64_t ld, int t) {
-    mb = t % (R / 8);
-    kb = t / (R / 8);
-    off0 = (uint32_t)(((int64_t)(8 * kb) * ld + 8 * mb) * 2);
-    step = (uint32_t)(ld * 2);
-  }
-
-  // base: element (k0, r0) of the operand.
-  __device__ __forceinline__ void load(const uint16_t* base, int r_left, int k_left) {
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base);
-    const bool r_ok = 8 * mb < r_left;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const bool ok = r_ok && (8 * kb + i < k_left);
-      v[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, ok ? off0 + i * step : OOB, 0, 0));
-    }
-  }
-
-  // Row r of the block gets the 8 k-values of element r: dword e packs
-  // (k = 2e, k = 2e+1), i.e. the halves of v[2e] and v[2e+1] that hold r.
-  __device__ __forceinline__ void store(char* tile) const {
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const uint32_t sel = (r & 1) ? 0x07060302u : 0x05040100u;
-      u32x4_t o;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = __builtin_amdgcn_perm(v[2 * e + 1][r >> 1], v[2 * e][r >> 1], sel);
-      *reinterpret_cast<u32x4_t*>(tile + tile_off(8 * mb + r, kb)) = o;
-    }
-  }
-};
-
-// MFMA operand fragment of a 32-row slice at sub-step kk (16 wide) of a
-// [rows][64] tile: lane l gets the 8 k-values 16*kk + 8*(l/32) .. +7 of row l%32.
-__device__ __forceinline__ bf16x8_t read_frag(const char* tile, int r0, int kk, int lane) {
-  const int r = r0 + (lane & 31);
-  return *reinterpret_cast<const bf16x8_t*>(tile + tile_off(r, 2 * kk + (lane >> 5)));
 }
 
 // ds_read_b64_tr_b16 from LDS address `p`.  Issued through inline assembly:
@@ -308,70 +210,76 @@ constexpr int ROW_B = 256;  // staged row stride in bytes (64 float32)
 // positions, two lanes per bank pair (the same as the row-contiguous reads).
 __device__ __forceinline__ int gt_swz(int r) { return (r + 4 * (r >> 3)) & 7; }
 
-// The epilogue proper, independent of the MFMA accumulator layout: for each of
-// NH 64-row halves of the wave's (64 NH) x 64 region, stage_half(h) writes the
-// half's float32 values into `stage` (row r in 0..63 at r * ROW_B, 16-byte chunk c
-// in 0..15 at position c ^ (r & 15)), and the half is finished from there.
-template <int EPI, int NH, class StageHalf>
-__device__ __forceinline__ void store_staged(StageHalf&& stage_half, const GemmArgs& args, char* stage, int row_w,
-                                             int col_w, int split, int lane) {
+// The epilogue proper, independent of the MFMA accumulator layout.  The wave's
+// region is NC chunks of 64 x 64, laid out nh chunks tall: chunk c covers rows
+// row_w + 64 (c % nh) and columns col_w + 64 (c / nh) onward.  stage_chunk(c)
+// writes the chunk's float32 values into `stage` (row r in 0..63 at r * ROW_B,
+// 16-byte chunk q in 0..15 at position q ^ (r & 15)), and the chunk is finished
+// from there.
+template <int EPI, int NC, class StageChunk>
+__device__ __forceinline__ void store_staged(StageChunk&& stage_chunk, const GemmArgs& args, char* stage, int row_w,
+                                             int col_w, int nh, int split, int lane) {
   // Each phase below issues all of its memory operations before it waits for
-  // any: the dGeLU pre-activations of a 64-row half are loaded together (one
-  // memory latency instead of one per vector; the next half's are in flight
-  // while this half is finished), and LDS reads are batched ahead of the
-  // stores that use them.  The pre-activations come through a buffer
-  // descriptor on the wave's (uniform) first row and column, so rows and
-  // columns outside the output read as zero without a branch.
+  // any, and the global loads an epilogue needs (the dGeLU pre-activations, the
+  // EPI_F32_ACC running sum) are double-buffered: chunk c + 1's are in flight
+  // while chunk c is finished, so only the first chunk's latency is exposed.
+  // LDS reads are batched ahead of the stores that use them.  Both loads go
+  // through a buffer descriptor on the chunk's (uniform) first row and column,
+  // so rows and columns outside the output read as zero without a branch.
   u16x8_t pre[2][8];
-  __amdgpu_buffer_rsrc_t pre_rs;
-  // EPI_F32_ACC: the running sum under a 64-row half, loaded before the half is
-  // staged so that the loads overlap the staging (descriptor on the half's first
-  // row and column; rows and columns outside the output read as zero).
-  f32x4_t old[16];
-  auto load_old = [&](int h) {
-    const __amdgpu_buffer_rsrc_t rs =
-        make_rsrc(reinterpret_cast<const float*>(args.out) + (int64_t)(row_w + 64 * h) * args.ldo + col_w);
+  f32x4_t old[2][16];
+  auto row0 = [&](int c) { return row_w + 64 * (c % nh); };
+  auto col0 = [&](int c) { return col_w + 64 * (c / nh); };
+  auto load_old = [&](int c) {
+    const int r0 = row0(c), c0 = col0(c);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(reinterpret_cast<const float*>(args.out) + (int64_t)r0 * args.ldo + c0);
 #pragma unroll
     for (int it = 0; it < 16; ++it) {
-      const int q = it * 64 + lane, r = q >> 4, c = q & 15;
-      const bool ok = row_w + 64 * h + r < args.M && col_w + 4 * c < args.N;
-      const uint32_t off = (uint32_t)(((int64_t)r * args.ldo + 4 * c) * 4);
-      old[it] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, ok ? off : OOB, 0, 0));
+      const int q = it * 64 + lane, r = q >> 4, cq = q & 15;
+      const bool ok = r0 + r < args.M && c0 + 4 * cq < args.N;
+      const uint32_t off = (uint32_t)(((int64_t)r * args.ldo + 4 * cq) * 4);
+      old[c & 1][it] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, ok ? off : OOB, 0, 0));
     }
   };
-  auto load_pre = [&](int h) {
+  auto load_pre = [&](int c) {
+    const int r0 = row0(c), c0 = col0(c);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(args.aux + (int64_t)r0 * args.ldo + c0);
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
       const int q = it * 64 + lane, r = q >> 3, cp = q & 7;
-      const int row = row_w + 64 * h + r, col = col_w + 8 * cp;
-      const bool ok = row < args.M && col < args.N;  // N % 8 == 0: 8 columns in or out together
-      const uint32_t off = (uint32_t)(((int64_t)(64 * h + r) * args.ldo + 8 * cp) * 2);
-      pre[h & 1][it] = __builtin_bit_cast(u16x8_t, __builtin_amdgcn_raw_buffer_load_b128(pre_rs, ok ? off : OOB, 0, 0));
+      const bool ok = r0 + r < args.M && c0 + 8 * cp < args.N;  // N % 8 == 0: 8 columns in or out together
+      const uint32_t off = (uint32_t)(((int64_t)r * args.ldo + 8 * cp) * 2);
+      pre[c & 1][it] = __builtin_bit_cast(u16x8_t, __builtin_amdgcn_raw_buffer_load_b128(rs, ok ? off : OOB, 0, 0));
     }
   };
-  if (EPI == EPI_DGELU) {
-    pre_rs = make_rsrc(args.aux + (int64_t)row_w * args.ldo + col_w);
-    load_pre(0);
-  }
+  if (EPI == EPI_DGELU) load_pre(0);
+  if (EPI == EPI_F32_ACC) load_old(0);
 #pragma unroll
-  for (int h = 0; h < NH; ++h) {
-    if (EPI == EPI_F32_ACC) load_old(h);
-    stage_half(h);
-    if (EPI == EPI_DGELU && h + 1 < NH) load_pre(h + 1);
+  for (int ch = 0; ch < NC; ++ch) {
+    const int h = ch % nh;  // used by the stores below through row_w + 64 * h
+    const int col_c = col0(ch);
+    if (EPI == EPI_F32_ACC && ch + 1 < NC) load_old(ch + 1);
+    stage_chunk(ch);
+    if (EPI == EPI_DGELU && ch + 1 < NC) load_pre(ch + 1);
     if (EPI == EPI_F32 || EPI == EPI_F32_ACC) {
       float* out = reinterpret_cast<float*>(args.out) + (int64_t)split * args.split_stride;
-      f32x4_t xs[16];
+      // Two batches of 8 vectors: with both running-sum buffers live, 16 would
+      // not fit beside the accumulators.
 #pragma unroll
-      for (int it = 0; it < 16; ++it) {
-        const int q = it * 64 + lane, r = q >> 4, c = q & 15;
-        xs[it] = *reinterpret_cast<const f32x4_t*>(stage + r * ROW_B + ((c ^ (r & 15)) << 4));
-      }
+      for (int b8 = 0; b8 < 16; b8 += 8) {
+        f32x4_t xs[8];
 #pragma unroll
-      for (int it = 0; it < 16; ++it) {
-        const int q = it * 64 + lane, r = q >> 4, c = q & 15;
-        const int row = row_w + 64 * h + r, col = col_w + 4 * c;
-        if (EPI == EPI_F32_ACC) xs[it] += old[it];
-        if (row < args.M && col < args.N) *reinterpret_cast<f32x4_t*>(out + (int64_t)row * args.ldo + col) = xs[it];
+        for (int u = 0; u < 8; ++u) {
+          const int q = (b8 + u) * 64 + lane, r = q >> 4, c = q & 15;
+          xs[u] = *reinterpret_cast<const f32x4_t*>(stage + r * ROW_B + ((c ^ (r & 15)) << 4));
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int it = b8 + u, q = it * 64 + lane, r = q >> 4, c = q & 15;
+          const int row = row_w + 64 * h + r, col = col_c + 4 * c;
+          if (EPI == EPI_F32_ACC) xs[u] += old[ch & 1][it];
+          if (row < args.M && col < args.N) *reinterpret_cast<f32x4_t*>(out + (int64_t)row * args.ldo + col) = xs[u];
+        }
       }
     } else {
       f32x4_t x0s[8], x1s[8];
@@ -386,7 +294,7 @@ __device__ __forceinline__ void store_staged(StageHalf&& stage_half, const GemmA
         const int q = it * 64 + lane, r = q >> 3, cp = q & 7;
         const float x[8] = {x0s[it][0], x0s[it][1], x0s[it][2], x0s[it][3],
                             x1s[it][0], x1s[it][1], x1s[it][2], x1s[it][3]};
-        const int row = row_w + 64 * h + r, col = col_w + 8 * cp;
+        const int row = row_w + 64 * h + r, col = col_c + 8 * cp;
         const bool ok = row < args.M && col < args.N;  // N % 8 == 0: 8 columns in or out together
         const int64_t o = (int64_t)row * args.ldo + col;
         u16x8_t v1, v2;
@@ -407,7 +315,7 @@ __device__ __forceinline__ void store_staged(StageHalf&& stage_half, const GemmA
         } else {  // EPI_DGELU
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const DGelu d = epi_dgelu(x[e], pre[h & 1][it][e]);
+            const DGelu d = epi_dgelu(x[e], pre[ch & 1][it][e]);
             v1[e] = d.dp;
             v2[e] = d.g;
           }
@@ -442,7 +350,7 @@ __device__ __forceinline__ void store_staged(StageHalf&& stage_half, const GemmA
 #pragma unroll
         for (int it = 0; it < 8; ++it) {
           // destination role: lane 4 q + e with q = jr, e = jq
-          const int f = col_w + 8 * it + 4 * (g >> 1) + jq, m = row_w + 64 * h + 32 * (g & 1) + 8 * jr;
+          const int f = col_c + 8 * it + 4 * (g >> 1) + jq, m = row_w + 64 * h + 32 * (g & 1) + 8 * jr;
           if (f < args.N && m < args.M) {
             const u16x8_t v = {(uint16_t)lo[it][0], (uint16_t)lo[it][1], (uint16_t)lo[it][2], (uint16_t)lo[it][3],
                                (uint16_t)hi[it][0], (uint16_t)hi[it][1], (uint16_t)hi[it][2], (uint16_t)hi[it][3]};
@@ -454,206 +362,46 @@ __device__ __forceinline__ void store_staged(StageHalf&& stage_half, const GemmA
   }
 }
 
-// Epilogue of a (32 FM) x 64 region held as 32 x 32 MFMA accumulators: register
-// r of fragment (i, j) holds C[32i + lane%32][32j + 8(r/4) + 4(lane/32) + r%4].
-template <int EPI, int FM, int FN>
-__device__ __forceinline__ void store_tile(const f32x16_t (&acc)[FM][FN], const GemmArgs& args, char* stage,
-                                           int row_w, int col_w, int split, int lane) {
-  static_assert(FN == 2 && FM % 2 == 0, "staging layout: 64 columns, 64-row halves");
-  store_staged<EPI, FM / 2>(
-      [&](int h) {
-#pragma unroll
-        for (int ii = 0; ii < 2; ++ii)
-#pragma unroll
-          for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              const int r = 32 * ii + (lane & 31);
-              const int c = 8 * j + 2 * g + (lane >> 5);  // 16-byte chunk (4 columns) of the row
-              const f32x4_t x = {acc[2 * h + ii][j][4 * g], acc[2 * h + ii][j][4 * g + 1],
-                                 acc[2 * h + ii][j][4 * g + 2], acc[2 * h + ii][j][4 * g + 3]};
-              *reinterpret_cast<f32x4_t*>(stage + r * ROW_B + ((c ^ (r & 15)) << 4)) = x;
-            }
-      },
-      args, stage, row_w, col_w, split, lane);
-}
-
 }  // namespace
 
 // The kernel has external linkage (a kernel template in an anonymous namespace
 // does not get its host launch stubs emitted for every instantiation).
 namespace kern {
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int LA, int LB, int EPI>
-__global__ void __launch_bounds__(64 * WAVES_M * WAVES_N)
-gemm_kernel(GemmArgs args) {
-  // The body is compiled for the device only: the host pass needs just the
-  // launch stub, and device builtins (buffer descriptors, LDS DMA) have no host
-  // form.
-#if defined(__HIP_DEVICE_COMPILE__)
-  constexpr int BK = TILE_BK;
-  constexpr int NWAVES = WAVES_M * WAVES_N;
-  constexpr int THREADS = 64 * NWAVES;
-  constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
-  constexpr int FM = WM / 32, FN = WN / 32;
-  constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
-  constexpr int STAGE = A_BYTES + B_BYTES;
-  // Threads that load an M/N-contiguous operand: A's blocks first, then B's.
-  constexpr int A_REG_T = (LA == MC) ? BM : 0;
-  constexpr int B_REG_T = (LB == MC) ? BN : 0;
-  static_assert(A_REG_T + B_REG_T <= THREADS, "one 8x8 block per loading thread");
-  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
-
-  int tm, tn, split;
-  tile_of(blockIdx.x, gridDim.x, args.tiles_m, args.tiles_n, tm, tn, split);
-  const int m0 = tm * BM, n0 = tn * BN;
-  const int k_begin = split * args.k_split;
-  const int k_end = min(args.K, k_begin + args.k_split);
-  const int nk = (k_end - k_begin + BK - 1) / BK;
-
-  DmaLoader<BM, NWAVES> da;
-  DmaLoader<BN, NWAVES> db;
-  if (LA == KC) da.init(args.lda, wave, lane);
-  if (LB == KC) db.init(args.ldb, wave, lane);
-
-  // One register loader per thread: threads [0, A_REG_T) take 8x8 blocks of
-  // A (when A is M/N-contiguous), threads [A_REG_T, A_REG_T + B_REG_T) blocks
-  // of B.  Both operands' tiles have R rows in LDS.
-  static_assert(LA == KC || LB == KC || BM == BN, "one register loader shape");
-  constexpr int R_REG = (LA == MC) ? BM : BN;
-  RegLoader<R_REG> rl;
-  const bool reg_a = (LA == MC) && tid < A_REG_T;
-  const bool reg_b = (LB == MC) && tid >= A_REG_T && tid < A_REG_T + B_REG_T;
-  const bool reg_any = reg_a || reg_b;
-  const uint16_t* reg_src = reg_a ? args.a : args.b;
-  const int64_t reg_ld = reg_a ? args.lda : args.ldb;
-  const int reg_o0 = reg_a ? m0 : n0;
-  const int reg_left = reg_a ? args.M - m0 : args.N - n0;
-  const int reg_tile = reg_a ? 0 : A_BYTES;
-  if (LA == MC || LB == MC) rl.init(reg_ld, reg_a ? tid : tid - A_REG_T);
-
-  // Issue the memory loads of K step `step`: DMA into its stage for
-  // K-contiguous operands, into registers for M/N-contiguous ones.
-  auto issue = [&](int step) {
-    const int k = k_begin + step * BK;
-    char* st = smem + (step & 1) * STAGE;
-    if (LA == KC) da.issue(args.a + (int64_t)m0 * args.lda + k, st, args.M - m0, k_end - k, wave);
-    if (LB == KC) db.issue(args.b + (int64_t)n0 * args.ldb + k, st + A_BYTES, args.N - n0, k_end - k, wave);
-    if ((LA == MC || LB == MC) && reg_any) rl.load(reg_src + (int64_t)k * reg_ld + reg_o0, reg_left, k_end - k);
-  };
-  // Write the register-held blocks of K step `step` into its stage.
-  auto commit = [&](int step) {
-    if ((LA == MC || LB == MC) && reg_any) rl.store(smem + (step & 1) * STAGE + reg_tile);
-  };
-
-  f32x16_t acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-  // Fragments of one 16-wide sub-step, double-buffered in registers: the reads
-  // of sub-step kk+1 are in flight while the MFMAs of sub-step kk issue.
-  bf16x8_t fa[2][FM], fb[2][FN];
-  auto read_sub = [&](int buf, const char* st, int kk) {
-#pragma unroll
-    for (int i = 0; i < FM; ++i) fa[buf][i] = read_frag(st, wm * WM + 32 * i, kk, lane);
-#pragma unroll
-    for (int j = 0; j < FN; ++j) fb[buf][j] = read_frag(st + A_BYTES, wn * WN + 32 * j, kk, lane);
-  };
-  auto mfma_sub = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf][j], fa[buf][i], acc[i][j], 0, 0, 0);
-  };
-  constexpr int SUB = BK / 16;
-  static_assert(SUB % 2 == 0, "sub-steps alternate between the two fragment buffers");
-
-  if (nk > 0) {
-    issue(0);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    commit(0);
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-    __builtin_amdgcn_s_barrier();
-    if (nk > 1) issue(1);
-    read_sub(0, smem, 0);
-  }
-
-  // One K step.  With a next step: after the reads of the last sub-step, wait
-  // for this wave's loads of step kt+1, write its register-held blocks, and
-  // wait until its LDS reads and writes are complete; after the barrier the
-  // same holds for every wave, so step kt+1's stage can be read and the
-  // current stage refilled, while the last sub-step's MFMAs run from
-  // registers.  The last step is peeled so that the loop body has one path (no
-  // conservative waits at a merge).
-  auto k_step = [&](int kt, bool has_next) {
-    const char* cur = smem + (kt & 1) * STAGE;
-#pragma unroll
-    for (int kk = 0; kk < SUB - 1; ++kk) {
-      read_sub((kk + 1) & 1, cur, kk + 1);
-      mfma_sub(kk & 1);
-    }
-    if (has_next) {
-      // sched_barrier(0): the compiler may not move instructions across, so the
-      // last sub-step's MFMAs stay behind the barrier and the next reads.
-      __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-      commit(kt + 1);
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-      __builtin_amdgcn_s_barrier();
-      if (kt + 2 < nk) issue(kt + 2);
-      read_sub(0, smem + ((kt + 1) & 1) * STAGE, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    mfma_sub((SUB - 1) & 1);
-  };
-  for (int kt = 0; kt < nk - 1; ++kt) k_step(kt, true);
-  if (nk > 0) k_step(nk - 1, false);
-
-  // Epilogue: each wave stages its tile through its own 16 KiB of LDS.
-  static_assert(NWAVES * 64 * ROW_B <= 2 * STAGE, "staging fits in the operand stages");
-  __syncthreads();  // every wave is done with the operand stages
-  store_tile<EPI>(acc, args, smem + wave * (64 * ROW_B), m0 + wm * WM, n0 + wn * WN, split, lane);
-#else
-  (void)args;
-#endif
-}
-
-
-// 256 x BN tile (BN = 256 or 128) on v_mfma_f32_16x16x32_bf16: the four-wave
-// kernel's ring of ten 16 KiB slots, LDS layouts and loads, with 16 x 16
-// accumulator blocks.  Wave (wm, wn) computes a 128 x (BN / 2) sub-tile as 8 x FJ
-// blocks (FJ = 8 or 4, 256 or 128 accumulator registers).  A K step (64) is two
-// sub-steps of 32 k; in each a wave issues 8 FJ MFMAs of 16 cycles and, between
-// them, the LDS reads of the next sub-step's fragments and one batch of loads:
-//   sub-step 0 of step k: quarters 0 and 1 of step k+2 (into step k-1's slots 2, 3)
+// BM x BN tile (256 x 256, 256 x 128 or 128 x 128) on v_mfma_f32_16x16x32_bf16.
+// The LDS is a ring of ten 16 KiB slots, each one 128-row (or 128-column)
+// quarter of a K step (64): A's BM / 128 quarters, then B's BN / 128.  Wave (wm,
+// wn) computes a (BM / 2) x (BN / 2) sub-tile as FI x FJ blocks of 16 x 16 (FI =
+// BM / 32, FJ = BN / 32: 256, 128 or 64 accumulator registers).  A K step is two
+// sub-steps of 32 k; in each a wave issues FI FJ MFMAs of 16 cycles and, between
+// them, the LDS reads of the next sub-step's fragments and one batch of loads for
+// step k+D (D = 2 for 256-row tiles, whose steps take four slots; D = 4 for 128 x
+// 128, whose steps take two):
+//   sub-step 0 of step k: the A quarters of step k+D (into slots of step k-1,
+//         which no wave reads any more)
 //   then: wait until the next sub-step's fragments are in registers and step k+1
-//         has landed (vmcnt: only the batch just issued may be in flight); barrier
-//   sub-step 1 of step k: quarters 2 and 3 of step k+2 (into step k's slots 0, 1,
-//         which no wave reads any more), and the reads of step k+1's sub-step 0.
+//         has landed (vmcnt: only loads issued after step k+1's may be in
+//         flight); barrier
+//   sub-step 1 of step k: the B quarters of step k+D (256-row tiles: into step
+//         k's first slots, which no wave reads after the barrier), and the reads
+//         of step k+1's sub-step 0.
 // The next sub-step's B fragments go to the other half of a double buffer; an A
 // fragment is reloaded as soon as its row of MFMAs has been issued (MFMAs run
-// row by row), so A needs no second buffer.
-template <int LB, int EPI, int BN>
+// row by row), so A needs no second buffer.  The deeper prefetch of the small
+// tile covers memory latency over its shorter K steps (a quarter of the MFMAs).
+template <int LB, int EPI, int BM, int BN>
 __global__ void __launch_bounds__(256)
 gemm_x16_kernel(GemmArgs args) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  static_assert(BN == 256 || BN == 128, "tile widths");
+  static_assert((BM == 256 && (BN == 256 || BN == 128)) || (BM == 128 && BN == 128), "tile shapes");
   constexpr int BK = TILE_BK;
   constexpr int SLOT = 128 * BK * 2;
+  constexpr int NA = BM / 128;              // A quarters (128 rows x BK) per K step
+  constexpr int NQ = NA + BN / 128;         // quarters loaded per K step
   constexpr int NSLOT = 10;
-  constexpr int FI = 8, FJ = BN / 32;     // 16 x 16 blocks per wave: 8 x FJ
-  constexpr int NQ = BN == 256 ? 4 : 3;   // quarters loaded per K step
-  constexpr int NM = FI * FJ;             // MFMAs per sub-step
+  constexpr int SPS = BM == 128 ? 2 : 4;    // ring slots per K step
+  constexpr int QS0 = NA;                   // quarters loaded in sub-step 0; the rest in sub-step 1
+  constexpr int FI = BM / 32, FJ = BN / 32;  // 16 x 16 blocks per wave: FI x FJ
   static_assert(BK == 64 && NSLOT * SLOT == 160 * 1024, "ten 16 KiB slots fill the LDS");
   __shared__ __attribute__((aligned(1024))) char smem[NSLOT * SLOT];
 
@@ -664,33 +412,33 @@ gemm_x16_kernel(GemmArgs args) {
 
   int tm, tn, split;
   tile_of(blockIdx.x, gridDim.x, args.tiles_m, args.tiles_n, tm, tn, split);
-  const int m0 = tm * 256, n0 = tn * BN;
+  const int m0 = tm * BM, n0 = tn * BN;
   const int k_begin = split * args.k_split;
   const int k_end = min(args.K, k_begin + args.k_split);
   const int nk = (k_end - k_begin + BK - 1) / BK;
 
-  QuarterKC qa[2], qb[2];
-  QuarterMC qm[2];
+  QuarterKC qa[NA], qb[BN / 128];
+  QuarterMC qm[BN / 128];
 #pragma unroll
-  for (int q = 0; q < 2; ++q) qa[q].init(args.lda, args.M - m0 - 128 * q, wave, lane);
+  for (int q = 0; q < NA; ++q) qa[q].init(args.lda, args.M - m0 - 128 * q, wave, lane);
 #pragma unroll
-  for (int q = 0; q < NQ - 2; ++q) {
+  for (int q = 0; q < NQ - NA; ++q) {
     if (LB == KC) qb[q].init(args.ldb, args.N - n0 - 128 * q, wave, lane);
     else qm[q].init(args.ldb, args.N - n0 - 128 * q, wave, lane);
   }
 
-  auto slot = [&](int r, int q) -> char* { return smem + ((4 * r + q) % NSLOT) * SLOT; };
+  auto slot = [&](int r, int q) -> char* { return smem + ((SPS * r + q) % NSLOT) * SLOT; };
   // Instruction i of this wave's share of quarter q of K step `step` (r = step % 5).
   auto load = [&](int step, int r, int q, int i) {
     if (q >= NQ) return;
     const int k = k_begin + step * BK;
     char* dst = slot(r, q);
-    if (q < 2) {
+    if (q < NA) {
       qa[q].issue(make_rsrc(args.a + (int64_t)(m0 + 128 * q) * args.lda + k), dst, k_end - k, wave, i);
     } else if (LB == KC) {
-      qb[q - 2].issue(make_rsrc(args.b + (int64_t)(n0 + 128 * (q - 2)) * args.ldb + k), dst, k_end - k, wave, i);
+      qb[q - NA].issue(make_rsrc(args.b + (int64_t)(n0 + 128 * (q - NA)) * args.ldb + k), dst, k_end - k, wave, i);
     } else {
-      qm[q - 2].issue(make_rsrc(args.b + (int64_t)k * args.ldb + n0 + 128 * (q - 2)), dst, k_end - k, wave, i);
+      qm[q - NA].issue(make_rsrc(args.b + (int64_t)k * args.ldb + n0 + 128 * (q - NA)), dst, k_end - k, wave, i);
     }
   };
 
@@ -709,11 +457,14 @@ gemm_x16_kernel(GemmArgs args) {
   const int wcol = BN == 256 ? 0 : 64 * wn;  // the wave's first column inside its B quarter
 #pragma unroll
   for (int j = 0; j < FJ; ++j) lane_mc[j] = mc16_lane_off(wcol + 16 * j, lane);
+  // A fragment f of the wave: rows 16 f of its quarter (BM = 256: quarter wm),
+  // or of its half of the one quarter (BM = 128: rows 64 wm + 16 f).
   auto read_a = [&](int r, int kk, int f) {
-    fa[f] = *reinterpret_cast<const bf16x8_t*>(slot(r, wm) + lane_kc[kk] + 2048 * f);
+    const char* ta = BM == 256 ? slot(r, wm) + 2048 * f : slot(r, 0) + 2048 * (4 * wm + f);
+    fa[f] = *reinterpret_cast<const bf16x8_t*>(ta + lane_kc[kk]);
   };
   auto read_b = [&](int buf, int r, int kk, int j) {
-    const char* tb = slot(r, BN == 256 ? 2 + wn : 2);
+    const char* tb = slot(r, BN == 256 ? NA + wn : NA);
     if (LB == KC) {
       const int f = (BN == 256 ? 0 : 4 * wn) + j;  // 16-row block of the B quarter
       fb[buf][j] = *reinterpret_cast<const bf16x8_t*>(tb + lane_kc[kk] + 2048 * f);
@@ -776,24 +527,30 @@ gemm_x16_kernel(GemmArgs args) {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
   };
   using L0 = std::integral_constant<int, 0>;
-  constexpr int HALF_LOADS = 8;                 // quarters 0 and 1: 4 instructions each
-  constexpr int TAIL_LOADS = 4 * (NQ - 2);      // quarters 2 (and 3)
+  constexpr int HALF_LOADS = 4 * QS0;          // sub-step 0's quarters: 4 instructions each
+  constexpr int TAIL_LOADS = 4 * (NQ - QS0);    // sub-step 1's
+  constexpr int STEP_LOADS = HALF_LOADS + TAIL_LOADS;
+  // Prefetch distance in K steps: the ring holds 2.5 steps of a 256-row tile
+  // (step k+2's second half reuses step k's first slots) and 5 of a 128-row one
+  // (step k+4 reuses step k-1's, free once every wave has passed step k-1's
+  // mid-step barrier).
+  constexpr int D = BM == 128 ? 4 : 2;
+  static_assert(3 * STEP_LOADS < 64, "vmcnt");
 
   if (nk > 0) {
-    // Prologue: steps 0 and 1 (slots 0-7); wait for step 0.
+    // Prologue: steps 0 .. D-1 (as many as there are); wait for step 0.
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int st = 0; st < D; ++st)
+      if (st < nk) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) load(0, 0, q, i);
-    if (nk > 1) {
+        for (int q = 0; q < NQ; ++q)
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) load(1, 1, q, i);
-      vm_wait(std::integral_constant<int, HALF_LOADS + TAIL_LOADS>{});
-    } else {
-      vm_wait(L0{});
-    }
+          for (int i = 0; i < 4; ++i) load(st, st, q, i);
+      }
+    if (D == 4 && nk >= 4) vm_wait(std::integral_constant<int, 3 * STEP_LOADS>{});
+    else if (D == 4 && nk == 3) vm_wait(std::integral_constant<int, 2 * STEP_LOADS>{});
+    else if (nk >= 2) vm_wait(std::integral_constant<int, STEP_LOADS>{});
+    else vm_wait(L0{});
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -801,33 +558,47 @@ gemm_x16_kernel(GemmArgs args) {
 #pragma unroll
     for (int f = 0; f < FI; ++f) read_a(0, 0, f);
 
-    // K step k with LEFT = min(2, steps after it) known at compile time; r = k % 5.
+    // K step k with LEFT = min(D, steps after it) known at compile time; r = k % 5.
     auto k_step = [&](int k, auto left, int r) {
       constexpr int LEFT = decltype(left)::value;
-      const int r1 = r == 4 ? 0 : r + 1, r2 = r >= 3 ? r - 3 : r + 2;
-      // sub-step 0: reads sub-step 1 of this step; loads quarters 0, 1 of step k+2
-      sub_step(0, true, r, 1, std::integral_constant<int, LEFT >= 2 ? HALF_LOADS : 0>{},
-               [&](int n) { load(k + 2, r2, n >> 2, n & 3); });
+      const int r1 = r == 4 ? 0 : r + 1, rd = (r + D) % 5;
+      // sub-step 0: reads sub-step 1 of this step; loads the quarters of step k+D
+      // whose slots step k does not use
+      sub_step(0, true, r, 1, std::integral_constant<int, LEFT >= D ? HALF_LOADS : 0>{},
+               [&](int n) { load(k + D, rd, n >> 2, n & 3); });
       if constexpr (LEFT >= 1) {
+        // Step k+1 has landed once at most the loads issued after its own are
+        // in flight: whole steps k+2 .. k+D-1 and the part of step k+D just issued.
+        constexpr int WHOLE = LEFT - 1 < D - 2 ? LEFT - 1 : D - 2;
+        constexpr int AFTER = STEP_LOADS * (WHOLE > 0 ? WHOLE : 0) + (LEFT >= D ? HALF_LOADS : 0);
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): sub-step 1's fragments are in registers
-        if constexpr (LEFT >= 2) vm_wait(std::integral_constant<int, HALF_LOADS>{});  // step k+1 has landed
-        else vm_wait(L0{});
+        vm_wait(std::integral_constant<int, AFTER>{});
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
       }
-      // sub-step 1: reads sub-step 0 of step k+1; loads quarters 2, 3 of step k+2
-      sub_step(1, LEFT >= 1, r1, 0, std::integral_constant<int, LEFT >= 2 ? TAIL_LOADS : 0>{},
-               [&](int n) { load(k + 2, r2, 2 + (n >> 2), n & 3); });
+      // sub-step 1: reads sub-step 0 of step k+1; loads the rest of step k+D (for
+      // 256-row tiles into step k's first slots)
+      sub_step(1, LEFT >= 1, r1, 0, std::integral_constant<int, LEFT >= D ? TAIL_LOADS : 0>{},
+               [&](int n) { load(k + D, rd, QS0 + (n >> 2), n & 3); });
     };
-    using Full = std::integral_constant<int, 2>;
+    using Full = std::integral_constant<int, D>;
     int k = 0;
-    for (; k + 7 <= nk; k += 5) {  // steps k .. k+4, each with two more after it
+    for (; k + 5 + D <= nk; k += 5) {  // steps k .. k+4, each with D more after it
 #pragma unroll
       for (int u = 0; u < 5; ++u) k_step(k + u, Full{}, u);
     }
-    for (; k + 2 < nk; ++k) k_step(k, Full{}, k % 5);
-    if (nk >= 2) k_step(nk - 2, std::integral_constant<int, 1>{}, (nk - 2) % 5);
-    k_step(nk - 1, std::integral_constant<int, 0>{}, (nk - 1) % 5);
+    for (; k + D < nk; ++k) k_step(k, Full{}, k % 5);
+    // The last D steps (or all of them, if fewer), each with its own LEFT.
+    auto tail = [&](auto jc) {
+      constexpr int J = decltype(jc)::value;
+      if constexpr (J < D) {
+        if (nk >= J + 1) k_step(nk - 1 - J, std::integral_constant<int, J>{}, (nk - 1 - J) % 5);
+      }
+    };
+    tail(std::integral_constant<int, 3>{});
+    tail(std::integral_constant<int, 2>{});
+    tail(std::integral_constant<int, 1>{});
+    tail(std::integral_constant<int, 0>{});
     vm_wait(L0{});
   }
   // The last MFMAs' results are read below; 32 wait states cover the longest
@@ -836,24 +607,23 @@ gemm_x16_kernel(GemmArgs args) {
   asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
   __syncthreads();  // every wave is done with the operand slots
 
-  // Epilogue, one 64-column half of the wave's sub-tile at a time, staged in the
-  // wave's own 16 KiB of LDS.  Block (i, j) register e holds C[16i + lane%16][16j +
-  // 4 (lane/16) + e] of the wave's sub-tile.
+  // Epilogue, one 64 x 64 chunk of the wave's sub-tile at a time (FI / 4 chunks
+  // tall, FJ / 4 wide), staged in the wave's own 16 KiB of LDS.  Block (i, j)
+  // register e holds C[16i + lane%16][16j + 4 (lane/16) + e] of the wave's
+  // sub-tile.
+  store_staged<EPI, (FI / 4) * (FJ / 4)>(
+      [&](int ch) {
+        const int h = ch % (FI / 4), hc = ch / (FI / 4);
 #pragma unroll
-  for (int hc = 0; hc < FJ / 4; ++hc) {
-    store_staged<EPI, 2>(
-        [&](int h) {
+        for (int ii = 0; ii < 4; ++ii)
 #pragma unroll
-          for (int ii = 0; ii < 4; ++ii)
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-              const int r = 16 * ii + (lane & 15), c = 4 * jj + (lane >> 4);
-              *reinterpret_cast<f32x4_t*>(smem + wave * (64 * ROW_B) + r * ROW_B + ((c ^ (r & 15)) << 4)) =
-                  acc[4 * h + ii][4 * hc + jj];
-            }
-        },
-        args, smem + wave * (64 * ROW_B), m0 + 128 * wm, n0 + (BN / 2) * wn + 64 * hc, split, lane);
-  }
+          for (int jj = 0; jj < 4; ++jj) {
+            const int r = 16 * ii + (lane & 15), c = 4 * jj + (lane >> 4);
+            *reinterpret_cast<f32x4_t*>(smem + wave * (64 * ROW_B) + r * ROW_B + ((c ^ (r & 15)) << 4)) =
+                acc[4 * h + ii][4 * hc + jj];
+          }
+      },
+      args, smem + wave * (64 * ROW_B), m0 + (BM / 2) * wm, n0 + (BN / 2) * wn, FI / 4, split, lane);
 #else
   (void)args;
 #endif
@@ -863,32 +633,31 @@ gemm_x16_kernel(GemmArgs args) {
 
 namespace {
 
-template <int BM, int BN, int WM_, int WN_, int LA, int LB, int EPI>
+template <int BM, int BN, int LB, int EPI>
 hipError_t launch_one(const GemmArgs& a, int splits, hipStream_t s) {
   const int blocks = a.tiles_m * a.tiles_n * splits;
-  if constexpr (BM == 256 && LA == KC)
-    return launch_kernel(kern::gemm_x16_kernel<LB, EPI, BN>, dim3(blocks), dim3(256), s, a);
-  else
-    return launch_kernel(kern::gemm_kernel<BM, BN, WM_, WN_, LA, LB, EPI>, dim3(blocks), dim3(64 * WM_ * WN_), s, a);
+  return launch_kernel(kern::gemm_x16_kernel<LB, EPI, BM, BN>, dim3(blocks), dim3(256), s, a);
 }
 
-template <int BM, int BN, int WM_, int WN_>
+// Every product reads A K-contiguous; B is K- or N-contiguous.
+template <int BM, int BN>
 hipError_t dispatch_layout(Layout la, Layout lb, Epi epi, const GemmArgs& a, int splits, hipStream_t s) {
-  if (la == KC && lb == MC) {
+  if (la != KC) return hipErrorInvalidValue;
+  if (lb == MC) {
     switch (epi) {
-      case EPI_GELU: return launch_one<BM, BN, WM_, WN_, KC, MC, EPI_GELU>(a, splits, s);
-      case EPI_F32: return launch_one<BM, BN, WM_, WN_, KC, MC, EPI_F32>(a, splits, s);
-      case EPI_F32_ACC: return launch_one<BM, BN, WM_, WN_, KC, MC, EPI_F32_ACC>(a, splits, s);
-      case EPI_BF16: return launch_one<BM, BN, WM_, WN_, KC, MC, EPI_BF16>(a, splits, s);
+      case EPI_GELU: return launch_one<BM, BN, MC, EPI_GELU>(a, splits, s);
+      case EPI_F32: return launch_one<BM, BN, MC, EPI_F32>(a, splits, s);
+      case EPI_F32_ACC: return launch_one<BM, BN, MC, EPI_F32_ACC>(a, splits, s);
+      case EPI_BF16: return launch_one<BM, BN, MC, EPI_BF16>(a, splits, s);
       default: break;
     }
-  } else if (la == KC && lb == KC) {
+  } else {
     switch (epi) {
-      case EPI_DGELU: return launch_one<BM, BN, WM_, WN_, KC, KC, EPI_DGELU>(a, splits, s);
-      case EPI_F32: return launch_one<BM, BN, WM_, WN_, KC, KC, EPI_F32>(a, splits, s);
-      case EPI_F32_ACC: return launch_one<BM, BN, WM_, WN_, KC, KC, EPI_F32_ACC>(a, splits, s);
-      case EPI_GELU: return launch_one<BM, BN, WM_, WN_, KC, KC, EPI_GELU>(a, splits, s);
-      case EPI_BF16: return launch_one<BM, BN, WM_, WN_, KC, KC, EPI_BF16>(a, splits, s);
+      case EPI_DGELU: return launch_one<BM, BN, KC, EPI_DGELU>(a, splits, s);
+      case EPI_F32: return launch_one<BM, BN, KC, EPI_F32>(a, splits, s);
+      case EPI_F32_ACC: return launch_one<BM, BN, KC, EPI_F32_ACC>(a, splits, s);
+      case EPI_GELU: return launch_one<BM, BN, KC, EPI_GELU>(a, splits, s);
+      case EPI_BF16: return launch_one<BM, BN, KC, EPI_BF16>(a, splits, s);
       default: break;
     }
   }
@@ -903,9 +672,9 @@ int tile_bn(TileCfg t) { return t == TILE_256x256 ? 256 : 128; }
 hipError_t launch_gemm(TileCfg tile, Layout la, Layout lb, Epi epi, const GemmArgs& args, int splits,
                        hipStream_t stream) {
   switch (tile) {
-    case TILE_256x256: return dispatch_layout<256, 256, 2, 2>(la, lb, epi, args, splits, stream);
-    case TILE_128x128: return dispatch_layout<128, 128, 2, 2>(la, lb, epi, args, splits, stream);
-    case TILE_256x128: return dispatch_layout<256, 128, 2, 2>(la, lb, epi, args, splits, stream);
+    case TILE_256x256: return dispatch_layout<256, 256>(la, lb, epi, args, splits, stream);
+    case TILE_128x128: return dispatch_layout<128, 128>(la, lb, epi, args, splits, stream);
+    case TILE_256x128: return dispatch_layout<256, 128>(la, lb, epi, args, splits, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -75,14 +75,14 @@ struct GemmPlan {
 int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
 // Time model used to pick a tile and a split-K count: workgroups run in waves
-// over the chip's slots (one 256x256 block or two 128x128 blocks per CU); a
+// over the chip's CUs (one block per CU: every tile takes the whole LDS); a
 // block's time is proportional to its MACs at the measured per-CU rate of its
-// tile; split-K adds a float32 round trip of the slices through memory and
-// one reduction launch.  Splits keep at least 512 of K each.
-constexpr double CU_RATE_256 = 4.3e12;   // flop/s per CU, 256x256 tile
-constexpr double CU_RATE_256x128 = 3.8e12;  // flop/s per CU, 256x128 tile (same kernel, half the MFMAs per load)
-constexpr double CU_RATE_128 = 1.3e12;   // flop/s per 128x128 block, two per CU
-constexpr double SPLIT_BW = 4.0e12;      // bytes/s for the slices' write and re-read
+// tile; split-K adds a float32 round trip of the slices through memory and one
+// reduction launch.  Splits keep at least 512 of K each.
+constexpr double CU_RATE_256 = 4.3e12;      // flop/s per CU, 256x256 tile
+constexpr double CU_RATE_256x128 = 3.8e12;  // flop/s per CU, 256x128 tile (half the MFMAs per load)
+constexpr double CU_RATE_128 = 3.3e12;      // flop/s per CU, 128x128 tile (a quarter)
+constexpr double SPLIT_BW = 4.0e12;         // bytes/s for the slices' write and re-read
 constexpr double LAUNCH_S = 5e-6;
 
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
@@ -91,15 +91,15 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
   for (TileCfg tile : {TILE_256x256, TILE_256x128, TILE_128x128}) {
     const int64_t bm = tile_bm(tile), bn = tile_bn(tile);
     const int64_t tiles = (int64_t)ceil_div(M, bm) * ceil_div(N, bn);
-    const int64_t slots = tile == TILE_128x128 ? 2 * NUM_CU : NUM_CU;
-    const double rate = tile == TILE_256x256 ? CU_RATE_256 : tile == TILE_256x128 ? CU_RATE_256x128 : CU_RATE_128;
     for (int s = 1; s <= 16; ++s) {
       const int64_t kslice = ((K + s - 1) / s + TILE_BK - 1) / TILE_BK * TILE_BK;
       const int splits = ceil_div(K, kslice);
       if (splits != s) continue;
       if (s > 1 && kslice < 512) break;
-      const int64_t waves = (tiles * s + slots - 1) / slots;
-      double t = double(waves) * double(bm * bn * 2 * kslice) / rate;
+      const double flops = double(bm * bn * 2 * kslice);
+      const int64_t blocks = tiles * s;
+      const double rate = tile == TILE_256x256 ? CU_RATE_256 : tile == TILE_256x128 ? CU_RATE_256x128 : CU_RATE_128;
+      double t = double((blocks + NUM_CU - 1) / NUM_CU) * flops / rate;
       if (s > 1) t += double(s) * M * N * 4 * 2 / SPLIT_BW + LAUNCH_S;
       if (t < best_t * (1 - 1e-9)) {
         best_t = t;

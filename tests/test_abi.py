@@ -177,8 +177,8 @@ def test_fwd_noalloc_argument_errors():
         assert L.tpmlp_fwd_workspace_bytes(M, H, F) > L.NOALLOC_SCRATCH_BYTES
         st, msg = _fwd_noalloc(M=M, H=H, F=F)
         assert st == WS and "TPMLP_NOALLOC_SCRATCH_BYTES" in msg
-    # the largest of the benchmark shapes that fits uses all of it
-    assert L.tpmlp_fwd_workspace_bytes(4096, 1024, 4096) == L.NOALLOC_SCRATCH_BYTES
+    # the GPT-2-medium-like shape fits
+    assert L.tpmlp_fwd_workspace_bytes(4096, 1024, 4096) <= L.NOALLOC_SCRATCH_BYTES
     assert _fwd_noalloc(M=4096, H=1024, F=4096)[0] in (HIP, UNSUP)  # no GPU here
 
 

@@ -22,10 +22,10 @@ def _need_gpu():
     L.lib()
 
 
-# First a shape whose forward takes the two products with a split-K slice
-# buffer (the workspace fills most of the 64 MiB), then a smaller one that takes
-# the fused small-H kernel with several chunk partials, then a mid-size one.
-SHAPES = [(4096, 1024, 4096), (200, 192, 392), (1000, 520, 776)]
+# First a shape whose forward takes the two products, the second split along K
+# into a slice buffer (48 of the 64 MiB), then a smaller one that takes the
+# fused small-H kernel with several chunk partials, then a mid-size one.
+SHAPES = [(1024, 1024, 16384), (200, 192, 392), (1000, 520, 776)]
 
 
 def test_noalloc_matches_workspace_forward():
