@@ -400,7 +400,14 @@ gemm_x16_kernel(GemmArgs args) {
   constexpr int NQ = NA + BN / 128;         // quarters loaded per K step
   constexpr int NSLOT = 10;
   constexpr int SPS = BM == 128 ? 2 : 4;    // ring slots per K step
-  constexpr int QS0 = NA;                   // quarters loaded in sub-step 0; the rest in sub-step 1
+  constexpr int P = 5;                      // ring period in K steps (SPS P = 0 mod 10)
+  // Prefetch distance in K steps: as far as the ring allows.  Step k+D takes
+  // step k-1's last slots (free once every wave has passed step k-1's mid-step
+  // barrier) and, for 256-row tiles, step k's first ones (free after step k's).
+  // (Packing 256 x 128 steps into three slots for a distance of 3 needs a
+  // period of 10 steps, and measured slower.)
+  constexpr int D = BM == 128 ? 4 : 2;
+  constexpr int QS0 = BM == 128 ? 1 : 2;    // quarters of step k+D loaded in sub-step 0
   constexpr int FI = BM / 32, FJ = BN / 32;  // 16 x 16 blocks per wave: FI x FJ
   static_assert(BK == 64 && NSLOT * SLOT == 160 * 1024, "ten 16 KiB slots fill the LDS");
   __shared__ __attribute__((aligned(1024))) char smem[NSLOT * SLOT];
@@ -428,7 +435,7 @@ gemm_x16_kernel(GemmArgs args) {
   }
 
   auto slot = [&](int r, int q) -> char* { return smem + ((SPS * r + q) % NSLOT) * SLOT; };
-  // Instruction i of this wave's share of quarter q of K step `step` (r = step % 5).
+  // Instruction i of this wave's share of quarter q of K step `step` (r = step % P).
   auto load = [&](int step, int r, int q, int i) {
     if (q >= NQ) return;
     const int k = k_begin + step * BK;
@@ -530,12 +537,7 @@ gemm_x16_kernel(GemmArgs args) {
   constexpr int HALF_LOADS = 4 * QS0;          // sub-step 0's quarters: 4 instructions each
   constexpr int TAIL_LOADS = 4 * (NQ - QS0);    // sub-step 1's
   constexpr int STEP_LOADS = HALF_LOADS + TAIL_LOADS;
-  // Prefetch distance in K steps: the ring holds 2.5 steps of a 256-row tile
-  // (step k+2's second half reuses step k's first slots) and 5 of a 128-row one
-  // (step k+4 reuses step k-1's, free once every wave has passed step k-1's
-  // mid-step barrier).
-  constexpr int D = BM == 128 ? 4 : 2;
-  static_assert(3 * STEP_LOADS < 64, "vmcnt");
+  static_assert((D - 1) * STEP_LOADS < 64, "vmcnt");
 
   if (nk > 0) {
     // Prologue: steps 0 .. D-1 (as many as there are); wait for step 0.
@@ -547,8 +549,8 @@ gemm_x16_kernel(GemmArgs args) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) load(st, st, q, i);
       }
-    if (D == 4 && nk >= 4) vm_wait(std::integral_constant<int, 3 * STEP_LOADS>{});
-    else if (D == 4 && nk == 3) vm_wait(std::integral_constant<int, 2 * STEP_LOADS>{});
+    if (D >= 4 && nk >= 4) vm_wait(std::integral_constant<int, (D >= 4 ? 3 : 0) * STEP_LOADS>{});
+    else if (D >= 3 && nk >= 3) vm_wait(std::integral_constant<int, (D >= 3 ? 2 : 0) * STEP_LOADS>{});
     else if (nk >= 2) vm_wait(std::integral_constant<int, STEP_LOADS>{});
     else vm_wait(L0{});
     __builtin_amdgcn_s_barrier();
@@ -558,10 +560,10 @@ gemm_x16_kernel(GemmArgs args) {
 #pragma unroll
     for (int f = 0; f < FI; ++f) read_a(0, 0, f);
 
-    // K step k with LEFT = min(D, steps after it) known at compile time; r = k % 5.
+    // K step k with LEFT = min(D, steps after it) known at compile time; r = k % P.
     auto k_step = [&](int k, auto left, int r) {
       constexpr int LEFT = decltype(left)::value;
-      const int r1 = r == 4 ? 0 : r + 1, rd = (r + D) % 5;
+      const int r1 = r == P - 1 ? 0 : r + 1, rd = (r + D) % P;
       // sub-step 0: reads sub-step 1 of this step; loads the quarters of step k+D
       // whose slots step k does not use
       sub_step(0, true, r, 1, std::integral_constant<int, LEFT >= D ? HALF_LOADS : 0>{},
@@ -583,16 +585,16 @@ gemm_x16_kernel(GemmArgs args) {
     };
     using Full = std::integral_constant<int, D>;
     int k = 0;
-    for (; k + 5 + D <= nk; k += 5) {  // steps k .. k+4, each with D more after it
+    for (; k + P + D <= nk; k += P) {  // steps k .. k+P-1, each with D more after it
 #pragma unroll
-      for (int u = 0; u < 5; ++u) k_step(k + u, Full{}, u);
+      for (int u = 0; u < P; ++u) k_step(k + u, Full{}, u);
     }
-    for (; k + D < nk; ++k) k_step(k, Full{}, k % 5);
+    for (; k + D < nk; ++k) k_step(k, Full{}, k % P);
     // The last D steps (or all of them, if fewer), each with its own LEFT.
     auto tail = [&](auto jc) {
       constexpr int J = decltype(jc)::value;
       if constexpr (J < D) {
-        if (nk >= J + 1) k_step(nk - 1 - J, std::integral_constant<int, J>{}, (nk - 1 - J) % 5);
+        if (nk >= J + 1) k_step(nk - 1 - J, std::integral_constant<int, J>{}, (nk - 1 - J) % P);
       }
     };
     tail(std::integral_constant<int, 3>{});
