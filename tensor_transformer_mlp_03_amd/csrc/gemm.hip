@@ -204,11 +204,16 @@ __device__ __forceinline__ void tile_of(int bid, int nblocks, int tiles_m, int t
 // are the first output row and column of the wave's (32 FM) x 64 tile.
 constexpr int ROW_B = 256;  // staged row stride in bytes (64 float32)
 
-// Chunk swizzle of the bf16 G rows that the dGeLU epilogue keeps in staging
-// rows.  A transposing read of a 16-lane group takes rows b + 8 q + r (q, r < 4)
-// at one column chunk; shifting the chunk by r + 4 q spreads them over 8
-// positions, two lanes per bank pair (the same as the row-contiguous reads).
-__device__ __forceinline__ int gt_swz(int r) { return (r + 4 * (r >> 3)) & 7; }
+// The dGeLU epilogue keeps the bf16 G rows of a chunk in its staging bytes at a
+// 128-byte pitch (rows 2i and 2i+1 share one 256-byte line, so a store of two
+// rows covers all 64 banks), 16-byte chunks swizzled by the row.  A transposing
+// read of a 16-lane group takes rows b + 8 q + r (q, r < 4; b a multiple of 32)
+// at one column chunk: for each parity of r those are 8 rows, and the swizzle
+// puts them on 8 distinct chunks (one bank half per parity); the two groups that
+// share a 32-lane half read different 8-byte halves of their chunks, so every
+// read and store is free of bank conflicts.
+__device__ __forceinline__ int gt_swz(int r) { return ((r >> 3) + 4 * ((r >> 1) & 1)) & 7; }
+constexpr int G_ROW_B = 128;  // staged G row pitch in bytes
 
 // The epilogue proper, independent of the MFMA accumulator layout.  The wave's
 // region is NC chunks of 64 x 64, laid out nh chunks tall: chunk c covers rows
@@ -320,37 +325,38 @@ __device__ __forceinline__ void store_staged(StageChunk&& stage_chunk, const Gem
             v2[e] = d.g;
           }
           if (ok) *reinterpret_cast<u16x8_t*>(reinterpret_cast<uint16_t*>(args.out) + o) = v1;
-          // Keep G of this row in LDS, in place of its float32 values (every
-          // lane has read its float32 values above), in bytes [0, 128) of the
-          // row, 16-byte chunks swizzled by the row (gt_swz).  Rows and columns
-          // outside the output hold values that no transposed store below reads.
-          *reinterpret_cast<u16x8_t*>(stage + r * ROW_B + ((cp ^ gt_swz(r)) << 4)) = v2;
+          // Keep G of this row in LDS, over the chunk's float32 values (the
+          // wave has read all of them above, and its LDS accesses complete in
+          // order), at G_ROW_B pitch, 16-byte chunks swizzled by the row
+          // (gt_swz).  Rows and columns outside the output hold values that no
+          // transposed store below reads.
+          *reinterpret_cast<u16x8_t*>(stage + r * G_ROW_B + ((cp ^ gt_swz(r)) << 4)) = v2;
         }
       }
       if (EPI == EPI_DGELU) {
         // Transposed store of G in whole 128-byte lines.  ds_read_b64_tr_b16
         // takes, in each 16-lane group, 4 rows x 16 columns (source lane 4 r + q:
         // row r, columns 4 q .. +3) and hands lane i column i.  Source lane
-        // 4 r + q reads the 4 columns 8 it + 4 (g / 2) .. +3 of G row
-        // m0(q) + r, with m0(q) = 32 (g % 2) + 8 q, so lane 4 q + e receives
-        // rows m0(q) .. +3 of column 8 it + 4 (g / 2) + e; a second read gives
-        // rows +4 .. +7.  The 8 lanes (g % 2, q) of a column then hold its 64
+        // 4 r + q reads the 4 columns 8 it + 4 (g % 2) .. +3 of G row
+        // m0(q) + r, with m0(q) = 32 (g / 2) + 8 q, so lane 4 q + e receives
+        // rows m0(q) .. +3 of column 8 it + 4 (g % 2) + e; a second read gives
+        // rows +4 .. +7.  The 8 lanes (g / 2, q) of a column then hold its 64
         // rows: one store instruction writes 8 columns x 128 bytes of G^T.  All
         // eight steps are read first, then stored.
         const int g = lane >> 4, j = lane & 15, jq = j & 3, jr = j >> 2;
-        const int half = (g >> 1) ? 8 : 0;
+        const int half = (g & 1) ? 8 : 0;
         i16x4_t lo[8], hi[8];
 #pragma unroll
         for (int it = 0; it < 8; ++it) {
-          const int ka = 32 * (g & 1) + 8 * jq + jr, kb = ka + 4;  // source role: q = jq, r = jr
-          lo[it] = ds_read_tr_after_stores(stage + ka * ROW_B + ((it ^ gt_swz(ka)) << 4) + half);
-          hi[it] = ds_read_tr_after_stores(stage + kb * ROW_B + ((it ^ gt_swz(kb)) << 4) + half);
+          const int ka = 32 * (g >> 1) + 8 * jq + jr, kb = ka + 4;  // source role: q = jq, r = jr
+          lo[it] = ds_read_tr_after_stores(stage + ka * G_ROW_B + ((it ^ gt_swz(ka)) << 4) + half);
+          hi[it] = ds_read_tr_after_stores(stage + kb * G_ROW_B + ((it ^ gt_swz(kb)) << 4) + half);
         }
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the transposed reads above are complete
 #pragma unroll
         for (int it = 0; it < 8; ++it) {
           // destination role: lane 4 q + e with q = jr, e = jq
-          const int f = col_c + 8 * it + 4 * (g >> 1) + jq, m = row_w + 64 * h + 32 * (g & 1) + 8 * jr;
+          const int f = col_c + 8 * it + 4 * (g & 1) + jq, m = row_w + 64 * h + 32 * (g >> 1) + 8 * jr;
           if (f < args.N && m < args.M) {
             const u16x8_t v = {(uint16_t)lo[it][0], (uint16_t)lo[it][1], (uint16_t)lo[it][2], (uint16_t)lo[it][3],
                                (uint16_t)hi[it][0], (uint16_t)hi[it][1], (uint16_t)hi[it][2], (uint16_t)hi[it][3]};
