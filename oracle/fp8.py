@@ -19,10 +19,14 @@ The pages give no scaling recipe.  The one taken here (per-tensor current scalin
 * its value in a product is decode(q) * s.
 
 E4M3 carries the activations and weights (X, A_i, B_i, G_i), E5M2 the gradients (dZ,
-dP_i).  Products accumulate exactly here (float64) from the dequantized operands;
-the GeLU and its derivative take the float64 pre-activation.  Where the rounding of
-a float32 product decides a code, the oracle rounds in float32 exactly as stated
-above, so quantizing the same float32 tensor gives the same bytes on both sides.
+dP_i).  Products accumulate exactly here (float64) from the dequantized operands.
+The pre-activation P_i and the gradient dP_i are held in bf16 between the products,
+as in the bf16 path (its reading of the intermediate precision): G_i = GeLU(bf16(P_i))
+is what gets quantized, dP_i = bf16(dG_i GeLU'(bf16(P_i))) likewise, each value
+rounded to float32 first and then to bf16 (nearest, ties to even).  Where the
+rounding of a float32 product decides a code, the oracle rounds in float32 exactly
+as stated above, so quantizing the same float32 tensor gives the same bytes on both
+sides.
 """
 from __future__ import annotations
 
@@ -112,6 +116,14 @@ def quantize(T: np.ndarray, fmt: Fp8Format) -> Tuple[np.ndarray, np.float32]:
     return encode(t32 * inv, fmt), s
 
 
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """x rounded to float32, then to bf16 (nearest, ties to even), as float64."""
+    f = np.asarray(x, dtype=np.float32)
+    b = f.view(np.uint32).astype(np.uint64)
+    b = ((b + np.uint64(0x7FFF) + ((b >> np.uint64(16)) & np.uint64(1))) >> np.uint64(16)) << np.uint64(16)
+    return b.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
 def dequant(codes: np.ndarray, s, fmt: Fp8Format) -> np.ndarray:
     return decode(codes, fmt) * np.float64(s)
 
@@ -127,24 +139,24 @@ def qdq(T: np.ndarray, fmt: Fp8Format) -> np.ndarray:
 # its operands through qdq)
 # ---------------------------------------------------------------------------
 def mlp_forward_fp8(X: np.ndarray, A_i: np.ndarray, B_i: np.ndarray) -> Dict[str, np.ndarray]:
-    """P_i = qdq(X) qdq(A_i); G_i = GeLU(P_i); Z_i = qdq(G_i) qdq(B_i)."""
+    """P_i = bf16(qdq(X) qdq(A_i)); G_i = GeLU(P_i); Z_i = qdq(G_i) qdq(B_i)."""
     Xq, Aq, Bq = qdq(X, E4M3), qdq(A_i, E4M3), qdq(B_i, E4M3)
-    P = Xq @ Aq
+    P = round_bf16(Xq @ Aq)
     G = gelu(P)
     Gq = qdq(G, E4M3)
     return {"P": P, "G": G, "Gq": Gq, "Z": Gq @ Bq}
 
 
 def mlp_backward_fp8(dZ: np.ndarray, X: np.ndarray, A_i: np.ndarray, B_i: np.ndarray) -> Dict[str, np.ndarray]:
-    """dG_i = qdq5(dZ) qdq(B_i)^T; dP_i = dG_i GeLU'(P_i); with dPq = qdq5(dP_i):
+    """dG_i = qdq5(dZ) qdq(B_i)^T; dP_i = bf16(dG_i GeLU'(P_i)); with dPq = qdq5(dP_i):
     dB_i = qdq(G_i)^T qdq5(dZ), dA_i = qdq(X)^T dPq, dX_i = dPq qdq(A_i)^T."""
     f = mlp_forward_fp8(X, A_i, B_i)
     Xq, Aq, Bq = qdq(X, E4M3), qdq(A_i, E4M3), qdq(B_i, E4M3)
     dZq = qdq(dZ, E5M2)
     dG = dZq @ Bq.T
-    dP = dG * gelu_grad(f["P"])
+    dP = round_bf16(dG * gelu_grad(f["P"]))
     dPq = qdq(dP, E5M2)
-    return {"P": f["P"], "dP": dP, "dB": f["Gq"].T @ dZq, "dA": Xq.T @ dPq, "dX": dPq @ Aq.T}
+    return {"P": f["P"], "dG": dG, "dP": dP, "dB": f["Gq"].T @ dZq, "dA": Xq.T @ dPq, "dX": dPq @ Aq.T}
 
 
 def _rank_order_sum(parts: Sequence[np.ndarray]) -> np.ndarray:

@@ -9,8 +9,9 @@ implementations fix, CPU only.
 * The scaling recipe: the largest element maps to +-FMAX, and scaling a tensor by a
   power of two changes its scale and not its codes.
 * The FP8 path: its outputs stay within a first-order error bound, derived from the
-  formats' rounding bounds and the products' structure, of the exact (float64,
-  unquantized) oracle, and do differ from it.
+  formats' rounding bounds, the bf16 rounding of P and dP, and the products'
+  structure, of the exact (float64, unquantized) oracle, and do differ from it.
+* bf16 rounding: round_bf16 against torch's float32 -> bfloat16 conversion.
 """
 import numpy as np
 import pytest
@@ -115,6 +116,7 @@ def _inputs(seed, M=48, H=64, Fi=80):
 
 
 L_GELU, L_DGELU = 1.1290, 0.7980  # max |GeLU'| and max |GeLU''| (= 2 phi(0))
+U16 = 2.0 ** -8  # bound of the relative rounding of float64 -> float32 -> bf16 (half a bf16 ulp, plus slack)
 
 
 def test_fp8_path_within_error_bound_of_exact():
@@ -126,7 +128,7 @@ def test_fp8_path_within_error_bound_of_exact():
     ab = np.abs
     EX, EA, EB = _qbound(X, F.E4M3), _qbound(A, F.E4M3), _qbound(B, F.E4M3)
     Xq, Aq, Bq = ab(X) + EX, ab(A) + EA, ab(B) + EB          # bounds of |qdq(.)|
-    EP = EX @ Aq + ab(X) @ EA                               # |P_fp8 - P|
+    EP = EX @ Aq + ab(X) @ EA + U16 * ab(f["P"]) * (1 + U16)  # |bf16(P_fp8) - P|
     G8 = O.gelu(f["P"])
     EGq = _qbound(G8, F.E4M3) + L_GELU * EP                 # |qdq(G(P_fp8)) - G(P)|
     EZ = EGq @ Bq + ab(ex_f["G"]) @ EB
@@ -136,7 +138,7 @@ def test_fp8_path_within_error_bound_of_exact():
     dZq = ab(dZ) + EdZ
     EdG = EdZ @ Bq.T + ab(dZ) @ EB.T
     dG8 = (F.qdq(dZ, F.E5M2)) @ F.qdq(B, F.E4M3).T
-    EdPpre = EdG * np.abs(O.gelu_grad(f["P"])) + ab(ex_b["dG"]) * L_DGELU * EP
+    EdPpre = (EdG * np.abs(O.gelu_grad(f["P"])) + ab(ex_b["dG"]) * L_DGELU * EP) + U16 * ab(b["dP"]) * (1 + U16)
     EdP = _qbound(b["dP"], F.E5M2) + EdPpre
     assert np.all(ab(b["dP"] - ex_b["dP"]) <= tol(EdPpre))
     dPq = ab(ex_b["dP"]) + EdP
@@ -180,3 +182,10 @@ def test_fp8_forward_closed_form_two_tokens():
     assert abs(Z[1] - 192.0 / 448.0 * phi1) < 1e-6
     assert abs(Z[1] - 0.5 * phi05) > 1e-2  # not the unquantized GeLU(0.5)
     assert abs(0.5 * phi05 * 448 / phi1 - 184.0953) < 1e-3
+
+
+def test_round_bf16_matches_torch():
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal(200000) * np.exp2(rng.integers(-30, 30, 200000))
+    ref = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).float().numpy().astype(np.float64)
+    assert np.array_equal(F.round_bf16(x), ref)
