@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define TPMLP_ABI_VERSION 9
+#define TPMLP_ABI_VERSION 10
 #define TPMLP_MAX_SHARDS 64
 
 typedef uint16_t tpmlp_bf16; /* raw bf16 bits */
@@ -253,6 +253,51 @@ tpmlp_status tpmlp_sp_bwd(const tpmlp_bf16* const* dZ_sl, const tpmlp_bf16* cons
                           void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* The t-shard driver with FP8 operands                                      */
+/* ------------------------------------------------------------------------ */
+/* The same products as tpmlp_tp_fwd / tpmlp_tp_bwd with every operand in one of
+ * the two 8-bit float formats of the "大模型训练" notes (§6.1 数据类型对比): E4M3
+ * (4 exponent, 3 mantissa bits, range +-448) for the activations and weights X,
+ * A_i, B_i and G_i, E5M2 (5 and 2 bits, range +-57344) for the gradients dZ and
+ * dP_i.  The encodings are the OCP ones those ranges imply (E4M3: bias 7, no
+ * infinities; E5M2: bias 15, IEEE specials).  The pages give no scaling recipe;
+ * the one used is per-tensor current scaling: a tensor T's scale is
+ * s = amax|T| / FMAX (1 if T is all zero), its codes are fp8(T * (1/s)) with the
+ * product rounded to float32, then to the nearest FP8 value (ties to even),
+ * saturating at +-FMAX; a product of two tensors accumulates the codes'
+ * products in float32 and multiplies the sum by the two scales.  G_i is
+ * quantized from GeLU of the bf16 pre-activation P_i, dP_i from its bf16 value.
+ * Inputs, outputs and the bf16 P_i are as in tpmlp_tp_fwd / tpmlp_tp_bwd (the
+ * rank sums of Z and dX are always formed by the drivers, rank order 0..t-1).
+ *
+ * M, H and F_i must be positive multiples of 16, at most 2^23 (TPMLP_ERR_SHAPE).
+ * The workspace (tpmlp_fp8_workspace_bytes, for either call) holds the FP8
+ * copies of the operands, the amax slots and the split-K slices. */
+size_t tpmlp_fp8_workspace_bytes(int t, int64_t M, int64_t H, int64_t F_i);
+
+/* Z = sum_i Z_i with FP8 operands.  P_sh: NULL, or t entries (each nullable)
+ * receiving P_i [M, F_i] bf16 for a backward that keeps it. */
+tpmlp_status tpmlp_fp8_tp_fwd(const tpmlp_bf16* X, const tpmlp_bf16* const* A_sh, const tpmlp_bf16* const* B_sh,
+                              tpmlp_bf16* const* P_sh, float* Z, int t, int64_t M, int64_t H, int64_t F_i,
+                              void* ws, size_t ws_bytes, void* stream);
+
+/* Backward with FP8 operands: dA_sh[i], dB_sh[i] (float32, shard i's weight
+ * gradients) and dX = sum_i dX_i (float32).  P_sh: NULL => every shard
+ * recomputes P_i with the FP8 forward product; otherwise t device pointers
+ * written by tpmlp_fp8_tp_fwd. */
+tpmlp_status tpmlp_fp8_tp_bwd(const tpmlp_bf16* dZ, const tpmlp_bf16* X, const tpmlp_bf16* const* A_sh,
+                              const tpmlp_bf16* const* B_sh, const tpmlp_bf16* const* P_sh,
+                              float* const* dA_sh, float* const* dB_sh, float* dX, int t, int64_t M, int64_t H,
+                              int64_t F_i, void* ws, size_t ws_bytes, void* stream);
+
+/* FP8 codes of one bf16 tensor T[R, C] under the scaling above: *amax (device
+ * float, overwritten) receives max|T|, and codes[R, C] (or codes[C, R] with
+ * transpose != 0, row-major bytes) its codes in format fmt (0: E4M3, 1: E5M2).
+ * R and C positive multiples of 16; T, codes and amax 16-byte aligned. */
+tpmlp_status tpmlp_fp8_quantize(const tpmlp_bf16* T, int64_t R, int64_t C, int fmt, int transpose,
+                                uint8_t* codes, float* amax, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* Forward without allocation or workspace                                  */
 /* ------------------------------------------------------------------------ */
 
@@ -294,7 +339,8 @@ typedef enum {
   TPMLP_K_SHARD_SUM = 8,      /* tpmlp_shard_sum and the drivers' partial sums */
   TPMLP_K_TRANSPOSE = 9,      /* X^T and dZ^T for the weight-gradient products */
   TPMLP_K_FWD_FUSED = 10,     /* Z_i chunk partials = GeLU(X A_i) B_i in one launch, G in LDS */
-  TPMLP_K_COUNT = 11
+  TPMLP_K_FP8_QUANT = 11,     /* FP8 drivers: amax and quantization of operands */
+  TPMLP_K_COUNT = 12
 } tpmlp_kernel_kind;
 
 /* Static name of a kernel kind ("?" if out of range). */

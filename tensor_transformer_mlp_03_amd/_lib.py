@@ -25,7 +25,7 @@ STATUS = {
     4: "TPMLP_ERR_WORKSPACE", 5: "TPMLP_ERR_SHARDS", 6: "TPMLP_ERR_HIP",
     7: "TPMLP_ERR_UNSUPPORTED", 8: "TPMLP_ERR_ALIAS",
 }
-KERNEL_COUNT = 11
+KERNEL_COUNT = 12
 MAX_SHARDS = 64
 
 
@@ -61,6 +61,10 @@ _SIGS = {
     "tpmlp_sp_workspace_bytes": ([_int, _i64, _i64, _i64], _sz),
     "tpmlp_sp_fwd": ([_PP, _PP, _PP, _PP, _PP, _int, _i64, _i64, _i64, _vp, _sz, _vp], _int),
     "tpmlp_sp_bwd": ([_PP, _PP, _PP, _PP, _PP, _PP, _PP, _PP, _int, _i64, _i64, _i64, _vp, _sz, _vp], _int),
+    "tpmlp_fp8_workspace_bytes": ([_int, _i64, _i64, _i64], _sz),
+    "tpmlp_fp8_tp_fwd": ([_vp, _PP, _PP, _PP, _vp, _int, _i64, _i64, _i64, _vp, _sz, _vp], _int),
+    "tpmlp_fp8_tp_bwd": ([_vp, _vp, _PP, _PP, _PP, _PP, _PP, _vp, _int, _i64, _i64, _i64, _vp, _sz, _vp], _int),
+    "tpmlp_fp8_quantize": ([_vp, _i64, _i64, _int, _int, _vp, _vp, _vp], _int),
     "tpmlp_timing_begin": ([_int], _int),
     "tpmlp_timing_begin_kinds": ([_int, ctypes.c_uint], _int),
     "tpmlp_timing_end": ([ctypes.POINTER(_int), ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_int)], _int),
@@ -376,6 +380,58 @@ def tpmlp_shard_sum(parts, out, stream=None):
             raise ValueError(f"parts[{i}] holds {p.numel()} elements, out {out.numel()}")
     st = lib().tpmlp_shard_sum(_ptr_array(parts, t), t, _ptr(out), out.numel(), _stream(stream))
     _check(st, "tpmlp_shard_sum")
+
+
+def tpmlp_fp8_workspace_bytes(t: int, M: int, H: int, F_i: int) -> int:
+    return lib().tpmlp_fp8_workspace_bytes(t, M, H, F_i)
+
+
+def tpmlp_fp8_tp_fwd(X, A_sh, B_sh, P_sh, Z, ws, stream=None):
+    """The t-shard forward with FP8 operands (per-tensor scaling), Z[M,H] float32."""
+    t = len(A_sh)
+    M, H = X.shape
+    F = A_sh[0].shape[1]
+    _bf16(X, "X"), _f32(Z, "Z"), _shape(Z, (M, H), "Z")
+    _shards(A_sh, t, (H, F), "A_sh", _bf16)
+    _shards(B_sh, t, (F, H), "B_sh", _bf16)
+    _shards(P_sh, t, (M, F), "P_sh", _bf16, nullable=True)
+    st = lib().tpmlp_fp8_tp_fwd(_ptr(X), _ptr_array(A_sh, t), _ptr_array(B_sh, t), _ptr_array(P_sh, t), _ptr(Z),
+                                t, M, H, F, _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "tpmlp_fp8_tp_fwd")
+
+
+def tpmlp_fp8_tp_bwd(dZ, X, A_sh, B_sh, P_sh, dA_sh, dB_sh, dX, ws, stream=None):
+    """The t-shard backward with FP8 operands; P_sh None recomputes P_i."""
+    t = len(A_sh)
+    M, H = X.shape
+    F = A_sh[0].shape[1]
+    _bf16(dZ, "dZ"), _shape(dZ, (M, H), "dZ"), _bf16(X, "X"), _f32(dX, "dX"), _shape(dX, (M, H), "dX")
+    _shards(A_sh, t, (H, F), "A_sh", _bf16)
+    _shards(B_sh, t, (F, H), "B_sh", _bf16)
+    _shards(P_sh, t, (M, F), "P_sh", _bf16)
+    _shards(dA_sh, t, (H, F), "dA_sh", _f32)
+    _shards(dB_sh, t, (F, H), "dB_sh", _f32)
+    st = lib().tpmlp_fp8_tp_bwd(_ptr(dZ), _ptr(X), _ptr_array(A_sh, t), _ptr_array(B_sh, t), _ptr_array(P_sh, t),
+                                _ptr_array(dA_sh, t), _ptr_array(dB_sh, t), _ptr(dX), t, M, H, F, _ptr(ws),
+                                ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "tpmlp_fp8_tp_bwd")
+
+
+def tpmlp_fp8_quantize(T, fmt: int, transpose: bool, codes, amax, stream=None):
+    """FP8 codes of a bf16 tensor T[R,C] (uint8 codes [R,C], or [C,R] transposed) and
+    its amax (one float32 element, overwritten)."""
+    import torch
+    R, C = T.shape
+    _bf16(T, "T")
+    if codes.dtype != torch.uint8 or not codes.is_contiguous():
+        raise TypeError("codes must be a contiguous uint8 tensor")
+    _shape(codes, (C, R) if transpose else (R, C), "codes")
+    _f32(amax, "amax")
+    if amax.numel() != 1:
+        raise ValueError("amax must hold one float32")
+    st = lib().tpmlp_fp8_quantize(_ptr(T), R, C, int(fmt), 1 if transpose else 0, _ptr(codes), _ptr(amax),
+                                  _stream(stream))
+    _check(st, "tpmlp_fp8_quantize")
 
 
 def tpmlp_timing_begin(capacity: int):

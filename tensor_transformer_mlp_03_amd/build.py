@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libtpmlp.so")
-SOURCES = ["gemm.hip", "reduce.hip", "ffn.hip", "tpmlp.hip"]
+SOURCES = ["gemm.hip", "reduce.hip", "ffn.hip", "fp8.hip", "tpmlp.hip"]
 
 ARCH = "gfx950"
 CFLAGS = [

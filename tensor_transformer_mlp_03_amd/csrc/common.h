@@ -68,6 +68,14 @@ struct GemmArgs {
   int64_t ldt;        // leading dimension of EPI_DGELU's transposed outputs
   int64_t split_stride;  // elements between split-K partial outputs
   int tiles_m, tiles_n;  // output tiles along M and N
+  // FP8 products only (gemm kernels instantiated with operand formats): the
+  // operands' amax slots (float bits; the scales follow from them), and an
+  // optional slot that receives the amax of the bf16 output, of its GeLU when
+  // amax_gelu is set (EPI_BF16), or of dP (EPI_DGELU, which then writes no G^T).
+  const uint32_t* amax_a;
+  const uint32_t* amax_b;
+  uint32_t* amax_out;
+  int amax_gelu;
 };
 
 // Tile shapes the library instantiates.
@@ -130,5 +138,41 @@ hipError_t launch_ffn_fwd(const FfnArgs& a, hipStream_t stream);
 int tile_bm(TileCfg t);
 int tile_bn(TileCfg t);
 constexpr int TILE_BK = 64;
+
+// FP8 products: C = (A_codes B_codes) s_a s_b with A [M][lda] and B [N][ldb] FP8
+// codes (both K-contiguous; K, lda, ldb and k_split counted in FP8 elements, all
+// multiples of 16), fmt_a and fmt_b 0 for E4M3 and 1 for E5M2 (pairs (0,0), (1,0)
+// and (0,1)), the scales from args.amax_a / amax_b.  `a` and `b` point at the codes.
+hipError_t launch_gemm_fp8(TileCfg tile, int fmt_a, int fmt_b, Epi epi, const GemmArgs& args, int splits,
+                           hipStream_t stream);
+
+// The FP8 element-wise kernels (fp8.hip).
+struct Fp8ZeroArgs {
+  uint32_t* p;
+  int n;
+};
+struct Fp8AmaxArgs {
+  const uint16_t* in;
+  int64_t R, C, ld;
+  int gelu;
+  uint32_t* slot;
+};
+struct Fp8QuantArgs {
+  const uint16_t* in;
+  uint8_t* out;
+  int64_t R, C, ld_in, ld_out;
+  int gelu, fmt;
+  const uint32_t* slot;
+};
+// p[0 .. n) = 0 (amax slots; n <= 256 per call).
+hipError_t launch_fp8_zero(uint32_t* p, int n, hipStream_t s);
+// slot = max(slot, max |x|) over a bf16 [R][C] tensor (rows of ld; C % 8 == 0), x
+// the element or, with gelu, its GeLU.
+hipError_t launch_fp8_amax(const uint16_t* in, int64_t R, int64_t C, int64_t ld, bool gelu, uint32_t* slot,
+                           hipStream_t s);
+// FP8 codes of a bf16 [R][C] tensor (or of its GeLU) under the scale in `slot`:
+// out [R][ld_out] bytes, or with transpose out [C][ld_out] (R, C multiples of 16).
+hipError_t launch_fp8_quant(const uint16_t* in, int64_t R, int64_t C, int64_t ld_in, bool gelu, int fmt,
+                            const uint32_t* slot, uint8_t* out, int64_t ld_out, bool transpose, hipStream_t s);
 
 }  // namespace tpmlp

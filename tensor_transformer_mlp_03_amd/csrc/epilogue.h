@@ -50,12 +50,15 @@ __device__ __forceinline__ NormalTail normal_tail(float x) {
   return NormalTail{q * e, e};
 }
 
-// G = GeLU(acc) -> bf16, as x Phi(x) = max(x, 0) - |x| Phi(-|x|), which holds
-// for either sign of x.
-__device__ __forceinline__ uint16_t epi_gelu(float acc) {
-  const NormalTail n = normal_tail(acc);
-  return f32_to_bf16(__builtin_fmaf(-fabsf(acc), n.he, acc > 0.0f ? acc : 0.0f));
+// GeLU(x) in float32, as x Phi(x) = max(x, 0) - |x| Phi(-|x|), which holds for
+// either sign of x.
+__device__ __forceinline__ float gelu_f32(float x) {
+  const NormalTail n = normal_tail(x);
+  return __builtin_fmaf(-fabsf(x), n.he, x > 0.0f ? x : 0.0f);
 }
+
+// G = GeLU(acc) -> bf16.
+__device__ __forceinline__ uint16_t epi_gelu(float acc) { return f32_to_bf16(gelu_f32(acc)); }
 
 // From the stored bf16 pre-activation p and the accumulated dG: dP = dG GeLU'(p)
 // and G = GeLU(p), both bf16.
@@ -69,6 +72,69 @@ __device__ __forceinline__ DGelu epi_dgelu(float dg, uint16_t p_bits) {
   const float cdf = p >= 0.0f ? 1.0f - n.he : n.he;                  // Phi(p)
   const float grad = __builtin_fmaf(p * n.e, INV_SQRT_2PI, cdf);     // Phi(p) + p phi(p)
   return DGelu{f32_to_bf16(dg * grad), f32_to_bf16(p * cdf)};
+}
+
+// dP = dG GeLU'(p) in float32 (the FP8 path's dGeLU, which needs no G).
+__device__ __forceinline__ float dgelu_f32(float dg, uint16_t p_bits) {
+  constexpr float INV_SQRT_2PI = 0.39894228040143268f;
+  const float p = bf16_to_f32(p_bits);
+  const NormalTail n = normal_tail(p);
+  const float cdf = p >= 0.0f ? 1.0f - n.he : n.he;
+  return dg * __builtin_fmaf(p * n.e, INV_SQRT_2PI, cdf);
+}
+
+// ---------------------------------------------------------------------------
+// FP8 operands ("大模型训练" notes §6.1: E4M3, 4 exponent and 3 mantissa bits,
+// range +-448; E5M2, 5 and 2 bits, range +-57344) under per-tensor scaling: a
+// tensor's scale is s = amax / FMAX (1 for an all-zero tensor), its codes are
+// fp8(x * (1 / s)) with the product in float32, saturated to +-FMAX and rounded
+// to nearest even by the conversion instruction; in a product each code stands
+// for code * s.  Every consumer of a tensor derives s and 1/s from the same
+// amax bits with the same two correctly rounded divisions, so the scales agree
+// bit for bit across kernels.
+// ---------------------------------------------------------------------------
+constexpr float FP8_E4M3_MAX = 448.0f;
+constexpr float FP8_E5M2_MAX = 57344.0f;
+
+__device__ __forceinline__ float fp8_fmax(int fmt) { return fmt ? FP8_E5M2_MAX : FP8_E4M3_MAX; }
+
+// Max over the 64 lanes of a wave.
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+// Max over a wave of per-lane values (all >= 0), added to an amax slot by lane 0.
+__device__ __forceinline__ void slot_max(uint32_t* slot, float lane_max) {
+  const float m = wave_max(lane_max);
+  if ((threadIdx.x & 63) == 0) atomicMax(slot, __builtin_bit_cast(uint32_t, m));
+}
+
+// Scale of a tensor from its amax (float bits, the value is >= 0).
+__device__ __forceinline__ float fp8_scale(uint32_t amax_bits, float fmax) {
+  const float amax = __builtin_bit_cast(float, amax_bits);
+  return amax == 0.0f ? 1.0f : amax / fmax;
+}
+
+// Four float32 values, already multiplied by 1/s, to four FP8 codes (byte e of
+// the result holds value e): clamped to +-FMAX, then converted (nearest, ties to
+// even).  fmt 0: E4M3, 1: E5M2.
+__device__ __forceinline__ uint32_t fp8_pack4(float a, float b, float c, float d, int fmt) {
+  const float m = fp8_fmax(fmt);
+  a = fminf(fmaxf(a, -m), m);
+  b = fminf(fmaxf(b, -m), m);
+  c = fminf(fmaxf(c, -m), m);
+  d = fminf(fmaxf(d, -m), m);
+  int v;
+  if (fmt == 0) {
+    v = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    v = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, v, true);
+  } else {
+    v = __builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false);
+    v = __builtin_amdgcn_cvt_pk_bf8_f32(c, d, v, true);
+  }
+  return (uint32_t)v;
 }
 
 }  // namespace tpmlp

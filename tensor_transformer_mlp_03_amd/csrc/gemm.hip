@@ -221,9 +221,13 @@ constexpr int G_ROW_B = 128;  // staged G row pitch in bytes
 // writes the chunk's float32 values into `stage` (row r in 0..63 at r * ROW_B,
 // 16-byte chunk q in 0..15 at position q ^ (r & 15)), and the chunk is finished
 // from there.
-template <int EPI, int NC, class StageChunk>
+// FP8 (FP8 products): EPI_BF16 and EPI_DGELU also collect the amax of what they
+// write into args.amax_out when set (of the GeLU of the written values with
+// args.amax_gelu), and EPI_DGELU writes dP only (no G^T).
+template <int EPI, int NC, bool FP8, class StageChunk>
 __device__ __forceinline__ void store_staged(StageChunk&& stage_chunk, const GemmArgs& args, char* stage, int row_w,
                                              int col_w, int nh, int split, int lane) {
+  float amax = 0.0f;  // FP8: this lane's max |written value| (valid elements only)
   // Each phase below issues all of its memory operations before it waits for
   // any, and the global loads an epilogue needs (the dGeLU pre-activations, the
   // EPI_F32_ACC running sum) are double-buffered: chunk c + 1's are in flight
@@ -317,6 +321,21 @@ __device__ __forceinline__ void store_staged(StageChunk&& stage_chunk, const Gem
 #pragma unroll
           for (int e = 0; e < 8; ++e) v1[e] = f32_to_bf16(x[e]);
           if (ok) *reinterpret_cast<u16x8_t*>(reinterpret_cast<uint16_t*>(args.out) + o) = v1;
+          if (FP8 && ok && args.amax_out) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float v = bf16_to_f32(v1[e]);
+              amax = fmaxf(amax, fabsf(args.amax_gelu ? gelu_f32(v) : v));
+            }
+          }
+        } else if (FP8) {  // EPI_DGELU of an FP8 product: dP and its amax
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v1[e] = f32_to_bf16(dgelu_f32(x[e], pre[ch & 1][it][e]));
+          if (ok) {
+            *reinterpret_cast<u16x8_t*>(reinterpret_cast<uint16_t*>(args.out) + o) = v1;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(bf16_to_f32(v1[e])));
+          }
         } else {  // EPI_DGELU
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
@@ -333,7 +352,7 @@ __device__ __forceinline__ void store_staged(StageChunk&& stage_chunk, const Gem
           *reinterpret_cast<u16x8_t*>(stage + r * G_ROW_B + ((cp ^ gt_swz(r)) << 4)) = v2;
         }
       }
-      if (EPI == EPI_DGELU) {
+      if (EPI == EPI_DGELU && !FP8) {
         // Transposed store of G in whole 128-byte lines.  ds_read_b64_tr_b16
         // takes, in each 16-lane group, 4 rows x 16 columns (source lane 4 r + q:
         // row r, columns 4 q .. +3) and hands lane i column i.  Source lane
@@ -366,6 +385,7 @@ __device__ __forceinline__ void store_staged(StageChunk&& stage_chunk, const Gem
       }
     }
   }
+  if (FP8 && (EPI == EPI_BF16 || EPI == EPI_DGELU) && args.amax_out) slot_max(args.amax_out, amax);
 }
 
 }  // namespace
@@ -395,11 +415,12 @@ namespace kern {
 // fragment is reloaded as soon as its row of MFMAs has been issued (MFMAs run
 // row by row), so A needs no second buffer.  The deeper prefetch of the small
 // tile covers memory latency over its shorter K steps (a quarter of the MFMAs).
-template <int LB, int EPI, int BM, int BN>
+template <int LB, int EPI, int BM, int BN, int F8>
 __global__ void __launch_bounds__(256)
 gemm_x16_kernel(GemmArgs args) {
 #if defined(__HIP_DEVICE_COMPILE__)
   static_assert((BM == 256 && (BN == 256 || BN == 128)) || (BM == 128 && BN == 128), "tile shapes");
+  static_assert(F8 == 0 || LB == KC, "FP8 operands are K-contiguous");
   constexpr int BK = TILE_BK;
   constexpr int SLOT = 128 * BK * 2;
   constexpr int NA = BM / 128;              // A quarters (128 rows x BK) per K step
@@ -461,6 +482,7 @@ gemm_x16_kernel(GemmArgs args) {
 #pragma unroll
     for (int j = 0; j < FJ; ++j) acc[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
+  if constexpr (F8 == 0) {
   bf16x8_t fa[FI], fb[2][FJ];
   // K-contiguous fragment f (rows 16f .. +15 of a 128-row quarter) in sub-step kk:
   // lane l reads row 16f + l % 16, 16-byte chunk 4kk + l / 16, at lane_kc[kk] + 2048 f.
@@ -609,6 +631,142 @@ gemm_x16_kernel(GemmArgs args) {
     tail(std::integral_constant<int, 0>{});
     vm_wait(L0{});
   }
+  } else {
+    // FP8 operands (formats FA of A, FB of B: 0 E4M3, 1 E5M2).  A K step holds 128
+    // FP8 values per row, the bytes of a bf16 step, so the ring, the loads and the
+    // slot schedule are those above.  Each 16 x 16 block takes one
+    // v_mfma_scale_f32_16x16x128_f8f6f4 per step (unit block scales; the tensors'
+    // scales multiply the accumulators in the epilogue), on fragments of 32
+    // bytes per lane: the two 16-byte fragments of a row that the bf16 sub-steps
+    // read, in the same order for A and B (the instruction pairs the K positions
+    // of its two operands lane by lane, so any common order is the same sum).
+    // A step runs in two halves of FI/2 rows each, split by the mid-step wait and
+    // barrier.  Half 0 reads A rows FI/2.. of this step after its rows; half 1
+    // reads A rows 0..FI/2-1 of step k+1 after its rows, and B fragment j of step
+    // k+1 right after the last MFMA that uses this step's fragment j.
+    constexpr int FA = (F8 - 1) & 1, FB = (F8 - 1) >> 1, HR = FI / 2;
+    typedef int i32x8_t __attribute__((ext_vector_type(8)));
+    i32x8_t fa8[FI], fb8[FJ];
+    uint32_t lane_kc[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) lane_kc[kk] = tile16_off(lane & 15, 4 * kk + (lane >> 4));
+    auto frag8 = [&](const char* base) -> i32x8_t {
+      const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(base + lane_kc[0]);
+      const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(base + lane_kc[1]);
+      return i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    };
+    auto read_a8 = [&](int r, int f) {
+      fa8[f] = frag8(BM == 256 ? slot(r, wm) + 2048 * f : slot(r, 0) + 2048 * (4 * wm + f));
+    };
+    auto read_b8 = [&](int r, int j) {
+      fb8[j] = frag8(slot(r, BN == 256 ? NA + wn : NA) + 2048 * ((BN == 256 ? 0 : 4 * wn) + j));
+    };
+    const int unit_scale = 127;  // E8M0 block scale 2^0
+    auto mfma8 = [&](f32x4_t& c, const i32x8_t& b, const i32x8_t& a) {
+      if constexpr (FB == 0 && FA == 0)
+        asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %3 op_sel_hi:[0,0,0]"
+                     : "+a"(c) : "v"(b), "v"(a), "v"(unit_scale));
+      else if constexpr (FB == 1 && FA == 0)
+        asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %3 op_sel_hi:[0,0,0] cbsz:1"
+                     : "+a"(c) : "v"(b), "v"(a), "v"(unit_scale));
+      else
+        asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %3 op_sel_hi:[0,0,0] blgp:1"
+                     : "+a"(c) : "v"(b), "v"(a), "v"(unit_scale));
+    };
+    auto vm_wait = [&](auto n) {
+      constexpr int N = decltype(n)::value;
+      static_assert(N >= 0 && N < 64, "vmcnt");
+      __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+    };
+    using L0 = std::integral_constant<int, 0>;
+    constexpr int HALF_LOADS = 4 * QS0, TAIL_LOADS = 4 * (NQ - QS0), STEP_LOADS = HALF_LOADS + TAIL_LOADS;
+    static_assert((D - 1) * STEP_LOADS < 64, "vmcnt");
+
+    // Half h of a step at ring position r: rows h HR .. h HR + HR - 1.  With
+    // `reads` (half 1 only), the next step's fragments come from ring position rn.
+    auto half8 = [&](int h, int r, bool reads, int rn, auto nl, auto&& issue_load) {
+      constexpr int NL = decltype(nl)::value;
+#pragma unroll
+      for (int ii = 0; ii < HR; ++ii) {
+        const int i = h * HR + ii;
+        int n_row = 0, n_first = 0;
+#pragma unroll
+        for (int n = NL - 1; n >= 0; --n)
+          if (n * HR / NL == ii) {
+            ++n_row;
+            n_first = n;
+          }
+#pragma unroll
+        for (int j = 0; j < FJ; ++j) {
+          mfma8(acc[i][j], fb8[j], fa8[i]);
+          if (h == 1 && reads && ii == HR - 1) read_b8(rn, j);
+          if (j == 1 && n_row >= 1) issue_load(n_first);
+          if (j == FJ / 2 + 1 && n_row >= 2) issue_load(n_first + 1);
+          if (j == FJ - 1) {
+            if (h == 0) read_a8(r, i + HR);
+            else if (reads) read_a8(rn, i - HR);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    };
+
+    if (nk > 0) {
+#pragma unroll
+      for (int st = 0; st < D; ++st)
+        if (st < nk) {
+#pragma unroll
+          for (int q = 0; q < NQ; ++q)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) load(st, st, q, i);
+        }
+      if (D >= 4 && nk >= 4) vm_wait(std::integral_constant<int, (D >= 4 ? 3 : 0) * STEP_LOADS>{});
+      else if (D >= 3 && nk >= 3) vm_wait(std::integral_constant<int, (D >= 3 ? 2 : 0) * STEP_LOADS>{});
+      else if (nk >= 2) vm_wait(std::integral_constant<int, STEP_LOADS>{});
+      else vm_wait(L0{});
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < FJ; ++j) read_b8(0, j);
+#pragma unroll
+      for (int f = 0; f < HR; ++f) read_a8(0, f);
+
+      auto k_step8 = [&](int k, auto left, int r) {
+        constexpr int LEFT = decltype(left)::value;
+        const int r1 = r == P - 1 ? 0 : r + 1, rd = (r + D) % P;
+        half8(0, r, false, r1, std::integral_constant<int, LEFT >= D ? HALF_LOADS : 0>{},
+              [&](int n) { load(k + D, rd, n >> 2, n & 3); });
+        if constexpr (LEFT >= 1) {
+          constexpr int WHOLE = LEFT - 1 < D - 2 ? LEFT - 1 : D - 2;
+          constexpr int AFTER = STEP_LOADS * (WHOLE > 0 ? WHOLE : 0) + (LEFT >= D ? HALF_LOADS : 0);
+          __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): half 1's A fragments are in registers
+          vm_wait(std::integral_constant<int, AFTER>{});
+          __builtin_amdgcn_s_barrier();
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        half8(1, r, LEFT >= 1, r1, std::integral_constant<int, LEFT >= D ? TAIL_LOADS : 0>{},
+              [&](int n) { load(k + D, rd, QS0 + (n >> 2), n & 3); });
+      };
+      using Full = std::integral_constant<int, D>;
+      int k = 0;
+      for (; k + P + D <= nk; k += P) {
+#pragma unroll
+        for (int u = 0; u < P; ++u) k_step8(k + u, Full{}, u);
+      }
+      for (; k + D < nk; ++k) k_step8(k, Full{}, k % P);
+      auto tail = [&](auto jc) {
+        constexpr int J = decltype(jc)::value;
+        if constexpr (J < D) {
+          if (nk >= J + 1) k_step8(nk - 1 - J, std::integral_constant<int, J>{}, (nk - 1 - J) % P);
+        }
+      };
+      tail(std::integral_constant<int, 3>{});
+      tail(std::integral_constant<int, 2>{});
+      tail(std::integral_constant<int, 1>{});
+      tail(std::integral_constant<int, 0>{});
+      vm_wait(L0{});
+    }
+  }
   // The last MFMAs' results are read below; 32 wait states cover the longest
   // write-to-read distance of a 16 x 16 x 32 MFMA (issued as inline assembly, so
   // the compiler does not insert them).
@@ -619,7 +777,11 @@ gemm_x16_kernel(GemmArgs args) {
   // tall, FJ / 4 wide), staged in the wave's own 16 KiB of LDS.  Block (i, j)
   // register e holds C[16i + lane%16][16j + 4 (lane/16) + e] of the wave's
   // sub-tile.
-  store_staged<EPI, (FI / 4) * (FJ / 4)>(
+  // FP8: the product of the two tensors' scales (unit for bf16 operands).
+  float sc = 1.0f;
+  if constexpr (F8 != 0)
+    sc = fp8_scale(*args.amax_a, fp8_fmax((F8 - 1) & 1)) * fp8_scale(*args.amax_b, fp8_fmax((F8 - 1) >> 1));
+  store_staged<EPI, (FI / 4) * (FJ / 4), F8 != 0>(
       [&](int ch) {
         const int h = ch % (FI / 4), hc = ch / (FI / 4);
 #pragma unroll
@@ -627,8 +789,9 @@ gemm_x16_kernel(GemmArgs args) {
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
             const int r = 16 * ii + (lane & 15), c = 4 * jj + (lane >> 4);
-            *reinterpret_cast<f32x4_t*>(smem + wave * (64 * ROW_B) + r * ROW_B + ((c ^ (r & 15)) << 4)) =
-                acc[4 * h + ii][4 * hc + jj];
+            f32x4_t v = acc[4 * h + ii][4 * hc + jj];
+            if constexpr (F8 != 0) v = v * sc;
+            *reinterpret_cast<f32x4_t*>(smem + wave * (64 * ROW_B) + r * ROW_B + ((c ^ (r & 15)) << 4)) = v;
           }
       },
       args, smem + wave * (64 * ROW_B), m0 + (BM / 2) * wm, n0 + (BN / 2) * wn, FI / 4, split, lane);
@@ -641,10 +804,34 @@ gemm_x16_kernel(GemmArgs args) {
 
 namespace {
 
-template <int BM, int BN, int LB, int EPI>
+template <int BM, int BN, int LB, int EPI, int F8 = 0>
 hipError_t launch_one(const GemmArgs& a, int splits, hipStream_t s) {
   const int blocks = a.tiles_m * a.tiles_n * splits;
-  return launch_kernel(kern::gemm_x16_kernel<LB, EPI, BM, BN>, dim3(blocks), dim3(256), s, a);
+  return launch_kernel(kern::gemm_x16_kernel<LB, EPI, BM, BN, F8>, dim3(blocks), dim3(256), s, a);
+}
+
+// FP8 products: (fmt_a, fmt_b) in {(0, 0), (1, 0), (0, 1)} with the epilogues the
+// FP8 path uses for each.
+template <int BM, int BN>
+hipError_t dispatch_fp8(int fa, int fb, Epi epi, const GemmArgs& a, int splits, hipStream_t s) {
+  if (fa == 0 && fb == 0) {
+    switch (epi) {
+      case EPI_BF16: return launch_one<BM, BN, KC, EPI_BF16, 1>(a, splits, s);
+      case EPI_F32: return launch_one<BM, BN, KC, EPI_F32, 1>(a, splits, s);
+      case EPI_F32_ACC: return launch_one<BM, BN, KC, EPI_F32_ACC, 1>(a, splits, s);
+      default: break;
+    }
+  } else if (fa == 1 && fb == 0) {
+    switch (epi) {
+      case EPI_DGELU: return launch_one<BM, BN, KC, EPI_DGELU, 2>(a, splits, s);
+      case EPI_F32: return launch_one<BM, BN, KC, EPI_F32, 2>(a, splits, s);
+      case EPI_F32_ACC: return launch_one<BM, BN, KC, EPI_F32_ACC, 2>(a, splits, s);
+      default: break;
+    }
+  } else if (fa == 0 && fb == 1) {
+    if (epi == EPI_F32) return launch_one<BM, BN, KC, EPI_F32, 3>(a, splits, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 // Every product reads A K-contiguous; B is K- or N-contiguous.
@@ -676,6 +863,24 @@ hipError_t dispatch_layout(Layout la, Layout lb, Epi epi, const GemmArgs& a, int
 
 int tile_bm(TileCfg t) { return t == TILE_128x128 ? 128 : 256; }
 int tile_bn(TileCfg t) { return t == TILE_256x256 ? 256 : 128; }
+
+hipError_t launch_gemm_fp8(TileCfg tile, int fmt_a, int fmt_b, Epi epi, const GemmArgs& args, int splits,
+                           hipStream_t stream) {
+  // The kernel counts K, leading dimensions and K slices in 16-bit units: an FP8
+  // row of K bytes is K/2 of them, and a K step of 64 units is 128 FP8 values.
+  if ((args.K | args.lda | args.ldb | args.k_split) & 15) return hipErrorInvalidValue;
+  GemmArgs g = args;
+  g.K /= 2;
+  g.lda /= 2;
+  g.ldb /= 2;
+  g.k_split /= 2;
+  switch (tile) {
+    case TILE_256x256: return dispatch_fp8<256, 256>(fmt_a, fmt_b, epi, g, splits, stream);
+    case TILE_128x128: return dispatch_fp8<128, 128>(fmt_a, fmt_b, epi, g, splits, stream);
+    case TILE_256x128: return dispatch_fp8<256, 128>(fmt_a, fmt_b, epi, g, splits, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 hipError_t launch_gemm(TileCfg tile, Layout la, Layout lb, Epi epi, const GemmArgs& args, int splits,
                        hipStream_t stream) {

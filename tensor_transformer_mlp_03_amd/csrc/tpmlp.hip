@@ -738,6 +738,231 @@ tpmlp_status check_sp_shape(int t, int64_t M, int64_t H, int64_t F) {
   return TPMLP_OK;
 }
 
+
+// ---------------------------------------------------------------------------
+// FP8 drivers: per-tensor scaled E4M3 / E5M2 operands (see the header).
+// ---------------------------------------------------------------------------
+constexpr int F8_E4M3 = 0, F8_E5M2 = 1;
+
+bool shape16_ok(int64_t v) { return v > 0 && v <= MAX_DIM && (v % 16) == 0; }
+
+tpmlp_status check_shape_fp8(int64_t M, int64_t H, int64_t F) {
+  if (!shape16_ok(M) || !shape16_ok(H) || !shape16_ok(F))
+    return fail(TPMLP_ERR_SHAPE, "M, H and F_i must be positive multiples of 16, at most 2^23");
+  return TPMLP_OK;
+}
+
+// A plan without split-K, for products whose epilogue collects an amax (a
+// split reduction does not).
+GemmPlan plan_gemm_whole(int64_t M, int64_t N, int64_t K) {
+  GemmPlan best{TILE_256x256, 1, (int)((K + TILE_BK - 1) / TILE_BK * TILE_BK)};
+  double best_t = 1e30;
+  for (TileCfg tile : {TILE_256x256, TILE_256x128, TILE_128x128}) {
+    const int64_t tiles = (int64_t)ceil_div(M, tile_bm(tile)) * ceil_div(N, tile_bn(tile));
+    const double rate = tile == TILE_256x256 ? CU_RATE_256 : tile == TILE_256x128 ? CU_RATE_256x128 : CU_RATE_128;
+    const double t = double((tiles + NUM_CU - 1) / NUM_CU) * double(tile_bm(tile) * tile_bn(tile) * 2 * K) / rate;
+    if (t < best_t * (1 - 1e-9)) {
+      best_t = t;
+      best = GemmPlan{tile, 1, (int)((K + TILE_BK - 1) / TILE_BK * TILE_BK)};
+    }
+  }
+  return best;
+}
+
+// Amax slots: X, dZ, then per shard A_i, B_i, G_i, dP_i.
+constexpr int SLOT_X = 0, SLOT_DZ = 1;
+inline int slot_of(int i, int which) { return 2 + 4 * i + which; }  // which: 0 A, 1 B, 2 G, 3 dP
+
+struct Fp8Layout {
+  GemmPlan g1, g2, gdg, gdb, gda, gdx;
+  size_t slots, qX, qXt, qdZ, qdZt, qAt, qBt, qA, qB, P, qG, qGt, dP, qdP, qdPt, part, total;
+};
+
+Fp8Layout fp8_layout(int t, int64_t M, int64_t H, int64_t F) {
+  Fp8Layout L;
+  L.g1 = plan_gemm_whole(M, F, H);  // P_i = X A_i (epilogue collects amax|GeLU(P_i)|)
+  L.g2 = plan_gemm(M, H, F);        // Z_i = G_i B_i
+  L.gdg = plan_gemm_whole(M, F, H); // dG_i = dZ B_i^T (epilogue collects amax|dP_i|)
+  L.gdb = plan_gemm(F, H, M);
+  L.gda = plan_gemm(H, F, M);
+  L.gdx = plan_gemm(M, H, F);
+  const size_t mh = size_t(M) * H, hf = size_t(H) * F, mf = size_t(M) * F;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += align_up(bytes);
+    return at;
+  };
+  L.slots = take(size_t(2 + 4 * t) * 4);
+  L.qX = take(mh);
+  L.qXt = take(mh);
+  L.qdZ = take(mh);
+  L.qdZt = take(mh);
+  L.qAt = take(hf);
+  L.qBt = take(hf);
+  L.qA = take(hf);
+  L.qB = take(hf);
+  L.P = take(mf * 2);
+  L.qG = take(mf);
+  L.qGt = take(mf);
+  L.dP = take(mf * 2);
+  L.qdP = take(mf);
+  L.qdPt = take(mf);
+  L.part = take(std::max({part_bytes(L.g2, M, H), part_bytes(L.gdb, F, H), part_bytes(L.gda, H, F),
+                          part_bytes(L.gdx, M, H), size_t(1)}));
+  L.total = o;
+  return L;
+}
+
+// One FP8 product (codes a [M][lda], b [N][ldb], both K-contiguous) with its
+// epilogue; the scales come from the operands' amax slots.  Split along K, the
+// scaled float32 slices are reduced by the bf16 path's reduction.
+hipError_t run_gemm_fp8(int kind, int fa, int fb, Epi epi, const uint8_t* a, int64_t lda, const uint8_t* b,
+                        int64_t ldb, int64_t M, int64_t N, int64_t K, const GemmPlan& p, void* out,
+                        const uint16_t* aux, const uint32_t* amax_a, const uint32_t* amax_b, uint32_t* amax_out,
+                        bool amax_gelu, float* part, hipStream_t s) {
+  auto args = [&](const uint8_t* bb, int64_t n, const GemmPlan& pl, void* o, int64_t ldo) {
+    GemmArgs g = gemm_args(a, lda, bb, ldb, M, n, K, pl, o, ldo);
+    // K slices of whole FP8 K steps (128 values); a slice past K adds zeros.
+    g.k_split = (int)(((K + pl.splits - 1) / pl.splits + 127) / 128 * 128);
+    g.aux = aux;
+    g.amax_a = amax_a;
+    g.amax_b = amax_b;
+    g.amax_out = amax_out;
+    g.amax_gelu = amax_gelu ? 1 : 0;
+    return g;
+  };
+  if (p.splits == 1) {
+    const GemmArgs g = args(b, N, p, out, N);
+    return timed(kind, s, [&] { return launch_gemm_fp8(p.tile, fa, fb, epi, g, 1, s); });
+  }
+  if (p.n_full > 0) {
+    const int64_t nf = p.n_full, nt = N - nf;
+    const GemmPlan pf{p.tile, 1, (int)((K + TILE_BK - 1) / TILE_BK * TILE_BK)};
+    GemmArgs gf = args(b, nf, pf, out, N);
+    GemmArgs gt = args(b + nf * ldb, nt, p, part, nt);
+    gt.amax_out = nullptr;
+    hipError_t e = timed(
+        kind, s,
+        [&] {
+          hipError_t r = launch_gemm_fp8(p.tile, fa, fb, epi, gf, 1, s);
+          return r != hipSuccess ? r : launch_gemm_fp8(p.tile, fa, fb, EPI_F32, gt, p.splits, s);
+        },
+        2);
+    if (e != hipSuccess) return e;
+    float* out_tail = static_cast<float*>(out) + nf;
+    return timed(TPMLP_K_SPLITK_REDUCE, s, [&] {
+      return launch_splitk_epilogue(epi, part, p.splits, M, nt, out_tail, nullptr, nullptr, N, M, s);
+    });
+  }
+  GemmArgs g = args(b, N, p, part, N);
+  g.amax_out = nullptr;
+  hipError_t e = timed(kind, s, [&] { return launch_gemm_fp8(p.tile, fa, fb, EPI_F32, g, p.splits, s); });
+  if (e != hipSuccess) return e;
+  return timed(TPMLP_K_SPLITK_REDUCE, s,
+               [&] { return launch_splitk_epilogue(epi, part, p.splits, M, N, out, nullptr, nullptr, N, M, s); });
+}
+
+hipError_t fp8_amax(const tpmlp_bf16* in, int64_t R, int64_t C, bool gelu, uint32_t* slot, hipStream_t s) {
+  return timed(TPMLP_K_FP8_QUANT, s, [&] { return launch_fp8_amax(in, R, C, C, gelu, slot, s); });
+}
+
+hipError_t fp8_quant(const tpmlp_bf16* in, int64_t R, int64_t C, bool gelu, int fmt, const uint32_t* slot,
+                     uint8_t* out, bool transpose, hipStream_t s) {
+  return timed(TPMLP_K_FP8_QUANT, s,
+               [&] { return launch_fp8_quant(in, R, C, C, gelu, fmt, slot, out, transpose ? R : C, transpose, s); });
+}
+
+#define F8_TRY(x)                         \
+  do {                                    \
+    const hipError_t e_ = (x);            \
+    if (e_ != hipSuccess) return e_;      \
+  } while (0)
+
+hipError_t enqueue_fp8_fwd(const tpmlp_bf16* X, const tpmlp_bf16* const* A_sh, const tpmlp_bf16* const* B_sh,
+                           tpmlp_bf16* const* P_sh, float* Z, int t, int64_t M, int64_t H, int64_t F, void* ws,
+                           hipStream_t s) {
+  const Fp8Layout L = fp8_layout(t, M, H, F);
+  uint32_t* slots = reinterpret_cast<uint32_t*>(ws_at(ws, L.slots));
+  uint8_t* qX = reinterpret_cast<uint8_t*>(ws_at(ws, L.qX));
+  uint8_t* qAt = reinterpret_cast<uint8_t*>(ws_at(ws, L.qAt));
+  uint8_t* qBt = reinterpret_cast<uint8_t*>(ws_at(ws, L.qBt));
+  uint8_t* qG = reinterpret_cast<uint8_t*>(ws_at(ws, L.qG));
+  float* part = reinterpret_cast<float*>(ws_at(ws, L.part));
+  F8_TRY(timed(TPMLP_K_FP8_QUANT, s, [&] { return launch_fp8_zero(slots, 2 + 4 * t, s); }));
+  F8_TRY(fp8_amax(X, M, H, false, slots + SLOT_X, s));
+  F8_TRY(fp8_quant(X, M, H, false, F8_E4M3, slots + SLOT_X, qX, false, s));
+  for (int i = 0; i < t; ++i) {
+    uint32_t* sA = slots + slot_of(i, 0);
+    uint32_t* sB = slots + slot_of(i, 1);
+    uint32_t* sG = slots + slot_of(i, 2);
+    tpmlp_bf16* P = (P_sh && P_sh[i]) ? P_sh[i] : reinterpret_cast<tpmlp_bf16*>(ws_at(ws, L.P));
+    F8_TRY(fp8_amax(A_sh[i], H, F, false, sA, s));
+    F8_TRY(fp8_quant(A_sh[i], H, F, false, F8_E4M3, sA, qAt, true, s));  // A_i^T [F][H]
+    F8_TRY(fp8_amax(B_sh[i], F, H, false, sB, s));
+    F8_TRY(fp8_quant(B_sh[i], F, H, false, F8_E4M3, sB, qBt, true, s));  // B_i^T [H][F]
+    F8_TRY(run_gemm_fp8(TPMLP_K_FWD_GEMM1_GELU, F8_E4M3, F8_E4M3, EPI_BF16, qX, H, qAt, H, M, F, H, L.g1, P, nullptr,
+                        slots + SLOT_X, sA, sG, true, part, s));
+    F8_TRY(fp8_quant(P, M, F, true, F8_E4M3, sG, qG, false, s));
+    F8_TRY(run_gemm_fp8(TPMLP_K_FWD_GEMM2, F8_E4M3, F8_E4M3, i == 0 ? EPI_F32 : EPI_F32_ACC, qG, F, qBt, F, M, H, F,
+                        L.g2, Z, nullptr, sG, sB, nullptr, false, part, s));
+  }
+  return hipSuccess;
+}
+
+hipError_t enqueue_fp8_bwd(const tpmlp_bf16* dZ, const tpmlp_bf16* X, const tpmlp_bf16* const* A_sh,
+                           const tpmlp_bf16* const* B_sh, const tpmlp_bf16* const* P_sh, float* const* dA_sh,
+                           float* const* dB_sh, float* dX, int t, int64_t M, int64_t H, int64_t F, void* ws,
+                           hipStream_t s) {
+  const Fp8Layout L = fp8_layout(t, M, H, F);
+  auto q = [&](size_t off) { return reinterpret_cast<uint8_t*>(ws_at(ws, off)); };
+  uint32_t* slots = reinterpret_cast<uint32_t*>(ws_at(ws, L.slots));
+  tpmlp_bf16* dP = reinterpret_cast<tpmlp_bf16*>(ws_at(ws, L.dP));
+  float* part = reinterpret_cast<float*>(ws_at(ws, L.part));
+  const bool recompute = P_sh == nullptr;
+  F8_TRY(timed(TPMLP_K_FP8_QUANT, s, [&] { return launch_fp8_zero(slots, 2 + 4 * t, s); }));
+  F8_TRY(fp8_amax(dZ, M, H, false, slots + SLOT_DZ, s));
+  F8_TRY(fp8_quant(dZ, M, H, false, F8_E5M2, slots + SLOT_DZ, q(L.qdZ), false, s));
+  F8_TRY(fp8_quant(dZ, M, H, false, F8_E5M2, slots + SLOT_DZ, q(L.qdZt), true, s));  // dZ^T [H][M]
+  F8_TRY(fp8_amax(X, M, H, false, slots + SLOT_X, s));
+  F8_TRY(fp8_quant(X, M, H, false, F8_E4M3, slots + SLOT_X, q(L.qXt), true, s));  // X^T [H][M]
+  if (recompute) F8_TRY(fp8_quant(X, M, H, false, F8_E4M3, slots + SLOT_X, q(L.qX), false, s));
+  for (int i = 0; i < t; ++i) {
+    uint32_t* sA = slots + slot_of(i, 0);
+    uint32_t* sB = slots + slot_of(i, 1);
+    uint32_t* sG = slots + slot_of(i, 2);
+    uint32_t* sdP = slots + slot_of(i, 3);
+    F8_TRY(fp8_amax(A_sh[i], H, F, false, sA, s));
+    F8_TRY(fp8_quant(A_sh[i], H, F, false, F8_E4M3, sA, q(L.qA), false, s));  // A_i [H][F]
+    F8_TRY(fp8_amax(B_sh[i], F, H, false, sB, s));
+    F8_TRY(fp8_quant(B_sh[i], F, H, false, F8_E4M3, sB, q(L.qB), false, s));  // B_i [F][H]
+    const tpmlp_bf16* P;
+    if (recompute) {
+      tpmlp_bf16* Pw = reinterpret_cast<tpmlp_bf16*>(ws_at(ws, L.P));
+      F8_TRY(fp8_quant(A_sh[i], H, F, false, F8_E4M3, sA, q(L.qAt), true, s));
+      F8_TRY(run_gemm_fp8(TPMLP_K_BWD_RECOMPUTE, F8_E4M3, F8_E4M3, EPI_BF16, q(L.qX), H, q(L.qAt), H, M, F, H, L.g1,
+                          Pw, nullptr, slots + SLOT_X, sA, sG, true, part, s));
+      P = Pw;
+    } else {
+      P = P_sh[i];
+      F8_TRY(fp8_amax(P, M, F, true, sG, s));
+    }
+    F8_TRY(fp8_quant(P, M, F, true, F8_E4M3, sG, q(L.qGt), true, s));  // G_i^T [F][M]
+    F8_TRY(run_gemm_fp8(TPMLP_K_BWD_DGELU, F8_E5M2, F8_E4M3, EPI_DGELU, q(L.qdZ), H, q(L.qB), H, M, F, H, L.gdg, dP, P,
+                        slots + SLOT_DZ, sB, sdP, false, part, s));
+    F8_TRY(fp8_quant(dP, M, F, false, F8_E5M2, sdP, q(L.qdP), false, s));
+    F8_TRY(fp8_quant(dP, M, F, false, F8_E5M2, sdP, q(L.qdPt), true, s));  // dP_i^T [F][M]
+    F8_TRY(run_gemm_fp8(TPMLP_K_BWD_DB, F8_E4M3, F8_E5M2, EPI_F32, q(L.qGt), M, q(L.qdZt), M, F, H, M, L.gdb, dB_sh[i],
+                        nullptr, sG, slots + SLOT_DZ, nullptr, false, part, s));
+    F8_TRY(run_gemm_fp8(TPMLP_K_BWD_DA, F8_E4M3, F8_E5M2, EPI_F32, q(L.qXt), M, q(L.qdPt), M, H, F, M, L.gda, dA_sh[i],
+                        nullptr, slots + SLOT_X, sdP, nullptr, false, part, s));
+    F8_TRY(run_gemm_fp8(TPMLP_K_BWD_DX, F8_E5M2, F8_E4M3, i == 0 ? EPI_F32 : EPI_F32_ACC, q(L.qdP), F, q(L.qA), F, M,
+                        H, F, L.gdx, dX, nullptr, sdP, sA, nullptr, false, part, s));
+  }
+  return hipSuccess;
+}
+#undef F8_TRY
+
 }  // namespace
 }  // namespace tpmlp
 
@@ -766,7 +991,8 @@ const char* tpmlp_last_error(void) { return g_last_error.c_str(); }
 
 const char* tpmlp_kernel_name(int kind) {
   static const char* names[TPMLP_K_COUNT] = {"fwd_gemm1_gelu", "fwd_gemm2", "bwd_recompute", "bwd_dgelu",
-                                             "bwd_dB", "bwd_dA", "bwd_dX", "splitk_reduce", "shard_sum", "transpose", "fwd_fused"};
+                                             "bwd_dB", "bwd_dA", "bwd_dX", "splitk_reduce", "shard_sum", "transpose", "fwd_fused",
+                                             "fp8_quant"};
   return (kind >= 0 && kind < TPMLP_K_COUNT) ? names[kind] : "?";
 }
 
@@ -1161,6 +1387,93 @@ tpmlp_status tpmlp_sp_bwd(const tpmlp_bf16* const* dZ_sl, const tpmlp_bf16* cons
     if (e != hipSuccess) return hip_fail(e, "tpmlp_sp_bwd launch");
   }
   return TPMLP_OK;
+}
+
+size_t tpmlp_fp8_workspace_bytes(int t, int64_t M, int64_t H, int64_t F_i) {
+  if (t < 1 || t > TPMLP_MAX_SHARDS || !shape16_ok(M) || !shape16_ok(H) || !shape16_ok(F_i)) return 0;
+  return fp8_layout(t, M, H, F_i).total;
+}
+
+tpmlp_status tpmlp_fp8_tp_fwd(const tpmlp_bf16* X, const tpmlp_bf16* const* A_sh, const tpmlp_bf16* const* B_sh,
+                              tpmlp_bf16* const* P_sh, float* Z, int t, int64_t M, int64_t H, int64_t F_i,
+                              void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  if (!A_sh || !B_sh) return fail(TPMLP_ERR_NULL, "A_sh or B_sh is NULL");
+  if (t < 1 || t > TPMLP_MAX_SHARDS) return fail(TPMLP_ERR_SHARDS, "t outside 1..TPMLP_MAX_SHARDS");
+  tpmlp_status st = check_ptrs({{X, "X"}, {Z, "Z"}, {ws, "ws"}});
+  if (st) return st;
+  if ((st = check_shape_fp8(M, H, F_i))) return st;
+  const size_t need = tpmlp_fp8_workspace_bytes(t, M, H, F_i);
+  if (ws_bytes < need) return fail(TPMLP_ERR_WORKSPACE, "ws_bytes below tpmlp_fp8_workspace_bytes");
+  const size_t mh = size_t(M) * H, hf = size_t(H) * F_i, mf = size_t(M) * F_i;
+  std::vector<Range> ins = {{X, mh * 2, "X"}};
+  std::vector<Range> outs = {{Z, mh * 4, "Z"}, {ws, need, "ws"}};
+  for (int i = 0; i < t; ++i) {
+    if (!A_sh[i] || !B_sh[i]) return fail(TPMLP_ERR_NULL, "A_sh[" + std::to_string(i) + "] or B_sh[i] is NULL");
+    if (!aligned16(A_sh[i]) || !aligned16(B_sh[i])) return fail(TPMLP_ERR_ALIGN, "a weight shard is not 16-byte aligned");
+    ins.push_back({A_sh[i], hf * 2, "A_sh[i]"});
+    ins.push_back({B_sh[i], hf * 2, "B_sh[i]"});
+    if (P_sh && P_sh[i]) {
+      if (!aligned16(P_sh[i])) return fail(TPMLP_ERR_ALIGN, "P_sh[i] is not 16-byte aligned");
+      outs.push_back({P_sh[i], mf * 2, "P_sh[i]"});
+    }
+  }
+  if ((st = check_alias(outs, ins))) return st;
+  if ((st = check_device())) return st;
+  hipError_t e = enqueue_fp8_fwd(X, A_sh, B_sh, P_sh, Z, t, M, H, F_i, ws, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TPMLP_OK : hip_fail(e, "tpmlp_fp8_tp_fwd launch");
+}
+
+tpmlp_status tpmlp_fp8_tp_bwd(const tpmlp_bf16* dZ, const tpmlp_bf16* X, const tpmlp_bf16* const* A_sh,
+                              const tpmlp_bf16* const* B_sh, const tpmlp_bf16* const* P_sh,
+                              float* const* dA_sh, float* const* dB_sh, float* dX, int t, int64_t M, int64_t H,
+                              int64_t F_i, void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  if (!A_sh || !B_sh || !dA_sh || !dB_sh) return fail(TPMLP_ERR_NULL, "a shard array is NULL");
+  if (t < 1 || t > TPMLP_MAX_SHARDS) return fail(TPMLP_ERR_SHARDS, "t outside 1..TPMLP_MAX_SHARDS");
+  tpmlp_status st = check_ptrs({{dZ, "dZ"}, {X, "X"}, {dX, "dX"}, {ws, "ws"}});
+  if (st) return st;
+  if ((st = check_shape_fp8(M, H, F_i))) return st;
+  const size_t need = tpmlp_fp8_workspace_bytes(t, M, H, F_i);
+  if (ws_bytes < need) return fail(TPMLP_ERR_WORKSPACE, "ws_bytes below tpmlp_fp8_workspace_bytes");
+  const size_t mh = size_t(M) * H, hf = size_t(H) * F_i, mf = size_t(M) * F_i;
+  std::vector<Range> ins = {{dZ, mh * 2, "dZ"}, {X, mh * 2, "X"}};
+  std::vector<Range> outs = {{dX, mh * 4, "dX"}, {ws, need, "ws"}};
+  for (int i = 0; i < t; ++i) {
+    const std::string idx = "[" + std::to_string(i) + "]";
+    if (!A_sh[i] || !B_sh[i] || !dA_sh[i] || !dB_sh[i]) return fail(TPMLP_ERR_NULL, "a shard pointer" + idx + " is NULL");
+    if (P_sh && !P_sh[i]) return fail(TPMLP_ERR_NULL, "P_sh" + idx + " is NULL");
+    for (const void* p : {(const void*)A_sh[i], (const void*)B_sh[i], (const void*)dA_sh[i], (const void*)dB_sh[i]})
+      if (!aligned16(p)) return fail(TPMLP_ERR_ALIGN, "a shard pointer" + idx + " is not 16-byte aligned");
+    if (P_sh && !aligned16(P_sh[i])) return fail(TPMLP_ERR_ALIGN, "P_sh" + idx + " is not 16-byte aligned");
+    ins.push_back({A_sh[i], hf * 2, "A_sh[i]"});
+    ins.push_back({B_sh[i], hf * 2, "B_sh[i]"});
+    if (P_sh) ins.push_back({P_sh[i], mf * 2, "P_sh[i]"});
+    outs.push_back({dA_sh[i], hf * 4, "dA_sh[i]"});
+    outs.push_back({dB_sh[i], hf * 4, "dB_sh[i]"});
+  }
+  if ((st = check_alias(outs, ins))) return st;
+  if ((st = check_device())) return st;
+  hipError_t e =
+      enqueue_fp8_bwd(dZ, X, A_sh, B_sh, P_sh, dA_sh, dB_sh, dX, t, M, H, F_i, ws, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TPMLP_OK : hip_fail(e, "tpmlp_fp8_tp_bwd launch");
+}
+
+tpmlp_status tpmlp_fp8_quantize(const tpmlp_bf16* T, int64_t R, int64_t C, int fmt, int transpose, uint8_t* codes,
+                                float* amax, void* stream) {
+  g_last_error.clear();
+  tpmlp_status st = check_ptrs({{T, "T"}, {codes, "codes"}, {amax, "amax"}});
+  if (st) return st;
+  if (!shape16_ok(R) || !shape16_ok(C)) return fail(TPMLP_ERR_SHAPE, "R and C must be positive multiples of 16, at most 2^23");
+  if (fmt != 0 && fmt != 1) return fail(TPMLP_ERR_SHAPE, "fmt must be 0 (E4M3) or 1 (E5M2)");
+  if ((st = check_alias({{codes, size_t(R) * C, "codes"}, {amax, 4, "amax"}}, {{T, size_t(R) * C * 2, "T"}}))) return st;
+  if ((st = check_device())) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint32_t* slot = reinterpret_cast<uint32_t*>(amax);
+  hipError_t e = launch_fp8_zero(slot, 1, s);
+  if (e == hipSuccess) e = launch_fp8_amax(T, R, C, C, false, slot, s);
+  if (e == hipSuccess) e = launch_fp8_quant(T, R, C, C, false, fmt, slot, codes, transpose ? R : C, transpose != 0, s);
+  return e == hipSuccess ? TPMLP_OK : hip_fail(e, "tpmlp_fp8_quantize launch");
 }
 
 tpmlp_status tpmlp_timing_begin(int capacity) { return tpmlp_timing_begin_kinds(capacity, (1u << TPMLP_K_COUNT) - 1); }

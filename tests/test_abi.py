@@ -99,7 +99,7 @@ def test_last_error_is_per_thread():
 
 
 def test_version_and_strings():
-    assert L.tpmlp_abi_version() == 9
+    assert L.tpmlp_abi_version() == 10
     assert L.tpmlp_status_str(0) == "ok"
     assert L.tpmlp_status_str(ALIAS) == "output overlaps another buffer"
     assert L.tpmlp_status_str(99) == "unknown status"
@@ -374,3 +374,59 @@ def test_sp_workspace_query():
     assert L.tpmlp_sp_workspace_bytes(4, 96, 64, 64) > 0
     assert L.tpmlp_sp_workspace_bytes(3, 96, 64, 64) > 0     # 32 rows per slice
     assert L.tpmlp_sp_workspace_bytes(4, 48, 64, 64) == 0     # 12 rows per slice 
+
+
+def _fp8(fn, t=2, M=128, H=64, F=96, **kw):
+    arr = lambda base: L._ptr_array([_p(base + i) for i in range(t)], t)
+    ws = kw.pop("ws", _p(60))
+    wsb = kw.pop("wsb", 1 << 30)
+    if fn == "fwd":
+        a = dict(X=_p(0), A=arr(10), B=arr(20), P=None, Z=_p(30))
+        a.update(kw)
+        st = L.lib().tpmlp_fp8_tp_fwd(a["X"], a["A"], a["B"], a["P"], a["Z"], t, M, H, F, ws, wsb, None)
+    else:
+        a = dict(dZ=_p(0), X=_p(1), A=arr(10), B=arr(20), P=None, dA=arr(30), dB=arr(40), dX=_p(50))
+        a.update(kw)
+        st = L.lib().tpmlp_fp8_tp_bwd(a["dZ"], a["X"], a["A"], a["B"], a["P"], a["dA"], a["dB"], a["dX"], t, M, H,
+                                      F, ws, wsb, None)
+    return st, L.lib().tpmlp_last_error().decode()
+
+
+def test_fp8_argument_errors():
+    """The FP8 drivers check their arguments before any HIP call: NULL arrays and
+    pointers, shard counts, dimensions that are not multiples of 16, a short
+    workspace, misalignment and outputs that overlap inputs."""
+    for fn in ("fwd", "bwd"):
+        key = "X" if fn == "fwd" else "dZ"
+        assert _fp8(fn, **{key: None})[0] == NULL
+        assert _fp8(fn, A=None)[0] == NULL
+        assert _fp8(fn, t=0)[0] == SHARDS
+        st, msg = _fp8(fn, F=104)  # a multiple of 8 but not of 16
+        assert st == SHAPE and "multiples of 16" in msg
+        assert _fp8(fn, M=136)[0] == SHAPE
+        need = L.tpmlp_fp8_workspace_bytes(2, 128, 64, 96)
+        assert _fp8(fn, wsb=need - 1)[0] == WS
+        assert _fp8(fn, ws=_p(60) + 8)[0] == ALIGN
+        assert _fp8(fn)[0] in (HIP, UNSUP)  # valid: reaches the device check
+    st, msg = _fp8("fwd", Z=_p(0))  # Z on top of X
+    assert st == ALIAS
+    st, msg = _fp8("bwd", dX=_p(1))
+    assert st == ALIAS
+    # the quantizer
+    q = lambda **kw: L.lib().tpmlp_fp8_quantize(kw.get("T", _p(0)), kw.get("R", 64), kw.get("C", 32),
+                                                kw.get("fmt", 0), kw.get("tr", 0), kw.get("codes", _p(1)),
+                                                kw.get("amax", _p(2)), None)
+    assert q(T=None) == NULL and q(amax=None) == NULL
+    assert q(R=40) == SHAPE and q(fmt=2) == SHAPE
+    assert q(codes=_p(0)) == ALIAS
+    assert q() in (HIP, UNSUP)
+
+
+def test_fp8_workspace_query():
+    assert L.tpmlp_fp8_workspace_bytes(4, 32768, 3584, 3584) > 0
+    assert L.tpmlp_fp8_workspace_bytes(1, 64, 256, 512) > 0
+    assert L.tpmlp_fp8_workspace_bytes(1, 64, 256, 520) == 0   # F_i not a multiple of 16
+    assert L.tpmlp_fp8_workspace_bytes(0, 64, 256, 512) == 0
+    assert L.tpmlp_fp8_workspace_bytes(65, 64, 256, 512) == 0
+    # the workspace grows with t only through the amax slots
+    assert L.tpmlp_fp8_workspace_bytes(8, 2048, 4096, 2048) - L.tpmlp_fp8_workspace_bytes(1, 2048, 4096, 2048) <= 512

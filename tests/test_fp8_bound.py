@@ -1,0 +1,136 @@
+"""The element-wise FP8 acceptance bound (tests/fp8_bound.py) on the CPU.
+
+A float32 emulation of the FP8 path (float32 products of the codes, bf16 P and dP,
+float32 GeLU from torch's erf, codes from the oracle's encoder, whose bytes the GPU
+quantizer matches) must lie inside the bound, although it moves some FP8 codes
+away from the oracle's; the same emulation with a planted mistake (a tile of G
+codes lost, dP's scale taken from dZ's, dZ off by one row in dB, a 5% error in a
+scale) must fall outside it.
+"""
+import numpy as np
+import pytest
+
+import fp8_bound as FB
+from oracle import fp8 as F
+from oracle import oracle as O
+from tensor_transformer_mlp_03_amd import inputs as I
+
+torch = pytest.importorskip("torch")
+
+
+def _codes(T, fmt):
+    c, s = F.quantize(T, fmt)
+    return torch.from_numpy(F.decode(c, fmt).astype(np.float32)), np.float32(s)
+
+
+def _requant(T32: torch.Tensor, fmt):
+    """FP8 codes (as float32 values) and scale of a float32 tensor: amax, scale and
+    the float32 product T / s as the recipe states, codes by the oracle's encoder."""
+    return _codes(T32.numpy(), fmt)
+
+
+def _gelu32(p):
+    return torch.nn.functional.gelu(p)
+
+
+def _gelu_grad32(p):
+    cdf = 0.5 * (1.0 + torch.erf(p * np.float32(1.0 / np.sqrt(2.0))))
+    return cdf + p * torch.exp(-0.5 * p * p) * np.float32(1.0 / np.sqrt(2.0 * np.pi))
+
+
+def _bf16(x):
+    return x.to(torch.bfloat16).to(torch.float32)
+
+
+def emulate(X, A_sh, B_sh, dZ, mistake=None):
+    """The FP8 path in float32; returns Z, dX, [dA_i], [dB_i] and how many codes of
+    G and dP differ from the oracle's."""
+    cX, sX = _codes(X, F.E4M3)
+    cdZ, sdZ = _codes(dZ, F.E5M2)
+    Z = dX = None
+    dA, dB, moved = [], [], 0
+    dP_scales = []
+    cache = []
+    z_scale = np.float32(1.05) if mistake == "scale5pct" else np.float32(1.0)
+    for i, (A, B) in enumerate(zip(A_sh, B_sh)):
+        cA, sA = _codes(A, F.E4M3)
+        cB, sB = _codes(B, F.E4M3)
+        P = _bf16((cX @ cA) * np.float32(sX * sA))
+        cG, sG = _requant(_gelu32(P), F.E4M3)
+        if mistake == "tile" and i == 0:
+            cG = cG.clone()
+            cG[16:32, 16:32] = 0.0
+        Zi = (cG @ cB) * np.float32(sG * sB) * z_scale
+        dG = (cdZ @ cB.T) * np.float32(sdZ * sB)
+        dP = _bf16(dG * _gelu_grad32(P))
+        cdP, sdP = _requant(dP, F.E5M2)
+        dP_scales.append(sdP)
+        cache.append((cA, sA, cG, sG, cdP))
+        ref = FB.shard_moves(X, A, B, dZ)
+        moved += int(np.count_nonzero(cG.numpy() * np.float32(sG) != ref.fwd["Gq"].astype(np.float32)))
+        moved += int(np.count_nonzero(cdP.numpy() * np.float32(sdP)
+                                      != F.qdq(ref.bwd["dP"], F.E5M2).astype(np.float32)))
+        Z = Zi if Z is None else Z + Zi
+    for i, (cA, sA, cG, sG, cdP) in enumerate(cache):
+        sdP = sdZ if mistake == "dzscale" else dP_scales[i]
+        dZ_rows = torch.roll(cdZ, 1, 0) if (mistake == "offbyone" and i == 0) else cdZ
+        dB.append((cG.T @ dZ_rows) * np.float32(sG * sdZ))
+        dA.append((cX.T @ cdP) * np.float32(sX * sdP))
+        dXi = (cdP @ cA.T) * np.float32(sdP * sA)
+        dX = dXi if dX is None else dX + dXi
+    return Z.numpy(), dX.numpy(), [a.numpy() for a in dA], [b.numpy() for b in dB], moved
+
+
+def _case(M, H, Fi, t, seed):
+    w = I.custom_workload(seed, M=M, H=H, F_i=Fi, t=t, w_std=0.05)
+    inp = I.make_inputs(w)
+    X, dZ = O.decode_bf16(inp.X), O.decode_bf16(inp.dZ)
+    return X, [O.decode_bf16(a) for a in inp.A], [O.decode_bf16(b) for b in inp.B], dZ
+
+
+def _ratios(got, bounds):
+    Z, dX, dA, dB = got
+    r = {"Z": FB.worst_ratio(Z, bounds.Z, bounds.tol_Z)[0], "dX": FB.worst_ratio(dX, bounds.dX, bounds.tol_dX)[0]}
+    for i in range(len(dA)):
+        r[f"dA_{i}"] = FB.worst_ratio(dA[i], bounds.dA[i], bounds.tol_dA[i])[0]
+        r[f"dB_{i}"] = FB.worst_ratio(dB[i], bounds.dB[i], bounds.tol_dB[i])[0]
+    return r
+
+
+@pytest.fixture(scope="module")
+def case():
+    X, A, B, dZ = _case(528, 272, 400, 2, 402)
+    return X, A, B, dZ, FB.path_bounds(X, A, B, dZ)
+
+
+def test_float32_emulation_lies_inside_the_bound(case):
+    X, A, B, dZ, bounds = case
+    *got, moved = emulate(X, A, B, dZ)
+    r = _ratios(got, bounds)
+    assert max(r.values()) <= 1.0, r
+    # the bound is exercised: the emulation moves codes, and the interval admits moves
+    assert moved > 0
+    assert bounds.ambiguous_g > 0 and bounds.ambiguous_dp > 0
+
+
+@pytest.mark.parametrize("mistake, hit", [("tile", "Z"), ("dzscale", "dX"), ("dzscale", "dA_1"),
+                                          ("offbyone", "dB_0"), ("scale5pct", "Z")])
+def test_planted_mistakes_fall_outside_the_bound(case, mistake, hit):
+    X, A, B, dZ, bounds = case
+    *got, _ = emulate(X, A, B, dZ, mistake=mistake)
+    r = _ratios(got, bounds)
+    assert r[hit] > 1.0, r
+
+
+def test_unique_decisions_admit_no_move():
+    """Where no value is near a rounding boundary the bound is the bf16 path's rule,
+    up to the width GeLU's float32 error gives the scale of G (a few 1e-7 relative):
+    a single-element product of exactly representable values."""
+    X = np.array([[1.0]])
+    A = [np.array([[1.0]])]
+    B = [np.array([[0.5]])]
+    dZ = np.array([[1.0]])
+    b = FB.path_bounds(X, A, B, dZ)
+    assert b.ambiguous_g == 0 and b.ambiguous_dp == 0
+    assert float(b.tol_Z[0, 0]) == pytest.approx(O.tolerance(b.Z), abs=1e-6)
+    assert float(b.tol_dX[0, 0]) == pytest.approx(O.tolerance(b.dX), abs=1e-6)

@@ -1,0 +1,133 @@
+"""The FP8 path on the GPU (through the C ABI) against the FP8 oracle (oracle/fp8.py).
+
+* Quantization: the codes and the amax of tpmlp_fp8_quantize equal the oracle's,
+  byte for byte, for both formats, row-major and transposed (the codes are integer
+  decisions taken in float32 on both sides).
+* The t-shard FP8 forward and backward: Z, dX, dA_i, dB_i against the oracle's
+  FP8 path, element by element, within the bound of tests/fp8_bound.py (the bf16
+  path's rule plus the moves of the FP8 codes that float32 accumulation can
+  legitimately decide otherwise), and each stored bf16 P_i inside the interval of
+  admissible roundings that bound assumes.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import fp8_bound as FB
+import margins
+from oracle import fp8 as F
+from oracle import oracle as O
+from tensor_transformer_mlp_03_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from tensor_transformer_mlp_03_amd import _lib as L
+    L.lib()
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def check(name, got, ref, tol, ratios):
+    """Element-wise: |got - ref| <= tol (an array of ref's shape)."""
+    ratio, where = FB.worst_ratio(got, ref, tol)
+    ratios[name] = ratio
+    margins.record(name, ratio)
+    assert np.all(np.isfinite(got)), f"{name}: non-finite values"
+    assert ratio <= 1.0, (f"{name}: |err| / tol = {ratio:.3f} at {where}: got {float(got[where]):.6g}, "
+                          f"oracle {float(ref[where]):.6g}, tol {float(tol[where]):.3g}")
+
+
+def _bf16_bits(x):
+    f = np.asarray(x, dtype=np.float32)
+    b = f.view(np.uint32).astype(np.uint64)
+    return (((b + 0x7FFF + ((b >> 16) & 1)) >> 16) & 0xFFFF).astype(np.uint16)
+
+
+@pytest.mark.parametrize("shape", [(272, 400), (16, 16), (1040, 64)], ids=lambda s: f"{s[0]}x{s[1]}")
+@pytest.mark.parametrize("fmt", [0, 1], ids=["e4m3", "e5m2"])
+@pytest.mark.parametrize("transpose", [False, True], ids=["rows", "transposed"])
+def test_fp8_quantize_matches_oracle_bytes(shape, fmt, transpose):
+    from tensor_transformer_mlp_03_amd import _lib as L
+    R, C = shape
+    say(f"[fp8 quantize] {R}x{C} fmt={fmt} transpose={transpose}")
+    rng = np.random.default_rng(1000 + R + 7 * fmt)
+    # a wide spread of magnitudes (codes deep in the subnormals), exact and signed zeros
+    x = rng.standard_normal((R, C)) * np.exp2(rng.integers(-14, 3, (R, C)))
+    x[rng.random((R, C)) < 0.02] = 0.0
+    x[rng.random((R, C)) < 0.02] = -0.0
+    bits = _bf16_bits(x)
+    T32 = O.decode_bf16(bits).astype(np.float32)
+    ref_codes, ref_s = F.quantize(T32, F.E4M3 if fmt == 0 else F.E5M2)
+    Td = torch.from_numpy(bits.view(np.int16)).cuda()
+    codes = torch.empty((C, R) if transpose else (R, C), dtype=torch.uint8, device="cuda")
+    amax = torch.full((1,), float("nan"), dtype=torch.float32, device="cuda")
+    L.tpmlp_fp8_quantize(Td, fmt, transpose, codes, amax)
+    torch.cuda.synchronize()
+    got = codes.cpu().numpy()
+    if transpose:
+        got = got.T
+    assert amax.item() == float(np.max(np.abs(T32)))
+    diff = int((got != ref_codes).sum())
+    assert diff == 0, f"{diff} codes differ, e.g. {np.argwhere(got != ref_codes)[:3].tolist()}"
+
+
+FP8_CASES = [
+    # (M, H, F_i, t, store_p): multiples of 16, ragged against the 128 / 256 tiles
+    (96, 64, 48, 1, True),
+    (256, 192, 320, 2, True),
+    (528, 272, 400, 2, False),
+    (1040, 1056, 1072, 1, True),
+    (2048, 1024, 2048, 2, False),  # 256-row tiles, long K for dB / dA
+    (8192, 256, 512, 1, True),     # K = 8192 for dB / dA: split-K slices
+]
+
+
+@pytest.mark.parametrize("case", FP8_CASES,
+                         ids=lambda c: "x".join(map(str, c[:4])) + ("_store" if c[4] else "_recompute"))
+def test_fp8_path_matches_oracle(case):
+    from tensor_transformer_mlp_03_amd import _lib as L
+    from tensor_transformer_mlp_03_amd.device import to_device
+    M, H, F_, t, store = case
+    say(f"[fp8 path] M={M} H={H} F_i={F_} t={t} store_p={store}")
+    w = I.custom_workload(400 + t, M=M, H=H, F_i=F_, t=t, w_std=0.05)
+    inp = I.make_inputs(w)
+    X, dZ = to_device(inp.X), to_device(inp.dZ)
+    A = [to_device(a) for a in inp.A]
+    B = [to_device(b) for b in inp.B]
+    P = [torch.empty((M, F_), dtype=torch.int16, device="cuda") for _ in range(t)] if store else None
+    Z = torch.empty((M, H), dtype=torch.float32, device="cuda")
+    dX = torch.empty((M, H), dtype=torch.float32, device="cuda")
+    dA = [torch.empty((H, F_), dtype=torch.float32, device="cuda") for _ in range(t)]
+    dB = [torch.empty((F_, H), dtype=torch.float32, device="cuda") for _ in range(t)]
+    ws = torch.empty(L.tpmlp_fp8_workspace_bytes(t, M, H, F_), dtype=torch.uint8, device="cuda")
+    L.tpmlp_fp8_tp_fwd(X, A, B, P, Z, ws)
+    L.tpmlp_fp8_tp_bwd(dZ, X, A, B, P, dA, dB, dX, ws)
+    torch.cuda.synchronize()
+    Xo, dZo = O.decode_bf16(inp.X), O.decode_bf16(inp.dZ)
+    Ao, Bo = [O.decode_bf16(a) for a in inp.A], [O.decode_bf16(b) for b in inp.B]
+    bd = FB.path_bounds(Xo, Ao, Bo, dZo)
+    r = {}
+    check("Z", Z.cpu().numpy(), bd.Z, bd.tol_Z, r)
+    check("dX", dX.cpu().numpy(), bd.dX, bd.tol_dX, r)
+    for i in range(t):
+        check(f"dA_{i}", dA[i].cpu().numpy(), bd.dA[i], bd.tol_dA[i], r)
+        check(f"dB_{i}", dB[i].cpu().numpy(), bd.dB[i], bd.tol_dB[i], r)
+        if store:
+            Pg = O.decode_bf16(P[i].cpu().numpy().view(np.uint16))
+            sh = bd.shards[i]
+            outside = int(np.count_nonzero((Pg < sh.p_lo) | (Pg > sh.p_hi)))
+            assert outside == 0, f"P_{i}: {outside} values outside the admissible roundings"
+            r[f"P_{i} != oracle"] = int(np.count_nonzero(Pg != sh.fwd["P"]))
+    say("  err/tol:", {k: round(v, 3) for k, v in r.items()},
+        f"ambiguous codes G {bd.ambiguous_g} dP {bd.ambiguous_dp}")
