@@ -14,7 +14,10 @@ its average launch time from HIP events recorded on its stream inside the timed
 region), ``cpu_baseline`` is the CPU oracle timed on a bounded row sample of the
 same workload.
 
-    python bench.py [--config 3] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+``fp8`` times the FP8 path (E4M3 activations and weights, E5M2 gradients) on the
+first workload, against the dense fp8 MFMA peak.
+
+    python bench.py [--config 3] [--steps 20] [--warmup 5] [--no-cpu-baseline] [--no-fp8]
 """
 from __future__ import annotations
 
@@ -29,6 +32,7 @@ import time
 
 METRIC = "TP-MLP fwd+bwd TFLOP/s per rank shard (bf16) and % of MFMA dense peak"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+PEAK_FP8_TFLOPS = 5000.0   # MI355X dense fp8 MFMA, published
 ROOT = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(ROOT, "tensor_transformer_mlp_03_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
@@ -428,6 +432,56 @@ def measure(w, args, L, I, DeviceMLP, torch):
             "dropped": dropped}
 
 
+def measure_fp8(w, args, L, I, torch):
+    """The FP8 path (E4M3 activations and weights, E5M2 gradients, per-tensor
+    scaling) on the same workload and shards: warmup with every launch timed, then
+    timed steps with the dominant product kind's launches timed."""
+    from tensor_transformer_mlp_03_amd.device import DeviceFp8MLP
+    shards = list(w.shards_timed)
+    log(f"[bench] FP8 path on {w.name}, shards {shards}: generating inputs")
+    inp = I.make_inputs(w, shards=shards)
+    d = DeviceFp8MLP(inp, store_p=not w.recompute)
+    del inp
+    torch.cuda.synchronize()
+    per_launch = gemm_flops(w)
+    log("[bench] FP8 inputs resident; warmup")
+    L.tpmlp_timing_begin(64 * (len(shards) + 1) * max(args.warmup, 1))
+    for _ in range(max(args.warmup, 1)):
+        d.step()
+    torch.cuda.synchronize()
+    warm, _ = L.tpmlp_timing_end()
+    dom = max((n for n in per_launch if warm.get(n, (0, 0))[0]), key=lambda n: warm[n][1])
+    L.tpmlp_timing_begin_kinds(64 * (len(shards) + 1) * max(args.steps, 1), [dom])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        d.step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    stats, dropped = L.tpmlp_timing_end()
+    ms = (t1 - t0) * 1e3 / max(args.steps, 1)
+    value = w.model_flops_per_shard() * len(shards) / (ms * 1e-3) / 1e12
+    avg_s = stats[dom][1] * 1e-3 / stats[dom][0]
+    achieved = per_launch[dom] / avg_s / 1e12
+    total = sum(v[1] for v in warm.values())
+    kernels = {k: {"launches": c, "avg_us": round(ms_ * 1e3 / c, 2), "share": round(ms_ / total, 4),
+                   **({"tflops": round(per_launch[k] / (ms_ * 1e-3 / c) / 1e12, 1)} if k in per_launch else {})}
+               for k, (c, ms_) in warm.items() if c}
+    for name, k in sorted(kernels.items(), key=lambda kv: -kv[1]["share"]):
+        log(f"  fp8 {name:16s} {k}")
+    log(f"[bench] FP8 {w.name}: {ms:.4f} ms per step, {value:.1f} TFLOP/s")
+    del d
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return {"workload": w.name, "formats": "E4M3 X, A_i, B_i, G_i; E5M2 dZ, dP_i; per-tensor current scaling",
+            "shards_per_step": len(shards), "ms_per_step": round(ms, 4), "value": round(value, 2),
+            "unit": "TFLOP/s", "frac_of_fp8_peak": round(value / PEAK_FP8_TFLOPS, 4),
+            "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1), "peak": PEAK_FP8_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
+                         "avg_launch_us": round(avg_s * 1e6, 2)},
+            "kernels_warmup": kernels, "timing_dropped": dropped}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -438,6 +492,8 @@ def main():
                     help="second workload timed in the same run and reported under \"workloads\" (default 4, "
                          "the 530B-class shard; -1 for none; skipped with --graph or --trace-order)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-fp8", action="store_true",
+                    help="skip the FP8 path's measurement on the first workload (reported under \"fp8\")")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of one step captured into a HIP graph (for launch-latency-bound "
                          "workloads); per-kernel times then come from the eager warmup steps")
@@ -492,6 +548,9 @@ def main():
             "frac_of_peak": round(m2["value"] / PEAK_BF16_TFLOPS, 4),
             "hfu_tflops": round(m2["value"] * (14.0 if w2.recompute else 12.0) / 12.0, 2),
             "roofline": m2["roofline"], "timing_dropped": m2["dropped"]}
+    fp8 = None
+    if not (args.no_fp8 or args.graph or args.trace_order or args.full_weights) and w.backward:
+        fp8 = measure_fp8(w, args, L, I, torch)
     shards, ms_per_step, value, roofline, dropped = m["shards"], m["ms_per_step"], m["value"], m["roofline"], \
         m["dropped"]
 
@@ -522,6 +581,9 @@ def main():
     }
     if extra:
         result["workloads"] = extra
+    if fp8:
+        fp8["vs_bf16"] = round(fp8["value"] / value, 3)
+        result["fp8"] = fp8
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a row sample")
         result["cpu_baseline"] = cpu_baseline(w)

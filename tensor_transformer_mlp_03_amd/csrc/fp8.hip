@@ -29,20 +29,46 @@ __global__ void __launch_bounds__(256) fp8_zero_kernel(Fp8ZeroArgs a) {
 }
 
 // max |x| (or |GeLU(x)|) over a bf16 [R][C] tensor with rows of ld elements.
-__global__ void __launch_bounds__(256) fp8_amax_kernel(Fp8AmaxArgs a) {
-  const int64_t vpr = a.C / 8;  // 16-byte vectors per row
-  const int64_t nv = a.R * vpr;
-  float m = 0.0f;
-  for (int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x; v < nv; v += (int64_t)gridDim.x * 256) {
-    const int64_t r = v / vpr, c = (v - r * vpr) * 8;
-    const u32x4_t x = *reinterpret_cast<const u32x4_t*>(a.in + r * a.ld + c);
+// Each workgroup reduces its lanes' maxima through LDS and adds one atomic max
+// to the slot: atomics on one address serialize, so their count (the grid size,
+// at most AMAX_BLOCKS) is kept small.
+constexpr int AMAX_BLOCKS = 1024;
+
+__device__ __forceinline__ float amax8(const u32x4_t x, int gelu, float m) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float f = bf16_to_f32((uint16_t)(x[e / 2] >> (16 * (e % 2))));
-      m = fmaxf(m, fabsf(a.gelu ? gelu_f32(f) : f));
+  for (int e = 0; e < 8; ++e) {
+    const float f = bf16_to_f32((uint16_t)(x[e / 2] >> (16 * (e % 2))));
+    m = fmaxf(m, fabsf(gelu ? gelu_f32(f) : f));
+  }
+  return m;
+}
+
+__global__ void __launch_bounds__(256) fp8_amax_kernel(Fp8AmaxArgs a) {
+  __shared__ float red[4];
+  float m = 0.0f;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  if (a.ld == a.C) {  // contiguous rows: one flat range of 16-byte vectors
+    const int64_t nv = a.R * a.C / 8;
+    const u32x4_t* in = reinterpret_cast<const u32x4_t*>(a.in);
+    int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    for (; v + stride < nv; v += 2 * stride) {  // two loads in flight per lane
+      const u32x4_t x0 = in[v], x1 = in[v + stride];
+      m = amax8(x1, a.gelu, amax8(x0, a.gelu, m));
+    }
+    if (v < nv) m = amax8(in[v], a.gelu, m);
+  } else {
+    const int64_t vpr = a.C / 8;  // 16-byte vectors per row
+    const int64_t nv = a.R * vpr;
+    for (int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x; v < nv; v += stride) {
+      const int64_t r = v / vpr, c = (v - r * vpr) * 8;
+      m = amax8(*reinterpret_cast<const u32x4_t*>(a.in + r * a.ld + c), a.gelu, m);
     }
   }
-  slot_max(a.slot, m);
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    atomicMax(a.slot, __builtin_bit_cast(uint32_t, fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]))));
 }
 
 // out[r][c] = fp8(x[r][c] / s) (x = in, or GeLU(in)); 16 elements per thread.
@@ -124,7 +150,7 @@ hipError_t launch_fp8_zero(uint32_t* p, int n, hipStream_t s) {
 hipError_t launch_fp8_amax(const uint16_t* in, int64_t R, int64_t C, int64_t ld, bool gelu, uint32_t* slot,
                            hipStream_t s) {
   const int64_t nv = R * (C / 8);
-  const int blocks = (int)std::min<int64_t>(4096, std::max<int64_t>(1, (nv + 255) / 256));
+  const int blocks = (int)std::min<int64_t>(kern::AMAX_BLOCKS, std::max<int64_t>(1, (nv + 511) / 512));
   return launch_kernel(kern::fp8_amax_kernel, dim3(blocks), dim3(256), s, Fp8AmaxArgs{in, R, C, ld, gelu ? 1 : 0, slot});
 }
 

@@ -127,3 +127,38 @@ class DeviceMLP:
             self.step()
         torch.cuda.current_stream().wait_stream(s)
         return g
+
+
+class DeviceFp8MLP:
+    """Buffers of one workload for the FP8 path: bf16 inputs, float32 outputs, the
+    stored bf16 pre-activations (unless recomputed) and the FP8 workspace; ``step``
+    runs tpmlp_fp8_tp_fwd then tpmlp_fp8_tp_bwd over the placed shards (their
+    partials summed into Z and dX)."""
+
+    def __init__(self, inputs: Inputs, store_p: bool = True, device="cuda"):
+        import torch
+        w = inputs.workload
+        self.shards = [i for i in range(w.t) if inputs.A[i] is not None]
+        M, H, F = w.M, w.H, w.F_i
+        n = len(self.shards)
+        f32 = dict(dtype=torch.float32, device=device)
+        self.X = to_device(inputs.X, device)
+        self.dZ = to_device(inputs.dZ, device)
+        self.A = [to_device(inputs.A[i], device) for i in self.shards]
+        self.B = [to_device(inputs.B[i], device) for i in self.shards]
+        self.P = [torch.empty((M, F), dtype=torch.int16, device=device) for _ in range(n)] if store_p else None
+        self.Z = torch.empty((M, H), **f32)
+        self.dX = torch.empty((M, H), **f32)
+        self.dA = [torch.empty((H, F), **f32) for _ in range(n)]
+        self.dB = [torch.empty((F, H), **f32) for _ in range(n)]
+        self.ws = torch.empty(L.tpmlp_fp8_workspace_bytes(n, M, H, F), dtype=torch.uint8, device=device)
+
+    def forward(self):
+        L.tpmlp_fp8_tp_fwd(self.X, self.A, self.B, self.P, self.Z, self.ws)
+
+    def backward(self):
+        L.tpmlp_fp8_tp_bwd(self.dZ, self.X, self.A, self.B, self.P, self.dA, self.dB, self.dX, self.ws)
+
+    def step(self):
+        self.forward()
+        self.backward()
