@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define TPMLP_ABI_VERSION 10
+#define TPMLP_ABI_VERSION 11
 #define TPMLP_MAX_SHARDS 64
 
 typedef uint16_t tpmlp_bf16; /* raw bf16 bits */
@@ -55,7 +55,8 @@ typedef enum {
   TPMLP_ERR_SHARDS = 5,      /* t outside 1..TPMLP_MAX_SHARDS */
   TPMLP_ERR_HIP = 6,         /* a HIP runtime call or a kernel launch failed */
   TPMLP_ERR_UNSUPPORTED = 7, /* the current device is not gfx950 */
-  TPMLP_ERR_ALIAS = 8        /* an output overlaps an input or another output */
+  TPMLP_ERR_ALIAS = 8,       /* an output overlaps an input or another output */
+  TPMLP_ERR_NO_FORWARD = 9   /* tpmlp_fp8_tp_bwd: ws holds no forward of these inputs */
 } tpmlp_status;
 
 /* TPMLP_ABI_VERSION of the built library. */
@@ -272,7 +273,12 @@ tpmlp_status tpmlp_sp_bwd(const tpmlp_bf16* const* dZ_sl, const tpmlp_bf16* cons
  *
  * M, H and F_i must be positive multiples of 16, at most 2^23 (TPMLP_ERR_SHAPE).
  * The workspace (tpmlp_fp8_workspace_bytes, for either call) holds the FP8
- * copies of the operands, the amax slots and the split-K slices. */
+ * copies of the operands, the amax slots and the split-K slices.  The forward
+ * leaves there what the backward reuses: the codes of X and of every A_i and
+ * B_i in both layouts, the codes of G_i^T for every shard whose P_i it stored,
+ * and the scales of X, A_i, B_i and G_i; so a backward takes the workspace of
+ * the matching forward, unchanged in between (one workspace per forward whose
+ * backward is still to run, as for the stored P_i). */
 size_t tpmlp_fp8_workspace_bytes(int t, int64_t M, int64_t H, int64_t F_i);
 
 /* Z = sum_i Z_i with FP8 operands.  P_sh: NULL, or t entries (each nullable)
@@ -284,7 +290,11 @@ tpmlp_status tpmlp_fp8_tp_fwd(const tpmlp_bf16* X, const tpmlp_bf16* const* A_sh
 /* Backward with FP8 operands: dA_sh[i], dB_sh[i] (float32, shard i's weight
  * gradients) and dX = sum_i dX_i (float32).  P_sh: NULL => every shard
  * recomputes P_i with the FP8 forward product; otherwise t device pointers
- * written by tpmlp_fp8_tp_fwd. */
+ * written by tpmlp_fp8_tp_fwd.  ws: the workspace of the tpmlp_fp8_tp_fwd call
+ * with the same X, A_sh, B_sh, t, M, H, F_i (and, with P_sh, the same P_sh),
+ * not written since.  The library records each forward's arguments per
+ * workspace address on the host and returns TPMLP_ERR_NO_FORWARD when they do
+ * not match; it cannot see a workspace or an input changed in between. */
 tpmlp_status tpmlp_fp8_tp_bwd(const tpmlp_bf16* dZ, const tpmlp_bf16* X, const tpmlp_bf16* const* A_sh,
                               const tpmlp_bf16* const* B_sh, const tpmlp_bf16* const* P_sh,
                               float* const* dA_sh, float* const* dB_sh, float* dX, int t, int64_t M, int64_t H,

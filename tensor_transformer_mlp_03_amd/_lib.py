@@ -23,7 +23,7 @@ HEADER = os.path.join(os.path.dirname(PKG), "include", "tpmlp.h")
 STATUS = {
     0: "TPMLP_OK", 1: "TPMLP_ERR_NULL", 2: "TPMLP_ERR_SHAPE", 3: "TPMLP_ERR_ALIGN",
     4: "TPMLP_ERR_WORKSPACE", 5: "TPMLP_ERR_SHARDS", 6: "TPMLP_ERR_HIP",
-    7: "TPMLP_ERR_UNSUPPORTED", 8: "TPMLP_ERR_ALIAS",
+    7: "TPMLP_ERR_UNSUPPORTED", 8: "TPMLP_ERR_ALIAS", 9: "TPMLP_ERR_NO_FORWARD",
 }
 KERNEL_COUNT = 12
 MAX_SHARDS = 64

@@ -163,6 +163,8 @@ struct Fp8QuantArgs {
   int64_t R, C, ld_in, ld_out;
   int gelu, fmt;
   const uint32_t* slot;
+  uint8_t* out2;  // transposed launches: also the row-major codes (nullable)
+  int64_t ld_out2;
 };
 // p[0 .. n) = 0 (amax slots; n <= 256 per call).
 hipError_t launch_fp8_zero(uint32_t* p, int n, hipStream_t s);
@@ -171,8 +173,10 @@ hipError_t launch_fp8_zero(uint32_t* p, int n, hipStream_t s);
 hipError_t launch_fp8_amax(const uint16_t* in, int64_t R, int64_t C, int64_t ld, bool gelu, uint32_t* slot,
                            hipStream_t s);
 // FP8 codes of a bf16 [R][C] tensor (or of its GeLU) under the scale in `slot`:
-// out [R][ld_out] bytes, or with transpose out [C][ld_out] (R, C multiples of 16).
+// out [R][ld_out] bytes, or with transpose out [C][ld_out] (R, C multiples of 16)
+// and, when out_rows is set, the row-major codes in out_rows [R][ld_rows] too.
 hipError_t launch_fp8_quant(const uint16_t* in, int64_t R, int64_t C, int64_t ld_in, bool gelu, int fmt,
-                            const uint32_t* slot, uint8_t* out, int64_t ld_out, bool transpose, hipStream_t s);
+                            const uint32_t* slot, uint8_t* out, int64_t ld_out, bool transpose, hipStream_t s,
+                            uint8_t* out_rows = nullptr, int64_t ld_rows = 0);
 
 }  // namespace tpmlp

@@ -99,7 +99,8 @@ __global__ void __launch_bounds__(256) fp8_quant_kernel(Fp8QuantArgs a) {
 }
 
 // out[c][r] = fp8(x[r][c] / s): one 64 x 64 tile per workgroup, staged in LDS as
-// bytes at a 80-byte pitch (16-byte aligned rows for the 16-byte reads).
+// bytes at a 80-byte pitch (16-byte aligned rows for the 16-byte reads).  With
+// out2 set, the same codes also go to out2[r][c] (row-major), from the one read.
 __global__ void __launch_bounds__(256) fp8_quant_t_kernel(Fp8QuantArgs a) {
   constexpr int PITCH = 80;
   __shared__ __attribute__((aligned(16))) uint8_t tile[64 * PITCH];
@@ -122,15 +123,19 @@ __global__ void __launch_bounds__(256) fp8_quant_t_kernel(Fp8QuantArgs a) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) f[e] = 0.0f;
     }
+    u32x4_t o;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       float g[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) g[e] = (a.gelu ? gelu_f32(f[4 * w + e]) : f[4 * w + e]) * inv;
       const uint32_t q = fp8_pack4(g[0], g[1], g[2], g[3], a.fmt);
+      o[w] = q;
 #pragma unroll
       for (int e = 0; e < 4; ++e) tile[(cs + 4 * w + e) * PITCH + r] = (uint8_t)(q >> (8 * e));
     }
+    if (a.out2 && r0 + r < a.R && c0 + cs < a.C)
+      *reinterpret_cast<u32x4_t*>(a.out2 + (r0 + r) * a.ld_out2 + c0 + cs) = o;
   }
   __syncthreads();
   {
@@ -155,8 +160,10 @@ hipError_t launch_fp8_amax(const uint16_t* in, int64_t R, int64_t C, int64_t ld,
 }
 
 hipError_t launch_fp8_quant(const uint16_t* in, int64_t R, int64_t C, int64_t ld_in, bool gelu, int fmt,
-                            const uint32_t* slot, uint8_t* out, int64_t ld_out, bool transpose, hipStream_t s) {
-  const Fp8QuantArgs a{in, out, R, C, ld_in, ld_out, gelu ? 1 : 0, fmt, slot};
+                            const uint32_t* slot, uint8_t* out, int64_t ld_out, bool transpose, hipStream_t s,
+                            uint8_t* out_rows, int64_t ld_rows) {
+  const Fp8QuantArgs a{in, out, R, C, ld_in, ld_out, gelu ? 1 : 0, fmt, slot, transpose ? out_rows : nullptr,
+                       ld_rows};
   if (transpose)
     return launch_kernel(kern::fp8_quant_t_kernel, dim3((unsigned)((C + 63) / 64), (unsigned)((R + 63) / 64)),
                          dim3(256), s, a);

@@ -769,13 +769,25 @@ GemmPlan plan_gemm_whole(int64_t M, int64_t N, int64_t K) {
   return best;
 }
 
-// Amax slots: X, dZ, then per shard A_i, B_i, G_i, dP_i.
-constexpr int SLOT_X = 0, SLOT_DZ = 1;
-inline int slot_of(int i, int which) { return 2 + 4 * i + which; }  // which: 0 A, 1 B, 2 G, 3 dP
+// Amax slots: the forward's (X, then A_i, B_i, G_i per shard), then the
+// backward's (dZ, then dP_i per shard), so that each call clears one range.
+constexpr int SLOT_X = 0;
+inline int slot_fwd(int i, int which) { return 1 + 3 * i + which; }  // which: 0 A, 1 B, 2 G
+inline int slot_bwd0(int t) { return 1 + 3 * t; }                     // dZ; dP_i at slot_bwd0(t) + 1 + i
+inline int n_slots(int t) { return 2 + 4 * t; }
 
+// Workspace of the FP8 path.  What the forward writes and the backward reads
+// stays put between the two calls: qX, qXt, the per-shard weight codes and
+// qGt (shards whose P_i the forward stored).  The rest is per-call scratch.
 struct Fp8Layout {
   GemmPlan g1, g2, gdg, gdb, gda, gdx;
   size_t slots, qX, qXt, qdZ, qdZt, qAt, qBt, qA, qB, P, qG, qGt, dP, qdP, qdPt, part, total;
+  size_t hf, mf;  // bytes of one shard's weight codes, of one shard's G codes
+  size_t qAt_i(int i) const { return qAt + size_t(i) * hf; }
+  size_t qBt_i(int i) const { return qBt + size_t(i) * hf; }
+  size_t qA_i(int i) const { return qA + size_t(i) * hf; }
+  size_t qB_i(int i) const { return qB + size_t(i) * hf; }
+  size_t qGt_i(int i) const { return qGt + size_t(i) * mf; }
 };
 
 Fp8Layout fp8_layout(int t, int64_t M, int64_t H, int64_t F) {
@@ -787,24 +799,26 @@ Fp8Layout fp8_layout(int t, int64_t M, int64_t H, int64_t F) {
   L.gda = plan_gemm(H, F, M);
   L.gdx = plan_gemm(M, H, F);
   const size_t mh = size_t(M) * H, hf = size_t(H) * F, mf = size_t(M) * F;
+  L.hf = align_up(hf);
+  L.mf = align_up(mf);
   size_t o = 0;
   auto take = [&](size_t bytes) {
     const size_t at = o;
     o += align_up(bytes);
     return at;
   };
-  L.slots = take(size_t(2 + 4 * t) * 4);
+  L.slots = take(size_t(n_slots(t)) * 4);
   L.qX = take(mh);
   L.qXt = take(mh);
   L.qdZ = take(mh);
   L.qdZt = take(mh);
-  L.qAt = take(hf);
-  L.qBt = take(hf);
-  L.qA = take(hf);
-  L.qB = take(hf);
+  L.qAt = take(size_t(t) * L.hf);
+  L.qBt = take(size_t(t) * L.hf);
+  L.qA = take(size_t(t) * L.hf);
+  L.qB = take(size_t(t) * L.hf);
   L.P = take(mf * 2);
   L.qG = take(mf);
-  L.qGt = take(mf);
+  L.qGt = take(size_t(t) * L.mf);
   L.dP = take(mf * 2);
   L.qdP = take(mf);
   L.qdPt = take(mf);
@@ -814,9 +828,6 @@ Fp8Layout fp8_layout(int t, int64_t M, int64_t H, int64_t F) {
   return L;
 }
 
-// One FP8 product (codes a [M][lda], b [N][ldb], both K-contiguous) with its
-// epilogue; the scales come from the operands' amax slots.  Split along K, the
-// scaled float32 slices are reduced by the bf16 path's reduction.
 hipError_t run_gemm_fp8(int kind, int fa, int fb, Epi epi, const uint8_t* a, int64_t lda, const uint8_t* b,
                         int64_t ldb, int64_t M, int64_t N, int64_t K, const GemmPlan& p, void* out,
                         const uint16_t* aux, const uint32_t* amax_a, const uint32_t* amax_b, uint32_t* amax_out,
@@ -873,6 +884,13 @@ hipError_t fp8_quant(const tpmlp_bf16* in, int64_t R, int64_t C, bool gelu, int 
                [&] { return launch_fp8_quant(in, R, C, C, gelu, fmt, slot, out, transpose ? R : C, transpose, s); });
 }
 
+// Both layouts from one read: rows [R][C] into `rows`, the transpose [C][R] into `cols`.
+hipError_t fp8_quant2(const tpmlp_bf16* in, int64_t R, int64_t C, bool gelu, int fmt, const uint32_t* slot,
+                      uint8_t* rows, uint8_t* cols, hipStream_t s) {
+  return timed(TPMLP_K_FP8_QUANT, s,
+               [&] { return launch_fp8_quant(in, R, C, C, gelu, fmt, slot, cols, R, true, s, rows, C); });
+}
+
 #define F8_TRY(x)                         \
   do {                                    \
     const hipError_t e_ = (x);            \
@@ -883,35 +901,35 @@ hipError_t enqueue_fp8_fwd(const tpmlp_bf16* X, const tpmlp_bf16* const* A_sh, c
                            tpmlp_bf16* const* P_sh, float* Z, int t, int64_t M, int64_t H, int64_t F, void* ws,
                            hipStream_t s) {
   const Fp8Layout L = fp8_layout(t, M, H, F);
+  auto q = [&](size_t off) { return reinterpret_cast<uint8_t*>(ws_at(ws, off)); };
   uint32_t* slots = reinterpret_cast<uint32_t*>(ws_at(ws, L.slots));
-  uint8_t* qX = reinterpret_cast<uint8_t*>(ws_at(ws, L.qX));
-  uint8_t* qAt = reinterpret_cast<uint8_t*>(ws_at(ws, L.qAt));
-  uint8_t* qBt = reinterpret_cast<uint8_t*>(ws_at(ws, L.qBt));
-  uint8_t* qG = reinterpret_cast<uint8_t*>(ws_at(ws, L.qG));
   float* part = reinterpret_cast<float*>(ws_at(ws, L.part));
-  F8_TRY(timed(TPMLP_K_FP8_QUANT, s, [&] { return launch_fp8_zero(slots, 2 + 4 * t, s); }));
+  F8_TRY(timed(TPMLP_K_FP8_QUANT, s, [&] { return launch_fp8_zero(slots, n_slots(t), s); }));
   F8_TRY(fp8_amax(X, M, H, false, slots + SLOT_X, s));
-  F8_TRY(fp8_quant(X, M, H, false, F8_E4M3, slots + SLOT_X, qX, false, s));
+  F8_TRY(fp8_quant2(X, M, H, false, F8_E4M3, slots + SLOT_X, q(L.qX), q(L.qXt), s));  // X, X^T
   for (int i = 0; i < t; ++i) {
-    uint32_t* sA = slots + slot_of(i, 0);
-    uint32_t* sB = slots + slot_of(i, 1);
-    uint32_t* sG = slots + slot_of(i, 2);
-    tpmlp_bf16* P = (P_sh && P_sh[i]) ? P_sh[i] : reinterpret_cast<tpmlp_bf16*>(ws_at(ws, L.P));
+    uint32_t* sA = slots + slot_fwd(i, 0);
+    uint32_t* sB = slots + slot_fwd(i, 1);
+    uint32_t* sG = slots + slot_fwd(i, 2);
+    const bool keep = P_sh && P_sh[i];
+    tpmlp_bf16* P = keep ? P_sh[i] : reinterpret_cast<tpmlp_bf16*>(ws_at(ws, L.P));
     F8_TRY(fp8_amax(A_sh[i], H, F, false, sA, s));
-    F8_TRY(fp8_quant(A_sh[i], H, F, false, F8_E4M3, sA, qAt, true, s));  // A_i^T [F][H]
+    F8_TRY(fp8_quant2(A_sh[i], H, F, false, F8_E4M3, sA, q(L.qA_i(i)), q(L.qAt_i(i)), s));  // A_i, A_i^T
     F8_TRY(fp8_amax(B_sh[i], F, H, false, sB, s));
-    F8_TRY(fp8_quant(B_sh[i], F, H, false, F8_E4M3, sB, qBt, true, s));  // B_i^T [H][F]
-    F8_TRY(run_gemm_fp8(TPMLP_K_FWD_GEMM1_GELU, F8_E4M3, F8_E4M3, EPI_BF16, qX, H, qAt, H, M, F, H, L.g1, P, nullptr,
-                        slots + SLOT_X, sA, sG, true, part, s));
-    F8_TRY(fp8_quant(P, M, F, true, F8_E4M3, sG, qG, false, s));
-    F8_TRY(run_gemm_fp8(TPMLP_K_FWD_GEMM2, F8_E4M3, F8_E4M3, i == 0 ? EPI_F32 : EPI_F32_ACC, qG, F, qBt, F, M, H, F,
-                        L.g2, Z, nullptr, sG, sB, nullptr, false, part, s));
+    F8_TRY(fp8_quant2(B_sh[i], F, H, false, F8_E4M3, sB, q(L.qB_i(i)), q(L.qBt_i(i)), s));  // B_i, B_i^T
+    F8_TRY(run_gemm_fp8(TPMLP_K_FWD_GEMM1_GELU, F8_E4M3, F8_E4M3, EPI_BF16, q(L.qX), H, q(L.qAt_i(i)), H, M, F, H,
+                        L.g1, P, nullptr, slots + SLOT_X, sA, sG, true, part, s));
+    if (keep)  // G_i for the second product and G_i^T for the backward's dB_i
+      F8_TRY(fp8_quant2(P, M, F, true, F8_E4M3, sG, q(L.qG), q(L.qGt_i(i)), s));
+    else
+      F8_TRY(fp8_quant(P, M, F, true, F8_E4M3, sG, q(L.qG), false, s));
+    F8_TRY(run_gemm_fp8(TPMLP_K_FWD_GEMM2, F8_E4M3, F8_E4M3, i == 0 ? EPI_F32 : EPI_F32_ACC, q(L.qG), F,
+                        q(L.qBt_i(i)), F, M, H, F, L.g2, Z, nullptr, sG, sB, nullptr, false, part, s));
   }
   return hipSuccess;
 }
 
-hipError_t enqueue_fp8_bwd(const tpmlp_bf16* dZ, const tpmlp_bf16* X, const tpmlp_bf16* const* A_sh,
-                           const tpmlp_bf16* const* B_sh, const tpmlp_bf16* const* P_sh, float* const* dA_sh,
+hipError_t enqueue_fp8_bwd(const tpmlp_bf16* dZ, const tpmlp_bf16* const* P_sh, float* const* dA_sh,
                            float* const* dB_sh, float* dX, int t, int64_t M, int64_t H, int64_t F, void* ws,
                            hipStream_t s) {
   const Fp8Layout L = fp8_layout(t, M, H, F);
@@ -920,46 +938,96 @@ hipError_t enqueue_fp8_bwd(const tpmlp_bf16* dZ, const tpmlp_bf16* X, const tpml
   tpmlp_bf16* dP = reinterpret_cast<tpmlp_bf16*>(ws_at(ws, L.dP));
   float* part = reinterpret_cast<float*>(ws_at(ws, L.part));
   const bool recompute = P_sh == nullptr;
-  F8_TRY(timed(TPMLP_K_FP8_QUANT, s, [&] { return launch_fp8_zero(slots, 2 + 4 * t, s); }));
-  F8_TRY(fp8_amax(dZ, M, H, false, slots + SLOT_DZ, s));
-  F8_TRY(fp8_quant(dZ, M, H, false, F8_E5M2, slots + SLOT_DZ, q(L.qdZ), false, s));
-  F8_TRY(fp8_quant(dZ, M, H, false, F8_E5M2, slots + SLOT_DZ, q(L.qdZt), true, s));  // dZ^T [H][M]
-  F8_TRY(fp8_amax(X, M, H, false, slots + SLOT_X, s));
-  F8_TRY(fp8_quant(X, M, H, false, F8_E4M3, slots + SLOT_X, q(L.qXt), true, s));  // X^T [H][M]
-  if (recompute) F8_TRY(fp8_quant(X, M, H, false, F8_E4M3, slots + SLOT_X, q(L.qX), false, s));
+  uint32_t* sdZ = slots + slot_bwd0(t);
+  F8_TRY(timed(TPMLP_K_FP8_QUANT, s, [&] { return launch_fp8_zero(sdZ, 1 + t, s); }));
+  F8_TRY(fp8_amax(dZ, M, H, false, sdZ, s));
+  F8_TRY(fp8_quant2(dZ, M, H, false, F8_E5M2, sdZ, q(L.qdZ), q(L.qdZt), s));  // dZ, dZ^T
   for (int i = 0; i < t; ++i) {
-    uint32_t* sA = slots + slot_of(i, 0);
-    uint32_t* sB = slots + slot_of(i, 1);
-    uint32_t* sG = slots + slot_of(i, 2);
-    uint32_t* sdP = slots + slot_of(i, 3);
-    F8_TRY(fp8_amax(A_sh[i], H, F, false, sA, s));
-    F8_TRY(fp8_quant(A_sh[i], H, F, false, F8_E4M3, sA, q(L.qA), false, s));  // A_i [H][F]
-    F8_TRY(fp8_amax(B_sh[i], F, H, false, sB, s));
-    F8_TRY(fp8_quant(B_sh[i], F, H, false, F8_E4M3, sB, q(L.qB), false, s));  // B_i [F][H]
+    uint32_t* sA = slots + slot_fwd(i, 0);
+    uint32_t* sB = slots + slot_fwd(i, 1);
+    uint32_t* sG = slots + slot_fwd(i, 2);
+    uint32_t* sdP = sdZ + 1 + i;
     const tpmlp_bf16* P;
-    if (recompute) {
+    if (recompute) {  // the forward's product again (its codes and scales are in ws); same P_i, same amax
       tpmlp_bf16* Pw = reinterpret_cast<tpmlp_bf16*>(ws_at(ws, L.P));
-      F8_TRY(fp8_quant(A_sh[i], H, F, false, F8_E4M3, sA, q(L.qAt), true, s));
-      F8_TRY(run_gemm_fp8(TPMLP_K_BWD_RECOMPUTE, F8_E4M3, F8_E4M3, EPI_BF16, q(L.qX), H, q(L.qAt), H, M, F, H, L.g1,
-                          Pw, nullptr, slots + SLOT_X, sA, sG, true, part, s));
+      F8_TRY(run_gemm_fp8(TPMLP_K_BWD_RECOMPUTE, F8_E4M3, F8_E4M3, EPI_BF16, q(L.qX), H, q(L.qAt_i(i)), H, M, F, H,
+                          L.g1, Pw, nullptr, slots + SLOT_X, sA, sG, true, part, s));
+      F8_TRY(fp8_quant(Pw, M, F, true, F8_E4M3, sG, q(L.qGt_i(i)), true, s));  // G_i^T [F][M]
       P = Pw;
     } else {
-      P = P_sh[i];
-      F8_TRY(fp8_amax(P, M, F, true, sG, s));
+      P = P_sh[i];  // G_i^T's codes came with the forward
     }
-    F8_TRY(fp8_quant(P, M, F, true, F8_E4M3, sG, q(L.qGt), true, s));  // G_i^T [F][M]
-    F8_TRY(run_gemm_fp8(TPMLP_K_BWD_DGELU, F8_E5M2, F8_E4M3, EPI_DGELU, q(L.qdZ), H, q(L.qB), H, M, F, H, L.gdg, dP, P,
-                        slots + SLOT_DZ, sB, sdP, false, part, s));
-    F8_TRY(fp8_quant(dP, M, F, false, F8_E5M2, sdP, q(L.qdP), false, s));
-    F8_TRY(fp8_quant(dP, M, F, false, F8_E5M2, sdP, q(L.qdPt), true, s));  // dP_i^T [F][M]
-    F8_TRY(run_gemm_fp8(TPMLP_K_BWD_DB, F8_E4M3, F8_E5M2, EPI_F32, q(L.qGt), M, q(L.qdZt), M, F, H, M, L.gdb, dB_sh[i],
-                        nullptr, sG, slots + SLOT_DZ, nullptr, false, part, s));
-    F8_TRY(run_gemm_fp8(TPMLP_K_BWD_DA, F8_E4M3, F8_E5M2, EPI_F32, q(L.qXt), M, q(L.qdPt), M, H, F, M, L.gda, dA_sh[i],
-                        nullptr, slots + SLOT_X, sdP, nullptr, false, part, s));
-    F8_TRY(run_gemm_fp8(TPMLP_K_BWD_DX, F8_E5M2, F8_E4M3, i == 0 ? EPI_F32 : EPI_F32_ACC, q(L.qdP), F, q(L.qA), F, M,
-                        H, F, L.gdx, dX, nullptr, sdP, sA, nullptr, false, part, s));
+    F8_TRY(run_gemm_fp8(TPMLP_K_BWD_DGELU, F8_E5M2, F8_E4M3, EPI_DGELU, q(L.qdZ), H, q(L.qB_i(i)), H, M, F, H, L.gdg,
+                        dP, P, sdZ, sB, sdP, false, part, s));
+    F8_TRY(fp8_quant2(dP, M, F, false, F8_E5M2, sdP, q(L.qdP), q(L.qdPt), s));  // dP_i, dP_i^T
+    F8_TRY(run_gemm_fp8(TPMLP_K_BWD_DB, F8_E4M3, F8_E5M2, EPI_F32, q(L.qGt_i(i)), M, q(L.qdZt), M, F, H, M, L.gdb,
+                        dB_sh[i], nullptr, sG, sdZ, nullptr, false, part, s));
+    F8_TRY(run_gemm_fp8(TPMLP_K_BWD_DA, F8_E4M3, F8_E5M2, EPI_F32, q(L.qXt), M, q(L.qdPt), M, H, F, M, L.gda,
+                        dA_sh[i], nullptr, slots + SLOT_X, sdP, nullptr, false, part, s));
+    F8_TRY(run_gemm_fp8(TPMLP_K_BWD_DX, F8_E5M2, F8_E4M3, i == 0 ? EPI_F32 : EPI_F32_ACC, q(L.qdP), F, q(L.qA_i(i)),
+                        F, M, H, F, L.gdx, dX, nullptr, sdP, sA, nullptr, false, part, s));
   }
   return hipSuccess;
+}
+
+// The arguments of the last forward per workspace address, for the backward's
+// check that the workspace holds the forward of its inputs.
+struct Fp8Stamp {
+  int t;
+  int64_t M, H, F;
+  int device;
+  const void* X;
+  std::vector<const void*> A, B, P;  // P: nullptr where the forward did not store P_i
+};
+std::mutex g_fp8_mu;
+std::vector<std::pair<const void*, Fp8Stamp>> g_fp8_stamps;
+
+Fp8Stamp make_stamp(const void* X, const tpmlp_bf16* const* A_sh, const tpmlp_bf16* const* B_sh,
+                    const tpmlp_bf16* const* P_sh, int t, int64_t M, int64_t H, int64_t F) {
+  Fp8Stamp st{t, M, H, F, -1, X, {}, {}, {}};
+  (void)hipGetDevice(&st.device);
+  for (int i = 0; i < t; ++i) {
+    st.A.push_back(A_sh[i]);
+    st.B.push_back(B_sh[i]);
+    st.P.push_back(P_sh ? static_cast<const void*>(P_sh[i]) : nullptr);
+  }
+  return st;
+}
+
+// A forward overwrites what an earlier forward left in ws, so its stamp goes
+// first, and the new one is recorded only once every launch was enqueued.
+void forget_fp8_forward(const void* ws) {
+  std::lock_guard<std::mutex> lk(g_fp8_mu);
+  g_fp8_stamps.erase(std::remove_if(g_fp8_stamps.begin(), g_fp8_stamps.end(),
+                                    [&](const std::pair<const void*, Fp8Stamp>& e) { return e.first == ws; }),
+                     g_fp8_stamps.end());
+}
+
+void record_fp8_forward(const void* ws, Fp8Stamp st) {
+  std::lock_guard<std::mutex> lk(g_fp8_mu);
+  for (auto& e : g_fp8_stamps)
+    if (e.first == ws) {
+      e.second = std::move(st);
+      return;
+    }
+  g_fp8_stamps.emplace_back(ws, std::move(st));
+}
+
+// "" when ws holds the forward of these arguments, else what differs.
+std::string check_fp8_forward(const void* ws, const Fp8Stamp& want, bool store) {
+  std::lock_guard<std::mutex> lk(g_fp8_mu);
+  for (const auto& e : g_fp8_stamps) {
+    if (e.first != ws) continue;
+    const Fp8Stamp& got = e.second;
+    if (got.t != want.t || got.M != want.M || got.H != want.H || got.F != want.F) return "other shapes or t";
+    if (got.device != want.device) return "another device";
+    if (got.X != want.X || got.A != want.A || got.B != want.B) return "other X, A_sh or B_sh";
+    if (store)
+      for (int i = 0; i < want.t; ++i)
+        if (!got.P[i] || got.P[i] != want.P[i]) return "P_sh[" + std::to_string(i) + "] was not stored there by it";
+    return "";
+  }
+  return "no forward on this workspace";
 }
 #undef F8_TRY
 
@@ -983,6 +1051,7 @@ const char* tpmlp_status_str(int status) {
     case TPMLP_ERR_HIP: return "HIP error";
     case TPMLP_ERR_UNSUPPORTED: return "unsupported device";
     case TPMLP_ERR_ALIAS: return "output overlaps another buffer";
+    case TPMLP_ERR_NO_FORWARD: return "workspace holds no forward of these inputs";
     default: return "unknown status";
   }
 }
@@ -1420,8 +1489,11 @@ tpmlp_status tpmlp_fp8_tp_fwd(const tpmlp_bf16* X, const tpmlp_bf16* const* A_sh
   }
   if ((st = check_alias(outs, ins))) return st;
   if ((st = check_device())) return st;
+  forget_fp8_forward(ws);
   hipError_t e = enqueue_fp8_fwd(X, A_sh, B_sh, P_sh, Z, t, M, H, F_i, ws, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? TPMLP_OK : hip_fail(e, "tpmlp_fp8_tp_fwd launch");
+  if (e != hipSuccess) return hip_fail(e, "tpmlp_fp8_tp_fwd launch");
+  record_fp8_forward(ws, make_stamp(X, A_sh, B_sh, P_sh, t, M, H, F_i));
+  return TPMLP_OK;
 }
 
 tpmlp_status tpmlp_fp8_tp_bwd(const tpmlp_bf16* dZ, const tpmlp_bf16* X, const tpmlp_bf16* const* A_sh,
@@ -1453,9 +1525,10 @@ tpmlp_status tpmlp_fp8_tp_bwd(const tpmlp_bf16* dZ, const tpmlp_bf16* X, const t
     outs.push_back({dB_sh[i], hf * 4, "dB_sh[i]"});
   }
   if ((st = check_alias(outs, ins))) return st;
+  const std::string why = check_fp8_forward(ws, make_stamp(X, A_sh, B_sh, P_sh, t, M, H, F_i), P_sh != nullptr);
+  if (!why.empty()) return fail(TPMLP_ERR_NO_FORWARD, "ws does not hold the forward of these inputs: " + why);
   if ((st = check_device())) return st;
-  hipError_t e =
-      enqueue_fp8_bwd(dZ, X, A_sh, B_sh, P_sh, dA_sh, dB_sh, dX, t, M, H, F_i, ws, static_cast<hipStream_t>(stream));
+  hipError_t e = enqueue_fp8_bwd(dZ, P_sh, dA_sh, dB_sh, dX, t, M, H, F_i, ws, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? TPMLP_OK : hip_fail(e, "tpmlp_fp8_tp_bwd launch");
 }
 

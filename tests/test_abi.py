@@ -27,7 +27,7 @@ pytestmark = [
     pytest.mark.skipif(_gpu_visible(), reason="made-up device addresses are only passed where no GPU is visible"),
 ]
 
-OK, NULL, SHAPE, ALIGN, WS, SHARDS, HIP, UNSUP, ALIAS = range(9)
+OK, NULL, SHAPE, ALIGN, WS, SHARDS, HIP, UNSUP, ALIAS, NO_FORWARD = range(10)
 
 
 def test_exports_every_declared_function():
@@ -99,7 +99,7 @@ def test_last_error_is_per_thread():
 
 
 def test_version_and_strings():
-    assert L.tpmlp_abi_version() == 10
+    assert L.tpmlp_abi_version() == 11
     assert L.tpmlp_status_str(0) == "ok"
     assert L.tpmlp_status_str(ALIAS) == "output overlaps another buffer"
     assert L.tpmlp_status_str(99) == "unknown status"
@@ -407,7 +407,10 @@ def test_fp8_argument_errors():
         need = L.tpmlp_fp8_workspace_bytes(2, 128, 64, 96)
         assert _fp8(fn, wsb=need - 1)[0] == WS
         assert _fp8(fn, ws=_p(60) + 8)[0] == ALIGN
-        assert _fp8(fn)[0] in (HIP, UNSUP)  # valid: reaches the device check
+    assert _fp8("fwd")[0] in (HIP, UNSUP)  # valid: reaches the device check
+    # a backward needs the workspace of its forward (none has run here)
+    st, msg = _fp8("bwd")
+    assert st == NO_FORWARD and "no forward on this workspace" in msg
     st, msg = _fp8("fwd", Z=_p(0))  # Z on top of X
     assert st == ALIAS
     st, msg = _fp8("bwd", dX=_p(1))
@@ -428,5 +431,7 @@ def test_fp8_workspace_query():
     assert L.tpmlp_fp8_workspace_bytes(1, 64, 256, 520) == 0   # F_i not a multiple of 16
     assert L.tpmlp_fp8_workspace_bytes(0, 64, 256, 512) == 0
     assert L.tpmlp_fp8_workspace_bytes(65, 64, 256, 512) == 0
-    # the workspace grows with t only through the amax slots
-    assert L.tpmlp_fp8_workspace_bytes(8, 2048, 4096, 2048) - L.tpmlp_fp8_workspace_bytes(1, 2048, 4096, 2048) <= 512
+    # per shard the workspace keeps the weight codes in both layouts and G_i^T's
+    # codes for the backward: 4 H F_i + M F_i bytes, plus the amax slots
+    grow = L.tpmlp_fp8_workspace_bytes(8, 2048, 4096, 2048) - L.tpmlp_fp8_workspace_bytes(1, 2048, 4096, 2048)
+    assert 7 * (4 * 4096 * 2048 + 2048 * 2048) <= grow <= 7 * (4 * 4096 * 2048 + 2048 * 2048) + 4096
