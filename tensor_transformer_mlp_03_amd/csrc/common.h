@@ -146,6 +146,14 @@ constexpr int TILE_BK = 64;
 hipError_t launch_gemm_fp8(TileCfg tile, int fmt_a, int fmt_b, Epi epi, const GemmArgs& args, int splits,
                            hipStream_t stream);
 
+// An amax slot: AMAX_SUB 32-bit words, AMAX_SUB_STRIDE words apart so that each
+// sits in its own 128-byte line.  Atomics on one address serialize (about 12 ns
+// each here), so writers spread theirs over the words and readers take the max.
+// The library's workspace slots have AMAX_SUB words; a caller's single float
+// (tpmlp_fp8_quantize) is a slot of one word.
+constexpr int AMAX_SUB = 16, AMAX_SUB_STRIDE = 32;
+constexpr int AMAX_SLOT_WORDS = AMAX_SUB * AMAX_SUB_STRIDE;
+
 // The FP8 element-wise kernels (fp8.hip).
 struct Fp8ZeroArgs {
   uint32_t* p;
@@ -154,8 +162,8 @@ struct Fp8ZeroArgs {
 struct Fp8AmaxArgs {
   const uint16_t* in;
   int64_t R, C, ld;
-  int gelu;
   uint32_t* slot;
+  int nsub;  // words of the slot (epilogue.h)
 };
 struct Fp8QuantArgs {
   const uint16_t* in;
@@ -163,20 +171,21 @@ struct Fp8QuantArgs {
   int64_t R, C, ld_in, ld_out;
   int gelu, fmt;
   const uint32_t* slot;
+  int nsub;       // words of the slot (epilogue.h)
   uint8_t* out2;  // transposed launches: also the row-major codes (nullable)
   int64_t ld_out2;
 };
-// p[0 .. n) = 0 (amax slots; n <= 256 per call).
+// p[0 .. n) = 0 (amax slots).
 hipError_t launch_fp8_zero(uint32_t* p, int n, hipStream_t s);
-// slot = max(slot, max |x|) over a bf16 [R][C] tensor (rows of ld; C % 8 == 0), x
-// the element or, with gelu, its GeLU.
-hipError_t launch_fp8_amax(const uint16_t* in, int64_t R, int64_t C, int64_t ld, bool gelu, uint32_t* slot,
+// slot = max(slot, max |x|) over a bf16 [R][C] tensor (rows of ld; C % 8 == 0);
+// the slot has nsub words (epilogue.h; 1 or AMAX_SUB).
+hipError_t launch_fp8_amax(const uint16_t* in, int64_t R, int64_t C, int64_t ld, uint32_t* slot, int nsub,
                            hipStream_t s);
 // FP8 codes of a bf16 [R][C] tensor (or of its GeLU) under the scale in `slot`:
 // out [R][ld_out] bytes, or with transpose out [C][ld_out] (R, C multiples of 16)
 // and, when out_rows is set, the row-major codes in out_rows [R][ld_rows] too.
 hipError_t launch_fp8_quant(const uint16_t* in, int64_t R, int64_t C, int64_t ld_in, bool gelu, int fmt,
-                            const uint32_t* slot, uint8_t* out, int64_t ld_out, bool transpose, hipStream_t s,
+                            const uint32_t* slot, int nsub, uint8_t* out, int64_t ld_out, bool transpose, hipStream_t s,
                             uint8_t* out_rows = nullptr, int64_t ld_rows = 0);
 
 }  // namespace tpmlp

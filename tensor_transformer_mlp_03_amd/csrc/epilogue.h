@@ -19,6 +19,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "common.h"
+
 namespace tpmlp {
 
 __device__ __forceinline__ uint16_t f32_to_bf16(float x) {
@@ -105,15 +107,28 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-// Max over a wave of per-lane values (all >= 0), added to an amax slot by lane 0.
-__device__ __forceinline__ void slot_max(uint32_t* slot, float lane_max) {
+// An amax slot (AMAX_SUB etc. in common.h) is `nsub` 32-bit words of float
+// bits; the values are >= 0, so unsigned order is float order.
+
+// Max over a wave of per-lane values (all >= 0), added to one word of the slot
+// by lane 0 (nsub a power of two).
+__device__ __forceinline__ void slot_max(uint32_t* slot, int nsub, float lane_max) {
   const float m = wave_max(lane_max);
-  if ((threadIdx.x & 63) == 0) atomicMax(slot, __builtin_bit_cast(uint32_t, m));
+  if ((threadIdx.x & 63) == 0) {
+    const int sub = (int)(blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6)) & (nsub - 1);
+    atomicMax(slot + sub * AMAX_SUB_STRIDE, __builtin_bit_cast(uint32_t, m));
+  }
 }
 
-// Scale of a tensor from its amax (float bits, the value is >= 0).
-__device__ __forceinline__ float fp8_scale(uint32_t amax_bits, float fmax) {
-  const float amax = __builtin_bit_cast(float, amax_bits);
+__device__ __forceinline__ float slot_read(const uint32_t* slot, int nsub) {
+  uint32_t m = 0;
+  for (int i = 0; i < nsub; ++i) m = max(m, slot[i * AMAX_SUB_STRIDE]);
+  return __builtin_bit_cast(float, m);
+}
+
+// Scale of a tensor from its amax slot.
+__device__ __forceinline__ float fp8_scale(const uint32_t* slot, int nsub, float fmax) {
+  const float amax = slot_read(slot, nsub);
   return amax == 0.0f ? 1.0f : amax / fmax;
 }
 

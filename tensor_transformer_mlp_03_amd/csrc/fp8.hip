@@ -28,18 +28,15 @@ __global__ void __launch_bounds__(256) fp8_zero_kernel(Fp8ZeroArgs a) {
   for (int i = blockIdx.x * 256 + threadIdx.x; i < a.n; i += gridDim.x * 256) a.p[i] = 0u;
 }
 
-// max |x| (or |GeLU(x)|) over a bf16 [R][C] tensor with rows of ld elements.
+// max |x| over a bf16 [R][C] tensor with rows of ld elements.
 // Each workgroup reduces its lanes' maxima through LDS and adds one atomic max
-// to the slot: atomics on one address serialize, so their count (the grid size,
-// at most AMAX_BLOCKS) is kept small.
+// to a word of the slot: atomics on one address serialize, so their count (the
+// grid size, at most AMAX_BLOCKS) is kept small and spread over the slot's words.
 constexpr int AMAX_BLOCKS = 1024;
 
-__device__ __forceinline__ float amax8(const u32x4_t x, int gelu, float m) {
+__device__ __forceinline__ float amax8(const u32x4_t x, float m) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float f = bf16_to_f32((uint16_t)(x[e / 2] >> (16 * (e % 2))));
-    m = fmaxf(m, fabsf(gelu ? gelu_f32(f) : f));
-  }
+  for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(bf16_to_f32((uint16_t)(x[e / 2] >> (16 * (e % 2))))));
   return m;
 }
 
@@ -53,27 +50,28 @@ __global__ void __launch_bounds__(256) fp8_amax_kernel(Fp8AmaxArgs a) {
     int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x;
     for (; v + stride < nv; v += 2 * stride) {  // two loads in flight per lane
       const u32x4_t x0 = in[v], x1 = in[v + stride];
-      m = amax8(x1, a.gelu, amax8(x0, a.gelu, m));
+      m = amax8(x1, amax8(x0, m));
     }
-    if (v < nv) m = amax8(in[v], a.gelu, m);
+    if (v < nv) m = amax8(in[v], m);
   } else {
     const int64_t vpr = a.C / 8;  // 16-byte vectors per row
     const int64_t nv = a.R * vpr;
     for (int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x; v < nv; v += stride) {
       const int64_t r = v / vpr, c = (v - r * vpr) * 8;
-      m = amax8(*reinterpret_cast<const u32x4_t*>(a.in + r * a.ld + c), a.gelu, m);
+      m = amax8(*reinterpret_cast<const u32x4_t*>(a.in + r * a.ld + c), m);
     }
   }
   m = wave_max(m);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
   if (threadIdx.x == 0)
-    atomicMax(a.slot, __builtin_bit_cast(uint32_t, fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]))));
+    atomicMax(a.slot + (blockIdx.x & (a.nsub - 1)) * AMAX_SUB_STRIDE,
+              __builtin_bit_cast(uint32_t, fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]))));
 }
 
 // out[r][c] = fp8(x[r][c] / s) (x = in, or GeLU(in)); 16 elements per thread.
 __global__ void __launch_bounds__(256) fp8_quant_kernel(Fp8QuantArgs a) {
-  const float inv = 1.0f / fp8_scale(*a.slot, fp8_fmax(a.fmt));
+  const float inv = 1.0f / fp8_scale(a.slot, a.nsub, fp8_fmax(a.fmt));
   const int64_t vpr = a.C / 16;
   const int64_t nv = a.R * vpr;
   for (int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x; v < nv; v += (int64_t)gridDim.x * 256) {
@@ -104,7 +102,7 @@ __global__ void __launch_bounds__(256) fp8_quant_kernel(Fp8QuantArgs a) {
 __global__ void __launch_bounds__(256) fp8_quant_t_kernel(Fp8QuantArgs a) {
   constexpr int PITCH = 80;
   __shared__ __attribute__((aligned(16))) uint8_t tile[64 * PITCH];
-  const float inv = 1.0f / fp8_scale(*a.slot, fp8_fmax(a.fmt));
+  const float inv = 1.0f / fp8_scale(a.slot, a.nsub, fp8_fmax(a.fmt));
   const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
   const int t = threadIdx.x;
   {
@@ -149,20 +147,21 @@ __global__ void __launch_bounds__(256) fp8_quant_t_kernel(Fp8QuantArgs a) {
 }  // namespace kern
 
 hipError_t launch_fp8_zero(uint32_t* p, int n, hipStream_t s) {
-  return launch_kernel(kern::fp8_zero_kernel, dim3(1), dim3(256), s, Fp8ZeroArgs{p, n});
+  const int blocks = std::max(1, std::min(64, (n + 255) / 256));
+  return launch_kernel(kern::fp8_zero_kernel, dim3(blocks), dim3(256), s, Fp8ZeroArgs{p, n});
 }
 
-hipError_t launch_fp8_amax(const uint16_t* in, int64_t R, int64_t C, int64_t ld, bool gelu, uint32_t* slot,
+hipError_t launch_fp8_amax(const uint16_t* in, int64_t R, int64_t C, int64_t ld, uint32_t* slot, int nsub,
                            hipStream_t s) {
   const int64_t nv = R * (C / 8);
   const int blocks = (int)std::min<int64_t>(kern::AMAX_BLOCKS, std::max<int64_t>(1, (nv + 511) / 512));
-  return launch_kernel(kern::fp8_amax_kernel, dim3(blocks), dim3(256), s, Fp8AmaxArgs{in, R, C, ld, gelu ? 1 : 0, slot});
+  return launch_kernel(kern::fp8_amax_kernel, dim3(blocks), dim3(256), s, Fp8AmaxArgs{in, R, C, ld, slot, nsub});
 }
 
 hipError_t launch_fp8_quant(const uint16_t* in, int64_t R, int64_t C, int64_t ld_in, bool gelu, int fmt,
-                            const uint32_t* slot, uint8_t* out, int64_t ld_out, bool transpose, hipStream_t s,
+                            const uint32_t* slot, int nsub, uint8_t* out, int64_t ld_out, bool transpose, hipStream_t s,
                             uint8_t* out_rows, int64_t ld_rows) {
-  const Fp8QuantArgs a{in, out, R, C, ld_in, ld_out, gelu ? 1 : 0, fmt, slot, transpose ? out_rows : nullptr,
+  const Fp8QuantArgs a{in, out, R, C, ld_in, ld_out, gelu ? 1 : 0, fmt, slot, nsub, transpose ? out_rows : nullptr,
                        ld_rows};
   if (transpose)
     return launch_kernel(kern::fp8_quant_t_kernel, dim3((unsigned)((C + 63) / 64), (unsigned)((R + 63) / 64)),

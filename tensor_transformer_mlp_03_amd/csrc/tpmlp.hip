@@ -771,10 +771,12 @@ GemmPlan plan_gemm_whole(int64_t M, int64_t N, int64_t K) {
 
 // Amax slots: the forward's (X, then A_i, B_i, G_i per shard), then the
 // backward's (dZ, then dP_i per shard), so that each call clears one range.
+// Each slot is AMAX_SLOT_WORDS words (epilogue.h).
 constexpr int SLOT_X = 0;
 inline int slot_fwd(int i, int which) { return 1 + 3 * i + which; }  // which: 0 A, 1 B, 2 G
 inline int slot_bwd0(int t) { return 1 + 3 * t; }                     // dZ; dP_i at slot_bwd0(t) + 1 + i
 inline int n_slots(int t) { return 2 + 4 * t; }
+inline uint32_t* slot_at(uint32_t* slots, int k) { return slots + size_t(k) * AMAX_SLOT_WORDS; }
 
 // Workspace of the FP8 path.  What the forward writes and the backward reads
 // stays put between the two calls: qX, qXt, the per-shard weight codes and
@@ -807,7 +809,7 @@ Fp8Layout fp8_layout(int t, int64_t M, int64_t H, int64_t F) {
     o += align_up(bytes);
     return at;
   };
-  L.slots = take(size_t(n_slots(t)) * 4);
+  L.slots = take(size_t(n_slots(t)) * AMAX_SLOT_WORDS * 4);
   L.qX = take(mh);
   L.qXt = take(mh);
   L.qdZ = take(mh);
@@ -874,21 +876,22 @@ hipError_t run_gemm_fp8(int kind, int fa, int fb, Epi epi, const uint8_t* a, int
                [&] { return launch_splitk_epilogue(epi, part, p.splits, M, N, out, nullptr, nullptr, N, M, s); });
 }
 
-hipError_t fp8_amax(const tpmlp_bf16* in, int64_t R, int64_t C, bool gelu, uint32_t* slot, hipStream_t s) {
-  return timed(TPMLP_K_FP8_QUANT, s, [&] { return launch_fp8_amax(in, R, C, C, gelu, slot, s); });
+hipError_t fp8_amax(const tpmlp_bf16* in, int64_t R, int64_t C, uint32_t* slot, hipStream_t s) {
+  return timed(TPMLP_K_FP8_QUANT, s, [&] { return launch_fp8_amax(in, R, C, C, slot, AMAX_SUB, s); });
 }
 
 hipError_t fp8_quant(const tpmlp_bf16* in, int64_t R, int64_t C, bool gelu, int fmt, const uint32_t* slot,
                      uint8_t* out, bool transpose, hipStream_t s) {
-  return timed(TPMLP_K_FP8_QUANT, s,
-               [&] { return launch_fp8_quant(in, R, C, C, gelu, fmt, slot, out, transpose ? R : C, transpose, s); });
+  return timed(TPMLP_K_FP8_QUANT, s, [&] {
+    return launch_fp8_quant(in, R, C, C, gelu, fmt, slot, AMAX_SUB, out, transpose ? R : C, transpose, s);
+  });
 }
 
 // Both layouts from one read: rows [R][C] into `rows`, the transpose [C][R] into `cols`.
 hipError_t fp8_quant2(const tpmlp_bf16* in, int64_t R, int64_t C, bool gelu, int fmt, const uint32_t* slot,
                       uint8_t* rows, uint8_t* cols, hipStream_t s) {
   return timed(TPMLP_K_FP8_QUANT, s,
-               [&] { return launch_fp8_quant(in, R, C, C, gelu, fmt, slot, cols, R, true, s, rows, C); });
+               [&] { return launch_fp8_quant(in, R, C, C, gelu, fmt, slot, AMAX_SUB, cols, R, true, s, rows, C); });
 }
 
 #define F8_TRY(x)                         \
@@ -904,21 +907,21 @@ hipError_t enqueue_fp8_fwd(const tpmlp_bf16* X, const tpmlp_bf16* const* A_sh, c
   auto q = [&](size_t off) { return reinterpret_cast<uint8_t*>(ws_at(ws, off)); };
   uint32_t* slots = reinterpret_cast<uint32_t*>(ws_at(ws, L.slots));
   float* part = reinterpret_cast<float*>(ws_at(ws, L.part));
-  F8_TRY(timed(TPMLP_K_FP8_QUANT, s, [&] { return launch_fp8_zero(slots, n_slots(t), s); }));
-  F8_TRY(fp8_amax(X, M, H, false, slots + SLOT_X, s));
-  F8_TRY(fp8_quant2(X, M, H, false, F8_E4M3, slots + SLOT_X, q(L.qX), q(L.qXt), s));  // X, X^T
+  F8_TRY(timed(TPMLP_K_FP8_QUANT, s, [&] { return launch_fp8_zero(slots, n_slots(t) * AMAX_SLOT_WORDS, s); }));
+  F8_TRY(fp8_amax(X, M, H, slot_at(slots, SLOT_X), s));
+  F8_TRY(fp8_quant2(X, M, H, false, F8_E4M3, slot_at(slots, SLOT_X), q(L.qX), q(L.qXt), s));  // X, X^T
   for (int i = 0; i < t; ++i) {
-    uint32_t* sA = slots + slot_fwd(i, 0);
-    uint32_t* sB = slots + slot_fwd(i, 1);
-    uint32_t* sG = slots + slot_fwd(i, 2);
+    uint32_t* sA = slot_at(slots, slot_fwd(i, 0));
+    uint32_t* sB = slot_at(slots, slot_fwd(i, 1));
+    uint32_t* sG = slot_at(slots, slot_fwd(i, 2));
     const bool keep = P_sh && P_sh[i];
     tpmlp_bf16* P = keep ? P_sh[i] : reinterpret_cast<tpmlp_bf16*>(ws_at(ws, L.P));
-    F8_TRY(fp8_amax(A_sh[i], H, F, false, sA, s));
+    F8_TRY(fp8_amax(A_sh[i], H, F, sA, s));
     F8_TRY(fp8_quant2(A_sh[i], H, F, false, F8_E4M3, sA, q(L.qA_i(i)), q(L.qAt_i(i)), s));  // A_i, A_i^T
-    F8_TRY(fp8_amax(B_sh[i], F, H, false, sB, s));
+    F8_TRY(fp8_amax(B_sh[i], F, H, sB, s));
     F8_TRY(fp8_quant2(B_sh[i], F, H, false, F8_E4M3, sB, q(L.qB_i(i)), q(L.qBt_i(i)), s));  // B_i, B_i^T
     F8_TRY(run_gemm_fp8(TPMLP_K_FWD_GEMM1_GELU, F8_E4M3, F8_E4M3, EPI_BF16, q(L.qX), H, q(L.qAt_i(i)), H, M, F, H,
-                        L.g1, P, nullptr, slots + SLOT_X, sA, sG, true, part, s));
+                        L.g1, P, nullptr, slot_at(slots, SLOT_X), sA, sG, true, part, s));
     if (keep)  // G_i for the second product and G_i^T for the backward's dB_i
       F8_TRY(fp8_quant2(P, M, F, true, F8_E4M3, sG, q(L.qG), q(L.qGt_i(i)), s));
     else
@@ -938,20 +941,20 @@ hipError_t enqueue_fp8_bwd(const tpmlp_bf16* dZ, const tpmlp_bf16* const* P_sh, 
   tpmlp_bf16* dP = reinterpret_cast<tpmlp_bf16*>(ws_at(ws, L.dP));
   float* part = reinterpret_cast<float*>(ws_at(ws, L.part));
   const bool recompute = P_sh == nullptr;
-  uint32_t* sdZ = slots + slot_bwd0(t);
-  F8_TRY(timed(TPMLP_K_FP8_QUANT, s, [&] { return launch_fp8_zero(sdZ, 1 + t, s); }));
-  F8_TRY(fp8_amax(dZ, M, H, false, sdZ, s));
+  uint32_t* sdZ = slot_at(slots, slot_bwd0(t));
+  F8_TRY(timed(TPMLP_K_FP8_QUANT, s, [&] { return launch_fp8_zero(sdZ, (1 + t) * AMAX_SLOT_WORDS, s); }));
+  F8_TRY(fp8_amax(dZ, M, H, sdZ, s));
   F8_TRY(fp8_quant2(dZ, M, H, false, F8_E5M2, sdZ, q(L.qdZ), q(L.qdZt), s));  // dZ, dZ^T
   for (int i = 0; i < t; ++i) {
-    uint32_t* sA = slots + slot_fwd(i, 0);
-    uint32_t* sB = slots + slot_fwd(i, 1);
-    uint32_t* sG = slots + slot_fwd(i, 2);
-    uint32_t* sdP = sdZ + 1 + i;
+    uint32_t* sA = slot_at(slots, slot_fwd(i, 0));
+    uint32_t* sB = slot_at(slots, slot_fwd(i, 1));
+    uint32_t* sG = slot_at(slots, slot_fwd(i, 2));
+    uint32_t* sdP = slot_at(slots, slot_bwd0(t) + 1 + i);
     const tpmlp_bf16* P;
     if (recompute) {  // the forward's product again (its codes and scales are in ws); same P_i, same amax
       tpmlp_bf16* Pw = reinterpret_cast<tpmlp_bf16*>(ws_at(ws, L.P));
       F8_TRY(run_gemm_fp8(TPMLP_K_BWD_RECOMPUTE, F8_E4M3, F8_E4M3, EPI_BF16, q(L.qX), H, q(L.qAt_i(i)), H, M, F, H,
-                          L.g1, Pw, nullptr, slots + SLOT_X, sA, sG, true, part, s));
+                          L.g1, Pw, nullptr, slot_at(slots, SLOT_X), sA, sG, true, part, s));
       F8_TRY(fp8_quant(Pw, M, F, true, F8_E4M3, sG, q(L.qGt_i(i)), true, s));  // G_i^T [F][M]
       P = Pw;
     } else {
@@ -963,7 +966,7 @@ hipError_t enqueue_fp8_bwd(const tpmlp_bf16* dZ, const tpmlp_bf16* const* P_sh, 
     F8_TRY(run_gemm_fp8(TPMLP_K_BWD_DB, F8_E4M3, F8_E5M2, EPI_F32, q(L.qGt_i(i)), M, q(L.qdZt), M, F, H, M, L.gdb,
                         dB_sh[i], nullptr, sG, sdZ, nullptr, false, part, s));
     F8_TRY(run_gemm_fp8(TPMLP_K_BWD_DA, F8_E4M3, F8_E5M2, EPI_F32, q(L.qXt), M, q(L.qdPt), M, H, F, M, L.gda,
-                        dA_sh[i], nullptr, slots + SLOT_X, sdP, nullptr, false, part, s));
+                        dA_sh[i], nullptr, slot_at(slots, SLOT_X), sdP, nullptr, false, part, s));
     F8_TRY(run_gemm_fp8(TPMLP_K_BWD_DX, F8_E5M2, F8_E4M3, i == 0 ? EPI_F32 : EPI_F32_ACC, q(L.qdP), F, q(L.qA_i(i)),
                         F, M, H, F, L.gdx, dX, nullptr, sdP, sA, nullptr, false, part, s));
   }
@@ -1543,9 +1546,10 @@ tpmlp_status tpmlp_fp8_quantize(const tpmlp_bf16* T, int64_t R, int64_t C, int f
   if ((st = check_device())) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint32_t* slot = reinterpret_cast<uint32_t*>(amax);
-  hipError_t e = launch_fp8_zero(slot, 1, s);
-  if (e == hipSuccess) e = launch_fp8_amax(T, R, C, C, false, slot, s);
-  if (e == hipSuccess) e = launch_fp8_quant(T, R, C, C, false, fmt, slot, codes, transpose ? R : C, transpose != 0, s);
+  hipError_t e = launch_fp8_zero(slot, 1, s);  // the caller's float is a one-word slot
+  if (e == hipSuccess) e = launch_fp8_amax(T, R, C, C, slot, 1, s);
+  if (e == hipSuccess)
+    e = launch_fp8_quant(T, R, C, C, false, fmt, slot, 1, codes, transpose ? R : C, transpose != 0, s);
   return e == hipSuccess ? TPMLP_OK : hip_fail(e, "tpmlp_fp8_quantize launch");
 }
 

@@ -432,6 +432,7 @@ def test_fp8_workspace_query():
     assert L.tpmlp_fp8_workspace_bytes(0, 64, 256, 512) == 0
     assert L.tpmlp_fp8_workspace_bytes(65, 64, 256, 512) == 0
     # per shard the workspace keeps the weight codes in both layouts and G_i^T's
-    # codes for the backward: 4 H F_i + M F_i bytes, plus the amax slots
+    # codes for the backward: 4 H F_i + M F_i bytes, plus four amax slots of 2 KiB
     grow = L.tpmlp_fp8_workspace_bytes(8, 2048, 4096, 2048) - L.tpmlp_fp8_workspace_bytes(1, 2048, 4096, 2048)
-    assert 7 * (4 * 4096 * 2048 + 2048 * 2048) <= grow <= 7 * (4 * 4096 * 2048 + 2048 * 2048) + 4096
+    per_shard = 4 * 4096 * 2048 + 2048 * 2048
+    assert 7 * per_shard <= grow <= 7 * (per_shard + 4 * 2048) + 4096

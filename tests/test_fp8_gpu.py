@@ -185,3 +185,48 @@ def test_fp8_backward_needs_its_forward():
     L.tpmlp_fp8_tp_bwd(dZ, X2, A, B, None, dA, dB, dX, ws)
     torch.cuda.synchronize()
     say("  err/tol:", {k: round(v, 3) for k, v in r.items()})
+
+
+FP8_CANARY_CASES = [
+    (528, 272, 400, 2, True),   # ragged against every tile shape
+    (8192, 256, 512, 1, True),  # split-K weight gradients
+    (272, 144, 176, 2, False),  # recomputed P_i
+]
+
+
+@pytest.mark.parametrize("case", FP8_CANARY_CASES,
+                         ids=lambda c: "x".join(map(str, c[:4])) + ("_store" if c[4] else "_recompute"))
+def test_fp8_no_writes_outside_outputs(case):
+    """Every output and the workspace sit inside a larger allocation whose bands
+    before and after hold a byte pattern; a forward and backward leave the bands
+    unchanged."""
+    from tensor_transformer_mlp_03_amd import _lib as L
+    from tensor_transformer_mlp_03_amd.device import to_device
+    M, H, F_, t, store = case
+    say(f"[fp8 canary] M={M} H={H} F_i={F_} t={t} store_p={store}")
+    w = I.custom_workload(470 + t, M=M, H=H, F_i=F_, t=t, w_std=0.05)
+    inp = I.make_inputs(w)
+    X, dZ = to_device(inp.X), to_device(inp.dZ)
+    A = [to_device(a) for a in inp.A]
+    B = [to_device(b) for b in inp.B]
+    BAND = 4096  # bytes on each side, a multiple of 256
+    bufs = []
+
+    def banded(shape, dtype):
+        n = int(np.prod(shape)) * torch.empty((), dtype=dtype).element_size()
+        raw = torch.full((n + 2 * BAND,), 0xA5, dtype=torch.uint8, device="cuda")
+        bufs.append((raw, n))
+        return raw[BAND:BAND + n].view(dtype).view(*shape)
+
+    P = [banded((M, F_), torch.int16) for _ in range(t)] if store else None
+    Z, dX = banded((M, H), torch.float32), banded((M, H), torch.float32)
+    dA = [banded((H, F_), torch.float32) for _ in range(t)]
+    dB = [banded((F_, H), torch.float32) for _ in range(t)]
+    ws = banded((L.tpmlp_fp8_workspace_bytes(t, M, H, F_),), torch.uint8)
+    L.tpmlp_fp8_tp_fwd(X, A, B, P, Z, ws)
+    L.tpmlp_fp8_tp_bwd(dZ, X, A, B, P, dA, dB, dX, ws)
+    torch.cuda.synchronize()
+    for k, (raw, n) in enumerate(bufs):
+        head, tail = raw[:BAND], raw[BAND + n:]
+        assert bool((head == 0xA5).all()) and bool((tail == 0xA5).all()), f"buffer {k}: a band was written"
+    assert torch.isfinite(Z).all() and torch.isfinite(dX).all()
