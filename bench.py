@@ -47,14 +47,14 @@ def source_hash() -> str:
     return h.hexdigest()
 
 
-def traffic_path(workload_name: str) -> str:
-    return os.path.join(PROFILES, f"{workload_name}_traffic.md")
+def traffic_path(workload_name: str, fp8: bool = False) -> str:
+    return os.path.join(PROFILES, f"{workload_name}{'_fp8' if fp8 else ''}_traffic.md")
 
 
-def read_traffic(workload_name: str):
+def read_traffic(workload_name: str, fp8: bool = False):
     """{kernel kind: HBM bytes per launch} from the committed counter summary, or None
     if there is none or it was taken from other sources than the current ones."""
-    path = traffic_path(workload_name)
+    path = traffic_path(workload_name, fp8)
     if not os.path.exists(path):
         return None
     sha, table = None, {}
@@ -97,6 +97,23 @@ def gemm_alg_bytes(w, recompute, fold=False):
         "transpose": 4 * M * H,                                                       # X -> X^T, dZ -> dZ^T
         # X, A_i, B_i -> float32 partials of Z_i, one per chunk of 64 intermediate columns (+P)
         "fwd_fused": 2 * (M * H + 2 * H * F) + 4 * M * H * (-(-F // 64)) + (0 if recompute else 2 * M * F),
+    }
+
+
+def fp8_alg_bytes(w, fold=False):
+    """Algorithmic HBM bytes of one launch of each product kind of the FP8 path:
+    FP8 codes 1 byte, bf16 2, float32 4; operands read once, outputs written once
+    (fold: as in gemm_alg_bytes, the accumulating launches' running-sum reads)."""
+    M, H, F = w.M, w.H, w.F_i
+    acc = 4 * M * H * (w.t - 1) / w.t if fold else 0
+    return {
+        "fwd_gemm1_gelu": (M * H + H * F) + 2 * M * F,              # X, A_i codes -> P (bf16)
+        "bwd_recompute": (M * H + H * F) + 2 * M * F,
+        "fwd_gemm2": (M * F + F * H) + 4 * M * H + acc,             # G, B_i codes -> Z
+        "bwd_dgelu": (M * H + F * H) + 2 * M * F + 2 * M * F,       # dZ, B_i codes, P -> dP (bf16)
+        "bwd_dB": (M * F + M * H) + 4 * F * H,                      # G^T, dZ^T codes -> dB_i
+        "bwd_dA": (M * H + M * F) + 4 * H * F,                      # X^T, dP^T codes -> dA_i
+        "bwd_dX": (M * F + H * F) + 4 * M * H + acc,                # dP, A_i codes -> dX
     }
 
 
@@ -208,11 +225,14 @@ def _copy_scale(csv_path, counter, mib):
     return (mib * 1024.0) / (sum(vals) / len(vals))  # expected KiB / counted KiB
 
 
-def summarize(d, config):
-    """Write profiles/<workload>_kernels.md and profiles/<workload>_traffic.md from the
-    rocprofv3 outputs in directory d (layout of the commands quoted in them)."""
+def summarize(d, config, fp8=False):
+    """Write profiles/<workload>[_fp8]_kernels.md and ..._traffic.md (and _counters.md)
+    from the rocprofv3 outputs in directory d (layout of the commands quoted in
+    them); fp8: the runs timed the FP8 path only (--fp8-only)."""
     from tensor_transformer_mlp_03_amd import inputs as I
     w = I.CONFIGS[config]
+    tag = "_fp8" if fp8 else ""
+    path_name = "FP8 path, " if fp8 else ""
     cmd = json.load(open(os.path.join(d, "commands.json")))
     stats = list(csv.DictReader(open(glob.glob(os.path.join(d, "trace", "*_kernel_stats.csv"))[0])))
     order = json.load(open(os.path.join(d, "order.json")))
@@ -228,8 +248,8 @@ def summarize(d, config):
         a["n"] += 1
         a["fetch"] += f["counters"]["FETCH_SIZE"] * 1024 * f_scale
         a["write"] += wr["counters"]["WRITE_SIZE"] * 1024 * w_scale
-    alg = gemm_alg_bytes(w, w.recompute, fold=folds(w))
-    if "transpose" in agg:
+    alg = fp8_alg_bytes(w, fold=folds(w)) if fp8 else gemm_alg_bytes(w, w.recompute, fold=folds(w))
+    if "transpose" in agg and not fp8:
         # A backward step transposes X and dZ ([M,H]) once each, and dP ([M,F_i]) once per
         # shard when the planner transposes it for dA (large H: the library's rule is
         # restated in dp_transposed); every further launch is a weight transpose
@@ -241,15 +261,15 @@ def summarize(d, config):
                             + (n_t - n_x - n_p) * 4 * w.H * w.F_i) / n_t
     alg["shard_sum"] = (w.t + 1) * w.M * w.H * 4  # t float32 partials in, their sum out
     os.makedirs(PROFILES, exist_ok=True)
-    with open(os.path.join(PROFILES, f"{w.name}_kernels.md"), "w") as f:
-        f.write(f"# Kernel times, {w.name} (M={w.M}, H={w.H}, F_i={w.F_i}, t={w.t})\n\n")
+    with open(os.path.join(PROFILES, f"{w.name}{tag}_kernels.md"), "w") as f:
+        f.write(f"# Kernel times, {path_name}{w.name} (M={w.M}, H={w.H}, F_i={w.F_i}, t={w.t})\n\n")
         f.write("Command (rocprofv3 kernel trace and stats):\n\n```\n" + cmd["trace"] + "\n```\n\n")
         f.write("| kernel | calls | average us | total ms | % |\n|---|---|---|---|---|\n")
         for r in stats:
             f.write(f"| `{r['Name']}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                     f"{float(r['TotalDurationNs']) / 1e6:.2f} | {float(r['Percentage']):.1f} |\n")
-    with open(traffic_path(w.name), "w") as f:
-        f.write(f"# HBM traffic per launch, {w.name} (M={w.M}, H={w.H}, F_i={w.F_i}, t={w.t})\n\n")
+    with open(traffic_path(w.name, fp8), "w") as f:
+        f.write(f"# HBM traffic per launch, {path_name}{w.name} (M={w.M}, H={w.H}, F_i={w.F_i}, t={w.t})\n\n")
         f.write("FETCH_SIZE and WRITE_SIZE (KiB per dispatch, L2-to-fabric traffic) from two rocprofv3 --pmc "
                 "runs of one step, each scaled by what the same counter reads for a plain copy of "
                 f"{mib} MiB through tpmlp_shard_sum (one part): fetch x{f_scale:.3f}, write x{w_scale:.3f}. "
@@ -269,11 +289,12 @@ def summarize(d, config):
         for kind, a in agg.items():
             f.write(f"traffic_bytes {kind} {a['fetch'] / a['n']:.0f} {a['write'] / a['n']:.0f}\n")
         f.write("```\n")
-    counters_md = _summarize_counters(d, w, cmd, order, agg)
-    print(f"wrote {PROFILES}/{w.name}_kernels.md and {traffic_path(w.name)}" + (f" and {counters_md}" if counters_md else ""))
+    counters_md = _summarize_counters(d, w, cmd, order, agg, tag)
+    print(f"wrote {PROFILES}/{w.name}{tag}_kernels.md and {traffic_path(w.name, fp8)}"
+          + (f" and {counters_md}" if counters_md else ""))
 
 
-def _summarize_counters(d, w, cmd, order, traffic):
+def _summarize_counters(d, w, cmd, order, traffic, tag=""):
     """profiles/<workload>_counters.md: per kernel kind, the launch time (kernel trace),
     the shader clock and MFMA utilisation implied by GRBM_GUI_ACTIVE, the SQ MFMA-busy
     ratio, LDS bank conflicts per LDS instruction and HBM GB/s.  Needs the trace run's
@@ -298,9 +319,11 @@ def _summarize_counters(d, w, cmd, order, traffic):
         for c, v in rec["counters"].items():
             a[c] = a.get(c, 0.0) + v
     flops = gemm_flops(w)
-    path = os.path.join(PROFILES, f"{w.name}_counters.md")
+    path = os.path.join(PROFILES, f"{w.name}{tag}_counters.md")
+    peak_flop_clk = 8192 if tag == "_fp8" else 4096  # per CU: dense fp8 / bf16 MFMA
     with open(path, "w") as f:
-        f.write(f"# Counters per kernel kind, {w.name} (M={w.M}, H={w.H}, F_i={w.F_i}, t={w.t})\n\n")
+        f.write(f"# Counters per kernel kind, {'FP8 path, ' if tag else ''}{w.name} "
+                f"(M={w.M}, H={w.H}, F_i={w.F_i}, t={w.t})\n\n")
         f.write("Launch times from the kernel trace (the timed steps' dispatches), counters from one "
                 "rocprofv3 --pmc pass over one step. A launch is one timed call of a kind: one kernel "
                 "dispatch, or two where a product runs as whole waves of unsplit tiles plus a split tail "
@@ -308,8 +331,9 @@ def _summarize_counters(d, w, cmd, order, traffic):
         f.write("```\n" + cmd["trace"] + "\n" + cmd["sq"] + "\n```\n\n")
         f.write("- cycles = GRBM_GUI_ACTIVE / 8 (the counter is summed over the 8 XCDs); clock = cycles / launch time "
                 "(launches of 100 us or more only).\n"
-                "- MFMA util = the launch's algorithmic flops / (cycles x 256 CUs x 4096 bf16 flop/clk), i.e. "
-                "the fraction of the MFMA peak at the clock the launch actually ran at.\n"
+                f"- MFMA util = the launch's algorithmic flops / (cycles x 256 CUs x {peak_flop_clk} "
+                f"{'fp8' if tag else 'bf16'} flop/clk), i.e. the fraction of the MFMA peak at the clock the "
+                "launch actually ran at.\n"
                 "- SQ MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (cycles x 1024 SIMDs).\n"
                 "- LDS conflicts = SQ_LDS_BANK_CONFLICT / SQ_INSTS_LDS (conflict cycles per LDS instruction).\n"
                 "- HBM GB/s = (FETCH_SIZE + WRITE_SIZE bytes, scaled as in the traffic file) / launch time.\n\n")
@@ -322,7 +346,7 @@ def _summarize_counters(d, w, cmd, order, traffic):
             # The counter pass's dispatch is not the timed one; for short launches the two differ
             # too much for their ratio to be a clock.
             clock = cyc / (us * 1e3) if us >= 100 else float("nan")
-            util = (flops[kind] / (cyc * 256 * 4096)) if kind in flops and cyc else float("nan")
+            util = (flops[kind] / (cyc * 256 * peak_flop_clk)) if kind in flops and cyc else float("nan")
             busy = a.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / n / (cyc * 1024) if cyc else float("nan")
             confl = a.get("SQ_LDS_BANK_CONFLICT", 0.0) / max(a.get("SQ_INSTS_LDS", 0.0), 1.0)
             t = traffic.get(kind)
@@ -445,13 +469,19 @@ def measure_fp8(w, args, L, I, torch):
     torch.cuda.synchronize()
     per_launch = gemm_flops(w)
     log("[bench] FP8 inputs resident; warmup")
-    L.tpmlp_timing_begin(64 * (len(shards) + 1) * max(args.warmup, 1))
-    for _ in range(max(args.warmup, 1)):
-        d.step()
-    torch.cuda.synchronize()
-    warm, _ = L.tpmlp_timing_end()
-    dom = max((n for n in per_launch if warm.get(n, (0, 0))[0]), key=lambda n: warm[n][1])
-    L.tpmlp_timing_begin_kinds(64 * (len(shards) + 1) * max(args.steps, 1), [dom])
+    warm, dom = None, None
+    if args.warmup:
+        L.tpmlp_timing_begin(64 * (len(shards) + 1) * args.warmup)
+        for _ in range(args.warmup):
+            d.step()
+        torch.cuda.synchronize()
+        warm, _ = L.tpmlp_timing_end()
+        dom = max((n for n in per_launch if warm.get(n, (0, 0))[0]), key=lambda n: warm[n][1])
+    n_launch = 64 * (len(shards) + 1) * max(args.steps, 1)
+    if dom is None or args.trace_order:  # every launch timed (a profiler run records their kinds in order)
+        L.tpmlp_timing_begin(n_launch)
+    else:
+        L.tpmlp_timing_begin_kinds(n_launch, [dom])
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -459,6 +489,13 @@ def measure_fp8(w, args, L, I, torch):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     stats, dropped = L.tpmlp_timing_end()
+    if args.trace_order:
+        with open(args.trace_order, "w") as f:
+            json.dump([[k, n] for (k, _), n in zip(L.tpmlp_timing_records(), L.tpmlp_timing_dispatches())], f)
+    if dom is None:
+        dom = max((n for n in per_launch if stats.get(n, (0, 0))[0]), key=lambda n: stats[n][1])
+    if warm is None:
+        warm = stats
     ms = (t1 - t0) * 1e3 / max(args.steps, 1)
     value = w.model_flops_per_shard() * len(shards) / (ms * 1e-3) / 1e12
     avg_s = stats[dom][1] * 1e-3 / stats[dom][0]
@@ -470,15 +507,21 @@ def measure_fp8(w, args, L, I, torch):
     for name, k in sorted(kernels.items(), key=lambda kv: -kv[1]["share"]):
         log(f"  fp8 {name:16s} {k}")
     log(f"[bench] FP8 {w.name}: {ms:.4f} ms per step, {value:.1f} TFLOP/s")
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1), "peak": PEAK_FP8_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4), "traffic": None,
+                "avg_launch_us": round(avg_s * 1e6, 2), "alg_bytes": fp8_alg_bytes(w, fold=folds(w))[dom]}
+    traffic = read_traffic(w.name, fp8=True)
+    if traffic and dom in traffic:
+        fetch, write = traffic[dom]
+        roofline["traffic"] = int(fetch + write)
+        roofline["traffic_fetch"], roofline["traffic_write"] = int(fetch), int(write)
     del d
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     return {"workload": w.name, "formats": "E4M3 X, A_i, B_i, G_i; E5M2 dZ, dP_i; per-tensor current scaling",
             "shards_per_step": len(shards), "ms_per_step": round(ms, 4), "value": round(value, 2),
             "unit": "TFLOP/s", "frac_of_fp8_peak": round(value / PEAK_FP8_TFLOPS, 4),
-            "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1), "peak": PEAK_FP8_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
-                         "avg_launch_us": round(avg_s * 1e6, 2)},
+            "roofline": roofline,
             "kernels_warmup": kernels, "timing_dropped": dropped}
 
 
@@ -494,6 +537,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp8", action="store_true",
                     help="skip the FP8 path's measurement on the first workload (reported under \"fp8\")")
+    ap.add_argument("--fp8-only", action="store_true",
+                    help="time the FP8 path only (profiler runs of it; with --summarize: its summaries)")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of one step captured into a HIP graph (for launch-latency-bound "
                          "workloads); per-kernel times then come from the eager warmup steps")
@@ -508,7 +553,7 @@ def main():
                          "(reference dispatch for scaling HBM byte counters), then exit")
     args = ap.parse_args()
     if args.summarize:
-        summarize(args.summarize, args.config)
+        summarize(args.summarize, args.config, fp8=args.fp8_only)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the tensor-parallel "
@@ -534,6 +579,12 @@ def main():
         log(f"[bench] copy probe: 3 dispatches, each reads and writes {args.copy_probe_mib} MiB")
         return
     w = I.CONFIGS[args.config]
+    if args.fp8_only:
+        if not w.backward:
+            print("--fp8-only needs a workload with a backward", file=sys.stderr)
+            sys.exit(2)
+        print(json.dumps({"workload": w.name, "fp8": measure_fp8(w, args, L, I, torch)}), flush=True)
+        return
     m = measure(w, args, L, I, DeviceMLP, torch)
     extra = {}
     if args.also >= 0 and args.also != args.config and not (args.graph or args.trace_order or args.full_weights):

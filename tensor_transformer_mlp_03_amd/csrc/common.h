@@ -99,10 +99,12 @@ hipError_t launch_sum(const float* const* parts, int n_parts, float* out, int64_
 // rows of N) finished with the epilogue `epi` into out/out2 as the GEMM
 // epilogue would.  out, out2 (GeLU's pre-activation) and aux (the dGeLU
 // pre-activation) have rows of ldo elements; dGeLU's transposed out2 has rows
-// of ldt.  The outputs may be a column block of wider matrices.
+// of ldt (null: none written).  The outputs may be a column block of wider
+// matrices.  FP8 products: `amax` (an AMAX_SUB-word slot, or null) collects the
+// max |output| of EPI_BF16 (of its GeLU with amax_gelu) or of EPI_DGELU's dP.
 hipError_t launch_splitk_epilogue(Epi epi, const float* part, int splits, int64_t M, int64_t N, void* out,
                                   uint16_t* out2, const uint16_t* aux, int64_t ldo, int64_t ldt,
-                                  hipStream_t stream);
+                                  hipStream_t stream, uint32_t* amax = nullptr, bool amax_gelu = false);
 
 // out[c][r] = in[r][c] for a bf16 matrix in[R][C] with rows of ld_in >= C
 // elements, into out with rows of ld_out >= R elements (0: R), so that the

@@ -120,6 +120,27 @@ __device__ __forceinline__ void slot_max(uint32_t* slot, int nsub, float lane_ma
   }
 }
 
+// Running extremes of values v, for max|v| or max|GeLU(v)| without a GeLU per
+// value: GeLU rises on v >= 0, so there the largest v gives the max; on v < 0,
+// |GeLU| rises towards its one maximum at v = -GELU_MODE from either side, so the
+// largest v below the mode and the smallest v between it and 0 hold the max
+// there.  Branch-free; a value of 0 moves nothing (an invalid element enters as
+// 0).  The initial -1e30 has GeLU 0.
+struct AmaxTrack {
+  static constexpr float GELU_MODE = 0.7517915f;
+  float v_max = 0.0f, v_min = 0.0f, g_left = -1e30f, g_right = 0.0f;
+  __device__ __forceinline__ void add(float v) {
+    v_max = fmaxf(v_max, v);
+    v_min = fminf(v_min, v);
+    g_left = v < -GELU_MODE ? fmaxf(g_left, v) : g_left;
+    g_right = (v >= -GELU_MODE && v < 0.0f) ? fminf(g_right, v) : g_right;
+  }
+  __device__ __forceinline__ float result(bool of_gelu) const {
+    return of_gelu ? fmaxf(gelu_f32(v_max), fmaxf(fabsf(gelu_f32(g_left)), fabsf(gelu_f32(g_right))))
+                   : fmaxf(v_max, -v_min);
+  }
+};
+
 __device__ __forceinline__ float slot_read(const uint32_t* slot, int nsub) {
   uint32_t m = 0;
   for (int i = 0; i < nsub; ++i) m = max(m, slot[i * AMAX_SUB_STRIDE]);

@@ -227,21 +227,9 @@ constexpr int G_ROW_B = 128;  // staged G row pitch in bytes
 template <int EPI, int NC, bool FP8, class StageChunk>
 __device__ __forceinline__ void store_staged(StageChunk&& stage_chunk, const GemmArgs& args, char* stage, int row_w,
                                              int col_w, int nh, int split, int lane) {
-  // FP8: running extremes of the written values (valid elements only; the others
-  // enter as 0, which moves none of them), updated without branches.  max|v| is
-  // max(v_max, -v_min).  max|GeLU(v)| needs no GeLU per element: GeLU rises on
-  // v >= 0, so there the largest v gives the max; on v < 0, |GeLU| rises towards
-  // its one maximum at v = -GELU_MODE from either side, so the largest v below the
-  // mode and the smallest v between it and 0 hold the max there.  (The initial
-  // -1e30 has GeLU 0.)
-  constexpr float GELU_MODE = 0.7517915f;
-  float v_max = 0.0f, v_min = 0.0f, g_left = -1e30f, g_right = 0.0f;
-  auto track = [&](float v) {
-    v_max = fmaxf(v_max, v);
-    v_min = fminf(v_min, v);
-    g_left = v < -GELU_MODE ? fmaxf(g_left, v) : g_left;
-    g_right = (v >= -GELU_MODE && v < 0.0f) ? fminf(g_right, v) : g_right;
-  };
+  // FP8: running extremes of the written values (AmaxTrack, epilogue.h; invalid
+  // elements enter as 0), updated without branches.
+  AmaxTrack am;
   // Each phase below issues all of its memory operations before it waits for
   // any, and the global loads an epilogue needs (the dGeLU pre-activations, the
   // EPI_F32_ACC running sum) are double-buffered: chunk c + 1's are in flight
@@ -337,7 +325,7 @@ __device__ __forceinline__ void store_staged(StageChunk&& stage_chunk, const Gem
           if (ok) *reinterpret_cast<u16x8_t*>(reinterpret_cast<uint16_t*>(args.out) + o) = v1;
           if (FP8) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) track(ok ? bf16_to_f32(v1[e]) : 0.0f);
+            for (int e = 0; e < 8; ++e) am.add(ok ? bf16_to_f32(v1[e]) : 0.0f);
           }
         } else if (FP8) {  // EPI_DGELU of an FP8 product: dP and its amax
 #pragma unroll
@@ -346,8 +334,8 @@ __device__ __forceinline__ void store_staged(StageChunk&& stage_chunk, const Gem
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const float v = ok ? bf16_to_f32(v1[e]) : 0.0f;
-            v_max = fmaxf(v_max, v);
-            v_min = fminf(v_min, v);
+            am.v_max = fmaxf(am.v_max, v);
+            am.v_min = fminf(am.v_min, v);
           }
         } else {  // EPI_DGELU
 #pragma unroll
@@ -398,12 +386,8 @@ __device__ __forceinline__ void store_staged(StageChunk&& stage_chunk, const Gem
       }
     }
   }
-  if (FP8 && (EPI == EPI_BF16 || EPI == EPI_DGELU) && args.amax_out) {
-    const float amax = (EPI == EPI_BF16 && args.amax_gelu)
-                           ? fmaxf(gelu_f32(v_max), fmaxf(fabsf(gelu_f32(g_left)), fabsf(gelu_f32(g_right))))
-                           : fmaxf(v_max, -v_min);
-    slot_max(args.amax_out, AMAX_SUB, amax);
-  }
+  if (FP8 && (EPI == EPI_BF16 || EPI == EPI_DGELU) && args.amax_out)
+    slot_max(args.amax_out, AMAX_SUB, am.result(EPI == EPI_BF16 && args.amax_gelu));
 }
 
 }  // namespace

@@ -51,6 +51,8 @@ struct SplitArgs {
   void* out;          // float* (EPI_F32) or uint16_t*
   uint16_t* out2;     // second bf16 output or null
   const uint16_t* aux;
+  uint32_t* amax;     // EPI_BF16 of an FP8 product: amax slot of the output (or its GeLU), or null
+  int amax_gelu;
 };
 
 template <int EPI>
@@ -59,6 +61,7 @@ __global__ void __launch_bounds__(256) splitk_kernel(SplitArgs a) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   const bool dense = a.ldo == a.cols;
   const uint32_t c4n = (uint32_t)a.cols / 4;
+  AmaxTrack am;
   for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < n4; j += stride) {
     f32x4_t s = reinterpret_cast<const f32x4_t*>(a.part)[j];
     for (int i = 1; i < a.splits; ++i) s += reinterpret_cast<const f32x4_t*>(a.part + i * a.n)[j];
@@ -82,10 +85,14 @@ __global__ void __launch_bounds__(256) splitk_kernel(SplitArgs a) {
     } else if (EPI == EPI_BF16) {
       u16x4_t p;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) p[e] = f32_to_bf16(s[e]);
+      for (int e = 0; e < 4; ++e) {
+        p[e] = f32_to_bf16(s[e]);
+        if (a.amax) am.add(bf16_to_f32(p[e]));
+      }
       *reinterpret_cast<u16x4_t*>(reinterpret_cast<uint16_t*>(a.out) + o) = p;
     }
   }
+  if (EPI == EPI_BF16 && a.amax) slot_max(a.amax, AMAX_SUB, am.result(a.amax_gelu != 0));
 }
 
 struct SplitDGeluArgs {
@@ -94,8 +101,9 @@ struct SplitDGeluArgs {
   int M, N;
   int64_t ldo, ldt;     // row strides of dp and p, and of g_t
   uint16_t* dp;         // [M][ldo]
-  uint16_t* g_t;        // [N][ldt]
+  uint16_t* g_t;        // [N][ldt], or null (an FP8 product: no G^T)
   const uint16_t* p;    // [M][ldo] pre-activation
+  uint32_t* amax;       // FP8 product: amax slot of dP, or null
 };
 
 typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
@@ -135,6 +143,7 @@ __global__ void __launch_bounds__(256) splitk_dgelu_kernel(SplitDGeluArgs a) {
         s1[v] += *reinterpret_cast<const f32x4_t*>(a.part + i * plane + o[v] + 4);
       }
     }
+    AmaxTrack am;
 #pragma unroll
     for (int v = 0; v < 2; ++v) {
       if (!ok[v]) continue;
@@ -143,13 +152,16 @@ __global__ void __launch_bounds__(256) splitk_dgelu_kernel(SplitDGeluArgs a) {
       u16x8_t dp;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const DGelu d = epi_dgelu(x[e], pb[v][e]);
+        const DGelu d = epi_dgelu(x[e], pb[v][e]);  // dP's bits equal bf16(dgelu_f32(x, p))
         dp[e] = d.dp;
         s_g[r][c + e] = d.g;
+        if (a.amax) am.add(bf16_to_f32(d.dp));
       }
       *reinterpret_cast<u16x8_t*>(a.dp + (int64_t)(m0 + r) * a.ldo + col) = dp;
     }
+    if (a.amax) slot_max(a.amax, AMAX_SUB, am.result(false));
   }
+  if (!a.g_t) return;  // uniform: the whole block returns before the barrier
   __syncthreads();
   {
     const int c = t >> 2, col = n0 + c;   // a column of the tile = a row of the transposed output
@@ -244,15 +256,15 @@ hipError_t launch_sum(const float* const* parts, int n_parts, float* out, int64_
 
 hipError_t launch_splitk_epilogue(Epi epi, const float* part, int splits, int64_t M, int64_t N, void* out,
                                   uint16_t* out2, const uint16_t* aux, int64_t ldo, int64_t ldt,
-                                  hipStream_t stream) {
+                                  hipStream_t stream, uint32_t* amax, bool amax_gelu) {
   const int64_t n = M * N;
   if (!part || splits < 1 || (N & 3) || ldo < N) return hipErrorInvalidValue;
   if (epi == EPI_DGELU) {
-    SplitDGeluArgs a{part, splits, (int)M, (int)N, ldo, ldt, static_cast<uint16_t*>(out), out2, aux};
+    SplitDGeluArgs a{part, splits, (int)M, (int)N, ldo, ldt, static_cast<uint16_t*>(out), out2, aux, amax};
     const int64_t tiles = ((M + 63) / 64) * ((N + 63) / 64);
     return launch_kernel(splitk_dgelu_kernel, dim3((unsigned)tiles), dim3(256), stream, a);
   }
-  SplitArgs a{part, splits, n, (int)N, ldo, out, out2, aux};
+  SplitArgs a{part, splits, n, (int)N, ldo, out, out2, aux, amax, amax_gelu ? 1 : 0};
   const dim3 grid(grid_for(n / 4)), block(256);
   switch (epi) {
     case EPI_F32: return launch_kernel(splitk_kernel<EPI_F32>, grid, block, stream, a);

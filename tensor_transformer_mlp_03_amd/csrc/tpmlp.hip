@@ -752,23 +752,6 @@ tpmlp_status check_shape_fp8(int64_t M, int64_t H, int64_t F) {
   return TPMLP_OK;
 }
 
-// A plan without split-K, for products whose epilogue collects an amax (a
-// split reduction does not).
-GemmPlan plan_gemm_whole(int64_t M, int64_t N, int64_t K) {
-  GemmPlan best{TILE_256x256, 1, (int)((K + TILE_BK - 1) / TILE_BK * TILE_BK)};
-  double best_t = 1e30;
-  for (TileCfg tile : {TILE_256x256, TILE_256x128, TILE_128x128}) {
-    const int64_t tiles = (int64_t)ceil_div(M, tile_bm(tile)) * ceil_div(N, tile_bn(tile));
-    const double rate = tile == TILE_256x256 ? CU_RATE_256 : tile == TILE_256x128 ? CU_RATE_256x128 : CU_RATE_128;
-    const double t = double((tiles + NUM_CU - 1) / NUM_CU) * double(tile_bm(tile) * tile_bn(tile) * 2 * K) / rate;
-    if (t < best_t * (1 - 1e-9)) {
-      best_t = t;
-      best = GemmPlan{tile, 1, (int)((K + TILE_BK - 1) / TILE_BK * TILE_BK)};
-    }
-  }
-  return best;
-}
-
 // Amax slots: the forward's (X, then A_i, B_i, G_i per shard), then the
 // backward's (dZ, then dP_i per shard), so that each call clears one range.
 // Each slot is AMAX_SLOT_WORDS words (epilogue.h).
@@ -794,9 +777,9 @@ struct Fp8Layout {
 
 Fp8Layout fp8_layout(int t, int64_t M, int64_t H, int64_t F) {
   Fp8Layout L;
-  L.g1 = plan_gemm_whole(M, F, H);  // P_i = X A_i (epilogue collects amax|GeLU(P_i)|)
-  L.g2 = plan_gemm(M, H, F);        // Z_i = G_i B_i
-  L.gdg = plan_gemm_whole(M, F, H); // dG_i = dZ B_i^T (epilogue collects amax|dP_i|)
+  L.g1 = plan_gemm(M, F, H);   // P_i = X A_i (epilogue collects amax|GeLU(P_i)|)
+  L.g2 = plan_gemm(M, H, F);   // Z_i = G_i B_i
+  L.gdg = plan_gemm(M, F, H);  // dG_i = dZ B_i^T (epilogue collects amax|dP_i|)
   L.gdb = plan_gemm(F, H, M);
   L.gda = plan_gemm(H, F, M);
   L.gdx = plan_gemm(M, H, F);
@@ -824,8 +807,8 @@ Fp8Layout fp8_layout(int t, int64_t M, int64_t H, int64_t F) {
   L.dP = take(mf * 2);
   L.qdP = take(mf);
   L.qdPt = take(mf);
-  L.part = take(std::max({part_bytes(L.g2, M, H), part_bytes(L.gdb, F, H), part_bytes(L.gda, H, F),
-                          part_bytes(L.gdx, M, H), size_t(1)}));
+  L.part = take(std::max({part_bytes(L.g1, M, F), part_bytes(L.g2, M, H), part_bytes(L.gdg, M, F),
+                          part_bytes(L.gdb, F, H), part_bytes(L.gda, H, F), part_bytes(L.gdx, M, H), size_t(1)}));
   L.total = o;
   return L;
 }
@@ -849,12 +832,16 @@ hipError_t run_gemm_fp8(int kind, int fa, int fb, Epi epi, const uint8_t* a, int
     const GemmArgs g = args(b, N, p, out, N);
     return timed(kind, s, [&] { return launch_gemm_fp8(p.tile, fa, fb, epi, g, 1, s); });
   }
-  if (p.n_full > 0) {
+  // Split products: the float32 slices go to `part`; the reduction applies the
+  // epilogue, collects the amax (bf16 and dGeLU outputs) and writes no G^T.
+  const size_t out_elem = (epi == EPI_F32 || epi == EPI_F32_ACC) ? 4 : 2;
+  if (p.n_full > 0) {  // whole-wave tiles on the first n_full columns, split tiles on the rest
     const int64_t nf = p.n_full, nt = N - nf;
     const GemmPlan pf{p.tile, 1, (int)((K + TILE_BK - 1) / TILE_BK * TILE_BK)};
     GemmArgs gf = args(b, nf, pf, out, N);
     GemmArgs gt = args(b + nf * ldb, nt, p, part, nt);
     gt.amax_out = nullptr;
+    gt.aux = nullptr;
     hipError_t e = timed(
         kind, s,
         [&] {
@@ -863,17 +850,21 @@ hipError_t run_gemm_fp8(int kind, int fa, int fb, Epi epi, const uint8_t* a, int
         },
         2);
     if (e != hipSuccess) return e;
-    float* out_tail = static_cast<float*>(out) + nf;
+    void* out_tail = static_cast<char*>(out) + nf * out_elem;
+    const uint16_t* aux_tail = aux ? aux + nf : nullptr;
     return timed(TPMLP_K_SPLITK_REDUCE, s, [&] {
-      return launch_splitk_epilogue(epi, part, p.splits, M, nt, out_tail, nullptr, nullptr, N, M, s);
+      return launch_splitk_epilogue(epi, part, p.splits, M, nt, out_tail, nullptr, aux_tail, N, M, s, amax_out,
+                                    amax_gelu);
     });
   }
   GemmArgs g = args(b, N, p, part, N);
   g.amax_out = nullptr;
+  g.aux = nullptr;
   hipError_t e = timed(kind, s, [&] { return launch_gemm_fp8(p.tile, fa, fb, EPI_F32, g, p.splits, s); });
   if (e != hipSuccess) return e;
-  return timed(TPMLP_K_SPLITK_REDUCE, s,
-               [&] { return launch_splitk_epilogue(epi, part, p.splits, M, N, out, nullptr, nullptr, N, M, s); });
+  return timed(TPMLP_K_SPLITK_REDUCE, s, [&] {
+    return launch_splitk_epilogue(epi, part, p.splits, M, N, out, nullptr, aux, N, M, s, amax_out, amax_gelu);
+  });
 }
 
 hipError_t fp8_amax(const tpmlp_bf16* in, int64_t R, int64_t C, uint32_t* slot, hipStream_t s) {

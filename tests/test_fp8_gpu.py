@@ -230,3 +230,58 @@ def test_fp8_no_writes_outside_outputs(case):
         head, tail = raw[:BAND], raw[BAND + n:]
         assert bool((head == 0xA5).all()) and bool((tail == 0xA5).all()), f"buffer {k}: a band was written"
     assert torch.isfinite(Z).all() and torch.isfinite(dX).all()
+
+
+FP8_SPLIT_CASES = [
+    # (M, H, F_i, t, store_p, the first product's plan): F1 and dGeLU split along K
+    (512, 4096, 2560, 1, True, "split"),      # 128 x 128 tiles, 3 K slices
+    (256, 1536, 65552, 1, False, "hybrid"),   # 256 whole tiles + a 16-column split tail
+]
+
+
+@pytest.mark.parametrize("case", FP8_SPLIT_CASES, ids=lambda c: "x".join(map(str, c[:4])) + "_" + c[5])
+def test_fp8_split_products_collect_amax(case):
+    """F1 and dGeLU split along K (or as whole-wave tiles plus a split tail): the
+    split-K reduction finishes the bf16 output and collects its amax (of GeLU(P_i)
+    for F1, of dP_i for dGeLU), and the path matches the oracle.  The launch order
+    shows that the split path ran."""
+    from tensor_transformer_mlp_03_amd import _lib as L
+    from tensor_transformer_mlp_03_amd.device import to_device
+    M, H, F_, t, store, kind = case
+    say(f"[fp8 split] M={M} H={H} F_i={F_} t={t} store_p={store} plan={kind}")
+    w = I.custom_workload(480 + t, M=M, H=H, F_i=F_, t=t, w_std=0.05)
+    inp = I.make_inputs(w)
+    X, dZ = to_device(inp.X), to_device(inp.dZ)
+    A = [to_device(a) for a in inp.A]
+    B = [to_device(b) for b in inp.B]
+    P = [torch.empty((M, F_), dtype=torch.int16, device="cuda") for _ in range(t)] if store else None
+    Z = torch.empty((M, H), dtype=torch.float32, device="cuda")
+    dX = torch.empty((M, H), dtype=torch.float32, device="cuda")
+    dA = [torch.empty((H, F_), dtype=torch.float32, device="cuda") for _ in range(t)]
+    dB = [torch.empty((F_, H), dtype=torch.float32, device="cuda") for _ in range(t)]
+    ws = torch.empty(L.tpmlp_fp8_workspace_bytes(t, M, H, F_), dtype=torch.uint8, device="cuda")
+    L.tpmlp_timing_begin(256)
+    L.tpmlp_fp8_tp_fwd(X, A, B, P, Z, ws)
+    L.tpmlp_fp8_tp_bwd(dZ, X, A, B, P, dA, dB, dX, ws)
+    torch.cuda.synchronize()
+    L.tpmlp_timing_end()
+    recs = [k for k, _ in L.tpmlp_timing_records()]
+    disp = L.tpmlp_timing_dispatches()
+    for prod in ("fwd_gemm1_gelu", "bwd_dgelu"):
+        at = [i for i, k in enumerate(recs) if k == prod]
+        assert at and all(i + 1 < len(recs) and recs[i + 1] == "splitk_reduce" for i in at), (prod, recs)
+        assert all(disp[i] == (2 if kind == "hybrid" else 1) for i in at), (prod, disp)
+    Xo, dZo = O.decode_bf16(inp.X), O.decode_bf16(inp.dZ)
+    Ao, Bo = [O.decode_bf16(a) for a in inp.A], [O.decode_bf16(b) for b in inp.B]
+    bd = FB.path_bounds(Xo, Ao, Bo, dZo)
+    r = {}
+    check("Z", Z.cpu().numpy(), bd.Z, bd.tol_Z, r)
+    check("dX", dX.cpu().numpy(), bd.dX, bd.tol_dX, r)
+    for i in range(t):
+        check(f"dA_{i}", dA[i].cpu().numpy(), bd.dA[i], bd.tol_dA[i], r)
+        check(f"dB_{i}", dB[i].cpu().numpy(), bd.dB[i], bd.tol_dB[i], r)
+        if store:
+            Pg = O.decode_bf16(P[i].cpu().numpy().view(np.uint16))
+            sh = bd.shards[i]
+            assert int(np.count_nonzero((Pg < sh.p_lo) | (Pg > sh.p_hi))) == 0, f"P_{i} outside the admissible roundings"
+    say("  err/tol:", {k: round(v, 3) for k, v in r.items()})
