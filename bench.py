@@ -79,6 +79,17 @@ def gemm_flops(w):
             "bwd_dX": f, "fwd_fused": 2 * f}
 
 
+def batch_factor(w, kind, launches, steps):
+    """Shards one launch of a product kind covers: the t-shard driver may run
+    several shards' F1, recompute or dGeLU as one batched launch, so a kind
+    launched fewer times per step than there are shards covers several each."""
+    shards = len(w.shards_timed)
+    per_step = launches / steps if steps else 0
+    if kind not in ("fwd_gemm1_gelu", "bwd_recompute", "bwd_dgelu") or per_step <= 0:
+        return 1.0
+    return max(1.0, shards / per_step)
+
+
 def gemm_alg_bytes(w, recompute, fold=False):
     """Algorithmic HBM bytes of one launch of each GEMM kind (operands read once,
     outputs written once; bf16 = 2 bytes, float32 = 4).  fold: the t-shard driver adds
@@ -260,6 +271,9 @@ def summarize(d, config, fp8=False):
         alg["transpose"] = (n_x * 4 * w.M * w.H + n_p * 4 * w.M * w.F_i
                             + (n_t - n_x - n_p) * 4 * w.H * w.F_i) / n_t
     alg["shard_sum"] = (w.t + 1) * w.M * w.H * 4  # t float32 partials in, their sum out
+    for kind, a in agg.items():  # a batched launch covers several shards (the counter passes run one step)
+        if kind in alg:
+            alg[kind] *= batch_factor(w, kind, a["n"], 1)
     os.makedirs(PROFILES, exist_ok=True)
     with open(os.path.join(PROFILES, f"{w.name}{tag}_kernels.md"), "w") as f:
         f.write(f"# Kernel times, {path_name}{w.name} (M={w.M}, H={w.H}, F_i={w.F_i}, t={w.t})\n\n")
@@ -346,7 +360,8 @@ def _summarize_counters(d, w, cmd, order, traffic, tag=""):
             # The counter pass's dispatch is not the timed one; for short launches the two differ
             # too much for their ratio to be a clock.
             clock = cyc / (us * 1e3) if us >= 100 else float("nan")
-            util = (flops[kind] / (cyc * 256 * peak_flop_clk)) if kind in flops and cyc else float("nan")
+            fl = flops[kind] * batch_factor(w, kind, n, 1) if kind in flops else 0.0
+            util = (fl / (cyc * 256 * peak_flop_clk)) if kind in flops and cyc else float("nan")
             busy = a.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / n / (cyc * 1024) if cyc else float("nan")
             confl = a.get("SQ_LDS_BANK_CONFLICT", 0.0) / max(a.get("SQ_INSTS_LDS", 0.0), 1.0)
             t = traffic.get(kind)
@@ -426,24 +441,32 @@ def measure(w, args, L, I, DeviceMLP, torch):
 
     kernels = {}
     src = warm_stats if (dom or graph is not None) else stats
+    src_steps = args.warmup if (dom or graph is not None) else args.steps
     log(f"[bench] {w.name} per kernel kind, {'warmup' if dom else 'timed'} steps:")
     for name, (count, total_ms) in src.items():
         if count:
             kernels[name] = {"launches": count, "avg_us": round(total_ms * 1e3 / count, 2),
                              "share": round(total_ms / sum(v[1] for v in src.values()), 4)}
             if name in per_launch:
-                kernels[name]["tflops"] = round(per_launch[name] / (total_ms * 1e-3 / count) / 1e12, 1)
+                f = per_launch[name] * batch_factor(w, name, count, src_steps)
+                kernels[name]["tflops"] = round(f / (total_ms * 1e-3 / count) / 1e12, 1)
+                if f != per_launch[name]:
+                    kernels[name]["shards_per_launch"] = round(f / per_launch[name], 2)
     for name, k in sorted(kernels.items(), key=lambda kv: -kv[1]["share"]):
         log(f"  {name:16s} {k}")
     if dom is None:
         dom = max((n for n in kernels if n in per_launch), key=lambda n: stats[n][1])
     avg_s = stats[dom][1] * 1e-3 / stats[dom][0]
-    achieved = per_launch[dom] / avg_s / 1e12
+    stat_steps = args.warmup if graph is not None else args.steps
+    factor = batch_factor(w, dom, stats[dom][0], stat_steps)
+    achieved = per_launch[dom] * factor / avg_s / 1e12
     traffic = read_traffic(w.name)
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": None, "avg_launch_us": round(avg_s * 1e6, 2),
-                "alg_bytes": gemm_alg_bytes(w, w.recompute, fold=folds(w))[dom]}
+                "alg_bytes": gemm_alg_bytes(w, w.recompute, fold=folds(w))[dom] * factor}
+    if factor != 1.0:
+        roofline["shards_per_launch"] = round(factor, 2)
     if traffic and dom in traffic:
         fetch, write = traffic[dom]
         roofline["traffic"] = int(fetch + write)

@@ -55,6 +55,9 @@ enum Epi : int {
 // sum take 32-bit byte offsets within a 64-row band).
 constexpr int64_t ACC_MAX_LDO = int64_t(1) << 22;
 
+// Most products one batched launch holds (GemmArgs::batch).
+constexpr int MAX_BATCH = 8;
+
 struct GemmArgs {
   const uint16_t* a;  // A operand base (bf16 bits)
   const uint16_t* b;  // B operand base
@@ -76,6 +79,16 @@ struct GemmArgs {
   const uint32_t* amax_b;
   uint32_t* amax_out;
   int amax_gelu;
+  // Batched launch (batch > 1, no split-K): `batch` products of one shape that
+  // share the A operand and differ in the B operand, the outputs and aux;
+  // product j's are b_arr[j], out_arr[j], out2_arr[j] and aux_arr[j].  The
+  // workgroups cover batch x tiles_m x tiles_n tiles.  batch 0 or 1: b, out,
+  // out2 and aux.
+  int batch;
+  const uint16_t* b_arr[MAX_BATCH];
+  void* out_arr[MAX_BATCH];
+  uint16_t* out2_arr[MAX_BATCH];
+  const uint16_t* aux_arr[MAX_BATCH];
 };
 
 // Tile shapes the library instantiates.

@@ -419,7 +419,7 @@ namespace kern {
 // tile covers memory latency over its shorter K steps (a quarter of the MFMAs).
 template <int LB, int EPI, int BM, int BN, int F8>
 __global__ void __launch_bounds__(256)
-gemm_x16_kernel(GemmArgs args) {
+gemm_x16_kernel(GemmArgs args_in) {
 #if defined(__HIP_DEVICE_COMPILE__)
   static_assert((BM == 256 && (BN == 256 || BN == 128)) || (BM == 128 && BN == 128), "tile shapes");
   static_assert(F8 == 0 || LB == KC, "FP8 operands are K-contiguous");
@@ -447,7 +447,17 @@ gemm_x16_kernel(GemmArgs args) {
   const int wm = wave >> 1, wn = wave & 1;
 
   int tm, tn, split;
-  tile_of(blockIdx.x, gridDim.x, args.tiles_m, args.tiles_n, tm, tn, split);
+  tile_of(blockIdx.x, gridDim.x, args_in.tiles_m, args_in.tiles_n, tm, tn, split);
+  // A batched launch is unsplit: the "split" index names the workgroup's product.
+  GemmArgs args = args_in;
+  if (args_in.batch > 1) {
+    const int j = split;
+    split = 0;
+    args.b = args_in.b_arr[j];
+    args.out = args_in.out_arr[j];
+    args.out2 = args_in.out2_arr[j];
+    args.aux = args_in.aux_arr[j];
+  }
   const int m0 = tm * BM, n0 = tn * BN;
   const int k_begin = split * args.k_split;
   const int k_end = min(args.K, k_begin + args.k_split);
@@ -799,7 +809,7 @@ gemm_x16_kernel(GemmArgs args) {
       },
       args, smem + wave * (64 * ROW_B), m0 + (BM / 2) * wm, n0 + (BN / 2) * wn, FI / 4, split, lane);
 #else
-  (void)args;
+  (void)args_in;
 #endif
 }
 
@@ -809,7 +819,8 @@ namespace {
 
 template <int BM, int BN, int LB, int EPI, int F8 = 0>
 hipError_t launch_one(const GemmArgs& a, int splits, hipStream_t s) {
-  const int blocks = a.tiles_m * a.tiles_n * splits;
+  if (a.batch > 1 && (splits != 1 || a.batch > MAX_BATCH)) return hipErrorInvalidValue;
+  const int blocks = a.tiles_m * a.tiles_n * splits * (a.batch > 1 ? a.batch : 1);
   return launch_kernel(kern::gemm_x16_kernel<LB, EPI, BM, BN, F8>, dim3(blocks), dim3(256), s, a);
 }
 

@@ -138,6 +138,44 @@ size_t part_bytes(const GemmPlan& p, int64_t M, int64_t N) {
   return p.splits > 1 ? size_t(p.splits) * M * (N - p.n_full) * 4 : 0;
 }
 
+// Batches of the t-shard drivers' first products.  F1, the recompute and dGeLU
+// of different shards share their A operand (X or dZ) and differ only in the
+// weight and the outputs, so several shards' can run as one launch.  Where one
+// shard's product is a single unsplit wave of small tiles (short K, few
+// tiles: the 7B-class shard), a batch of g shards on 256 x 256 tiles fills the
+// chip with the faster tile and pays the launch, the ramp and the last tiles'
+// epilogue once per g.  Taken when the model above gives at least 10% less
+// time per shard.  Unsplit either way, so every output element is summed in
+// the same order and the results have the same bits as unbatched launches.
+struct BatchPlan {
+  int g = 1;     // shards per launch (1: no batching)
+  GemmPlan plan;
+};
+
+double unsplit_time(TileCfg tile, int64_t M, int64_t N, int64_t K, int copies) {
+  const int64_t tiles = (int64_t)ceil_div(M, tile_bm(tile)) * ceil_div(N, tile_bn(tile)) * copies;
+  const double rate = tile == TILE_256x256 ? CU_RATE_256 : tile == TILE_256x128 ? CU_RATE_256x128 : CU_RATE_128;
+  const int64_t kfull = (K + TILE_BK - 1) / TILE_BK * TILE_BK;
+  return double((tiles + NUM_CU - 1) / NUM_CU) * double(tile_bm(tile) * tile_bn(tile) * 2 * kfull) / rate;
+}
+
+BatchPlan plan_batch(int64_t M, int64_t N, int64_t K, int t) {
+  BatchPlan b;
+  b.plan = plan_gemm(M, N, K);
+  if (t < 2 || b.plan.splits != 1) return b;
+  double best = unsplit_time(b.plan.tile, M, N, K, 1);
+  for (int g = 2; g <= std::min(t, MAX_BATCH); ++g)
+    for (TileCfg tile : {TILE_256x256, TILE_256x128, TILE_128x128}) {
+      const double per_shard = unsplit_time(tile, M, N, K, g) / g;
+      if (per_shard < 0.9 * best) {
+        best = per_shard;
+        b.g = g;
+        b.plan = GemmPlan{tile, 1, (int)((K + TILE_BK - 1) / TILE_BK * TILE_BK)};
+      }
+    }
+  return b;
+}
+
 // The forward products read A_i and B_i N-contiguous.  Transposing them first
 // (4*H*F bytes of memory traffic at about 5.5 TB/s) lets the products run with
 // both operands K-contiguous, measured at about 1.2 PFLOP/s against about 1.14
@@ -240,6 +278,21 @@ BwdPlan plan_bwd(int64_t M, int64_t H, int64_t F, bool recompute) {
 // backward modes; the drivers' partial buffers follow it.
 size_t shard_ws_bytes(int64_t M, int64_t H, int64_t F) {
   return align_up(std::max(plan_fwd(M, H, F).total, plan_bwd(M, H, F, true).total));
+}
+
+// The t-shard drivers batch the shards' first products (F1; the recompute and
+// dGeLU) when the forward runs unfused on weights read in place.
+BatchPlan plan_shard_batch(int t, int64_t M, int64_t H, int64_t F) {
+  if (fused_fwd(M, H, F) || transpose_weights(M, H, F)) return BatchPlan{1, plan_gemm(M, F, H)};
+  return plan_batch(M, F, H, t);
+}
+
+// Per batched shard: G_i (forward) or P_i, G_i^T and dP_i (backward), bf16 [M][F].
+size_t batch_slot_bytes(int64_t M, int64_t F) { return 3 * align_up(size_t(M) * F * 2); }
+
+size_t batch_area_bytes(int t, int64_t M, int64_t H, int64_t F) {
+  const BatchPlan b = plan_shard_batch(t, M, H, F);
+  return b.g > 1 ? size_t(b.g) * batch_slot_bytes(M, F) : 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -435,6 +488,26 @@ hipError_t run_gemm(int kind, Layout la, Layout lb, Epi epi, const void* a, int6
                [&] { return launch_splitk_epilogue(epi, part, p.splits, M, N, out, out2, aux, ldo, ldt, s); });
 }
 
+// g products of one plan (unsplit) in one launch: A shared, product j's B
+// operand b[j] and outputs out[j], out2[j] (nullable array), aux[j] (nullable).
+hipError_t run_gemm_batch(int kind, Layout lb, Epi epi, const void* a, int64_t lda, const void* const* b,
+                          int64_t ldb, int64_t M, int64_t N, int64_t K, const GemmPlan& p, int g, void* const* out,
+                          uint16_t* const* out2, const uint16_t* const* aux, hipStream_t s) {
+  if (g < 1 || g > MAX_BATCH || p.splits != 1) return hipErrorInvalidValue;
+  GemmArgs ga = gemm_args(a, lda, b[0], ldb, M, N, K, p, out[0], N);
+  ga.ldt = M;
+  ga.batch = g;
+  for (int j = 0; j < g; ++j) {
+    ga.b_arr[j] = static_cast<const uint16_t*>(b[j]);
+    ga.out_arr[j] = out[j];
+    ga.out2_arr[j] = out2 ? out2[j] : nullptr;
+    ga.aux_arr[j] = aux ? aux[j] : nullptr;
+  }
+  ga.out2 = ga.out2_arr[0];
+  ga.aux = ga.aux_arr[0];
+  return timed(kind, s, [&] { return launch_gemm(p.tile, KC, lb, epi, ga, 1, s); });
+}
+
 char* ws_at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
 
 // Enqueue rank i's forward (arguments already checked).
@@ -525,6 +598,11 @@ hipError_t enqueue_transposes(const tpmlp_bf16* dZ, const tpmlp_bf16* X, int64_t
   return timed(TPMLP_K_TRANSPOSE, s, [&] { return launch_transpose(dZ, M, H, H, dZt, s); });
 }
 
+hipError_t enqueue_bwd_weights_dx(const BwdPlan& p, const uint16_t* dP, const uint16_t* Gt, const uint16_t* Xt,
+                                  const uint16_t* dZt, const tpmlp_bf16* A, int64_t lda, float* dX, float* dA,
+                                  int64_t ldda, float* dB, int64_t M, int64_t H, int64_t F, void* ws, hipStream_t s,
+                                  bool acc);
+
 // Enqueue rank i's backward (arguments already checked; X^T and dZ^T already
 // in the workspace).
 // A (A_i) has rows of lda >= F elements and dA (dA_i) rows of ldda >= F.
@@ -561,6 +639,16 @@ hipError_t enqueue_bwd(const tpmlp_bf16* dZ, const tpmlp_bf16* X, const tpmlp_bf
   //   dZ: [M][H] (K-contig), B_i: [F][H] = [N][K] (K-contig)
   e = run_gemm(TPMLP_K_BWD_DGELU, KC, KC, EPI_DGELU, dZ, H, B, H, M, F, H, p.g1, dP, Gt, P, part, s);
   if (e != hipSuccess) return e;
+  return enqueue_bwd_weights_dx(p, dP, Gt, Xt, dZt, A, lda, dX, dA, ldda, dB, M, H, F, ws, s, acc);
+}
+
+// The rest of rank i's backward once dP_i and G_i^T exist: dB_i, dA_i and dX_i.
+hipError_t enqueue_bwd_weights_dx(const BwdPlan& p, const uint16_t* dP, const uint16_t* Gt, const uint16_t* Xt,
+                                  const uint16_t* dZt, const tpmlp_bf16* A, int64_t lda, float* dX, float* dA,
+                                  int64_t ldda, float* dB, int64_t M, int64_t H, int64_t F, void* ws, hipStream_t s,
+                                  bool acc) {
+  float* part = reinterpret_cast<float*>(ws_at(ws, p.off_part));
+  hipError_t e;
   // dB_i = G_i^T dZ    G_i^T: [F][M] = [M'][K], dZ^T: [H][M] = [N'][K] (both K-contig)
   e = run_gemm(TPMLP_K_BWD_DB, KC, KC, EPI_F32, Gt, M, dZt, M, F, H, M, p.gdb, dB, nullptr, nullptr, part, s);
   if (e != hipSuccess) return e;
@@ -1149,7 +1237,7 @@ int tpmlp_recompute_policy(int64_t M, int64_t H, int64_t F_i, size_t budget_byte
 
 size_t tpmlp_tp_workspace_bytes(int t, int64_t M, int64_t H, int64_t F_i) {
   if (t < 1 || t > TPMLP_MAX_SHARDS || !shape_ok(M) || !shape_ok(H) || !shape_ok(F_i)) return 0;
-  return shard_ws_bytes(M, H, F_i) + align_up(size_t(t) * M * H * 4);
+  return shard_ws_bytes(M, H, F_i) + align_up(size_t(t) * M * H * 4) + batch_area_bytes(t, M, H, F_i);
 }
 
 tpmlp_status tpmlp_shard_sum(const float* const* parts, int t, float* out, int64_t n, void* stream) {
@@ -1207,12 +1295,44 @@ tpmlp_status tpmlp_tp_fwd(const tpmlp_bf16* X, const tpmlp_bf16* const* A_sh, co
   const bool direct = (t == 1) && !(Z_sh && Z_sh[0]);
   const bool fold = fold_sum(Z_sh, t, H);
   const float* parts[TPMLP_MAX_SHARDS];
+  float* Zs[TPMLP_MAX_SHARDS];
   for (int i = 0; i < t; ++i) {
-    float* Zi = (direct || fold) ? Z : (Z_sh && Z_sh[i]) ? Z_sh[i] : partials + size_t(i) * mh;
-    parts[i] = Zi;
-    hipError_t e =
-        enqueue_fwd(X, A_sh[i], F_i, B_sh[i], Zi, P_sh ? P_sh[i] : nullptr, M, H, F_i, ws, s, fold && i > 0);
-    if (e != hipSuccess) return hip_fail(e, "tpmlp_tp_fwd launch");
+    Zs[i] = (direct || fold) ? Z : (Z_sh && Z_sh[i]) ? Z_sh[i] : partials + size_t(i) * mh;
+    parts[i] = Zs[i];
+  }
+  const BatchPlan bp = plan_shard_batch(t, M, H, F_i);
+  if (bp.g > 1) {
+    // F1 of bp.g shards per launch (G_i in the batch area), then each shard's F3.
+    const FwdPlan fp = plan_fwd(M, H, F_i);
+    char* area = ws_at(ws, shard_ws_bytes(M, H, F_i) + align_up(size_t(t) * mh * 4));
+    float* part = reinterpret_cast<float*>(ws_at(ws, fp.off_part));
+    for (int i0 = 0; i0 < t; i0 += bp.g) {
+      const int g = std::min(bp.g, t - i0);
+      const void* b[MAX_BATCH];
+      void* G[MAX_BATCH];
+      uint16_t* P[MAX_BATCH];
+      for (int j = 0; j < g; ++j) {
+        b[j] = A_sh[i0 + j];
+        G[j] = area + size_t(j) * batch_slot_bytes(M, F_i);
+        P[j] = P_sh ? P_sh[i0 + j] : nullptr;
+      }
+      // P_i = X A_i; G_i = GeLU(P_i)      X: [M][H] (K-contig), A_i: [H][F] (N-contig)
+      hipError_t e = run_gemm_batch(TPMLP_K_FWD_GEMM1_GELU, MC, EPI_GELU, X, H, b, F_i, M, F_i, H, bp.plan, g, G, P,
+                                    nullptr, s);
+      for (int j = 0; j < g && e == hipSuccess; ++j) {
+        const int i = i0 + j;
+        // Z_i = G_i B_i                    G_i: [M][F] (K-contig), B_i: [F][H] (N-contig)
+        e = run_gemm(TPMLP_K_FWD_GEMM2, KC, MC, fold && i > 0 ? EPI_F32_ACC : EPI_F32, G[j], F_i, B_sh[i], H, M, H,
+                     F_i, fp.g2, Zs[i], nullptr, nullptr, part, s);
+      }
+      if (e != hipSuccess) return hip_fail(e, "tpmlp_tp_fwd launch");
+    }
+  } else {
+    for (int i = 0; i < t; ++i) {
+      hipError_t e =
+          enqueue_fwd(X, A_sh[i], F_i, B_sh[i], Zs[i], P_sh ? P_sh[i] : nullptr, M, H, F_i, ws, s, fold && i > 0);
+      if (e != hipSuccess) return hip_fail(e, "tpmlp_tp_fwd launch");
+    }
   }
   if (!direct && !fold) {
     hipError_t e = timed(TPMLP_K_SHARD_SUM, s, [&] { return launch_sum(parts, t, Z, int64_t(mh), s); });
@@ -1262,12 +1382,58 @@ tpmlp_status tpmlp_tp_bwd(const tpmlp_bf16* dZ, const tpmlp_bf16* X, const tpmlp
   const float* parts[TPMLP_MAX_SHARDS];
   hipError_t et = enqueue_transposes(dZ, X, M, H, ws, s);
   if (et != hipSuccess) return hip_fail(et, "tpmlp_tp_bwd transpose");
+  float* dXs[TPMLP_MAX_SHARDS];
   for (int i = 0; i < t; ++i) {
-    float* dXi = (direct || fold) ? dX : (dX_sh && dX_sh[i]) ? dX_sh[i] : partials + size_t(i) * mh;
-    parts[i] = dXi;
-    hipError_t e = enqueue_bwd(dZ, X, A_sh[i], F_i, B_sh[i], P_sh ? P_sh[i] : nullptr, dXi, dA_sh[i], F_i,
-                               dB_sh[i], M, H, F_i, ws, s, fold && i > 0);
-    if (e != hipSuccess) return hip_fail(e, "tpmlp_tp_bwd launch");
+    dXs[i] = (direct || fold) ? dX : (dX_sh && dX_sh[i]) ? dX_sh[i] : partials + size_t(i) * mh;
+    parts[i] = dXs[i];
+  }
+  const BatchPlan bp = plan_shard_batch(t, M, H, F_i);
+  if (bp.g > 1) {
+    // The recompute and dGeLU of bp.g shards per launch (P_i, G_i^T and dP_i in
+    // the batch area), then each shard's dB_i, dA_i and dX_i.
+    const bool recompute = P_sh == nullptr;
+    const BwdPlan p = plan_bwd(M, H, F_i, recompute);
+    const uint16_t* Xt = reinterpret_cast<const uint16_t*>(ws_at(ws, p.off_Xt));
+    const uint16_t* dZt = reinterpret_cast<const uint16_t*>(ws_at(ws, p.off_dZt));
+    char* area = ws_at(ws, shard_ws_bytes(M, H, F_i) + align_up(size_t(t) * mh * 4));
+    const size_t mfa = align_up(mf * 2);
+    for (int i0 = 0; i0 < t; i0 += bp.g) {
+      const int g = std::min(bp.g, t - i0);
+      const void* a_w[MAX_BATCH];
+      const void* b_w[MAX_BATCH];
+      void* Pw[MAX_BATCH];
+      const uint16_t* P[MAX_BATCH];
+      void* dPs[MAX_BATCH];
+      uint16_t* Gts[MAX_BATCH];
+      for (int j = 0; j < g; ++j) {
+        char* slot = area + size_t(j) * batch_slot_bytes(M, F_i);
+        a_w[j] = A_sh[i0 + j];
+        b_w[j] = B_sh[i0 + j];
+        Pw[j] = slot;
+        P[j] = recompute ? reinterpret_cast<const uint16_t*>(slot) : P_sh[i0 + j];
+        Gts[j] = reinterpret_cast<uint16_t*>(slot + mfa);
+        dPs[j] = slot + 2 * mfa;
+      }
+      hipError_t e = hipSuccess;
+      if (recompute)  // P_i = X A_i again   X: [M][H] (K-contig), A_i: [H][F] (N-contig)
+        e = run_gemm_batch(TPMLP_K_BWD_RECOMPUTE, MC, EPI_BF16, X, H, a_w, F_i, M, F_i, H, bp.plan, g, Pw, nullptr,
+                           nullptr, s);
+      // dG_i = dZ B_i^T; dP_i = dG_i GeLU'(P_i); G_i^T    dZ: [M][H], B_i: [F][H] (both K-contig)
+      if (e == hipSuccess)
+        e = run_gemm_batch(TPMLP_K_BWD_DGELU, KC, EPI_DGELU, dZ, H, b_w, H, M, F_i, H, bp.plan, g, dPs, Gts, P, s);
+      for (int j = 0; j < g && e == hipSuccess; ++j) {
+        const int i = i0 + j;
+        e = enqueue_bwd_weights_dx(p, static_cast<const uint16_t*>(dPs[j]), Gts[j], Xt, dZt, A_sh[i], F_i, dXs[i],
+                                   dA_sh[i], F_i, dB_sh[i], M, H, F_i, ws, s, fold && i > 0);
+      }
+      if (e != hipSuccess) return hip_fail(e, "tpmlp_tp_bwd launch");
+    }
+  } else {
+    for (int i = 0; i < t; ++i) {
+      hipError_t e = enqueue_bwd(dZ, X, A_sh[i], F_i, B_sh[i], P_sh ? P_sh[i] : nullptr, dXs[i], dA_sh[i], F_i,
+                                 dB_sh[i], M, H, F_i, ws, s, fold && i > 0);
+      if (e != hipSuccess) return hip_fail(e, "tpmlp_tp_bwd launch");
+    }
   }
   if (!direct && !fold) {
     hipError_t e = timed(TPMLP_K_SHARD_SUM, s, [&] { return launch_sum(parts, t, dX, int64_t(mh), s); });
