@@ -79,12 +79,12 @@ struct GemmArgs {
   const uint32_t* amax_b;
   uint32_t* amax_out;
   int amax_gelu;
-  // Batched launch (batch > 1, no split-K): `batch` products of one shape that
-  // share the A operand and differ in the B operand, the outputs and aux;
-  // product j's are b_arr[j], out_arr[j], out2_arr[j] and aux_arr[j].  The
-  // workgroups cover batch x tiles_m x tiles_n tiles.  batch 0 or 1: b, out,
-  // out2 and aux.
+  // Batched launch (batch > 1, no split-K): `batch` products of one shape and
+  // leading dimensions; product j's operands and outputs are a_arr[j],
+  // b_arr[j], out_arr[j], out2_arr[j] and aux_arr[j].  The workgroups cover
+  // batch x tiles_m x tiles_n tiles.  batch 0 or 1: a, b, out, out2 and aux.
   int batch;
+  const uint16_t* a_arr[MAX_BATCH];
   const uint16_t* b_arr[MAX_BATCH];
   void* out_arr[MAX_BATCH];
   uint16_t* out2_arr[MAX_BATCH];

@@ -453,6 +453,7 @@ gemm_x16_kernel(GemmArgs args_in) {
   if (args_in.batch > 1) {
     const int j = split;
     split = 0;
+    args.a = args_in.a_arr[j];
     args.b = args_in.b_arr[j];
     args.out = args_in.out_arr[j];
     args.out2 = args_in.out2_arr[j];

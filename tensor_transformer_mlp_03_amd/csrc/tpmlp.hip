@@ -488,16 +488,18 @@ hipError_t run_gemm(int kind, Layout la, Layout lb, Epi epi, const void* a, int6
                [&] { return launch_splitk_epilogue(epi, part, p.splits, M, N, out, out2, aux, ldo, ldt, s); });
 }
 
-// g products of one plan (unsplit) in one launch: A shared, product j's B
-// operand b[j] and outputs out[j], out2[j] (nullable array), aux[j] (nullable).
-hipError_t run_gemm_batch(int kind, Layout lb, Epi epi, const void* a, int64_t lda, const void* const* b,
+// g products of one plan (unsplit) in one launch: product j's A operand a[j],
+// B operand b[j] and outputs out[j], out2[j] (nullable array), aux[j]
+// (nullable); ldo is the outputs' row stride (0: N).
+hipError_t run_gemm_batch(int kind, Layout lb, Epi epi, const void* const* a, int64_t lda, const void* const* b,
                           int64_t ldb, int64_t M, int64_t N, int64_t K, const GemmPlan& p, int g, void* const* out,
-                          uint16_t* const* out2, const uint16_t* const* aux, hipStream_t s) {
+                          uint16_t* const* out2, const uint16_t* const* aux, hipStream_t s, int64_t ldo = 0) {
   if (g < 1 || g > MAX_BATCH || p.splits != 1) return hipErrorInvalidValue;
-  GemmArgs ga = gemm_args(a, lda, b[0], ldb, M, N, K, p, out[0], N);
+  GemmArgs ga = gemm_args(a[0], lda, b[0], ldb, M, N, K, p, out[0], ldo ? ldo : N);
   ga.ldt = M;
   ga.batch = g;
   for (int j = 0; j < g; ++j) {
+    ga.a_arr[j] = static_cast<const uint16_t*>(a[j]);
     ga.b_arr[j] = static_cast<const uint16_t*>(b[j]);
     ga.out_arr[j] = out[j];
     ga.out2_arr[j] = out2 ? out2[j] : nullptr;
@@ -601,7 +603,7 @@ hipError_t enqueue_transposes(const tpmlp_bf16* dZ, const tpmlp_bf16* X, int64_t
 hipError_t enqueue_bwd_weights_dx(const BwdPlan& p, const uint16_t* dP, const uint16_t* Gt, const uint16_t* Xt,
                                   const uint16_t* dZt, const tpmlp_bf16* A, int64_t lda, float* dX, float* dA,
                                   int64_t ldda, float* dB, int64_t M, int64_t H, int64_t F, void* ws, hipStream_t s,
-                                  bool acc);
+                                  bool acc, bool do_db = true, bool do_da = true);
 
 // Enqueue rank i's backward (arguments already checked; X^T and dZ^T already
 // in the workspace).
@@ -642,17 +644,20 @@ hipError_t enqueue_bwd(const tpmlp_bf16* dZ, const tpmlp_bf16* X, const tpmlp_bf
   return enqueue_bwd_weights_dx(p, dP, Gt, Xt, dZt, A, lda, dX, dA, ldda, dB, M, H, F, ws, s, acc);
 }
 
-// The rest of rank i's backward once dP_i and G_i^T exist: dB_i, dA_i and dX_i.
+// The rest of rank i's backward once dP_i and G_i^T exist: dB_i, dA_i (unless
+// a batched launch made them) and dX_i.
 hipError_t enqueue_bwd_weights_dx(const BwdPlan& p, const uint16_t* dP, const uint16_t* Gt, const uint16_t* Xt,
                                   const uint16_t* dZt, const tpmlp_bf16* A, int64_t lda, float* dX, float* dA,
                                   int64_t ldda, float* dB, int64_t M, int64_t H, int64_t F, void* ws, hipStream_t s,
-                                  bool acc) {
+                                  bool acc, bool do_db, bool do_da) {
   float* part = reinterpret_cast<float*>(ws_at(ws, p.off_part));
-  hipError_t e;
+  hipError_t e = hipSuccess;
   // dB_i = G_i^T dZ    G_i^T: [F][M] = [M'][K], dZ^T: [H][M] = [N'][K] (both K-contig)
-  e = run_gemm(TPMLP_K_BWD_DB, KC, KC, EPI_F32, Gt, M, dZt, M, F, H, M, p.gdb, dB, nullptr, nullptr, part, s);
+  if (do_db)
+    e = run_gemm(TPMLP_K_BWD_DB, KC, KC, EPI_F32, Gt, M, dZt, M, F, H, M, p.gdb, dB, nullptr, nullptr, part, s);
   if (e != hipSuccess) return e;
-  if (p.tdp) {
+  if (!do_da) {
+  } else if (p.tdp) {
     uint16_t* dPt = reinterpret_cast<uint16_t*>(ws_at(ws, p.off_dPt));
     e = timed(TPMLP_K_TRANSPOSE, s, [&] { return launch_transpose(dP, M, F, F, dPt, s); });
     if (e != hipSuccess) return e;
@@ -1308,16 +1313,18 @@ tpmlp_status tpmlp_tp_fwd(const tpmlp_bf16* X, const tpmlp_bf16* const* A_sh, co
     float* part = reinterpret_cast<float*>(ws_at(ws, fp.off_part));
     for (int i0 = 0; i0 < t; i0 += bp.g) {
       const int g = std::min(bp.g, t - i0);
+      const void* a[MAX_BATCH];
       const void* b[MAX_BATCH];
       void* G[MAX_BATCH];
       uint16_t* P[MAX_BATCH];
       for (int j = 0; j < g; ++j) {
+        a[j] = X;
         b[j] = A_sh[i0 + j];
         G[j] = area + size_t(j) * batch_slot_bytes(M, F_i);
         P[j] = P_sh ? P_sh[i0 + j] : nullptr;
       }
       // P_i = X A_i; G_i = GeLU(P_i)      X: [M][H] (K-contig), A_i: [H][F] (N-contig)
-      hipError_t e = run_gemm_batch(TPMLP_K_FWD_GEMM1_GELU, MC, EPI_GELU, X, H, b, F_i, M, F_i, H, bp.plan, g, G, P,
+      hipError_t e = run_gemm_batch(TPMLP_K_FWD_GEMM1_GELU, MC, EPI_GELU, a, H, b, F_i, M, F_i, H, bp.plan, g, G, P,
                                     nullptr, s);
       for (int j = 0; j < g && e == hipSuccess; ++j) {
         const int i = i0 + j;
@@ -1399,6 +1406,8 @@ tpmlp_status tpmlp_tp_bwd(const tpmlp_bf16* dZ, const tpmlp_bf16* X, const tpmlp
     const size_t mfa = align_up(mf * 2);
     for (int i0 = 0; i0 < t; i0 += bp.g) {
       const int g = std::min(bp.g, t - i0);
+      const void* xs[MAX_BATCH];
+      const void* dzs[MAX_BATCH];
       const void* a_w[MAX_BATCH];
       const void* b_w[MAX_BATCH];
       void* Pw[MAX_BATCH];
@@ -1407,6 +1416,8 @@ tpmlp_status tpmlp_tp_bwd(const tpmlp_bf16* dZ, const tpmlp_bf16* X, const tpmlp
       uint16_t* Gts[MAX_BATCH];
       for (int j = 0; j < g; ++j) {
         char* slot = area + size_t(j) * batch_slot_bytes(M, F_i);
+        xs[j] = X;
+        dzs[j] = dZ;
         a_w[j] = A_sh[i0 + j];
         b_w[j] = B_sh[i0 + j];
         Pw[j] = slot;
@@ -1416,15 +1427,40 @@ tpmlp_status tpmlp_tp_bwd(const tpmlp_bf16* dZ, const tpmlp_bf16* X, const tpmlp
       }
       hipError_t e = hipSuccess;
       if (recompute)  // P_i = X A_i again   X: [M][H] (K-contig), A_i: [H][F] (N-contig)
-        e = run_gemm_batch(TPMLP_K_BWD_RECOMPUTE, MC, EPI_BF16, X, H, a_w, F_i, M, F_i, H, bp.plan, g, Pw, nullptr,
+        e = run_gemm_batch(TPMLP_K_BWD_RECOMPUTE, MC, EPI_BF16, xs, H, a_w, F_i, M, F_i, H, bp.plan, g, Pw, nullptr,
                            nullptr, s);
       // dG_i = dZ B_i^T; dP_i = dG_i GeLU'(P_i); G_i^T    dZ: [M][H], B_i: [F][H] (both K-contig)
       if (e == hipSuccess)
-        e = run_gemm_batch(TPMLP_K_BWD_DGELU, KC, EPI_DGELU, dZ, H, b_w, H, M, F_i, H, bp.plan, g, dPs, Gts, P, s);
+        e = run_gemm_batch(TPMLP_K_BWD_DGELU, KC, EPI_DGELU, dzs, H, b_w, H, M, F_i, H, bp.plan, g, dPs, Gts, P, s);
+      // dB_i and dA_i (no cross-shard sum) in batches of their own size where that
+      // pays, else one launch per shard; then each shard's dX_i.
+      const BatchPlan bdb = plan_batch(F_i, H, M, g), bda = plan_batch(H, F_i, M, g);
+      const void* dzt[MAX_BATCH];
+      const void* xt[MAX_BATCH];
+      for (int j = 0; j < g; ++j) {
+        dzt[j] = dZt;
+        xt[j] = Xt;
+      }
+      float* const* dBs = dB_sh + i0;
+      float* const* dAs = dA_sh + i0;
+      for (int j0 = 0; bdb.g > 1 && j0 < g && e == hipSuccess; j0 += bdb.g) {
+        // dB_i = G_i^T dZ    G_i^T: [F][M], dZ^T: [H][M] (both K-contig)
+        const int gb = std::min(bdb.g, g - j0);
+        e = run_gemm_batch(TPMLP_K_BWD_DB, KC, EPI_F32, reinterpret_cast<const void* const*>(Gts + j0), M,
+                           dzt + j0, M, F_i, H, M, bdb.plan, gb, reinterpret_cast<void* const*>(dBs + j0), nullptr,
+                           nullptr, s);
+      }
+      const bool batch_da = bda.g > 1 && !p.tdp;
+      for (int j0 = 0; batch_da && j0 < g && e == hipSuccess; j0 += bda.g) {
+        // dA_i = X^T dP_i    X^T: [H][M] (K-contig), dP_i: [M][F] (N-contig)
+        const int ga = std::min(bda.g, g - j0);
+        e = run_gemm_batch(TPMLP_K_BWD_DA, MC, EPI_F32, xt + j0, M, const_cast<const void* const*>(dPs + j0), F_i,
+                           H, F_i, M, bda.plan, ga, reinterpret_cast<void* const*>(dAs + j0), nullptr, nullptr, s);
+      }
       for (int j = 0; j < g && e == hipSuccess; ++j) {
         const int i = i0 + j;
         e = enqueue_bwd_weights_dx(p, static_cast<const uint16_t*>(dPs[j]), Gts[j], Xt, dZt, A_sh[i], F_i, dXs[i],
-                                   dA_sh[i], F_i, dB_sh[i], M, H, F_i, ws, s, fold && i > 0);
+                                   dA_sh[i], F_i, dB_sh[i], M, H, F_i, ws, s, fold && i > 0, bdb.g == 1, !batch_da);
       }
       if (e != hipSuccess) return hip_fail(e, "tpmlp_tp_bwd launch");
     }
