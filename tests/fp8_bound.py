@@ -220,3 +220,186 @@ def worst_ratio(got: np.ndarray, ref: np.ndarray, tol: np.ndarray):
         return 0.0, ()
     k = np.unravel_index(int(np.argmax(r)), r.shape)
     return float(r[k]), tuple(int(i) for i in k)
+
+
+# ---------------------------------------------------------------------------
+# Sampled outputs at full size
+# ---------------------------------------------------------------------------
+def _err_bound(a, b):
+    """The accumulation-error bound of a @ b (as accumulation_error in shard_moves,
+    K + 4 roundings): a [m, K], b [K, n].  The sum of |terms| is formed in float32
+    and raised by 1e-4 relative, far more than float32's own error on it."""
+    K = a.shape[1]
+    aa, ab = np.abs(a).astype(np.float32), np.abs(b).astype(np.float32)
+    return (K + 4) * U32 * (1 + 1e-4) * (aa @ ab).astype(np.float64) + \
+        (-(-K // MFMA_K)) * MFMA_REL_ERR * np.max(aa, axis=1).astype(np.float64)[:, None] * \
+        np.max(ab, axis=0).astype(np.float64)[None, :]
+
+
+def _g_interval(P_ex, e_p):
+    """Admissible bf16 P, and GeLU(P) in float32 (its error included)."""
+    plo, phi = F.round_bf16(P_ex - e_p), F.round_bf16(P_ex + e_p)
+    glo, ghi = _range_of(O.gelu, plo, phi, [GELU_MIN_AT])
+    w = GELU_ABS_ERR_PER_P * np.maximum(np.abs(plo), np.abs(phi))
+    return plo, phi, glo - w, ghi + w
+
+
+def _dp_interval(dG_ex, e_dg, plo, phi):
+    """Admissible bf16 dP = bf16(dG GeLU'(P))."""
+    d_lo, d_hi = _range_of(O.gelu_grad, plo, phi, [-SQRT2, SQRT2])
+    d_lo, d_hi = d_lo - GRAD_ABS_ERR, d_hi + GRAD_ABS_ERR
+    c = [(dG_ex - e_dg) * d_lo, (dG_ex - e_dg) * d_hi, (dG_ex + e_dg) * d_lo, (dG_ex + e_dg) * d_hi]
+    return F.round_bf16(np.minimum.reduce(c)), F.round_bf16(np.maximum.reduce(c))
+
+
+def _moves_given_amax(lo, hi, ref_q, fmt, amax_lo, amax_hi):
+    """_code_moves with the tensor's amax interval given."""
+    s_lo = F.scale_of(np.float32(amax_lo), fmt)
+    s_hi = F.scale_of(np.float32(amax_hi), fmt)
+    inv_hi = np.float32(np.float32(1.0) / s_lo)
+    inv_lo = np.float32(np.float32(1.0) / s_hi)
+    ends = [_f32(lo) * inv_lo, _f32(lo) * inv_hi, _f32(hi) * inv_lo, _f32(hi) * inv_hi]
+    v_lo = F.decode(F.encode(np.minimum.reduce(ends), fmt), fmt)
+    v_hi = F.decode(F.encode(np.maximum.reduce(ends), fmt), fmt)
+    move = np.zeros(ref_q.shape, dtype=np.float64)
+    for v in (v_lo, v_hi):
+        for sc in (np.float64(s_lo), np.float64(s_hi)):
+            move = np.maximum(move, np.abs(v * sc - ref_q))
+    return move
+
+
+def qdq_fast(T, fmt: F.Fp8Format) -> np.ndarray:
+    """F.qdq for large tensors: the same scale, the same float32 product, the same
+    clamp to +-FMAX, then torch's float8 casts (round to nearest, ties to even)
+    as the library primitive for the rounding.  Equal to F.qdq (CPU test)."""
+    import torch
+    t32 = np.asarray(T, dtype=np.float32)
+    amax = np.float32(np.max(np.abs(t32))) if t32.size else np.float32(0)
+    sc = F.scale_of(amax, fmt)
+    y = np.clip(t32 * np.float32(np.float32(1.0) / sc), -fmt.fmax, fmt.fmax).astype(np.float32)
+    dt = torch.float8_e4m3fn if fmt is F.E4M3 else torch.float8_e5m2
+    v = torch.from_numpy(y).to(dt).to(torch.float32).numpy()
+    return v.astype(np.float64) * np.float64(sc)
+
+
+def _quant_with(T, s, fmt):
+    """The oracle's quantization of T under a given scale s (its dequantized value)."""
+    return F.decode(F.encode(_f32(T) * np.float32(np.float32(1.0) / s), fmt), fmt) * np.float64(s)
+
+
+@dataclass
+class SampledBounds:
+    rows: np.ndarray
+    cols: np.ndarray
+    Z: np.ndarray          # [rows, H]
+    dX: np.ndarray         # [rows, H]
+    dA: List[np.ndarray]   # [H, cols] per shard
+    dB: List[np.ndarray]   # [cols, H] per shard
+    P: List[np.ndarray]    # [rows, F_i] per shard (the oracle's bf16 P_i)
+    p_lo: List[np.ndarray]
+    p_hi: List[np.ndarray]
+    tol_Z: np.ndarray
+    tol_dX: np.ndarray
+    tol_dA: List[np.ndarray]
+    tol_dB: List[np.ndarray]
+
+
+def sampled_path_bounds(X, A_sh, B_sh, dZ, rows, cols, chunk=2048) -> SampledBounds:
+    """path_bounds on rows `rows` of Z and dX and on columns `cols` of every dA_i
+    (rows of dB_i), for shapes too large to hold whole.  The scales need the max
+    over whole tensors: the full products are formed one chunk of rows at a time,
+    with the same element-wise intervals, and only their maxima kept.  The R10
+    part of each tolerance uses the max |oracle| over the sampled elements."""
+    rows, cols = np.asarray(rows), np.asarray(cols)
+    M, H = X.shape
+    Xq, dZq = qdq_fast(X, F.E4M3), qdq_fast(dZ, F.E5M2)
+    Z = dX = mZ = mdX = None
+    dA, dB, Ps, plos, phis, tdA, tdB = [], [], [], [], [], [], []
+    for A_i, B_i in zip(A_sh, B_sh):
+        Aq, Bq = qdq_fast(A_i, F.E4M3), qdq_fast(B_i, F.E4M3)
+        BqT = np.ascontiguousarray(Bq.T)
+        # Maxima of |G| and |dP| over all rows: the oracle's and the admissible
+        # interval ends.  A float32 pass over all elements finds the few that
+        # can hold a max; float64 then gives their exact values and intervals.
+        # Screening window per element (a bound on how far its float32 estimate
+        # can lie from any admissible or oracle value): the GPU error bound, the
+        # float32 pass's own error ((K + 2) u on the sum of |terms|, inputs
+        # rounded to float32 included), one bf16 step of P (2^-7 |P|), GeLU' at
+        # most 1.13 and GeLU'' at most 0.8 in magnitude, GeLU's error, one bf16
+        # step of dP.
+        Xq32, Aq32 = Xq.astype(np.float32), Aq.astype(np.float32)
+        dZq32, BqT32 = dZq.astype(np.float32), BqT.astype(np.float32)
+        g_est, dp_est = [], []
+        for r0 in range(0, M, chunk):
+            xs, dzs = Xq32[r0:r0 + chunk], dZq32[r0:r0 + chunk]
+            P32, S = xs @ Aq32, _err_bound(xs, Aq32)
+            eP = S * (1 + (H + 2) / (H + 4))  # the GPU's bound plus the float32 pass's
+            Pm = np.abs(P32) + eP
+            mP = eP + 2.0 ** -6 * Pm
+            G = np.abs(O.gelu(P32.astype(np.float64)))
+            wG = 1.13 * mP + GELU_ABS_ERR_PER_P * Pm
+            dG32, SD = dzs @ BqT32, _err_bound(dzs, BqT32)
+            edG = SD * (1 + (H + 2) / (H + 4))
+            dGm = np.abs(dG32) + edG
+            dP = np.abs(dG32.astype(np.float64) * O.gelu_grad(P32.astype(np.float64)))
+            wD = 1.13 * edG + dGm * (0.8 * mP + GRAD_ABS_ERR) + 2.0 ** -6 * (dP + 1.13 * edG)
+            g_est.append((r0, (G - wG).max(), G.astype(np.float32), wG.astype(np.float32)))
+            dp_est.append((r0, (dP - wD).max(), dP.astype(np.float32), wD.astype(np.float32)))
+
+        def exact_max(est, kind):
+            floor = max(e[1] for e in est)  # no max is below the largest lower estimate
+            rows_c, cols_c = [], []
+            for r0, _, v, w in est:
+                rr, cc = np.nonzero(v.astype(np.float64) + w.astype(np.float64) * (1 + 1e-6) >= floor)
+                rows_c.append(rr + r0)
+                cols_c.append(cc)
+            rr, cc = np.concatenate(rows_c), np.concatenate(cols_c)
+            P_ex = np.einsum("ij,ji->i", Xq[rr], Aq[:, cc])
+            eP = np.array([_err_bound(Xq[r:r + 1], Aq[:, c:c + 1])[0, 0] for r, c in zip(rr, cc)])
+            plo, phi, glo, ghi = _g_interval(P_ex, eP)
+            P = F.round_bf16(P_ex)
+            if kind == "g":
+                lo, hi = _abs_range(glo, ghi)
+                return float(np.max(np.abs(O.gelu(P)))), float(lo.max()), float(hi.max())
+            dG_ex = np.einsum("ij,ij->i", dZq[rr], Bq[cc])
+            edG = np.array([_err_bound(dZq[r:r + 1], BqT[:, c:c + 1])[0, 0] for r, c in zip(rr, cc)])
+            lo, hi = _abs_range(*_dp_interval(dG_ex, edG, plo, phi))
+            return float(np.max(np.abs(F.round_bf16(dG_ex * O.gelu_grad(P))))), float(lo.max()), float(hi.max())
+
+        g_or, g_lo, g_hi = exact_max(g_est, "g")
+        dp_or, dp_lo, dp_hi = exact_max(dp_est, "d")
+        del g_est, dp_est
+        sG = F.scale_of(np.float32(g_or), F.E4M3)
+        sdP = F.scale_of(np.float32(dp_or), F.E5M2)
+
+        def sample(xs, aq, dzs, bqT):
+            """G's and dP's dequantized oracle values and admissible moves, and the
+            P interval, for the product block xs @ aq (rows of dZ: dzs)."""
+            P_ex, eP = xs @ aq, _err_bound(xs, aq)
+            P = F.round_bf16(P_ex)
+            plo, phi, glo, ghi = _g_interval(P_ex, eP)
+            Gq = _quant_with(O.gelu(P), sG, F.E4M3)
+            mG = _moves_given_amax(glo, ghi, Gq, F.E4M3, g_lo, g_hi)
+            dG_ex, edG = dzs @ bqT, _err_bound(dzs, bqT)
+            dPq = _quant_with(F.round_bf16(dG_ex * O.gelu_grad(P)), sdP, F.E5M2)
+            lo, hi = _dp_interval(dG_ex, edG, plo, phi)
+            mdP = _moves_given_amax(lo, hi, dPq, F.E5M2, dp_lo, dp_hi)
+            return P, plo, phi, Gq, mG, dPq, mdP
+
+        # sampled rows (all columns): Z and dX rows; sampled columns (all rows): dA, dB
+        Pr, plo_r, phi_r, Gq_r, mG_r, dPq_r, mdP_r = sample(Xq[rows], Aq, dZq[rows], BqT)
+        _, _, _, Gq_c, mG_c, dPq_c, mdP_c = sample(Xq, Aq[:, cols], dZq, BqT[:, cols])
+        z, mz = Gq_r @ Bq, mG_r @ np.abs(Bq)
+        dx, mdx = dPq_r @ Aq.T, mdP_r @ np.abs(Aq).T
+        Z, mZ = (z, mz) if Z is None else (Z + z, mZ + mz)
+        dX, mdX = (dx, mdx) if dX is None else (dX + dx, mdX + mdx)
+        dA_c, dB_c = Xq.T @ dPq_c, Gq_c.T @ dZq
+        dA.append(dA_c)
+        dB.append(dB_c)
+        tdA.append(O.tolerance(dA_c) + np.abs(Xq).T @ mdP_c)
+        tdB.append(O.tolerance(dB_c) + mG_c.T @ np.abs(dZq))
+        Ps.append(Pr)
+        plos.append(plo_r)
+        phis.append(phi_r)
+    return SampledBounds(rows, cols, Z, dX, dA, dB, Ps, plos, phis, O.tolerance(Z) + mZ, O.tolerance(dX) + mdX,
+                         tdA, tdB)

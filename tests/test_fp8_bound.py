@@ -134,3 +134,53 @@ def test_unique_decisions_admit_no_move():
     assert b.ambiguous_g == 0 and b.ambiguous_dp == 0
     assert float(b.tol_Z[0, 0]) == pytest.approx(O.tolerance(b.Z), abs=1e-6)
     assert float(b.tol_dX[0, 0]) == pytest.approx(O.tolerance(b.dX), abs=1e-6)
+
+
+def test_sampled_bounds_equal_the_whole_tensor_bounds():
+    """sampled_path_bounds (chunked full products, sampled outputs) gives the same
+    oracle values and P intervals as path_bounds restricted to the sampled rows
+    and columns, and the same admissible moves up to its float32 sums of |terms|
+    (raised by 1e-4); only the R10 part of each tolerance, taken over the
+    sampled elements, differs."""
+    X, A, B, dZ = _case(528, 272, 400, 2, 405)
+    full = FB.path_bounds(X, A, B, dZ)
+    rng = np.random.default_rng(7)
+    rows = np.sort(rng.choice(528, 40, replace=False))
+    cols = np.sort(rng.choice(400, 24, replace=False))
+    sb = FB.sampled_path_bounds(X, A, B, dZ, rows, cols, chunk=96)
+    close = lambda a, b: np.testing.assert_allclose(a, b, rtol=1e-9, atol=1e-12)
+    near = lambda a, b: np.testing.assert_allclose(a, b, rtol=1e-3, atol=1e-9)
+    close(sb.Z, full.Z[rows])
+    close(sb.dX, full.dX[rows])
+    near(sb.tol_Z - O.tolerance(sb.Z), (full.tol_Z - O.tolerance(full.Z))[rows])
+    near(sb.tol_dX - O.tolerance(sb.dX), (full.tol_dX - O.tolerance(full.dX))[rows])
+    for i in range(2):
+        close(sb.dA[i], full.dA[i][:, cols])
+        close(sb.dB[i], full.dB[i][cols, :])
+        near(sb.tol_dA[i] - O.tolerance(sb.dA[i]), (full.tol_dA[i] - O.tolerance(full.dA[i]))[:, cols])
+        near(sb.tol_dB[i] - O.tolerance(sb.dB[i]), (full.tol_dB[i] - O.tolerance(full.dB[i]))[cols, :])
+        # bf16 values: float64 sums in another blocking may land on the other side of
+        # a rounding tie, so one bf16 step apart at most
+        bf = lambda a, b: np.testing.assert_allclose(a, b, rtol=2.0 ** -7, atol=1e-30)
+        bf(sb.P[i], full.P[i][rows])
+        bf(sb.p_lo[i], full.shards[i].p_lo[rows])
+        bf(sb.p_hi[i], full.shards[i].p_hi[rows])
+
+
+def test_fast_quantization_equals_the_oracle():
+    """qdq_fast (torch's float8 casts after the oracle's clamp) gives F.qdq's
+    values, bit for bit, for both formats: random magnitudes over the whole range,
+    values deep in the subnormals, exact zeros, ties, and the saturating max."""
+    rng = np.random.default_rng(11)
+    for fmt in (F.E4M3, F.E5M2):
+        x = rng.standard_normal(200000) * np.exp2(rng.integers(-20, 6, 200000))
+        x[:1000] = 0.0
+        x[1000:2000] = -0.0
+        # exact midpoints between neighbouring codes (after scaling by 1/s = FMAX/amax)
+        codes = np.arange(256, dtype=np.uint8)
+        vals = F.decode(codes, fmt)
+        ok = np.isfinite(vals)
+        mids = (np.sort(vals[ok])[1:] + np.sort(vals[ok])[:-1]) / 2
+        amax = float(np.max(np.abs(x)))
+        x[2000:2000 + mids.size] = mids * amax / fmt.fmax
+        np.testing.assert_array_equal(FB.qdq_fast(x, fmt), F.qdq(x, fmt))

@@ -285,3 +285,57 @@ def test_fp8_split_products_collect_amax(case):
             sh = bd.shards[i]
             assert int(np.count_nonzero((Pg < sh.p_lo) | (Pg > sh.p_hi))) == 0, f"P_{i} outside the admissible roundings"
     say("  err/tol:", {k: round(v, 3) for k, v in r.items()})
+
+
+def test_fp8_long_context_chunk_sampled():
+    """The FP8 path at the long-context chunk's full size (M=32768, H=3584,
+    F_i=3584, t=4, P_i kept) in the launch configuration the benchmark times
+    (DeviceFp8MLP: the t-shard driver over all four shards).  Rows of Z and dX
+    in two classes, each with the R10 part of its tolerance from its own
+    max|oracle|: two seeded rows from every 256-row tile of the rows that are
+    not outliers, and 32 of the outlier rows (X scaled x8); columns of every
+    dA_i and rows of every dB_i, two from every 256-wide block; the stored P_i on
+    the sampled rows inside their admissible roundings.  The oracle's scales
+    come from its full products (tests/fp8_bound.py, sampled_path_bounds)."""
+    from tensor_transformer_mlp_03_amd.device import DeviceFp8MLP
+    w = I.CONFIGS[3]
+    say(f"[fp8 config3 sampled] {w}")
+    inp = I.make_inputs(w)
+    d = DeviceFp8MLP(inp, store_p=True)
+    d.step()
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(1234 + 8)
+    normal = []
+    ex = np.zeros(w.M, dtype=bool)
+    ex[np.asarray(inp.outliers)] = True
+    for b0 in range(0, w.M, 256):
+        cand = np.nonzero(~ex[b0:b0 + 256])[0] + b0
+        normal.extend(rng.choice(cand, size=2, replace=False).tolist())
+    normal = np.array(sorted(normal))
+    outl = np.sort(rng.choice(inp.outliers, size=32, replace=False))
+    rows = np.concatenate([normal, outl])
+    cols = np.array(sorted(c for b0 in range(0, w.F_i, 256)
+                           for c in rng.choice(np.arange(b0, min(b0 + 256, w.F_i)), 2, replace=False)))
+    got = {"Z": d.Z[rows].cpu().numpy(), "dX": d.dX[rows].cpu().numpy(),
+           "dA": [a[:, cols].cpu().numpy() for a in d.dA], "dB": [b[cols, :].cpu().numpy() for b in d.dB],
+           "P": [O.decode_bf16(p[rows].cpu().numpy().view(np.uint16)) for p in d.P]}
+    del d
+    torch.cuda.empty_cache()
+    X, dZ = O.decode_bf16(inp.X), O.decode_bf16(inp.dZ)
+    A, B = [O.decode_bf16(a) for a in inp.A], [O.decode_bf16(b) for b in inp.B]
+    del inp
+    say(f"  {normal.size} normal rows, {outl.size} outlier rows, {cols.size} dA columns / dB rows; oracle ...")
+    sb = FB.sampled_path_bounds(X, A, B, dZ, rows, cols)
+    r = {}
+    n = normal.size
+    for cls, sl in (("normal", slice(0, n)), ("outlier", slice(n, None))):
+        for name in ("Z", "dX"):
+            ref = getattr(sb, name)[sl]
+            moves = (getattr(sb, "tol_" + name) - O.tolerance(getattr(sb, name)))[sl]
+            check(f"{name}[{cls}]", got[name][sl], ref, O.tolerance(ref) + moves, r)
+    for i in range(w.t):
+        check(f"dA_{i}[:,cols]", got["dA"][i], sb.dA[i], sb.tol_dA[i], r)
+        check(f"dB_{i}[cols,:]", got["dB"][i], sb.dB[i], sb.tol_dB[i], r)
+        outside = int(np.count_nonzero((got["P"][i] < sb.p_lo[i]) | (got["P"][i] > sb.p_hi[i])))
+        assert outside == 0, f"P_{i}: {outside} sampled values outside the admissible roundings"
+    say("  err/tol:", {k: round(v, 3) for k, v in r.items()})
