@@ -293,8 +293,9 @@ tpmlp_status tpmlp_fp8_tp_fwd(const tpmlp_bf16* X, const tpmlp_bf16* const* A_sh
  * written by tpmlp_fp8_tp_fwd.  ws: the workspace of the tpmlp_fp8_tp_fwd call
  * with the same X, A_sh, B_sh, t, M, H, F_i (and, with P_sh, the same P_sh),
  * not written since.  The library records each forward's arguments per
- * workspace address on the host and returns TPMLP_ERR_NO_FORWARD when they do
- * not match; it cannot see a workspace or an input changed in between. */
+ * workspace address on the host (of the 256 latest forwards' workspaces) and
+ * returns TPMLP_ERR_NO_FORWARD when they do not match or were not kept; it
+ * cannot see a workspace or an input changed in between. */
 tpmlp_status tpmlp_fp8_tp_bwd(const tpmlp_bf16* dZ, const tpmlp_bf16* X, const tpmlp_bf16* const* A_sh,
                               const tpmlp_bf16* const* B_sh, const tpmlp_bf16* const* P_sh,
                               float* const* dA_sh, float* const* dB_sh, float* dX, int t, int64_t M, int64_t H,

@@ -1090,13 +1090,16 @@ void forget_fp8_forward(const void* ws) {
                      g_fp8_stamps.end());
 }
 
+// At most this many workspaces' forwards are remembered; the least recently
+// recorded goes first (its backward then returns TPMLP_ERR_NO_FORWARD).
+constexpr size_t MAX_FP8_STAMPS = 256;
+
 void record_fp8_forward(const void* ws, Fp8Stamp st) {
-  std::lock_guard<std::mutex> lk(g_fp8_mu);
-  for (auto& e : g_fp8_stamps)
-    if (e.first == ws) {
-      e.second = std::move(st);
-      return;
-    }
+  std::lock_guard<std::mutex> lk(g_fp8_mu);  // the newest record is at the back
+  g_fp8_stamps.erase(std::remove_if(g_fp8_stamps.begin(), g_fp8_stamps.end(),
+                                    [&](const std::pair<const void*, Fp8Stamp>& e) { return e.first == ws; }),
+                     g_fp8_stamps.end());
+  if (g_fp8_stamps.size() >= MAX_FP8_STAMPS) g_fp8_stamps.erase(g_fp8_stamps.begin());
   g_fp8_stamps.emplace_back(ws, std::move(st));
 }
 
