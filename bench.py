@@ -612,19 +612,30 @@ def main():
     extra = {}
     if args.also >= 0 and args.also != args.config and not (args.graph or args.trace_order or args.full_weights):
         # The second target workload, timed the same way in the same run, reported
-        # in its own object; the headline stays the first.
+        # in its own object; the headline stays the first and is printed whatever
+        # happens here.
         w2 = I.CONFIGS[args.also]
-        m2 = measure(w2, args, L, I, DeviceMLP, torch)
-        extra[w2.name] = {
-            "workload": w2.name, "M": w2.M, "H": w2.H, "F_i": w2.F_i, "t": w2.t,
-            "shards_per_step": m2["shards"], "pre_activation": "recompute" if w2.recompute else "stored",
-            "ms_per_step": round(m2["ms_per_step"], 4), "value": round(m2["value"], 2), "unit": "TFLOP/s",
-            "frac_of_peak": round(m2["value"] / PEAK_BF16_TFLOPS, 4),
-            "hfu_tflops": round(m2["value"] * (14.0 if w2.recompute else 12.0) / 12.0, 2),
-            "roofline": m2["roofline"], "timing_dropped": m2["dropped"]}
+        try:
+            m2 = measure(w2, args, L, I, DeviceMLP, torch)
+            extra[w2.name] = {
+                "workload": w2.name, "M": w2.M, "H": w2.H, "F_i": w2.F_i, "t": w2.t,
+                "shards_per_step": m2["shards"], "pre_activation": "recompute" if w2.recompute else "stored",
+                "ms_per_step": round(m2["ms_per_step"], 4), "value": round(m2["value"], 2), "unit": "TFLOP/s",
+                "frac_of_peak": round(m2["value"] / PEAK_BF16_TFLOPS, 4),
+                "hfu_tflops": round(m2["value"] * (14.0 if w2.recompute else 12.0) / 12.0, 2),
+                "roofline": m2["roofline"], "timing_dropped": m2["dropped"]}
+        except Exception as e:
+            log(f"[bench] {w2.name} failed: {e!r}")
+            extra[w2.name] = {"workload": w2.name, "error": repr(e)}
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
     fp8 = None
     if not (args.no_fp8 or args.graph or args.trace_order or args.full_weights) and w.backward:
-        fp8 = measure_fp8(w, args, L, I, torch)
+        try:
+            fp8 = measure_fp8(w, args, L, I, torch)
+        except Exception as e:  # the headline line is printed whatever happens here
+            log(f"[bench] FP8 path failed: {e!r}")
+            fp8 = {"workload": w.name, "error": repr(e)}
     shards, ms_per_step, value, roofline, dropped = m["shards"], m["ms_per_step"], m["value"], m["roofline"], \
         m["dropped"]
 
@@ -656,7 +667,8 @@ def main():
     if extra:
         result["workloads"] = extra
     if fp8:
-        fp8["vs_bf16"] = round(fp8["value"] / value, 3)
+        if "value" in fp8:
+            fp8["vs_bf16"] = round(fp8["value"] / value, 3)
         result["fp8"] = fp8
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a row sample")

@@ -90,6 +90,7 @@ FP8_CASES = [
     (1040, 1056, 1072, 1, True),
     (2048, 1024, 2048, 2, False),  # 256-row tiles, long K for dB / dA
     (8192, 256, 512, 1, True),     # K = 8192 for dB / dA: split-K slices
+    (272, 144, 176, 8, False),     # eight shards: eight sets of codes and scales, sums in rank order
 ]
 
 
