@@ -195,6 +195,42 @@ def cpu_baseline(w, target_s=12.0):
                       f"(H={w.H}, F_i={w.F_i}); {dt:.2f} s on {cpu}, numpy BLAS {blas}"}
 
 
+def cpu_baseline_fp8(w, target_s=8.0):
+    """The FP8 oracle's forward+backward of shard 0 on a bounded sample of token
+    rows (the sample is the tensor the oracle quantizes), as cpu_baseline does
+    for the bf16 oracle."""
+    import numpy as np
+    from oracle import fp8 as F8
+    from oracle import oracle as O
+    from tensor_transformer_mlp_03_amd import inputs as I
+    i = w.shards_timed[0]
+    A = O.decode_bf16(I.make_A_shard(w, i))
+    B = O.decode_bf16(I.make_B_shard(w, i))
+    X_all, dZ_all = I.make_X(w), I.make_dZ(w)
+
+    def run(rows):
+        X, dZ = O.decode_bf16(X_all[:rows]), O.decode_bf16(dZ_all[:rows])
+        t0 = time.perf_counter()
+        F8.mlp_forward_fp8(X, A, B)
+        F8.mlp_backward_fp8(dZ, X, A, B)
+        return time.perf_counter() - t0
+
+    rows = min(w.M, 128)
+    dt = run(rows)
+    if dt < target_s / 4 and rows < w.M:
+        rows = int(min(w.M, max(rows, rows * target_s / max(dt, 1e-3))) // 16 * 16)
+        dt = run(rows)
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    return {"value": round(12.0 * rows * w.H * w.F_i / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"float64 FP8 oracle (oracle/fp8.py) forward+backward of shard {i} on the first {rows} of "
+                      f"{w.M} token rows (H={w.H}, F_i={w.F_i}); {dt:.2f} s"}
+
+
 def _order_entries(order):
     """Recorded launch order as [(kind, kernel dispatches)]: a timing record covers one
     dispatch, or two where a product runs as whole-wave tiles plus a split tail."""
@@ -673,6 +709,9 @@ def main():
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a row sample")
         result["cpu_baseline"] = cpu_baseline(w)
+        if fp8 and "value" in fp8:
+            log("[bench] timing the FP8 CPU oracle on a row sample")
+            fp8["cpu_baseline"] = cpu_baseline_fp8(w)
     print(json.dumps(result), flush=True)
 
 
