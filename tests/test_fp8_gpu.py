@@ -340,3 +340,21 @@ def test_fp8_long_context_chunk_sampled():
         outside = int(np.count_nonzero((got["P"][i] < sb.p_lo[i]) | (got["P"][i] > sb.p_hi[i])))
         assert outside == 0, f"P_{i}: {outside} sampled values outside the admissible roundings"
     say("  err/tol:", {k: round(v, 3) for k, v in r.items()})
+
+
+@pytest.mark.parametrize("case", [(528, 272, 400, 2), (512, 4096, 2560, 1)], ids=lambda c: "x".join(map(str, c)))
+def test_fp8_store_equals_recompute_bitwise(case):
+    """The FP8 backward gives the same bits whether it takes the stored P_i or
+    recomputes it: the recompute is the forward's product on the forward's codes
+    and plan, its amax is the same, and G_i^T's codes come out the same."""
+    from tensor_transformer_mlp_03_amd.device import DeviceFp8MLP
+    M, H, F_, t = case
+    say(f"[fp8 store vs recompute] M={M} H={H} F_i={F_} t={t}")
+    inp = I.make_inputs(I.custom_workload(490 + t, M=M, H=H, F_i=F_, t=t, w_std=0.05))
+    st, rc = DeviceFp8MLP(inp, store_p=True), DeviceFp8MLP(inp, store_p=False)
+    st.step()
+    rc.step()
+    torch.cuda.synchronize()
+    assert torch.equal(st.Z, rc.Z) and torch.equal(st.dX, rc.dX)
+    for i in range(t):
+        assert torch.equal(st.dA[i], rc.dA[i]) and torch.equal(st.dB[i], rc.dB[i]), f"shard {i}"
