@@ -52,11 +52,40 @@ __device__ __forceinline__ NormalTail normal_tail(float x) {
   return NormalTail{q * e, e};
 }
 
+// The same tail with the density itself: he = Phi(-|x|) and f = phi(x) =
+// exp(-x^2/2) / sqrt(2 pi).  log2(1/sqrt(2 pi)) enters the exponent and the
+// fit's coefficients carry sqrt(2 pi)/2 instead of 1/2, so that the polynomial
+// times f is he; GeLU' then takes p phi(p) in one fused multiply-add.
+struct NormalTailDensity {
+  float he;  // Phi(-|x|)
+  float f;   // phi(x)
+};
+
+__device__ __forceinline__ NormalTailDensity normal_tail_density(float x) {
+  constexpr float P = 0.3275911f;
+  constexpr double C = 1.2533141373155003;  // sqrt(2 pi) / 2
+  constexpr float A1 = (float)(C * 0.254829592), A2 = (float)(C * -0.284496736), A3 = (float)(C * 1.421413741),
+                  A4 = (float)(C * -1.453152027), A5 = (float)(C * 1.061405429);
+  constexpr float INV_SQRT2 = 0.70710678118654752f, LOG2E = 1.4426950408889634f;
+  constexpr float LOG2_INV_SQRT_2PI = -1.3257480647361594f;  // -log2(2 pi) / 2
+  const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(fabsf(x), P * INV_SQRT2, 1.0f));
+  const float f = __builtin_amdgcn_exp2f(__builtin_fmaf(x * x, -0.5f * LOG2E, LOG2_INV_SQRT_2PI));
+  const float q = t * (A1 + t * (A2 + t * (A3 + t * (A4 + t * A5))));
+  return NormalTailDensity{q * f, f};
+}
+
+// max(x, 0) as a signed-integer max of the bits: a float with the sign bit clear
+// orders as a non-negative integer, one with it set as a negative integer (and
+// maps to +0).  Unlike fmaxf it needs no canonicalizing of x first.
+__device__ __forceinline__ float relu_bits(float x) {
+  return __builtin_bit_cast(float, max(__builtin_bit_cast(int, x), 0));
+}
+
 // GeLU(x) in float32, as x Phi(x) = max(x, 0) - |x| Phi(-|x|), which holds for
 // either sign of x.
 __device__ __forceinline__ float gelu_f32(float x) {
   const NormalTail n = normal_tail(x);
-  return __builtin_fmaf(-fabsf(x), n.he, x > 0.0f ? x : 0.0f);
+  return __builtin_fmaf(-fabsf(x), n.he, relu_bits(x));
 }
 
 // G = GeLU(acc) -> bf16.
@@ -68,21 +97,19 @@ struct DGelu {
   uint16_t dp, g;
 };
 __device__ __forceinline__ DGelu epi_dgelu(float dg, uint16_t p_bits) {
-  constexpr float INV_SQRT_2PI = 0.39894228040143268f;
   const float p = bf16_to_f32(p_bits);
-  const NormalTail n = normal_tail(p);
-  const float cdf = p >= 0.0f ? 1.0f - n.he : n.he;                  // Phi(p)
-  const float grad = __builtin_fmaf(p * n.e, INV_SQRT_2PI, cdf);     // Phi(p) + p phi(p)
+  const NormalTailDensity n = normal_tail_density(p);
+  const float cdf = p >= 0.0f ? 1.0f - n.he : n.he;  // Phi(p)
+  const float grad = __builtin_fmaf(p, n.f, cdf);    // Phi(p) + p phi(p)
   return DGelu{f32_to_bf16(dg * grad), f32_to_bf16(p * cdf)};
 }
 
 // dP = dG GeLU'(p) in float32 (the FP8 path's dGeLU, which needs no G).
 __device__ __forceinline__ float dgelu_f32(float dg, uint16_t p_bits) {
-  constexpr float INV_SQRT_2PI = 0.39894228040143268f;
   const float p = bf16_to_f32(p_bits);
-  const NormalTail n = normal_tail(p);
+  const NormalTailDensity n = normal_tail_density(p);
   const float cdf = p >= 0.0f ? 1.0f - n.he : n.he;
-  return dg * __builtin_fmaf(p * n.e, INV_SQRT_2PI, cdf);
+  return dg * __builtin_fmaf(p, n.f, cdf);
 }
 
 // ---------------------------------------------------------------------------
@@ -147,10 +174,11 @@ __device__ __forceinline__ float slot_read(const uint32_t* slot, int nsub) {
   return __builtin_bit_cast(float, m);
 }
 
-// Scale of a tensor from its amax slot.
+// Scale of a tensor from its amax, and from its amax slot.
+__device__ __forceinline__ float fp8_scale_of(float amax, float fmax) { return amax == 0.0f ? 1.0f : amax / fmax; }
+
 __device__ __forceinline__ float fp8_scale(const uint32_t* slot, int nsub, float fmax) {
-  const float amax = slot_read(slot, nsub);
-  return amax == 0.0f ? 1.0f : amax / fmax;
+  return fp8_scale_of(slot_read(slot, nsub), fmax);
 }
 
 // Four float32 values, already multiplied by 1/s, to four FP8 codes (byte e of

@@ -84,13 +84,11 @@ __device__ __forceinline__ i16x4_t ds_read_tr(const char* p) {
   asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(a));
   return v;
 }
-// The same, ordered after every earlier memory access of the calling code (for
-// reads of bytes that the same wave has just written with ordinary stores).
-__device__ __forceinline__ i16x4_t ds_read_tr_after_stores(const char* p) {
-  i16x4_t v;
-  const uint32_t a = (uint32_t)(uintptr_t)(const lds_char_t*)p;
-  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(a) : "memory");
-  return v;
+// The same through the builtin, for the epilogue: no LDS-DMA load is in flight
+// there, so the compiler orders the read after the wave's own LDS stores and
+// waits for its result by itself, without waiting for the global loads.
+__device__ __forceinline__ i16x4_t ds_read_tr_lds(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(const lds_char_t*)p);
 }
 
 // ---------------------------------------------------------------------------
@@ -217,16 +215,17 @@ constexpr int G_ROW_B = 128;  // staged G row pitch in bytes
 
 // The epilogue proper, independent of the MFMA accumulator layout.  The wave's
 // region is NC chunks of 64 x 64, laid out nh chunks tall: chunk c covers rows
-// row_w + 64 (c % nh) and columns col_w + 64 (c / nh) onward.  stage_chunk(c)
-// writes the chunk's float32 values into `stage` (row r in 0..63 at r * ROW_B,
+// row_w + 64 (c % nh) and columns col_w + 64 (c / nh) onward.  stage_chunk(c, sc)
+// writes the chunk's float32 values (times sc for FP8 products, scale_fn() the
+// product of the operands' scales) into `stage` (row r in 0..63 at r * ROW_B,
 // 16-byte chunk q in 0..15 at position q ^ (r & 15)), and the chunk is finished
 // from there.
 // FP8 (FP8 products): EPI_BF16 and EPI_DGELU also collect the amax of what they
 // write into args.amax_out when set (of the GeLU of the written values with
 // args.amax_gelu), and EPI_DGELU writes dP only (no G^T).
-template <int EPI, int NC, bool FP8, class StageChunk>
-__device__ __forceinline__ void store_staged(StageChunk&& stage_chunk, const GemmArgs& args, char* stage, int row_w,
-                                             int col_w, int nh, int split, int lane) {
+template <int EPI, int NC, bool FP8, class StageChunk, class ScaleFn>
+__device__ __forceinline__ void store_staged(StageChunk&& stage_chunk, ScaleFn&& scale_fn, const GemmArgs& args,
+                                             char* stage, int row_w, int col_w, int nh, int split, int lane) {
   // FP8: running extremes of the written values (AmaxTrack, epilogue.h; invalid
   // elements enter as 0), updated without branches.
   AmaxTrack am;
@@ -263,17 +262,32 @@ __device__ __forceinline__ void store_staged(StageChunk&& stage_chunk, const Gem
       pre[c & 1][it] = __builtin_bit_cast(u16x8_t, __builtin_amdgcn_raw_buffer_load_b128(rs, ok ? off : OOB, 0, 0));
     }
   };
+  // The loads stay where they are issued: a scheduling barrier after each batch
+  // keeps the compiler from sinking them to their uses (one round trip each)
+  // when registers run short.
   if (EPI == EPI_DGELU) load_pre(0);
   if (EPI == EPI_F32_ACC) load_old(0);
+  __builtin_amdgcn_sched_barrier(0);
+  // FP8: the product of the operands' scales, which stage_chunk applies (taken
+  // after the first loads are issued, so that the scales' load overlaps them).
+  const float sc = FP8 ? scale_fn() : 1.0f;
 #pragma unroll
   for (int ch = 0; ch < NC; ++ch) {
     const int h = ch % nh;  // used by the stores below through row_w + 64 * h
     const int col_c = col0(ch);
-    if (EPI == EPI_F32_ACC && ch + 1 < NC) load_old(ch + 1);
-    stage_chunk(ch);
-    if (EPI == EPI_DGELU && ch + 1 < NC) load_pre(ch + 1);
+    if (EPI == EPI_F32_ACC && ch + 1 < NC) {
+      load_old(ch + 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    stage_chunk(ch, sc);
+    if (EPI == EPI_DGELU && ch + 1 < NC) {
+      load_pre(ch + 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     if (EPI == EPI_F32 || EPI == EPI_F32_ACC) {
-      float* out = reinterpret_cast<float*>(args.out) + (int64_t)split * args.split_stride;
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(reinterpret_cast<float*>(args.out) +
+                                                  (int64_t)split * args.split_stride +
+                                                  (int64_t)(row_w + 64 * h) * args.ldo + col_c);
       // Two batches of 8 vectors: with both running-sum buffers live, 16 would
       // not fit beside the accumulators.
 #pragma unroll
@@ -284,15 +298,19 @@ __device__ __forceinline__ void store_staged(StageChunk&& stage_chunk, const Gem
           const int q = (b8 + u) * 64 + lane, r = q >> 4, c = q & 15;
           xs[u] = *reinterpret_cast<const f32x4_t*>(stage + r * ROW_B + ((c ^ (r & 15)) << 4));
         }
+        __builtin_amdgcn_sched_barrier(0);  // the reads stay one batch
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
           const int it = b8 + u, q = it * 64 + lane, r = q >> 4, c = q & 15;
-          const int row = row_w + 64 * h + r, col = col_c + 4 * c;
+          const bool ok = row_w + 64 * h + r < args.M && col_c + 4 * c < args.N;
           if (EPI == EPI_F32_ACC) xs[u] += old[ch & 1][it];
-          if (row < args.M && col < args.N) *reinterpret_cast<f32x4_t*>(out + (int64_t)row * args.ldo + col) = xs[u];
+          const uint32_t off = (uint32_t)(((int64_t)r * args.ldo + 4 * c) * 4);
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, xs[u]), rs, ok ? off : OOB, 0, 0);
         }
       }
     } else {
+      const int64_t base = (int64_t)(row_w + 64 * h) * args.ldo + col_c;
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(reinterpret_cast<uint16_t*>(args.out) + base);
       f32x4_t x0s[8], x1s[8];
 #pragma unroll
       for (int it = 0; it < 8; ++it) {
@@ -300,14 +318,17 @@ __device__ __forceinline__ void store_staged(StageChunk&& stage_chunk, const Gem
         x0s[it] = *reinterpret_cast<const f32x4_t*>(stage + r * ROW_B + (((2 * cp) ^ (r & 15)) << 4));
         x1s[it] = *reinterpret_cast<const f32x4_t*>(stage + r * ROW_B + (((2 * cp + 1) ^ (r & 15)) << 4));
       }
+      __builtin_amdgcn_sched_barrier(0);  // the reads stay one batch
 #pragma unroll
       for (int it = 0; it < 8; ++it) {
         const int q = it * 64 + lane, r = q >> 3, cp = q & 7;
         const float x[8] = {x0s[it][0], x0s[it][1], x0s[it][2], x0s[it][3],
                             x1s[it][0], x1s[it][1], x1s[it][2], x1s[it][3]};
-        const int row = row_w + 64 * h + r, col = col_c + 8 * cp;
-        const bool ok = row < args.M && col < args.N;  // N % 8 == 0: 8 columns in or out together
-        const int64_t o = (int64_t)row * args.ldo + col;
+        const bool ok = row_w + 64 * h + r < args.M && col_c + 8 * cp < args.N;  // N % 8 == 0
+        const uint32_t off = ok ? (uint32_t)(((int64_t)r * args.ldo + 8 * cp) * 2) : OOB;
+        auto store = [&](const __amdgpu_buffer_rsrc_t& rd, const u16x8_t& v) {
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), rd, off, 0, 0);
+        };
         u16x8_t v1, v2;
         if (EPI == EPI_GELU) {
 #pragma unroll
@@ -315,14 +336,12 @@ __device__ __forceinline__ void store_staged(StageChunk&& stage_chunk, const Gem
             v1[e] = epi_gelu(x[e]);
             v2[e] = f32_to_bf16(x[e]);
           }
-          if (ok) {
-            *reinterpret_cast<u16x8_t*>(reinterpret_cast<uint16_t*>(args.out) + o) = v1;
-            if (args.out2) *reinterpret_cast<u16x8_t*>(args.out2 + o) = v2;
-          }
+          store(rs, v1);
+          if (args.out2) store(make_rsrc(args.out2 + base), v2);
         } else if (EPI == EPI_BF16) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) v1[e] = f32_to_bf16(x[e]);
-          if (ok) *reinterpret_cast<u16x8_t*>(reinterpret_cast<uint16_t*>(args.out) + o) = v1;
+          store(rs, v1);
           if (FP8) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) am.add(ok ? bf16_to_f32(v1[e]) : 0.0f);
@@ -330,7 +349,7 @@ __device__ __forceinline__ void store_staged(StageChunk&& stage_chunk, const Gem
         } else if (FP8) {  // EPI_DGELU of an FP8 product: dP and its amax
 #pragma unroll
           for (int e = 0; e < 8; ++e) v1[e] = f32_to_bf16(dgelu_f32(x[e], pre[ch & 1][it][e]));
-          if (ok) *reinterpret_cast<u16x8_t*>(reinterpret_cast<uint16_t*>(args.out) + o) = v1;
+          store(rs, v1);
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const float v = ok ? bf16_to_f32(v1[e]) : 0.0f;
@@ -344,7 +363,7 @@ __device__ __forceinline__ void store_staged(StageChunk&& stage_chunk, const Gem
             v1[e] = d.dp;
             v2[e] = d.g;
           }
-          if (ok) *reinterpret_cast<u16x8_t*>(reinterpret_cast<uint16_t*>(args.out) + o) = v1;
+          store(rs, v1);
           // Keep G of this row in LDS, over the chunk's float32 values (the
           // wave has read all of them above, and its LDS accesses complete in
           // order), at G_ROW_B pitch, 16-byte chunks swizzled by the row
@@ -369,19 +388,20 @@ __device__ __forceinline__ void store_staged(StageChunk&& stage_chunk, const Gem
 #pragma unroll
         for (int it = 0; it < 8; ++it) {
           const int ka = 32 * (g >> 1) + 8 * jq + jr, kb = ka + 4;  // source role: q = jq, r = jr
-          lo[it] = ds_read_tr_after_stores(stage + ka * G_ROW_B + ((it ^ gt_swz(ka)) << 4) + half);
-          hi[it] = ds_read_tr_after_stores(stage + kb * G_ROW_B + ((it ^ gt_swz(kb)) << 4) + half);
+          lo[it] = ds_read_tr_lds(stage + ka * G_ROW_B + ((it ^ gt_swz(ka)) << 4) + half);
+          hi[it] = ds_read_tr_lds(stage + kb * G_ROW_B + ((it ^ gt_swz(kb)) << 4) + half);
         }
-        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the transposed reads above are complete
+        const int m0 = row_w + 64 * h;
+        const __amdgpu_buffer_rsrc_t rt = make_rsrc(args.out2 + (int64_t)col_c * args.ldt + m0);
 #pragma unroll
         for (int it = 0; it < 8; ++it) {
           // destination role: lane 4 q + e with q = jr, e = jq
-          const int f = col_c + 8 * it + 4 * (g & 1) + jq, m = row_w + 64 * h + 32 * (g >> 1) + 8 * jr;
-          if (f < args.N && m < args.M) {
-            const u16x8_t v = {(uint16_t)lo[it][0], (uint16_t)lo[it][1], (uint16_t)lo[it][2], (uint16_t)lo[it][3],
-                               (uint16_t)hi[it][0], (uint16_t)hi[it][1], (uint16_t)hi[it][2], (uint16_t)hi[it][3]};
-            *reinterpret_cast<u16x8_t*>(args.out2 + (int64_t)f * args.ldt + m) = v;
-          }
+          const int fo = 8 * it + 4 * (g & 1) + jq, mo = 32 * (g >> 1) + 8 * jr;
+          const bool ok = col_c + fo < args.N && m0 + mo < args.M;
+          const uint32_t off = (uint32_t)(((int64_t)fo * args.ldt + mo) * 2);
+          const u16x8_t v = {(uint16_t)lo[it][0], (uint16_t)lo[it][1], (uint16_t)lo[it][2], (uint16_t)lo[it][3],
+                             (uint16_t)hi[it][0], (uint16_t)hi[it][1], (uint16_t)hi[it][2], (uint16_t)hi[it][3]};
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), rt, ok ? off : OOB, 0, 0);
         }
       }
     }
@@ -791,12 +811,24 @@ gemm_x16_kernel(GemmArgs args_in) {
   // register e holds C[16i + lane%16][16j + 4 (lane/16) + e] of the wave's
   // sub-tile.
   // FP8: the product of the two tensors' scales (unit for bf16 operands).
-  float sc = 1.0f;
-  if constexpr (F8 != 0)
-    sc = fp8_scale(args.amax_a, AMAX_SUB, fp8_fmax((F8 - 1) & 1)) *
-         fp8_scale(args.amax_b, AMAX_SUB, fp8_fmax((F8 - 1) >> 1));
+  // FP8: the two operands' amax slots in one load, one word per lane (lanes 0-15
+  // the words of A's slot, 16-31 B's); the epilogue takes the max over each
+  // 16-lane group (lane 0 then holds A's amax, lane 16 B's) once its first loads
+  // are issued.
+  static_assert(2 * AMAX_SUB <= 64 && (AMAX_SUB & (AMAX_SUB - 1)) == 0, "two slots' words fit one wave");
+  uint32_t amax_word = 0;
+  if (F8 != 0 && lane < 2 * AMAX_SUB)
+    amax_word = (lane < AMAX_SUB ? args.amax_a : args.amax_b)[(lane & (AMAX_SUB - 1)) * AMAX_SUB_STRIDE];
+  auto scales = [&]() {
+#pragma unroll
+    for (int off = AMAX_SUB / 2; off > 0; off >>= 1)
+      amax_word = max(amax_word, (uint32_t)__shfl_xor((int)amax_word, off, 64));
+    const float amax_a = __builtin_bit_cast(float, __builtin_amdgcn_readlane((int)amax_word, 0));
+    const float amax_b = __builtin_bit_cast(float, __builtin_amdgcn_readlane((int)amax_word, AMAX_SUB));
+    return fp8_scale_of(amax_a, fp8_fmax((F8 - 1) & 1)) * fp8_scale_of(amax_b, fp8_fmax((F8 - 1) >> 1));
+  };
   store_staged<EPI, (FI / 4) * (FJ / 4), F8 != 0>(
-      [&](int ch) {
+      [&](int ch, float sc) {
         const int h = ch % (FI / 4), hc = ch / (FI / 4);
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii)
@@ -808,7 +840,7 @@ gemm_x16_kernel(GemmArgs args_in) {
             *reinterpret_cast<f32x4_t*>(smem + wave * (64 * ROW_B) + r * ROW_B + ((c ^ (r & 15)) << 4)) = v;
           }
       },
-      args, smem + wave * (64 * ROW_B), m0 + (BM / 2) * wm, n0 + (BN / 2) * wn, FI / 4, split, lane);
+      scales, args, smem + wave * (64 * ROW_B), m0 + (BM / 2) * wm, n0 + (BN / 2) * wn, FI / 4, split, lane);
 #else
   (void)args_in;
 #endif
