@@ -170,7 +170,12 @@ struct AmaxTrack {
 
 __device__ __forceinline__ float slot_read(const uint32_t* slot, int nsub) {
   uint32_t m = 0;
-  for (int i = 0; i < nsub; ++i) m = max(m, slot[i * AMAX_SUB_STRIDE]);
+  if (nsub == AMAX_SUB) {  // the workspace slots: all loads issued before the first wait
+#pragma unroll
+    for (int i = 0; i < AMAX_SUB; ++i) m = max(m, slot[i * AMAX_SUB_STRIDE]);
+  } else {
+    for (int i = 0; i < nsub; ++i) m = max(m, slot[i * AMAX_SUB_STRIDE]);
+  }
   return __builtin_bit_cast(float, m);
 }
 
