@@ -508,11 +508,33 @@ def measure(w, args, L, I, DeviceMLP, torch):
         roofline["traffic"] = int(fetch + write)
         roofline["traffic_fetch"], roofline["traffic_write"] = int(fetch), int(write)
     log(f"[bench] {w.name}: {ms_per_step:.4f} ms per step, {value:.1f} TFLOP/s")
+    cold = None
+    if args.cold > 0 and graph is None:
+        # Cold steps: before each, a 512 MiB fill evicts the 256 MB Infinity Cache;
+        # events on the stream the library launches on bracket the step alone.
+        scrub = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        events = []
+        for i in range(args.cold):  # back to back, so that the GPU does not idle between steps
+            scrub.fill_(i & 0x7F)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            d.step()
+            e1.record()
+            events.append((e0, e1))
+        torch.cuda.synchronize()
+        times = [e0.elapsed_time(e1) for e0, e1 in events]
+        del scrub
+        cold_ms = sorted(times)[len(times) // 2]
+        cold = {"steps": args.cold, "ms_per_step_median": round(cold_ms, 4), "ms_per_step_min": round(min(times), 4),
+                "value": round(flops_step / (cold_ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+                "scrub_bytes": 512 << 20}
+        log(f"[bench] {w.name} cold (Infinity Cache evicted before each step): median {cold_ms:.4f} ms, "
+            f"{cold['value']:.1f} TFLOP/s")
     del d
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     return {"shards": len(shards), "ms_per_step": ms_per_step, "value": value, "roofline": roofline,
-            "dropped": dropped}
+            "dropped": dropped, "cold": cold}
 
 
 def measure_fp8(w, args, L, I, torch):
@@ -594,6 +616,9 @@ def main():
                     help="second workload timed in the same run and reported under \"workloads\" (default 4, "
                          "the 530B-class shard; -1 for none; skipped with --graph or --trace-order)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold", type=int, default=0,
+                    help="also time this many steps one at a time, each after a 512 MiB fill that evicts the "
+                         "Infinity Cache (reported as `cold`; the headline stays the back-to-back steps)")
     ap.add_argument("--no-fp8", action="store_true",
                     help="skip the FP8 path's measurement on the first workload (reported under \"fp8\")")
     ap.add_argument("--fp8-only", action="store_true",
@@ -660,6 +685,8 @@ def main():
                 "frac_of_peak": round(m2["value"] / PEAK_BF16_TFLOPS, 4),
                 "hfu_tflops": round(m2["value"] * (14.0 if w2.recompute else 12.0) / 12.0, 2),
                 "roofline": m2["roofline"], "timing_dropped": m2["dropped"]}
+            if m2["cold"]:
+                extra[w2.name]["cold"] = m2["cold"]
         except Exception as e:
             log(f"[bench] {w2.name} failed: {e!r}")
             extra[w2.name] = {"workload": w2.name, "error": repr(e)}
@@ -700,6 +727,8 @@ def main():
         "roofline": roofline,
         "cpu_baseline": None,
     }
+    if m["cold"]:
+        result["cold"] = m["cold"]
     if extra:
         result["workloads"] = extra
     if fp8:
