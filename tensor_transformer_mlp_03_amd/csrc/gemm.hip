@@ -73,10 +73,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
 // ds_read_b64_tr_b16 from LDS address `p`.  Issued through inline assembly:
 // the builtin makes the compiler wait for every vector-memory load in flight
 // (vmcnt(0)) before it, in case an LDS-DMA load targets the same bytes, which
-// would stall the load pipeline of this kernel on every memory phase.  Callers
-// read only bytes whose loads and writes have already been waited for and made
-// visible by a barrier, and wait for the results themselves (lgkmcnt(0))
-// before using them.
+// would stall the load pipeline of this kernel on every memory phase (30 such
+// waits in the main loop of the N-contiguous kernels with this compiler).
+// Callers read only bytes whose loads and writes have already been waited for
+// and made visible by a barrier, and wait for the results themselves
+// (lgkmcnt(0)) before using them.  The compiler takes the output register as
+// written when the statement issues, so no result may be left unused (its
+// register could be handed out again while the read is in flight): every one
+// is a fragment that the MFMAs after that wait consume.
 typedef __attribute__((address_space(3))) char lds_char_t;
 __device__ __forceinline__ i16x4_t ds_read_tr(const char* p) {
   i16x4_t v;

@@ -123,6 +123,26 @@ def test_small_full(case):
     say("  err/tol:", {k: round(v, 3) for k, v in r.items()})
 
 
+def _random_cases(n, seed):
+    """Seeded shapes off every tile and chunk boundary: M, H, F_i multiples of 8 up
+    to ~700 (some below 64, the epilogue chunk), t of 1-3, P kept or recomputed."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        M, H, F = (int(8 * rng.integers(1, 88)) for _ in range(3))
+        out.append((M, H, F, int(rng.integers(1, 4)), bool(rng.integers(0, 2))))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_cases(24, 2026),
+                         ids=lambda c: "x".join(map(str, c[:4])) + ("_store" if c[4] else "_recompute"))
+def test_random_shapes(case):
+    """The t-shard forward and backward on random ragged shapes, every output
+    element against the oracle (the planner's choices of tile, split, fused or
+    batched launch vary with the shape)."""
+    test_small_full(case)
+
+
 def test_config0_forward():
     w = I.CONFIGS[0]
     say(f"[parity config0] {w}")
