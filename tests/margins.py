@@ -1,6 +1,7 @@
 """Err/tol margins of the GPU parity checks, collected so that a quiet (-q) test
 run still prints them: tests/conftest.py writes one line per test at the end of
-the session (and a JSON file under gpurun_out/ when that folder exists).
+the session, and the same records as JSON into the run's output folder when one
+exists.
 
 A margin is max|gpu - oracle| / (1e-2 max|oracle| + 1e-3) for one output; it
 must be at most 1.  Rounding the bf16 intermediates alone costs 0.12-0.24 of it
