@@ -134,6 +134,25 @@ def test_fp8_path_matches_oracle(case):
         f"ambiguous codes G {bd.ambiguous_g} dP {bd.ambiguous_dp}")
 
 
+def _random_fp8_cases(n, seed):
+    """Seeded FP8 shapes: M, H, F_i multiples of 16 up to ~700 (some below one
+    epilogue chunk), t of 1-3, P kept or recomputed."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        M, H, F_ = (int(16 * rng.integers(1, 44)) for _ in range(3))
+        out.append((M, H, F_, int(rng.integers(1, 4)), bool(rng.integers(0, 2))))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_fp8_cases(12, 2027),
+                         ids=lambda c: "x".join(map(str, c[:4])) + ("_store" if c[4] else "_recompute"))
+def test_fp8_random_shapes(case):
+    """The FP8 forward and backward on random ragged shapes against the oracle's
+    FP8 path, element by element within the acceptance bound."""
+    test_fp8_path_matches_oracle(case)
+
+
 def test_fp8_backward_needs_its_forward():
     """The backward reuses what the forward left in the workspace, and refuses a
     workspace that holds no forward of its inputs (before any launch); a
