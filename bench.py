@@ -81,11 +81,13 @@ def gemm_flops(w):
 
 def batch_factor(w, kind, launches, steps):
     """Shards one launch of a product kind covers: the t-shard driver may run
-    several shards' F1, recompute, dGeLU, dB or dA as one batched launch, so a
-    kind launched fewer times per step than there are shards covers several."""
+    several shards' F1, recompute, dGeLU, dB or dA as one batched launch, and two
+    shards' F3 or dX as one paired launch, so a kind launched fewer times per step
+    than there are shards covers several."""
     shards = len(w.shards_timed)
     per_step = launches / steps if steps else 0
-    if kind not in ("fwd_gemm1_gelu", "bwd_recompute", "bwd_dgelu", "bwd_dB", "bwd_dA") or per_step <= 0:
+    if kind not in ("fwd_gemm1_gelu", "bwd_recompute", "bwd_dgelu", "bwd_dB", "bwd_dA", "fwd_gemm2",
+                    "bwd_dX") or per_step <= 0:
         return 1.0
     return max(1.0, shards / per_step)
 

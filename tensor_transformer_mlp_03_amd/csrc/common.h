@@ -49,6 +49,12 @@ enum Epi : int {
                     //   out2_bf16[n,m] = GeLU(p)
   EPI_F32_ACC = 4,  // out_f32[m,n] = out_f32[m,n] + acc: adds the product to a running
                     //   float32 sum (no split-K slices; the reduction applies it instead)
+  // Two products of one shape in one launch (no split-K, 256 x 128 or 128 x 128
+  // tiles): product p takes A from a_arr[p] and B from b_arr[p], a workgroup runs
+  // both K loops for its tile into two accumulator sets, and the epilogue adds
+  // them in order, as two launches of EPI_F32 / EPI_F32_ACC would:
+  EPI_F32_PAIR = 5,      // out_f32[m,n] = acc0 + acc1
+  EPI_F32_ACC_PAIR = 6,  // out_f32[m,n] = (out_f32[m,n] + acc0) + acc1
 };
 
 // Largest output row stride of an EPI_F32_ACC product (its loads of the running

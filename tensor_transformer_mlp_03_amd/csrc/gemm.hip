@@ -227,9 +227,15 @@ constexpr int G_ROW_B = 128;  // staged G row pitch in bytes
 // FP8 (FP8 products): EPI_BF16 and EPI_DGELU also collect the amax of what they
 // write into args.amax_out when set (of the GeLU of the written values with
 // args.amax_gelu), and EPI_DGELU writes dP only (no G^T).
-template <int EPI, int NC, bool FP8, class StageChunk, class ScaleFn>
+// Paired products (EPI_F32_PAIR, EPI_F32_ACC_PAIR): stage_chunk2(c) writes product
+// 1's values of chunk c the same way into `stage2`, and each output element is
+// (running sum + product 0) + product 1, in that order.
+template <int EPI, int NC, bool FP8, class StageChunk, class ScaleFn, class StageChunk2>
 __device__ __forceinline__ void store_staged(StageChunk&& stage_chunk, ScaleFn&& scale_fn, const GemmArgs& args,
-                                             char* stage, int row_w, int col_w, int nh, int split, int lane) {
+                                             char* stage, int row_w, int col_w, int nh, int split, int lane,
+                                             StageChunk2&& stage_chunk2, char* stage2) {
+  constexpr bool PAIR = EPI == EPI_F32_PAIR || EPI == EPI_F32_ACC_PAIR;
+  constexpr bool ACC = EPI == EPI_F32_ACC || EPI == EPI_F32_ACC_PAIR;
   // FP8: running extremes of the written values (AmaxTrack, epilogue.h; invalid
   // elements enter as 0), updated without branches.
   AmaxTrack am;
@@ -270,7 +276,9 @@ __device__ __forceinline__ void store_staged(StageChunk&& stage_chunk, ScaleFn&&
   // keeps the compiler from sinking them to their uses (one round trip each)
   // when registers run short.
   if (EPI == EPI_DGELU) load_pre(0);
-  if (EPI == EPI_F32_ACC) load_old(0);
+  // (Paired launches hold two staged products: their running-sum loads are not
+  // double-buffered, which leaves the registers that holds.)
+  if (ACC && !PAIR) load_old(0);
   __builtin_amdgcn_sched_barrier(0);
   // FP8: the product of the operands' scales, which stage_chunk applies (taken
   // after the first loads are issued, so that the scales' load overlaps them).
@@ -279,16 +287,21 @@ __device__ __forceinline__ void store_staged(StageChunk&& stage_chunk, ScaleFn&&
   for (int ch = 0; ch < NC; ++ch) {
     const int h = ch % nh;  // used by the stores below through row_w + 64 * h
     const int col_c = col0(ch);
-    if (EPI == EPI_F32_ACC && ch + 1 < NC) {
+    if (ACC && PAIR) {
+      load_old(ch);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (ACC && !PAIR && ch + 1 < NC) {
       load_old(ch + 1);
       __builtin_amdgcn_sched_barrier(0);
     }
     stage_chunk(ch, sc);
+    if (PAIR) stage_chunk2(ch);
     if (EPI == EPI_DGELU && ch + 1 < NC) {
       load_pre(ch + 1);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (EPI == EPI_F32 || EPI == EPI_F32_ACC) {
+    if (EPI == EPI_F32 || ACC || PAIR) {
       const __amdgpu_buffer_rsrc_t rs = make_rsrc(reinterpret_cast<float*>(args.out) +
                                                   (int64_t)split * args.split_stride +
                                                   (int64_t)(row_w + 64 * h) * args.ldo + col_c);
@@ -296,18 +309,20 @@ __device__ __forceinline__ void store_staged(StageChunk&& stage_chunk, ScaleFn&&
       // not fit beside the accumulators.
 #pragma unroll
       for (int b8 = 0; b8 < 16; b8 += 8) {
-        f32x4_t xs[8];
+        f32x4_t xs[8], ys[PAIR ? 8 : 1];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
           const int q = (b8 + u) * 64 + lane, r = q >> 4, c = q & 15;
           xs[u] = *reinterpret_cast<const f32x4_t*>(stage + r * ROW_B + ((c ^ (r & 15)) << 4));
+          if constexpr (PAIR) ys[u] = *reinterpret_cast<const f32x4_t*>(stage2 + r * ROW_B + ((c ^ (r & 15)) << 4));
         }
         __builtin_amdgcn_sched_barrier(0);  // the reads stay one batch
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
           const int it = b8 + u, q = it * 64 + lane, r = q >> 4, c = q & 15;
           const bool ok = row_w + 64 * h + r < args.M && col_c + 4 * c < args.N;
-          if (EPI == EPI_F32_ACC) xs[u] += old[ch & 1][it];
+          if (ACC) xs[u] += old[ch & 1][it];
+          if constexpr (PAIR) xs[u] += ys[u];
           const uint32_t off = (uint32_t)(((int64_t)r * args.ldo + 4 * c) * 4);
           __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, xs[u]), rs, ok ? off : OOB, 0, 0);
         }
@@ -447,6 +462,11 @@ gemm_x16_kernel(GemmArgs args_in) {
 #if defined(__HIP_DEVICE_COMPILE__)
   static_assert((BM == 256 && (BN == 256 || BN == 128)) || (BM == 128 && BN == 128), "tile shapes");
   static_assert(F8 == 0 || LB == KC, "FP8 operands are K-contiguous");
+  // Paired products (EPI_F32_PAIR, EPI_F32_ACC_PAIR): two accumulator sets, which
+  // only the 256 x 128 and 128 x 128 tiles have registers for.
+  constexpr bool PAIR = EPI == EPI_F32_PAIR || EPI == EPI_F32_ACC_PAIR;
+  static_assert(!PAIR || (F8 == 0 && BN == 128), "paired products: bf16, 256 x 128 or 128 x 128 tiles");
+  static_assert(8 * 64 * ROW_B <= 160 * 1024, "two staging regions per wave fit the LDS");
   constexpr int BK = TILE_BK;
   constexpr int SLOT = 128 * BK * 2;
   constexpr int NA = BM / 128;              // A quarters (128 rows x BK) per K step
@@ -483,10 +503,16 @@ gemm_x16_kernel(GemmArgs args_in) {
     args.out2 = args_in.out2_arr[j];
     args.aux = args_in.aux_arr[j];
   }
+  if (PAIR) {  // product 0's operands; product 1's are a_arr[1] and b_arr[1]
+    args.a = args_in.a_arr[0];
+    args.b = args_in.b_arr[0];
+  }
   const int m0 = tm * BM, n0 = tn * BN;
   const int k_begin = split * args.k_split;
   const int k_end = min(args.K, k_begin + args.k_split);
   const int nk = (k_end - k_begin + BK - 1) / BK;
+  // K steps of the whole loop: product 1 (paired launches) follows product 0's nk.
+  const int nk_all = PAIR ? 2 * nk : nk;
 
   QuarterKC qa[NA], qb[BN / 128];
   QuarterMC qm[BN / 128];
@@ -500,24 +526,30 @@ gemm_x16_kernel(GemmArgs args_in) {
 
   auto slot = [&](int r, int q) -> char* { return smem + ((SPS * r + q) % NSLOT) * SLOT; };
   // Instruction i of this wave's share of quarter q of K step `step` (r = step % P).
+  // Paired launches: steps nk .. 2 nk - 1 are product 1's steps 0 .. nk - 1.
   auto load = [&](int step, int r, int q, int i) {
     if (q >= NQ) return;
-    const int k = k_begin + step * BK;
+    const bool second = PAIR && step >= nk;
+    const int k = k_begin + (second ? step - nk : step) * BK;
+    const uint16_t* pa = second ? args_in.a_arr[1] : args.a;
+    const uint16_t* pb = second ? args_in.b_arr[1] : args.b;
     char* dst = slot(r, q);
     if (q < NA) {
-      qa[q].issue(make_rsrc(args.a + (int64_t)(m0 + 128 * q) * args.lda + k), dst, k_end - k, wave, i);
+      qa[q].issue(make_rsrc(pa + (int64_t)(m0 + 128 * q) * args.lda + k), dst, k_end - k, wave, i);
     } else if (LB == KC) {
-      qb[q - NA].issue(make_rsrc(args.b + (int64_t)(n0 + 128 * (q - NA)) * args.ldb + k), dst, k_end - k, wave, i);
+      qb[q - NA].issue(make_rsrc(pb + (int64_t)(n0 + 128 * (q - NA)) * args.ldb + k), dst, k_end - k, wave, i);
     } else {
-      qm[q - NA].issue(make_rsrc(args.b + (int64_t)k * args.ldb + n0 + 128 * (q - NA)), dst, k_end - k, wave, i);
+      qm[q - NA].issue(make_rsrc(pb + (int64_t)k * args.ldb + n0 + 128 * (q - NA)), dst, k_end - k, wave, i);
     }
   };
 
   f32x4_t acc[FI][FJ];
+  f32x4_t acc2[PAIR ? FI : 1][PAIR ? FJ : 1];  // product 1's (paired launches)
 #pragma unroll
   for (int i = 0; i < FI; ++i)
 #pragma unroll
     for (int j = 0; j < FJ; ++j) acc[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  // (acc2 is cleared where product 1 starts, so that it holds no registers before.)
 
   if constexpr (F8 == 0) {
   bf16x8_t fa[FI], fb[2][FJ];
@@ -564,7 +596,7 @@ gemm_x16_kernel(GemmArgs args_in) {
   // last MFMA).  Load n of the sub-step's NL goes after MFMA 1 (and FJ/2 + 1 for a
   // second) of row n * FI / NL.  Every MFMA with the reads and loads placed after it
   // is its own scheduling region, so the order is exactly this one.
-  auto sub_step = [&](int cur, bool reads, int rn, int kn, auto nl, auto&& issue_load) {
+  auto sub_step = [&](auto& C, int cur, bool reads, int rn, int kn, auto nl, auto&& issue_load) {
     constexpr int NL = decltype(nl)::value;
 #pragma unroll
     for (int i = 0; i < FI; ++i) {
@@ -577,7 +609,7 @@ gemm_x16_kernel(GemmArgs args_in) {
         }
 #pragma unroll
       for (int j = 0; j < FJ; ++j) {
-        mfma16(acc[i][j], fb[cur][j], fa[i]);
+        mfma16(C[i][j], fb[cur][j], fa[i]);
         if (reads && i == 0) {
 #pragma unroll
           for (int u = 0; u < NB / FJ; ++u) {
@@ -604,19 +636,19 @@ gemm_x16_kernel(GemmArgs args_in) {
   constexpr int STEP_LOADS = HALF_LOADS + TAIL_LOADS;
   static_assert((D - 1) * STEP_LOADS < 64, "vmcnt");
 
-  if (nk > 0) {
+  if (nk_all > 0) {
     // Prologue: steps 0 .. D-1 (as many as there are); wait for step 0.
 #pragma unroll
     for (int st = 0; st < D; ++st)
-      if (st < nk) {
+      if (st < nk_all) {
 #pragma unroll
         for (int q = 0; q < NQ; ++q)
 #pragma unroll
           for (int i = 0; i < 4; ++i) load(st, st, q, i);
       }
-    if (D >= 4 && nk >= 4) vm_wait(std::integral_constant<int, (D >= 4 ? 3 : 0) * STEP_LOADS>{});
-    else if (D >= 3 && nk >= 3) vm_wait(std::integral_constant<int, (D >= 3 ? 2 : 0) * STEP_LOADS>{});
-    else if (nk >= 2) vm_wait(std::integral_constant<int, STEP_LOADS>{});
+    if (D >= 4 && nk_all >= 4) vm_wait(std::integral_constant<int, (D >= 4 ? 3 : 0) * STEP_LOADS>{});
+    else if (D >= 3 && nk_all >= 3) vm_wait(std::integral_constant<int, (D >= 3 ? 2 : 0) * STEP_LOADS>{});
+    else if (nk_all >= 2) vm_wait(std::integral_constant<int, STEP_LOADS>{});
     else vm_wait(L0{});
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
@@ -625,13 +657,14 @@ gemm_x16_kernel(GemmArgs args_in) {
 #pragma unroll
     for (int f = 0; f < FI; ++f) read_a(0, 0, f);
 
-    // K step k with LEFT = min(D, steps after it) known at compile time; r = k % P.
-    auto k_step = [&](int k, auto left, int r) {
+    // K step k with LEFT = min(D, steps after it) known at compile time; r = k % P;
+    // C the accumulator set of the step's product.
+    auto k_step = [&](int k, auto left, int r, auto& C) {
       constexpr int LEFT = decltype(left)::value;
       const int r1 = r == P - 1 ? 0 : r + 1, rd = (r + D) % P;
       // sub-step 0: reads sub-step 1 of this step; loads the quarters of step k+D
       // whose slots step k does not use
-      sub_step(0, true, r, 1, std::integral_constant<int, LEFT >= D ? HALF_LOADS : 0>{},
+      sub_step(C, 0, true, r, 1, std::integral_constant<int, LEFT >= D ? HALF_LOADS : 0>{},
                [&](int n) { load(k + D, rd, n >> 2, n & 3); });
       if constexpr (LEFT >= 1) {
         // Step k+1 has landed once at most the loads issued after its own are
@@ -645,27 +678,57 @@ gemm_x16_kernel(GemmArgs args_in) {
       }
       // sub-step 1: reads sub-step 0 of step k+1; loads the rest of step k+D (for
       // 256-row tiles into step k's first slots)
-      sub_step(1, LEFT >= 1, r1, 0, std::integral_constant<int, LEFT >= D ? TAIL_LOADS : 0>{},
+      sub_step(C, 1, LEFT >= 1, r1, 0, std::integral_constant<int, LEFT >= D ? TAIL_LOADS : 0>{},
                [&](int n) { load(k + D, rd, QS0 + (n >> 2), n & 3); });
     };
     using Full = std::integral_constant<int, D>;
     int k = 0;
-    for (; k + P + D <= nk; k += P) {  // steps k .. k+P-1, each with D more after it
+    if constexpr (PAIR) {
+      // Product 0: steps 0 .. nk - 1 into acc, each with D or more steps after it
+      // (the host pairs products of at least D K steps).
+      for (; k + P <= nk; k += P) {
 #pragma unroll
-      for (int u = 0; u < P; ++u) k_step(k + u, Full{}, u);
-    }
-    for (; k + D < nk; ++k) k_step(k, Full{}, k % P);
-    // The last D steps (or all of them, if fewer), each with its own LEFT.
-    auto tail = [&](auto jc) {
-      constexpr int J = decltype(jc)::value;
-      if constexpr (J < D) {
-        if (nk >= J + 1) k_step(nk - 1 - J, std::integral_constant<int, J>{}, (nk - 1 - J) % P);
+        for (int u = 0; u < P; ++u) k_step(k + u, Full{}, u, acc);
       }
+      for (; k < nk; ++k) k_step(k, Full{}, k % P, acc);
+#pragma unroll
+      for (int i = 0; i < FI; ++i)
+#pragma unroll
+        for (int j = 0; j < FJ; ++j) acc2[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    // The rest (product 1's steps into acc2 for paired launches), the last D
+    // steps (or all of them, if fewer) each with its own LEFT.
+    auto rest = [&](auto& C) {
+      if constexpr (PAIR) {
+        // Whole ring periods with the ring position known at compile time (both
+        // accumulator sets are live here, and run-time positions cost registers);
+        // the steps before nk and from the tail on are skipped.
+        const int stop = nk_all - D;
+        for (int k0 = nk - nk % P; k0 < stop; k0 += P) {
+#pragma unroll
+          for (int u = 0; u < P; ++u)
+            if (k0 + u >= nk && k0 + u < stop) k_step(k0 + u, Full{}, u, C);
+        }
+      } else {
+        for (; k + P + D <= nk_all; k += P) {  // steps k .. k+P-1, each with D more after it
+#pragma unroll
+          for (int u = 0; u < P; ++u) k_step(k + u, Full{}, u, C);
+        }
+        for (; k + D < nk_all; ++k) k_step(k, Full{}, k % P, C);
+      }
+      auto tail = [&](auto jc) {
+        constexpr int J = decltype(jc)::value;
+        if constexpr (J < D) {
+          if (nk_all >= J + 1) k_step(nk_all - 1 - J, std::integral_constant<int, J>{}, (nk_all - 1 - J) % P, C);
+        }
+      };
+      tail(std::integral_constant<int, 3>{});
+      tail(std::integral_constant<int, 2>{});
+      tail(std::integral_constant<int, 1>{});
+      tail(std::integral_constant<int, 0>{});
     };
-    tail(std::integral_constant<int, 3>{});
-    tail(std::integral_constant<int, 2>{});
-    tail(std::integral_constant<int, 1>{});
-    tail(std::integral_constant<int, 0>{});
+    if constexpr (PAIR) rest(acc2);
+    else rest(acc);
     vm_wait(L0{});
   }
   } else {
@@ -844,7 +907,22 @@ gemm_x16_kernel(GemmArgs args_in) {
             *reinterpret_cast<f32x4_t*>(smem + wave * (64 * ROW_B) + r * ROW_B + ((c ^ (r & 15)) << 4)) = v;
           }
       },
-      scales, args, smem + wave * (64 * ROW_B), m0 + (BM / 2) * wm, n0 + (BN / 2) * wn, FI / 4, split, lane);
+      scales, args, smem + wave * (64 * ROW_B), m0 + (BM / 2) * wm, n0 + (BN / 2) * wn, FI / 4, split, lane,
+      // paired launches: product 1's chunk in the LDS above the four waves' first regions
+      [&](int ch) {
+        if constexpr (PAIR) {
+          const int h = ch % (FI / 4), hc = ch / (FI / 4);
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+              const int r = 16 * ii + (lane & 15), c = 4 * jj + (lane >> 4);
+              *reinterpret_cast<f32x4_t*>(smem + (4 + wave) * (64 * ROW_B) + r * ROW_B + ((c ^ (r & 15)) << 4)) =
+                  acc2[4 * h + ii][4 * hc + jj];
+            }
+        }
+      },
+      smem + (4 + wave) * (64 * ROW_B));
 #else
   (void)args_in;
 #endif
@@ -889,6 +967,16 @@ hipError_t dispatch_fp8(int fa, int fb, Epi epi, const GemmArgs& a, int splits, 
 template <int BM, int BN>
 hipError_t dispatch_layout(Layout la, Layout lb, Epi epi, const GemmArgs& a, int splits, hipStream_t s) {
   if (la != KC) return hipErrorInvalidValue;
+  if constexpr (BN == 128) {  // paired products: no split-K, no batch
+    if (epi == EPI_F32_PAIR || epi == EPI_F32_ACC_PAIR) {
+      if (splits != 1 || a.batch > 1) return hipErrorInvalidValue;
+      if (lb == MC)
+        return epi == EPI_F32_PAIR ? launch_one<BM, BN, MC, EPI_F32_PAIR>(a, 1, s)
+                                   : launch_one<BM, BN, MC, EPI_F32_ACC_PAIR>(a, 1, s);
+      return epi == EPI_F32_PAIR ? launch_one<BM, BN, KC, EPI_F32_PAIR>(a, 1, s)
+                                 : launch_one<BM, BN, KC, EPI_F32_ACC_PAIR>(a, 1, s);
+    }
+  }
   if (lb == MC) {
     switch (epi) {
       case EPI_GELU: return launch_one<BM, BN, MC, EPI_GELU>(a, splits, s);

@@ -510,6 +510,30 @@ hipError_t run_gemm_batch(int kind, Layout lb, Epi epi, const void* const* a, in
   return timed(kind, s, [&] { return launch_gemm(p.tile, KC, lb, epi, ga, 1, s); });
 }
 
+// Whether two products of this plan and K can share a paired launch: unsplit
+// whole tiles, a tile with registers for two accumulator sets (256 x 128 or
+// 128 x 128), and at least the prefetch distance in K steps in each product.
+bool pair_ok(const GemmPlan& p, int64_t K) {
+  return p.splits == 1 && p.n_full == 0 && p.tile != TILE_256x256 &&
+         K >= (p.tile == TILE_128x128 ? 4 : 2) * TILE_BK;
+}
+
+// Two products of one shape added into the float32 [M][N] `out` in one launch:
+// out = (out + a0 b0) + a1 b1 with acc, else a0 b0 + a1 b1, rounded as two
+// launches of EPI_F32_ACC (or EPI_F32) and EPI_F32_ACC in that order would.
+hipError_t run_gemm_pair(int kind, Layout lb, bool acc, const void* a0, const void* a1, int64_t lda, const void* b0,
+                         const void* b1, int64_t ldb, int64_t M, int64_t N, int64_t K, const GemmPlan& p, float* out,
+                         hipStream_t s) {
+  if (!pair_ok(p, K)) return hipErrorInvalidValue;
+  GemmArgs ga = gemm_args(a0, lda, b0, ldb, M, N, K, p, out, N);
+  ga.a_arr[0] = static_cast<const uint16_t*>(a0);
+  ga.a_arr[1] = static_cast<const uint16_t*>(a1);
+  ga.b_arr[0] = static_cast<const uint16_t*>(b0);
+  ga.b_arr[1] = static_cast<const uint16_t*>(b1);
+  return timed(kind, s,
+               [&] { return launch_gemm(p.tile, KC, lb, acc ? EPI_F32_ACC_PAIR : EPI_F32_PAIR, ga, 1, s); });
+}
+
 char* ws_at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
 
 // Enqueue rank i's forward (arguments already checked).
@@ -603,7 +627,7 @@ hipError_t enqueue_transposes(const tpmlp_bf16* dZ, const tpmlp_bf16* X, int64_t
 hipError_t enqueue_bwd_weights_dx(const BwdPlan& p, const uint16_t* dP, const uint16_t* Gt, const uint16_t* Xt,
                                   const uint16_t* dZt, const tpmlp_bf16* A, int64_t lda, float* dX, float* dA,
                                   int64_t ldda, float* dB, int64_t M, int64_t H, int64_t F, void* ws, hipStream_t s,
-                                  bool acc, bool do_db = true, bool do_da = true);
+                                  bool acc, bool do_db = true, bool do_da = true, bool do_dx = true);
 
 // Enqueue rank i's backward (arguments already checked; X^T and dZ^T already
 // in the workspace).
@@ -649,7 +673,7 @@ hipError_t enqueue_bwd(const tpmlp_bf16* dZ, const tpmlp_bf16* X, const tpmlp_bf
 hipError_t enqueue_bwd_weights_dx(const BwdPlan& p, const uint16_t* dP, const uint16_t* Gt, const uint16_t* Xt,
                                   const uint16_t* dZt, const tpmlp_bf16* A, int64_t lda, float* dX, float* dA,
                                   int64_t ldda, float* dB, int64_t M, int64_t H, int64_t F, void* ws, hipStream_t s,
-                                  bool acc, bool do_db, bool do_da) {
+                                  bool acc, bool do_db, bool do_da, bool do_dx) {
   float* part = reinterpret_cast<float*>(ws_at(ws, p.off_part));
   hipError_t e = hipSuccess;
   // dB_i = G_i^T dZ    G_i^T: [F][M] = [M'][K], dZ^T: [H][M] = [N'][K] (both K-contig)
@@ -669,7 +693,7 @@ hipError_t enqueue_bwd_weights_dx(const BwdPlan& p, const uint16_t* dP, const ui
     e = run_gemm(TPMLP_K_BWD_DA, KC, MC, EPI_F32, Xt, M, dP, F, H, F, M, p.gda, dA, nullptr, nullptr, part, s,
                  ldda);
   }
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || !do_dx) return e;
   // dX_i = dP_i A_i^T  dP_i: [M][F] (K-contig), A_i: [H][F] = [N][K] (K-contig)
   return run_gemm(TPMLP_K_BWD_DX, KC, KC, acc ? EPI_F32_ACC : EPI_F32, dP, F, A, lda, M, H, F, p.gdx, dX,
                   nullptr, nullptr, part, s);
@@ -1329,11 +1353,21 @@ tpmlp_status tpmlp_tp_fwd(const tpmlp_bf16* X, const tpmlp_bf16* const* A_sh, co
       // P_i = X A_i; G_i = GeLU(P_i)      X: [M][H] (K-contig), A_i: [H][F] (N-contig)
       hipError_t e = run_gemm_batch(TPMLP_K_FWD_GEMM1_GELU, MC, EPI_GELU, a, H, b, F_i, M, F_i, H, bp.plan, g, G, P,
                                     nullptr, s);
-      for (int j = 0; j < g && e == hipSuccess; ++j) {
+      // Z_i = G_i B_i                    G_i: [M][F] (K-contig), B_i: [F][H] (N-contig)
+      // Folded into one Z, two consecutive shards' products share a launch when
+      // their plan allows it (rank order kept: Z + Z_i, then + Z_{i+1}).
+      const bool pairs = fold && pair_ok(fp.g2, F_i);
+      for (int j = 0; j < g && e == hipSuccess;) {
         const int i = i0 + j;
-        // Z_i = G_i B_i                    G_i: [M][F] (K-contig), B_i: [F][H] (N-contig)
-        e = run_gemm(TPMLP_K_FWD_GEMM2, KC, MC, fold && i > 0 ? EPI_F32_ACC : EPI_F32, G[j], F_i, B_sh[i], H, M, H,
-                     F_i, fp.g2, Zs[i], nullptr, nullptr, part, s);
+        if (pairs && j + 1 < g) {
+          e = run_gemm_pair(TPMLP_K_FWD_GEMM2, MC, i > 0, G[j], G[j + 1], F_i, B_sh[i], B_sh[i + 1], H, M, H, F_i,
+                            fp.g2, Z, s);
+          j += 2;
+        } else {
+          e = run_gemm(TPMLP_K_FWD_GEMM2, KC, MC, fold && i > 0 ? EPI_F32_ACC : EPI_F32, G[j], F_i, B_sh[i], H, M,
+                       H, F_i, fp.g2, Zs[i], nullptr, nullptr, part, s);
+          j += 1;
+        }
       }
       if (e != hipSuccess) return hip_fail(e, "tpmlp_tp_fwd launch");
     }
@@ -1460,10 +1494,21 @@ tpmlp_status tpmlp_tp_bwd(const tpmlp_bf16* dZ, const tpmlp_bf16* X, const tpmlp
         e = run_gemm_batch(TPMLP_K_BWD_DA, MC, EPI_F32, xt + j0, M, const_cast<const void* const*>(dPs + j0), F_i,
                            H, F_i, M, bda.plan, ga, reinterpret_cast<void* const*>(dAs + j0), nullptr, nullptr, s);
       }
-      for (int j = 0; j < g && e == hipSuccess; ++j) {
+      // Folded into one dX, two consecutive shards' dX products share a launch when
+      // their plan allows it (rank order kept), after both shards' dB and dA.
+      const bool pairs = fold && pair_ok(p.gdx, F_i);
+      for (int j = 0; j < g && e == hipSuccess;) {
         const int i = i0 + j;
-        e = enqueue_bwd_weights_dx(p, static_cast<const uint16_t*>(dPs[j]), Gts[j], Xt, dZt, A_sh[i], F_i, dXs[i],
-                                   dA_sh[i], F_i, dB_sh[i], M, H, F_i, ws, s, fold && i > 0, bdb.g == 1, !batch_da);
+        const bool pair = pairs && j + 1 < g;
+        for (int u = 0; u < (pair ? 2 : 1) && e == hipSuccess; ++u)
+          e = enqueue_bwd_weights_dx(p, static_cast<const uint16_t*>(dPs[j + u]), Gts[j + u], Xt, dZt, A_sh[i + u],
+                                     F_i, dXs[i + u], dA_sh[i + u], F_i, dB_sh[i + u], M, H, F_i, ws, s,
+                                     fold && i + u > 0, bdb.g == 1, !batch_da, !pair);
+        // dX_i = dP_i A_i^T  dP_i: [M][F] (K-contig), A_i: [H][F] = [N][K] (K-contig)
+        if (pair && e == hipSuccess)
+          e = run_gemm_pair(TPMLP_K_BWD_DX, KC, i > 0, dPs[j], dPs[j + 1], F_i, A_sh[i], A_sh[i + 1], F_i, M, H, F_i,
+                            p.gdx, dX, s);
+        j += pair ? 2 : 1;
       }
       if (e != hipSuccess) return hip_fail(e, "tpmlp_tp_bwd launch");
     }

@@ -492,6 +492,35 @@ def test_folded_sum_equals_separate_sum_bitwise(case):
     assert (a.Z.double() - Z).abs().max() <= t * 2.0 ** -23 * Z.abs().max()
 
 
+@pytest.mark.parametrize("case", [(2048, 4096, 2048, 4, True), (2048, 4096, 2048, 3, False),
+                                  (2048, 1024, 1024, 8, True)],
+                         ids=lambda c: "x".join(map(str, c[:4])) + ("_store" if c[4] else "_recompute"))
+def test_paired_products_equal_separate_sum_bitwise(case):
+    """7B-class shard shapes: after a batched F1 (and dGeLU), two consecutive
+    shards' F3 (and dX) run as one launch with two accumulator sets, adding into Z
+    (dX) in rank order; the bits are those of the separate rank-order sum of the
+    per-shard partials, and an odd shard count leaves one product unpaired."""
+    from tensor_transformer_mlp_03_amd import _lib as L
+    from tensor_transformer_mlp_03_amd.device import DeviceMLP
+    M, H, F, t, store = case
+    say(f"[paired products] M={M} H={H} F_i={F} t={t} store_p={store}")
+    w = I.custom_workload(340 + t, M=M, H=H, F_i=F, t=t, w_std=0.05)
+    inp = I.make_inputs(w)
+    a = DeviceMLP(inp, store_p=store, driver=True, keep_partials=True)   # partials + separate sum
+    b = DeviceMLP(inp, store_p=store, driver=True, keep_partials=False)  # folded, paired
+    a.step()
+    L.tpmlp_timing_begin(256)
+    b.step()
+    stats, dropped = L.tpmlp_timing_end()
+    torch.cuda.synchronize()
+    assert dropped == 0
+    assert stats["fwd_gemm1_gelu"][0] < t, "the shapes batch F1"
+    assert stats["fwd_gemm2"][0] == (t + 1) // 2 and stats["bwd_dX"][0] == (t + 1) // 2, stats
+    assert torch.equal(a.Z, b.Z) and torch.equal(a.dX, b.dX)
+    for i in range(t):
+        assert torch.equal(a.dA[i], b.dA[i]) and torch.equal(a.dB[i], b.dB[i]), f"shard {i}"
+
+
 @pytest.mark.parametrize("shape", [(200, 192, 392, 2), (1000, 520, 776, 2)], ids=["fused_forward", "two_products"])
 def test_graph_replay_matches_eager(shape):
     """A step captured into a HIP graph gives, on every replay, the bits of the eager
@@ -758,11 +787,14 @@ def test_timing_counts_launches():
     d.step()
     stats, dropped = L.tpmlp_timing_end()
     assert dropped == 0
-    # F1 and dGeLU of the two shards: one launch each, or one batched launch for both
+    # F1 and dGeLU of the two shards: one launch each, or one batched launch for both;
+    # F3 and dX: one launch each, or (after a batched F1 or dGeLU) one paired launch
     n1 = stats["fwd_gemm1_gelu"][0]
-    assert n1 in (1, 2) and stats["bwd_dgelu"][0] == n1 and stats["fwd_gemm2"][0] == 2
+    assert n1 in (1, 2) and stats["bwd_dgelu"][0] == n1
+    n3 = stats["fwd_gemm2"][0]
+    assert n3 in ((1, 2) if n1 == 1 else (2,))
     # no per-shard partials asked for: the sums are folded into the products' epilogues
-    assert stats["bwd_dX"][0] == 2 and stats["shard_sum"][0] == 0
+    assert stats["bwd_dX"][0] == n3 and stats["shard_sum"][0] == 0
     assert stats["bwd_recompute"][0] == 0
     assert stats["transpose"][0] == 2  # X^T and dZ^T once for both shards
     assert all(ms >= 0 for _, ms in stats.values())
@@ -773,9 +805,9 @@ def test_timing_counts_launches():
     d.step()
     stats, dropped = L.tpmlp_timing_end()
     assert dropped == 0
-    assert {k: n for k, (n, _) in stats.items() if n} == {"fwd_gemm2": 2}
-    assert [k for k, _ in L.tpmlp_timing_records()] == ["fwd_gemm2"] * 2
-    assert L.tpmlp_timing_dispatches() == [1, 1]
+    assert {k: n for k, (n, _) in stats.items() if n} == {"fwd_gemm2": n3}
+    assert [k for k, _ in L.tpmlp_timing_records()] == ["fwd_gemm2"] * n3
+    assert L.tpmlp_timing_dispatches() == [1] * n3
 
 
 @pytest.mark.parametrize("case", [(512, 1024, 512, 4, True), (640, 1032, 520, 3, False)],
