@@ -113,6 +113,19 @@ def gemm_alg_bytes(w, recompute, fold=False):
     }
 
 
+def launch_alg_bytes(w, kind, factor, shards):
+    """Algorithmic bytes of one launch of `kind` covering `factor` shards: batched
+    launches move each shard's operands and outputs; a paired F3 or dX launch
+    reads its two shards' operands but writes the output, and reads the running
+    sum (all pairs but the first), once."""
+    base = gemm_alg_bytes(w, w.recompute, fold=folds(w))
+    if kind not in ("fwd_gemm2", "bwd_dX") or factor <= 1:
+        return base[kind] * factor
+    M, H, F = w.M, w.H, w.F_i
+    per_step = shards / factor
+    return factor * 2 * (M * F + F * H) + 4 * M * H + 4 * M * H * (per_step - 1) / per_step
+
+
 def fp8_alg_bytes(w, fold=False):
     """Algorithmic HBM bytes of one launch of each product kind of the FP8 path:
     FP8 codes 1 byte, bf16 2, float32 4; operands read once, outputs written once
@@ -502,7 +515,7 @@ def measure(w, args, L, I, DeviceMLP, torch):
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": None, "avg_launch_us": round(avg_s * 1e6, 2),
-                "alg_bytes": gemm_alg_bytes(w, w.recompute, fold=folds(w))[dom] * factor}
+                "alg_bytes": launch_alg_bytes(w, dom, factor, len(shards))}
     if factor != 1.0:
         roofline["shards_per_launch"] = round(factor, 2)
     if traffic and dom in traffic:
