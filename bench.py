@@ -324,7 +324,8 @@ def summarize(d, config, fp8=False):
     alg["shard_sum"] = (w.t + 1) * w.M * w.H * 4  # t float32 partials in, their sum out
     for kind, a in agg.items():  # a batched launch covers several shards (the counter passes run one step)
         if kind in alg:
-            alg[kind] *= batch_factor(w, kind, a["n"], 1)
+            f = batch_factor(w, kind, a["n"], 1)
+            alg[kind] = alg[kind] * f if fp8 else launch_alg_bytes(w, kind, f, len(w.shards_timed))
     os.makedirs(PROFILES, exist_ok=True)
     with open(os.path.join(PROFILES, f"{w.name}{tag}_kernels.md"), "w") as f:
         f.write(f"# Kernel times, {path_name}{w.name} (M={w.M}, H={w.H}, F_i={w.F_i}, t={w.t})\n\n")
