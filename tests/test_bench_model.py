@@ -1,0 +1,39 @@
+"""bench.py's accounting on the CPU: the FLOPs and algorithmic bytes it divides
+by launch times, for plain, batched and paired launches (no GPU needed)."""
+import bench
+from tensor_transformer_mlp_03_amd import inputs as I
+
+
+def test_flops_per_launch_kind():
+    w = I.CONFIGS[3]
+    f = 2.0 * w.M * w.H * w.F_i
+    fl = bench.gemm_flops(w)
+    assert all(fl[k] == f for k in ("fwd_gemm1_gelu", "fwd_gemm2", "bwd_dgelu", "bwd_dB", "bwd_dA", "bwd_dX"))
+    # the step's model FLOPs: six products per shard, all shards
+    assert w.model_flops_per_shard() * w.t == 6 * f * w.t
+
+
+def test_batch_factor_counts_shards_per_launch():
+    w = I.CONFIGS[2]  # t = 8, every shard timed
+    steps = 5
+    assert bench.batch_factor(w, "fwd_gemm1_gelu", 2 * steps, steps) == 4.0  # batches of 4
+    assert bench.batch_factor(w, "fwd_gemm2", 4 * steps, steps) == 2.0       # pairs
+    assert bench.batch_factor(w, "bwd_dX", 8 * steps, steps) == 1.0          # one launch per shard
+    assert bench.batch_factor(w, "transpose", 2 * steps, steps) == 1.0       # not a per-shard product
+
+
+def test_paired_launch_bytes():
+    """A paired F3 or dX launch reads both shards' operands, writes the output once
+    and reads the running sum once unless it is the first pair; unpaired and
+    batched launches scale the per-shard bytes."""
+    w = I.CONFIGS[2]
+    M, H, F, t = w.M, w.H, w.F_i, w.t
+    base = bench.gemm_alg_bytes(w, w.recompute, fold=bench.folds(w))
+    assert bench.launch_alg_bytes(w, "fwd_gemm2", 1.0, t) == base["fwd_gemm2"]
+    assert bench.launch_alg_bytes(w, "bwd_dgelu", 4.0, t) == 4 * base["bwd_dgelu"]
+    pairs = t // 2
+    want = 2 * 2 * (M * F + F * H) + 4 * M * H + 4 * M * H * (pairs - 1) / pairs
+    assert bench.launch_alg_bytes(w, "fwd_gemm2", 2.0, t) == want
+    assert bench.launch_alg_bytes(w, "bwd_dX", 2.0, t) == want
+    # over a step, the paired launches move less than twice as many single ones
+    assert pairs * want < t * base["fwd_gemm2"]
