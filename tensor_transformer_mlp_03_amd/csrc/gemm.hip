@@ -302,6 +302,7 @@ __device__ __forceinline__ void store_staged(StageChunk&& stage_chunk, ScaleFn&&
       __builtin_amdgcn_sched_barrier(0);
     }
     if (EPI == EPI_F32 || ACC || PAIR) {
+      const bool final_out = args.k_split >= args.K;  // not a split-K slice
       const __amdgpu_buffer_rsrc_t rs = make_rsrc(reinterpret_cast<float*>(args.out) +
                                                   (int64_t)split * args.split_stride +
                                                   (int64_t)(row_w + 64 * h) * args.ldo + col_c);
@@ -324,7 +325,10 @@ __device__ __forceinline__ void store_staged(StageChunk&& stage_chunk, ScaleFn&&
           if (ACC) xs[u] += old[ch & 1][it];
           if constexpr (PAIR) xs[u] += ys[u];
           const uint32_t off = (uint32_t)(((int64_t)r * args.ldo + 4 * c) * 4);
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, xs[u]), rs, ok ? off : OOB, 0, 0);
+          if (final_out)  // non-temporal: a final output is not read again by this launch
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, xs[u]), rs, ok ? off : OOB, 0, 2);
+          else
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, xs[u]), rs, ok ? off : OOB, 0, 0);
         }
       }
     } else {
