@@ -107,10 +107,19 @@ def gemm_alg_bytes(w, recompute, fold=False):
         "bwd_dB": 2 * (M * F + M * H) + 4 * F * H,                                    # G^T, dZ^T -> dB_i
         "bwd_dA": 2 * (M * H + M * F) + 4 * H * F,                                    # X^T, dP -> dA_i
         "bwd_dX": 2 * (M * F + H * F) + 4 * M * H + acc,                              # dP, A_i (+dX) -> dX
-        "transpose": 4 * M * H,                                                       # X -> X^T, dZ -> dZ^T
+        "transpose": 8 * M * H,                                                       # X, dZ -> X^T, dZ^T (one launch)
         # X, A_i, B_i -> float32 partials of Z_i, one per chunk of 64 intermediate columns (+P)
         "fwd_fused": 2 * (M * H + 2 * H * F) + 4 * M * H * (-(-F // 64)) + (0 if recompute else 2 * M * F),
     }
+
+
+def transpose_alg_bytes(w, launches):
+    """Average algorithmic bytes of one transpose launch over a step with `launches`
+    of them: X and dZ together (8 M H bytes) before a backward, dP_i (4 M F_i) per
+    shard when dA reads it transposed, and weight transposes (4 H F_i each) for the rest."""
+    n_x = 1 if w.backward else 0
+    n_p = len(w.shards_timed) if (w.backward and dp_transposed(w)) else 0
+    return (n_x * 8 * w.M * w.H + n_p * 4 * w.M * w.F_i + (launches - n_x - n_p) * 4 * w.H * w.F_i) / launches
 
 
 def launch_alg_bytes(w, kind, factor, shards):
@@ -312,18 +321,14 @@ def summarize(d, config, fp8=False):
         a["write"] += wr["counters"]["WRITE_SIZE"] * 1024 * w_scale
     alg = fp8_alg_bytes(w, fold=folds(w)) if fp8 else gemm_alg_bytes(w, w.recompute, fold=folds(w))
     if "transpose" in agg and not fp8:
-        # A backward step transposes X and dZ ([M,H]) once each, and dP ([M,F_i]) once per
-        # shard when the planner transposes it for dA (large H: the library's rule is
+        # A backward step transposes X and dZ ([M,H]) in one launch, and dP ([M,F_i]) once
+        # per shard when the planner transposes it for dA (large H: the library's rule is
         # restated in dp_transposed); every further launch is a weight transpose
         # ([H,F_i] or [F_i,H]).  Per launch: the step's average.
-        n_t = agg["transpose"]["n"]
-        n_x = 2 if w.backward else 0
-        n_p = len(w.shards_timed) if (w.backward and dp_transposed(w)) else 0
-        alg["transpose"] = (n_x * 4 * w.M * w.H + n_p * 4 * w.M * w.F_i
-                            + (n_t - n_x - n_p) * 4 * w.H * w.F_i) / n_t
+        alg["transpose"] = transpose_alg_bytes(w, agg["transpose"]["n"])
     alg["shard_sum"] = (w.t + 1) * w.M * w.H * 4  # t float32 partials in, their sum out
     for kind, a in agg.items():  # a batched launch covers several shards (the counter passes run one step)
-        if kind in alg:
+        if kind in alg and kind not in ("transpose", "shard_sum"):  # those two are per launch already
             f = batch_factor(w, kind, a["n"], 1)
             alg[kind] = alg[kind] * f if fp8 else launch_alg_bytes(w, kind, f, len(w.shards_timed))
     os.makedirs(PROFILES, exist_ok=True)

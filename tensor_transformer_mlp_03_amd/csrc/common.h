@@ -131,6 +131,9 @@ hipError_t launch_splitk_epilogue(Epi epi, const float* part, int splits, int64_
 // multiples of 8).
 hipError_t launch_transpose(const uint16_t* in, int64_t R, int64_t C, int64_t ld_in, uint16_t* out,
                             hipStream_t stream, int64_t ld_out = 0);
+// Two matrices of the same shape and strides in one launch (in1 null: one).
+hipError_t launch_transpose2(const uint16_t* in0, uint16_t* out0, const uint16_t* in1, uint16_t* out1, int64_t R,
+                             int64_t C, int64_t ld_in, hipStream_t stream, int64_t ld_out = 0);
 
 // Fused forward for small hidden sizes (ffn.hip): workgroup (row block r,
 // chunk c) computes GeLU(X[r] A_i[:, c]) B_i[c, :] with G kept in LDS and

@@ -195,21 +195,28 @@ int grid_for(int64_t n4) {
 // tile, and consecutive workgroups continue along the rows, so that the output
 // rows (R * 2 bytes apart, often a power of two) are written in long runs
 // rather than 64 rows at a time at one stride, which would load one memory
-// channel.
+// channel.  One launch can transpose two matrices of the same shape (X and dZ
+// before a backward): workgroups [0, blocks) take the first, [blocks, 2 blocks)
+// the second.
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 struct TransposeArgs {
-  const uint16_t* in;
-  uint16_t* out;
+  const uint16_t* in[2];
+  uint16_t* out[2];
   int64_t R, C;  // in is [R][C] (rows of ld_in elements), out is [C][R] (rows of ld_out)
   int64_t ld_in, ld_out;
   int row_groups;  // groups of four 64-row tiles
+  int blocks;      // workgroups per matrix
 };
 
 __global__ void __launch_bounds__(256) transpose_kernel(TransposeArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   const int lane = threadIdx.x & 63;
-  const int rg = blockIdx.x % a.row_groups, ct = blockIdx.x / a.row_groups;
+  const int job = (int)blockIdx.x >= a.blocks ? 1 : 0;  // uniform over the workgroup
+  const int bid = (int)blockIdx.x - job * a.blocks;
+  const uint16_t* in = job ? a.in[1] : a.in[0];
+  uint16_t* out = job ? a.out[1] : a.out[0];
+  const int rg = bid % a.row_groups, ct = bid / a.row_groups;
   // The wave's 64 x 64 tile starts at (tr, tc); the buffer descriptor is built
   // from that wave-uniform origin (a per-lane base would not fit the scalar
   // descriptor and would serialize the loads).
@@ -220,7 +227,7 @@ __global__ void __launch_bounds__(256) transpose_kernel(TransposeArgs a) {
   const int64_t r0 = tr + lr, c0 = tc + lc;
   if (r0 >= a.R || c0 >= a.C) return;
   const __amdgpu_buffer_rsrc_t rs =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.in + tr * a.ld_in + tc), (short)0, 0x7FFFFFF0, 0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(in + tr * a.ld_in + tc), (short)0, 0x7FFFFFF0, 0x00020000);
   u32x4_t v[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
@@ -235,7 +242,7 @@ __global__ void __launch_bounds__(256) transpose_kernel(TransposeArgs a) {
     u32x4_t o;
 #pragma unroll
     for (int e = 0; e < 4; ++e) o[e] = __builtin_amdgcn_perm(v[2 * e + 1][j >> 1], v[2 * e][j >> 1], sel);
-    *reinterpret_cast<u32x4_t*>(a.out + (c0 + j) * a.ld_out + r0) = o;
+    *reinterpret_cast<u32x4_t*>(out + (c0 + j) * a.ld_out + r0) = o;
   }
 #else
   (void)a;
@@ -275,20 +282,31 @@ hipError_t launch_splitk_epilogue(Epi epi, const float* part, int splits, int64_
   }
 }
 
-hipError_t launch_transpose(const uint16_t* in, int64_t R, int64_t C, int64_t ld_in, uint16_t* out,
-                            hipStream_t stream, int64_t ld_out) {
+hipError_t launch_transpose2(const uint16_t* in0, uint16_t* out0, const uint16_t* in1, uint16_t* out1, int64_t R,
+                             int64_t C, int64_t ld_in, hipStream_t stream, int64_t ld_out) {
   if (ld_out == 0) ld_out = R;
   if (ld_in < C || (ld_in & 7) || ld_out < R || (ld_out & 7)) return hipErrorInvalidValue;
+  if (!in0 || !out0 || (in1 && !out1)) return hipErrorInvalidValue;
   TransposeArgs a;
-  a.in = in;
-  a.out = out;
+  a.in[0] = in0;
+  a.out[0] = out0;
+  a.in[1] = in1;
+  a.out[1] = out1;
   a.R = R;
   a.C = C;
   a.ld_in = ld_in;
   a.ld_out = ld_out;
   a.row_groups = (int)((R + 255) / 256);
   const int64_t blocks = (int64_t)a.row_groups * ((C + 63) / 64);
-  return launch_kernel(transpose_kernel, dim3((unsigned)blocks), dim3(256), stream, a);
+  const int jobs = in1 ? 2 : 1;
+  if (blocks * jobs > INT32_MAX) return hipErrorInvalidValue;
+  a.blocks = (int)blocks;
+  return launch_kernel(transpose_kernel, dim3((unsigned)(blocks * jobs)), dim3(256), stream, a);
+}
+
+hipError_t launch_transpose(const uint16_t* in, int64_t R, int64_t C, int64_t ld_in, uint16_t* out,
+                            hipStream_t stream, int64_t ld_out) {
+  return launch_transpose2(in, out, nullptr, nullptr, R, C, ld_in, stream, ld_out);
 }
 
 }  // namespace tpmlp

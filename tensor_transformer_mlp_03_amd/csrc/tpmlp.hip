@@ -599,7 +599,8 @@ hipError_t enqueue_fwd(const tpmlp_bf16* X, const tpmlp_bf16* A, int64_t lda, co
 }
 
 // Enqueue rank i's backward (arguments already checked).
-// X^T and dZ^T [H][M] into the backward workspace (shared by all shards).
+// X^T and dZ^T [H][M] into the backward workspace (shared by all shards), in
+// one launch.
 // The drivers fold the rank-order sum of the shards' partials into the
 // products that make them when no per-shard partial is asked for: shard 0's
 // row-parallel product (forward) or input-gradient product (backward) writes
@@ -619,9 +620,7 @@ hipError_t enqueue_transposes(const tpmlp_bf16* dZ, const tpmlp_bf16* X, int64_t
   const BwdPlan p = plan_bwd(M, H, 8, false);  // the transposes' offsets do not depend on F or recompute
   uint16_t* Xt = reinterpret_cast<uint16_t*>(ws_at(ws, p.off_Xt));
   uint16_t* dZt = reinterpret_cast<uint16_t*>(ws_at(ws, p.off_dZt));
-  hipError_t e = timed(TPMLP_K_TRANSPOSE, s, [&] { return launch_transpose(X, M, H, H, Xt, s); });
-  if (e != hipSuccess) return e;
-  return timed(TPMLP_K_TRANSPOSE, s, [&] { return launch_transpose(dZ, M, H, H, dZt, s); });
+  return timed(TPMLP_K_TRANSPOSE, s, [&] { return launch_transpose2(X, Xt, dZ, dZt, M, H, H, s); });
 }
 
 hipError_t enqueue_bwd_weights_dx(const BwdPlan& p, const uint16_t* dP, const uint16_t* Gt, const uint16_t* Xt,
@@ -770,16 +769,17 @@ size_t sp_ws_bytes(int t, int64_t M, int64_t H, int64_t F) {
                             sp_bwd_layout(t, M, H, F, false).total}));
 }
 
-// X^T and dZ^T [H][M] from the ranks' slices: slice r fills columns [r S, (r+1) S).
+// X^T and dZ^T [H][M] from the ranks' slices: slice r fills columns [r S, (r+1) S);
+// one launch per rank takes both.
 hipError_t enqueue_sp_transposes(const tpmlp_bf16* const* dZ_sl, const tpmlp_bf16* const* X_sl, int t, int64_t M,
                                  int64_t H, void* ws, hipStream_t s) {
   const SpBwdLayout L = sp_bwd_layout(t, M, H, 8, false);  // the transposes' offsets depend on M and H only
   uint16_t* Xt = reinterpret_cast<uint16_t*>(ws_at(ws, L.off_Xt));
   uint16_t* dZt = reinterpret_cast<uint16_t*>(ws_at(ws, L.off_dZt));
   for (int r = 0; r < t; ++r) {
-    hipError_t e = timed(TPMLP_K_TRANSPOSE, s, [&] { return launch_transpose(X_sl[r], L.S, H, H, Xt + r * L.S, s, M); });
-    if (e != hipSuccess) return e;
-    e = timed(TPMLP_K_TRANSPOSE, s, [&] { return launch_transpose(dZ_sl[r], L.S, H, H, dZt + r * L.S, s, M); });
+    const hipError_t e = timed(TPMLP_K_TRANSPOSE, s, [&] {
+      return launch_transpose2(X_sl[r], Xt + r * L.S, dZ_sl[r], dZt + r * L.S, L.S, H, H, s, M);
+    });
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

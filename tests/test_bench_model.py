@@ -37,3 +37,17 @@ def test_paired_launch_bytes():
     assert bench.launch_alg_bytes(w, "bwd_dX", 2.0, t) == want
     # over a step, the paired launches move less than twice as many single ones
     assert pairs * want < t * base["fwd_gemm2"]
+
+
+def test_transpose_launch_bytes():
+    """X and dZ are transposed in one launch before a backward; the other transpose
+    launches of a step are dP_i (when dA reads it transposed) and the weights."""
+    w = I.CONFIGS[1]  # one shard, no weight or dP transposes
+    assert not bench.dp_transposed(w)
+    assert bench.transpose_alg_bytes(w, 1) == 8 * w.M * w.H
+    w = I.CONFIGS[3]  # four shards, A_i and B_i transposed for the forward
+    want = (8 * w.M * w.H + 8 * 4 * w.H * w.F_i) / 9
+    assert bench.transpose_alg_bytes(w, 9) == want
+    w = I.CONFIGS[4]  # shard 0 timed; dP_0 transposed for dA, A_0 for nothing else
+    assert bench.dp_transposed(w)
+    assert bench.transpose_alg_bytes(w, 2) == (8 * w.M * w.H + 4 * w.M * w.F_i) / 2

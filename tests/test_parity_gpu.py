@@ -796,7 +796,7 @@ def test_timing_counts_launches():
     # no per-shard partials asked for: the sums are folded into the products' epilogues
     assert stats["bwd_dX"][0] == n3 and stats["shard_sum"][0] == 0
     assert stats["bwd_recompute"][0] == 0
-    assert stats["transpose"][0] == 2  # X^T and dZ^T once for both shards
+    assert stats["transpose"][0] == 1  # X^T and dZ^T in one launch, once for both shards
     assert all(ms >= 0 for _, ms in stats.values())
     recs = L.tpmlp_timing_records()
     assert len(recs) == sum(n for n, _ in stats.values()) and all(ms > 0 for _, ms in recs)
