@@ -114,12 +114,19 @@ def gemm_alg_bytes(w, recompute, fold=False):
 
 
 def transpose_alg_bytes(w, launches):
-    """Average algorithmic bytes of one transpose launch over a step with `launches`
-    of them: X and dZ together (8 M H bytes) before a backward, dP_i (4 M F_i) per
-    shard when dA reads it transposed, and weight transposes (4 H F_i each) for the rest."""
-    n_x = 1 if w.backward else 0
-    n_p = len(w.shards_timed) if (w.backward and dp_transposed(w)) else 0
-    return (n_x * 8 * w.M * w.H + n_p * 4 * w.M * w.F_i + (launches - n_x - n_p) * 4 * w.H * w.F_i) / launches
+    """Average algorithmic bytes of one of a step's `launches` transpose launches.
+    The step transposes X and dZ (4 M H bytes each) before a backward, dP_i
+    (4 M F_i) per shard when dA reads it transposed, and A_i and B_i (4 H F_i each)
+    per shard in the forward, A_i again for the recompute, when the planner
+    transposes the weights.  How many launches carry them (X with dZ, A_i with B_i
+    when they share a shape) changes only the divisor."""
+    n = len(w.shards_timed)
+    total = 8 * w.M * w.H if w.backward else 0
+    if w.backward and dp_transposed(w):
+        total += n * 4 * w.M * w.F_i
+    if weights_transposed(w):
+        total += n * (2 + (1 if (w.backward and w.recompute) else 0)) * 4 * w.H * w.F_i
+    return total / launches
 
 
 def launch_alg_bytes(w, kind, factor, shards):
@@ -158,6 +165,14 @@ def dp_transposed(w):
     transpose, 4 M F_i / 5.5e12 s (the planner's rates), i.e. for H above ~12400."""
     saved = 2.0 * w.M * w.H * w.F_i * (1.0 / 1.14e15 - 1.0 / 1.2e15)
     return saved > 1.5 * 4.0 * w.M * w.F_i / 5.5e12
+
+
+def weights_transposed(w):
+    """Whether the library transposes A_i and B_i for the forward products (the
+    planner's rule restated): the saving on two products, 4 M H F_i (1/1.14e15 -
+    1/1.2e15) s, is 1.5 times the transposes' 4 H F_i / 5.5e12 s, i.e. M above ~6200."""
+    saved = 4.0 * w.M * w.H * w.F_i * (1.0 / 1.14e15 - 1.0 / 1.2e15)
+    return saved > 1.5 * 4.0 * w.H * w.F_i / 5.5e12
 
 
 def folds(w):

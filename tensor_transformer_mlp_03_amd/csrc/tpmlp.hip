@@ -575,7 +575,10 @@ hipError_t enqueue_fwd(const tpmlp_bf16* X, const tpmlp_bf16* A, int64_t lda, co
   if (p.wt) {
     uint16_t* At = reinterpret_cast<uint16_t*>(ws_at(ws, p.off_At));
     uint16_t* Bt = reinterpret_cast<uint16_t*>(ws_at(ws, p.off_Bt));
-    if (!weights_ready) {
+    if (!weights_ready && H == F && lda == H) {  // A_i and B_i of one shape: one launch
+      e = timed(TPMLP_K_TRANSPOSE, s, [&] { return launch_transpose2(A, At, B, Bt, H, F, H, s); });
+      if (e != hipSuccess) return e;
+    } else if (!weights_ready) {
       e = timed(TPMLP_K_TRANSPOSE, s, [&] { return launch_transpose(A, H, F, lda, At, s); });
       if (e != hipSuccess) return e;
       e = timed(TPMLP_K_TRANSPOSE, s, [&] { return launch_transpose(B, F, H, H, Bt, s); });

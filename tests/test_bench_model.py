@@ -45,9 +45,12 @@ def test_transpose_launch_bytes():
     w = I.CONFIGS[1]  # one shard, no weight or dP transposes
     assert not bench.dp_transposed(w)
     assert bench.transpose_alg_bytes(w, 1) == 8 * w.M * w.H
-    w = I.CONFIGS[3]  # four shards, A_i and B_i transposed for the forward
-    want = (8 * w.M * w.H + 8 * 4 * w.H * w.F_i) / 9
-    assert bench.transpose_alg_bytes(w, 9) == want
+    w = I.CONFIGS[3]  # four shards, A_i and B_i (one shape) transposed together for the forward
+    assert bench.weights_transposed(w) and w.H == w.F_i
+    want = (8 * w.M * w.H + 8 * 4 * w.H * w.F_i) / 5
+    assert bench.transpose_alg_bytes(w, 5) == want
+    for c in (0, 1, 2, 4):  # M = 4096 or less: the weights are read in place
+        assert not bench.weights_transposed(I.CONFIGS[c])
     w = I.CONFIGS[4]  # shard 0 timed; dP_0 transposed for dA, A_0 for nothing else
     assert bench.dp_transposed(w)
     assert bench.transpose_alg_bytes(w, 2) == (8 * w.M * w.H + 4 * w.M * w.F_i) / 2
