@@ -348,7 +348,7 @@ typedef enum {
   TPMLP_K_BWD_DX = 6,         /* dX_i = dP_i A_i^T */
   TPMLP_K_SPLITK_REDUCE = 7,  /* sum of split-K float32 partials */
   TPMLP_K_SHARD_SUM = 8,      /* tpmlp_shard_sum and the drivers' partial sums */
-  TPMLP_K_TRANSPOSE = 9,      /* X^T and dZ^T for the weight-gradient products */
+  TPMLP_K_TRANSPOSE = 9,      /* X^T with dZ^T (one launch), dP_i^T, and the weights transposed */
   TPMLP_K_FWD_FUSED = 10,     /* Z_i chunk partials = GeLU(X A_i) B_i in one launch, G in LDS */
   TPMLP_K_FP8_QUANT = 11,     /* FP8 drivers: amax and quantization of operands */
   TPMLP_K_COUNT = 12
