@@ -76,7 +76,7 @@ def gemm_flops(w):
     M, H, F = w.M, w.H, w.F_i
     f = 2.0 * M * H * F
     return {"fwd_gemm1_gelu": f, "fwd_gemm2": f, "bwd_recompute": f, "bwd_dgelu": f, "bwd_dB": f, "bwd_dA": f,
-            "bwd_dX": f, "fwd_fused": 2 * f}
+            "bwd_dX": f, "fwd_fused": 2 * f, "bwd_dB_dX": 2 * f}
 
 
 def batch_factor(w, kind, launches, steps):
@@ -107,6 +107,8 @@ def gemm_alg_bytes(w, recompute, fold=False):
         "bwd_dB": 2 * (M * F + M * H) + 4 * F * H,                                    # G^T, dZ^T -> dB_i
         "bwd_dA": 2 * (M * H + M * F) + 4 * H * F,                                    # X^T, dP -> dA_i
         "bwd_dX": 2 * (M * F + H * F) + 4 * M * H + acc,                              # dP, A_i (+dX) -> dX
+        # dB_i and dX_i as one launch (M = F_i, no running sum)
+        "bwd_dB_dX": 2 * (M * F + M * H) + 4 * F * H + 2 * (M * F + H * F) + 4 * M * H,
         "transpose": 8 * M * H,                                                       # X, dZ -> X^T, dZ^T (one launch)
         # X, A_i, B_i -> float32 partials of Z_i, one per chunk of 64 intermediate columns (+P)
         "fwd_fused": 2 * (M * H + 2 * H * F) + 4 * M * H * (-(-F // 64)) + (0 if recompute else 2 * M * F),

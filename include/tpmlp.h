@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define TPMLP_ABI_VERSION 11
+#define TPMLP_ABI_VERSION 12
 #define TPMLP_MAX_SHARDS 64
 
 typedef uint16_t tpmlp_bf16; /* raw bf16 bits */
@@ -351,7 +351,8 @@ typedef enum {
   TPMLP_K_TRANSPOSE = 9,      /* X^T with dZ^T (one launch), dP_i^T, and the weights transposed */
   TPMLP_K_FWD_FUSED = 10,     /* Z_i chunk partials = GeLU(X A_i) B_i in one launch, G in LDS */
   TPMLP_K_FP8_QUANT = 11,     /* FP8 drivers: amax and quantization of operands */
-  TPMLP_K_COUNT = 12
+  TPMLP_K_BWD_DB_DX = 12,     /* dB_i and dX_i in one launch (one shape: M = F_i, no running sum) */
+  TPMLP_K_COUNT = 13
 } tpmlp_kernel_kind;
 
 /* Static name of a kernel kind ("?" if out of range). */

@@ -25,7 +25,7 @@ STATUS = {
     4: "TPMLP_ERR_WORKSPACE", 5: "TPMLP_ERR_SHARDS", 6: "TPMLP_ERR_HIP",
     7: "TPMLP_ERR_UNSUPPORTED", 8: "TPMLP_ERR_ALIAS", 9: "TPMLP_ERR_NO_FORWARD",
 }
-KERNEL_COUNT = 12
+KERNEL_COUNT = 13
 MAX_SHARDS = 64
 
 

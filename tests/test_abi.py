@@ -99,7 +99,7 @@ def test_last_error_is_per_thread():
 
 
 def test_version_and_strings():
-    assert L.tpmlp_abi_version() == 11
+    assert L.tpmlp_abi_version() == 12
     assert L.tpmlp_status_str(0) == "ok"
     assert L.tpmlp_status_str(ALIAS) == "output overlaps another buffer"
     assert L.tpmlp_status_str(99) == "unknown status"

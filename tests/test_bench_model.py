@@ -9,6 +9,7 @@ def test_flops_per_launch_kind():
     f = 2.0 * w.M * w.H * w.F_i
     fl = bench.gemm_flops(w)
     assert all(fl[k] == f for k in ("fwd_gemm1_gelu", "fwd_gemm2", "bwd_dgelu", "bwd_dB", "bwd_dA", "bwd_dX"))
+    assert fl["bwd_dB_dX"] == 2 * f  # two products in one launch
     # the step's model FLOPs: six products per shard, all shards
     assert w.model_flops_per_shard() * w.t == 6 * f * w.t
 
@@ -54,3 +55,13 @@ def test_transpose_launch_bytes():
     w = I.CONFIGS[4]  # shard 0 timed; dP_0 transposed for dA, A_0 for nothing else
     assert bench.dp_transposed(w)
     assert bench.transpose_alg_bytes(w, 2) == (8 * w.M * w.H + 4 * w.M * w.F_i) / 2
+
+
+def test_grouped_db_dx_bytes():
+    """A launch that runs dB_i and dX_i together (M = F_i, no running sum) moves
+    both products' operands and outputs."""
+    w = I.CONFIGS[1]
+    assert w.M == w.F_i and w.t == 1
+    base = bench.gemm_alg_bytes(w, w.recompute, fold=bench.folds(w))
+    assert base["bwd_dB_dX"] == base["bwd_dB"] + base["bwd_dX"]
+    assert bench.launch_alg_bytes(w, "bwd_dB_dX", bench.batch_factor(w, "bwd_dB_dX", 5, 5), 1) == base["bwd_dB_dX"]

@@ -816,7 +816,9 @@ def test_batched_shards_equal_rank_calls_bitwise(case):
     """Short-K shapes: the t-shard driver runs several shards' F1 (and the
     recompute and dGeLU) as one batched launch.  Each product stays unsplit, so
     every shard's P_i, Z_i, dX_i, dA_i and dB_i have the bits of that rank's own
-    tpmlp_fwd / tpmlp_bwd calls."""
+    tpmlp_fwd / tpmlp_bwd calls.  With M = F_i a rank's call runs its dB_i and dX_i
+    as one launch, while the driver batches the shards' dB instead: the two ways
+    give the same bits too."""
     from tensor_transformer_mlp_03_amd import _lib as L
     from tensor_transformer_mlp_03_amd.device import DeviceMLP
     M, H, F_, t, store = case
@@ -829,8 +831,12 @@ def test_batched_shards_equal_rank_calls_bitwise(case):
     stats, _ = L.tpmlp_timing_end()
     assert stats["fwd_gemm1_gelu"][0] < t and stats["bwd_dgelu"][0] < t, stats  # batched
     rank = DeviceMLP(inp, store_p=store, driver=False)
+    L.tpmlp_timing_begin(256)
     rank.step()
+    stats, _ = L.tpmlp_timing_end()
     torch.cuda.synchronize()
+    if M == F_:  # each rank's dB_i and dX_i share one launch; the driver batched dB instead
+        assert stats["bwd_dB_dX"][0] == t and stats["bwd_dB"][0] == 0 and stats["bwd_dX"][0] == 0, stats
     for i in range(t):
         assert torch.equal(drv.Z_sh[i], rank.Z_sh[i]), f"Z_{i}"
         assert torch.equal(drv.dX_sh[i], rank.dX_sh[i]), f"dX_{i}"
