@@ -97,6 +97,10 @@ SMALL = [
     # ... many chunks and row blocks, backward recomputing
     (520, 128, 1032, 2, False),
     (72, 256, 2056, 2, True),
+    # M = F_i, ragged: with one shard its dB_i and dX_i run as one launch; with two the
+    # driver batches the shards' dB instead
+    (1048, 264, 1048, 1, True),
+    (520, 1040, 520, 2, False),
 ]
 
 
